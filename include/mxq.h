@@ -1,0 +1,267 @@
+/*
+ * mxq.h -- C ABI of the microscaling quantization library for MI355X (gfx950).
+ *
+ * What it computes (sources are the web pages this library is written from):
+ *
+ *  - MXFP8: blocks of 32 E4M3 values sharing one E8M0 power-of-two scale
+ *    ("Miles Blackwell RL Troca a Uniformidade BF16 por MXFP8 e NVFP4
+ *    Nativos", section "O Suporte Miles Blackwell Agora Abrange Todo o Loop
+ *    de RL"; "End-to-End MXFP8 Reinforcement Learning on Blackwell",
+ *    Table 10 F6: an E8M0 scale keeps only an exponent), plus a 32x32 tile
+ *    variant for weights read in both orientations.
+ *  - NVFP4: blocks of 16 E2M1 values with an E4M3 block scale under a second
+ *    FP32 scale that is per token (same Miles page, same section; "NVFP4 RL
+ *    training", baseline-recipe section) or per tensor, with 16x16 weight
+ *    blocks shared by FPROP and DGRAD, RNE for weights/activations and
+ *    stochastic rounding for gradients ("Train models faster with JAX and
+ *    MaxText using NVFP4 on NVIDIA Blackwell", section "NVFP4 pretraining
+ *    recipe").
+ *  - BF16 dequantization DQ(Q(x)) for the dequantized backward ("NVFP4 RL
+ *    training", section on the dequantized backward).
+ *  - FPROP / DGRAD / WGRAD GEMMs on the quantized operands with BF16 output
+ *    (NVFP4 MaxText page, "NVFP4 pretraining recipe"), dense or grouped per
+ *    MoE expert.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory, never synchronizes, and keeps no pointer
+ *    after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it; results are ready when the stream reaches that point.
+ *  - BF16 values are passed as their uint16_t bit patterns; matrices are
+ *    row-major with an explicit leading dimension (elements, unless stated).
+ *  - Arguments are validated on the host before anything is launched.  On any
+ *    error nothing is written, no kernel is launched, the status says why, and
+ *    mxq_last_error() (thread-local) gives a message.  No C++ exception ever
+ *    crosses this interface.
+ *  - Inputs must be finite.  Non-finite inputs give unspecified codes.
+ *  - Calls may run concurrently on different streams when their output
+ *    buffers do not overlap.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_VERSION 1
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_EINVAL = 1,        /* null pointer, negative size, bad enum value        */
+  MXQ_ESHAPE = 2,        /* a size is not a multiple of what the format needs  */
+  MXQ_EALIGN = 3,        /* pointer or leading dimension not 16-byte aligned   */
+  MXQ_EUNSUPPORTED = 4,  /* a valid but unsupported combination (never emulated) */
+  MXQ_EHIP = 5           /* the HIP runtime reported an error at launch        */
+} mxq_status;
+
+typedef enum {
+  MXQ_FMT_MXFP8 = 0,     /* E4M3 codes (1 byte) + E8M0 scales                  */
+  MXQ_FMT_NVFP4 = 1,     /* E2M1 codes (2 per byte) + E4M3 scales + FP32 scale */
+  MXQ_FMT_BF16 = 2       /* plain BF16 (GEMM operands only)                    */
+} mxq_format;
+
+typedef enum {
+  /* Blocks along the contiguous dimension: 1x32 (MXFP8) or 1x16 (NVFP4). */
+  MXQ_BLOCK_ROW = 0,
+  /* Blocks along rows: 32x1 or 16x1.  The copy is stored TRANSPOSED,
+   * [cols, rows], so that its blocks are contiguous again (the copy a WGRAD
+   * GEMM reads). */
+  MXQ_BLOCK_COL = 1,
+  /* One scale per 32x32 (MXFP8) or 16x16 (NVFP4) tile; the same codes and
+   * scales read transposed serve the transposed GEMM operand. */
+  MXQ_BLOCK_TILE = 2,
+  /* MXFP8 only: ROW and COL copies from one read of the input. */
+  MXQ_BLOCK_DUAL = 3,
+  /* BF16 operands: no blocks. */
+  MXQ_BLOCK_NONE = 4
+} mxq_block;
+
+typedef enum {
+  MXQ_GS_NONE = 0,       /* MXFP8 / BF16: no second-level scale                 */
+  MXQ_GS_PER_ROW = 1,    /* NVFP4: one FP32 scale per row (per token)           */
+  MXQ_GS_PER_TENSOR = 2, /* NVFP4: one FP32 scale for the whole tensor          */
+  MXQ_GS_GIVEN = 3       /* NVFP4: the caller supplies the per-tensor scale     */
+} mxq_gscale;
+
+typedef enum {
+  MXQ_ROUND_RNE = 0,     /* round to nearest, ties to even                      */
+  MXQ_ROUND_SR = 1       /* stochastic rounding (NVFP4 elements only)           */
+} mxq_round;
+
+typedef enum {
+  /* Scale grid row-major: [rows, cols/B] for 1D blocks, [rows/B, cols/B] for
+   * tiles (B = block size; for a COL copy "rows" are the input's columns). */
+  MXQ_LAYOUT_LINEAR = 0,
+  /* 1D blocks only: chunks of 32 rows x 4 consecutive blocks, 128 bytes each,
+   * stored chunk-row-major; inside a chunk row r%32 owns bytes 4*(r%32)..+3
+   * (its 4 blocks in order).  Byte offset of (row r, block b), with
+   * B = blocks per row:  ((r/32)*(B/4) + b/4)*128 + (r%32)*4 + b%4.
+   * Needs rows % 32 == 0 and B % 4 == 0.  This is the order in which the GEMM
+   * kernels fetch scales, one 128-byte line per 32-row MFMA tile. */
+  MXQ_LAYOUT_MFMA = 1
+} mxq_scale_layout;
+
+/*
+ * mx_quantize -- MXFP8 quantization of a BF16 matrix x [rows, cols].
+ *
+ * Block rule (the pages give none; this is the plainest reading of "no block
+ * overflows after scaling"): the block's E8M0 exponent e is the smallest
+ * integer in [-127, 127] with max|x| <= 448 * 2^e (all-zero block: e = -127,
+ * code 0x00); each code is E4M3 round-to-nearest-even of x * 2^-e, which is an
+ * exact scaling and never saturates.
+ *
+ *   x, ld_x            input, row-major, ld_x >= cols (elements)
+ *   block              ROW: codes [rows, cols] (ld_codes), scales per layout
+ *                      COL: codes [cols, rows] (ld_codes), scales [cols, rows/32]
+ *                      TILE: codes [rows, cols], scales [rows/32, cols/32] LINEAR
+ *                      DUAL: ROW copy into codes/scales AND COL copy into
+ *                            codes_col/scales_col (ld_codes_col)
+ *   layout             LINEAR or MFMA (MFMA: ROW/COL/DUAL only)
+ *   codes_col, scales_col, ld_codes_col   DUAL only, else ignored (may be NULL)
+ * Shapes: cols % 32 == 0; rows % 32 == 0 for COL, TILE, DUAL.
+ * Alignment: x, codes, codes_col 16-byte aligned; ld_x*2, ld_codes and
+ * ld_codes_col multiples of 16.
+ */
+mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       mxq_block block, mxq_scale_layout layout,
+                       uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                       uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
+                       void* stream);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of a BF16 matrix x [rows, cols].
+ *
+ * Steps, each fl() one binary32 IEEE operation (round-to-nearest-even,
+ * subnormals kept, no fused multiply-add):
+ *   S   = fl(A / 2688), A = max|x| over the row (PER_ROW) or tensor
+ *         (PER_TENSOR); GIVEN reads S from gscales[0].  A = 0 gives S = 0.
+ *   s_b = E4M3 RNE (saturating) of fl(a_b / fl(6*S)), a_b = block max|x|.
+ *   code: s_b == 0 -> signed zero; else E2M1 of fl(x * fl(1 / fl(s_b*S))),
+ *         RNE or stochastic (saturating at 6).
+ * Stochastic rounding draws 16 bits per element from Philox4x32-10 with key
+ * (seed lo, seed hi) and counter (n lo, n hi, stream_id, tensor_tag),
+ * n = idx / 8, idx = row*cols + col of the element in x; element idx takes
+ * output word (idx%8)/2, low half if idx is even, high half if odd; it rounds
+ * up iff draw * 2^-16 < the fraction of the way to the next grid point.
+ *
+ *   block   ROW (1x16): codes [rows, cols/2] bytes (ld_codes_bytes),
+ *                        block_scales per layout, gscales [rows] (PER_ROW) or [1]
+ *           COL (16x1): transposed copy, codes [cols, rows/2] bytes,
+ *                        block_scales [cols, rows/16]; PER_TENSOR or GIVEN only
+ *           TILE (16x16): codes [rows, cols/2], block_scales [rows/16, cols/16]
+ *                        LINEAR; PER_TENSOR or GIVEN only
+ *   gs      PER_ROW (ROW only), PER_TENSOR, GIVEN
+ *   rnd     RNE or SR
+ *   codes   two E2M1 codes per byte, even element in the low nibble
+ *   gscales PER_ROW/PER_TENSOR: written; GIVEN: read (caller's S >= 0)
+ * With PER_TENSOR the call enqueues an extra read pass over x for A, using
+ * gscales[0] as its accumulator; gscales must not alias x, codes or scales.
+ * Shapes: cols % 16 == 0 (ROW); rows % 16 == 0 and cols % 16 == 0 (COL,
+ * TILE).  Alignment: x, codes 16-byte aligned, ld_x*2 and ld_codes_bytes
+ * multiples of 16; gscales 4-byte aligned.
+ * Precondition for exactness: a nonzero row/tensor has A >= 2^-64.
+ */
+mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, mxq_gscale gs, mxq_round rnd,
+                          uint64_t seed, uint32_t stream_id, uint32_t tensor_tag,
+                          mxq_scale_layout layout,
+                          uint8_t* codes, int64_t ld_codes_bytes,
+                          uint8_t* block_scales, float* gscales,
+                          void* stream);
+
+/*
+ * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16 (the operand of the
+ * dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
+ * COL copy that is [input cols, input rows]); block says how its scales are
+ * laid out (ROW for a COL copy too, since the stored copy is row-blocked).
+ *   MXFP8: bf16_RNE(value(c) * 2^e)  (exact unless beyond the BF16 range)
+ *   NVFP4: bf16_RNE(fl(fl(value(c) * s_b) * S))
+ *   ld_codes  elements for MXFP8, BYTES for NVFP4; ld_out elements.
+ *   gscales   NVFP4 only ([rows] for PER_ROW, [1] otherwise); may be NULL for MXFP8.
+ */
+mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
+                         const uint8_t* scales, const float* gscales,
+                         int64_t rows, int64_t cols, mxq_block block, mxq_gscale gs,
+                         mxq_scale_layout layout, uint16_t* out, int64_t ld_out,
+                         void* stream);
+
+/*
+ * A GEMM operand: one stored copy made by the quantizers above, or BF16.
+ *
+ * A is logically [M, K], B logically [N, K]; both are normally stored with K
+ * contiguous (rowwise blocks along K).  B with transposed != 0 is stored
+ * [K, N] (N contiguous) and must be tile-blocked (MXFP8 32x32, NVFP4 16x16)
+ * or BF16: that is how a DGRAD reads the FPROP weight copy.
+ *   data     codes (MXFP8: 1 B/elem; NVFP4: packed, 2 elem/B) or BF16 values
+ *   ld       leading dimension of the stored matrix in ELEMENTS (even for NVFP4)
+ *   scales   block scales of the stored copy (NULL for BF16)
+ *   gscales  NVFP4 second-level scales (per row of A, or per tensor; for a
+ *            grouped B one per group); NULL otherwise
+ *   block    ROW (1D along K), TILE (2D), NONE (BF16)
+ *   gs       PER_ROW (A only), PER_TENSOR / GIVEN (same meaning here), NONE
+ *   layout   scale layout (MFMA allowed for ROW blocks)
+ * Grouped B: num_groups matrices stored back to back, group g at
+ *   data + g*N*ld elements, scales + g*(N*K/B) bytes, gscales + g.
+ */
+typedef struct {
+  mxq_format fmt;
+  const void* data;
+  const uint8_t* scales;
+  const float* gscales;
+  mxq_block block;
+  mxq_gscale gs;
+  mxq_scale_layout layout;
+  int64_t ld;
+  int32_t transposed;
+} mxq_operand;
+
+/*
+ * mx_gemm -- C[M, N] = sum_k A[m, k] * B[n, k], FP32 accumulation, BF16 out.
+ *   FPROP  Y  = X  * W^T : A = rowwise X,  B = W (rowwise or tile)
+ *   DGRAD  dX = dY * W   : A = rowwise dY, B = W tile copy with transposed=1
+ *   WGRAD  dW = dY^T * X : A = columnwise dY copy, B = columnwise X copy
+ * A and B must have the same format (MXFP8 x MXFP8 on the scaled MFMA,
+ * NVFP4 x NVFP4 dequantized exactly to FP16 for the FP16 MFMA, or
+ * BF16 x BF16); mixed formats give MXQ_EUNSUPPORTED.
+ *   c, ldc              BF16 output, row-major
+ *   num_groups          0 for a dense GEMM; else grouped (MoE experts)
+ *   group_row_offsets   device int32 [num_groups+1], non-decreasing, from 0 to
+ *                       M; rows [off[g], off[g+1]) of C use B group g
+ *   a_row_index         device int32 [M] or NULL: row r of C reads A row
+ *                       a_row_index[r] (gather), every entry in [0, a_rows)
+ *   a_rows              rows stored in A (== M when a_row_index is NULL)
+ * Shapes: K % 32 (MXFP8), K % 16 (NVFP4), K % 8 (BF16); a transposed B needs
+ * N and K multiples of its tile size.  M, N any positive size.
+ * Offsets and indices are read on the device and are NOT validated: values
+ * outside the stated ranges give undefined results.
+ */
+mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b,
+                   int64_t M, int64_t N, int64_t K, int64_t a_rows,
+                   uint16_t* c, int64_t ldc,
+                   int32_t num_groups, const int32_t* group_row_offsets,
+                   const int32_t* a_row_index, void* stream);
+
+/*
+ * mx_swiglu -- h = silu(g) * u for a [rows, 2*inter] BF16 gate_up output
+ * (gate = first inter columns, up = last inter columns), computed in binary32
+ * with silu(g) = g / (1 + exp(-g)), stored as BF16 RNE [rows, inter].
+ * This sits between the grouped gate_up and down GEMMs of the MoE experts
+ * (SwiGLU experts: "Miles Blackwell RL ...", section "Um Quantizador
+ * Compartilhado É o Verdadeiro Mecanismo").  inter % 8 == 0; 16-byte aligned.
+ */
+mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
+                     uint16_t* h, int64_t ld_h, void* stream);
+
+const char* mxq_status_str(mxq_status s);
+const char* mxq_last_error(void);
+int mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */
