@@ -1,0 +1,238 @@
+"""Python binding of libmxq, the MI355X (gfx950) microscaling quantization
+library.  Argument marshalling only: every step of the hot path runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.
+
+The names and arguments follow the C ABI in include/mxq.h:
+    mx_quantize, nvfp4_quantize, mx_dequantize, mx_gemm, mx_swiglu
+Outputs the caller does not pass are allocated here with torch (the library
+itself never allocates).  Every call is asynchronous on the current stream.
+
+There is no fallback: if libmxq.so is missing or a call fails, this raises.
+"""
+
+import ctypes
+import enum
+import os
+
+import torch
+
+__all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
+           "mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu",
+           "library_path", "lib"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmxq.so")
+
+
+class Format(enum.IntEnum):
+    MXFP8 = 0
+    NVFP4 = 1
+    BF16 = 2
+
+
+class Block(enum.IntEnum):
+    ROW = 0
+    COL = 1
+    TILE = 2
+    DUAL = 3
+    NONE = 4
+
+
+class GScale(enum.IntEnum):
+    NONE = 0
+    PER_ROW = 1
+    PER_TENSOR = 2
+    GIVEN = 3
+
+
+class Round(enum.IntEnum):
+    RNE = 0
+    SR = 1
+
+
+class Layout(enum.IntEnum):
+    LINEAR = 0
+    MFMA = 1
+
+
+class MXQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class _Operand(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("gscales", ctypes.c_void_p), ("block", ctypes.c_int), ("gs", ctypes.c_int),
+                ("layout", ctypes.c_int), ("ld", ctypes.c_int64), ("transposed", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmxq (ctypes).  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is missing: build it with "
+                          "`python -m microscaling_quantization_block_amd.build`")
+    L = ctypes.CDLL(library_path)
+    i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    L.mx_quantize.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, i64, vp, vp]
+    L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
+    L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
+    L.mx_gemm.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
+                          vp, i64, ctypes.c_int32, vp, vp, vp]
+    L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
+    for f in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu"):
+        getattr(L, f).restype = ci
+    L.mxq_last_error.restype = ctypes.c_char_p
+    L.mxq_status_str.restype = ctypes.c_char_p
+    L.mxq_status_str.argtypes = [ci]
+    L.mxq_version.restype = ci
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise MXQError(status, L.mxq_last_error().decode() or L.mxq_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_2d(x, dtype, name):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != dtype or not x.is_cuda:
+        raise TypeError(f"{name} must be a 2-D {dtype} CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+
+
+def _u8(shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- quantizers
+
+def mx_quantize(x, block=Block.ROW, layout=Layout.LINEAR, codes=None, scales=None,
+                codes_col=None, scales_col=None, stream=None):
+    """MXFP8 quantization of a BF16 matrix.  Returns (codes, scales) or, for
+    DUAL, (codes, scales, codes_col, scales_col)."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    block = Block(block)
+    if block == Block.COL:
+        codes = _u8((cols, rows), dev) if codes is None else codes
+        scales = _u8((cols, max(rows // 32, 0)), dev) if scales is None else scales
+    elif block == Block.TILE:
+        codes = _u8((rows, cols), dev) if codes is None else codes
+        scales = _u8((max(rows // 32, 0), cols // 32), dev) if scales is None else scales
+    else:
+        codes = _u8((rows, cols), dev) if codes is None else codes
+        scales = _u8((rows, cols // 32), dev) if scales is None else scales
+    if block == Block.DUAL:
+        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
+        scales_col = _u8((cols, max(rows // 32, 0)), dev) if scales_col is None else scales_col
+    ldc = codes.stride(0)
+    ldcc = codes_col.stride(0) if codes_col is not None else 0
+    _check(lib().mx_quantize(_ptr(x), rows, cols, x.stride(0), int(block), int(layout), _ptr(codes),
+                             ldc, _ptr(scales), _ptr(codes_col), ldcc, _ptr(scales_col), _stream(stream)))
+    if block == Block.DUAL:
+        return codes, scales, codes_col, scales_col
+    return codes, scales
+
+
+def nvfp4_quantize(x, block=Block.ROW, gs=GScale.PER_ROW, rnd=Round.RNE, seed=0, stream_id=0,
+                   tensor_tag=0, layout=Layout.LINEAR, codes=None, block_scales=None,
+                   gscales=None, stream=None):
+    """NVFP4 quantization.  Returns (packed codes, E4M3 block scales, FP32 S).
+    For gs=GIVEN pass `gscales` holding S (a 1-element float32 CUDA tensor)."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    block, gs = Block(block), GScale(gs)
+    if block == Block.COL:
+        codes = _u8((cols, rows // 2), dev) if codes is None else codes
+        block_scales = _u8((cols, rows // 16), dev) if block_scales is None else block_scales
+    elif block == Block.TILE:
+        codes = _u8((rows, cols // 2), dev) if codes is None else codes
+        block_scales = _u8((rows // 16, cols // 16), dev) if block_scales is None else block_scales
+    else:
+        codes = _u8((rows, cols // 2), dev) if codes is None else codes
+        block_scales = _u8((rows, cols // 16), dev) if block_scales is None else block_scales
+    if gscales is None:
+        if gs == GScale.GIVEN:
+            raise ValueError("gs=GIVEN needs gscales")
+        gscales = torch.empty(rows if gs == GScale.PER_ROW else 1, dtype=torch.float32, device=dev)
+    _check(lib().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), int(block), int(gs), int(rnd),
+                                int(seed), int(stream_id), int(tensor_tag), int(layout), _ptr(codes),
+                                codes.stride(0), _ptr(block_scales), _ptr(gscales), _stream(stream)))
+    return codes, block_scales, gscales
+
+
+def mx_dequantize(fmt, codes, scales, rows, cols, block=Block.ROW, gscales=None, gs=GScale.NONE,
+                  layout=Layout.LINEAR, out=None, stream=None):
+    """DQ(Q(x)) of one stored copy ([rows, cols] as stored) to BF16."""
+    fmt = Format(fmt)
+    dev = codes.device
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check(lib().mx_dequantize(int(fmt), _ptr(codes), codes.stride(0), _ptr(scales), _ptr(gscales),
+                               rows, cols, int(block), int(gs), int(layout), _ptr(out),
+                               out.stride(0), _stream(stream)))
+    return out
+
+
+class Operand:
+    """A GEMM operand: a stored quantized copy (or BF16 tensor) plus its format.
+    `ld` defaults to the row stride of `data` in elements."""
+
+    def __init__(self, fmt, data, scales=None, gscales=None, block=Block.ROW, gs=GScale.NONE,
+                 layout=Layout.LINEAR, ld=None, transposed=False):
+        self.fmt, self.data, self.scales, self.gscales = Format(fmt), data, scales, gscales
+        self.block, self.gs, self.layout = Block(block), GScale(gs), Layout(layout)
+        if ld is None:
+            ld = data.stride(-2) * (2 if self.fmt == Format.NVFP4 else 1)
+        self.ld, self.transposed = int(ld), bool(transposed)
+
+    def _c(self):
+        return _Operand(int(self.fmt), self.data.data_ptr(),
+                        0 if self.scales is None else self.scales.data_ptr(),
+                        0 if self.gscales is None else self.gscales.data_ptr(),
+                        int(self.block), int(self.gs), int(self.layout), self.ld,
+                        1 if self.transposed else 0)
+
+
+def mx_gemm(a, b, M, N, K, out=None, group_row_offsets=None, a_row_index=None, a_rows=None,
+            stream=None):
+    """C[M, N] = sum_k A[m, k] B[n, k] in BF16 (FP32 accumulation)."""
+    dev = a.data.device
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    ng = 0 if group_row_offsets is None else group_row_offsets.numel() - 1
+    if a_rows is None:
+        a_rows = M
+    ca, cb = a._c(), b._c()
+    _check(lib().mx_gemm(ctypes.byref(ca), ctypes.byref(cb), M, N, K, int(a_rows), _ptr(out),
+                         out.stride(0), ng, _ptr(group_row_offsets), _ptr(a_row_index),
+                         _stream(stream)))
+    return out
+
+
+def mx_swiglu(gu, inter, out=None, stream=None):
+    """h = silu(g) * u for gate_up [rows, 2*inter] BF16 -> [rows, inter] BF16."""
+    _check_2d(gu, torch.bfloat16, "gu")
+    rows = gu.shape[0]
+    out = torch.empty((rows, inter), dtype=torch.bfloat16, device=gu.device) if out is None else out
+    _check(lib().mx_swiglu(_ptr(gu), rows, inter, gu.stride(0), _ptr(out), out.stride(0),
+                           _stream(stream)))
+    return out

@@ -1,0 +1,316 @@
+// C ABI of the library: argument validation on the host, then kernel launches
+// on the caller's stream.  See include/mxq.h for the contract of every entry.
+// No allocation, no synchronization, no state kept between calls except the
+// thread-local text of the last error.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "mxq.h"
+#include "mxq_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mxq_status fail(mxq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mxq_status ok() {
+  g_err[0] = 0;
+  return MXQ_OK;
+}
+
+mxq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MXQ_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mxq_version(void) { return MXQ_VERSION; }
+
+const char* mxq_last_error(void) { return g_err; }
+
+const char* mxq_status_str(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_EINVAL: return "MXQ_EINVAL: invalid argument";
+    case MXQ_ESHAPE: return "MXQ_ESHAPE: size not a multiple of the block";
+    case MXQ_EALIGN: return "MXQ_EALIGN: pointer or leading dimension not 16-byte aligned";
+    case MXQ_EUNSUPPORTED: return "MXQ_EUNSUPPORTED: unsupported combination";
+    case MXQ_EHIP: return "MXQ_EHIP: HIP runtime error";
+  }
+  return "unknown mxq_status";
+}
+
+// ---------------------------------------------------------------- quantize
+mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       mxq_block block, mxq_scale_layout layout, uint8_t* codes,
+                       int64_t ld_codes, uint8_t* scales, uint8_t* codes_col,
+                       int64_t ld_codes_col, uint8_t* scales_col, void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "mx_quantize: negative size");
+  if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE &&
+      block != MXQ_BLOCK_DUAL)
+    return fail(MXQ_EINVAL, "mx_quantize: block must be ROW, COL, TILE or DUAL");
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
+    return fail(MXQ_EINVAL, "mx_quantize: bad scale layout");
+  if (rows == 0 || cols == 0) return ok();
+  if (!x || !codes || !scales) return fail(MXQ_EINVAL, "mx_quantize: null pointer");
+  if (block == MXQ_BLOCK_DUAL && (!codes_col || !scales_col))
+    return fail(MXQ_EINVAL, "mx_quantize: DUAL needs codes_col and scales_col");
+  if (cols % 32) return fail(MXQ_ESHAPE, "mx_quantize: cols %% 32 != 0 (cols=%lld)", (long long)cols);
+  if (block != MXQ_BLOCK_ROW && rows % 32)
+    return fail(MXQ_ESHAPE, "mx_quantize: rows %% 32 != 0 for a COL/TILE/DUAL copy (rows=%lld)", (long long)rows);
+  const bool mfma = layout == MXQ_LAYOUT_MFMA;
+  if (mfma) {
+    if (block == MXQ_BLOCK_TILE)
+      return fail(MXQ_EUNSUPPORTED, "mx_quantize: the MFMA scale layout is for 1D blocks only");
+    if ((block == MXQ_BLOCK_ROW || block == MXQ_BLOCK_DUAL) && (rows % 32 || cols % 128))
+      return fail(MXQ_ESHAPE, "mx_quantize: MFMA layout of a rowwise copy needs rows %% 32 == 0 and cols %% 128 == 0");
+    if ((block == MXQ_BLOCK_COL || block == MXQ_BLOCK_DUAL) && rows % 128)
+      return fail(MXQ_ESHAPE, "mx_quantize: MFMA layout of a columnwise copy needs rows %% 128 == 0");
+  }
+  const int64_t need_row = block == MXQ_BLOCK_COL ? rows : cols;
+  if (ld_x < cols || ld_codes < need_row || (block == MXQ_BLOCK_DUAL && ld_codes_col < rows))
+    return fail(MXQ_EINVAL, "mx_quantize: leading dimension smaller than the row");
+  if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes % 16 ||
+      (block == MXQ_BLOCK_DUAL && (!aligned16(codes_col) || ld_codes_col % 16)))
+    return fail(MXQ_EALIGN, "mx_quantize: pointers and leading dimensions must be 16-byte aligned");
+  hipError_t e;
+  if (block == MXQ_BLOCK_ROW)
+    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, mfma, S(stream));
+  else
+    e = mxq::launch_mxfp8_tile(block == MXQ_BLOCK_COL ? 0 : block == MXQ_BLOCK_TILE ? 1 : 2, x,
+                               rows, cols, ld_x, codes, ld_codes, scales, codes_col, ld_codes_col,
+                               scales_col, mfma, S(stream));
+  return hip_status(e, "mx_quantize");
+}
+
+mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, mxq_gscale gs, mxq_round rnd, uint64_t seed,
+                          uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
+                          uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                          float* gscales, void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "nvfp4_quantize: negative size");
+  if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE)
+    return fail(block == MXQ_BLOCK_DUAL ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
+                "nvfp4_quantize: block must be ROW, COL or TILE");
+  if (gs != MXQ_GS_PER_ROW && gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
+    return fail(MXQ_EINVAL, "nvfp4_quantize: gs must be PER_ROW, PER_TENSOR or GIVEN");
+  if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR) return fail(MXQ_EINVAL, "nvfp4_quantize: bad rounding");
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
+    return fail(MXQ_EINVAL, "nvfp4_quantize: bad scale layout");
+  if (gs == MXQ_GS_PER_ROW && block != MXQ_BLOCK_ROW)
+    return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize: a per-row second scale needs ROW blocks "
+                                  "(a columnwise or tiled copy takes a per-tensor scale)");
+  if (rows == 0 || cols == 0) return ok();
+  if (!x || !codes || !block_scales || !gscales) return fail(MXQ_EINVAL, "nvfp4_quantize: null pointer");
+  if (cols % 16) return fail(MXQ_ESHAPE, "nvfp4_quantize: cols %% 16 != 0 (cols=%lld)", (long long)cols);
+  if (block != MXQ_BLOCK_ROW && rows % 16)
+    return fail(MXQ_ESHAPE, "nvfp4_quantize: rows %% 16 != 0 for a COL/TILE copy (rows=%lld)", (long long)rows);
+  const bool mfma = layout == MXQ_LAYOUT_MFMA;
+  if (mfma) {
+    if (block == MXQ_BLOCK_TILE)
+      return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize: the MFMA scale layout is for 1D blocks only");
+    if (block == MXQ_BLOCK_ROW && (rows % 32 || cols % 64))
+      return fail(MXQ_ESHAPE, "nvfp4_quantize: MFMA layout needs rows %% 32 == 0 and cols %% 64 == 0");
+    if (block == MXQ_BLOCK_COL && (cols % 32 || rows % 64))
+      return fail(MXQ_ESHAPE, "nvfp4_quantize: MFMA layout of a columnwise copy needs cols %% 32 == 0 and rows %% 64 == 0");
+  }
+  const int64_t need = block == MXQ_BLOCK_COL ? rows / 2 : cols / 2;
+  if (ld_x < cols || ld_codes_bytes < need)
+    return fail(MXQ_EINVAL, "nvfp4_quantize: leading dimension smaller than the row");
+  if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes_bytes % 8 ||
+      ((uintptr_t)gscales & 3u))
+    return fail(MXQ_EALIGN, "nvfp4_quantize: x/codes must be 16-byte aligned, ld_x*2 %% 16 == 0, "
+                            "ld_codes_bytes %% 8 == 0, gscales 4-byte aligned");
+  hipStream_t st = S(stream);
+  const bool sr = rnd == MXQ_ROUND_SR;
+  hipError_t e = hipSuccess;
+  if (gs == MXQ_GS_PER_TENSOR) {
+    e = mxq::launch_nvfp4_tensor_scale(x, rows, cols, ld_x, gscales, st);
+    if (e == hipSuccess) e = mxq::launch_nvfp4_finalize(gscales, st);
+    if (e != hipSuccess) return hip_status(e, "nvfp4_quantize (tensor amax)");
+  }
+  if (block == MXQ_BLOCK_ROW)
+    e = mxq::launch_nvfp4_row(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
+                              gs == MXQ_GS_PER_ROW ? 0 : 1, mfma, sr, seed, stream_id, tensor_tag, st);
+  else if (block == MXQ_BLOCK_TILE)
+    e = mxq::launch_nvfp4_tile16(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
+                                 sr, seed, stream_id, tensor_tag, st);
+  else
+    e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales, sr,
+                              seed, stream_id, tensor_tag, st);
+  return hip_status(e, "nvfp4_quantize");
+}
+
+// ---------------------------------------------------------------- dequantize
+mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
+                         const uint8_t* scales, const float* gscales, int64_t rows, int64_t cols,
+                         mxq_block block, mxq_gscale gs, mxq_scale_layout layout, uint16_t* out,
+                         int64_t ld_out, void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "mx_dequantize: negative size");
+  if (fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4) return fail(MXQ_EINVAL, "mx_dequantize: format must be MXFP8 or NVFP4");
+  if (block == MXQ_BLOCK_COL || block == MXQ_BLOCK_DUAL)
+    return fail(MXQ_EUNSUPPORTED, "mx_dequantize: pass ROW for a stored columnwise copy (it is row-blocked)");
+  if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_TILE) return fail(MXQ_EINVAL, "mx_dequantize: bad block");
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA) return fail(MXQ_EINVAL, "mx_dequantize: bad layout");
+  const bool mfma = layout == MXQ_LAYOUT_MFMA;
+  if (mfma && block == MXQ_BLOCK_TILE)
+    return fail(MXQ_EUNSUPPORTED, "mx_dequantize: the MFMA scale layout is for 1D blocks only");
+  if (rows == 0 || cols == 0) return ok();
+  if (!codes || !scales || !out) return fail(MXQ_EINVAL, "mx_dequantize: null pointer");
+  if (!aligned16(codes) || !aligned16(out) || (ld_out * 2) % 16 || ld_codes % 8)
+    return fail(MXQ_EALIGN, "mx_dequantize: codes/out 16-byte aligned, ld_out*2 %% 16 == 0, ld_codes %% 8 == 0");
+  if (ld_out < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_out < cols");
+  hipError_t e;
+  if (fmt == MXQ_FMT_MXFP8) {
+    if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: MXFP8 has no second-level scale");
+    if (cols % 32 || (block == MXQ_BLOCK_TILE && rows % 32))
+      return fail(MXQ_ESHAPE, "mx_dequantize: MXFP8 needs cols %% 32 == 0 (and rows %% 32 for TILE)");
+    if (mfma && (rows % 32 || cols % 128)) return fail(MXQ_ESHAPE, "mx_dequantize: MFMA layout needs rows %% 32, cols %% 128");
+    if (ld_codes < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_codes < cols");
+    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, mfma, out,
+                             ld_out, S(stream));
+  } else {
+    if (!gscales) return fail(MXQ_EINVAL, "mx_dequantize: NVFP4 needs gscales");
+    if (gs != MXQ_GS_PER_ROW && gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
+      return fail(MXQ_EINVAL, "mx_dequantize: NVFP4 needs a second-level scale mode");
+    if (gs == MXQ_GS_PER_ROW && block != MXQ_BLOCK_ROW)
+      return fail(MXQ_EUNSUPPORTED, "mx_dequantize: per-row second scale with tile blocks");
+    if (cols % 16 || (block == MXQ_BLOCK_TILE && rows % 16))
+      return fail(MXQ_ESHAPE, "mx_dequantize: NVFP4 needs cols %% 16 == 0 (and rows %% 16 for TILE)");
+    if (mfma && (rows % 32 || cols % 64)) return fail(MXQ_ESHAPE, "mx_dequantize: MFMA layout needs rows %% 32, cols %% 64");
+    if (ld_codes < cols / 2) return fail(MXQ_EINVAL, "mx_dequantize: ld_codes (bytes) < cols/2");
+    e = mxq::launch_dq_nvfp4(codes, ld_codes, scales, gscales, rows, cols, block == MXQ_BLOCK_TILE,
+                             gs == MXQ_GS_PER_ROW ? 0 : 1, mfma, out, ld_out, S(stream));
+  }
+  return hip_status(e, "mx_dequantize");
+}
+
+// ---------------------------------------------------------------- GEMM
+static mxq_status check_operand(const char* name, const mxq_operand* o, bool is_b, int64_t rows,
+                                int64_t K, int64_t N_for_bt) {
+  if (!o->data) return fail(MXQ_EINVAL, "mx_gemm: %s->data is NULL", name);
+  if (o->fmt != MXQ_FMT_MXFP8 && o->fmt != MXQ_FMT_NVFP4 && o->fmt != MXQ_FMT_BF16)
+    return fail(MXQ_EINVAL, "mx_gemm: %s has a bad format", name);
+  if (!aligned16(o->data)) return fail(MXQ_EALIGN, "mx_gemm: %s->data not 16-byte aligned", name);
+  if (o->transposed && !is_b) return fail(MXQ_EUNSUPPORTED, "mx_gemm: only B may be stored transposed");
+  const int blk = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : 1;
+  if (o->fmt == MXQ_FMT_BF16) {
+    if (o->block != MXQ_BLOCK_NONE) return fail(MXQ_EINVAL, "mx_gemm: a BF16 %s takes block NONE", name);
+    if ((o->ld * 2) % 16) return fail(MXQ_EALIGN, "mx_gemm: %s->ld*2 %% 16 != 0", name);
+  } else {
+    if (!o->scales) return fail(MXQ_EINVAL, "mx_gemm: %s->scales is NULL", name);
+    if (o->block == MXQ_BLOCK_NONE || o->block == MXQ_BLOCK_DUAL)
+      return fail(MXQ_EINVAL, "mx_gemm: %s block must be ROW or TILE", name);
+    if (o->block == MXQ_BLOCK_COL)
+      return fail(MXQ_EINVAL, "mx_gemm: a stored columnwise copy is row-blocked: pass ROW for %s", name);
+    if (o->block == MXQ_BLOCK_TILE && !is_b)
+      return fail(MXQ_EUNSUPPORTED, "mx_gemm: tile blocks are supported for B only");
+    if (o->ld % 16) return fail(MXQ_EALIGN, "mx_gemm: %s->ld %% 16 != 0", name);
+    if (o->layout == MXQ_LAYOUT_MFMA) {
+      if (o->block != MXQ_BLOCK_ROW) return fail(MXQ_EUNSUPPORTED, "mx_gemm: MFMA layout with tile blocks");
+      if (rows % 32 || (K / blk) % 4) return fail(MXQ_ESHAPE, "mx_gemm: MFMA layout of %s needs rows %% 32 and K/block %% 4", name);
+    } else if (o->layout != MXQ_LAYOUT_LINEAR) {
+      return fail(MXQ_EINVAL, "mx_gemm: bad scale layout for %s", name);
+    }
+  }
+  if (o->fmt == MXQ_FMT_NVFP4) {
+    if (!o->gscales) return fail(MXQ_EINVAL, "mx_gemm: %s->gscales is NULL", name);
+    if (o->gs == MXQ_GS_PER_ROW) {
+      if (is_b) return fail(MXQ_EUNSUPPORTED, "mx_gemm: B takes a per-tensor second scale");
+    } else if (o->gs != MXQ_GS_PER_TENSOR && o->gs != MXQ_GS_GIVEN) {
+      return fail(MXQ_EINVAL, "mx_gemm: NVFP4 %s needs a second-level scale mode", name);
+    }
+  }
+  if (o->transposed) {
+    if (o->fmt != MXQ_FMT_BF16 && o->block != MXQ_BLOCK_TILE)
+      return fail(MXQ_EUNSUPPORTED, "mx_gemm: a transposed quantized B must be tile-blocked");
+    const int t = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : 8;
+    if (N_for_bt % t || K % t) return fail(MXQ_ESHAPE, "mx_gemm: transposed B needs N and K multiples of %d", t);
+    if (o->ld < N_for_bt) return fail(MXQ_EINVAL, "mx_gemm: B->ld < N");
+  } else {
+    if (o->ld < K) return fail(MXQ_EINVAL, "mx_gemm: %s->ld < K", name);
+    if (o->block == MXQ_BLOCK_TILE && (rows % blk || K % blk))
+      return fail(MXQ_ESHAPE, "mx_gemm: tile-blocked %s needs rows and K multiples of %d", name, blk);
+  }
+  return MXQ_OK;
+}
+
+mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
+                   int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
+                   const int32_t* group_row_offsets, const int32_t* a_row_index, void* stream) {
+  if (!a || !b) return fail(MXQ_EINVAL, "mx_gemm: null operand");
+  if (M < 0 || N < 0 || K < 0 || num_groups < 0 || a_rows < 0) return fail(MXQ_EINVAL, "mx_gemm: negative size");
+  if (a->fmt != b->fmt) return fail(MXQ_EUNSUPPORTED, "mx_gemm: A and B formats differ");
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(MXQ_EUNSUPPORTED, "mx_gemm: K == 0 (nothing would be written)");
+  if (!c) return fail(MXQ_EINVAL, "mx_gemm: c is NULL");
+  if (num_groups > 0 && !group_row_offsets) return fail(MXQ_EINVAL, "mx_gemm: grouped call without offsets");
+  if (!a_row_index && a_rows != M) return fail(MXQ_EINVAL, "mx_gemm: a_rows must equal M without a gather index");
+  if (a_rows < 1) return fail(MXQ_EINVAL, "mx_gemm: a_rows < 1");
+  const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16 : 8;
+  if (K % blk) return fail(MXQ_ESHAPE, "mx_gemm: K %% %d != 0 (K=%lld)", blk, (long long)K);
+  if (ldc < N) return fail(MXQ_EINVAL, "mx_gemm: ldc < N");
+  mxq_status s = check_operand("A", a, false, a_rows, K, 0);
+  if (s != MXQ_OK) return s;
+  s = check_operand("B", b, true, N, K, N);
+  if (s != MXQ_OK) return s;
+  if (a->fmt != MXQ_FMT_BF16 && a->block != MXQ_BLOCK_ROW) return fail(MXQ_EUNSUPPORTED, "mx_gemm: A must be row-blocked");
+
+  mxq::GemmArgs g = {};
+  g.a = static_cast<const uint8_t*>(a->data);
+  g.a_scales = a->scales;
+  g.a_gs = a->gscales;
+  g.lda = a->ld;
+  g.a_mfma_layout = a->layout == MXQ_LAYOUT_MFMA;
+  g.a_gs_per_row = a->gs == MXQ_GS_PER_ROW;
+  g.b = static_cast<const uint8_t*>(b->data);
+  g.b_scales = b->scales;
+  g.b_gs = b->gscales;
+  g.ldb = b->ld;
+  g.b_mfma_layout = b->layout == MXQ_LAYOUT_MFMA;
+  g.b_tile = b->block == MXQ_BLOCK_TILE;
+  g.b_group_elems = (b->transposed ? K : N) * b->ld;
+  const int bb = b->fmt == MXQ_FMT_MXFP8 ? 32 : 16;
+  g.b_group_scales = b->fmt == MXQ_FMT_BF16 ? 0 : (g.b_tile ? (N / bb) * (K / bb) : N * (K / bb));
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c = c;
+  g.ldc = ldc;
+  g.num_groups = num_groups;
+  g.offsets = group_row_offsets;
+  g.row_index = a_row_index;
+  const int path = a->fmt == MXQ_FMT_MXFP8 ? mxq::P_FP8 : a->fmt == MXQ_FMT_NVFP4 ? mxq::P_F16 : mxq::P_BF16;
+  return hip_status(mxq::launch_gemm(path, b->transposed != 0, g, S(stream)), "mx_gemm");
+}
+
+// ---------------------------------------------------------------- SwiGLU
+mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu, uint16_t* h,
+                     int64_t ld_h, void* stream) {
+  if (rows < 0 || inter < 0) return fail(MXQ_EINVAL, "mx_swiglu: negative size");
+  if (rows == 0 || inter == 0) return ok();
+  if (!gu || !h) return fail(MXQ_EINVAL, "mx_swiglu: null pointer");
+  if (inter % 8) return fail(MXQ_ESHAPE, "mx_swiglu: inter %% 8 != 0");
+  if (ld_gu < 2 * inter || ld_h < inter) return fail(MXQ_EINVAL, "mx_swiglu: leading dimension too small");
+  if (!aligned16(gu) || !aligned16(h) || (ld_gu * 2) % 16 || (ld_h * 2) % 16)
+    return fail(MXQ_EALIGN, "mx_swiglu: 16-byte alignment required");
+  return hip_status(mxq::launch_swiglu(gu, rows, inter, ld_gu, h, ld_h, S(stream)), "mx_swiglu");
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Dequantizers and the SwiGLU elementwise kernel.
+//
+// The dequantized backward runs its BF16 GEMMs on DQ(Q(w)), the BF16 values
+// the forward pass actually used ("NVFP4 RL training" (The 4-bitter Lesson),
+// section on the dequantized backward; "Miles Blackwell RL ...", section "O
+// Suporte Miles Blackwell Agora Abrange Todo o Loop de RL").
+//   MXFP8: bf16_RNE(value(c) * 2^e)            (ldexp is exact in binary32)
+//   NVFP4: bf16_RNE(fl(fl(value(c) * s_b) * S)) (value(c) * s_b is exact)
+// Both are pure bandwidth kernels: codes and scales in, 16-byte BF16 stores out.
+
+#include "mxq_device.h"
+#include "mxq_kernels.h"
+
+namespace mxq {
+
+// MXFP8: one lane per 8 codes.  tile = 1 for 32x32 scales.
+__global__ __launch_bounds__(256) void dq_mxfp8_kernel(
+    const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
+    int64_t rows, int64_t cols, int tile, int mfma_layout, uint16_t* __restrict__ out,
+    int64_t ld_out) {
+  const int64_t cpr = cols >> 3;
+  const int64_t total = rows * cpr;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * 256) {
+    int64_t r = id / cpr, c = id - r * cpr;
+    uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + c * 8);
+    uint32_t s = tile ? scales[(r >> 5) * (cols >> 5) + (c >> 2)]
+                      : scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)];
+    int e = (int)s - 127;
+    uint32_t w[2] = {q.x, q.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t word = w[i >> 1] >> (16 * (i & 1));
+      float a = __builtin_ldexpf(e4m3_to_f32(word & 0xFF), e);
+      float b = __builtin_ldexpf(e4m3_to_f32((word >> 8) & 0xFF), e);
+      o[i] = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + r * ld_out + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// NVFP4: one lane per 16-element block (8 code bytes, one scale).
+// gmode: 0 = S per row, 1 = S per tensor.  tile = 1 for 16x16 scales.
+__global__ __launch_bounds__(256) void dq_nvfp4_kernel(
+    const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ gscales, int64_t rows, int64_t cols, int tile, int gmode,
+    int mfma_layout, uint16_t* __restrict__ out, int64_t ld_out) {
+  const int64_t bpr = cols >> 4;
+  const int64_t total = rows * bpr;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * 256) {
+    int64_t r = id / bpr, b = id - r * bpr;
+    uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + b * 8);
+    uint32_t sc = tile ? scales[(r >> 4) * bpr + b] : scales[scale_offset(r, b, bpr, mfma_layout)];
+    float sb = e4m3_to_f32(sc);
+    float S = gmode == 0 ? gscales[r] : gscales[0];
+    uint32_t w[2] = {q.x, q.y};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
+      uint32_t ca = byte & 0xF, cb = byte >> 4;
+      float va = (ca & 8) ? -e2m1_mag(ca & 7) : e2m1_mag(ca & 7);
+      float vb = (cb & 8) ? -e2m1_mag(cb & 7) : e2m1_mag(cb & 7);
+      float pa = va * sb, pb = vb * sb;      // exact
+      float da = pa * S, db = pb * S;        // one rounding each
+      o[i] = f32_to_bf16_rne(da) | (f32_to_bf16_rne(db) << 16);
+    }
+    uint16_t* dst = out + r * ld_out + b * 16;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// SwiGLU: h = silu(g) * u, silu(g) = g / (1 + exp(-g)), binary32, BF16 out.
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu, int64_t rows,
+                                                     int64_t inter, int64_t ld_gu,
+                                                     uint16_t* __restrict__ h, int64_t ld_h) {
+  const int64_t cpr = inter >> 3;
+  const int64_t total = rows * cpr;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * 256) {
+    int64_t r = id / cpr, c = id - r * cpr;
+    uint4 g = *reinterpret_cast<const uint4*>(gu + r * ld_gu + c * 8);
+    uint4 u = *reinterpret_cast<const uint4*>(gu + r * ld_gu + inter + c * 8);
+    uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w}, o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
+      float u0 = bf16_lo(uw[i]), u1 = bf16_hi(uw[i]);
+      float h0 = g0 / (1.0f + expf(-g0)) * u0;
+      float h1 = g1 / (1.0f + expf(-g1)) * u1;
+      o[i] = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+    }
+    *reinterpret_cast<uint4*>(h + r * ld_h + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+static unsigned grid_for(int64_t total) {
+  int64_t b = (total + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                           int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,
+                           int64_t ld_out, hipStream_t st) {
+  hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid_for(rows * (cols / 8))), dim3(256), 0, st, codes,
+                     ld_codes, scales, rows, cols, (int)tile, (int)mfma, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                           const float* gscales, int64_t rows, int64_t cols, bool tile,
+                           int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st) {
+  hipLaunchKernelGGL(dq_nvfp4_kernel, dim3(grid_for(rows * (cols / 16))), dim3(256), 0, st, codes,
+                     ld_codes, scales, gscales, rows, cols, (int)tile, gmode, (int)mfma, out,
+                     ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
+                         uint16_t* h, int64_t ld_h, hipStream_t st) {
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(rows * (inter / 8))), dim3(256), 0, st, gu, rows,
+                     inter, ld_gu, h, ld_h);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

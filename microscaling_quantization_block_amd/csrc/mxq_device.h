@@ -1,0 +1,140 @@
+// Device helpers shared by the quantizer, dequantizer and GEMM kernels
+// (gfx950 / CDNA4, wave64).  Everything here is bit-level format handling;
+// no routine depends on fast-math, and the library is compiled with
+// -ffp-contract=off so that a*b+c is never fused where the format contract
+// names two roundings.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round a binary32 value to BF16, nearest-even (finite or infinite inputs;
+// a finite value that rounds past the largest BF16 becomes infinity).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// |x| of both BF16 halves, then the larger as a 16-bit magnitude pattern.
+// For finite values the order of magnitude patterns is the order of |x|.
+__device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
+  uint32_t a = w & 0x7FFFu;
+  uint32_t b = (w >> 16) & 0x7FFFu;
+  return a > b ? a : b;
+}
+
+// ------------------------------------------------------------------ E4M3
+// Exact value of an E4M3 byte (OCP FN variant, no infinities) via the
+// hardware conversion (exact: every E4M3 value is a binary32 value).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Round-to-nearest-even of two binary32 values to E4M3, packed into the low
+// 16 bits (first value in the low byte).  Inputs must be below 464 in
+// magnitude (they are: every caller bounds them by 448 * (1 + 2^-22)).
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------ E2M1
+// E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7.
+__device__ __forceinline__ float e2m1_mag(uint32_t code3) {
+  // 2^(e-1) * (1 + m/2) for e > 0, 0.5 * m for e == 0
+  uint32_t e = (code3 >> 1) & 3u, m = code3 & 1u;
+  float nrm = __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return e ? nrm : 0.5f * (float)m;
+}
+
+// Round-to-nearest-even onto the E2M1 grid, saturating at 6.  Returns the
+// 4-bit code (sign in bit 3 taken from the sign bit of y).
+//   |y| in [1, 5]: round the binary32 mantissa to one bit (RNE on the bit
+//                  pattern); the result (exponent, bit) maps to the code.
+//   |y| < 1:       the code is rint(2|y|) (0 -> 0, 1 -> 0.5, 2 -> 1.0).
+//   |y| > 5:       6 (code 7).
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne(float y) {
+  uint32_t b = __float_as_uint(y);
+  uint32_t s = (b >> 28) & 8u;
+  uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t rnd = a + 0x1FFFFFu + ((a >> 22) & 1u);
+  uint32_t big = (rnd >> 22) - 252u;                       // 2..6 for |y| in [1, 5]
+  uint32_t small = (uint32_t)__builtin_rintf(2.0f * __uint_as_float(a));
+  uint32_t mag = a >= 0x3F800000u ? big : small;
+  mag = a > 0x40A00000u ? 7u : mag;
+  return s | mag;
+}
+
+// Stochastic rounding onto the E2M1 grid: with lo <= |y| < hi the grid
+// neighbours, round up iff r16 < (|y| - lo) / (hi - lo) * 2^16 (exact: the
+// difference is exact and the step is a power of two); |y| >= 6 gives 6.
+__device__ __forceinline__ uint32_t f32_to_e2m1_sr(float y, uint32_t r16) {
+  uint32_t b = __float_as_uint(y);
+  uint32_t s = (b >> 28) & 8u;
+  float a = __uint_as_float(b & 0x7FFFFFFFu);
+  // lower neighbour code: truncate onto the grid
+  uint32_t lo;
+  float lov, step;
+  if (a < 2.0f) {
+    lo = (uint32_t)(a * 2.0f);          // 0..3 (0, 0.5, 1, 1.5)
+    lov = 0.5f * (float)lo;
+    step = 0.5f;
+  } else if (a < 4.0f) {
+    uint32_t k = (uint32_t)a;           // 2 or 3
+    lo = k + 2u;                        // codes 4 (2.0), 5 (3.0)
+    lov = (float)k;
+    step = 1.0f;
+  } else {
+    lo = 6u;                            // 4.0
+    lov = 4.0f;
+    step = 2.0f;
+  }
+  float f = (a - lov) * (65536.0f / step);   // exact
+  uint32_t mag = ((float)r16 < f) ? lo + 1u : lo;
+  mag = a >= 6.0f ? 7u : mag;
+  return s | mag;
+}
+
+// ------------------------------------------------------------------ Philox
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64
+// multiplies with the published multipliers and Weyl key increments.
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// The 8 16-bit draws of elements [8n, 8n+8) of the logical input.
+__device__ __forceinline__ u32x4 philox_draws8(uint64_t n, uint64_t seed, uint32_t stream_id,
+                                               uint32_t tensor_tag) {
+  return philox4x32_10(u32x4{(uint32_t)n, (uint32_t)(n >> 32), stream_id, tensor_tag},
+                       (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// ------------------------------------------------------------------ lanes
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, 64);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// MFMA scale layout (1D blocks): chunks of 32 rows x 4 blocks, 128 bytes.
+__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t blocks_per_row,
+                                                bool mfma) {
+  if (!mfma) return r * blocks_per_row + b;
+  return ((r >> 5) * (blocks_per_row >> 2) + (b >> 2)) * 128 + (r & 31) * 4 + (b & 3);
+}
+
+}  // namespace mxq

@@ -1,0 +1,71 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma,
+                            hipStream_t st);
+// mode: 0 = COL (32x1, transposed copy), 1 = TILE (32x32), 2 = DUAL (ROW + COL)
+hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t cols,
+                             int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                             uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
+                             bool mfma, hipStream_t st);
+
+hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     float* gscale, hipStream_t st);
+hipError_t launch_nvfp4_finalize(float* gscale, hipStream_t st);
+// gmode: 0 = per row (computed), 1 = per tensor / given (read from gscales[0])
+hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
+                            int gmode, bool mfma, bool sr, uint64_t seed, uint32_t sid,
+                            uint32_t tag, hipStream_t st);
+hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
+                               const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                               uint32_t tag, hipStream_t st);
+hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
+                            const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                            uint32_t tag, hipStream_t st);
+
+hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                           int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,
+                           int64_t ld_out, hipStream_t st);
+hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                           const float* gscales, int64_t rows, int64_t cols, bool tile,
+                           int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st);
+hipError_t launch_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
+                         uint16_t* h, int64_t ld_h, hipStream_t st);
+
+enum Path { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
+
+struct GemmArgs {
+  const uint8_t* a;            // A data (codes / values)
+  const uint8_t* a_scales;
+  const float* a_gs;
+  int64_t lda;                 // elements
+  int a_mfma_layout;
+  int a_gs_per_row;
+  const uint8_t* b;
+  const uint8_t* b_scales;
+  const float* b_gs;
+  int64_t ldb;                 // elements
+  int b_mfma_layout;
+  int b_tile;                  // 2D blocks (32x32 / 16x16)
+  int64_t b_group_elems;       // elements between groups' matrices (N * ldb)
+  int64_t b_group_scales;      // scale bytes between groups
+  int64_t M, N, K;
+  uint16_t* c;
+  int64_t ldc;
+  int num_groups;
+  const int32_t* offsets;
+  const int32_t* row_index;
+};
+
+hipError_t launch_gemm(int path, bool b_transposed, const GemmArgs& a, hipStream_t st);
+
+}  // namespace mxq

@@ -1,0 +1,393 @@
+// NVFP4 quantizers for gfx950.
+//
+// NVFP4 = 16 E2M1 values with an E4M3 block scale under a second FP32 scale
+// ("Miles Blackwell RL Troca a Uniformidade BF16 por MXFP8 e NVFP4 Nativos",
+// section "O Suporte Miles Blackwell Agora Abrange Todo o Loop de RL").  Miles
+// computes the second scale per token online and fuses it into the activation
+// quantizer, which yields packed FP4, block scales and token scales in one op
+// (same page, section "Um Quantizador Compartilhado É o Verdadeiro
+// Mecanismo"); the NVIDIA pretraining recipe uses a per-tensor scale, 16x16
+// weight tiles, and stochastic rounding for gradients ("Train models faster
+// with JAX and MaxText using NVFP4 on NVIDIA Blackwell", section "NVFP4
+// pretraining recipe").
+//
+// Binary32 chain (each step one IEEE operation, RNE, subnormals kept, no FMA):
+//   S   = A / 2688                 (A = max|x| of the row or tensor)
+//   s_b = E4M3_RNE(a_b / (6 * S))  (0 when S == 0)
+//   r   = 1 / (s_b * S)            (once per block)
+//   q   = E2M1(x * r)              (RNE, or SR with a Philox4x32-10 draw)
+// Divisions are the correctly rounded IEEE ones (the build keeps HIP's
+// correctly rounded fp32 division and sqrt).
+//
+// Kernels:
+//   * nvfp4_row_kernel: one wave per row, the row held in registers, the
+//     token amax a wave reduction; 16-byte loads, two lanes per 16-block.
+//   * nvfp4_tile16_kernel: each lane owns 8 columns x 16 rows; two lanes form
+//     a 16x16 tile.
+//   * nvfp4_col_kernel: each lane owns 4 columns x 16 rows, each column one
+//     16x1 block, written into the transposed copy.
+//   * amax kernels for the per-tensor scale: an unsigned atomic max on the
+//     magnitude bits (exact and order-independent), then one thread turns A
+//     into S in place.
+
+#include "mxq_device.h"
+#include "mxq_kernels.h"
+
+namespace mxq {
+
+// Block scale and per-block reciprocal from the block amax (binary32 bits of
+// a BF16 magnitude widened) and S.
+struct BlockScale { uint32_t code; float r; };
+
+__device__ __forceinline__ BlockScale nv_block_scale(float a_b, float S) {
+  BlockScale bs;
+  if (!(S > 0.0f)) { bs.code = 0; bs.r = 0.0f; return bs; }
+  float six_s = 6.0f * S;
+  float t = a_b / six_s;
+  // saturating encode: with a caller-given S, t may exceed the E4M3 range
+  // (every value >= 448 rounds to 448; the hardware conversion would not
+  // saturate on its own)
+  t = t < 448.0f ? t : 448.0f;
+  bs.code = f32x2_to_e4m3(t, 0.0f) & 0xFFu;
+  float sb = e4m3_to_f32(bs.code);
+  float den = sb * S;
+  bs.r = bs.code ? 1.0f / den : 0.0f;
+  return bs;
+}
+
+// Encode the 8 BF16 values of one chunk with reciprocal r; returns 8 nibbles
+// (element 2j in the low nibble of byte j).  zero_block forces signed zeros.
+template <bool SR>
+__device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, bool zero_block, u32x4 draws) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t d[4] = {draws.x, draws.y, draws.z, draws.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+    float ya = a * r, yb = b * r;
+    if (zero_block) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
+    uint32_t qa, qb;
+    if (SR) {
+      qa = f32_to_e2m1_sr(ya, d[i] & 0xFFFFu);
+      qb = f32_to_e2m1_sr(yb, d[i] >> 16);
+    } else {
+      qa = f32_to_e2m1_rne(ya);
+      qb = f32_to_e2m1_rne(yb);
+    }
+    out |= (qa | (qb << 4)) << (8 * i);
+  }
+  return out;
+}
+
+// Max |x| of 8 BF16 values as the binary32 bit pattern of the magnitude
+// (integer max on magnitude bits: exact, and immune to denormal flushing).
+__device__ __forceinline__ uint32_t amax8_bits(uint4 v) {
+  uint32_t m = umax(umax(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                    umax(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
+  return m << 16;
+}
+
+// ------------------------------------------------------------ ROW (1x16)
+// gmode: 0 = per row (S computed here and stored), 1 = per tensor / given
+// (S read from gscale[0]).  One wave per row, CPT chunks of 8 per lane.
+template <int CPT, bool SR>
+__global__ __launch_bounds__(256) void nvfp4_row_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    float* __restrict__ gscales, int gmode, int mfma_layout,
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;                       // whole wave leaves together
+  const int64_t cpr = cols >> 3;
+  const uint16_t* xr = x + row * ld_x;
+  uint4 v[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    int64_t c = lane + 64 * k;
+    v[k] = c < cpr ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+  float S;
+  if (gmode == 0) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) mb = umax(mb, amax8_bits(v[k]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mb = umax(mb, lane_xor_u32(mb, o));
+    S = __uint_as_float(mb) / 2688.0f;
+    if (lane == 0) gscales[row] = S;
+  } else {
+    S = gscales[0];
+  }
+  const int64_t bpr = cols >> 4;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    int64_t c = lane + 64 * k;                   // chunk; block = c >> 1
+    uint32_t ab = amax8_bits(v[k]);
+    float a = __uint_as_float(umax(ab, lane_xor_u32(ab, 1)));
+    if (c < cpr) {
+      BlockScale bs = nv_block_scale(a, S);
+      u32x4 dr = {0, 0, 0, 0};
+      if (SR) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
+      uint32_t q = nv_encode8<SR>(v[k], bs.r, bs.code == 0, dr);
+      *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
+      if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)bs.code;
+    }
+  }
+}
+
+// Rows too long to keep in registers: two passes over the row (the second
+// read is served from cache).  One wave per row.
+template <bool SR>
+__global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    float* __restrict__ gscales, int gmode, int mfma_layout,
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t cpr = cols >> 3;
+  const uint16_t* xr = x + row * ld_x;
+  float S;
+  if (gmode == 0) {
+    uint32_t mb = 0;
+    for (int64_t c = lane; c < cpr; c += 64)
+      mb = umax(mb, amax8_bits(*reinterpret_cast<const uint4*>(xr + c * 8)));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mb = umax(mb, lane_xor_u32(mb, o));
+    S = __uint_as_float(mb) / 2688.0f;
+    if (lane == 0) gscales[row] = S;
+  } else {
+    S = gscales[0];
+  }
+  const int64_t bpr = cols >> 4;
+  for (int64_t c0 = 0; c0 < cpr; c0 += 64) {     // uniform trip count across the wave
+    int64_t c = c0 + lane;
+    uint4 v = c < cpr ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
+    uint32_t ab = amax8_bits(v);
+    float a = __uint_as_float(umax(ab, lane_xor_u32(ab, 1)));
+    if (c < cpr) {
+      BlockScale bs = nv_block_scale(a, S);
+      u32x4 dr = {0, 0, 0, 0};
+      if (SR) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
+      uint32_t q = nv_encode8<SR>(v, bs.r, bs.code == 0, dr);
+      *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
+      if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)bs.code;
+    }
+  }
+}
+
+// ------------------------------------------------------------ TILE (16x16)
+// Lane owns columns [8j, 8j+8) of a 16-row strip; lanes 2i, 2i+1 form tile i.
+template <bool SR>
+__global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    const float* __restrict__ gscales, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  const int64_t cpr = cols >> 3;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;   // chunk column
+  const int64_t r0 = (int64_t)blockIdx.y * 16;
+  const bool valid = j < cpr;
+  uint4 v[16];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = valid ? *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + j * 8) : make_uint4(0, 0, 0, 0);
+    mb = umax(mb, amax8_bits(v[i]));
+  }
+  float m = __uint_as_float(umax(mb, lane_xor_u32(mb, 1)));
+  if (!valid) return;
+  const float S = gscales[0];
+  BlockScale bs = nv_block_scale(m, S);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int64_t r = r0 + i;
+    u32x4 dr = {0, 0, 0, 0};
+    if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
+    uint32_t q = nv_encode8<SR>(v[i], bs.r, bs.code == 0, dr);
+    *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
+  }
+  if ((j & 1) == 0) bscales[(r0 >> 4) * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
+}
+
+// ------------------------------------------------------------ COL (16x1)
+// Lane owns columns [4j, 4j+4) of a 16-row strip; each column is one block of
+// the transposed copy ([cols, rows], 8 bytes per block).
+template <bool SR>
+__global__ __launch_bounds__(256) void nvfp4_col_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    const float* __restrict__ gscales, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  const int64_t q4 = cols >> 2;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 16;
+  if (j >= q4) return;
+  const float S = gscales[0];
+  uint2 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint2*>(x + (r0 + i) * ld_x + j * 4);
+  // column values: column cidx (0..3) of row i is half (cidx&1) of word (cidx>>1)
+  u32x4 dr[16];
+  if (SR) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + j * 4) >> 3, seed, stream_id, tensor_tag);
+  }
+  const int64_t bpr = rows >> 4;
+#pragma unroll
+  for (int cidx = 0; cidx < 4; ++cidx) {
+    uint32_t colw[8];                 // 16 values of this column, two per word
+    uint32_t rr16[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t wa = (cidx >> 1) ? v[2 * i].y : v[2 * i].x;
+      uint32_t wb = (cidx >> 1) ? v[2 * i + 1].y : v[2 * i + 1].x;
+      uint32_t ha = (cidx & 1) ? (wa >> 16) : (wa & 0xFFFFu);
+      uint32_t hb = (cidx & 1) ? (wb >> 16) : (wb & 0xFFFFu);
+      colw[i] = ha | (hb << 16);
+    }
+    if (SR) {
+      // element (r, 4j + cidx) has logical index idx = r*cols + 4j + cidx; its
+      // draw is half (idx & 1) of word ((idx & 7) >> 1) of block idx >> 3.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint64_t idx = (uint64_t)((r0 + i) * cols + j * 4 + cidx);
+        uint32_t wsel = (uint32_t)((idx & 7) >> 1);
+        uint32_t w = wsel == 0 ? dr[i].x : wsel == 1 ? dr[i].y : wsel == 2 ? dr[i].z : dr[i].w;
+        rr16[i] = (idx & 1) ? (w >> 16) : (w & 0xFFFFu);
+      }
+    }
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mb = umax(mb, bf16x2_absmax_bits(colw[i]));
+    BlockScale bs = nv_block_scale(__uint_as_float(mb << 16), S);
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float a = bf16_lo(colw[i]), b = bf16_hi(colw[i]);
+      float ya = a * bs.r, yb = b * bs.r;
+      if (bs.code == 0) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
+      uint32_t qa = SR ? f32_to_e2m1_sr(ya, rr16[2 * i]) : f32_to_e2m1_rne(ya);
+      uint32_t qb = SR ? f32_to_e2m1_sr(yb, rr16[2 * i + 1]) : f32_to_e2m1_rne(yb);
+      out[i >> 2] |= (qa | (qb << 4)) << (8 * (i & 3));
+    }
+    int64_t c = j * 4 + cidx;
+    *reinterpret_cast<uint2*>(codes + c * ld_codes + (r0 >> 1)) = make_uint2(out[0], out[1]);
+    bscales[c * bpr + (r0 >> 4)] = (uint8_t)bs.code;
+  }
+}
+
+// ------------------------------------------------------------ tensor amax
+__global__ void nv_zero_u32(uint32_t* p) { *p = 0u; }
+
+__global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                      int64_t cols, int64_t ld_x,
+                                                      uint32_t* __restrict__ out_bits) {
+  const int64_t cpr = cols >> 3;
+  const int64_t total = rows * cpr;
+  uint32_t m = 0;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * 256) {
+    int64_t r = id / cpr, c = id - r * cpr;
+    uint4 v = *reinterpret_cast<const uint4*>(x + r * ld_x + c * 8);
+    m = umax(m, umax(umax(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                     umax(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w))));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = umax(m, lane_xor_u32(m, o));
+  __shared__ uint32_t wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = umax(umax(wm[0], wm[1]), umax(wm[2], wm[3]));
+    atomicMax(out_bits, b << 16);     // binary32 bits of the BF16 magnitude
+  }
+}
+
+__global__ void nv_finalize_scale(float* g) {
+  float A = __uint_as_float(*reinterpret_cast<uint32_t*>(g));
+  g[0] = A / 2688.0f;
+}
+
+// ------------------------------------------------------------ launchers
+hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     float* gscale, hipStream_t st) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(gscale);
+  hipLaunchKernelGGL(nv_zero_u32, dim3(1), dim3(1), 0, st, bits);
+  int64_t total = rows * (cols / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld_x,
+                     bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_finalize(float* gscale, hipStream_t st) {
+  hipLaunchKernelGGL(nv_finalize_scale, dim3(1), dim3(1), 0, st, gscale);
+  return hipGetLastError();
+}
+
+template <bool SR>
+static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
+                               int gmode, bool mfma, uint64_t seed, uint32_t sid, uint32_t tag,
+                               hipStream_t st) {
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t cpr = cols / 8;
+#define MXQ_ROW(CPT)                                                                         \
+  hipLaunchKernelGGL((nvfp4_row_kernel<CPT, SR>), grid, block, 0, st, x, rows, cols, ld_x,   \
+                     codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag)
+  if (cpr <= 64) MXQ_ROW(1);
+  else if (cpr <= 128) MXQ_ROW(2);
+  else if (cpr <= 256) MXQ_ROW(4);
+  else if (cpr <= 512) MXQ_ROW(8);
+  else if (cpr <= 1024) MXQ_ROW(16);
+  else
+    hipLaunchKernelGGL((nvfp4_row_long_kernel<SR>), grid, block, 0, st, x, rows, cols, ld_x, codes,
+                       ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
+#undef MXQ_ROW
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
+                            int gmode, bool mfma, bool sr, uint64_t seed, uint32_t sid,
+                            uint32_t tag, hipStream_t st) {
+  return sr ? row_dispatch<true>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode,
+                                 mfma, seed, sid, tag, st)
+            : row_dispatch<false>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode,
+                                  mfma, seed, sid, tag, st);
+}
+
+hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
+                               const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                               uint32_t tag, hipStream_t st) {
+  dim3 grid((unsigned)((cols / 8 + 255) / 256), (unsigned)(rows / 16));
+  if (sr)
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+  else
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
+                            const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                            uint32_t tag, hipStream_t st) {
+  dim3 grid((unsigned)((cols / 4 + 255) / 256), (unsigned)(rows / 16));
+  if (sr)
+    hipLaunchKernelGGL((nvfp4_col_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+  else
+    hipLaunchKernelGGL((nvfp4_col_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mxq.h declares, and rejects invalid arguments on the host with the
+documented status before anything is launched (no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.util import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def _lib():
+    import microscaling_quantization_block_amd as m
+    if not os.path.exists(m.library_path):
+        pytest.skip("libmxq.so not built (run __graft_entry__.build())")
+    return m, m.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu",
+                 "mxq_status_str", "mxq_last_error", "mxq_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    _, L = _lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    _, L = _lib()
+    assert L.mxq_version() == 1
+    for s in range(6):
+        assert L.mxq_status_str(s)
+    assert b"unknown" in L.mxq_status_str(99)
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10008)
+
+
+def _err(L):
+    return L.mxq_last_error().decode()
+
+
+def test_mx_quantize_rejects_bad_arguments():
+    m, L = _lib()
+    B, Lay = m.Block, m.Layout
+    assert L.mx_quantize(None, 32, 64, 64, B.ROW, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 1
+    assert L.mx_quantize(FAKE, 32, 48, 48, B.ROW, Lay.LINEAR, FAKE, 48, FAKE, None, 0, None, None) == 2
+    assert "cols % 32" in _err(L)
+    assert L.mx_quantize(FAKE, 40, 64, 64, B.COL, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 2
+    assert L.mx_quantize(FAKE_ODD, 32, 64, 64, B.ROW, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 3
+    assert L.mx_quantize(FAKE, 32, 64, 64, B.TILE, Lay.MFMA, FAKE, 64, FAKE, None, 0, None, None) == 4
+    assert L.mx_quantize(FAKE, 32, 64, 64, B.DUAL, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 1
+    assert L.mx_quantize(FAKE, -1, 64, 64, B.ROW, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 1
+    assert L.mx_quantize(FAKE, 32, 64, 32, B.ROW, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 1
+    assert L.mx_quantize(FAKE, 32, 64, 64, 9, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 1
+    # empty input: nothing to do, nothing launched
+    assert L.mx_quantize(FAKE, 0, 64, 64, B.ROW, Lay.LINEAR, FAKE, 64, FAKE, None, 0, None, None) == 0
+
+
+def test_nvfp4_quantize_rejects_bad_arguments():
+    m, L = _lib()
+    B, G, R, Lay = m.Block, m.GScale, m.Round, m.Layout
+    call = lambda *a: L.nvfp4_quantize(*a)
+    assert call(FAKE, 16, 24, 24, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 2
+    assert call(FAKE, 16, 32, 32, B.COL, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 4
+    assert "per-row" in _err(L)
+    assert call(FAKE, 16, 32, 32, B.TILE, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 4
+    assert call(FAKE, 16, 32, 32, B.DUAL, G.PER_TENSOR, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 4
+    assert call(FAKE, 24, 32, 32, B.TILE, G.PER_TENSOR, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 2
+    assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 20, FAKE, FAKE, None) == 3
+    assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, None, None) == 1
+    assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, 7, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 1
+
+
+def test_mx_gemm_rejects_bad_arguments():
+    m, L = _lib()
+    F, B, G = m.Format, m.Block, m.GScale
+    Op = m._Operand
+
+    def op(fmt, block=B.ROW, gs=G.NONE, ld=64, transposed=0, scales=FAKE.value, gsc=FAKE.value):
+        return Op(fmt, FAKE.value, scales, gsc, block, gs, 0, ld, transposed)
+
+    def gemm(a, b, M=32, N=32, K=64):
+        return L.mx_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, M, FAKE, N, 0, None, None, None)
+
+    assert gemm(op(F.MXFP8), op(F.NVFP4, gs=G.PER_TENSOR)) == 4          # mixed formats
+    assert "formats differ" in _err(L)
+    assert gemm(op(F.MXFP8), op(F.MXFP8), K=48) == 2                    # K % 32
+    assert gemm(op(F.NVFP4, gs=G.PER_ROW), op(F.NVFP4, gs=G.PER_ROW)) == 4   # per-row S on B
+    assert gemm(op(F.MXFP8), op(F.MXFP8, transposed=1)) == 4            # transposed needs TILE
+    assert gemm(op(F.MXFP8, transposed=1), op(F.MXFP8)) == 4            # A transposed
+    assert gemm(op(F.MXFP8, block=B.TILE), op(F.MXFP8)) == 4            # tile A
+    assert gemm(op(F.MXFP8), op(F.MXFP8, scales=None)) == 1
+    assert gemm(op(F.NVFP4, gs=G.PER_ROW, gsc=None), op(F.NVFP4, gs=G.PER_TENSOR)) == 1
+    assert gemm(op(F.MXFP8, ld=40), op(F.MXFP8)) == 3
+    assert gemm(op(F.BF16, block=B.NONE), op(F.BF16, block=B.NONE, ld=36)) == 3
+    assert gemm(op(F.MXFP8), op(F.MXFP8, block=B.TILE, transposed=1), N=48) == 2
+    # empty GEMM: no launch
+    assert gemm(op(F.MXFP8), op(F.MXFP8), M=0) == 0
+
+
+def test_dequantize_and_swiglu_reject_bad_arguments():
+    m, L = _lib()
+    F, B, G, Lay = m.Format, m.Block, m.GScale, m.Layout
+    assert L.mx_dequantize(F.MXFP8, FAKE, 64, FAKE, None, 32, 64, B.COL, G.NONE, Lay.LINEAR, FAKE, 64, None) == 4
+    assert L.mx_dequantize(F.NVFP4, FAKE, 32, FAKE, None, 32, 64, B.ROW, G.PER_ROW, Lay.LINEAR, FAKE, 64, None) == 1
+    assert L.mx_dequantize(F.MXFP8, FAKE, 64, FAKE, None, 32, 64, B.ROW, G.PER_ROW, Lay.LINEAR, FAKE, 64, None) == 4
+    assert L.mx_dequantize(F.BF16, FAKE, 64, FAKE, None, 32, 64, B.ROW, G.NONE, Lay.LINEAR, FAKE, 64, None) == 1
+    assert L.mx_swiglu(FAKE, 4, 12, 24, FAKE, 12, None) == 2
+    assert L.mx_swiglu(FAKE_ODD, 4, 16, 32, FAKE, 16, None) == 3

@@ -1,0 +1,279 @@
+"""GPU parity of the block-scaled GEMMs against the oracle's
+dequantize-then-matmul: relative Frobenius error <= 1e-2 against float64, and
+the element-wise bound |C - C32| <= 2^-8 |C32| + K 2^-23 (|A| |B|) against the
+binary32 path; bit-exact equality where every product and sum is exact (unit
+scales, small codes).  Operands are quantized by the GPU; the oracle
+dequantizes the GPU's own codes (already checked byte-identical to the
+oracle's in the quantizer tests) and also requantizes from the BF16 inputs to
+confirm they are the same bytes."""
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import mxfp8 as OM
+from oracle import nvfp4 as ON
+import synth
+from tests.util import requires_gpu, to_dev_bf16, from_dev_bf16, to_np, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def mxq():
+    import microscaling_quantization_block_amd as m
+    return m
+
+
+def _bf16(shape, std, seed):
+    return F.bf16_rne(np.random.default_rng(seed).standard_normal(shape) * std)
+
+
+def _assert_gemm(c_dev, a64, b64, a32, b32, rtol=1e-2):
+    c = from_dev_bf16(c_dev)
+    frob, worst, ok = G.check(c, a64, b64, a32, b32, rtol_frob=rtol)
+    assert ok, f"frobenius {frob:.3e}, worst element ratio {worst:.3f}"
+    return frob, worst
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def _mx_row(m, bits):
+    c, s = m.mx_quantize(to_dev_bf16(bits))
+    return c, s
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (200, 96, 128), (33, 160, 96), (512, 384, 1024)])
+def test_mxfp8_fprop(M, N, K):
+    m = mxq()
+    x = _bf16((M, K), 1.0, 1)
+    w = _bf16((N, K), 0.02, 2)
+    say(f"mxfp8 FPROP {M}x{N}x{K}")
+    cx, sx = _mx_row(m, x)
+    cw, sw = _mx_row(m, w)
+    A = m.Operand(m.Format.MXFP8, cx, sx)
+    B = m.Operand(m.Format.MXFP8, cw, sw)
+    out = m.mx_gemm(A, B, M, N, K)
+    a64 = OM.dequantize_f64(to_np(cx), to_np(sx))
+    b64 = OM.dequantize_f64(to_np(cw), to_np(sw))
+    _assert_gemm(out, a64, b64, a64, b64)
+
+
+def test_mxfp8_config1_gemm():
+    m = mxq()
+    d = synth.config1()
+    say("mxfp8 config-1 GEMM 256x512x256")
+    cx, sx = _mx_row(m, d["x"])
+    cw, sw = _mx_row(m, d["w"])
+    out = m.mx_gemm(m.Operand(m.Format.MXFP8, cx, sx), m.Operand(m.Format.MXFP8, cw, sw), 256, 256, 512)
+    rc, rs = OM.quantize_rowwise(F.bf16_bits_to_f64(d["x"]))
+    assert np.array_equal(to_np(cx), rc)
+    a64 = OM.dequantize_f64(to_np(cx), to_np(sx))
+    b64 = OM.dequantize_f64(to_np(cw), to_np(sw))
+    _assert_gemm(out, a64, b64, a64, b64)
+
+
+def test_mxfp8_unit_scale_exact():
+    """Codes restricted to small integers with E8M0 scale 1: every product and
+    partial sum is exact in binary32, so the BF16 output must equal the BF16
+    rounding of the exact result bit for bit."""
+    m = mxq()
+    import torch
+    rs = np.random.default_rng(3)
+    ints = np.array([v for v in range(-16, 17)], dtype=np.float64)
+    M, N, K = 96, 64, 256
+    a = rs.choice(ints, (M, K))
+    b = rs.choice(ints, (N, K))
+    ca = torch.from_numpy(F.encode_e4m3_rne(a)).cuda()
+    cb = torch.from_numpy(F.encode_e4m3_rne(b)).cuda()
+    one = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda")
+    oneb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda")
+    say("mxfp8 unit-scale exact 96x64x256")
+    out = m.mx_gemm(m.Operand(m.Format.MXFP8, ca, one), m.Operand(m.Format.MXFP8, cb, oneb), M, N, K)
+    assert np.array_equal(from_dev_bf16(out), F.bf16_rne(a @ b.T))
+
+
+def test_mxfp8_dgrad_transposed_32x32_weight_and_wgrad():
+    """DGRAD dX = dY W with W's 32x32-tile copy read transposed; WGRAD
+    dW = dY^T X with both operands' columnwise copies."""
+    m = mxq()
+    T, H, I = 256, 192, 160
+    x = _bf16((T, H), 1.0, 4)
+    w = _bf16((I, H), 0.02, 5)           # W [N_f=I, K_f=H]
+    dy = _bf16((T, I), 1e-3, 6)
+    say("mxfp8 DGRAD (transposed 32x32 W) and WGRAD")
+    cw, sw = m.mx_quantize(to_dev_bf16(w), block=m.Block.TILE)
+    cdy, sdy, cdyc, sdyc = m.mx_quantize(to_dev_bf16(dy), block=m.Block.DUAL)
+    cx, sx, cxc, sxc = m.mx_quantize(to_dev_bf16(x), block=m.Block.DUAL)
+    # DGRAD: C[T, H] = sum_i dY[t, i] W[i, h]  (B[n=h, k=i] = W[i, h], stored [K, N])
+    B = m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE, transposed=True)
+    dx = m.mx_gemm(m.Operand(m.Format.MXFP8, cdy, sdy), B, T, H, I)
+    a64 = OM.dequantize_f64(to_np(cdy), to_np(sdy))
+    w64 = OM.dequantize_f64(to_np(cw), to_np(sw), "32x32")
+    _assert_gemm(dx, a64, w64.T.copy(), a64, w64.T.copy())
+    # the same tile copy read untransposed serves FPROP
+    y = m.mx_gemm(m.Operand(m.Format.MXFP8, cx, sx),
+                  m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE), T, I, H)
+    x64 = OM.dequantize_f64(to_np(cx), to_np(sx))
+    _assert_gemm(y, x64, w64, x64, w64)
+    # WGRAD: C[I, H] = sum_t dY[t, i] X[t, h]: A = dY colwise [I, T], B = X colwise [H, T]
+    dw = m.mx_gemm(m.Operand(m.Format.MXFP8, cdyc, sdyc), m.Operand(m.Format.MXFP8, cxc, sxc), I, H, T)
+    ga = OM.dequantize_f64(to_np(cdyc), to_np(sdyc))
+    gb = OM.dequantize_f64(to_np(cxc), to_np(sxc))
+    _assert_gemm(dw, ga, gb, ga, gb)
+
+
+def test_mxfp8_mfma_layout_operands():
+    m = mxq()
+    M, N, K = 128, 96, 512
+    x = _bf16((M, K), 1.0, 7)
+    w = _bf16((N if N % 32 == 0 else 128, K), 0.02, 8)
+    say("mxfp8 GEMM with MFMA-layout scales")
+    cx, sx = m.mx_quantize(to_dev_bf16(x), layout=m.Layout.MFMA)
+    cw, sw = m.mx_quantize(to_dev_bf16(w), layout=m.Layout.MFMA)
+    out = m.mx_gemm(m.Operand(m.Format.MXFP8, cx, sx, layout=m.Layout.MFMA),
+                    m.Operand(m.Format.MXFP8, cw, sw, layout=m.Layout.MFMA), M, N, K)
+    rcx, rsx = OM.quantize_rowwise(F.bf16_bits_to_f64(x))
+    rcw, rsw = OM.quantize_rowwise(F.bf16_bits_to_f64(w))
+    a64, b64 = OM.dequantize_f64(rcx, rsx), OM.dequantize_f64(rcw, rsw)
+    _assert_gemm(out, a64, b64, a64, b64)
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def _nv_ops(m, x, w, w_tile=True):
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+    if w_tile:
+        cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(w), block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    else:
+        cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(w), gs=m.GScale.PER_TENSOR)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE if w_tile else m.Block.ROW,
+                  gs=m.GScale.PER_TENSOR)
+    a64 = ON.dequantize_f64(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+    a32 = ON.dequantize_f32(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+    bl = "16x16" if w_tile else "1x16"
+    b64 = ON.dequantize_f64(to_np(cw), to_np(sw), to_np(Sw), bl, "per_tensor")
+    b32 = ON.dequantize_f32(to_np(cw), to_np(sw), to_np(Sw), bl, "per_tensor")
+    return A, B, (a64, a32, b64, b32), (cw, sw, Sw)
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(256, 128, 512, True), (100, 48, 96, True), (64, 80, 256, False)])
+def test_nvfp4_fprop(M, N, K, tile):
+    m = mxq()
+    x = F.bf16_rne(np.random.default_rng(9).standard_normal((M, K)) *
+                   np.exp(np.random.default_rng(10).standard_normal((M, 1))))
+    w = _bf16((N, K), 0.02, 11)
+    say(f"nvfp4 FPROP {M}x{N}x{K} tile={tile}")
+    A, B, (a64, a32, b64, b32), _ = _nv_ops(m, x, w, tile)
+    out = m.mx_gemm(A, B, M, N, K)
+    _assert_gemm(out, a64, b64, a32, b32)
+
+
+def test_nvfp4_config2_fprop_full_size():
+    m = mxq()
+    d = synth.config2()
+    say("nvfp4 config-2 FPROP 4096x768x2048")
+    A, B, (a64, a32, b64, b32), _ = _nv_ops(m, d["x"], d["w"], True)
+    out = m.mx_gemm(A, B, 4096, 768, 2048)
+    frob, worst = _assert_gemm(out, a64, b64, a32, b32)
+    say(f"config-2 FPROP frobenius {frob:.3e}, worst {worst:.3f}")
+
+
+def test_nvfp4_unit_scale_exact():
+    m = mxq()
+    import torch
+    rs = np.random.default_rng(12)
+    M, N, K = 64, 96, 512
+    ca = rs.integers(0, 16, (M, K)).astype(np.uint8)
+    cb = rs.integers(0, 16, (N, K)).astype(np.uint8)
+    pa = torch.from_numpy(ON.pack_nibbles(ca)).cuda()
+    pb = torch.from_numpy(ON.pack_nibbles(cb)).cuda()
+    one_a = torch.full((M, K // 16), 0x38, dtype=torch.uint8, device="cuda")   # E4M3 1.0
+    one_b = torch.full((N, K // 16), 0x38, dtype=torch.uint8, device="cuda")
+    Sa = torch.ones(M, dtype=torch.float32, device="cuda")
+    Sb = torch.ones(1, dtype=torch.float32, device="cuda")
+    say("nvfp4 unit-scale exact 64x96x512")
+    out = m.mx_gemm(m.Operand(m.Format.NVFP4, pa, one_a, Sa, gs=m.GScale.PER_ROW),
+                    m.Operand(m.Format.NVFP4, pb, one_b, Sb, gs=m.GScale.PER_TENSOR), M, N, K)
+    exact = F.e2m1_value(ca) @ F.e2m1_value(cb).T
+    assert np.array_equal(from_dev_bf16(out), F.bf16_rne(exact))
+
+
+def test_nvfp4_dgrad_transposed_and_wgrad_with_sr():
+    m = mxq()
+    T, H, I = 256, 128, 96
+    x = _bf16((T, H), 1.0, 13)
+    w = _bf16((I, H), 0.02, 14)
+    dy = _bf16((T, I), 1e-3, 15)
+    say("nvfp4 DGRAD (transposed 16x16 W, SR dY) and WGRAD (columnwise copies)")
+    cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(w), block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    cdy, sdy, Sdy = m.nvfp4_quantize(to_dev_bf16(dy), gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=0)
+    dx = m.mx_gemm(m.Operand(m.Format.NVFP4, cdy, sdy, Sdy, gs=m.GScale.PER_ROW),
+                   m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
+                             transposed=True), T, H, I)
+    a64 = ON.dequantize_f64(to_np(cdy), to_np(sdy), to_np(Sdy), "1x16", "per_row")
+    a32 = ON.dequantize_f32(to_np(cdy), to_np(sdy), to_np(Sdy), "1x16", "per_row")
+    w64 = ON.dequantize_f64(to_np(cw), to_np(sw), to_np(Sw), "16x16", "per_tensor")
+    w32 = ON.dequantize_f32(to_np(cw), to_np(sw), to_np(Sw), "16x16", "per_tensor")
+    _assert_gemm(dx, a64, w64.T.copy(), a32, w32.T.copy())
+    # WGRAD with columnwise copies (per-tensor S; SR for dY with stream 1)
+    cdc, sdc, Sdc = m.nvfp4_quantize(to_dev_bf16(dy), block=m.Block.COL, gs=m.GScale.PER_TENSOR,
+                                     rnd=m.Round.SR, seed=0, stream_id=1)
+    cxc, sxc, Sxc = m.nvfp4_quantize(to_dev_bf16(x), block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    dw = m.mx_gemm(m.Operand(m.Format.NVFP4, cdc, sdc, Sdc, gs=m.GScale.PER_TENSOR),
+                   m.Operand(m.Format.NVFP4, cxc, sxc, Sxc, gs=m.GScale.PER_TENSOR), I, H, T)
+    ga64 = ON.dequantize_f64(to_np(cdc), to_np(sdc), to_np(Sdc), "1x16", "per_tensor")
+    ga32 = ON.dequantize_f32(to_np(cdc), to_np(sdc), to_np(Sdc), "1x16", "per_tensor")
+    gb64 = ON.dequantize_f64(to_np(cxc), to_np(sxc), to_np(Sxc), "1x16", "per_tensor")
+    gb32 = ON.dequantize_f32(to_np(cxc), to_np(sxc), to_np(Sxc), "1x16", "per_tensor")
+    _assert_gemm(dw, ga64, gb64, ga32, gb32)
+
+
+# ------------------------------------------------------------------ BF16 (dequantized backward)
+
+def test_dequantized_backward_dgrad_config2():
+    """dX = dY * DQ(Q(W)): the BF16 operand is the library's own dequantized
+    16x16 weight (bit-equal to the oracle's), read transposed."""
+    m = mxq()
+    d = synth.config2()
+    say("dequantized-backward DGRAD config-2 4096x2048x768")
+    cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(d["w"]), block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    wdq = m.mx_dequantize(m.Format.NVFP4, cw, sw, 768, 2048, block=m.Block.TILE, gscales=Sw,
+                          gs=m.GScale.PER_TENSOR)
+    ref_dq = ON.dequantize_bf16(to_np(cw), to_np(sw), to_np(Sw), "16x16", "per_tensor")
+    assert np.array_equal(from_dev_bf16(wdq), ref_dq)
+    dyd = to_dev_bf16(d["dy"])
+    dx = m.mx_gemm(m.Operand(m.Format.BF16, dyd, block=m.Block.NONE),
+                   m.Operand(m.Format.BF16, wdq, block=m.Block.NONE, transposed=True), 4096, 2048, 768)
+    a = F.bf16_bits_to_f64(d["dy"])
+    b = F.bf16_bits_to_f64(ref_dq).T.copy()
+    _assert_gemm(dx, a, b, a, b)
+
+
+def test_bf16_gemm_ragged_both_orientations():
+    m = mxq()
+    M, N, K = 70, 56, 72
+    a = _bf16((M, K), 1.0, 16)
+    b = _bf16((N, K), 1.0, 17)
+    say("bf16 GEMM ragged")
+    out = m.mx_gemm(m.Operand(m.Format.BF16, to_dev_bf16(a), block=m.Block.NONE),
+                    m.Operand(m.Format.BF16, to_dev_bf16(b), block=m.Block.NONE), M, N, K)
+    av, bv = F.bf16_bits_to_f64(a), F.bf16_bits_to_f64(b)
+    _assert_gemm(out, av, bv, av, bv)
+    bt = np.ascontiguousarray(b.T)                 # stored [K, N]
+    out2 = m.mx_gemm(m.Operand(m.Format.BF16, to_dev_bf16(a), block=m.Block.NONE),
+                     m.Operand(m.Format.BF16, to_dev_bf16(bt), block=m.Block.NONE, transposed=True),
+                     M, N, K)
+    assert np.array_equal(from_dev_bf16(out2), from_dev_bf16(out))
+
+
+def test_gemm_is_deterministic():
+    m = mxq()
+    x = _bf16((512, 1024), 1.0, 18)
+    w = _bf16((256, 1024), 0.02, 19)
+    say("GEMM determinism")
+    A, B, _, _ = _nv_ops(m, x, w, True)
+    o1 = from_dev_bf16(m.mx_gemm(A, B, 512, 256, 1024))
+    o2 = from_dev_bf16(m.mx_gemm(A, B, 512, 256, 1024))
+    assert np.array_equal(o1, o2)
