@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 linear-layer hot path on one MI355X.
+
+One step = one pass over one batch of the NVFP4 workload with 4096 tokens,
+hidden 2048 and 768 outputs (the second configuration of the benchmark set):
+  1. per-token NVFP4 quantization of the activations X [4096, 2048]
+  2. 16x16 NVFP4 quantization of the weight W [768, 2048] (per-tensor scale:
+     an amax pass, then the quantize pass)
+  3. FPROP  Y [4096, 768]  = Q(X) Q(W)^T       (NVFP4 x NVFP4, BF16 out)
+  4. DQ(Q(W)) -> BF16 [768, 2048]              (dequantized backward operand)
+  5. DGRAD dX [4096, 2048] = dY DQ(Q(W))       (BF16, weight read transposed)
+Inputs are seeded synthetic tensors (the pages' models and datasets stand in
+as shapes and distributions only), resident in HBM before timing; ten
+buffer sets (> 512 MB in total) rotate so reads come from HBM rather than
+the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout.  `value` is the step's GEMM throughput: the
+two GEMMs' algorithmic flops (2*M*N*K each) over the whole step's time,
+quantization and dequantization included.  Per-kernel times, GB/s, TFLOP/s
+and fractions of peak are in "kernels"; "roofline" describes the kernel with
+the largest share of the step.  The CPU oracle, timed on a bounded sample of
+the same step, is reported as "cpu_baseline".
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M, K, N = 4096, 2048, 768
+PEAK_HBM_GBPS = 8000.0
+PEAK_F16_TFLOPS = 2500.0     # dense FP16/BF16 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # dense FP4 MFMA (context for the NVFP4 GEMM)
+SETS = 10
+
+# algorithmic bytes / flops per launch
+BYTES_QX = M * K * 2 + M * K // 2 + M * (K // 16) + M * 4
+BYTES_QW = 2 * N * K * 2 + N * K // 2 + (N // 16) * (K // 16) + 4
+BYTES_DQW = N * K // 2 + (N // 16) * (K // 16) + 4 + N * K * 2
+FLOPS_FPROP = 2 * M * N * K
+FLOPS_DGRAD = 2 * M * K * N
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_sets(m, torch, data):
+    import numpy as np
+    dev = "cuda"
+
+    def bf(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, w0, dy0 = bf(data["x"]), bf(data["w"]), bf(data["dy"])
+    sets = []
+    for _ in range(SETS):
+        s = dict(x=x0.clone(), w=w0.clone(), dy=dy0.clone())
+        s["cx"] = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        s["sx"] = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        s["Sx"] = torch.empty(M, dtype=torch.float32, device=dev)
+        s["cw"] = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        s["sw"] = torch.empty((N // 16, K // 16), dtype=torch.uint8, device=dev)
+        s["Sw"] = torch.empty(1, dtype=torch.float32, device=dev)
+        s["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        s["wdq"] = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        s["dx"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+    return sets
+
+
+def step(m, s, ev=None):
+    """The five stages; ev (list of 6 events) brackets each stage if given."""
+    def mark(i):
+        if ev is not None:
+            ev[i].record()
+    mark(0)
+    m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
+    mark(1)
+    m.nvfp4_quantize(s["w"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=s["cw"],
+                     block_scales=s["sw"], gscales=s["Sw"])
+    mark(2)
+    m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
+              m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
+                        gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
+    mark(3)
+    m.mx_dequantize(m.Format.NVFP4, s["cw"], s["sw"], N, K, block=m.Block.TILE, gscales=s["Sw"],
+                    gs=m.GScale.PER_TENSOR, out=s["wdq"])
+    mark(4)
+    m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
+              m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
+              out=s["dx"])
+    mark(5)
+
+
+def cpu_baseline(data, min_seconds):
+    """The oracle, as it stands, on the same step: the full step (all tokens)
+    repeated until at least `min_seconds` of CPU time have passed; the sample
+    is bounded by that time."""
+    import numpy as np
+    from oracle import formats as F, nvfp4 as ON, gemm as G
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = len(os.sched_getaffinity(0))
+    xv = F.bf16_bits_to_f64(data["x"])
+    wv = F.bf16_bits_to_f64(data["w"])
+    dyv = F.bf16_bits_to_f64(data["dy"])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        wc, wsb, wS = ON.quantize_tile16(wv)
+        w64 = ON.dequantize_f64(wc, wsb, wS, "16x16", "per_tensor")
+        wdq = ON.dequantize_bf16(wc, wsb, wS, "16x16", "per_tensor")
+        xc, xsb, xS = ON.quantize_rowwise(xv, "per_row")
+        x64 = ON.dequantize_f64(xc, xsb, xS, "1x16", "per_row")
+        y = F.bf16_rne(G.gemm_f64(x64, w64))
+        dx = F.bf16_rne(G.gemm_f64(dyv, F.bf16_bits_to_f64(wdq).T.copy()))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    t_step = el / reps
+    assert y.shape == (M, N) and dx.shape == (M, K)
+    return dict(value=(FLOPS_FPROP + FLOPS_DGRAD) / t_step / 1e12, unit="TFLOP/s",
+                cores=int(blas_threads), kind="oracle",
+                sample=(f"the full step ({M} tokens: Q(X), 16x16 Q(W), DQ(W), FPROP and DGRAD "
+                        f"as float64 dequantize-then-matmul) repeated {reps} times in {el:.1f} s; "
+                        f"quantizers single-threaded NumPy, matmuls on {blas_threads} BLAS threads"),
+                seconds_per_step=round(t_step, 3))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time bound for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(the quantizers shard by rows with no exchange; see the design notes). "
+              f"Asked for --gpus {args.gpus} (WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import microscaling_quantization_block_amd as m
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    m.lib()
+    log("generating synthetic inputs (seeded)")
+    data = synth.config2()
+    sets = make_sets(m, torch, data)
+    torch.cuda.synchronize()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(m, sets[i % SETS])
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(m, sets[i % SETS], events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    names = ["quantize_x_nvfp4_1x16_per_token", "quantize_w_nvfp4_16x16_per_tensor",
+             "gemm_fprop_nvfp4", "dequantize_w_nvfp4", "gemm_dgrad_bf16_dequantized"]
+    stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(5)]
+    kernels = {}
+    for j, nm in enumerate(names):
+        us = stage_ms[j] * 1e3
+        d = {"us": round(us, 2)}
+        if j in (0, 1, 3):
+            b = [BYTES_QX, BYTES_QW, None, BYTES_DQW][j]
+            gbps = b / (us * 1e-6) / 1e9
+            d.update(bytes=b, GBps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
+        else:
+            f = FLOPS_FPROP if j == 2 else FLOPS_DGRAD
+            tf = f / (us * 1e-6) / 1e12
+            d.update(flops=f, TFLOPs=round(tf, 1), frac_mfma=round(tf / PEAK_F16_TFLOPS, 4))
+            if j == 2:
+                d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
+        kernels[nm] = d
+    dom = max(range(5), key=lambda j: stage_ms[j])
+    dk = kernels[names[dom]]
+    if "TFLOPs" in dk:
+        roofline = dict(kernel=names[dom], bound="mfma", achieved=dk["TFLOPs"], peak=PEAK_F16_TFLOPS,
+                        unit="TFLOP/s", frac=dk["frac_mfma"], traffic=None)
+    else:
+        roofline = dict(kernel=names[dom], bound="hbm", achieved=dk["GBps"], peak=PEAK_HBM_GBPS,
+                        unit="GB/s", frac=dk["frac_hbm"], traffic=None)
+    value = (FLOPS_FPROP + FLOPS_DGRAD) / (ms_step * 1e-3) / 1e12
+    qbytes = BYTES_QX + BYTES_QW + BYTES_DQW
+    qus = (stage_ms[0] + stage_ms[1] + stage_ms[3]) * 1e3
+    out = {
+        "metric": "MX/NVFP4 quantize GB/s + block-scaled GEMM TFLOP/s (% of gfx950 peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1/e4m3/fp32) -> f16 MFMA, f32 accumulate; bf16 MFMA for DGRAD",
+        "data": "synthetic",
+        "config": {"workload": "nvfp4_linear_tokens4096_hidden2048_out768",
+                   "stages": "per-token Q(X) 4096x2048, 16x16 Q(W) 768x2048, FPROP 4096x768x2048, "
+                             "DQ(W), dequantized-backward DGRAD 4096x2048x768",
+                   "tokens": M, "hidden": K, "out_features": N, "buffer_sets": SETS},
+        "quantize_GBps": round(qbytes / (qus * 1e-6) / 1e9, 1),
+        "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[4]) * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
