@@ -271,6 +271,15 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   s = check_operand("B", b, true, N, K, N);
   if (s != MXQ_OK) return s;
   if (a->fmt != MXQ_FMT_BF16 && a->block != MXQ_BLOCK_ROW) return fail(MXQ_EUNSUPPORTED, "mx_gemm: A must be row-blocked");
+  // the kernels address each operand with 32-bit offsets
+  {
+    auto row_bytes = [](const mxq_operand* o) {
+      return o->fmt == MXQ_FMT_NVFP4 ? o->ld / 2 : o->fmt == MXQ_FMT_BF16 ? o->ld * 2 : o->ld;
+    };
+    const int64_t lim = (int64_t)1 << 31;
+    if (a_rows * row_bytes(a) >= lim || (b->transposed ? K : N) * row_bytes(b) >= lim)
+      return fail(MXQ_EUNSUPPORTED, "mx_gemm: an operand (one group of B) must be smaller than 2 GiB");
+  }
 
   mxq::GemmArgs g = {};
   g.a = static_cast<const uint8_t*>(a->data);
@@ -291,6 +300,7 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   g.M = M;
   g.N = N;
   g.K = K;
+  g.a_rows = a_rows;
   g.c = c;
   g.ldc = ldc;
   g.num_groups = num_groups;

@@ -59,6 +59,7 @@ struct GemmArgs {
   int64_t b_group_elems;       // elements between groups' matrices (N * ldb)
   int64_t b_group_scales;      // scale bytes between groups
   int64_t M, N, K;
+  int64_t a_rows;              // rows stored in A (the gather index points into them)
   uint16_t* c;
   int64_t ldc;
   int num_groups;

@@ -277,3 +277,50 @@ def test_gemm_is_deterministic():
     o1 = from_dev_bf16(m.mx_gemm(A, B, 512, 256, 1024))
     o2 = from_dev_bf16(m.mx_gemm(A, B, 512, 256, 1024))
     assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
+@pytest.mark.parametrize("bt", [False, True])
+def test_gemm_large_tile_variants(path, bt):
+    """M = N = 4096 selects the largest tiles (256x256, or 256x128 for MXFP8);
+    checked on 256 sampled rows spread over every m-tile, all columns."""
+    m = mxq()
+    M, N, K = 4096, 4096, 256
+    x = _bf16((M, K), 1.0, 40)
+    w = _bf16((N, K), 0.02, 41)
+    wt = np.ascontiguousarray(w.T)                   # stored [K, N] for the transposed case
+    say(f"large-tile GEMM {path} bt={bt} {M}x{N}x{K}")
+    rows = np.sort(np.random.default_rng(42).choice(M, 256, replace=False))
+    if path == "mxfp8":
+        cx, sx = m.mx_quantize(to_dev_bf16(x))
+        a64 = OM.dequantize_f64(to_np(cx), to_np(sx))
+        A = m.Operand(m.Format.MXFP8, cx, sx)
+        if bt:
+            cw, sw = m.mx_quantize(to_dev_bf16(wt), block=m.Block.TILE)
+            B = m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE, transposed=True)
+            b64 = OM.dequantize_f64(to_np(cw), to_np(sw), "32x32").T.copy()
+        else:
+            cw, sw = m.mx_quantize(to_dev_bf16(w))
+            B = m.Operand(m.Format.MXFP8, cw, sw)
+            b64 = OM.dequantize_f64(to_np(cw), to_np(sw))
+        a32, b32 = a64, b64
+    elif path == "nvfp4":
+        cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+        A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+        a64 = ON.dequantize_f64(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+        a32 = ON.dequantize_f32(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+        src = wt if bt else w
+        cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(src), block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+        B = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=bt)
+        b64 = ON.dequantize_f64(to_np(cw), to_np(sw), to_np(Sw), "16x16", "per_tensor")
+        b32 = ON.dequantize_f32(to_np(cw), to_np(sw), to_np(Sw), "16x16", "per_tensor")
+        if bt:
+            b64, b32 = b64.T.copy(), b32.T.copy()
+    else:
+        A = m.Operand(m.Format.BF16, to_dev_bf16(x), block=m.Block.NONE)
+        B = m.Operand(m.Format.BF16, to_dev_bf16(wt if bt else w), block=m.Block.NONE, transposed=bt)
+        a64 = a32 = F.bf16_bits_to_f64(x)
+        b64 = b32 = F.bf16_bits_to_f64(w)
+    out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
+    frob, worst, ok = G.check(out[rows], a64[rows], b64, a32[rows], b32)
+    assert ok, f"frobenius {frob:.3e}, worst {worst:.3f}"
