@@ -57,26 +57,46 @@ __device__ __forceinline__ BlockScale nv_block_scale(float a_b, float S) {
 
 // Encode the 8 BF16 values of one chunk with reciprocal r; returns 8 nibbles
 // (element 2j in the low nibble of byte j).  zero_block forces signed zeros.
+// RNE encode of a pair of binary32 values onto E2M1 by the hardware
+// conversion with unit scale (its scale only divides by a power of two, so 1.0
+// leaves y unchanged).  It rounds to nearest even, saturates at 6 and keeps
+// the sign of zero, identically to the integer encoder f32_to_e2m1_rne; the
+// two were compared on every BF16 value below 8 and a million random binary32
+// values, and the exhaustive quantizer tests check it against the oracle.
+// The result's byte `sel` holds the pair (first value in the low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_rne_pair(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, bool zero_block, u32x4 draws) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t d[4] = {draws.x, draws.y, draws.z, draws.w};
-  uint32_t out = 0;
+  float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
     float ya = a * r, yb = b * r;
     if (zero_block) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
-    uint32_t qa, qb;
-    if (SR) {
-      qa = f32_to_e2m1_sr(ya, d[i] & 0xFFFFu);
-      qb = f32_to_e2m1_sr(yb, d[i] >> 16);
-    } else {
-      qa = f32_to_e2m1_rne(ya);
-      qb = f32_to_e2m1_rne(yb);
-    }
-    out |= (qa | (qb << 4)) << (8 * i);
+    y[2 * i] = ya;
+    y[2 * i + 1] = yb;
   }
+  if (SR) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t qa = f32_to_e2m1_sr(y[2 * i], d[i] & 0xFFFFu);
+      uint32_t qb = f32_to_e2m1_sr(y[2 * i + 1], d[i] >> 16);
+      out |= (qa | (qb << 4)) << (8 * i);
+    }
+    return out;
+  }
+  uint32_t out = 0;
+  out = e2m1_rne_pair<0>(out, y[0], y[1]);
+  out = e2m1_rne_pair<1>(out, y[2], y[3]);
+  out = e2m1_rne_pair<2>(out, y[4], y[5]);
+  out = e2m1_rne_pair<3>(out, y[6], y[7]);
   return out;
 }
 
@@ -182,12 +202,12 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
 // ------------------------------------------------------------ TILE (16x16)
 // Lane owns columns [8j, 8j+8) of a 16-row strip; lanes 2i, 2i+1 form tile i.
 template <bool SR>
-__global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
+__global__ __launch_bounds__(64) void nvfp4_tile16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     const float* __restrict__ gscales, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
   const int64_t cpr = cols >> 3;
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;   // chunk column
+  const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;    // chunk column
   const int64_t r0 = (int64_t)blockIdx.y * 16;
   const bool valid = j < cpr;
   uint4 v[16];
@@ -264,14 +284,31 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     for (int i = 0; i < 8; ++i) mb = umax(mb, bf16x2_absmax_bits(colw[i]));
     BlockScale bs = nv_block_scale(__uint_as_float(mb << 16), S);
     uint32_t out[2] = {0, 0};
+    float yv[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float a = bf16_lo(colw[i]), b = bf16_hi(colw[i]);
       float ya = a * bs.r, yb = b * bs.r;
       if (bs.code == 0) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
-      uint32_t qa = SR ? f32_to_e2m1_sr(ya, rr16[2 * i]) : f32_to_e2m1_rne(ya);
-      uint32_t qb = SR ? f32_to_e2m1_sr(yb, rr16[2 * i + 1]) : f32_to_e2m1_rne(yb);
-      out[i >> 2] |= (qa | (qb << 4)) << (8 * (i & 3));
+      yv[2 * i] = ya;
+      yv[2 * i + 1] = yb;
+    }
+    if (SR) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t qa = f32_to_e2m1_sr(yv[2 * i], rr16[2 * i]);
+        uint32_t qb = f32_to_e2m1_sr(yv[2 * i + 1], rr16[2 * i + 1]);
+        out[i >> 2] |= (qa | (qb << 4)) << (8 * (i & 3));
+      }
+    } else {
+      out[0] = e2m1_rne_pair<0>(out[0], yv[0], yv[1]);
+      out[0] = e2m1_rne_pair<1>(out[0], yv[2], yv[3]);
+      out[0] = e2m1_rne_pair<2>(out[0], yv[4], yv[5]);
+      out[0] = e2m1_rne_pair<3>(out[0], yv[6], yv[7]);
+      out[1] = e2m1_rne_pair<0>(out[1], yv[8], yv[9]);
+      out[1] = e2m1_rne_pair<1>(out[1], yv[10], yv[11]);
+      out[1] = e2m1_rne_pair<2>(out[1], yv[12], yv[13]);
+      out[1] = e2m1_rne_pair<3>(out[1], yv[14], yv[15]);
     }
     int64_t c = j * 4 + cidx;
     *reinterpret_cast<uint2*>(codes + c * ld_codes + (r0 >> 1)) = make_uint2(out[0], out[1]);
@@ -287,13 +324,21 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict
                                                       uint32_t* __restrict__ out_bits) {
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
+  const int64_t stride = (int64_t)gridDim.x * 256;
   uint32_t m = 0;
-  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
-       id += (int64_t)gridDim.x * 256) {
-    int64_t r = id / cpr, c = id - r * cpr;
-    uint4 v = *reinterpret_cast<const uint4*>(x + r * ld_x + c * 8);
-    m = umax(m, umax(umax(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
-                     umax(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w))));
+  // four independent 16-byte loads in flight per lane
+  for (int64_t base = (int64_t)blockIdx.x * 256 + threadIdx.x; base < total; base += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t id = base + u * stride;
+      const int64_t r = id / cpr, c = id - r * cpr;
+      v[u] = id < total ? *reinterpret_cast<const uint4*>(x + r * ld_x + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      m = umax(m, umax(umax(bf16x2_absmax_bits(v[u].x), bf16x2_absmax_bits(v[u].y)),
+                       umax(bf16x2_absmax_bits(v[u].z), bf16x2_absmax_bits(v[u].w))));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = umax(m, lane_xor_u32(m, o));
@@ -317,8 +362,8 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t co
   uint32_t* bits = reinterpret_cast<uint32_t*>(gscale);
   hipLaunchKernelGGL(nv_zero_u32, dim3(1), dim3(1), 0, st, bits);
   int64_t total = rows * (cols / 8);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  int64_t blocks = (total + 1023) / 1024;          // 4 chunks per lane
+  if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld_x,
                      bits);
@@ -366,12 +411,14 @@ hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, in
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
                                const float* gscales, bool sr, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st) {
-  dim3 grid((unsigned)((cols / 8 + 255) / 256), (unsigned)(rows / 16));
+  // one wave per workgroup: a 16-row strip of 512 columns (small weights
+  // still spread over many CUs)
+  dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
   if (sr)
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(64), 0, st, x, rows, cols, ld_x,
                        codes, ld_codes, bscales, gscales, seed, sid, tag);
   else
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(64), 0, st, x, rows, cols, ld_x,
                        codes, ld_codes, bscales, gscales, seed, sid, tag);
   return hipGetLastError();
 }
