@@ -25,13 +25,11 @@
 //    the accumulator in the epilogue.
 //  * BF16: v_mfma_f32_32x32x16_bf16 (the dequantized-backward DGRAD).
 //
-// Workgroup: 256 lanes as 2 x 2 waves; a BM x BN output tile, each wave a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles.  An LDS row holds 128 bytes of K
-// (128 FP8 or 64 FP16/BF16 values) as eight 16-byte chunks plus 16 bytes of
-// padding; chunk c of row r sits in slot c ^ ((r >> 3) & 7).  The padding
-// makes the 16-byte fragment reads of 8 consecutive rows conflict-free, and
-// the XOR keeps writes of rows 8 apart (the transposed-B loader) on distinct
-// banks.  The MFMA runs with B as its first operand, so each lane ends up
+// Workgroup: 4 or 8 waves as a WGM x WGN grid; a BM x BN output tile, each wave a
+// (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles.  An LDS row holds 128 bytes
+// of K (128 FP8 or 64 FP16/BF16 values) as eight 16-byte chunks, placed by an
+// XOR swizzle that keeps the fragment reads and the loader writes free of
+// bank conflicts (slot_of).  The MFMA runs with B as its first operand, so each lane ends up
 // with 4 consecutive output columns and the epilogue stores 8 bytes at a time.
 // B may be stored transposed ([K, N], the FPROP weight copy read by DGRAD):
 // the loader transposes R x 8 sub-blocks in registers (byte permutes).
@@ -50,18 +48,27 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-constexpr int LDS_ROW = 144;     // bytes per LDS row: 8 chunks of 16 + 16 pad
+constexpr int LDS_ROW = 128;     // bytes per LDS row: 8 chunks of 16
 
-__device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ ((row >> 3) & 7); }
+// LDS bank model of gfx950 (measured): 64 banks of 4 bytes; a 16-byte access
+// serves 16 lanes per cycle, so 16 lanes must cover the 64 banks once.  A row
+// is 32 banks, so rows r and r + 1 use opposite bank halves and chunk c of
+// row r goes to slot c ^ (((r >> 1) ^ (r >> 4)) & 7):
+//  * fragment reads (16 consecutive rows from a multiple of 16, one chunk):
+//    within each half the 8 rows get 8 distinct slots -> conflict-free;
+//  * row-major loader writes (2 rows x 8 chunks, or 4 rows x 4 even/odd
+//    chunks per 16 lanes) -> conflict-free;
+//  * transposed-B writes (16 lanes on rows 8 apart, one half) -> each slot
+//    twice, the minimum for 16-byte writes into 32 banks.
+__device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 4)) & 7); }
 
 // Raw buffer loads: the hardware range check returns zero for an offset at or
 // beyond the buffer size, so tails need neither branches nor selects around
 // the loads (branches would make the compiler drain every outstanding load,
 // the prefetched stage included, before the LDS stores).  Offsets are 32-bit:
-// every operand is below 2^31 bytes (checked by the host), and OOB = 2^31 is
-// always out of range.
+// every operand is below 2^31 bytes (checked by the host), so any offset with
+// bit 31 set is out of range.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t OOB = 0x80000000u;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -81,6 +88,12 @@ __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+// The offset itself when ok, else one at or beyond 2^31 (out of range).  Pure
+// arithmetic: a select here tends to be turned into a branch around two copies
+// of the load, which drains the loads in flight.
+__device__ __forceinline__ uint32_t in_range(bool ok, uint32_t off) {
+  return off | ((uint32_t)!ok << 31);
 }
 
 // ------------------------------------------------------------ FP4 -> FP16
@@ -169,13 +182,31 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 }
 
 // ------------------------------------------------------------ the kernel
-template <int PATH, int BM, int BN, bool BT, int DIST>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+// Template parameters: compute path, output tile BM x BN, transposed B, the
+// register prefetch distance (1 or 2 stages), the wave grid WGM x WGN and the
+// ping-pong schedule PP.
+//
+// PP (8 waves, two on each SIMD): waves 0-3 and 4-7 form two groups; group g
+// computes output rows [g BM/2, (g+1) BM/2) and loads half of every stage
+// (its A rows and half of the B rows).  The groups run one barrier phase
+// apart: while one group issues MFMAs, the other converts and stores its half
+// of the next stage and issues the global loads of the one after, so the
+// matrix cores see one group's MFMAs in every phase.  Phase p (each ends in a
+// workgroup barrier): group 0 computes stage p/2 (p even) or stores its half
+// of stage p/2 + 1 (p odd); group 1 the reverse.  Stage t lives in LDS buffer
+// t % 2, is written in phases 2t-2 and 2t-1 and read in phases 2t and 2t+1.
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NT = 64 * WGM * WGN;
+  static_assert(!PP || (NT == 512 && DIST == 1 && WGM % 2 == 0), "ping-pong: 8 waves, one staging set");
+  constexpr int LT = PP ? NT / 2 : NT;                      // threads loading one share
+  constexpr int LBM = PP ? BM / 2 : BM, LBN = PP ? BN / 2 : BN;   // rows of a share
   constexpr int ROWS = BM + BN;
   constexpr int STAGE_BYTES = ROWS * LDS_ROW;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && TM >= 1 && TN >= 1, "wave tile");
   constexpr int KSTEP = PATH == P_FP8 ? 128 : 64;          // K elements per stage
 
   // ---- XCD-aware tile id: workgroup b runs on XCD b % 8; give each XCD a
@@ -190,11 +221,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
   const TileOrigin to = tile_origin<BM>(p, mt);
   if (!to.active) return;
-  const int64_t n0 = (int64_t)nt * BN;
+  // Every operand is below 2^31 bytes (checked by the host), so K, N, row
+  // indices and byte offsets inside A, B and their scales fit 32 bits.
+  const int K = (int)p.K, N = (int)p.N;
+  const int n0 = nt * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
+  // loader: thread within its share, and the share's first A and B row
+  const int grp = PP ? (tid >> 8) : 0;
+  const int ltid = PP ? (tid & 255) : tid;
+  const int la0 = grp * LBM, lb0 = grp * LBN;
 
   // byte offset of this group's B matrix: FP8 1 B, NVFP4 1/2 B, BF16 2 B per element
   const int64_t gel = (int64_t)to.group * p.b_group_elems;
@@ -202,16 +240,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const uint8_t* bscl = p.b_scales ? p.b_scales + (int64_t)to.group * p.b_group_scales : nullptr;
 
   // ------------------------------------------------ loader geometry
-  // Row-major operands: a lane moves 16 global bytes per chunk.
-  //   FP8 / BF16: 16 B = one LDS chunk; 8 chunks per row per stage.
-  //   NVFP4: 16 B of codes = 32 values = 4 LDS chunks; 2 per row per stage.
-  constexpr int CPR = PATH == P_F16 ? 2 : 8;                 // global chunks per row per stage
-  constexpr int A_CH = BM * CPR / 256;
-  constexpr int B_CH = BN * CPR / 256;
-  // Transposed B: a lane owns R K-rows x 8 N-columns per stage (256 lanes
-  // cover KSTEP x BN exactly).
-  constexpr int R_BT = KSTEP * BN / 2048;
-  const int64_t nk = (p.K + KSTEP - 1) / KSTEP;
+  // Row-major operands, per lane and chunk:
+  //   FP8 / BF16: 16 global bytes = one LDS chunk; 8 chunks per row per stage.
+  //   NVFP4: 8 bytes of codes = one 16-value block (one scale byte) = 2 LDS
+  //   chunks; 4 per row per stage.  K % 16 == 0, so a block is in or out of
+  //   range whole, and an out-of-range block reads zero codes and a zero scale.
+  constexpr int CPR = PATH == P_F16 ? 4 : 8;                 // global chunks per row per stage
+  constexpr int CW = PATH == P_F16 ? 2 : 4;                  // words per chunk
+  constexpr uint32_t CB = 4u * CW;                           // global bytes per chunk
+  static_assert((LBM * CPR) % LT == 0 && (LBN * CPR) % LT == 0, "loader split");
+  constexpr int A_CH = LBM * CPR / LT;
+  constexpr int B_CH = LBN * CPR / LT;
+  // Transposed B: a lane owns R K-rows x 8 N-columns per stage (LT lanes
+  // cover KSTEP x LBN exactly).
+  constexpr int R_BT = KSTEP * LBN / (8 * LT);
+  static_assert(!BT || (R_BT >= (PATH == P_FP8 ? 4 : 2) && R_BT <= 16), "transposed loader");
+  const int nk = (K + KSTEP - 1) / KSTEP;
+  // bytes of K advanced per stage in a row-major operand row
+  constexpr uint32_t ROW_STEP = PATH == P_F16 ? 32 : 128;
 
   // buffer resources: A (all stored rows), its scales, and this group's B
   constexpr int ESZ_A = PATH == P_BF16 ? 2 : 1;           // bytes per element (NVFP4: 1/2)
@@ -221,249 +267,249 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const rsrc_t rAs = make_rsrc(p.a_scales, p.a_scales ? p.a_rows * (p.K >> (PATH == P_FP8 ? 5 : 4)) : 0);
   const rsrc_t rB = make_rsrc(bbase, (BT ? p.K : p.N) * b_row_bytes);
   const rsrc_t rBs = make_rsrc(bscl, bscl ? p.b_group_scales : 0);
+  const uint32_t arb = (uint32_t)a_row_bytes, brb = (uint32_t)b_row_bytes;
 
-  // per-lane A rows (gather + group bounds resolved once); rows past the
-  // tile's end read as zero and their outputs are never stored
-  uint32_t a_off[A_CH];
-  int a_r[A_CH], a_c[A_CH];
+  // Scale-byte offsets advance by a fixed step per stage: 4 blocks per stage
+  // (NVFP4: 64 / 16; MXFP8: 128 / 32), i.e. 4 bytes in a linear layout and
+  // one 128-byte chunk in the MFMA layout (blocks 4j..4j+3 of 32 rows).
+  const int nb16 = K >> 4, nb32 = K >> 5;
+  const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;
+
+  // per-lane A chunks: row, chunk, byte offset at stage 0, scale offset at stage 0
+  int a_c[A_CH], a_r[A_CH];
   bool a_ok[A_CH];
-  int64_t a_src[A_CH];
+  uint32_t a_off[A_CH], a_soff[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    int id = tid + 256 * i;
-    int r = id / CPR, c = id % CPR;
+    const int id = ltid + LT * i;
+    const int r = la0 + id / CPR, c = id % CPR;
     a_r[i] = r;
     a_c[i] = c;
-    int64_t m = to.m0 + r;
+    const int64_t m = to.m0 + r;
     a_ok[i] = m < to.m_end;
-    int64_t src = 0;
-    if (a_ok[i]) src = p.row_index ? (int64_t)p.row_index[m] : m;
-    a_src[i] = src;
-    a_off[i] = (uint32_t)(src * a_row_bytes);
+    int src = 0;
+    if (a_ok[i]) src = p.row_index ? p.row_index[m] : (int)m;
+    a_off[i] = (uint32_t)src * arb + (uint32_t)c * CB;
+    a_soff[i] = PATH == P_F16 ? (uint32_t)scale_offset(src, c, nb16, p.a_mfma_layout) : 0u;
   }
+  // per-lane B chunks (row-major B)
+  int b_c[B_CH], b_r[B_CH];
+  bool b_ok[B_CH];
+  uint32_t b_off[B_CH], b_soff[B_CH];
+  const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int id = ltid + LT * i;
+    const int r = lb0 + id / CPR, c = id % CPR;
+    b_r[i] = r;
+    b_c[i] = c;
+    const int n = n0 + r;
+    b_ok[i] = !BT && n < N;
+    b_off[i] = (uint32_t)n * brb + (uint32_t)c * CB;
+    b_soff[i] = 0;
+    if (PATH == P_F16 && !BT)
+      b_soff[i] = p.b_tile ? (uint32_t)((n >> 4) * nb16 + c)
+                           : (uint32_t)scale_offset(n, c, nb16, p.b_mfma_layout);
+  }
+  // transposed B: lane -> (k group, n group of 8), n fastest for coalesced row
+  // reads; K and N are multiples of the tile size, so a group is in or out whole.
+  const int bt_ng = lb0 / 8 + ltid % (LBN / 8), bt_kg = ltid / (LBN / 8);
+  const bool bt_nok = n0 + bt_ng * 8 < N;
+  constexpr int ESZ_BT = PATH == P_FP8 ? 1 : 2;                // bytes per value in LDS
+  const uint32_t bt_off = (uint32_t)(bt_kg * R_BT) * brb +
+                          (PATH == P_F16 ? (uint32_t)(n0 + bt_ng * 8) / 2 : (uint32_t)(n0 + bt_ng * 8) * ESZ_BT);
+  const uint32_t bt_step = (uint32_t)KSTEP * brb;
+  const uint32_t bt_soff = (uint32_t)(((bt_kg * R_BT) >> 4) * (N >> 4) + ((n0 + bt_ng * 8) >> 4));
+  const uint32_t bt_sstep = 4u * (uint32_t)(N >> 4);
 
   // DIST staging sets in registers: with DIST = 2 the stage being written to
   // LDS and the next one are both in flight.  Set indices are compile-time
   // constants once the K loop is unrolled by two.
-  uint4 ra_[DIST][A_CH];
-  uint32_t rsa_[DIST][A_CH][2];
-  uint4 rb_[DIST][BT ? 1 : B_CH];
-  uint32_t rsb_[DIST][BT ? 1 : B_CH][2];
+  uint32_t ra_[DIST][A_CH][CW];
+  uint32_t rsa_[DIST][A_CH];
+  uint32_t rb_[DIST][BT ? 1 : B_CH][CW];
+  uint32_t rsb_[DIST][BT ? 1 : B_CH];
   // transposed staging: FP8 R rows x 8 bytes (2 words); BF16 R rows x 8
   // values (4 words); NVFP4 R rows x 8 codes (1 word) + one 16x16 tile scale
   uint32_t rbt_[DIST][BT ? R_BT : 1][PATH == P_BF16 ? 4 : PATH == P_FP8 ? 2 : 1];
   uint32_t rbt_s_[DIST];
-  // MXFP8: the E8M0 bytes each lane feeds its MFMAs, prefetched with the stage
+
+  // MXFP8: the E8M0 bytes each lane feeds its MFMAs, prefetched with the
+  // stage.  Lane (r, h) needs, for each of its MFMA tiles, the bytes of blocks
+  // 4kt + h and 4kt + 2 + h of its row (one per 64-wide K slice).
   uint32_t sa_[2][TM][2], sb_[2][TN][2];
+  uint32_t sa_off[TM][2], sb_off[TN][2];
+  bool sa_ok[TM], sb_ok[TN];
   int64_t sa_row[TM];
+  const int hl = lane >> 5;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int64_t m = to.m0 + wm * WM + tm * 32 + (lane & 31);
     sa_row[tm] = m < to.m_end ? (p.row_index ? (int64_t)p.row_index[m] : m) : -1;
+    sa_ok[tm] = sa_row[tm] >= 0;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      sa_off[tm][ks] = (PATH == P_FP8 && sa_ok[tm])
+                           ? (uint32_t)scale_offset(sa_row[tm], ks * 2 + hl, nb32, p.a_mfma_layout) : 0u;
   }
+  uint32_t sb_step = 4u;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int n = n0 + wn * WN + tn * 32 + (lane & 31);
+    sb_ok[tn] = n < N;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kb = ks * 2 + hl;
+      uint32_t so = 0;
+      if (PATH == P_FP8) {
+        if (BT) so = (uint32_t)(kb * (N >> 5) + (n >> 5));            // stored [K/32, N/32]
+        else if (p.b_tile) so = (uint32_t)((n >> 5) * nb32 + kb);
+        else so = (uint32_t)scale_offset(n, kb, nb32, p.b_mfma_layout);
+      }
+      sb_off[tn][ks] = so;
+    }
+  }
+  if (PATH == P_FP8) sb_step = BT ? 4u * (uint32_t)(N >> 5) : (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 
-  // MXFP8 scale bytes of stage kt into scale set `set` (two sets, by parity):
-  // lane (r, h) needs, for each of its MFMA tiles, the E8M0 bytes of blocks
-  // 4kt + h and 4kt + 2 + h of its row (one per 64-wide K slice).
-  // Out-of-range blocks read 0 (their data are zero too).
-  auto load_scales = [&](int64_t kt, int set) {
+  auto load_scales = [&](int kt, int set) {
     if (PATH == P_FP8) {
-      const int64_t KB = p.K >> 5;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int64_t kb = kt * 4 + ks * 2 + (lane >> 5);
-          const bool ok = sa_row[tm] >= 0 && kb < KB;
-          sa_[set][tm][ks] = bload1(rAs, ok ? (uint32_t)scale_offset(sa_row[tm], kb, KB, p.a_mfma_layout) : OOB);
+          const bool ok = sa_ok[tm] && kt * 4 + ks * 2 + hl < nb32;
+          sa_[set][tm][ks] = bload1(rAs, in_range(ok, sa_off[tm][ks] + (uint32_t)kt * a_sstep));
         }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int64_t kb = kt * 4 + ks * 2 + (lane >> 5);
-          const int64_t n = n0 + wn * WN + tn * 32 + (lane & 31);
-          const bool ok = n < p.N && kb < KB;
-          int64_t so;
-          if (BT) so = kb * (p.N >> 5) + (n >> 5);                  // stored [K/32, N/32]
-          else if (p.b_tile) so = (n >> 5) * KB + kb;
-          else so = scale_offset(n, kb, KB, p.b_mfma_layout);
-          sb_[set][tn][ks] = bload1(rBs, ok ? (uint32_t)so : OOB);
+          const bool ok = sb_ok[tn] && kt * 4 + ks * 2 + hl < nb32;
+          sb_[set][tn][ks] = bload1(rBs, in_range(ok, sb_off[tn][ks] + (uint32_t)kt * sb_step));
         }
     }
   };
 
-  auto load_stage = [&](int64_t kt, int set) {
-    const int64_t k0 = kt * KSTEP;
-    uint4* ra = ra_[set];
-    uint32_t (*rsa)[2] = rsa_[set];
-    uint4* rb = rb_[set];
-    uint32_t (*rsb)[2] = rsb_[set];
+  auto load_stage = [&](int kt, int set) {
+    const int k0 = kt * KSTEP;
+    auto& ra = ra_[set];
+    uint32_t* rsa = rsa_[set];
+    auto& rb = rb_[set];
+    uint32_t* rsb = rsb_[set];
     auto& rbt = rbt_[set];
     uint32_t& rbt_s = rbt_s_[set];
+    // one chunk into w[CW]; values per chunk: NVFP4 16, FP8 16, BF16 8
+    auto chunk = [&](rsrc_t r, uint32_t off, uint32_t* w) {
+      if (PATH == P_F16) {
+        const uint2 v = bload8(r, off);
+        w[0] = v.x; w[1] = v.y;
+      } else {
+        const uint4 v = bload16(r, off);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      }
+    };
+    constexpr int VPC = PATH == P_BF16 ? 8 : 16;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      if (PATH == P_F16) {
-        // 32 codes = blocks kb, kb+1; K % 16 == 0, so a block is in or out whole
-        const int64_t kb = (k0 >> 4) + 2 * a_c[i];
-        const bool ok0 = a_ok[i] && kb * 16 < p.K, ok1 = a_ok[i] && (kb + 1) * 16 < p.K;
-        const uint2 lo = bload8(rA, ok0 ? a_off[i] + (uint32_t)(kb * 8) : OOB);
-        const uint2 hi = bload8(rA, ok1 ? a_off[i] + (uint32_t)(kb * 8 + 8) : OOB);
-        ra[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        // scale bytes of blocks kb, kb+1 are adjacent in every layout (kb
-        // even); kept raw here and split at the LDS store, so that nothing
-        // waits on this load before the next stage's compute
-        rsa[i][0] = bload2(rAs, ok0 ? (uint32_t)scale_offset(a_src[i], kb, p.K >> 4, p.a_mfma_layout) : OOB);
-      } else {
-        const int64_t ke = k0 + a_c[i] * (PATH == P_FP8 ? 16 : 8);
-        ra[i] = bload16(rA, (a_ok[i] && ke < p.K) ? a_off[i] + (uint32_t)(ke * ESZ_A) : OOB);
-      }
+      const bool ok = a_ok[i] && k0 + a_c[i] * VPC < K;
+      chunk(rA, in_range(ok, a_off[i] + (uint32_t)kt * ROW_STEP), ra[i]);
+      // the block's scale byte, kept raw until the LDS store so that nothing
+      // waits on this load before the next stage's compute
+      if (PATH == P_F16) rsa[i] = bload1(rAs, in_range(ok, a_soff[i] + (uint32_t)kt * a_sstep));
     }
     if (!BT) {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int id = tid + 256 * i;
-        const int r = id / CPR, c = id % CPR;
-        const int64_t n = n0 + r;
-        const bool rok = n < p.N;
-        if (PATH == P_F16) {
-          const int64_t kb = (k0 >> 4) + 2 * c;
-          const bool ok0 = rok && kb * 16 < p.K, ok1 = rok && (kb + 1) * 16 < p.K;
-          const uint32_t ro = (uint32_t)(n * b_row_bytes);
-          const uint2 lo = bload8(rB, ok0 ? ro + (uint32_t)(kb * 8) : OOB);
-          const uint2 hi = bload8(rB, ok1 ? ro + (uint32_t)(kb * 8 + 8) : OOB);
-          rb[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const int64_t nb = p.K >> 4;
-          const int64_t so = p.b_tile ? (n >> 4) * nb + kb : scale_offset(n, kb, nb, p.b_mfma_layout);
-          rsb[i][0] = bload2(rBs, ok0 ? (uint32_t)so : OOB);
-        } else {
-          const int64_t ke = k0 + c * (PATH == P_FP8 ? 16 : 8);
-          const int64_t boff = n * b_row_bytes + ke * (PATH == P_FP8 ? 1 : 2);
-          rb[i] = bload16(rB, (rok && ke < p.K) ? (uint32_t)boff : OOB);
-        }
+        const bool ok = b_ok[i] && k0 + b_c[i] * VPC < K;
+        chunk(rB, in_range(ok, b_off[i] + (uint32_t)kt * ROW_STEP), rb[i]);
+        if (PATH == P_F16) rsb[i] = bload1(rBs, in_range(ok, b_soff[i] + (uint32_t)kt * b_sstep));
       }
     } else {
-      // lane -> (k group, n group of 8), n fastest for coalesced row reads;
-      // K and N are multiples of the tile size, so a group is in or out whole.
-      const int ng = tid % (BN / 8), kg = tid / (BN / 8);
-      const int64_t kr = k0 + (int64_t)kg * R_BT;
-      const int64_t n = n0 + (int64_t)ng * 8;
-      const bool ok = kr < p.K && n < p.N;
+      const bool ok = bt_nok && k0 + bt_kg * R_BT < K;
+      const uint32_t o = bt_off + (uint32_t)kt * bt_step;
 #pragma unroll
       for (int q = 0; q < R_BT; ++q) {
+        const uint32_t oq = in_range(ok, o + (uint32_t)q * brb);
         if (PATH == P_FP8) {
-          const uint2 v = bload8(rB, ok ? (uint32_t)((kr + q) * b_row_bytes + n) : OOB);
+          const uint2 v = bload8(rB, oq);
           rbt[q][0] = v.x;
           rbt[q][1] = v.y;
         } else if (PATH == P_BF16) {
-          const uint4 v = bload16(rB, ok ? (uint32_t)((kr + q) * b_row_bytes + n * 2) : OOB);
+          const uint4 v = bload16(rB, oq);
           rbt[q][0] = v.x; rbt[q][1] = v.y; rbt[q][2] = v.z; rbt[q][3] = v.w;
         } else {
-          rbt[q][0] = bload4(rB, ok ? (uint32_t)((kr + q) * b_row_bytes + n / 2) : OOB);
+          rbt[q][0] = bload4(rB, oq);
         }
       }
-      if (PATH == P_F16) rbt_s = bload1(rBs, ok ? (uint32_t)((kr >> 4) * (p.N >> 4) + (n >> 4)) : OOB);
+      if (PATH == P_F16) rbt_s = bload1(rBs, in_range(ok, bt_soff + (uint32_t)kt * bt_sstep));
     }
   };
 
-  // Split the two raw scale bytes of blocks (kb, kb+1); the second is zeroed
-  // when block kb+1 lies beyond K (its codes read as zero; a zero scale keeps
-  // any byte found there out of the product).
-  auto split_scales = [&](uint32_t raw, int64_t kb) -> uint2 {
-    return make_uint2(raw & 0xFFu, (kb + 1) * 16 < p.K ? ((raw >> 8) & 0xFFu) : 0u);
+  // LDS store of a transposed column run of NW words (4, 8 or 16 bytes)
+  auto store_run = [](uint8_t* dst, const uint32_t* o, int nw) {
+    if (nw == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    else if (nw == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+    else *reinterpret_cast<uint32_t*>(dst) = o[0];
   };
 
-  auto store_stage = [&](uint8_t* L, int set, int64_t kt) {
-    const int64_t k0s = kt * KSTEP;
+  // One chunk -> LDS.  NVFP4: 16 codes of one block times its scale -> two
+  // FP16 chunks (slots 2c, 2c + 1); otherwise the 16 bytes as they are.
+  auto store_chunk = [&](uint8_t* row, int r, int c, const uint32_t* w, uint32_t sraw) {
+    if (PATH == P_F16) {
+      const uint32_t sp = e4m3_to_f16_pair(sraw & 0xFFu);
+      uint32_t o0[4], o1[4];
+      fp4x8_to_f16(w[0], sp, o0);
+      fp4x8_to_f16(w[1], sp, o1);
+      *reinterpret_cast<uint4*>(row + slot_of(r, 2 * c) * 16) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint4*>(row + slot_of(r, 2 * c + 1) * 16) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    } else {
+      *reinterpret_cast<uint4*>(row + slot_of(r, c) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+
+  auto store_stage = [&](uint8_t* L, int set) {
     uint8_t* LA = L;
     uint8_t* LB = L + BM * LDS_ROW;
-    const uint4* ra = ra_[set];
-    const uint32_t (*rsa)[2] = rsa_[set];
-    const uint4* rb = rb_[set];
-    const uint32_t (*rsb)[2] = rsb_[set];
+    const auto& ra = ra_[set];
+    const uint32_t* rsa = rsa_[set];
+    const auto& rb = rb_[set];
+    const uint32_t* rsb = rsb_[set];
     const auto& rbt = rbt_[set];
     const uint32_t rbt_s = rbt_s_[set];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int r = a_r[i];
-      uint8_t* row = LA + r * LDS_ROW;
-      if (PATH == P_F16) {
-        const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-        const uint2 scs = split_scales(rsa[i][0], (k0s >> 4) + 2 * a_c[i]);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint32_t sp = e4m3_to_f16_pair(hh ? scs.y : scs.x);
-          uint32_t o0[4], o1[4];
-          fp4x8_to_f16(w[2 * hh], sp, o0);
-          fp4x8_to_f16(w[2 * hh + 1], sp, o1);
-          const int c = a_c[i] * 4 + 2 * hh;
-          *reinterpret_cast<uint4*>(row + slot_of(r, c) * 16) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-          *reinterpret_cast<uint4*>(row + slot_of(r, c + 1) * 16) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-        }
-      } else {
-        *reinterpret_cast<uint4*>(row + slot_of(r, a_c[i]) * 16) = ra[i];
-      }
-    }
+    for (int i = 0; i < A_CH; ++i) store_chunk(LA + a_r[i] * LDS_ROW, a_r[i], a_c[i], ra[i], rsa[i]);
     if (!BT) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int id = tid + 256 * i;
-        const int r = id / CPR, c = id % CPR;
-        uint8_t* row = LB + r * LDS_ROW;
-        if (PATH == P_F16) {
-          const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-          const uint2 scs = split_scales(rsb[i][0], (k0s >> 4) + 2 * c);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t sp = e4m3_to_f16_pair(hh ? scs.y : scs.x);
-            uint32_t o0[4], o1[4];
-            fp4x8_to_f16(w[2 * hh], sp, o0);
-            fp4x8_to_f16(w[2 * hh + 1], sp, o1);
-            const int cc = c * 4 + 2 * hh;
-            *reinterpret_cast<uint4*>(row + slot_of(r, cc) * 16) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-            *reinterpret_cast<uint4*>(row + slot_of(r, cc + 1) * 16) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-          }
-        } else {
-          *reinterpret_cast<uint4*>(row + slot_of(r, c) * 16) = rb[i];
-        }
-      }
+      for (int i = 0; i < B_CH; ++i) store_chunk(LB + b_r[i] * LDS_ROW, b_r[i], b_c[i], rb[i], rsb[i]);
     } else {
-      const int ng = tid % (BN / 8), kg = tid / (BN / 8);
-      constexpr int ESZ = PATH == P_FP8 ? 1 : 2;
-      const int kbyte = kg * R_BT * ESZ;                     // this lane's K range: 8 or 16 bytes
-      if (PATH == P_F16) {
+      const int kbyte = bt_kg * R_BT * ESZ_BT;         // this lane's K range: 4, 8 or 16 bytes
+      if constexpr (PATH == P_F16) {
         const uint32_t sp = e4m3_to_f16_pair(rbt_s);
         uint32_t hv[R_BT][4];
 #pragma unroll
         for (int q = 0; q < R_BT; ++q) fp4x8_to_f16(rbt[q][0], sp, hv[q]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int r = ng * 8 + j;
-          uint32_t o[R_BT / 2];
+          const int r = bt_ng * 8 + j;
+          uint32_t o[R_BT >= 2 ? R_BT / 2 : 1];
           transpose16<R_BT>(hv, j, o);
-          uint8_t* dst = LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15);
-          if (R_BT == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-          else *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+          store_run(LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15), o, R_BT / 2);
         }
-      } else if (PATH == P_BF16) {
+      } else if constexpr (PATH == P_BF16) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int r = ng * 8 + j;
-          uint32_t o[R_BT / 2];
+          const int r = bt_ng * 8 + j;
+          uint32_t o[R_BT >= 2 ? R_BT / 2 : 1];
           transpose16<R_BT>(reinterpret_cast<const uint32_t(*)[4]>(rbt), j, o);
-          uint8_t* dst = LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15);
-          if (R_BT == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-          else *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+          store_run(LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15), o, R_BT / 2);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int r = ng * 8 + j;
-          uint32_t o[R_BT / 4];
+          const int r = bt_ng * 8 + j;
+          uint32_t o[R_BT >= 4 ? R_BT / 4 : 1];
           transpose8<R_BT>(reinterpret_cast<const uint32_t(*)[2]>(rbt), j, o);
-          uint8_t* dst = LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15);
-          if (R_BT == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-          else *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+          store_run(LB + r * LDS_ROW + slot_of(r, kbyte >> 4) * 16 + (kbyte & 15), o, R_BT / 4);
         }
       }
     }
@@ -477,24 +523,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // One stage of MFMAs.  Fragment reads are software-pipelined: the reads of
+  // K step ks + 1 are issued before the MFMAs of step ks (two register sets),
+  // and scheduling barriers keep the compiler from folding the two back into
+  // a read-wait-multiply chain that would expose the LDS latency every step.
+  // Wave tiles with 8 or more MFMAs per K step keep one set (registers are
+  // short there, and the step's MFMAs already outlast the next reads' latency
+  // of the other wave on the SIMD).
+  constexpr int FS = TM * TN >= 8 ? 1 : 2;
   auto compute = [&](const uint8_t* Lcur, int set) {
     const uint8_t* LA = Lcur + (wm * WM) * LDS_ROW;
     const uint8_t* LB = Lcur + (BM + wn * WN) * LDS_ROW;
     const int r32 = lane & 31, h = lane >> 5;
-    if (PATH == P_FP8) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // lane (row r, half h) holds K bytes [16h, 16h+16) of block 0 and
-        // [32+16h, 32+16h+16) of block 1 of this 64-wide slice: chunks
-        // 4ks + h and 4ks + 2 + h.
-        v8i af[TM], bf[TN];
+    if constexpr (PATH == P_FP8) {
+      // lane (row r, half h) holds K bytes [16h, 16h+16) of block 0 and
+      // [32+16h, 32+16h+16) of block 1 of each 64-wide slice: chunks
+      // 4ks + h and 4ks + 2 + h.
+      v8i af[FS][TM], bf[FS][TN];
+      auto read = [&](int ks, int q) {
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const int r = wm * WM + tm * 32 + r32;
           const uint8_t* sp = LA + (tm * 32 + r32) * LDS_ROW;
           uint4 x0 = *reinterpret_cast<const uint4*>(sp + slot_of(r, 4 * ks + h) * 16);
           uint4 x1 = *reinterpret_cast<const uint4*>(sp + slot_of(r, 4 * ks + 2 + h) * 16);
-          af[tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          af[q][tm] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -502,41 +555,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
           const uint8_t* sp = LB + (tn * 32 + r32) * LDS_ROW;
           uint4 x0 = *reinterpret_cast<const uint4*>(sp + slot_of(r, 4 * ks + h) * 16);
           uint4 x1 = *reinterpret_cast<const uint4*>(sp + slot_of(r, 4 * ks + 2 + h) * 16);
-          bf[tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          bf[q][tn] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
+      };
+      if (FS == 2) read(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int q = FS == 2 ? (ks & 1) : 0;
+        if (FS == 1) read(ks, 0);
+        else if (ks + 1 < 2) read(ks + 1, (ks + 1) & 1);
+        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[tn], af[tm], acc[tm][tn], 0, 0, 0, (int)sb_[set][tn][ks], 0, (int)sa_[set][tm][ks]);
+                bf[q][tn], af[q][tm], acc[tm][tn], 0, 0, 0, (int)sb_[set][tn][ks], 0,
+                (int)sa_[set][tm][ks]);
+        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      uint4 af[FS][TM], bf[FS][TN];
+      auto read = [&](int ks, int q) {
         const int chunk = 2 * ks + h;                 // K values [16ks + 8h, +8)
-        uint4 af[TM], bf[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const int r = wm * WM + tm * 32 + r32;
-          af[tm] = *reinterpret_cast<const uint4*>(LA + (tm * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
+          af[q][tm] = *reinterpret_cast<const uint4*>(LA + (tm * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int r = wn * WN + tn * 32 + r32;
-          bf[tn] = *reinterpret_cast<const uint4*>(LB + (tn * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
+          bf[q][tn] = *reinterpret_cast<const uint4*>(LB + (tn * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
         }
+      };
+      if (FS == 2) read(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int q = FS == 2 ? (ks & 1) : 0;
+        if (FS == 1) read(ks, 0);
+        else if (ks + 1 < 4) read(ks + 1, (ks + 1) & 1);
+        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
-            if (PATH == P_F16)
+            if constexpr (PATH == P_F16)
               acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(v8h, bf[tn]), __builtin_bit_cast(v8h, af[tm]), acc[tm][tn], 0, 0, 0);
+                  __builtin_bit_cast(v8h, bf[q][tn]), __builtin_bit_cast(v8h, af[q][tm]), acc[tm][tn], 0, 0, 0);
             else
               acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(v8bf, bf[tn]), __builtin_bit_cast(v8bf, af[tm]), acc[tm][tn], 0, 0, 0);
+                  __builtin_bit_cast(v8bf, bf[q][tn]), __builtin_bit_cast(v8bf, af[q][tm]), acc[tm][tn], 0, 0, 0);
           }
+        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -544,34 +615,79 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   // Pipeline.  Stage s goes to LDS buffer s % 2 and uses MXFP8 scale set s % 2.
   //  DIST == 2: stage s is staged in register set s % 2; while stage kt is
   //    computed the loads of stages kt+1 and kt+2 are in flight; then stage
-  //    kt+1 is written to LDS and stage kt+3 is loaded into the set it freed.
-  //  DIST == 1 (large tiles, where two register sets would spill): stage kt+1
-  //    is loaded while stage kt is computed, then written to LDS.
+  //    kt+1 is written to LDS.  The loop runs two stages per iteration so
+  //    that every register-set index is a compile-time constant, and its
+  //    loads are unconditional (past the end they are range-checked to zero),
+  //    so the compiler can keep the other set's loads outstanding across the
+  //    LDS stores instead of draining them.
+  //  DIST == 1: the next stage's loads are in flight during the compute.
   uint8_t* const L0 = lds;
   uint8_t* const L1 = lds + STAGE_BYTES;
-  // Loads past the last stage are issued anyway: their offsets are out of
-  // range, so they read zeros and touch no memory, and the number of loads
-  // in flight is the same on every path (a conditional load would make the
-  // compiler drain the whole queue before each LDS store).
-  if (DIST == 2) {
+  if constexpr (PP) {
+    // prologue: both halves of stage 0 in buffer 0, stage 1 staged in
+    // registers, MXFP8 scale sets 0 and 1 for stages 0 and 1
+    load_stage(0, 0);
+    load_scales(0, 0);
+    load_scales(1, 1);
+    store_stage(L0, 0);
+    load_stage(1, 0);
+    __syncthreads();
+    // Stage loop, unrolled by two so that buffer and scale-set indices are
+    // constants.  The barrier count is the same for both groups (two per
+    // stage); past the last stage the loads read zeros and the stores write
+    // them into the idle buffer.
+    if (grp == 0) {
+      for (int kt = 0; kt < nk; kt += 2) {
+        compute(L0, 0);                      // C(kt)
+        __syncthreads();
+        store_stage(L1, 0);                  // M: stage kt+1 -> buffer 1
+        load_stage(kt + 2, 0);
+        load_scales(kt + 2, 0);
+        __syncthreads();
+        if (kt + 1 < nk) {
+          compute(L1, 1);                    // C(kt+1)
+          __syncthreads();
+          store_stage(L0, 0);                // M: stage kt+2 -> buffer 0
+          load_stage(kt + 3, 0);
+          load_scales(kt + 3, 1);
+          __syncthreads();
+        }
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += 2) {
+        store_stage(L1, 0);                  // M: stage kt+1 -> buffer 1
+        load_stage(kt + 2, 0);
+        load_scales(kt + 1, 1);
+        __syncthreads();
+        compute(L0, 0);                      // C(kt)
+        __syncthreads();
+        if (kt + 1 < nk) {
+          store_stage(L0, 0);                // M: stage kt+2 -> buffer 0
+          load_stage(kt + 3, 0);
+          load_scales(kt + 2, 0);
+          __syncthreads();
+          compute(L1, 1);                    // C(kt+1)
+          __syncthreads();
+        }
+      }
+    }
+  } else if (DIST == 2) {
     load_stage(0, 0);
     load_scales(0, 0);
     load_stage(1, 1 % DIST);
     load_scales(1, 1);
-    store_stage(L0, 0, 0);
+    store_stage(L0, 0);
     load_stage(2, 0);
     __syncthreads();
-    // pairs of stages with no branch inside: stores of stages past the end
-    // write zeros into a buffer that is never computed
-    int64_t kt = 0;
+    int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
       compute(L0, 0);
-      store_stage(L1, 1 % DIST, kt + 1);
+      store_stage(L1, 1 % DIST);
       load_stage(kt + 3, 1 % DIST);
       load_scales(kt + 2, 0);
       __syncthreads();
       compute(L1, 1);
-      store_stage(L0, 0, kt + 2);
+      store_stage(L0, 0);
       load_stage(kt + 4, 0);
       load_scales(kt + 3, 1);
       __syncthreads();
@@ -579,15 +695,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     if (kt < nk) compute(L0, 0);          // odd stage count: the last stage
   } else {
     load_stage(0, 0);
-    store_stage(L0, 0, 0);
+    store_stage(L0, 0);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nk; ++kt) {
       uint8_t* const Lc = (kt & 1) ? L1 : L0;
       uint8_t* const Ln = (kt & 1) ? L0 : L1;
       load_stage(kt + 1, 0);
       load_scales(kt, 0);
       compute(Lc, 0);
-      store_stage(Ln, 0, kt + 1);
+      store_stage(Ln, 0);
       __syncthreads();
     }
   }
@@ -609,7 +725,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * WN + tn * 32 + g * 8 + (lane >> 5) * 4;
+        const int n = n0 + wn * WN + tn * 32 + g * 8 + (lane >> 5) * 4;
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -617,12 +733,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
           if (PATH == P_F16) v = (v * sa) * sbg;
           o[i] = f32_to_bf16_rne(v);
         }
-        if (vec_ok && n + 3 < p.N) {
+        if (vec_ok && n + 3 < N) {
           *reinterpret_cast<uint2*>(crow + n) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (n + i < p.N) crow[n + i] = (uint16_t)o[i];
+            if (n + i < N) crow[n + i] = (uint16_t)o[i];
         }
       }
     }
@@ -630,50 +746,58 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------ launcher
-template <int PATH, int BM, int BN, bool BT, int DIST>
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_n = (a.N + BN - 1) / BN;
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)(BM + BN) * LDS_ROW;
+  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<PATH, BM, BN, BT, DIST>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<PATH, BM, BN, BT, DIST>), dim3((unsigned)tiles_n, (unsigned)tiles_m),
-                     dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * WGM * WGN), lds, st, a);
   return hipGetLastError();
 }
 
-// Tile choice: the largest tile that still gives every CU work.  A 256x256
-// tile keeps each wave's MFMA block at 128x128, where fragment traffic is
-// about half the LDS bandwidth; 128x128 trades that for occupancy on small
-// GEMMs.
-static int choose_tile(const GemmArgs& a) {
-  const int64_t cus = 256;
-  auto tiles = [&](int bm, int bn) {
-    int64_t tm = a.num_groups == 0 ? (a.M + bm - 1) / bm : a.M / bm + a.num_groups;
-    return tm * ((a.N + bn - 1) / bn);
-  };
-  if (tiles(256, 256) >= cus) return 2;
-  if (tiles(256, 128) >= cus) return 1;
-  return 0;
+static int64_t tile_count(const GemmArgs& a, int bm, int bn) {
+  int64_t tm = a.num_groups == 0 ? (a.M + bm - 1) / bm : a.M / bm + a.num_groups;
+  return tm * ((a.N + bn - 1) / bn);
 }
 
+#ifndef MXQ_TILE_OVERRIDE
+#define MXQ_TILE_OVERRIDE -1
+#endif
+
+// Tile choice: the largest tile that still gives every CU work.  Larger wave
+// tiles need fewer LDS fragment bytes per MFMA; 8-wave workgroups put two
+// waves on each SIMD.
 template <int PATH, bool BT>
 static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
-  int t = choose_tile(a);
-  // the FP8 256x256 variant needs more than 512 registers per lane (it would
-  // spill), so FP8 stops at 256x128
-  if (PATH == P_FP8 && t == 2) t = 1;
+  const int64_t cus = 256;
+  int t = MXQ_TILE_OVERRIDE;
+  if (t < 0) {
+    // measured on MI355X (8192^3, 8192x28672x4096, 4096x768x2048,
+    // 4096x2048x768, 2048x2048x4096): NVFP4 prefers 256x256 ping-pong on
+    // large GEMMs and the 8-wave 128x128 tile otherwise; BF16 prefers
+    // ping-pong 256x128 / 128x128; MXFP8 the 8-wave 256x128 tile.
+    const bool big = tile_count(a, 256, 256) >= cus, mid = tile_count(a, 256, 128) >= cus;
+    if (PATH == P_F16) t = big ? (BT ? 5 : 6) : 1;      // transposed 256x256 would spill
+    else if (PATH == P_BF16) t = mid ? 5 : 4;
+    else t = mid ? 2 : 1;
+  }
   switch (t) {
-    case 2: return launch_t<PATH, 256, 256, BT, 1>(a, st);
-    case 1: return launch_t<PATH, 256, 128, BT, PATH == P_BF16 ? 2 : 1>(a, st);
-    default: return launch_t<PATH, 128, 128, BT, 2>(a, st);
+    case 6: return launch_t<PATH, 256, 256, BT, 1, 4, 2, true>(a, st);
+    case 5: return launch_t<PATH, 256, 128, BT, 1, 4, 2, true>(a, st);
+    case 4: return launch_t<PATH, 128, 128, BT, 1, 4, 2, true>(a, st);
+    case 3: return launch_t<PATH, 256, 256, BT, 1, 2, 4>(a, st);
+    case 2: return launch_t<PATH, 256, 128, BT, 1, 4, 2>(a, st);
+    case 1: return launch_t<PATH, 128, 128, BT, 2, 2, 4>(a, st);
+    default: return launch_t<PATH, 128, 128, BT, 2, 2, 2>(a, st);
   }
 }
 
