@@ -23,6 +23,7 @@ the same step, is reported as "cpu_baseline".
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,37 @@ FLOPS_DGRAD = 2 * M * K * N
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "microscaling_quantization_block_amd", "csrc", "gemm.hip")
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES, ten times: the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 10}), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record, or
+    None when there is none or the GEMM source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def make_sets(m, torch, data):
@@ -144,6 +176,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time bound for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,6 +192,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     m.lib()
     log("generating synthetic inputs (seeded)")
     data = synth.config2()
@@ -201,10 +238,10 @@ def main():
     dk = kernels[names[dom]]
     if "TFLOPs" in dk:
         roofline = dict(kernel=names[dom], bound="mfma", achieved=dk["TFLOPs"], peak=PEAK_F16_TFLOPS,
-                        unit="TFLOP/s", frac=dk["frac_mfma"], traffic=None)
+                        unit="TFLOP/s", frac=dk["frac_mfma"], traffic=measured_traffic(names[dom]))
     else:
         roofline = dict(kernel=names[dom], bound="hbm", achieved=dk["GBps"], peak=PEAK_HBM_GBPS,
-                        unit="GB/s", frac=dk["frac_hbm"], traffic=None)
+                        unit="GB/s", frac=dk["frac_hbm"], traffic=measured_traffic(names[dom]))
     value = (FLOPS_FPROP + FLOPS_DGRAD) / (ms_step * 1e-3) / 1e12
     qbytes = BYTES_QX + BYTES_QW + BYTES_DQW
     qus = (stage_ms[0] + stage_ms[1] + stage_ms[3]) * 1e3
