@@ -16,7 +16,10 @@ the 256 MB last-level cache.
 
 Prints ONE JSON line on stdout.  `value` is the step's GEMM throughput: the
 two GEMMs' algorithmic flops (2*M*N*K each) over the whole step's time,
-quantization and dequantization included.  Per-kernel times, GB/s, TFLOP/s
+quantization and dequantization included.  The timed steps replay the step
+captured once per buffer set as a HIP graph (eight kernels per step; the
+library records no memsets, so every node is a kernel); `--eager` times
+plain launches instead, and the eager time is always reported beside it.  Per-kernel times, GB/s, TFLOP/s
 and fractions of peak are in "kernels"; "roofline" describes the kernel with
 the largest share of the step.  The CPU oracle, timed on a bounded sample of
 the same step, is reported as "cpu_baseline".
@@ -176,6 +179,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time bound for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain launches instead of HIP-graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -206,15 +211,36 @@ def main():
         step(m, sets[i % SETS])
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
+    # per-stage timing: plain launches with HIP events around each stage, on
+    # the stream the library launches on (torch's current stream)
+    log(f"per-stage timing, {args.steps} eager steps")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(m, sets[i % SETS], events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
+    ms_eager = (time.perf_counter() - t0) / args.steps * 1e3
+
+    if args.eager:
+        ms_step = ms_eager
+    else:
+        log("capturing one HIP graph per buffer set")
+        graphs = []
+        for s_ in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(m, s_)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % SETS].replay()
+        torch.cuda.synchronize()
+        log(f"timing {args.steps} graph-replayed steps")
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % SETS].replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) / args.steps * 1e3
 
     names = ["quantize_x_nvfp4_1x16_per_token", "quantize_w_nvfp4_16x16_per_tensor",
              "gemm_fprop_nvfp4", "dequantize_w_nvfp4", "gemm_dgrad_bf16_dequantized"]
@@ -253,6 +279,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "launch": "eager" if args.eager else "hip_graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
