@@ -159,7 +159,9 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
  *   codes   two E2M1 codes per byte, even element in the low nibble
  *   gscales PER_ROW/PER_TENSOR: written; GIVEN: read (caller's S >= 0)
  * With PER_TENSOR the call enqueues an extra read pass over x for A, using
- * gscales[0] as its accumulator; gscales must not alias x, codes or scales.
+ * gscales[0] as its accumulator (between the two kernels it holds A tagged
+ * with bit 31; once the call's work completes it holds S); gscales must not
+ * alias x, codes or scales.
  * Shapes: cols % 16 == 0 (ROW); rows % 16 == 0 and cols % 16 == 0 (COL,
  * TILE).  Alignment: x, codes 16-byte aligned, ld_x*2 and ld_codes_bytes
  * multiples of 16; gscales 4-byte aligned.

@@ -140,20 +140,22 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   hipStream_t st = S(stream);
   const bool sr = rnd == MXQ_ROUND_SR;
   hipError_t e = hipSuccess;
+  // per-tensor: the amax kernel leaves a tagged amax in gscales[0], which the
+  // quantize kernel turns into S (and stores back)
   if (gs == MXQ_GS_PER_TENSOR) {
     e = mxq::launch_nvfp4_tensor_scale(x, rows, cols, ld_x, gscales, st);
-    if (e == hipSuccess) e = mxq::launch_nvfp4_finalize(gscales, st);
     if (e != hipSuccess) return hip_status(e, "nvfp4_quantize (tensor amax)");
   }
+  const int gmode = gs == MXQ_GS_PER_ROW ? 0 : gs == MXQ_GS_PER_TENSOR ? 1 : 2;
   if (block == MXQ_BLOCK_ROW)
     e = mxq::launch_nvfp4_row(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                              gs == MXQ_GS_PER_ROW ? 0 : 1, mfma, sr, seed, stream_id, tensor_tag, st);
+                              gmode, mfma, sr, seed, stream_id, tensor_tag, st);
   else if (block == MXQ_BLOCK_TILE)
     e = mxq::launch_nvfp4_tile16(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                                 sr, seed, stream_id, tensor_tag, st);
+                                 gmode, sr, seed, stream_id, tensor_tag, st);
   else
-    e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales, sr,
-                              seed, stream_id, tensor_tag, st);
+    e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
+                              gmode, sr, seed, stream_id, tensor_tag, st);
   return hip_status(e, "nvfp4_quantize");
 }
 

@@ -130,6 +130,21 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int mask) {
 }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Max over the 64 lanes of a wave (every lane active), wave-uniform result:
+// DPP quad permutes [1,0,3,2] and [2,3,0,1], then half-row and row mirrors
+// give each 16-lane row its max; four lane reads combine the rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return umax(umax(a, b), umax(c, d));
+}
+
 // MFMA scale layout (1D blocks): chunks of 32 rows x 4 blocks, 128 bytes.
 __device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t blocks_per_row,
                                                 bool mfma) {

@@ -15,21 +15,23 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
                              bool mfma, hipStream_t st);
 
+// per-tensor amax: zeroes gscale[0], then leaves the tensor amax there tagged
+// with bit 31 (the quantize kernel decodes it and writes S back)
 hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                      float* gscale, hipStream_t st);
-hipError_t launch_nvfp4_finalize(float* gscale, hipStream_t st);
-// gmode: 0 = per row (computed), 1 = per tensor / given (read from gscales[0])
+// gmode: 0 = per row (computed), 1 = per tensor (tagged amax in gscales[0]),
+// 2 = given (S in gscales[0])
 hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                             int gmode, bool mfma, bool sr, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st);
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                               const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                               float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st);
 hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                            const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                            float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st);
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,

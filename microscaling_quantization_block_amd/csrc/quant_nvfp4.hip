@@ -26,9 +26,12 @@
 //     a 16x16 tile.
 //   * nvfp4_col_kernel: each lane owns 4 columns x 16 rows, each column one
 //     16x1 block, written into the transposed copy.
-//   * amax kernels for the per-tensor scale: an unsigned atomic max on the
-//     magnitude bits (exact and order-independent), then one thread turns A
-//     into S in place.
+//   * per-tensor scale: a one-thread kernel zeroes gscale[0], then an
+//     unsigned atomic max on the magnitude bits (exact and order-independent)
+//     leaves A there tagged with bit 31.  The quantize kernel that follows
+//     decodes it (S = A / 2688) and every block writes the same S back, so
+//     gscale[0] ends as S whatever order the blocks run in, and a block that
+//     reads after another's write-back sees S itself (untagged).
 
 #include "mxq_device.h"
 #include "mxq_kernels.h"
@@ -69,18 +72,17 @@ __device__ __forceinline__ uint32_t e2m1_rne_pair(uint32_t old, float a, float b
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
+// A block whose scale code is 0 has r = 0, and x * 0 is the signed zero of
+// the (finite) input, so zero blocks need no separate path.
 template <bool SR>
-__device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, bool zero_block, u32x4 draws) {
+__device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, u32x4 draws) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t d[4] = {draws.x, draws.y, draws.z, draws.w};
   float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-    float ya = a * r, yb = b * r;
-    if (zero_block) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
-    y[2 * i] = ya;
-    y[2 * i + 1] = yb;
+    y[2 * i] = bf16_lo(w[i]) * r;
+    y[2 * i + 1] = bf16_hi(w[i]) * r;
   }
   if (SR) {
     uint32_t out = 0;
@@ -108,52 +110,94 @@ __device__ __forceinline__ uint32_t amax8_bits(uint4 v) {
   return m << 16;
 }
 
+// Second-level scale of a tensor-scaled call.  gmode 1: gscale[0] holds the
+// tagged amax (bit 31 set) or, once some block wrote it back, S itself.
+// gmode 2: S given by the caller.
+__device__ __forceinline__ float tensor_scale(const float* g, int gmode) {
+  const uint32_t v = __float_as_uint(g[0]);
+  if (gmode == 1 && (v >> 31)) return __uint_as_float(v & 0x7FFFFFFFu) / 2688.0f;
+  return __uint_as_float(v);
+}
+
 // ------------------------------------------------------------ ROW (1x16)
-// gmode: 0 = per row (S computed here and stored), 1 = per tensor / given
-// (S read from gscale[0]).  One wave per row, CPT chunks of 8 per lane.
-template <int CPT, bool SR>
+// gmode: 0 = per row (S computed here and stored), 1 = per tensor (tagged
+// amax, see tensor_scale), 2 = given.  One wave per row; lane owns the
+// 16-value blocks b = lane + 64k (k < BPT): two 16-byte loads, the block amax
+// and scale chain in the lane, 8 code bytes out.  Each wave walks rows row0,
+// row0 + W, ... (W = waves in the grid) with the next row's loads in flight
+// while the current one is encoded; a prefetch past the end is clamped to
+// the last row (a valid address, never used).  FULL: every lane's blocks
+// exist (cols == 1024 BPT).
+template <int BPT, bool SR, bool FULL>
 __global__ __launch_bounds__(256) void nvfp4_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
     uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;                       // whole wave leaves together
-  const int64_t cpr = cols >> 3;
-  const uint16_t* xr = x + row * ld_x;
-  uint4 v[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    int64_t c = lane + 64 * k;
-    v[k] = c < cpr ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
-  }
-  float S;
-  if (gmode == 0) {
-    uint32_t mb = 0;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) mb = umax(mb, amax8_bits(v[k]));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mb = umax(mb, lane_xor_u32(mb, o));
-    S = __uint_as_float(mb) / 2688.0f;
-    if (lane == 0) gscales[row] = S;
-  } else {
-    S = gscales[0];
-  }
   const int64_t bpr = cols >> 4;
+  float St = 0.0f;
+  if (gmode != 0) {
+    St = tensor_scale(gscales, gmode);
+    if (gmode == 1 && threadIdx.x == 0) gscales[0] = St;
+  }
+  auto load = [&](int64_t r, uint4 (*v)[2]) {
+    const uint16_t* xr = x + (r < rows ? r : rows - 1) * ld_x;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    int64_t c = lane + 64 * k;                   // chunk; block = c >> 1
-    uint32_t ab = amax8_bits(v[k]);
-    float a = __uint_as_float(umax(ab, lane_xor_u32(ab, 1)));
-    if (c < cpr) {
-      BlockScale bs = nv_block_scale(a, S);
-      u32x4 dr = {0, 0, 0, 0};
-      if (SR) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
-      uint32_t q = nv_encode8<SR>(v[k], bs.r, bs.code == 0, dr);
-      *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
-      if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)bs.code;
+    for (int k = 0; k < BPT; ++k) {
+      const int64_t b = lane + 64 * k;
+      const int64_t bb = FULL ? b : (b < bpr ? b : bpr - 1);
+      v[k][0] = *reinterpret_cast<const uint4*>(xr + bb * 16);
+      v[k][1] = *reinterpret_cast<const uint4*>(xr + bb * 16 + 8);
     }
+  };
+  auto process = [&](int64_t r, uint4 (*v)[2]) {
+    uint32_t ab[BPT];
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      ab[k] = umax(amax8_bits(v[k][0]), amax8_bits(v[k][1]));
+      if (!FULL && lane + 64 * k >= bpr) ab[k] = 0;
+    }
+    float S = St;
+    if (gmode == 0) {
+      uint32_t mb = ab[0];
+#pragma unroll
+      for (int k = 1; k < BPT; ++k) mb = umax(mb, ab[k]);
+      S = __uint_as_float(wave_max_u32(mb)) / 2688.0f;
+      if (lane == 0) gscales[r] = S;
+    }
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int64_t b = lane + 64 * k;
+      if (FULL || b < bpr) {
+        const BlockScale bs = nv_block_scale(__uint_as_float(ab[k]), S);
+        u32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+        if (SR) {
+          const uint64_t n = (uint64_t)(r * cols + b * 16) >> 3;
+          d0 = philox_draws8(n, seed, stream_id, tensor_tag);
+          d1 = philox_draws8(n + 1, seed, stream_id, tensor_tag);
+        }
+        const uint32_t q0 = nv_encode8<SR>(v[k][0], bs.r, d0);
+        const uint32_t q1 = nv_encode8<SR>(v[k][1], bs.r, d1);
+        *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = make_uint2(q0, q1);
+        bscales[scale_offset(r, b, bpr, mfma_layout)] = (uint8_t)bs.code;
+      }
+    }
+  };
+  uint4 va[BPT][2], vb[BPT][2];
+  load(row, va);
+  while (true) {                                 // trip count uniform across the wave
+    load(row + W, vb);
+    process(row, va);
+    row += W;
+    if (row >= rows) break;
+    load(row + W, va);
+    process(row, vb);
+    row += W;
+    if (row >= rows) break;
   }
 }
 
@@ -180,7 +224,8 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     S = __uint_as_float(mb) / 2688.0f;
     if (lane == 0) gscales[row] = S;
   } else {
-    S = gscales[0];
+    S = tensor_scale(gscales, gmode);
+    if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
   }
   const int64_t bpr = cols >> 4;
   for (int64_t c0 = 0; c0 < cpr; c0 += 64) {     // uniform trip count across the wave
@@ -192,7 +237,7 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
       BlockScale bs = nv_block_scale(a, S);
       u32x4 dr = {0, 0, 0, 0};
       if (SR) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
-      uint32_t q = nv_encode8<SR>(v, bs.r, bs.code == 0, dr);
+      uint32_t q = nv_encode8<SR>(v, bs.r, dr);
       *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
       if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)bs.code;
     }
@@ -200,36 +245,45 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
 }
 
 // ------------------------------------------------------------ TILE (16x16)
-// Lane owns columns [8j, 8j+8) of a 16-row strip; lanes 2i, 2i+1 form tile i.
+// A wave covers 16 chunk columns (128 columns) x 16 rows: lane = 16 rg + jj
+// owns columns [8j, 8j+8) of rows 4rg..4rg+3 of the strip, and the 8 lanes
+// {16 rg + 2t, 16 rg + 2t + 1 : rg = 0..3} form tile t (amax by three lane
+// exchanges).  Consecutive lanes read consecutive 16-byte chunks of a row.
 template <bool SR>
-__global__ __launch_bounds__(64) void nvfp4_tile16_kernel(
+__global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
-    const float* __restrict__ gscales, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+    float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id,
+    uint32_t tensor_tag) {
+  const int lane = threadIdx.x & 63;
   const int64_t cpr = cols >> 3;
-  const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;    // chunk column
-  const int64_t r0 = (int64_t)blockIdx.y * 16;
+  const int64_t j = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + (lane & 15);
+  const int rg = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * 16 + rg * 4;
   const bool valid = j < cpr;
-  uint4 v[16];
+  const int64_t jc = valid ? j : cpr - 1;        // a valid address; data unused
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + jc * 8);
   uint32_t mb = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = valid ? *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + j * 8) : make_uint4(0, 0, 0, 0);
-    mb = umax(mb, amax8_bits(v[i]));
-  }
-  float m = __uint_as_float(umax(mb, lane_xor_u32(mb, 1)));
+  for (int i = 0; i < 4; ++i) mb = umax(mb, amax8_bits(v[i]));
+  mb = umax(mb, lane_xor_u32(mb, 1));
+  mb = umax(mb, lane_xor_u32(mb, 16));
+  mb = umax(mb, lane_xor_u32(mb, 32));
+  const float S = tensor_scale(gscales, gmode);
+  if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
   if (!valid) return;
-  const float S = gscales[0];
-  BlockScale bs = nv_block_scale(m, S);
+  const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t r = r0 + i;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + i;
     u32x4 dr = {0, 0, 0, 0};
     if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
-    uint32_t q = nv_encode8<SR>(v[i], bs.r, bs.code == 0, dr);
+    const uint32_t q = nv_encode8<SR>(v[i], bs.r, dr);
     *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
   }
-  if ((j & 1) == 0) bscales[(r0 >> 4) * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
+  if ((j & 1) == 0 && rg == 0) bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
 }
 
 // ------------------------------------------------------------ COL (16x1)
@@ -239,12 +293,13 @@ template <bool SR>
 __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
-    const float* __restrict__ gscales, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+    float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
   const int64_t q4 = cols >> 2;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * 16;
+  const float S = tensor_scale(gscales, gmode);
+  if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
   if (j >= q4) return;
-  const float S = gscales[0];
   uint2 v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint2*>(x + (r0 + i) * ld_x + j * 4);
@@ -347,14 +402,10 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t b = umax(umax(wm[0], wm[1]), umax(wm[2], wm[3]));
-    atomicMax(out_bits, b << 16);     // binary32 bits of the BF16 magnitude
+    atomicMax(out_bits, (b << 16) | 0x80000000u);   // tagged binary32 bits of the magnitude
   }
 }
 
-__global__ void nv_finalize_scale(float* g) {
-  float A = __uint_as_float(*reinterpret_cast<uint32_t*>(g));
-  g[0] = A / 2688.0f;
-}
 
 // ------------------------------------------------------------ launchers
 hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -370,30 +421,31 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
-hipError_t launch_nvfp4_finalize(float* gscale, hipStream_t st) {
-  hipLaunchKernelGGL(nv_finalize_scale, dim3(1), dim3(1), 0, st, gscale);
-  return hipGetLastError();
-}
 
 template <bool SR>
 static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                                int gmode, bool mfma, uint64_t seed, uint32_t sid, uint32_t tag,
                                hipStream_t st) {
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  const int64_t cpr = cols / 8;
-#define MXQ_ROW(CPT)                                                                         \
-  hipLaunchKernelGGL((nvfp4_row_kernel<CPT, SR>), grid, block, 0, st, x, rows, cols, ld_x,   \
-                     codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag)
-  if (cpr <= 64) MXQ_ROW(1);
-  else if (cpr <= 128) MXQ_ROW(2);
-  else if (cpr <= 256) MXQ_ROW(4);
-  else if (cpr <= 512) MXQ_ROW(8);
-  else if (cpr <= 1024) MXQ_ROW(16);
-  else
-    hipLaunchKernelGGL((nvfp4_row_long_kernel<SR>), grid, block, 0, st, x, rows, cols, ld_x, codes,
-                       ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
-#undef MXQ_ROW
+  // at most 512 workgroups of 4 waves (8 waves per CU); a wave walks
+  // rows / 2048 rows with the next row's loads in flight
+  int64_t blocks = (rows + 3) / 4;
+  if (blocks > 512) blocks = 512;
+  dim3 grid((unsigned)blocks), block(256);
+  const int64_t bpr = cols / 16;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
+                       gscales, gmode, (int)mfma, seed, sid, tag);
+  };
+  if (bpr == 64) go(nvfp4_row_kernel<1, SR, true>);
+  else if (bpr < 64) go(nvfp4_row_kernel<1, SR, false>);
+  else if (bpr == 128) go(nvfp4_row_kernel<2, SR, true>);
+  else if (bpr < 128) go(nvfp4_row_kernel<2, SR, false>);
+  else if (bpr == 256) go(nvfp4_row_kernel<4, SR, true>);
+  else if (bpr < 256) go(nvfp4_row_kernel<4, SR, false>);
+  else if (bpr == 512) go(nvfp4_row_kernel<8, SR, true>);
+  else if (bpr < 512) go(nvfp4_row_kernel<8, SR, false>);
+  else go(nvfp4_row_long_kernel<SR>);
   return hipGetLastError();
 }
 
@@ -409,31 +461,30 @@ hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                               const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                               float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st) {
-  // one wave per workgroup: a 16-row strip of 512 columns (small weights
-  // still spread over many CUs)
+  // four waves per workgroup, each 128 columns of a 16-row strip
   dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
   if (sr)
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(64), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
   else
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(64), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                            const float* gscales, bool sr, uint64_t seed, uint32_t sid,
+                            float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st) {
   dim3 grid((unsigned)((cols / 4 + 255) / 256), (unsigned)(rows / 16));
   if (sr)
     hipLaunchKernelGGL((nvfp4_col_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
   else
     hipLaunchKernelGGL((nvfp4_col_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, seed, sid, tag);
+                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
   return hipGetLastError();
 }
 
