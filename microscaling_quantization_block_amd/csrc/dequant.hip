@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
       uint32_t word = w[i >> 1] >> (16 * (i & 1));
       float a = __builtin_ldexpf(e4m3_to_f32(word & 0xFF), e);
       float b = __builtin_ldexpf(e4m3_to_f32((word >> 8) & 0xFF), e);
-      o[i] = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+      o[i] = f32x2_to_bf16x2(a, b);
     }
     *reinterpret_cast<uint4*>(out + r * ld_out + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void dq_nvfp4_kernel(
       float vb = (cb & 8) ? -e2m1_mag(cb & 7) : e2m1_mag(cb & 7);
       float pa = va * sb, pb = vb * sb;      // exact
       float da = pa * S, db = pb * S;        // one rounding each
-      o[i] = f32_to_bf16_rne(da) | (f32_to_bf16_rne(db) << 16);
+      o[i] = f32x2_to_bf16x2(da, db);
     }
     uint16_t* dst = out + r * ld_out + b * 16;
     *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
       float u0 = bf16_lo(uw[i]), u1 = bf16_hi(uw[i]);
       float h0 = g0 / (1.0f + expf(-g0)) * u0;
       float h1 = g1 / (1.0f + expf(-g1)) * u1;
-      o[i] = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+      o[i] = f32x2_to_bf16x2(h0, h1);
     }
     *reinterpret_cast<uint4*>(h + r * ld_h + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }

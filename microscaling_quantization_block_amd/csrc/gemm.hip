@@ -711,34 +711,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // ------------------------------------------------ epilogue
   // With B as the MFMA's first operand, lane l holds for its output row
   // m = l % 32 the columns 8g + 4(l / 32) + i, i = 0..3, in acc[4g + i].
+  // Each wave stages one 32-row slab of its tile at a time in its own LDS
+  // region (BF16, rows padded by 8 bytes), then reads it back row-wise so
+  // that 8 lanes store one contiguous 128-byte run of C.
+  __syncthreads();                       // every wave is past its last LDS read
+  constexpr int EROW = WN * 2 + 8;       // bytes per staged row
+  constexpr int ECH = WN / 8;            // 16-byte chunks per row
+  constexpr int ERI = 64 / ECH;          // rows per read-back instruction
+  static_assert(8 * 32 * EROW <= 2 * STAGE_BYTES, "epilogue staging");
+  uint8_t* const E = lds + wave * (32 * EROW);
   float sbg = 1.0f;
   if (PATH == P_F16) sbg = p.b_gs[to.group];
-  const bool vec_ok = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0);
+  const bool vec16 = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const int64_t m = to.m0 + wm * WM + tm * 32 + (lane & 31);
-    if (m >= to.m_end) continue;
     float sa = 1.0f;
-    if (PATH == P_F16) sa = p.a_gs_per_row ? p.a_gs[sa_row[tm]] : p.a_gs[0];
-    uint16_t* crow = p.c + m * p.ldc;
+    if (PATH == P_F16) {
+      const int64_t srow = sa_row[tm];
+      sa = srow >= 0 ? (p.a_gs_per_row ? p.a_gs[srow] : p.a_gs[0]) : 0.0f;
+    }
+    uint8_t* const er = E + (lane & 31) * EROW + (lane >> 5) * 8;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
+    for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + tn * 32 + g * 8 + (lane >> 5) * 4;
-        uint32_t o[4];
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = acc[tm][tn][4 * g + i];
-          if (PATH == P_F16) v = (v * sa) * sbg;
-          o[i] = f32_to_bf16_rne(v);
+          v[i] = acc[tm][tn][4 * g + i];
+          if (PATH == P_F16) v[i] = (v[i] * sa) * sbg;
         }
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-        } else {
+        *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
+            make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (n + i < N) crow[n + i] = (uint16_t)o[i];
+    for (int it = 0; it < 32 / ERI; ++it) {
+      const int rr = it * ERI + lane / ECH, cc = lane % ECH;
+      const uint4 val = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+      const int64_t m = to.m0 + wm * WM + tm * 32 + rr;
+      const int n = n0 + wn * WN + cc * 8;
+      if (m < to.m_end) {
+        uint16_t* const dst = p.c + m * p.ldc + n;
+        if (vec16 && n + 7 < N) {
+          *reinterpret_cast<uint4*>(dst) = val;
+        } else {
+          const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) dst[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
         }
       }
     }

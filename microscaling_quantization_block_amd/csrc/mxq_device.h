@@ -16,10 +16,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Round a binary32 value to BF16, nearest-even (finite or infinite inputs;
 // a finite value that rounds past the largest BF16 becomes infinity).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two binary32 values to packed BF16 (a in the low half), round to nearest
+// even, by the hardware conversion: on MI355X it matches the integer rounding
+// (u + 0x7FFF + lsb) >> 16 on every tie and neighbour pattern of every BF16
+// value (subnormals, overflow to infinity included) and on 2^30 strided
+// patterns; NaN stays NaN.
+typedef __bf16 mxq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mxq_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const mxq_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mxq_bf16x2));
 }
 
 // |x| of both BF16 halves, then the larger as a 16-bit magnitude pattern.
