@@ -192,6 +192,7 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
                              bool mfma, hipStream_t st) {
   dim3 grid((unsigned)((cols + TCOLS - 1) / TCOLS), (unsigned)(rows / TROWS));
+  if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   if (mode == 0)
     hipLaunchKernelGGL((mxfp8_tile_kernel<0>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
                        codes, ld_codes, scales, codes_col, ld_codes_col, scales_col, (int)mfma);

@@ -445,7 +445,11 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
   else if (bpr < 256) go(nvfp4_row_kernel<4, SR, false>);
   else if (bpr == 512) go(nvfp4_row_kernel<8, SR, true>);
   else if (bpr < 512) go(nvfp4_row_kernel<8, SR, false>);
-  else go(nvfp4_row_long_kernel<SR>);
+  else
+    // one wave per row (no row loop in this kernel)
+    hipLaunchKernelGGL(nvfp4_row_long_kernel<SR>, dim3((unsigned)((rows + 3) / 4)), block, 0, st, x,
+                       rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed,
+                       sid, tag);
   return hipGetLastError();
 }
 
@@ -465,6 +469,7 @@ hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, in
                                uint32_t tag, hipStream_t st) {
   // four waves per workgroup, each 128 columns of a 16-row strip
   dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
+  if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   if (sr)
     hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
                        codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
@@ -479,6 +484,7 @@ hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64
                             float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st) {
   dim3 grid((unsigned)((cols / 4 + 255) / 256), (unsigned)(rows / 16));
+  if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   if (sr)
     hipLaunchKernelGGL((nvfp4_col_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
                        codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);

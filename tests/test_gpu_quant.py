@@ -183,6 +183,33 @@ def test_nvfp4_config2_activations_full_size():
     _nv_check_row(m, x, m.GScale.PER_ROW)
 
 
+@pytest.mark.parametrize("shape", [(5000, 2048), (2100, 8208)])
+@pytest.mark.parametrize("gs", ["per_row", "per_tensor"])
+def test_nvfp4_row_many_rows_sampled(shape, gs):
+    """More rows than waves in the grid (each wave walks several rows, an odd
+    count for some), and rows longer than 8192 (the two-pass kernel).  Rows
+    are independent given S, so the oracle runs on sampled rows: per row, or
+    with the tensor's S (the exact binary32 amax / 2688) given."""
+    m = mxq()
+    R, C = shape
+    x = F.bf16_rne(np.random.default_rng(31).standard_normal(shape) *
+                   np.exp(np.random.default_rng(32).standard_normal((R, 1))))
+    say(f"nvfp4 ROW {gs} {shape} sampled rows")
+    g = m.GScale.PER_ROW if gs == "per_row" else m.GScale.PER_TENSOR
+    c, s, S = m.nvfp4_quantize(to_dev_bf16(x), gs=g)
+    rows = sorted({0, 1, 2047, 2048, 2049, 4095, 4096, R - 2, R - 1} & set(range(R)))
+    v = _vals(x[rows])
+    if gs == "per_row":
+        rc, rs, rS = ON.quantize_rowwise(v, "per_row")
+        assert np.array_equal(to_np(S)[rows], rS)
+    else:
+        S_t = np.float32(np.float32(np.abs(_vals(x)).max()) / np.float32(2688.0))
+        assert to_np(S)[0] == S_t
+        rc, rs, rS = ON.quantize_rowwise(v, "given", S_given=S_t)
+    assert np.array_equal(to_np(s)[rows], rs)
+    assert np.array_equal(to_np(c)[rows], rc)
+
+
 @pytest.mark.parametrize("gs", ["per_tensor", "given"])
 def test_nvfp4_row_tensor_scale(gs):
     m = mxq()
