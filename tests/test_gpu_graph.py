@@ -1,7 +1,7 @@
 """HIP-graph capture of the hot path: a captured step (per-token NVFP4 Q(X),
 per-tensor 16x16 Q(W) with its amax kernels, FPROP, DQ(W), dequantized DGRAD,
-plus an MXFP8 DUAL quantization and an SR quantization) replayed several
-times, with the program's own eager work and synchronizations between the
+plus an MXFP8 DUAL quantization and an SR quantization), on one stream or
+with the weight path forked to a second stream, replayed several times, with the program's own eager work and synchronizations between the
 replays, must reproduce the eager step's bytes exactly on every replay.  The
 library records no memset, so every node is a kernel."""
 
@@ -60,7 +60,33 @@ def _bytes(t):
     return t.contiguous().view(torch.uint8).cpu().numpy().copy()
 
 
-def test_captured_step_replays_match_eager():
+def _step_two_streams(m, x, w, dy, o, side):
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        m.nvfp4_quantize(w, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=o["cw"],
+                         block_scales=o["sw"], gscales=o["Sw"])
+        done = torch.cuda.Event()
+        done.record(side)
+        m.mx_dequantize(m.Format.NVFP4, o["cw"], o["sw"], N, K, block=m.Block.TILE, gscales=o["Sw"],
+                        gs=m.GScale.PER_TENSOR, out=o["wdq"])
+    m.nvfp4_quantize(x, gs=m.GScale.PER_ROW, codes=o["cx"], block_scales=o["sx"], gscales=o["Sx"])
+    main.wait_event(done)
+    m.mx_gemm(m.Operand(m.Format.NVFP4, o["cx"], o["sx"], o["Sx"], gs=m.GScale.PER_ROW),
+              m.Operand(m.Format.NVFP4, o["cw"], o["sw"], o["Sw"], block=m.Block.TILE,
+                        gs=m.GScale.PER_TENSOR), M, N, K, out=o["y"])
+    main.wait_stream(side)
+    m.mx_gemm(m.Operand(m.Format.BF16, dy, block=m.Block.NONE),
+              m.Operand(m.Format.BF16, o["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
+              out=o["dx"])
+    m.mx_quantize(x, block=m.Block.DUAL, codes=o["mc"], scales=o["ms"], codes_col=o["mcc"],
+                  scales_col=o["msc"])
+    m.nvfp4_quantize(dy, gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=7, codes=o["gc"],
+                     block_scales=o["gs"], gscales=o["gS"])
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_captured_step_replays_match_eager(two_streams):
     import microscaling_quantization_block_amd as m
     say(f"graph capture of the NVFP4 linear step {M}x{K}x{N}")
     x = to_dev_bf16(_bf16((M, K), 1.0, 1))
@@ -73,8 +99,12 @@ def test_captured_step_replays_match_eager():
 
     cap = _outputs("cuda")
     g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()                          # default priority
     with torch.cuda.graph(g):
-        _step(m, x, w, dy, cap)
+        if two_streams:
+            _step_two_streams(m, x, w, dy, cap, side)   # weight path forked to a second stream
+        else:
+            _step(m, x, w, dy, cap)
     torch.cuda.synchronize()
 
     other = _outputs("cuda")
