@@ -198,6 +198,187 @@ def cpu_baseline(data, min_seconds):
                 seconds_per_step=round(t_step, 3))
 
 
+# ---------------------------------------------------------------- --rows
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def _time_us(torch, fn, iters, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
+
+
+def rows_report():
+    """Each hot-path row at the other configurations' shapes: quantizers and
+    dequantizers against HBM bandwidth, GEMMs against their dtype's MFMA
+    peak, the MoE stages of the Qwen3-30B-A3B-shaped layer.  One JSON line
+    per measurement (HIP events around repeated launches, inputs resident)."""
+    import numpy as np
+    import torch
+    import microscaling_quantization_block_amd as m
+    import synth
+    dev = "cuda"
+
+    def out(row, what, shape, us, nbytes=None, flops=None, peak=None, fp4=False):
+        d = dict(row=row, what=what, shape=shape, us=round(us, 2))
+        if nbytes is not None:
+            gbps = nbytes / (us * 1e-6) / 1e9
+            d.update(bytes=int(nbytes), GBps=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                     frac=round(gbps / PEAK_HBM_GBPS, 4), bound="hbm")
+        else:
+            tf = flops / (us * 1e-6) / 1e12
+            d.update(flops=int(flops), TFLOPs=round(tf, 1), peak=peak, unit="TFLOP/s",
+                     frac=round(tf / peak, 4), bound="mfma")
+            if fp4:
+                d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
+        print(json.dumps(d), flush=True)
+
+    # ---- Llama-3-8B-shaped dense MLP, NVFP4 (tokens 32768, hidden 4096, I 14336)
+    T5, H5, I5 = 32768, 4096, 14336
+    x5 = synth.torch_normal_bf16((T5, H5), 1.0, 51, dev)
+    n = T5 * H5
+    cx, sx, Sx = m.nvfp4_quantize(x5)
+    out("a1-a3", "nvfp4 1x16 per-token RNE (X)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
+        x5, codes=cx, block_scales=sx, gscales=Sx), 10), nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
+    dy5 = synth.torch_normal_bf16((T5, H5), 1e-3, 52, dev)          # down-projection output gradient
+    cg, sg, Sg = m.nvfp4_quantize(dy5, rnd=m.Round.SR)
+    out("a1-a3", "nvfp4 1x16 per-token SR (dY)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
+        dy5, rnd=m.Round.SR, codes=cg, block_scales=sg, gscales=Sg), 10), nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
+    cgc, sgc, Sgc = m.nvfp4_quantize(dy5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1)
+    out("a1-a3", "nvfp4 16x1 columnwise per-tensor SR (dY^T, WGRAD)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
+        dy5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1, codes=cgc,
+        block_scales=sgc, gscales=Sgc), 10), nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
+    w5 = synth.torch_normal_bf16((2 * I5, H5), 0.02, 53, dev)       # gate_up weight [N, K]
+    nw = w5.numel()
+    cw, sw, Sw = m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    out("a1-a3", "nvfp4 16x16 per-tensor (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
+        w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=cw, block_scales=sw, gscales=Sw), 10),
+        nbytes=2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    wdq = torch.empty_like(w5)
+    out("a4", "nvfp4 dequantize 16x16 -> bf16 (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.mx_dequantize(
+        m.Format.NVFP4, cw, sw, 2 * I5, H5, block=m.Block.TILE, gscales=Sw, gs=m.GScale.PER_TENSOR, out=wdq), 10),
+        nbytes=nw // 2 + nw // 256 + 4 + nw * 2)
+    y5 = torch.empty((T5, 2 * I5), dtype=torch.bfloat16, device=dev)
+    f = 2.0 * T5 * 2 * I5 * H5
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    out("a6", "nvfp4 FPROP gate_up", [T5, 2 * I5, H5], _time_us(torch, lambda: m.mx_gemm(A, B, T5, 2 * I5, H5, out=y5), 3),
+        flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
+    del y5, wdq
+    dyg = synth.torch_normal_bf16((T5, 2 * I5), 1e-3, 54, dev)       # gate_up output gradient
+    cdg, sdg, Sdg = m.nvfp4_quantize(dyg, rnd=m.Round.SR)
+    dx5 = torch.empty((T5, H5), dtype=torch.bfloat16, device=dev)
+    Bt = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=True)
+    Ad = m.Operand(m.Format.NVFP4, cdg, sdg, Sdg, gs=m.GScale.PER_ROW)
+    out("a6", "nvfp4 DGRAD gate_up (16x16 weight read transposed)", [T5, H5, 2 * I5],
+        _time_us(torch, lambda: m.mx_gemm(Ad, Bt, T5, H5, 2 * I5, out=dx5), 3), flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
+    ccg, scg, Scg = m.nvfp4_quantize(dyg, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1)
+    ccx, scx, Scx = m.nvfp4_quantize(x5, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    dw = torch.empty((2 * I5, H5), dtype=torch.bfloat16, device=dev)
+    Ag = m.Operand(m.Format.NVFP4, ccg, scg, Scg, gs=m.GScale.PER_TENSOR)
+    Bx = m.Operand(m.Format.NVFP4, ccx, scx, Scx, gs=m.GScale.PER_TENSOR)
+    out("a6", "nvfp4 WGRAD gate_up (columnwise copies)", [2 * I5, H5, T5],
+        _time_us(torch, lambda: m.mx_gemm(Ag, Bx, 2 * I5, H5, T5, out=dw), 3), flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
+    del x5, dy5, w5, dyg, cdg, ccg, dx5, dw, cx, cg, cgc, cw, ccx
+    torch.cuda.empty_cache()
+
+    # ---- Qwen3-8B-shaped dense MLP, MXFP8 (tokens 8192, hidden 4096, I 12288)
+    T4, H4, I4 = 8192, 4096, 12288
+    x4 = synth.torch_normal_bf16((T4, H4), 1.0, 41, dev)
+    n = T4 * H4
+    mc, ms = m.mx_quantize(x4)
+    out("a1-a3", "mxfp8 1x32 (X)", [T4, H4], _time_us(torch, lambda: m.mx_quantize(x4, codes=mc, scales=ms), 10),
+        nbytes=n * 2 + n + n // 32)
+    d4 = m.mx_quantize(x4, block=m.Block.DUAL)
+    out("a1-a3", "mxfp8 dual rowwise + columnwise (X)", [T4, H4], _time_us(torch, lambda: m.mx_quantize(
+        x4, block=m.Block.DUAL, codes=d4[0], scales=d4[1], codes_col=d4[2], scales_col=d4[3]), 10),
+        nbytes=n * 2 + 2 * n + 2 * (n // 32))
+    w4 = synth.torch_normal_bf16((2 * I4, H4), 0.02, 43, dev)
+    nw = w4.numel()
+    wc, wsc = m.mx_quantize(w4, block=m.Block.TILE)
+    out("a1-a3", "mxfp8 32x32 (W_gate_up)", [2 * I4, H4], _time_us(torch, lambda: m.mx_quantize(
+        w4, block=m.Block.TILE, codes=wc, scales=wsc), 10), nbytes=nw * 2 + nw + nw // 1024)
+    xo = torch.empty_like(x4)
+    out("a4", "mxfp8 dequantize 1x32 -> bf16 (X)", [T4, H4], _time_us(torch, lambda: m.mx_dequantize(
+        m.Format.MXFP8, mc, ms, T4, H4, out=xo), 10), nbytes=n + n // 32 + n * 2)
+    y4 = torch.empty((T4, 2 * I4), dtype=torch.bfloat16, device=dev)
+    f = 2.0 * T4 * 2 * I4 * H4
+    A = m.Operand(m.Format.MXFP8, mc, ms)
+    B = m.Operand(m.Format.MXFP8, wc, wsc, block=m.Block.TILE)
+    out("a5", "mxfp8 FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(A, B, T4, 2 * I4, H4, out=y4), 5),
+        flops=f, peak=PEAK_FP8_TFLOPS)
+    dyg4 = synth.torch_normal_bf16((T4, 2 * I4), 1e-3, 44, dev)
+    dd = m.mx_quantize(dyg4, block=m.Block.DUAL)
+    dx4 = torch.empty((T4, H4), dtype=torch.bfloat16, device=dev)
+    out("a5", "mxfp8 DGRAD gate_up (32x32 weight read transposed)", [T4, H4, 2 * I4], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(m.Format.MXFP8, dd[0], dd[1]), m.Operand(m.Format.MXFP8, wc, wsc, block=m.Block.TILE, transposed=True),
+        T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
+    dw4 = torch.empty((2 * I4, H4), dtype=torch.bfloat16, device=dev)
+    out("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(m.Format.MXFP8, dd[2], dd[3]), m.Operand(m.Format.MXFP8, d4[2], d4[3]), 2 * I4, H4, T4, out=dw4), 5),
+        flops=f, peak=PEAK_FP8_TFLOPS)
+    del x4, w4, dyg4, dd, d4, y4, dx4, dw4, xo
+    torch.cuda.empty_cache()
+
+    # ---- Qwen3-30B-A3B-shaped MoE layer, NVFP4 (tokens 8192, hidden 2048, 128 experts, I 768, top-8)
+    d = synth.config3()
+    T3, H3 = d["x"].shape
+    E, N2, _ = d["w_gu"].shape
+    I3 = N2 // 2
+    lg = d["logits"]
+    top = np.argsort(-lg, axis=1, kind="stable")[:, :d["topk"]]          # host routing
+    pairs = np.stack([np.repeat(np.arange(T3), d["topk"]), top.reshape(-1)], axis=1)
+    order = np.lexsort((pairs[:, 0], pairs[:, 1]))
+    row_token = pairs[order, 0].astype(np.int32)
+    off = np.zeros(E + 1, dtype=np.int32)
+    np.add.at(off, pairs[:, 1] + 1, 1)
+    off = np.cumsum(off).astype(np.int32)
+    Mr = len(row_token)
+
+    def bf(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x3 = bf(d["x"])
+    cx3, sx3, Sx3 = m.nvfp4_quantize(x3)
+    wgu = bf(d["w_gu"].reshape(E * N2, H3)).view(E, N2, H3)
+    wdn = bf(d["w_dn"].reshape(E * H3, I3)).view(E, H3, I3)
+    cgu = torch.empty((E, N2, H3 // 2), dtype=torch.uint8, device=dev)
+    sgu = torch.empty((E, N2, H3 // 16), dtype=torch.uint8, device=dev)
+    Sgu = torch.empty(E, dtype=torch.float32, device=dev)
+    cdn = torch.empty((E, H3, I3 // 2), dtype=torch.uint8, device=dev)
+    sdn = torch.empty((E, H3, I3 // 16), dtype=torch.uint8, device=dev)
+    Sdn = torch.empty(E, dtype=torch.float32, device=dev)
+    for e in range(E):
+        m.nvfp4_quantize(wgu[e], gs=m.GScale.PER_TENSOR, codes=cgu[e], block_scales=sgu[e], gscales=Sgu[e:e + 1])
+        m.nvfp4_quantize(wdn[e], gs=m.GScale.PER_TENSOR, codes=cdn[e], block_scales=sdn[e], gscales=Sdn[e:e + 1])
+    off_d = torch.from_numpy(off).to(dev)
+    idx_d = torch.from_numpy(row_token).to(dev)
+    A = m.Operand(m.Format.NVFP4, cx3, sx3, Sx3, gs=m.GScale.PER_ROW)
+    Bgu = m.Operand(m.Format.NVFP4, cgu.view(E * N2, H3 // 2), sgu, Sgu, gs=m.GScale.PER_TENSOR)
+    gu = torch.empty((Mr, N2), dtype=torch.bfloat16, device=dev)
+    out("a8", "MoE grouped gate_up (row gather, 128 experts)", [Mr, N2, H3], _time_us(torch, lambda: m.mx_gemm(
+        A, Bgu, Mr, N2, H3, out=gu, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T3), 10),
+        flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS)
+    h = torch.empty((Mr, I3), dtype=torch.bfloat16, device=dev)
+    out("a8", "MoE SwiGLU", [Mr, I3], _time_us(torch, lambda: m.mx_swiglu(gu, I3, out=h), 10),
+        nbytes=Mr * N2 * 2 + Mr * I3 * 2)
+    ch, sh, Sh = m.nvfp4_quantize(h)
+    out("a8", "MoE per-token Q(H)", [Mr, I3], _time_us(torch, lambda: m.nvfp4_quantize(
+        h, codes=ch, block_scales=sh, gscales=Sh), 10), nbytes=Mr * I3 * 2 + Mr * I3 // 2 + Mr * I3 // 16 + Mr * 4)
+    Bdn = m.Operand(m.Format.NVFP4, cdn.view(E * H3, I3 // 2), sdn, Sdn, gs=m.GScale.PER_TENSOR)
+    y3 = torch.empty((Mr, H3), dtype=torch.bfloat16, device=dev)
+    out("a8", "MoE grouped down", [Mr, H3, I3], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(m.Format.NVFP4, ch, sh, Sh, gs=m.GScale.PER_ROW), Bdn, Mr, H3, I3, out=y3,
+        group_row_offsets=off_d), 10), flops=2.0 * Mr * H3 * I3, peak=PEAK_F16_TFLOPS)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +392,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="capture the weight path (Q(W), DQ(W)) on a second stream (measured "
                          "slower on MI355X: 83.0 vs 73.7 us per step)")
+    ap.add_argument("--rows", action="store_true",
+                    help="only time each hot-path row at the other configurations' shapes "
+                         "(one JSON line per measurement)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -229,6 +413,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.rows:
+        rows_report()
         return
     m.lib()
     log("generating synthetic inputs (seeded)")
