@@ -78,32 +78,21 @@ __device__ __forceinline__ uint32_t f32_to_e2m1_rne(float y) {
 }
 
 // Stochastic rounding onto the E2M1 grid: with lo <= |y| < hi the grid
-// neighbours, round up iff r16 < (|y| - lo) / (hi - lo) * 2^16 (exact: the
-// difference is exact and the step is a power of two); |y| >= 6 gives 6.
+// neighbours, round up iff r16 < (|y| - lo) / (hi - lo) * 2^16; |y| >= 6
+// gives 6.  Branch-free: t = |y| * {2, 1, 1/2} on [0, 2), [2, 4), [4, 6)
+// puts the neighbours of every range one apart, so the lower code is
+// floor(t) + {0, 2, 4} and the fraction is t - floor(t); every step is exact
+// (power-of-two scalings of a binary32 value and its floor).
 __device__ __forceinline__ uint32_t f32_to_e2m1_sr(float y, uint32_t r16) {
-  uint32_t b = __float_as_uint(y);
-  uint32_t s = (b >> 28) & 8u;
-  float a = __uint_as_float(b & 0x7FFFFFFFu);
-  // lower neighbour code: truncate onto the grid
-  uint32_t lo;
-  float lov, step;
-  if (a < 2.0f) {
-    lo = (uint32_t)(a * 2.0f);          // 0..3 (0, 0.5, 1, 1.5)
-    lov = 0.5f * (float)lo;
-    step = 0.5f;
-  } else if (a < 4.0f) {
-    uint32_t k = (uint32_t)a;           // 2 or 3
-    lo = k + 2u;                        // codes 4 (2.0), 5 (3.0)
-    lov = (float)k;
-    step = 1.0f;
-  } else {
-    lo = 6u;                            // 4.0
-    lov = 4.0f;
-    step = 2.0f;
-  }
-  float f = (a - lov) * (65536.0f / step);   // exact
-  uint32_t mag = ((float)r16 < f) ? lo + 1u : lo;
-  mag = a >= 6.0f ? 7u : mag;
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t s = (b >> 28) & 8u;
+  const float a = __uint_as_float(b & 0x7FFFFFFFu);
+  const bool lt2 = a < 2.0f, lt4 = a < 4.0f;
+  const float t = a * (lt2 ? 2.0f : lt4 ? 1.0f : 0.5f);
+  const float fl = __builtin_floorf(t);
+  const uint32_t lo = (uint32_t)fl + (lt2 ? 0u : lt4 ? 2u : 4u);
+  const bool up = (float)r16 < (t - fl) * 65536.0f;
+  const uint32_t mag = a >= 6.0f ? 7u : lo + (up ? 1u : 0u);
   return s | mag;
 }
 
@@ -116,9 +105,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-    uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
-    uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
-    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    // one 32x32->64 product gives both halves
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
   }
   return c;
 }
