@@ -620,7 +620,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   //    loads are unconditional (past the end they are range-checked to zero),
   //    so the compiler can keep the other set's loads outstanding across the
   //    LDS stores instead of draining them.
-  //  DIST == 1: the next stage's loads are in flight during the compute.
+  //  DIST == 1: the next stage's loads (and MXFP8 scales) are in flight
+  //    during the compute.
   uint8_t* const L0 = lds;
   uint8_t* const L1 = lds + STAGE_BYTES;
   if constexpr (PP) {
@@ -694,17 +695,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     }
     if (kt < nk) compute(L0, 0);          // odd stage count: the last stage
   } else {
+    // one register staging set; unrolled by two so that the MXFP8 scale set
+    // of stage s (s % 2) is loaded a stage ahead, not right before its MFMAs
     load_stage(0, 0);
+    load_scales(0, 0);
     store_stage(L0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      uint8_t* const Lc = (kt & 1) ? L1 : L0;
-      uint8_t* const Ln = (kt & 1) ? L0 : L1;
+    for (int kt = 0; kt < nk; kt += 2) {
       load_stage(kt + 1, 0);
-      load_scales(kt, 0);
-      compute(Lc, 0);
-      store_stage(Ln, 0);
+      load_scales(kt + 1, 1);
+      compute(L0, 0);
+      store_stage(L1, 0);
       __syncthreads();
+      if (kt + 1 < nk) {
+        load_stage(kt + 2, 0);
+        load_scales(kt + 2, 0);
+        compute(L1, 1);
+        store_stage(L0, 0);
+        __syncthreads();
+      }
     }
   }
 
