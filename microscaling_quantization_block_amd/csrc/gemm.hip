@@ -195,8 +195,16 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 // workgroup barrier): group 0 computes stage p/2 (p even) or stores its half
 // of stage p/2 + 1 (p odd); group 1 the reverse.  Stage t lives in LDS buffer
 // t % 2, is written in phases 2t-2 and 2t-1 and read in phases 2t and 2t+1.
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
+//
+// SDW (MXFP8, K % 128 == 0): a stage's four 32-wide scale blocks of one row
+// are four adjacent bytes in every scale layout, so each lane loads them as
+// one word, shifts its half's byte to the bottom (byte h, 2 + h) and the MFMA
+// selects byte 0 or 2 of that word (its scale byte select) for K step 0 or 1.
+// Transposed B keeps byte loads (its blocks are a scale-row apart).
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
+  static_assert(!SDW || PATH == P_FP8, "scale words are an MXFP8 path");
+  constexpr bool SDWB = SDW && !BT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int NT = 64 * WGM * WGN;
   static_assert(!PP || (NT == 512 && DIST == 1 && WGM % 2 == 0), "ping-pong: 8 waves, one staging set");
@@ -373,20 +381,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 
   auto load_scales = [&](int kt, int set) {
     if (PATH == P_FP8) {
+      // (the word of blocks 4kt..4kt+3 starts hl bytes before block 4kt + hl)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TM; ++tm) {
+        if constexpr (SDW) {
+          const bool ok = sa_ok[tm] && kt * 4 < nb32;
+          sa_[set][tm][0] = bload4(rAs, in_range(ok, sa_off[tm][0] - hl + (uint32_t)kt * a_sstep)) >> (8 * hl);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bool ok = sa_ok[tm] && kt * 4 + ks * 2 + hl < nb32;
-          sa_[set][tm][ks] = bload1(rAs, in_range(ok, sa_off[tm][ks] + (uint32_t)kt * a_sstep));
+          for (int ks = 0; ks < 2; ++ks) {
+            const bool ok = sa_ok[tm] && kt * 4 + ks * 2 + hl < nb32;
+            sa_[set][tm][ks] = bload1(rAs, in_range(ok, sa_off[tm][ks] + (uint32_t)kt * a_sstep));
+          }
         }
+      }
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
+      for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (SDWB) {
+          const bool ok = sb_ok[tn] && kt * 4 < nb32;
+          sb_[set][tn][0] = bload4(rBs, in_range(ok, sb_off[tn][0] - hl + (uint32_t)kt * sb_step)) >> (8 * hl);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bool ok = sb_ok[tn] && kt * 4 + ks * 2 + hl < nb32;
-          sb_[set][tn][ks] = bload1(rBs, in_range(ok, sb_off[tn][ks] + (uint32_t)kt * sb_step));
+          for (int ks = 0; ks < 2; ++ks) {
+            const bool ok = sb_ok[tn] && kt * 4 + ks * 2 + hl < nb32;
+            sb_[set][tn][ks] = bload1(rBs, in_range(ok, sb_off[tn][ks] + (uint32_t)kt * sb_step));
+          }
         }
+      }
     }
   };
 
@@ -569,9 +590,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[q][tn], af[q][tm], acc[tm][tn], 0, 0, 0, (int)sb_[set][tn][ks], 0,
-                (int)sa_[set][tm][ks]);
+          {
+            const int sbv = (int)sb_[set][tn][SDWB ? 0 : ks], sav = (int)sa_[set][tm][SDW ? 0 : ks];
+            if (ks == 0)
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bf[q][tn], af[q][tm], acc[tm][tn], 0, 0, 0, sbv, 0, sav);
+            else
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bf[q][tn], af[q][tm], acc[tm][tn], 0, 0, SDWB ? 2 : 0, sbv, SDW ? 2 : 0, sav);
+          }
         if (FS == 2) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -776,13 +803,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------ launcher
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false>
-static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
+
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW>
+static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_n = (a.N + BN - 1) / BN;
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)(BM + BN) * LDS_ROW;
-  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP>;
+  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -791,6 +821,13 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * WGM * WGN), lds, st, a);
   return hipGetLastError();
+}
+
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
+static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+  if constexpr (PATH == P_FP8)
+    if ((a.K >> 5) % 4 == 0) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
+  return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false>(a, st);
 }
 
 static int64_t tile_count(const GemmArgs& a, int bm, int bn) {
