@@ -281,11 +281,14 @@ def test_gemm_is_deterministic():
 
 @pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
 @pytest.mark.parametrize("bt", [False, True])
-def test_gemm_large_tile_variants(path, bt):
+@pytest.mark.parametrize("K", [256, 288])
+def test_gemm_large_tile_variants(path, bt, K):
     """M = N = 4096 selects the largest tiles (256x256, or 256x128 for MXFP8);
-    checked on 256 sampled rows spread over every m-tile, all columns."""
+    checked on 256 sampled rows spread over every m-tile, all columns.  K = 288
+    ends on half a stage (and, for MXFP8, a scale count that is not a multiple
+    of four words), so the loaders' ragged-K paths run on these tiles too."""
     m = mxq()
-    M, N, K = 4096, 4096, 256
+    M, N = 4096, 4096
     x = _bf16((M, K), 1.0, 40)
     w = _bf16((N, K), 0.02, 41)
     wt = np.ascontiguousarray(w.T)                   # stored [K, N] for the transposed case
