@@ -248,6 +248,24 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b,
                    const int32_t* a_row_index, void* stream);
 
 /*
+ * mx_gemm_set_tile -- force the workgroup tile of every later mx_gemm call in
+ * the process (a tuning and test aid; the default is the measured choice).
+ *   tile  -1  the measured choice per path and shape (default)
+ *          0  128x128, 4 waves (2x2), two staging sets
+ *          1  128x128, 8 waves (2x4), two staging sets
+ *          2  256x128, 8 waves (4x2), one staging set
+ *          3  256x256, 8 waves (2x4), one staging set
+ *          4  128x128, 8 waves in two ping-pong groups
+ *          5  256x128, 8 waves in two ping-pong groups
+ *          6  256x256, 8 waves in two ping-pong groups
+ * Every configuration computes the same result bit for bit (the K order of
+ * the accumulation does not depend on the tile).  Returns MXQ_EINVAL outside
+ * [-1, 6].  Not synchronised with launches already queued: it applies to
+ * calls made after it returns.
+ */
+mxq_status mx_gemm_set_tile(int32_t tile);
+
+/*
  * mx_swiglu -- h = silu(g) * u for a [rows, 2*inter] BF16 gate_up output
  * (gate = first inter columns, up = last inter columns), computed in binary32
  * with silu(g) = g / (1 + exp(-g)), stored as BF16 RNE [rows, inter].

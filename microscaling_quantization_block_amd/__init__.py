@@ -3,7 +3,8 @@ library.  Argument marshalling only: every step of the hot path runs in the
 library's HIP kernels.  PyTorch supplies device memory and the current stream.
 
 The names and arguments follow the C ABI in include/mxq.h:
-    mx_quantize, nvfp4_quantize, mx_dequantize, mx_gemm, mx_swiglu
+    mx_quantize, nvfp4_quantize, mx_dequantize, mx_gemm, mx_swiglu,
+    mx_gemm_set_tile
 Outputs the caller does not pass are allocated here with torch (the library
 itself never allocates).  Every call is asynchronous on the current stream.
 
@@ -18,7 +19,7 @@ import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
            "mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu",
-           "library_path", "lib"]
+           "mx_gemm_set_tile", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmxq.so")
@@ -86,7 +87,8 @@ def lib():
     L.mx_gemm.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
-    for f in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu"):
+    L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
+    for f in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
     L.mxq_status_str.restype = ctypes.c_char_p
@@ -236,3 +238,10 @@ def mx_swiglu(gu, inter, out=None, stream=None):
     _check(lib().mx_swiglu(_ptr(gu), rows, inter, gu.stride(0), _ptr(out), out.stride(0),
                            _stream(stream)))
     return out
+
+
+def mx_gemm_set_tile(tile):
+    """Force the GEMM workgroup tile of every later mx_gemm call in the process
+    (0..6, as listed at mx_gemm_set_tile in include/mxq.h), or restore the
+    measured choice with -1."""
+    _check(lib().mx_gemm_set_tile(int(tile)))

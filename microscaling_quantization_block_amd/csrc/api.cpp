@@ -325,4 +325,10 @@ mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld
   return hip_status(mxq::launch_swiglu(gu, rows, inter, ld_gu, h, ld_h, S(stream)), "mx_swiglu");
 }
 
+mxq_status mx_gemm_set_tile(int32_t tile) {
+  if (tile < -1 || tile > 6) return fail(MXQ_EINVAL, "mx_gemm_set_tile: tile %d outside [-1, 6]", (int)tile);
+  mxq::gemm_set_tile((int)tile);
+  return ok();
+}
+
 }  // extern "C"

@@ -40,6 +40,8 @@
 #include "mxq_device.h"
 #include "mxq_kernels.h"
 
+#include <atomic>
+
 namespace mxq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -126,8 +128,48 @@ struct TileOrigin {
   bool active;
 };
 
+// Grouped launches: group g owns ceil(rows_g / BM) m-tiles, in group order.
+// The offsets are read by the whole wave at once: lane l takes groups
+// base + 4l .. base + 4l + 3 of each 256-group chunk (five offsets, one
+// round of loads), and a wave prefix sum of the per-lane tile counts places
+// the chunk.  Every wave computes the same wave-uniform result.
+struct GroupChunk {
+  int o[5];        // offsets[base + 4l + u], u = 0..4 (clamped to the last)
+  int cnt;         // m-tiles of this lane's (up to) four groups
+  int incl;        // inclusive prefix sum of cnt over lanes 0..l
+};
+
 template <int BM>
-__device__ __forceinline__ TileOrigin tile_origin(const GemmArgs& p, int mt) {
+__device__ __forceinline__ GroupChunk group_chunk(const GemmArgs& p, int base, int lane) {
+  GroupChunk c;
+  const int G = p.num_groups;
+  const int g0 = base + 4 * lane;
+#pragma unroll
+  for (int u = 0; u < 5; ++u) c.o[u] = p.offsets[min(g0 + u, G)];
+  c.cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (g0 + u < G) c.cnt += (c.o[u + 1] - c.o[u] + BM - 1) / BM;
+  c.incl = c.cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(c.incl, d, 64);
+    if (lane >= d) c.incl += y;
+  }
+  return c;
+}
+
+// total m-tiles over all groups (wave-uniform)
+template <int BM>
+__device__ __forceinline__ int group_mtiles(const GemmArgs& p, int lane) {
+  int total = 0;
+  for (int base = 0; base < p.num_groups; base += 256)
+    total += __shfl(group_chunk<BM>(p, base, lane).incl, 63, 64);
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+template <int BM>
+__device__ __forceinline__ TileOrigin tile_origin(const GemmArgs& p, int mt, int lane) {
   TileOrigin o;
   if (p.num_groups == 0) {
     o.m0 = (int64_t)mt * BM;
@@ -136,24 +178,39 @@ __device__ __forceinline__ TileOrigin tile_origin(const GemmArgs& p, int mt) {
     o.active = o.m0 < p.M;
     return o;
   }
-  // walk the groups: group g owns ceil(rows_g / BM) m-tiles
-  int acc = 0;
   o.active = false;
   o.group = 0;
   o.m0 = 0;
   o.m_end = 0;
-  for (int g = 0; g < p.num_groups; ++g) {
-    int lo = p.offsets[g], hi = p.offsets[g + 1];
-    int t = (hi - lo + BM - 1) / BM;
-    if (mt < acc + t) {
-      o.group = g;
-      o.m0 = lo + (int64_t)(mt - acc) * BM;
-      o.m_end = hi;
-      o.active = true;
+  int acc = 0;                                   // m-tiles of the chunks before
+  for (int base = 0; base < p.num_groups; base += 256) {
+    const GroupChunk c = group_chunk<BM>(p, base, lane);
+    const uint64_t hit = __ballot(mt < acc + c.incl);
+    if (hit) {
+      const int L = __builtin_ctzll(hit);       // first lane whose groups reach mt
+      int t0 = acc + __shfl(c.incl - c.cnt, L, 64);
+      int ov[5];
+#pragma unroll
+      for (int u = 0; u < 5; ++u) ov[u] = __shfl(c.o[u], L, 64);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = (ov[u + 1] - ov[u] + BM - 1) / BM;   // zero past the last group
+        if (!o.active && mt < t0 + t) {
+          o.group = base + 4 * L + u;
+          o.m0 = ov[u] + (int64_t)(mt - t0) * BM;
+          o.m_end = ov[u + 1];
+          o.active = true;
+        }
+        t0 += t;
+      }
       break;
     }
-    acc += t;
+    acc += __shfl(c.incl, 63, 64);
   }
+  o.group = __builtin_amdgcn_readfirstlane(o.group);
+  o.m0 = __builtin_amdgcn_readfirstlane((int)o.m0);
+  o.m_end = __builtin_amdgcn_readfirstlane((int)o.m_end);
+  o.active = __builtin_amdgcn_readfirstlane((int)o.active) != 0;
   return o;
 }
 
@@ -218,16 +275,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int KSTEP = PATH == P_FP8 ? 128 : 64;          // K elements per stage
 
   // ---- XCD-aware tile id: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of logical tiles.
+  // contiguous range of the real tiles.  A grouped grid is sized for the most
+  // m-tiles any split of M could need; its real count comes from the offsets,
+  // and each XCD's surplus workgroups (the last in its dispatch order) exit,
+  // so the real tiles are spread over all eight XCDs.
+  const int lane0 = threadIdx.x & 63;
   const int tiles_n = gridDim.x;
-  const int G = gridDim.x * gridDim.y;
+  const int tiles_m = p.num_groups ? group_mtiles<BM>(p, lane0) : (int)gridDim.y;
+  const int G = tiles_m * tiles_n;
   const int b = blockIdx.y * gridDim.x + blockIdx.x;
   const int q8 = G >> 3, r8 = G & 7, x = b & 7;
+  if ((b >> 3) >= q8 + (x < r8 ? 1 : 0)) return;
   const int logical = x * q8 + (x < r8 ? x : r8) + (b >> 3);
   const int nt = logical % tiles_n;
   const int mt = logical / tiles_n;
 
-  const TileOrigin to = tile_origin<BM>(p, mt);
+  const TileOrigin to = tile_origin<BM>(p, mt, lane0);
   if (!to.active) return;
   // Every operand is below 2^31 bytes (checked by the host), so K, N, row
   // indices and byte offsets inside A, B and their scales fit 32 bits.
@@ -835,9 +898,11 @@ static int64_t tile_count(const GemmArgs& a, int bm, int bn) {
   return tm * ((a.N + bn - 1) / bn);
 }
 
-#ifndef MXQ_TILE_OVERRIDE
-#define MXQ_TILE_OVERRIDE -1
-#endif
+// Forced tile configuration (the case numbers of launch_p), or -1 for the
+// measured choice.  Process-wide; set through mx_gemm_set_tile.
+static std::atomic<int> g_tile_override{-1};
+
+void gemm_set_tile(int tile) { g_tile_override.store(tile, std::memory_order_relaxed); }
 
 // Tile choice: the largest tile that still gives every CU work.  Larger wave
 // tiles need fewer LDS fragment bytes per MFMA; 8-wave workgroups put two
@@ -845,16 +910,22 @@ static int64_t tile_count(const GemmArgs& a, int bm, int bn) {
 template <int PATH, bool BT>
 static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
   const int64_t cus = 256;
-  int t = MXQ_TILE_OVERRIDE;
+  int t = g_tile_override.load(std::memory_order_relaxed);
   if (t < 0) {
-    // measured on MI355X (8192^3, 8192x28672x4096, 4096x768x2048,
-    // 4096x2048x768, 2048x2048x4096): NVFP4 prefers 256x256 ping-pong on
-    // large GEMMs and the 8-wave 128x128 tile otherwise; BF16 prefers
-    // ping-pong 256x128 / 128x128; MXFP8 the 8-wave 256x128 tile.
+    // measured on MI355X (8192^3, 8192x24576x4096, 8192x28672x4096,
+    // 8192x1536x2048, 4096x768x2048, 4096x2048x768, grouped 128 x 512 rows):
+    // the ping-pong 256x256 tile runs a tile in about 2.5x the time of the
+    // 8-wave 128x128 tile for 4x the work, so NVFP4 takes it whenever its
+    // rounds of tiles over the CUs cost less (5 * rounds <= 2 * rounds of
+    // 128x128), transposed B included; BF16 takes it once it fills the CUs,
+    // else ping-pong 256x128 / 128x128; MXFP8 takes ping-pong 256x128 once
+    // that fills the CUs, else the 8-wave 128x128 tile.
+    const int64_t r6 = (tile_count(a, 256, 256) + cus - 1) / cus;
+    const int64_t r1 = (tile_count(a, 128, 128) + cus - 1) / cus;
     const bool big = tile_count(a, 256, 256) >= cus, mid = tile_count(a, 256, 128) >= cus;
-    if (PATH == P_F16) t = big ? (BT ? 5 : 6) : 1;      // transposed 256x256 would spill
-    else if (PATH == P_BF16) t = mid ? 5 : 4;
-    else t = mid ? 2 : 1;
+    if (PATH == P_F16) t = 5 * r6 <= 2 * r1 ? 6 : 1;
+    else if (PATH == P_BF16) t = big ? 6 : mid ? 5 : 4;
+    else t = mid ? 5 : 1;
   }
   switch (t) {
     case 6: return launch_t<PATH, 256, 256, BT, 1, 4, 2, true>(a, st);

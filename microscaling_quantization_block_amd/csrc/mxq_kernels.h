@@ -70,5 +70,6 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int path, bool b_transposed, const GemmArgs& a, hipStream_t st);
+void gemm_set_tile(int tile);   // -1 = measured choice, 0..6 = forced configuration
 
 }  // namespace mxq

@@ -124,3 +124,10 @@ def test_dequantize_and_swiglu_reject_bad_arguments():
     assert L.mx_dequantize(F.BF16, FAKE, 64, FAKE, None, 32, 64, B.ROW, G.NONE, Lay.LINEAR, FAKE, 64, None) == 1
     assert L.mx_swiglu(FAKE, 4, 12, 24, FAKE, 12, None) == 2
     assert L.mx_swiglu(FAKE_ODD, 4, 16, 32, FAKE, 16, None) == 3
+
+
+def test_gemm_set_tile_range():
+    m, L = _lib()
+    assert L.mx_gemm_set_tile(7) == 1 and "outside" in _err(L)
+    assert L.mx_gemm_set_tile(-2) == 1
+    assert L.mx_gemm_set_tile(-1) == 0                # the default; no device work

@@ -279,21 +279,11 @@ def test_gemm_is_deterministic():
     assert np.array_equal(o1, o2)
 
 
-@pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
-@pytest.mark.parametrize("bt", [False, True])
-@pytest.mark.parametrize("K", [256, 288])
-def test_gemm_large_tile_variants(path, bt, K):
-    """M = N = 4096 selects the largest tiles (256x256, or 256x128 for MXFP8);
-    checked on 256 sampled rows spread over every m-tile, all columns.  K = 288
-    ends on half a stage (and, for MXFP8, a scale count that is not a multiple
-    of four words), so the loaders' ragged-K paths run on these tiles too."""
-    m = mxq()
-    M, N = 4096, 4096
-    x = _bf16((M, K), 1.0, 40)
-    w = _bf16((N, K), 0.02, 41)
+def _path_operands(m, path, bt, x, w):
+    """A (rowwise x) and B (w [N, K]; stored [K, N] and read transposed when
+    bt) on the GPU for one path, with the oracle's float64 / binary32
+    dequantized copies of both as [M, K] and [N, K]."""
     wt = np.ascontiguousarray(w.T)                   # stored [K, N] for the transposed case
-    say(f"large-tile GEMM {path} bt={bt} {M}x{N}x{K}")
-    rows = np.sort(np.random.default_rng(42).choice(M, 256, replace=False))
     if path == "mxfp8":
         cx, sx = m.mx_quantize(to_dev_bf16(x))
         a64 = OM.dequantize_f64(to_np(cx), to_np(sx))
@@ -324,6 +314,155 @@ def test_gemm_large_tile_variants(path, bt, K):
         B = m.Operand(m.Format.BF16, to_dev_bf16(wt if bt else w), block=m.Block.NONE, transposed=bt)
         a64 = a32 = F.bf16_bits_to_f64(x)
         b64 = b32 = F.bf16_bits_to_f64(w)
+    return A, B, (a64, a32, b64, b32)
+
+
+@pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
+@pytest.mark.parametrize("bt", [False, True])
+@pytest.mark.parametrize("K", [256, 288])
+def test_gemm_large_tile_variants(path, bt, K):
+    """M = N = 4096 selects the largest tiles (256x256, or 256x128 for MXFP8);
+    checked on 256 sampled rows spread over every m-tile, all columns.  K = 288
+    ends on half a stage (and, for MXFP8, a scale count that is not a multiple
+    of four words), so the loaders' ragged-K paths run on these tiles too."""
+    m = mxq()
+    M, N = 4096, 4096
+    x = _bf16((M, K), 1.0, 40)
+    w = _bf16((N, K), 0.02, 41)
+    say(f"large-tile GEMM {path} bt={bt} {M}x{N}x{K}")
+    rows = np.sort(np.random.default_rng(42).choice(M, 256, replace=False))
+    A, B, (a64, a32, b64, b32) = _path_operands(m, path, bt, x, w)
     out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
     frob, worst, ok = G.check(out[rows], a64[rows], b64, a32[rows], b32)
     assert ok, f"frobenius {frob:.3e}, worst {worst:.3f}"
+
+
+@pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
+@pytest.mark.parametrize("bt", [False, True])
+@pytest.mark.parametrize("K", [320, 384])
+def test_every_tile_configuration_gives_the_same_bits(path, bt, K):
+    """All seven workgroup tiles (forced with mx_gemm_set_tile) on one ragged
+    problem: the measured default is checked against the oracle, and every
+    forced tile must return the same BF16 bits (each output element sums its
+    K products in the same order whatever the tile)."""
+    m = mxq()
+    M, N = 600, 416                                  # ragged M; N, K multiples of the 32x32 tiles
+    x = _bf16((M, K), 1.0, 60)
+    w = _bf16((N, K), 0.02, 61)
+    A, B, (a64, a32, b64, b32) = _path_operands(m, path, bt, x, w)
+    say(f"tile sweep {path} bt={bt} {M}x{N}x{K}")
+    ref = m.mx_gemm(A, B, M, N, K)
+    _assert_gemm(ref, a64, b64, a32, b32)
+    ref = from_dev_bf16(ref)
+    try:
+        for t in range(7):
+            m.mx_gemm_set_tile(t)
+            out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
+            assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
+    finally:
+        m.mx_gemm_set_tile(-1)
+
+
+@pytest.mark.parametrize("path", ["mxfp8", "nvfp4", "bf16"])
+def test_every_tile_configuration_grouped(path):
+    """The grouped launch (three experts, one of them empty, gathered A rows)
+    under every forced tile returns the default's bits, and the default
+    matches the oracle expert by expert."""
+    import torch
+    m = mxq()
+    T, N, K, E = 300, 160, 256, 3
+    off = np.array([0, 230, 230, 410], dtype=np.int32)
+    M = int(off[-1])
+    idx = np.random.default_rng(70).integers(0, T, M).astype(np.int32)
+    x = _bf16((T, K), 1.0, 71)
+    w = _bf16((E * N, K), 0.02, 72)
+    say(f"grouped tile sweep {path} M={M} N={N} K={K} E={E}")
+    if path == "mxfp8":
+        cx, sx = m.mx_quantize(to_dev_bf16(x))
+        A = m.Operand(m.Format.MXFP8, cx, sx)
+        a64 = a32 = OM.dequantize_f64(to_np(cx), to_np(sx))
+        cw, sw = m.mx_quantize(to_dev_bf16(w))
+        B = m.Operand(m.Format.MXFP8, cw, sw)
+        b64 = b32 = OM.dequantize_f64(to_np(cw), to_np(sw))
+    elif path == "nvfp4":
+        cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+        A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+        a64 = ON.dequantize_f64(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+        a32 = ON.dequantize_f32(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+        # one per-tensor S per expert: the grouped GEMM reads S[g] for group g
+        cw = torch.empty((E * N, K // 2), dtype=torch.uint8, device="cuda")
+        sw = torch.empty((E * N, K // 16), dtype=torch.uint8, device="cuda")
+        Sw = torch.empty(E, dtype=torch.float32, device="cuda")
+        wd = to_dev_bf16(w)
+        for e in range(E):
+            r = slice(e * N, (e + 1) * N)
+            m.nvfp4_quantize(wd[r], gs=m.GScale.PER_TENSOR, codes=cw[r], block_scales=sw[r],
+                             gscales=Sw[e:e + 1])
+        B = m.Operand(m.Format.NVFP4, cw, sw, Sw, gs=m.GScale.PER_TENSOR)
+        b64 = np.concatenate([ON.dequantize_f64(to_np(cw[e * N:(e + 1) * N]), to_np(sw[e * N:(e + 1) * N]),
+                                                to_np(Sw[e:e + 1]), "1x16", "per_tensor") for e in range(E)])
+        b32 = np.concatenate([ON.dequantize_f32(to_np(cw[e * N:(e + 1) * N]), to_np(sw[e * N:(e + 1) * N]),
+                                                to_np(Sw[e:e + 1]), "1x16", "per_tensor") for e in range(E)])
+    else:
+        A = m.Operand(m.Format.BF16, to_dev_bf16(x), block=m.Block.NONE)
+        B = m.Operand(m.Format.BF16, to_dev_bf16(w), block=m.Block.NONE)
+        a64 = a32 = F.bf16_bits_to_f64(x)
+        b64 = b32 = F.bf16_bits_to_f64(w)
+    off_d = torch.from_numpy(off).cuda()
+    idx_d = torch.from_numpy(idx).cuda()
+    run = lambda: from_dev_bf16(m.mx_gemm(A, B, M, N, K, group_row_offsets=off_d,
+                                          a_row_index=idx_d, a_rows=T))
+    ref = run()
+    for g in range(E):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            rows = idx[lo:hi]
+            frob, worst, ok = G.check(ref[lo:hi], a64[rows], b64[g * N:(g + 1) * N],
+                                      a32[rows], b32[g * N:(g + 1) * N])
+            assert ok, f"expert {g}: frobenius {frob:.3e}, worst {worst:.3f}"
+    try:
+        for t in range(7):
+            m.mx_gemm_set_tile(t)
+            out = run()
+            assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
+    finally:
+        m.mx_gemm_set_tile(-1)
+
+
+def test_grouped_many_groups_and_empty_ones():
+    """600 groups (three chunks of the device-side group scan) with 0..40 rows
+    each, a third of them empty, gathered A rows: every group matches the
+    oracle, under the measured tile and under forced 128- and 256-row tiles."""
+    import torch
+    m = mxq()
+    E, N, K, T = 600, 64, 64, 500
+    rng = np.random.default_rng(80)
+    rows = rng.integers(0, 41, E)
+    rows[rng.random(E) < 0.33] = 0
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    M = int(off[-1])
+    idx = rng.integers(0, T, M).astype(np.int32)
+    x = _bf16((T, K), 1.0, 81)
+    w = _bf16((E * N, K), 0.05, 82)
+    say(f"grouped GEMM with {E} groups, M={M}")
+    A = m.Operand(m.Format.BF16, to_dev_bf16(x), block=m.Block.NONE)
+    B = m.Operand(m.Format.BF16, to_dev_bf16(w), block=m.Block.NONE)
+    off_d = torch.from_numpy(off).cuda()
+    idx_d = torch.from_numpy(idx).cuda()
+    x64, w64 = F.bf16_bits_to_f64(x), F.bf16_bits_to_f64(w)
+    run = lambda: from_dev_bf16(m.mx_gemm(A, B, M, N, K, group_row_offsets=off_d,
+                                          a_row_index=idx_d, a_rows=T))
+    ref = run()
+    for g in range(E):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            a = x64[idx[lo:hi]]
+            b = w64[g * N:(g + 1) * N]
+            frob, worst, ok = G.check(ref[lo:hi], a, b, a, b)
+            assert ok, f"group {g}: frobenius {frob:.3e}, worst {worst:.3f}"
+    try:
+        for t in (1, 6):
+            m.mx_gemm_set_tile(t)
+            assert np.array_equal(run(), ref), f"tile {t}"
+    finally:
+        m.mx_gemm_set_tile(-1)
