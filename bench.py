@@ -305,6 +305,10 @@ def rows_report():
     wc, wsc = m.mx_quantize(w4, block=m.Block.TILE)
     out("a1-a3", "mxfp8 32x32 (W_gate_up)", [2 * I4, H4], _time_us(torch, lambda: m.mx_quantize(
         w4, block=m.Block.TILE, codes=wc, scales=wsc), 10), nbytes=nw * 2 + nw + nw // 1024)
+    wt4 = m.mx_quantize(w4, block=m.Block.TILE, transposed_copy=True)
+    out("a1-a3", "mxfp8 32x32 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(torch, lambda: m.mx_quantize(
+        w4, block=m.Block.TILE, codes=wt4[0], scales=wt4[1], codes_col=wt4[2], scales_col=wt4[3],
+        transposed_copy=True), 10), nbytes=nw * 2 + 2 * nw + 2 * (nw // 1024))
     xo = torch.empty_like(x4)
     out("a4", "mxfp8 dequantize 1x32 -> bf16 (X)", [T4, H4], _time_us(torch, lambda: m.mx_dequantize(
         m.Format.MXFP8, mc, ms, T4, H4, out=xo), 10), nbytes=n + n // 32 + n * 2)
@@ -320,11 +324,14 @@ def rows_report():
     out("a5", "mxfp8 DGRAD gate_up (32x32 weight read transposed)", [T4, H4, 2 * I4], _time_us(torch, lambda: m.mx_gemm(
         m.Operand(m.Format.MXFP8, dd[0], dd[1]), m.Operand(m.Format.MXFP8, wc, wsc, block=m.Block.TILE, transposed=True),
         T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
+    out("a5", "mxfp8 DGRAD gate_up (transposed 32x32 copy)", [T4, H4, 2 * I4], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(m.Format.MXFP8, dd[0], dd[1]), m.Operand(m.Format.MXFP8, wt4[2], wt4[3], block=m.Block.TILE),
+        T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
     dw4 = torch.empty((2 * I4, H4), dtype=torch.bfloat16, device=dev)
     out("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(torch, lambda: m.mx_gemm(
         m.Operand(m.Format.MXFP8, dd[2], dd[3]), m.Operand(m.Format.MXFP8, d4[2], d4[3]), 2 * I4, H4, T4, out=dw4), 5),
         flops=f, peak=PEAK_FP8_TFLOPS)
-    del x4, w4, dyg4, dd, d4, y4, dx4, dw4, xo
+    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo
     torch.cuda.empty_cache()
 
     # ---- Qwen3-30B-A3B-shaped MoE layer, NVFP4 (tokens 8192, hidden 2048, 128 experts, I 768, top-8)

@@ -117,11 +117,18 @@ typedef enum {
  *   x, ld_x            input, row-major, ld_x >= cols (elements)
  *   block              ROW: codes [rows, cols] (ld_codes), scales per layout
  *                      COL: codes [cols, rows] (ld_codes), scales [cols, rows/32]
- *                      TILE: codes [rows, cols], scales [rows/32, cols/32] LINEAR
+ *                      TILE: codes [rows, cols], scales [rows/32, cols/32] LINEAR;
+ *                            with codes_col non-NULL also the transposed copy:
+ *                            codes_col [cols, rows] (ld_codes_col) and
+ *                            scales_col [cols/32, rows/32] LINEAR.  A 32x32
+ *                            block's scale serves its rows and its columns, so
+ *                            that copy is exactly the TILE quantization of x^T
+ *                            (the weight for DGRAD, read untransposed).
  *                      DUAL: ROW copy into codes/scales AND COL copy into
  *                            codes_col/scales_col (ld_codes_col)
  *   layout             LINEAR or MFMA (MFMA: ROW/COL/DUAL only)
- *   codes_col, scales_col, ld_codes_col   DUAL only, else ignored (may be NULL)
+ *   codes_col, scales_col, ld_codes_col   DUAL (required) and TILE (optional
+ *                      transposed copy), else ignored (may be NULL)
  * Shapes: cols % 32 == 0; rows % 32 == 0 for COL, TILE, DUAL.
  * Alignment: x, codes, codes_col 16-byte aligned; ld_x*2, ld_codes and
  * ld_codes_col multiples of 16.

@@ -127,9 +127,10 @@ def _u8(shape, device):
 # ---------------------------------------------------------------- quantizers
 
 def mx_quantize(x, block=Block.ROW, layout=Layout.LINEAR, codes=None, scales=None,
-                codes_col=None, scales_col=None, stream=None):
+                codes_col=None, scales_col=None, transposed_copy=False, stream=None):
     """MXFP8 quantization of a BF16 matrix.  Returns (codes, scales) or, for
-    DUAL, (codes, scales, codes_col, scales_col)."""
+    DUAL and for TILE with transposed_copy, (codes, scales, codes_col,
+    scales_col); TILE's transposed copy is the 32x32 quantization of x^T."""
     _check_2d(x, torch.bfloat16, "x")
     rows, cols = x.shape
     dev = x.device
@@ -146,11 +147,16 @@ def mx_quantize(x, block=Block.ROW, layout=Layout.LINEAR, codes=None, scales=Non
     if block == Block.DUAL:
         codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
         scales_col = _u8((cols, max(rows // 32, 0)), dev) if scales_col is None else scales_col
+    elif block == Block.TILE and transposed_copy:
+        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
+        scales_col = _u8((cols // 32, max(rows // 32, 0)), dev) if scales_col is None else scales_col
+    else:
+        codes_col = scales_col = None
     ldc = codes.stride(0)
     ldcc = codes_col.stride(0) if codes_col is not None else 0
     _check(lib().mx_quantize(_ptr(x), rows, cols, x.stride(0), int(block), int(layout), _ptr(codes),
                              ldc, _ptr(scales), _ptr(codes_col), ldcc, _ptr(scales_col), _stream(stream)))
-    if block == Block.DUAL:
+    if codes_col is not None:
         return codes, scales, codes_col, scales_col
     return codes, scales
 

@@ -71,6 +71,10 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
   if (!x || !codes || !scales) return fail(MXQ_EINVAL, "mx_quantize: null pointer");
   if (block == MXQ_BLOCK_DUAL && (!codes_col || !scales_col))
     return fail(MXQ_EINVAL, "mx_quantize: DUAL needs codes_col and scales_col");
+  // TILE: codes_col (with scales_col) asks for the transposed copy as well
+  const bool tile_t = block == MXQ_BLOCK_TILE && codes_col;
+  if (tile_t && !scales_col) return fail(MXQ_EINVAL, "mx_quantize: a transposed TILE copy needs scales_col");
+  const bool second = block == MXQ_BLOCK_DUAL || tile_t;
   if (cols % 32) return fail(MXQ_ESHAPE, "mx_quantize: cols %% 32 != 0 (cols=%lld)", (long long)cols);
   if (block != MXQ_BLOCK_ROW && rows % 32)
     return fail(MXQ_ESHAPE, "mx_quantize: rows %% 32 != 0 for a COL/TILE/DUAL copy (rows=%lld)", (long long)rows);
@@ -84,18 +88,19 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
       return fail(MXQ_ESHAPE, "mx_quantize: MFMA layout of a columnwise copy needs rows %% 128 == 0");
   }
   const int64_t need_row = block == MXQ_BLOCK_COL ? rows : cols;
-  if (ld_x < cols || ld_codes < need_row || (block == MXQ_BLOCK_DUAL && ld_codes_col < rows))
+  if (ld_x < cols || ld_codes < need_row || (second && ld_codes_col < rows))
     return fail(MXQ_EINVAL, "mx_quantize: leading dimension smaller than the row");
   if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes % 16 ||
-      (block == MXQ_BLOCK_DUAL && (!aligned16(codes_col) || ld_codes_col % 16)))
+      (second && (!aligned16(codes_col) || ld_codes_col % 16)))
     return fail(MXQ_EALIGN, "mx_quantize: pointers and leading dimensions must be 16-byte aligned");
   hipError_t e;
   if (block == MXQ_BLOCK_ROW)
     e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, mfma, S(stream));
   else
     e = mxq::launch_mxfp8_tile(block == MXQ_BLOCK_COL ? 0 : block == MXQ_BLOCK_TILE ? 1 : 2, x,
-                               rows, cols, ld_x, codes, ld_codes, scales, codes_col, ld_codes_col,
-                               scales_col, mfma, S(stream));
+                               rows, cols, ld_x, codes, ld_codes, scales,
+                               second ? codes_col : nullptr, ld_codes_col,
+                               second ? scales_col : nullptr, mfma, S(stream));
   return hip_status(e, "mx_quantize");
 }
 

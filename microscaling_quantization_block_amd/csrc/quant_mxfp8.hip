@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void mxfp8_row_kernel(
 //  * rowwise part (ROW copy of DUAL): one thread per (row, 32-column block);
 //  * columnwise part (COL, DUAL): one thread per column, 32 rows, stored into
 //    the transposed copy as 32 contiguous bytes;
-//  * TILE: one thread per (row, block); the 32x32 amax is a 32-lane reduction.
+//  * TILE: one thread per (row, block); the 32x32 amax is a 32-lane reduction;
+//    optionally also the transposed copy (the same codes, tile grid transposed).
 constexpr int TROWS = 32, TCOLS = 256, TPAD = 8;   // pad breaks LDS bank aliasing
 
 template <int MODE>   // 0 = COL, 1 = TILE, 2 = DUAL
@@ -140,6 +141,31 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
         if (rr == 0) scales[(r0 >> 5) * (cols >> 5) + ((c0 + cc) >> 5)] = (uint8_t)s;
       } else {
         scales[scale_offset(r0 + rr, (c0 + cc) >> 5, cols >> 5, mfma_layout)] = (uint8_t)s;
+      }
+    }
+    // TILE with a transposed copy: a 32x32 tile's scale is shared by its rows
+    // and columns, so the transposed copy is the same codes transposed.  The
+    // thread of (row rr, block blk) also encodes column 32 blk + rr of the
+    // staged tile with the block's scale s (it holds s after the reduction)
+    // and writes it as 32 contiguous bytes of codes_col [cols, rows].
+    if (MODE == 1 && codes_col) {
+      const int ct = cc + rr;                        // tile column of this thread
+      if (c0 + ct < cols) {
+        uint32_t col[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          col[q] = (uint32_t)tile[2 * q][ct] | ((uint32_t)tile[2 * q + 1][ct] << 16);
+        uint32_t o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 e = mx_encode8(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
+          o[2 * q] = e.x;
+          o[2 * q + 1] = e.y;
+        }
+        uint8_t* dst = codes_col + (c0 + ct) * ld_codes_col + r0;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+        if (rr == 0) scales_col[((c0 + cc) >> 5) * (rows >> 5) + (r0 >> 5)] = (uint8_t)s;
       }
     }
   }

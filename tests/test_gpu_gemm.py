@@ -111,6 +111,11 @@ def test_mxfp8_dgrad_transposed_32x32_weight_and_wgrad():
     a64 = OM.dequantize_f64(to_np(cdy), to_np(sdy))
     w64 = OM.dequantize_f64(to_np(cw), to_np(sw), "32x32")
     _assert_gemm(dx, a64, w64.T.copy(), a64, w64.T.copy())
+    # the quantizer's transposed tile copy, read untransposed, gives the same bits
+    _, _, cwt, swt = m.mx_quantize(to_dev_bf16(w), block=m.Block.TILE, transposed_copy=True)
+    dx2 = m.mx_gemm(m.Operand(m.Format.MXFP8, cdy, sdy),
+                    m.Operand(m.Format.MXFP8, cwt, swt, block=m.Block.TILE), T, H, I)
+    assert np.array_equal(from_dev_bf16(dx2), from_dev_bf16(dx))
     # the same tile copy read untransposed serves FPROP
     y = m.mx_gemm(m.Operand(m.Format.MXFP8, cx, sx),
                   m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE), T, I, H)

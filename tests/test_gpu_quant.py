@@ -125,6 +125,11 @@ def test_mxfp8_col_tile_dual(shape):
     dqt = m.mx_dequantize(m.Format.MXFP8, *m.mx_quantize(xd, block=m.Block.TILE), shape[0], shape[1],
                           block=m.Block.TILE)
     assert np.array_equal(from_dev_bf16(dqt), OM.dequantize_bf16(tc, ts, "32x32"))
+    # TILE with its transposed copy: the oracle's 32x32 quantization of x^T
+    c, s, ct, st = m.mx_quantize(xd, block=m.Block.TILE, transposed_copy=True)
+    tct, tst = OM.quantize_tile32(np.ascontiguousarray(v.T))
+    assert np.array_equal(to_np(c), tc) and np.array_equal(to_np(s), ts)
+    assert np.array_equal(to_np(ct), tct) and np.array_equal(to_np(st), tst)
 
 
 def test_mxfp8_mfma_scale_layout_and_strided_input():
