@@ -263,10 +263,17 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 // one word, shifts its half's byte to the bottom (byte h, 2 + h) and the MFMA
 // selects byte 0 or 2 of that word (its scale byte select) for K step 0 or 1.
 // Transposed B keeps byte loads (its blocks are a scale-row apart).
+// SDW for NVFP4 (K % 64 == 0, and N % 64 == 0 for transposed B): the byte of
+// each chunk's block is read as the aligned word that holds it (a stage's four
+// blocks of a row are one word) and shifted down at the LDS store.  A byte
+// load kept in flight across the loop back edge is an 8-bit value the
+// compiler widens at the loop head, which waits for every load in flight
+// (the prefetched stage's too); a word needs no widening.
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
-  static_assert(!SDW || PATH == P_FP8, "scale words are an MXFP8 path");
-  constexpr bool SDWB = SDW && !BT;
+  static_assert(!SDW || PATH != P_BF16, "scale words: MXFP8 and NVFP4 only");
+  constexpr bool SDWB = SDW && !BT && PATH == P_FP8;
+  constexpr bool F16W = SDW && PATH == P_F16;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int NT = 64 * WGM * WGN;
   static_assert(!PP || (NT == 512 && DIST == 1 && WGM % 2 == 0), "ping-pong: 8 waves, one staging set");
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // per-lane A chunks: row, chunk, byte offset at stage 0, scale offset at stage 0
   int a_c[A_CH], a_r[A_CH];
   bool a_ok[A_CH];
-  uint32_t a_off[A_CH], a_soff[A_CH];
+  uint32_t a_off[A_CH], a_soff[A_CH], a_ssh[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int id = ltid + LT * i;
@@ -367,11 +374,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     if (a_ok[i]) src = p.row_index ? p.row_index[m] : (int)m;
     a_off[i] = (uint32_t)src * arb + (uint32_t)c * CB;
     a_soff[i] = PATH == P_F16 ? (uint32_t)scale_offset(src, c, nb16, p.a_mfma_layout) : 0u;
+    a_ssh[i] = F16W ? 8u * (a_soff[i] & 3u) : 0u;
+    if (F16W) a_soff[i] &= ~3u;
   }
   // per-lane B chunks (row-major B)
   int b_c[B_CH], b_r[B_CH];
   bool b_ok[B_CH];
-  uint32_t b_off[B_CH], b_soff[B_CH];
+  uint32_t b_off[B_CH], b_soff[B_CH], b_ssh[B_CH];
   const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
@@ -386,6 +395,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     if (PATH == P_F16 && !BT)
       b_soff[i] = p.b_tile ? (uint32_t)((n >> 4) * nb16 + c)
                            : (uint32_t)scale_offset(n, c, nb16, p.b_mfma_layout);
+    b_ssh[i] = F16W ? 8u * (b_soff[i] & 3u) : 0u;
+    if (F16W) b_soff[i] &= ~3u;
   }
   // transposed B: lane -> (k group, n group of 8), n fastest for coalesced row
   // reads; K and N are multiples of the tile size, so a group is in or out whole.
@@ -395,7 +406,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   const uint32_t bt_off = (uint32_t)(bt_kg * R_BT) * brb +
                           (PATH == P_F16 ? (uint32_t)(n0 + bt_ng * 8) / 2 : (uint32_t)(n0 + bt_ng * 8) * ESZ_BT);
   const uint32_t bt_step = (uint32_t)KSTEP * brb;
-  const uint32_t bt_soff = (uint32_t)(((bt_kg * R_BT) >> 4) * (N >> 4) + ((n0 + bt_ng * 8) >> 4));
+  const uint32_t bt_sidx = (uint32_t)(((bt_kg * R_BT) >> 4) * (N >> 4) + ((n0 + bt_ng * 8) >> 4));
+  const uint32_t bt_soff = F16W ? bt_sidx & ~3u : bt_sidx;
+  const uint32_t bt_ssh = F16W ? 8u * (bt_sidx & 3u) : 0u;
   const uint32_t bt_sstep = 4u * (uint32_t)(N >> 4);
 
   // DIST staging sets in registers: with DIST = 2 the stage being written to
@@ -504,14 +517,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       chunk(rA, in_range(ok, a_off[i] + (uint32_t)kt * ROW_STEP), ra[i]);
       // the block's scale byte, kept raw until the LDS store so that nothing
       // waits on this load before the next stage's compute
-      if (PATH == P_F16) rsa[i] = bload1(rAs, in_range(ok, a_soff[i] + (uint32_t)kt * a_sstep));
+      if (PATH == P_F16) {
+        const uint32_t so = in_range(ok, a_soff[i] + (uint32_t)kt * a_sstep);
+        rsa[i] = F16W ? bload4(rAs, so) : bload1(rAs, so);
+      }
     }
     if (!BT) {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
         const bool ok = b_ok[i] && k0 + b_c[i] * VPC < K;
         chunk(rB, in_range(ok, b_off[i] + (uint32_t)kt * ROW_STEP), rb[i]);
-        if (PATH == P_F16) rsb[i] = bload1(rBs, in_range(ok, b_soff[i] + (uint32_t)kt * b_sstep));
+        if (PATH == P_F16) {
+          const uint32_t so = in_range(ok, b_soff[i] + (uint32_t)kt * b_sstep);
+          rsb[i] = F16W ? bload4(rBs, so) : bload1(rBs, so);
+        }
       }
     } else {
       const bool ok = bt_nok && k0 + bt_kg * R_BT < K;
@@ -530,7 +549,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           rbt[q][0] = bload4(rB, oq);
         }
       }
-      if (PATH == P_F16) rbt_s = bload1(rBs, in_range(ok, bt_soff + (uint32_t)kt * bt_sstep));
+      if (PATH == P_F16) {
+        const uint32_t so = in_range(ok, bt_soff + (uint32_t)kt * bt_sstep);
+        rbt_s = F16W ? bload4(rBs, so) : bload1(rBs, so);
+      }
     }
   };
 
@@ -545,7 +567,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // FP16 chunks (slots 2c, 2c + 1); otherwise the 16 bytes as they are.
   auto store_chunk = [&](uint8_t* row, int r, int c, const uint32_t* w, uint32_t sraw) {
     if (PATH == P_F16) {
-      const uint32_t sp = e4m3_to_f16_pair(sraw & 0xFFu);
+      const uint32_t sp = e4m3_to_f16_pair(sraw);   // the conversion reads byte 0 only
       uint32_t o0[4], o1[4];
       fp4x8_to_f16(w[0], sp, o0);
       fp4x8_to_f16(w[1], sp, o1);
@@ -566,14 +588,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     const auto& rbt = rbt_[set];
     const uint32_t rbt_s = rbt_s_[set];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) store_chunk(LA + a_r[i] * LDS_ROW, a_r[i], a_c[i], ra[i], rsa[i]);
+    for (int i = 0; i < A_CH; ++i) store_chunk(LA + a_r[i] * LDS_ROW, a_r[i], a_c[i], ra[i], rsa[i] >> a_ssh[i]);
     if (!BT) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) store_chunk(LB + b_r[i] * LDS_ROW, b_r[i], b_c[i], rb[i], rsb[i]);
+      for (int i = 0; i < B_CH; ++i) store_chunk(LB + b_r[i] * LDS_ROW, b_r[i], b_c[i], rb[i], rsb[i] >> b_ssh[i]);
     } else {
       const int kbyte = bt_kg * R_BT * ESZ_BT;         // this lane's K range: 4, 8 or 16 bytes
       if constexpr (PATH == P_F16) {
-        const uint32_t sp = e4m3_to_f16_pair(rbt_s);
+        const uint32_t sp = e4m3_to_f16_pair(rbt_s >> bt_ssh);
         uint32_t hv[R_BT][4];
 #pragma unroll
         for (int q = 0; q < R_BT; ++q) fp4x8_to_f16(rbt[q][0], sp, hv[q]);
@@ -893,8 +915,11 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
 
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  if constexpr (PATH == P_FP8)
+  if constexpr (PATH == P_FP8) {
     if ((a.K >> 5) % 4 == 0) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
+  } else if constexpr (PATH == P_F16) {
+    if (a.K % 64 == 0 && (!BT || a.N % 64 == 0)) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
+  }
   return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false>(a, st);
 }
 
