@@ -692,7 +692,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         if (FS == 2) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      uint4 af[FS][TM], bf[FS][TN];
+      // FH fragment sets: 1 (read each K step right before its MFMAs), 2 (the
+      // next step's reads ahead of this step's MFMAs) or 4 (all four steps'
+      // reads issued at once, so one LDS latency per stage, not per step).
+      // 4 is taken where it measured faster: NVFP4 with small wave tiles in
+      // the two-set pipeline, where the scheduler then also spreads the next
+      // stage's FP4 -> FP16 conversion between the MFMAs (BF16 and the
+      // ping-pong schedule measured slower with it).
+      constexpr int FH = (PATH == P_F16 && !PP && !BT && TM * TN <= 2) ? 4 : FS;
+      uint4 af[FH][TM], bf[FH][TN];
       auto read = [&](int ks, int q) {
         const int chunk = 2 * ks + h;                 // K values [16ks + 8h, +8)
 #pragma unroll
@@ -706,13 +714,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           bf[q][tn] = *reinterpret_cast<const uint4*>(LB + (tn * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
         }
       };
-      if (FS == 2) read(0, 0);
+      if (FH == 4) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) read(ks, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (FH == 2) read(0, 0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int q = FS == 2 ? (ks & 1) : 0;
-        if (FS == 1) read(ks, 0);
-        else if (ks + 1 < 4) read(ks + 1, (ks + 1) & 1);
-        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
+        const int q = FH == 4 ? ks : FH == 2 ? (ks & 1) : 0;
+        if (FH == 1) read(ks, 0);
+        else if (FH == 2 && ks + 1 < 4) read(ks + 1, (ks + 1) & 1);
+        if (FH == 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -724,7 +737,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
               acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   __builtin_bit_cast(v8bf, bf[q][tn]), __builtin_bit_cast(v8bf, af[q][tm]), acc[tm][tn], 0, 0, 0);
           }
-        if (FS == 2) __builtin_amdgcn_sched_barrier(0);
+        if (FH == 2) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
