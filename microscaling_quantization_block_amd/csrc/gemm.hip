@@ -269,9 +269,24 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 // load kept in flight across the loop back edge is an 8-bit value the
 // compiler widens at the loop head, which waits for every load in flight
 // (the prefetched stage's too); a word needs no widening.
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false>
+//
+// BD (B direct; NVFP4 and BF16, row-major B, two-set pipeline, K % 64 == 0):
+// B skips LDS.  Each MFMA sums its 16 K values in any order as long as A and
+// B agree, so K step ks of a stage takes, in the lane of K half h, the K
+// values [32h + 8ks, +8) (all 16-bit paths use this order, so every tile
+// gives the same bits): a lane's B values for
+// the whole stage are then 32 consecutive K values of its column (one
+// 16-byte load of NVFP4 codes plus the stage's scale word, or four 16-byte
+// BF16 loads), loaded two stages ahead into registers, and the A fragments
+// are read from LDS chunk 4h + ks.  This removes B's LDS writes and reads
+// (a third of the LDS traffic of a 128x128 tile) at the cost of converting
+// each B column once per wave row.
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false,
+          bool BD = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert(!SDW || PATH != P_BF16, "scale words: MXFP8 and NVFP4 only");
+  static_assert(!BD || (PATH != P_FP8 && !BT && !PP && DIST == 2), "B direct: 16-bit MFMA, row-major B, two sets");
+  static_assert(!BD || PATH != P_F16 || SDW, "B direct NVFP4 reads scale words");
   constexpr bool SDWB = SDW && !BT && PATH == P_FP8;
   constexpr bool F16W = SDW && PATH == P_F16;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -333,7 +348,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr uint32_t CB = 4u * CW;                           // global bytes per chunk
   static_assert((LBM * CPR) % LT == 0 && (LBN * CPR) % LT == 0, "loader split");
   constexpr int A_CH = LBM * CPR / LT;
-  constexpr int B_CH = LBN * CPR / LT;
+  constexpr int B_CH = BD ? 0 : LBN * CPR / LT;
+  constexpr int B_CHA = B_CH > 0 ? B_CH : 1;                // array extent
   // Transposed B: a lane owns R K-rows x 8 N-columns per stage (LT lanes
   // cover KSTEP x LBN exactly).
   constexpr int R_BT = KSTEP * LBN / (8 * LT);
@@ -378,9 +394,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     if (F16W) a_soff[i] &= ~3u;
   }
   // per-lane B chunks (row-major B)
-  int b_c[B_CH], b_r[B_CH];
-  bool b_ok[B_CH];
-  uint32_t b_off[B_CH], b_soff[B_CH], b_ssh[B_CH];
+  int b_c[B_CHA], b_r[B_CHA];
+  bool b_ok[B_CHA];
+  uint32_t b_off[B_CHA], b_soff[B_CHA], b_ssh[B_CHA];
   const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
@@ -411,13 +427,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   const uint32_t bt_ssh = F16W ? 8u * (bt_sidx & 3u) : 0u;
   const uint32_t bt_sstep = 4u * (uint32_t)(N >> 4);
 
+  // B direct: lane (column n = l % 32 of each of its TN tiles, K half h) holds
+  // the stage's 32 K values [32h, 32h + 32) of column n, by stage parity.
+  constexpr int BDW = PATH == P_F16 ? 4 : 16;               // raw words per tile and stage
+  uint32_t bdr_[2][BD ? TN : 1][BD ? BDW : 1];
+  uint32_t bds_[2][BD ? TN : 1];                             // NVFP4: the stage's scale word
+  uint32_t bd_off[BD ? TN : 1], bd_soff[BD ? TN : 1];
+  bool bd_ok[BD ? TN : 1];
+  if constexpr (BD) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int n = n0 + wn * WN + tn * 32 + (lane & 31);
+      bd_ok[tn] = n < N;
+      const int nn = bd_ok[tn] ? n : 0;
+      bd_off[tn] = (uint32_t)nn * brb + (uint32_t)(lane >> 5) * (PATH == P_F16 ? 16u : 64u);
+      bd_soff[tn] = PATH == P_F16 ? (p.b_tile ? (uint32_t)((nn >> 4) * nb16)
+                                              : (uint32_t)scale_offset(nn, 0, nb16, p.b_mfma_layout))
+                                  : 0u;
+    }
+  }
+  // stage kt of B into set s (K % 64 == 0: a stage is in or out whole)
+  auto load_bd = [&](int kt, int s) {
+    if constexpr (BD) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const bool ok = bd_ok[tn] && kt < nk;
+        const uint32_t o = bd_off[tn] + (uint32_t)kt * ROW_STEP;
+#pragma unroll
+        for (int j = 0; j < BDW / 4; ++j) {
+          const uint4 v = bload16(rB, in_range(ok, o + 16u * j));
+          bdr_[s][tn][4 * j] = v.x; bdr_[s][tn][4 * j + 1] = v.y;
+          bdr_[s][tn][4 * j + 2] = v.z; bdr_[s][tn][4 * j + 3] = v.w;
+        }
+        if (PATH == P_F16) bds_[s][tn] = bload4(rBs, in_range(ok, bd_soff[tn] + (uint32_t)kt * b_sstep));
+      }
+    }
+  };
+
   // DIST staging sets in registers: with DIST = 2 the stage being written to
   // LDS and the next one are both in flight.  Set indices are compile-time
   // constants once the K loop is unrolled by two.
   uint32_t ra_[DIST][A_CH][CW];
   uint32_t rsa_[DIST][A_CH];
-  uint32_t rb_[DIST][BT ? 1 : B_CH][CW];
-  uint32_t rsb_[DIST][BT ? 1 : B_CH];
+  uint32_t rb_[DIST][BT ? 1 : B_CHA][CW];
+  uint32_t rsb_[DIST][BT ? 1 : B_CHA];
   // transposed staging: FP8 R rows x 8 bytes (2 words); BF16 R rows x 8
   // values (4 words); NVFP4 R rows x 8 codes (1 word) + one 16x16 tile scale
   uint32_t rbt_[DIST][BT ? R_BT : 1][PATH == P_BF16 ? 4 : PATH == P_FP8 ? 2 : 1];
@@ -702,7 +755,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       constexpr int FH = (PATH == P_F16 && !PP && !BT && TM * TN <= 2) ? 4 : FS;
       uint4 af[FH][TM], bf[FH][TN];
       auto read = [&](int ks, int q) {
-        const int chunk = 2 * ks + h;                 // K values [16ks + 8h, +8)
+        // K values [32h + 8ks, +8) of the stage (the order B direct needs;
+        // every 16-bit path uses it so that all tiles sum alike)
+        const int chunk = 4 * h + ks;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const int r = wm * WM + tm * 32 + r32;
@@ -710,8 +765,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const int r = wn * WN + tn * 32 + r32;
-          bf[q][tn] = *reinterpret_cast<const uint4*>(LB + (tn * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
+          if constexpr (BD) {
+            if constexpr (PATH == P_F16) {
+              // block 2h + ks / 2 of the stage: byte 2h + ks / 2 of the scale word
+              const uint32_t sp = e4m3_to_f16_pair(bds_[set][tn] >> (16 * h + 8 * (ks >> 1)));
+              uint32_t o[4];
+              fp4x8_to_f16(bdr_[set][tn][ks], sp, o);
+              bf[q][tn] = make_uint4(o[0], o[1], o[2], o[3]);
+            } else {
+              bf[q][tn] = make_uint4(bdr_[set][tn][4 * ks], bdr_[set][tn][4 * ks + 1],
+                                     bdr_[set][tn][4 * ks + 2], bdr_[set][tn][4 * ks + 3]);
+            }
+          } else {
+            const int r = wn * WN + tn * 32 + r32;
+            bf[q][tn] = *reinterpret_cast<const uint4*>(LB + (tn * 32 + r32) * LDS_ROW + slot_of(r, chunk) * 16);
+          }
         }
       };
       if (FH == 4) {
@@ -803,6 +871,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       }
     }
   } else if (DIST == 2) {
+    load_bd(0, 0);
+    load_bd(1, 1);
     load_stage(0, 0);
     load_scales(0, 0);
     load_stage(1, 1 % DIST);
@@ -813,11 +883,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
       compute(L0, 0);
+      load_bd(kt + 2, 0);
       store_stage(L1, 1 % DIST);
       load_stage(kt + 3, 1 % DIST);
       load_scales(kt + 2, 0);
       __syncthreads();
       compute(L1, 1);
+      load_bd(kt + 3, 1);
       store_stage(L0, 0);
       load_stage(kt + 4, 0);
       load_scales(kt + 3, 1);
@@ -908,14 +980,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
 
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW>
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW, bool BD = false>
 static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_n = (a.N + BN - 1) / BN;
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)(BM + BN) * LDS_ROW;
-  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW>;
+  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -926,12 +998,20 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// B direct (see gemm_kernel) where it applies
+static constexpr bool gemm_b_direct() { return true; }
+
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   if constexpr (PATH == P_FP8) {
     if ((a.K >> 5) % 4 == 0) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
   } else if constexpr (PATH == P_F16) {
+    if constexpr (!BT && !PP && DIST == 2)
+      if (a.K % 64 == 0 && gemm_b_direct()) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, true>(a, st);
     if (a.K % 64 == 0 && (!BT || a.N % 64 == 0)) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
+  } else {
+    if constexpr (!BT && !PP && DIST == 2)
+      if (a.K % 64 == 0 && gemm_b_direct()) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false, true>(a, st);
   }
   return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false>(a, st);
 }

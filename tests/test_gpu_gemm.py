@@ -471,3 +471,37 @@ def test_grouped_many_groups_and_empty_ones():
             assert np.array_equal(run(), ref), f"tile {t}"
     finally:
         m.mx_gemm_set_tile(-1)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 192, 512), (96, 160, 320)])
+def test_nvfp4_gemm_mfma_scale_layout_same_bits(M, N, K):
+    """NVFP4 FPROP with both operands' block scales in the MFMA layout returns
+    the bits of the LINEAR-layout call (same codes, scales only moved); the
+    LINEAR call is checked against the oracle.  Both the measured tile and a
+    forced 256x256 tile run."""
+    m = mxq()
+    x = _bf16((M, K), 1.0, 90)
+    w = _bf16((N, K), 0.02, 91)
+    say(f"nvfp4 GEMM MFMA scale layout {M}x{N}x{K}")
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    cx, sx, Sx = m.nvfp4_quantize(xd, gs=m.GScale.PER_ROW)
+    cw, sw, Sw = m.nvfp4_quantize(wd, gs=m.GScale.PER_TENSOR)
+    cxm, sxm, Sxm = m.nvfp4_quantize(xd, gs=m.GScale.PER_ROW, layout=m.Layout.MFMA)
+    cwm, swm, Swm = m.nvfp4_quantize(wd, gs=m.GScale.PER_TENSOR, layout=m.Layout.MFMA)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw, sw, Sw, gs=m.GScale.PER_TENSOR)
+    Am = m.Operand(m.Format.NVFP4, cxm, sxm, Sxm, gs=m.GScale.PER_ROW, layout=m.Layout.MFMA)
+    Bm = m.Operand(m.Format.NVFP4, cwm, swm, Swm, gs=m.GScale.PER_TENSOR, layout=m.Layout.MFMA)
+    ref = m.mx_gemm(A, B, M, N, K)
+    a64 = ON.dequantize_f64(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+    a32 = ON.dequantize_f32(to_np(cx), to_np(sx), to_np(Sx), "1x16", "per_row")
+    b64 = ON.dequantize_f64(to_np(cw), to_np(sw), to_np(Sw), "1x16", "per_tensor")
+    b32 = ON.dequantize_f32(to_np(cw), to_np(sw), to_np(Sw), "1x16", "per_tensor")
+    _assert_gemm(ref, a64, b64, a32, b32)
+    ref = from_dev_bf16(ref)
+    assert np.array_equal(from_dev_bf16(m.mx_gemm(Am, Bm, M, N, K)), ref)
+    try:
+        m.mx_gemm_set_tile(6)
+        assert np.array_equal(from_dev_bf16(m.mx_gemm(Am, Bm, M, N, K)), ref)
+    finally:
+        m.mx_gemm_set_tile(-1)
