@@ -270,6 +270,13 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 // compiler widens at the loop head, which waits for every load in flight
 // (the prefetched stage's too); a word needs no widening.
 //
+// SS (stages per barrier): the 16-bit two-set pipeline stages two K steps of
+// 64 per barrier (two LDS stages per buffer, register sets per stage), so the
+// fixed cost of a barrier phase (LDS latency at its start, the stores and the
+// wait at its end) is paid once per 128 of K.
+template <int PATH, bool BT, int DIST, bool PP>
+constexpr int stages_per_barrier() { return (DIST == 2 && PATH != P_FP8 && !BT && !PP) ? 2 : 1; }
+//
 // BD (B direct; NVFP4 and BF16, row-major B, two-set pipeline, K % 64 == 0):
 // B skips LDS.  Each MFMA sums its 16 K values in any order as long as A and
 // B agree, so K step ks of a stage takes, in the lane of K half h, the K
@@ -296,6 +303,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int LBM = PP ? BM / 2 : BM, LBN = PP ? BN / 2 : BN;   // rows of a share
   constexpr int ROWS = BM + BN;
   constexpr int STAGE_BYTES = ROWS * LDS_ROW;
+  constexpr int SS = stages_per_barrier<PATH, BT, DIST, PP>();
+  constexpr int NS = DIST * SS;                               // register staging sets
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0 && TM >= 1 && TN >= 1, "wave tile");
@@ -430,8 +439,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // B direct: lane (column n = l % 32 of each of its TN tiles, K half h) holds
   // the stage's 32 K values [32h, 32h + 32) of column n, by stage parity.
   constexpr int BDW = PATH == P_F16 ? 4 : 16;               // raw words per tile and stage
-  uint32_t bdr_[2][BD ? TN : 1][BD ? BDW : 1];
-  uint32_t bds_[2][BD ? TN : 1];                             // NVFP4: the stage's scale word
+  uint32_t bdr_[2 * SS][BD ? TN : 1][BD ? BDW : 1];
+  uint32_t bds_[2 * SS][BD ? TN : 1];                             // NVFP4: the stage's scale word
   uint32_t bd_off[BD ? TN : 1], bd_soff[BD ? TN : 1];
   bool bd_ok[BD ? TN : 1];
   if constexpr (BD) {
@@ -467,14 +476,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // DIST staging sets in registers: with DIST = 2 the stage being written to
   // LDS and the next one are both in flight.  Set indices are compile-time
   // constants once the K loop is unrolled by two.
-  uint32_t ra_[DIST][A_CH][CW];
-  uint32_t rsa_[DIST][A_CH];
-  uint32_t rb_[DIST][BT ? 1 : B_CHA][CW];
-  uint32_t rsb_[DIST][BT ? 1 : B_CHA];
+  uint32_t ra_[NS][A_CH][CW];
+  uint32_t rsa_[NS][A_CH];
+  uint32_t rb_[NS][BT ? 1 : B_CHA][CW];
+  uint32_t rsb_[NS][BT ? 1 : B_CHA];
   // transposed staging: FP8 R rows x 8 bytes (2 words); BF16 R rows x 8
   // values (4 words); NVFP4 R rows x 8 codes (1 word) + one 16x16 tile scale
-  uint32_t rbt_[DIST][BT ? R_BT : 1][PATH == P_BF16 ? 4 : PATH == P_FP8 ? 2 : 1];
-  uint32_t rbt_s_[DIST];
+  uint32_t rbt_[NS][BT ? R_BT : 1][PATH == P_BF16 ? 4 : PATH == P_FP8 ? 2 : 1];
+  uint32_t rbt_s_[NS];
 
   // MXFP8: the E8M0 bytes each lane feeds its MFMAs, prefetched with the
   // stage.  Lane (r, h) needs, for each of its MFMA tiles, the bytes of blocks
@@ -821,7 +830,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   //  DIST == 1: the next stage's loads (and MXFP8 scales) are in flight
   //    during the compute.
   uint8_t* const L0 = lds;
-  uint8_t* const L1 = lds + STAGE_BYTES;
+  uint8_t* const L1 = lds + SS * STAGE_BYTES;
   if constexpr (PP) {
     // prologue: both halves of stage 0 in buffer 0, stage 1 staged in
     // registers, MXFP8 scale sets 0 and 1 for stages 0 and 1
@@ -871,31 +880,55 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       }
     }
   } else if (DIST == 2) {
-    load_bd(0, 0);
-    load_bd(1, 1);
-    load_stage(0, 0);
-    load_scales(0, 0);
-    load_stage(1, 1 % DIST);
-    load_scales(1, 1);
-    store_stage(L0, 0);
-    load_stage(2, 0);
+    // super-stage u = stages u*SS .. u*SS + SS - 1, in LDS buffer u % 2 and
+    // register sets (u % 2)*SS + j; past the last stage loads read zeros, so
+    // a partial last super-stage adds zero products
+    auto load_su = [&](int u, int s) {
+#pragma unroll
+      for (int j = 0; j < SS; ++j) load_stage(u * SS + j, s * SS + j);
+    };
+    auto scales_su = [&](int u, int s) {
+#pragma unroll
+      for (int j = 0; j < SS; ++j) load_scales(u * SS + j, s * SS + j);
+    };
+    auto bd_su = [&](int u, int s) {
+#pragma unroll
+      for (int j = 0; j < SS; ++j) load_bd(u * SS + j, s * SS + j);
+    };
+    auto store_su = [&](uint8_t* L, int s) {
+#pragma unroll
+      for (int j = 0; j < SS; ++j) store_stage(L + j * STAGE_BYTES, s * SS + j);
+    };
+    auto compute_su = [&](const uint8_t* L, int s) {
+#pragma unroll
+      for (int j = 0; j < SS; ++j) compute(L + j * STAGE_BYTES, s * SS + j);
+    };
+    const int nu = (nk + SS - 1) / SS;
+    bd_su(0, 0);
+    bd_su(1, 1);
+    load_su(0, 0);
+    scales_su(0, 0);
+    load_su(1, 1);
+    scales_su(1, 1);
+    store_su(L0, 0);
+    load_su(2, 0);
     __syncthreads();
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      compute(L0, 0);
-      load_bd(kt + 2, 0);
-      store_stage(L1, 1 % DIST);
-      load_stage(kt + 3, 1 % DIST);
-      load_scales(kt + 2, 0);
+    int u = 0;
+    for (; u + 1 < nu; u += 2) {
+      compute_su(L0, 0);
+      bd_su(u + 2, 0);
+      store_su(L1, 1);
+      load_su(u + 3, 1);
+      scales_su(u + 2, 0);
       __syncthreads();
-      compute(L1, 1);
-      load_bd(kt + 3, 1);
-      store_stage(L0, 0);
-      load_stage(kt + 4, 0);
-      load_scales(kt + 3, 1);
+      compute_su(L1, 1);
+      bd_su(u + 3, 1);
+      store_su(L0, 0);
+      load_su(u + 4, 0);
+      scales_su(u + 3, 1);
       __syncthreads();
     }
-    if (kt < nk) compute(L0, 0);          // odd stage count: the last stage
+    if (u < nu) compute_su(L0, 0);          // odd super-stage count: the last one
   } else {
     // one register staging set; unrolled by two so that the MXFP8 scale set
     // of stage s (s % 2) is loaded a stage ahead, not right before its MFMAs
@@ -986,7 +1019,7 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
-  size_t lds = 2 * (size_t)(BM + BN) * LDS_ROW;
+  size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + BN) * LDS_ROW;
   auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD>;
   static bool attr_set = false;
   if (!attr_set) {
