@@ -106,8 +106,7 @@ __device__ __forceinline__ uint32_t in_range(bool ok, uint32_t off) {
 // ------------------------------------------------------------ FP4 -> FP16
 // Eight E2M1 codes (one word, element 2j in the low nibble of byte j) times
 // the block scale: four words of packed FP16 pairs.  Both steps are exact.
-__device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sb_pair, uint32_t out[4]) {
-  const h2 s = __builtin_bit_cast(h2, sb_pair);
+__device__ __forceinline__ void fp4x8_to_f16(uint32_t w, h2 s, uint32_t out[4]) {
   // unit scale: the exact code values (the conversion uses only the exponent
   // of its scale operand, so the E4M3 scale is applied by the multiply)
   const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
@@ -120,10 +119,12 @@ __device__ __forceinline__ void fp4x8_to_f16(uint32_t w, uint32_t sb_pair, uint3
   out[3] = __builtin_bit_cast(uint32_t, c3 * s);
 }
 
-__device__ __forceinline__ uint32_t e4m3_to_f16_pair(uint32_t code) {
-  _Float16 h = (_Float16)e4m3_to_f32(code);     // exact
-  uint32_t b = __builtin_bit_cast(uint16_t, h);
-  return b | (b << 16);
+// E4M3 byte SEL of v as FP16 (exact: every E4M3 value is an FP16 normal),
+// in both halves; the splat folds into the multiply's operand select.
+template <int SEL>
+__device__ __forceinline__ h2 e4m3_to_h2(uint32_t v) {
+  const h2 r = __builtin_amdgcn_cvt_scalef32_f16_fp8(h2{0, 0}, v, 1.0f, SEL, false);
+  return h2{r.x, r.x};
 }
 
 // ------------------------------------------------------------ tile origin
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert(!PP || (NT == 512 && DIST == 1 && WGM % 2 == 0), "ping-pong: 8 waves, one staging set");
   constexpr int LT = PP ? NT / 2 : NT;                      // threads loading one share
   constexpr int LBM = PP ? BM / 2 : BM, LBN = PP ? BN / 2 : BN;   // rows of a share
-  constexpr int ROWS = BM + BN;
+  constexpr int ROWS = BM + (BD ? 0 : BN);                   // B direct keeps no B rows in LDS
   constexpr int STAGE_BYTES = ROWS * LDS_ROW;
   constexpr int SS = stages_per_barrier<PATH, BT, DIST, PP>();
   constexpr int NS = DIST * SS;                               // register staging sets
@@ -423,6 +424,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     b_ssh[i] = F16W ? 8u * (b_soff[i] & 3u) : 0u;
     if (F16W) b_soff[i] &= ~3u;
   }
+  // NVFP4 with K % 64 == 0 (scale words): a stage is in or out of range as a
+  // whole, so a lane's row offsets carry only its row's validity (bit 31) and
+  // each stage adds one uniform term, the stage offset or 2^31 past the last
+  // stage.  An invalid row's offset is taken at row 0; adding 2^31 to it
+  // wraps to row 0's data, which only feeds that row's discarded outputs.
+  constexpr bool KF = F16W && !BT;
+  uint32_t a_voff[A_CH], a_svoff[A_CH], b_voff[B_CHA], b_svoff[B_CHA];
+  if constexpr (KF) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      a_voff[i] = in_range(a_ok[i], a_off[i]);       // src is row 0 when invalid
+      a_svoff[i] = in_range(a_ok[i], a_soff[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int n = b_ok[i] ? n0 + b_r[i] : 0;
+      b_voff[i] = in_range(b_ok[i], (uint32_t)n * brb + (uint32_t)b_c[i] * CB);
+      const uint32_t so = p.b_tile ? (uint32_t)((n >> 4) * nb16 + b_c[i])
+                                   : (uint32_t)scale_offset(n, b_c[i], nb16, p.b_mfma_layout);
+      b_svoff[i] = in_range(b_ok[i], so & ~3u);
+    }
+  }
   // transposed B: lane -> (k group, n group of 8), n fastest for coalesced row
   // reads; K and N are multiples of the tile size, so a group is in or out whole.
   const int bt_ng = lb0 / 8 + ltid % (LBN / 8), bt_kg = ltid / (LBN / 8);
@@ -462,13 +485,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       for (int tn = 0; tn < TN; ++tn) {
         const bool ok = bd_ok[tn] && kt < nk;
         const uint32_t o = bd_off[tn] + (uint32_t)kt * ROW_STEP;
+        // with KF: the row's validity bit plus one uniform stage term
+        const uint32_t ob = KF ? in_range(bd_ok[tn], bd_off[tn]) + (kt < nk ? (uint32_t)kt * ROW_STEP : 0x80000000u) : 0u;
 #pragma unroll
         for (int j = 0; j < BDW / 4; ++j) {
-          const uint4 v = bload16(rB, in_range(ok, o + 16u * j));
+          const uint4 v = bload16(rB, KF ? ob + 16u * j : in_range(ok, o + 16u * j));
           bdr_[s][tn][4 * j] = v.x; bdr_[s][tn][4 * j + 1] = v.y;
           bdr_[s][tn][4 * j + 2] = v.z; bdr_[s][tn][4 * j + 3] = v.w;
         }
-        if (PATH == P_F16) bds_[s][tn] = bload4(rBs, in_range(ok, bd_soff[tn] + (uint32_t)kt * b_sstep));
+        if (PATH == P_F16)
+          bds_[s][tn] = bload4(rBs, in_range(bd_ok[tn], bd_soff[tn]) + (kt < nk ? (uint32_t)kt * b_sstep : 0x80000000u));
       }
     }
   };
@@ -573,6 +599,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       }
     };
     constexpr int VPC = PATH == P_BF16 ? 8 : 16;
+    if constexpr (KF) {
+      const bool kin = kt < nk;
+      const uint32_t kso = kin ? (uint32_t)kt * ROW_STEP : 0x80000000u;
+      const uint32_t ksa = kin ? (uint32_t)kt * a_sstep : 0x80000000u;
+      const uint32_t ksb = kin ? (uint32_t)kt * b_sstep : 0x80000000u;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        chunk(rA, a_voff[i] + kso, ra[i]);
+        rsa[i] = bload4(rAs, a_svoff[i] + ksa);
+      }
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        chunk(rB, b_voff[i] + kso, rb[i]);
+        rsb[i] = bload4(rBs, b_svoff[i] + ksb);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const bool ok = a_ok[i] && k0 + a_c[i] * VPC < K;
@@ -629,7 +672,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // FP16 chunks (slots 2c, 2c + 1); otherwise the 16 bytes as they are.
   auto store_chunk = [&](uint8_t* row, int r, int c, const uint32_t* w, uint32_t sraw) {
     if (PATH == P_F16) {
-      const uint32_t sp = e4m3_to_f16_pair(sraw);   // the conversion reads byte 0 only
+      const h2 sp = e4m3_to_h2<0>(sraw);
       uint32_t o0[4], o1[4];
       fp4x8_to_f16(w[0], sp, o0);
       fp4x8_to_f16(w[1], sp, o1);
@@ -657,7 +700,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     } else {
       const int kbyte = bt_kg * R_BT * ESZ_BT;         // this lane's K range: 4, 8 or 16 bytes
       if constexpr (PATH == P_F16) {
-        const uint32_t sp = e4m3_to_f16_pair(rbt_s >> bt_ssh);
+        const h2 sp = e4m3_to_h2<0>(rbt_s >> bt_ssh);
         uint32_t hv[R_BT][4];
 #pragma unroll
         for (int q = 0; q < R_BT; ++q) fp4x8_to_f16(rbt[q][0], sp, hv[q]);
@@ -777,7 +820,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           if constexpr (BD) {
             if constexpr (PATH == P_F16) {
               // block 2h + ks / 2 of the stage: byte 2h + ks / 2 of the scale word
-              const uint32_t sp = e4m3_to_f16_pair(bds_[set][tn] >> (16 * h + 8 * (ks >> 1)));
+              const h2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bds_[set][tn] >> (16 * h), 1.0f, false);
+              const h2 sp = (ks >> 1) ? h2{s01.y, s01.y} : h2{s01.x, s01.x};
               uint32_t o[4];
               fp4x8_to_f16(bdr_[set][tn][ks], sp, o);
               bf[q][tn] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -962,7 +1006,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int EROW = WN * 2 + 8;       // bytes per staged row
   constexpr int ECH = WN / 8;            // 16-byte chunks per row
   constexpr int ERI = 64 / ECH;          // rows per read-back instruction
-  static_assert(8 * 32 * EROW <= 2 * STAGE_BYTES, "epilogue staging");
+  static_assert((NT / 64) * 32 * EROW <= 2 * SS * STAGE_BYTES, "epilogue staging");
   uint8_t* const E = lds + wave * (32 * EROW);
   float sbg = 1.0f;
   if (PATH == P_F16) sbg = p.b_gs[to.group];
@@ -1019,7 +1063,7 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
-  size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + BN) * LDS_ROW;
+  size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + (BD ? 0 : BN)) * LDS_ROW;
   auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD>;
   static bool attr_set = false;
   if (!attr_set) {
