@@ -271,14 +271,15 @@ __device__ __forceinline__ void transpose8(const uint32_t (*rows)[2], int j, uin
 // compiler widens at the loop head, which waits for every load in flight
 // (the prefetched stage's too); a word needs no widening.
 //
-// SS (stages per barrier): the 16-bit two-set pipeline stages two K steps of
-// 64 per barrier (two LDS stages per buffer, register sets per stage), so the
+// SS (stages per barrier): the NVFP4 two-set pipeline stages two K steps of
+// 64 per barrier (BF16 measured slower with it) (two LDS stages per buffer, register sets per stage), so the
 // fixed cost of a barrier phase (LDS latency at its start, the stores and the
 // wait at its end) is paid once per 128 of K.
 template <int PATH, bool BT, int DIST, bool PP>
-constexpr int stages_per_barrier() { return (DIST == 2 && PATH != P_FP8 && !BT && !PP) ? 2 : 1; }
+constexpr int stages_per_barrier() { return (DIST == 2 && PATH == P_F16 && !BT && !PP) ? 2 : 1; }
 //
-// BD (B direct; NVFP4 and BF16, row-major B, two-set pipeline, K % 64 == 0):
+// BD (B direct; row-major B, two-set pipeline, K % 64 == 0; launched for
+// NVFP4 only, see gemm_b_direct):
 // B skips LDS.  Each MFMA sums its 16 K values in any order as long as A and
 // B agree, so K step ks of a stage takes, in the lane of K half h, the K
 // values [32h + 8ks, +8) (all 16-bit paths use this order, so every tile
@@ -1075,7 +1076,9 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// B direct (see gemm_kernel) where it applies
+// B direct (see gemm_kernel): NVFP4 only.  For BF16 it measured slower
+// (4096x2048x768: 34 us against 20 us through LDS; its B needs four 16-byte
+// loads per lane and stage and BF16 is bound by LDS, not by the conversion).
 static constexpr bool gemm_b_direct() { return true; }
 
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
@@ -1086,9 +1089,6 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     if constexpr (!BT && !PP && DIST == 2)
       if (a.K % 64 == 0 && gemm_b_direct()) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, true>(a, st);
     if (a.K % 64 == 0 && (!BT || a.N % 64 == 0)) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
-  } else {
-    if constexpr (!BT && !PP && DIST == 2)
-      if (a.K % 64 == 0 && gemm_b_direct()) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false, true>(a, st);
   }
   return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, false>(a, st);
 }
