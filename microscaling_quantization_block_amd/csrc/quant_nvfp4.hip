@@ -427,10 +427,12 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                                int gmode, bool mfma, uint64_t seed, uint32_t sid, uint32_t tag,
                                hipStream_t st) {
-  // at most 512 workgroups of 4 waves (8 waves per CU); a wave walks
-  // rows / 2048 rows with the next row's loads in flight
+  // at most 2048 workgroups of 4 waves (32 waves per CU, 8 per SIMD: the
+  // stochastic-rounding encode is VALU work that needs them to hide its
+  // dependent chains, and short rows need them to keep loads in flight); a
+  // wave walks rows / 8192 rows with the next row's loads in flight
   int64_t blocks = (rows + 3) / 4;
-  if (blocks > 512) blocks = 512;
+  if (blocks > 2048) blocks = 2048;
   dim3 grid((unsigned)blocks), block(256);
   const int64_t bpr = cols / 16;
   auto go = [&](auto kern) {

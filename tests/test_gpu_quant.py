@@ -188,11 +188,11 @@ def test_nvfp4_config2_activations_full_size():
     _nv_check_row(m, x, m.GScale.PER_ROW)
 
 
-@pytest.mark.parametrize("shape", [(5000, 2048), (2100, 8208)])
+@pytest.mark.parametrize("shape", [(5000, 2048), (20000, 512), (2100, 8208)])
 @pytest.mark.parametrize("gs", ["per_row", "per_tensor"])
 def test_nvfp4_row_many_rows_sampled(shape, gs):
-    """More rows than waves in the grid (each wave walks several rows, an odd
-    count for some), and rows longer than 8192 (the two-pass kernel).  Rows
+    """A row per wave; more rows than the grid's 8192 waves (each wave walks
+    two or three rows); and rows longer than 8192 (the two-pass kernel).  Rows
     are independent given S, so the oracle runs on sampled rows: per row, or
     with the tensor's S (the exact binary32 amax / 2688) given."""
     m = mxq()
@@ -202,7 +202,8 @@ def test_nvfp4_row_many_rows_sampled(shape, gs):
     say(f"nvfp4 ROW {gs} {shape} sampled rows")
     g = m.GScale.PER_ROW if gs == "per_row" else m.GScale.PER_TENSOR
     c, s, S = m.nvfp4_quantize(to_dev_bf16(x), gs=g)
-    rows = sorted({0, 1, 2047, 2048, 2049, 4095, 4096, R - 2, R - 1} & set(range(R)))
+    rows = sorted({0, 1, 2047, 2048, 2049, 4095, 4096, 8191, 8192, 8193, 16383, 16384, 16385,
+                   R - 2, R - 1} & set(range(R)))
     v = _vals(x[rows])
     if gs == "per_row":
         rc, rs, rS = ON.quantize_rowwise(v, "per_row")
