@@ -42,6 +42,10 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
 
 // NVFP4: one lane per 16-element block (8 code bytes, one scale).
 // gmode: 0 = S per row, 1 = S per tensor.  tile = 1 for 16x16 scales.
+// Codes become binary32 through the hardware FP4 conversion with unit scale
+// (exact code values); IDX32: the block index fits 32 bits, so the row comes
+// from a 32-bit division.
+template <bool IDX32>
 __global__ __launch_bounds__(256) void dq_nvfp4_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ gscales, int64_t rows, int64_t cols, int tile, int gmode,
@@ -50,21 +54,32 @@ __global__ __launch_bounds__(256) void dq_nvfp4_kernel(
   const int64_t total = rows * bpr;
   for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
        id += (int64_t)gridDim.x * 256) {
-    int64_t r = id / bpr, b = id - r * bpr;
-    uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + b * 8);
-    uint32_t sc = tile ? scales[(r >> 4) * bpr + b] : scales[scale_offset(r, b, bpr, mfma_layout)];
-    float sb = e4m3_to_f32(sc);
-    float S = gmode == 0 ? gscales[r] : gscales[0];
-    uint32_t w[2] = {q.x, q.y};
+    int64_t r, b;
+    if (IDX32) {
+      const uint32_t u = (uint32_t)id, d = (uint32_t)bpr, q32 = u / d;
+      r = q32;
+      b = u - q32 * d;
+    } else {
+      r = id / bpr;
+      b = id - r * bpr;
+    }
+    const uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + b * 8);
+    const uint32_t sc = tile ? scales[(r >> 4) * bpr + b] : scales[scale_offset(r, b, bpr, mfma_layout)];
+    const float sb = e4m3_to_f32(sc);
+    const float S = gmode == 0 ? gscales[r] : gscales[0];
+    const uint32_t w[2] = {q.x, q.y};
+    mxq_f32x2 v[8];            // byte i: elements 2i (low nibble) and 2i + 1
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      v[4 * j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0);
+      v[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1);
+      v[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2);
+      v[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3);
+    }
     uint32_t o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFF;
-      uint32_t ca = byte & 0xF, cb = byte >> 4;
-      float va = (ca & 8) ? -e2m1_mag(ca & 7) : e2m1_mag(ca & 7);
-      float vb = (cb & 8) ? -e2m1_mag(cb & 7) : e2m1_mag(cb & 7);
-      float pa = va * sb, pb = vb * sb;      // exact
-      float da = pa * S, db = pb * S;        // one rounding each
+      const float da = (v[i].x * sb) * S, db = (v[i].y * sb) * S;   // exact product, then one rounding
       o[i] = f32x2_to_bf16x2(da, db);
     }
     uint16_t* dst = out + r * ld_out + b * 16;
@@ -115,9 +130,10 @@ hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t
 hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            const float* gscales, int64_t rows, int64_t cols, bool tile,
                            int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st) {
-  hipLaunchKernelGGL(dq_nvfp4_kernel, dim3(grid_for(rows * (cols / 16))), dim3(256), 0, st, codes,
-                     ld_codes, scales, gscales, rows, cols, (int)tile, gmode, (int)mfma, out,
-                     ld_out);
+  const int64_t total = rows * (cols / 16);
+  auto kern = total < (int64_t(1) << 32) ? dq_nvfp4_kernel<true> : dq_nvfp4_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid_for(total)), dim3(256), 0, st, codes, ld_codes, scales,
+                     gscales, rows, cols, (int)tile, gmode, (int)mfma, out, ld_out);
   return hipGetLastError();
 }
 

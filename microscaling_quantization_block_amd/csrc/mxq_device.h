@@ -51,13 +51,7 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
 }
 
 // ------------------------------------------------------------------ E2M1
-// E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7.
-__device__ __forceinline__ float e2m1_mag(uint32_t code3) {
-  // 2^(e-1) * (1 + m/2) for e > 0, 0.5 * m for e == 0
-  uint32_t e = (code3 >> 1) & 3u, m = code3 & 1u;
-  float nrm = __uint_as_float(((e + 126u) << 23) | (m << 22));
-  return e ? nrm : 0.5f * (float)m;
-}
+// E2M1 magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7.
 
 // Round-to-nearest-even onto the E2M1 grid, saturating at 6.  Returns the
 // 4-bit code (sign in bit 3 taken from the sign bit of y).
