@@ -14,6 +14,8 @@
 namespace mxq {
 
 // MXFP8: one lane per 8 codes.  tile = 1 for 32x32 scales.
+// IDX32: the chunk index fits 32 bits, so the row comes from a 32-bit division.
+template <bool IDX32>
 __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     int64_t rows, int64_t cols, int tile, int mfma_layout, uint16_t* __restrict__ out,
@@ -22,7 +24,15 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
   const int64_t total = rows * cpr;
   for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
        id += (int64_t)gridDim.x * 256) {
-    int64_t r = id / cpr, c = id - r * cpr;
+    int64_t r, c;
+    if (IDX32) {
+      const uint32_t u = (uint32_t)id, d = (uint32_t)cpr, q32 = u / d;
+      r = q32;
+      c = u - q32 * d;
+    } else {
+      r = id / cpr;
+      c = id - r * cpr;
+    }
     uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + c * 8);
     uint32_t s = tile ? scales[(r >> 5) * (cols >> 5) + (c >> 2)]
                       : scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)];
@@ -122,8 +132,10 @@ static unsigned grid_for(int64_t total) {
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,
                            int64_t ld_out, hipStream_t st) {
-  hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid_for(rows * (cols / 8))), dim3(256), 0, st, codes,
-                     ld_codes, scales, rows, cols, (int)tile, (int)mfma, out, ld_out);
+  const int64_t total = rows * (cols / 8);
+  auto kern = total < (int64_t(1) << 32) ? dq_mxfp8_kernel<true> : dq_mxfp8_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid_for(total)), dim3(256), 0, st, codes, ld_codes, scales, rows,
+                     cols, (int)tile, (int)mfma, out, ld_out);
   return hipGetLastError();
 }
 
