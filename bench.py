@@ -202,9 +202,15 @@ def cpu_baseline(data, min_seconds):
 PEAK_FP8_TFLOPS = 5000.0
 
 
-def _time_us(torch, fn, iters, warm=2):
-    for _ in range(warm):
+def _time_us(torch, fn, iters, warm_ms=30.0):
+    # warm up until about warm_ms of work has run (at least three calls): the
+    # clock drops while the host sets up a row, and a cold start reads slow
+    t0, n = time.perf_counter(), 0
+    while n < 3 or (time.perf_counter() - t0) * 1e3 < warm_ms:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
