@@ -62,6 +62,40 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "microscaling_quantization_block_amd", "csrc", "gemm.hip")
 
 
+def measured_reference(m, torch):
+    """Context for the spec peaks: the bandwidth of a plain device copy of
+    COPY_BYTES (read + write bytes over time, HIP events, 20 copies), and the
+    host cost of one library call from Python (binding + C ABI + launch,
+    2000 back-to-back calls of a 64x64 MXFP8 dequantize, no synchronization)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(20):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_BYTES * 20 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    x = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    c, s = m.mx_quantize(x)
+    out = torch.empty_like(x)
+    for _ in range(50):
+        m.mx_dequantize(m.Format.MXFP8, c, s, 64, 64, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(2000):
+        m.mx_dequantize(m.Format.MXFP8, c, s, 64, 64, out=out)
+    host_us = (time.perf_counter() - t0) / 2000 * 1e6
+    torch.cuda.synchronize()
+    return {"copy_GBps": round(copy_gbps, 1), "copy_frac_of_hbm_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "host_us_per_call": round(host_us, 2),
+            "note": "device copy of 256 MiB (read + write bytes); host time of one Python -> C ABI call"}
+
+
 def copy_calibration():
     """A plain device copy of COPY_BYTES, ten times: the reference for scaling
     the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -261,6 +295,17 @@ def rows_report():
     out("a1-a3", "nvfp4 16x1 columnwise per-tensor SR (dY^T, WGRAD)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
         dy5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1, codes=cgc,
         block_scales=sgc, gscales=Sgc), 10), nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
+    # the WGRAD inputs under the random Hadamard transform (two passes, both transforming)
+    out("f1", "nvfp4 16x1 columnwise + RHT per-tensor SR (dY^T, WGRAD)", [T5, H5], _time_us(
+        torch, lambda: m.nvfp4_quantize_rht(dy5, 0x6B2D, rnd=m.Round.SR, codes=cgc, block_scales=sgc,
+                                            gscales=Sgc), 10), nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
+    out("f1", "nvfp4 16x1 columnwise + RHT per-tensor RNE (X^T, WGRAD)", [T5, H5], _time_us(
+        torch, lambda: m.nvfp4_quantize_rht(x5, 0x6B2D, codes=cgc, block_scales=sgc, gscales=Sgc), 10),
+        nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
+    out("a1-a3", "nvfp4 16x1 columnwise per-tensor RNE (X^T, WGRAD)", [T5, H5], _time_us(
+        torch, lambda: m.nvfp4_quantize(x5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=cgc,
+                                        block_scales=sgc, gscales=Sgc), 10),
+        nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
     w5 = synth.torch_normal_bf16((2 * I5, H5), 0.02, 53, dev)       # gate_up weight [N, K]
     nw = w5.numel()
     cw, sw, Sw = m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
@@ -529,6 +574,7 @@ def main():
         "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[4]) * 1e-3) / 1e12, 1),
         "kernels": kernels,
         "roofline": roofline,
+        "measured_reference": measured_reference(m, torch),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -183,6 +183,44 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           void* stream);
 
 /*
+ * nvfp4_quantize_rht -- columnwise NVFP4 copy (COL, 16x1 blocks, stored
+ * transposed) of the random Hadamard transform of x [rows, cols].  The NVFP4
+ * pretraining recipe applies this transform to the two inputs of the WGRAD
+ * GEMM only ("Train models faster with JAX and MaxText using NVFP4 on NVIDIA
+ * Blackwell", section "NVFP4 pretraining recipe"); FPROP and DGRAD operands
+ * use nvfp4_quantize.
+ *
+ * Each 16-row block v of every column becomes y = (1/4) H16 D v, H16 the
+ * Sylvester Hadamard matrix (entry (i,j) = (-1)^popcount(i & j)), D the
+ * diagonal with -1 where bit i of sign_mask is set and +1 elsewhere.  The
+ * matrix is orthogonal: quantize both WGRAD operands (dY and X, rows = tokens)
+ * with the SAME mask and dY^T X is unchanged before rounding.  The caller
+ * draws the mask (the transform's randomness) and may redraw it per step.
+ * Binary32: sign flips, then the butterfly over strides 1, 2, 4, 8 (each
+ * (a, b) -> (a + b, a - b), one rounded operation), then the exact scaling
+ * by 1/4.  y is then quantized exactly as nvfp4_quantize quantizes a COL
+ * copy of a binary32 input: A = max|y| over the tensor (PER_TENSOR, one extra
+ * read pass over x that computes the transform too) or S given (GIVEN), block
+ * scales from the 16-value block max|y|, RNE or stochastic rounding with the
+ * draw of element (row, col) of y.
+ *
+ *   sign_mask  bits 0..15 (higher bits: MXQ_EINVAL)
+ *   gs         PER_TENSOR or GIVEN (PER_ROW: MXQ_EUNSUPPORTED)
+ *   outputs    as nvfp4_quantize with block COL: codes [cols, rows/2] bytes
+ *              (ld_codes_bytes), block_scales per layout ([cols, rows/16]
+ *              LINEAR; MFMA needs cols % 32 == 0 and rows % 64 == 0), gscales[0]
+ * Shapes: rows % 16 == 0, cols % 16 == 0.  Alignment as nvfp4_quantize.  x
+ * must be finite.
+ */
+mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint32_t sign_mask, mxq_gscale gs, mxq_round rnd,
+                              uint64_t seed, uint32_t stream_id, uint32_t tensor_tag,
+                              mxq_scale_layout layout,
+                              uint8_t* codes, int64_t ld_codes_bytes,
+                              uint8_t* block_scales, float* gscales,
+                              void* stream);
+
+/*
  * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16 (the operand of the
  * dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
  * COL copy that is [input cols, input rows]); block says how its scales are

@@ -18,8 +18,8 @@ import os
 import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
-           "mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu",
-           "mx_gemm_set_tile", "library_path", "lib"]
+           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
+           "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmxq.so")
@@ -83,12 +83,15 @@ def lib():
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     L.mx_quantize.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, i64, vp, vp]
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
+    L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
+                                     vp, vp]
     L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
     L.mx_gemm.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
-    for f in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu", "mx_gemm_set_tile"):
+    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
+              "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
     L.mxq_status_str.restype = ctypes.c_char_p
@@ -186,6 +189,30 @@ def nvfp4_quantize(x, block=Block.ROW, gs=GScale.PER_ROW, rnd=Round.RNE, seed=0,
     _check(lib().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), int(block), int(gs), int(rnd),
                                 int(seed), int(stream_id), int(tensor_tag), int(layout), _ptr(codes),
                                 codes.stride(0), _ptr(block_scales), _ptr(gscales), _stream(stream)))
+    return codes, block_scales, gscales
+
+
+def nvfp4_quantize_rht(x, sign_mask, gs=GScale.PER_TENSOR, rnd=Round.RNE, seed=0, stream_id=1,
+                       tensor_tag=0, layout=Layout.LINEAR, codes=None, block_scales=None,
+                       gscales=None, stream=None):
+    """Columnwise NVFP4 copy of the random Hadamard transform of x (16-row
+    blocks, signs from the 16-bit sign_mask).  Returns (packed codes [cols,
+    rows/2], E4M3 block scales [cols, rows/16], FP32 S [1]), like
+    nvfp4_quantize with block=COL."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    gs = GScale(gs)
+    codes = _u8((cols, rows // 2), dev) if codes is None else codes
+    block_scales = _u8((cols, rows // 16), dev) if block_scales is None else block_scales
+    if gscales is None:
+        if gs == GScale.GIVEN:
+            raise ValueError("gs=GIVEN needs gscales")
+        gscales = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib().nvfp4_quantize_rht(_ptr(x), rows, cols, x.stride(0), int(sign_mask), int(gs),
+                                    int(rnd), int(seed), int(stream_id), int(tensor_tag),
+                                    int(layout), _ptr(codes), codes.stride(0), _ptr(block_scales),
+                                    _ptr(gscales), _stream(stream)))
     return codes, block_scales, gscales
 
 

@@ -160,8 +160,47 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                                  gmode, sr, seed, stream_id, tensor_tag, st);
   else
     e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                              gmode, sr, seed, stream_id, tensor_tag, st);
+                              gmode, mfma, sr, false, 0u, seed, stream_id, tensor_tag, st);
   return hip_status(e, "nvfp4_quantize");
+}
+
+mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint32_t sign_mask, mxq_gscale gs, mxq_round rnd, uint64_t seed,
+                              uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
+                              uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                              float* gscales, void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "nvfp4_quantize_rht: negative size");
+  if (sign_mask > 0xFFFFu) return fail(MXQ_EINVAL, "nvfp4_quantize_rht: sign_mask has bits above 15");
+  if (gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
+    return fail(gs == MXQ_GS_PER_ROW ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
+                "nvfp4_quantize_rht: the columnwise copy takes a PER_TENSOR or GIVEN second scale");
+  if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR) return fail(MXQ_EINVAL, "nvfp4_quantize_rht: bad rounding");
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
+    return fail(MXQ_EINVAL, "nvfp4_quantize_rht: bad scale layout");
+  if (rows == 0 || cols == 0) return ok();
+  if (!x || !codes || !block_scales || !gscales) return fail(MXQ_EINVAL, "nvfp4_quantize_rht: null pointer");
+  if (rows % 16 || cols % 16)
+    return fail(MXQ_ESHAPE, "nvfp4_quantize_rht: rows %% 16 and cols %% 16 must be 0 (rows=%lld, cols=%lld)",
+                (long long)rows, (long long)cols);
+  const bool mfma = layout == MXQ_LAYOUT_MFMA;
+  if (mfma && (cols % 32 || rows % 64))
+    return fail(MXQ_ESHAPE, "nvfp4_quantize_rht: MFMA layout needs cols %% 32 == 0 and rows %% 64 == 0");
+  if (ld_x < cols || ld_codes_bytes < rows / 2)
+    return fail(MXQ_EINVAL, "nvfp4_quantize_rht: leading dimension smaller than the row");
+  if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes_bytes % 8 ||
+      ((uintptr_t)gscales & 3u))
+    return fail(MXQ_EALIGN, "nvfp4_quantize_rht: x/codes must be 16-byte aligned, ld_x*2 %% 16 == 0, "
+                            "ld_codes_bytes %% 8 == 0, gscales 4-byte aligned");
+  hipStream_t st = S(stream);
+  hipError_t e = hipSuccess;
+  if (gs == MXQ_GS_PER_TENSOR) {
+    e = mxq::launch_nvfp4_tensor_scale_rht(x, rows, cols, ld_x, sign_mask, gscales, st);
+    if (e != hipSuccess) return hip_status(e, "nvfp4_quantize_rht (tensor amax)");
+  }
+  e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
+                            gs == MXQ_GS_PER_TENSOR ? 1 : 2, mfma, rnd == MXQ_ROUND_SR, true,
+                            sign_mask, seed, stream_id, tensor_tag, st);
+  return hip_status(e, "nvfp4_quantize_rht");
 }
 
 // ---------------------------------------------------------------- dequantize

@@ -29,10 +29,17 @@ hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, in
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
                                float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st);
+// rht: the random Hadamard transform of each 16-row block before quantizing
+// (sign_mask bit i negates row i of the block)
 hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                            float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
-                            uint32_t tag, hipStream_t st);
+                            float* gscales, int gmode, bool mfma, bool sr, bool rht,
+                            uint32_t sign_mask, uint64_t seed, uint32_t sid, uint32_t tag,
+                            hipStream_t st);
+// per-tensor amax of the transformed tensor (same protocol as above)
+hipError_t launch_nvfp4_tensor_scale_rht(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ld_x, uint32_t sign_mask, float* gscale,
+                                         hipStream_t st);
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,

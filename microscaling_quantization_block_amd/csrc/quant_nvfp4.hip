@@ -24,8 +24,9 @@
 //     token amax a wave reduction; 16-byte loads, two lanes per 16-block.
 //   * nvfp4_tile16_kernel: each lane owns 8 columns x 16 rows; two lanes form
 //     a 16x16 tile.
-//   * nvfp4_col_kernel: each lane owns 4 columns x 16 rows, each column one
-//     16x1 block, written into the transposed copy.
+//   * nvfp4_col_kernel: each lane owns 8 columns x 16 rows, each column one
+//     16x1 block, written into the transposed copy (optionally after the
+//     random Hadamard transform of the 16 rows).
 //   * per-tensor scale: a one-thread kernel zeroes gscale[0], then an
 //     unsigned atomic max on the magnitude bits (exact and order-independent)
 //     leaves A there tagged with bit 31.  The quantize kernel that follows
@@ -287,67 +288,91 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
 }
 
 // ------------------------------------------------------------ COL (16x1)
-// Lane owns columns [4j, 4j+4) of a 16-row strip; each column is one block of
-// the transposed copy ([cols, rows], 8 bytes per block).
-template <bool SR>
+// Each column of a 16-row strip is one block of the transposed copy ([cols,
+// rows], 8 bytes per block).
+//
+// RHT: the 16 values of the column are first replaced by (1/4) H16 D v, the
+// random Hadamard transform that the NVFP4 pretraining recipe applies to the
+// WGRAD inputs ("Train models faster with JAX and MaxText using NVFP4 on
+// NVIDIA Blackwell", section "NVFP4 pretraining recipe"): H16 the Sylvester
+// Hadamard matrix, D = diag(-1 where bit i of sign_mask is set).  Binary32:
+// sign flip (exact), butterfly strides 1, 2, 4, 8 (one rounded add or subtract
+// each), times 1/4 (exact).  The block amax and the codes come from these
+// binary32 values; the stochastic draws keep the element's [rows, cols] index.
+
+// The transform of one column's 16 values (binary32 bit patterns, row order).
+__device__ __forceinline__ void rht_column(const uint32_t (&bits)[16], uint32_t sign_mask,
+                                           float (&u)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = __uint_as_float(bits[i] ^ (((sign_mask >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = u[i], c = u[i + h];
+      u[i] = a + c;
+      u[i + h] = a - c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] *= 0.25f;
+}
+
+template <bool SR, bool RHT>
 __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
-    float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
-  const int64_t q4 = cols >> 2;
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 16;
+    float* __restrict__ gscales, int gmode, int mfma_layout, uint32_t sign_mask, uint64_t seed,
+    uint32_t stream_id, uint32_t tensor_tag, int64_t n_ct) {
   const float S = tensor_scale(gscales, gmode);
   if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
-  if (j >= q4) return;
-  uint2 v[16];
+  const int lane = threadIdx.x & 63;
+  const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
+  const int64_t strips = rows >> 4;
+  const int64_t strip = rt * 16 + (lane & 15);
+  const int64_t c0 = ct * 128 + (threadIdx.x >> 6) * 32 + (lane >> 4) * 8;
+  if (strip >= strips || c0 >= cols) return;
+  const int64_t r0 = strip * 16;
+  uint4 v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint2*>(x + (r0 + i) * ld_x + j * 4);
-  // column values: column cidx (0..3) of row i is half (cidx&1) of word (cidx>>1)
+  for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + c0);
   u32x4 dr[16];
   if (SR) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + j * 4) >> 3, seed, stream_id, tensor_tag);
+      dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + c0) >> 3, seed, stream_id, tensor_tag);
   }
-  const int64_t bpr = rows >> 4;
 #pragma unroll
-  for (int cidx = 0; cidx < 4; ++cidx) {
-    uint32_t colw[8];                 // 16 values of this column, two per word
+  for (int k = 0; k < 8; ++k) {
+    // column k of row i: half (k & 1) of word (k >> 1); so is its draw
+    uint32_t col[16];
     uint32_t rr16[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t wa = (cidx >> 1) ? v[2 * i].y : v[2 * i].x;
-      uint32_t wb = (cidx >> 1) ? v[2 * i + 1].y : v[2 * i + 1].x;
-      uint32_t ha = (cidx & 1) ? (wa >> 16) : (wa & 0xFFFFu);
-      uint32_t hb = (cidx & 1) ? (wb >> 16) : (wb & 0xFFFFu);
-      colw[i] = ha | (hb << 16);
-    }
-    if (SR) {
-      // element (r, 4j + cidx) has logical index idx = r*cols + 4j + cidx; its
-      // draw is half (idx & 1) of word ((idx & 7) >> 1) of block idx >> 3.
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint64_t idx = (uint64_t)((r0 + i) * cols + j * 4 + cidx);
-        uint32_t wsel = (uint32_t)((idx & 7) >> 1);
-        uint32_t w = wsel == 0 ? dr[i].x : wsel == 1 ? dr[i].y : wsel == 2 ? dr[i].z : dr[i].w;
-        rr16[i] = (idx & 1) ? (w >> 16) : (w & 0xFFFFu);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = (k >> 1) == 0 ? v[i].x : (k >> 1) == 1 ? v[i].y : (k >> 1) == 2 ? v[i].z : v[i].w;
+      col[i] = (k & 1) ? (w & 0xFFFF0000u) : (w << 16);            // binary32 bits
+      if (SR) {
+        const uint32_t d = (k >> 1) == 0 ? dr[i].x : (k >> 1) == 1 ? dr[i].y : (k >> 1) == 2 ? dr[i].z : dr[i].w;
+        rr16[i] = (k & 1) ? (d >> 16) : (d & 0xFFFFu);
       }
+    }
+    float u[16];
+    if (RHT) {
+      rht_column(col, sign_mask, u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = __uint_as_float(col[i]);
     }
     uint32_t mb = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mb = umax(mb, bf16x2_absmax_bits(colw[i]));
-    BlockScale bs = nv_block_scale(__uint_as_float(mb << 16), S);
-    uint32_t out[2] = {0, 0};
+    for (int i = 0; i < 16; ++i) mb = umax(mb, __float_as_uint(u[i]) & 0x7FFFFFFFu);
+    const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
+    // a zero block has r = 0, and a finite u times 0 is u's signed zero
     float yv[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float a = bf16_lo(colw[i]), b = bf16_hi(colw[i]);
-      float ya = a * bs.r, yb = b * bs.r;
-      if (bs.code == 0) { ya = __builtin_copysignf(0.0f, a); yb = __builtin_copysignf(0.0f, b); }
-      yv[2 * i] = ya;
-      yv[2 * i + 1] = yb;
-    }
+    for (int i = 0; i < 16; ++i) yv[i] = u[i] * bs.r;
+    uint32_t out[2] = {0, 0};
     if (SR) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -365,9 +390,9 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
       out[1] = e2m1_rne_pair<2>(out[1], yv[12], yv[13]);
       out[1] = e2m1_rne_pair<3>(out[1], yv[14], yv[15]);
     }
-    int64_t c = j * 4 + cidx;
+    const int64_t c = c0 + k;
     *reinterpret_cast<uint2*>(codes + c * ld_codes + (r0 >> 1)) = make_uint2(out[0], out[1]);
-    bscales[c * bpr + (r0 >> 4)] = (uint8_t)bs.code;
+    bscales[scale_offset(c, strip, strips, mfma_layout)] = (uint8_t)bs.code;
   }
 }
 
@@ -406,6 +431,49 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict
   }
 }
 
+
+// Max |y| over the transformed tensor y (see rht_column), as tagged binary32
+// magnitude bits.  Lane layout of the COL kernel (4 columns x 16 rows); a
+// workgroup walks the strips blockIdx.y, blockIdx.y + gridDim.y, ...
+__global__ __launch_bounds__(256) void nv_amax_rht_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t rows, int64_t cols, int64_t ld_x,
+                                                          uint32_t sign_mask,
+                                                          uint32_t* __restrict__ out_bits) {
+  const int64_t q4 = cols >> 2;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t strips = rows >> 4;
+  uint32_t m = 0;
+  if (j < q4) {
+    for (int64_t s = blockIdx.y; s < strips; s += gridDim.y) {
+      uint2 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = *reinterpret_cast<const uint2*>(x + (s * 16 + i) * ld_x + j * 4);
+#pragma unroll
+      for (int cidx = 0; cidx < 4; ++cidx) {
+        uint32_t bits[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t w = (cidx >> 1) ? v[i].y : v[i].x;
+          bits[i] = (cidx & 1) ? (w & 0xFFFF0000u) : (w << 16);
+        }
+        float u[16];
+        rht_column(bits, sign_mask, u);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = umax(m, __float_as_uint(u[i]) & 0x7FFFFFFFu);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = umax(m, lane_xor_u32(m, o));
+  __shared__ uint32_t wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = umax(umax(wm[0], wm[1]), umax(wm[2], wm[3]));
+    atomicMax(out_bits, b | 0x80000000u);
+  }
+}
 
 // ------------------------------------------------------------ launchers
 hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -483,16 +551,40 @@ hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, in
 
 hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                            float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
-                            uint32_t tag, hipStream_t st) {
-  dim3 grid((unsigned)((cols / 4 + 255) / 256), (unsigned)(rows / 16));
-  if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
-  if (sr)
-    hipLaunchKernelGGL((nvfp4_col_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
-  else
-    hipLaunchKernelGGL((nvfp4_col_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
+                            float* gscales, int gmode, bool mfma, bool sr, bool rht,
+                            uint32_t sign_mask, uint64_t seed, uint32_t sid, uint32_t tag,
+                            hipStream_t st) {
+  // workgroup tile 256 rows x 128 columns
+  const int64_t n_rt = (rows / 16 + 15) / 16, n_ct = (cols + 127) / 128;
+  const int64_t nwg = n_rt * n_ct;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), 0, st, x, rows, cols, ld_x, codes,
+                       ld_codes, bscales, gscales, gmode, (int)mfma, sign_mask, seed, sid, tag, n_ct);
+  };
+  if (rht) {
+    if (sr) go(nvfp4_col_kernel<true, true>);
+    else go(nvfp4_col_kernel<false, true>);
+  } else {
+    if (sr) go(nvfp4_col_kernel<true, false>);
+    else go(nvfp4_col_kernel<false, false>);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_tensor_scale_rht(const uint16_t* x, int64_t rows, int64_t cols,
+                                         int64_t ld_x, uint32_t sign_mask, float* gscale,
+                                         hipStream_t st) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(gscale);
+  hipLaunchKernelGGL(nv_zero_u32, dim3(1), dim3(1), 0, st, bits);
+  // about 2048 workgroups, each walking a share of the 16-row strips
+  const int64_t gx = (cols / 4 + 255) / 256;
+  int64_t gy = 2048 / gx;
+  if (gy < 1) gy = 1;
+  if (gy > rows / 16) gy = rows / 16;
+  if (gy > 65535) gy = 65535;
+  hipLaunchKernelGGL(nv_amax_rht_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, x,
+                     rows, cols, ld_x, sign_mask, bits);
   return hipGetLastError();
 }
 

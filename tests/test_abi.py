@@ -29,8 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "mx_dequantize", "mx_gemm", "mx_swiglu",
-                 "mxq_status_str", "mxq_last_error", "mxq_version"):
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
+                 "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
 
 
@@ -86,6 +86,25 @@ def test_nvfp4_quantize_rejects_bad_arguments():
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 20, FAKE, FAKE, None) == 3
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, None, None) == 1
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, 7, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 1
+
+
+def test_nvfp4_quantize_rht_rejects_bad_arguments():
+    m, L = _lib()
+    G, R, Lay = m.GScale, m.Round, m.Layout
+    call = lambda rows, cols, mask, gs, rnd=R.RNE, lay=Lay.LINEAR, ldc=16, x=FAKE, g=FAKE: \
+        L.nvfp4_quantize_rht(x, rows, cols, cols, mask, gs, rnd, 0, 1, 0, lay, FAKE, ldc, FAKE, g, None)
+    assert call(32, 32, 0x10000, G.PER_TENSOR) == 1
+    assert "sign_mask" in _err(L)
+    assert call(32, 32, 0x1234, G.PER_ROW) == 4
+    assert call(32, 32, 0x1234, G.NONE) == 1
+    assert call(24, 32, 0x1234, G.PER_TENSOR) == 2
+    assert call(32, 24, 0x1234, G.PER_TENSOR) == 2
+    assert call(32, 32, 0x1234, G.PER_TENSOR, rnd=5) == 1
+    assert call(32, 32, 0x1234, G.PER_TENSOR, lay=Lay.MFMA) == 2          # rows % 64
+    assert call(32, 32, 0x1234, G.PER_TENSOR, ldc=8) == 1                 # ld_codes < rows/2
+    assert call(32, 32, 0x1234, G.PER_TENSOR, x=FAKE_ODD) == 3
+    assert call(32, 32, 0x1234, G.PER_TENSOR, g=None) == 1
+    assert call(0, 32, 0x1234, G.PER_TENSOR) == 0                         # empty: nothing launched
 
 
 def test_mx_gemm_rejects_bad_arguments():
