@@ -88,13 +88,27 @@ __global__ __launch_bounds__(256) void mxfp8_row_kernel(
 }
 
 // ------------------------------------------------ COL / TILE / DUAL (LDS tile)
-// A workgroup stages a 32-row x 256-column BF16 tile in LDS.
-//  * rowwise part (ROW copy of DUAL): one thread per (row, 32-column block);
-//  * columnwise part (COL, DUAL): one thread per column, 32 rows, stored into
-//    the transposed copy as 32 contiguous bytes;
-//  * TILE: one thread per (row, block); the 32x32 amax is a 32-lane reduction;
-//    optionally also the transposed copy (the same codes, tile grid transposed).
-constexpr int TROWS = 32, TCOLS = 256, TPAD = 8;   // pad breaks LDS bank aliasing
+// A workgroup stages a 128-row x 128-column BF16 tile in LDS (16-byte loads,
+// each wave instruction four whole 256-byte row segments), then:
+//  * rowwise part (ROW copy of DUAL, TILE): thread = (row, 32-column block),
+//    block index fastest, so the four lanes of a row write its 128 code bytes
+//    side by side;
+//  * columnwise part (COL, DUAL, TILE's transposed copy): thread = (column,
+//    32-row group), group fastest, so the four threads of a column write its
+//    128 bytes of the transposed copy side by side;
+//  * TILE: a wave's rows are one 32-row group, so the 32x32 amax is a
+//    reduction over the wave's lanes of one block; the transposed copy reads
+//    the tile scales through LDS.
+// LDS holds 16-byte chunks (8 columns) of each 256-byte row; chunk ch of row
+// r sits at slot ch ^ (r & 3) ^ (4 * ((r >> 5) & 3)).  The first term spreads
+// the four rows read together by the rowwise part over all 16 slots, the
+// second spreads the four 32-row groups read together by the columnwise part
+// over the banks.
+constexpr int TR = 128, TC = 128;
+
+__device__ __forceinline__ int mx_slot(int r, int ch) {
+  return r * 16 + (ch ^ (r & 3) ^ (((r >> 5) & 3) << 2));
+}
 
 template <int MODE>   // 0 = COL, 1 = TILE, 2 = DUAL
 __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
@@ -102,100 +116,140 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ codes_col, int64_t ld_codes_col, uint8_t* __restrict__ scales_col,
     int mfma_layout) {
-  __shared__ uint16_t tile[TROWS][TCOLS + TPAD];
-  const int64_t r0 = (int64_t)blockIdx.y * TROWS;
-  const int64_t c0 = (int64_t)blockIdx.x * TCOLS;
+  __shared__ uint4 tile[TR * TC / 8];
+  __shared__ uint32_t tscale[4][4];            // TILE: scale of 32x32 tile (group, block)
+  const int64_t r0 = (int64_t)blockIdx.y * TR;
+  const int64_t c0 = (int64_t)blockIdx.x * TC;
   const int t = threadIdx.x;
-  // load: 32 rows x 256 cols = 1024 chunks of 8, 4 per thread
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = t + 256 * k, r = i >> 4, ch = i & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows && c0 + ch * 8 < cols)
+      v = *reinterpret_cast<const uint4*>(x + (r0 + r) * ld_x + c0 + ch * 8);
+    tile[mx_slot(r, ch)] = v;
+  }
+  __syncthreads();
+
+  if (MODE == 1 || MODE == 2) {
+    // wave w owns rows 32w .. 32w + 31 (one 32-row group): lane l takes row
+    // 32w + 16k + l / 4, block l % 4
+    const int w = t >> 6, l = t & 63, j = l & 3;
+    uint4 v[2][4];
+    uint32_t m[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 32 * w + 16 * k + (l >> 2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[k][q] = tile[mx_slot(r, 4 * j + q)];
+      m[k] = umax(umax(absmax8(v[k][0]), absmax8(v[k][1])), umax(absmax8(v[k][2]), absmax8(v[k][3])));
+    }
+    uint32_t s[2];
+    if (MODE == 1) {
+      uint32_t mt = umax(m[0], m[1]);
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) mt = umax(mt, lane_xor_u32(mt, o));
+      s[0] = s[1] = e8m0_from_amax_bits(mt);
+    } else {
+      s[0] = e8m0_from_amax_bits(m[0]);
+      s[1] = e8m0_from_amax_bits(m[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 32 * w + 16 * k + (l >> 2);
+      if (r0 + r < rows && c0 + 32 * j < cols) {
+        const uint2 o0 = mx_encode8(v[k][0], s[k]), o1 = mx_encode8(v[k][1], s[k]);
+        const uint2 o2 = mx_encode8(v[k][2], s[k]), o3 = mx_encode8(v[k][3], s[k]);
+        uint8_t* dst = codes + (r0 + r) * ld_codes + c0 + 32 * j;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o0.x, o0.y, o1.x, o1.y);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o2.x, o2.y, o3.x, o3.y);
+        if (MODE == 1) {
+          if ((r & 31) == 0) {
+            scales[((r0 + r) >> 5) * (cols >> 5) + ((c0 >> 5) + j)] = (uint8_t)s[k];
+            tscale[w][j] = s[k];
+          }
+        } else {
+          scales[scale_offset(r0 + r, (c0 >> 5) + j, cols >> 5, mfma_layout)] = (uint8_t)s[k];
+        }
+      }
+    }
+  }
+  if (MODE == 0 || MODE == 2 || (MODE == 1 && codes_col)) {
+    if (MODE == 1) __syncthreads();              // tscale
+    uint8_t* dcodes = MODE == 0 ? codes : codes_col;
+    uint8_t* dscales = MODE == 0 ? scales : scales_col;
+    const int64_t ldc = MODE == 0 ? ld_codes : ld_codes_col;
+    const uint16_t* tv = reinterpret_cast<const uint16_t*>(tile);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = t + 256 * k, g = i & 3, c = i >> 2;
+      if (r0 + 32 * g >= rows || c0 + c >= cols) continue;
+      uint32_t col[16];                          // 32 values, two per word (row pairs)
+      uint32_t m = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t a = tv[mx_slot(32 * g + 2 * q, c >> 3) * 8 + (c & 7)];
+        const uint32_t b = tv[mx_slot(32 * g + 2 * q + 1, c >> 3) * 8 + (c & 7)];
+        col[q] = a | (b << 16);
+        m = umax(m, bf16x2_absmax_bits(col[q]));
+      }
+      const uint32_t s = MODE == 1 ? tscale[g][c >> 5] : e8m0_from_amax_bits(m);
+      uint32_t o[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint2 e = mx_encode8(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
+        o[2 * q] = e.x;
+        o[2 * q + 1] = e.y;
+      }
+      uint8_t* dst = dcodes + (c0 + c) * ldc + r0 + 32 * g;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+      if (MODE == 1) {
+        if ((c & 31) == 0) scales_col[((c0 + c) >> 5) * (rows >> 5) + ((r0 >> 5) + g)] = (uint8_t)s;
+      } else {
+        dscales[scale_offset(c0 + c, (r0 >> 5) + g, rows >> 5, mfma_layout)] = (uint8_t)s;
+      }
+    }
+  }
+}
+
+// TILE without the transposed copy: a 32-row x 256-column tile per workgroup
+// (twice the workgroups of the 128x128 kernel, which pays off when nothing is
+// written column-wise).  Thread = (row, block) with the row fastest, so the
+// 32 lanes of a block hold the tile's 32 rows and the 32x32 amax is a lane
+// reduction.
+constexpr int T32R = 32, T32C = 256, T32PAD = 8;   // pad breaks LDS bank aliasing
+
+__global__ __launch_bounds__(256) void mxfp8_tile32_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales) {
+  __shared__ uint16_t tile[T32R][T32C + T32PAD];
+  const int64_t r0 = (int64_t)blockIdx.y * T32R;
+  const int64_t c0 = (int64_t)blockIdx.x * T32C;
+  const int t = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int chunk = t + 256 * k;
-    int rr = chunk >> 5, cc = (chunk & 31) * 8;
+    const int chunk = t + 256 * k, rr = chunk >> 5, cc = (chunk & 31) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (c0 + cc < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + rr) * ld_x + c0 + cc);
     *reinterpret_cast<uint4*>(&tile[rr][cc]) = v;
   }
   __syncthreads();
-
-  if (MODE == 1 || MODE == 2) {
-    // (row, block) per thread: threads 0..31 = rows 0..31 of block 0, etc.
-    const int rr = t & 31, blk = t >> 5;
-    const int cc = blk * 32;
-    const bool valid = c0 + cc < cols;
-    uint4 v[4];
+  const int rr = t & 31, cc = (t >> 5) * 32;
+  uint4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4*>(&tile[rr][cc + 8 * q]);
-    uint32_t m = umax(umax(absmax8(v[0]), absmax8(v[1])), umax(absmax8(v[2]), absmax8(v[3])));
-    if (MODE == 1) {
+  for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4*>(&tile[rr][cc + 8 * q]);
+  uint32_t m = umax(umax(absmax8(v[0]), absmax8(v[1])), umax(absmax8(v[2]), absmax8(v[3])));
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) m = umax(m, lane_xor_u32(m, o));
-    }
-    uint32_t s = e8m0_from_amax_bits(m);
-    if (valid) {
-      uint2 o0 = mx_encode8(v[0], s), o1 = mx_encode8(v[1], s);
-      uint2 o2 = mx_encode8(v[2], s), o3 = mx_encode8(v[3], s);
-      uint8_t* dst = codes + (r0 + rr) * ld_codes + c0 + cc;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o0.x, o0.y, o1.x, o1.y);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o2.x, o2.y, o3.x, o3.y);
-      if (MODE == 1) {
-        if (rr == 0) scales[(r0 >> 5) * (cols >> 5) + ((c0 + cc) >> 5)] = (uint8_t)s;
-      } else {
-        scales[scale_offset(r0 + rr, (c0 + cc) >> 5, cols >> 5, mfma_layout)] = (uint8_t)s;
-      }
-    }
-    // TILE with a transposed copy: a 32x32 tile's scale is shared by its rows
-    // and columns, so the transposed copy is the same codes transposed.  The
-    // thread of (row rr, block blk) also encodes column 32 blk + rr of the
-    // staged tile with the block's scale s (it holds s after the reduction)
-    // and writes it as 32 contiguous bytes of codes_col [cols, rows].
-    if (MODE == 1 && codes_col) {
-      const int ct = cc + rr;                        // tile column of this thread
-      if (c0 + ct < cols) {
-        uint32_t col[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          col[q] = (uint32_t)tile[2 * q][ct] | ((uint32_t)tile[2 * q + 1][ct] << 16);
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint2 e = mx_encode8(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
-          o[2 * q] = e.x;
-          o[2 * q + 1] = e.y;
-        }
-        uint8_t* dst = codes_col + (c0 + ct) * ld_codes_col + r0;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-        if (rr == 0) scales_col[((c0 + cc) >> 5) * (rows >> 5) + (r0 >> 5)] = (uint8_t)s;
-      }
-    }
-  }
-  if (MODE == 0 || MODE == 2) {
-    uint8_t* dcodes = MODE == 0 ? codes : codes_col;
-    uint8_t* dscales = MODE == 0 ? scales : scales_col;
-    const int64_t ldc = MODE == 0 ? ld_codes : ld_codes_col;
-    const int cc = t;                      // one column per thread
-    if (c0 + cc < cols) {
-      uint32_t col[16];                    // 32 values, two per word (row pairs)
-      uint32_t m = 0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        uint32_t a = tile[2 * q][cc], b = tile[2 * q + 1][cc];
-        col[q] = a | (b << 16);
-        m = umax(m, bf16x2_absmax_bits(col[q]));
-      }
-      uint32_t s = e8m0_from_amax_bits(m);
-      uint32_t o[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint2 e = mx_encode8(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
-        o[2 * q] = e.x;
-        o[2 * q + 1] = e.y;
-      }
-      uint8_t* dst = dcodes + (c0 + cc) * ldc + r0;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-      dscales[scale_offset(c0 + cc, r0 >> 5, rows >> 5, mfma_layout)] = (uint8_t)s;
-    }
+  for (int o = 1; o < 32; o <<= 1) m = umax(m, lane_xor_u32(m, o));
+  const uint32_t s = e8m0_from_amax_bits(m);
+  if (c0 + cc < cols) {
+    const uint2 o0 = mx_encode8(v[0], s), o1 = mx_encode8(v[1], s);
+    const uint2 o2 = mx_encode8(v[2], s), o3 = mx_encode8(v[3], s);
+    uint8_t* dst = codes + (r0 + rr) * ld_codes + c0 + cc;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(o0.x, o0.y, o1.x, o1.y);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o2.x, o2.y, o3.x, o3.y);
+    if (rr == 0) scales[(r0 >> 5) * (cols >> 5) + ((c0 + cc) >> 5)] = (uint8_t)s;
   }
 }
 
@@ -217,7 +271,14 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
                              int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
                              bool mfma, hipStream_t st) {
-  dim3 grid((unsigned)((cols + TCOLS - 1) / TCOLS), (unsigned)(rows / TROWS));
+  if (mode == 1 && !codes_col) {
+    dim3 g32((unsigned)((cols + T32C - 1) / T32C), (unsigned)(rows / T32R));
+    if (g32.y > 65535u) return hipErrorInvalidValue;     // more row strips than a grid holds
+    hipLaunchKernelGGL(mxfp8_tile32_kernel, g32, dim3(256), 0, st, x, rows, cols, ld_x, codes,
+                       ld_codes, scales);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)((cols + TC - 1) / TC), (unsigned)((rows + TR - 1) / TR));
   if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   if (mode == 0)
     hipLaunchKernelGGL((mxfp8_tile_kernel<0>), grid, dim3(256), 0, st, x, rows, cols, ld_x,

@@ -103,7 +103,7 @@ def test_mxfp8_every_bf16_value_under_every_exponent():
     assert np.array_equal(from_dev_bf16(dq), OM.dequantize_bf16(rc, rs))
 
 
-@pytest.mark.parametrize("shape", [(64, 96), (96, 512), (32, 32), (256, 288)])
+@pytest.mark.parametrize("shape", [(64, 96), (96, 512), (32, 32), (256, 288), (160, 416), (384, 1024)])
 def test_mxfp8_col_tile_dual(shape):
     m = mxq()
     x = _edge_bf16(*shape, 11)
