@@ -287,6 +287,9 @@ def rows_report():
     cx, sx, Sx = m.nvfp4_quantize(x5)
     out("a1-a3", "nvfp4 1x16 per-token RNE (X)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
         x5, codes=cx, block_scales=sx, gscales=Sx), 10), nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
+    out("f2", "nvfp4 1x16 per-token RNE + Four-Over-Six (X)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
+        x5, rnd=m.Round.RNE_4OVER6, codes=cx, block_scales=sx, gscales=Sx), 10),
+        nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
     dy5 = synth.torch_normal_bf16((T5, H5), 1e-3, 52, dev)          # down-projection output gradient
     cg, sg, Sg = m.nvfp4_quantize(dy5, rnd=m.Round.SR)
     out("a1-a3", "nvfp4 1x16 per-token SR (dY)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
@@ -311,6 +314,10 @@ def rows_report():
     cw, sw, Sw = m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
     out("a1-a3", "nvfp4 16x16 per-tensor (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
         w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=cw, block_scales=sw, gscales=Sw), 10),
+        nbytes=2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    out("f2", "nvfp4 16x16 per-tensor + Four-Over-Six (W_gate_up)", [2 * I5, H5], _time_us(
+        torch, lambda: m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
+                                        rnd=m.Round.RNE_4OVER6, codes=cw, block_scales=sw, gscales=Sw), 10),
         nbytes=2 * nw * 2 + nw // 2 + nw // 256 + 4)
     wdq = torch.empty_like(w5)
     out("a4", "nvfp4 dequantize 16x16 -> bf16 (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.mx_dequantize(

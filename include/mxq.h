@@ -89,7 +89,19 @@ typedef enum {
 
 typedef enum {
   MXQ_ROUND_RNE = 0,     /* round to nearest, ties to even                      */
-  MXQ_ROUND_SR = 1       /* stochastic rounding (NVFP4 elements only)           */
+  MXQ_ROUND_SR = 1,      /* stochastic rounding (NVFP4 elements only)           */
+  /* NVFP4 ROW and TILE copies: RNE with the Four-Over-Six block-scale choice
+   * ("NVFP4 RL training" / "The 4-bitter Lesson", section on Four-Over-Six
+   * for RL weights and activations).  Each block (or 16x16 tile) is encoded
+   * under s6 = E4M3(fl(a_b / fl(6*S))) and s4 = E4M3(fl(a_b / fl(4*S)))
+   * (both RNE, saturating at 448) and keeps s4 iff the binary32 sum of its
+   * squared dequantization errors e = fl(x - fl(fl(value(code)*s_b)*S)),
+   * squared with one rounding each, is strictly smaller.  The sum is a
+   * pairwise tree in element order (neighbours first); a tile sums each
+   * row's 16 squares by that tree and then the 16 row sums by it.  Ties keep
+   * s6.  The stored copy is plain NVFP4 (the chosen s_b is its block scale),
+   * so mx_dequantize and mx_gemm read it unchanged. */
+  MXQ_ROUND_RNE_4OVER6 = 2
 } mxq_round;
 
 typedef enum {
@@ -162,7 +174,7 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
  *           TILE (16x16): codes [rows, cols/2], block_scales [rows/16, cols/16]
  *                        LINEAR; PER_TENSOR or GIVEN only
  *   gs      PER_ROW (ROW only), PER_TENSOR, GIVEN
- *   rnd     RNE or SR
+ *   rnd     RNE, SR, or RNE_4OVER6 (ROW and TILE; COL gives MXQ_EUNSUPPORTED)
  *   codes   two E2M1 codes per byte, even element in the low nibble
  *   gscales PER_ROW/PER_TENSOR: written; GIVEN: read (caller's S >= 0)
  * With PER_TENSOR the call enqueues an extra read pass over x for A, using

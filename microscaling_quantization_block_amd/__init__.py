@@ -49,6 +49,7 @@ class GScale(enum.IntEnum):
 class Round(enum.IntEnum):
     RNE = 0
     SR = 1
+    RNE_4OVER6 = 2
 
 
 class Layout(enum.IntEnum):

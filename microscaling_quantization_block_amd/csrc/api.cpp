@@ -115,7 +115,10 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                 "nvfp4_quantize: block must be ROW, COL or TILE");
   if (gs != MXQ_GS_PER_ROW && gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
     return fail(MXQ_EINVAL, "nvfp4_quantize: gs must be PER_ROW, PER_TENSOR or GIVEN");
-  if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR) return fail(MXQ_EINVAL, "nvfp4_quantize: bad rounding");
+  if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR && rnd != MXQ_ROUND_RNE_4OVER6)
+    return fail(MXQ_EINVAL, "nvfp4_quantize: bad rounding");
+  if (rnd == MXQ_ROUND_RNE_4OVER6 && block == MXQ_BLOCK_COL)
+    return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize: the Four-Over-Six choice is for ROW and TILE copies");
   if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
     return fail(MXQ_EINVAL, "nvfp4_quantize: bad scale layout");
   if (gs == MXQ_GS_PER_ROW && block != MXQ_BLOCK_ROW)
@@ -143,7 +146,7 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     return fail(MXQ_EALIGN, "nvfp4_quantize: x/codes must be 16-byte aligned, ld_x*2 %% 16 == 0, "
                             "ld_codes_bytes %% 8 == 0, gscales 4-byte aligned");
   hipStream_t st = S(stream);
-  const bool sr = rnd == MXQ_ROUND_SR;
+  const int rm = rnd == MXQ_ROUND_SR ? 1 : rnd == MXQ_ROUND_RNE_4OVER6 ? 2 : 0;
   hipError_t e = hipSuccess;
   // per-tensor: the amax kernel leaves a tagged amax in gscales[0], which the
   // quantize kernel turns into S (and stores back)
@@ -154,13 +157,13 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   const int gmode = gs == MXQ_GS_PER_ROW ? 0 : gs == MXQ_GS_PER_TENSOR ? 1 : 2;
   if (block == MXQ_BLOCK_ROW)
     e = mxq::launch_nvfp4_row(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                              gmode, mfma, sr, seed, stream_id, tensor_tag, st);
+                              gmode, mfma, rm, seed, stream_id, tensor_tag, st);
   else if (block == MXQ_BLOCK_TILE)
     e = mxq::launch_nvfp4_tile16(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                                 gmode, sr, seed, stream_id, tensor_tag, st);
+                                 gmode, rm, seed, stream_id, tensor_tag, st);
   else
     e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                              gmode, mfma, sr, false, 0u, seed, stream_id, tensor_tag, st);
+                              gmode, mfma, rm == 1, false, 0u, seed, stream_id, tensor_tag, st);
   return hip_status(e, "nvfp4_quantize");
 }
 
@@ -174,6 +177,8 @@ mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int
   if (gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
     return fail(gs == MXQ_GS_PER_ROW ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
                 "nvfp4_quantize_rht: the columnwise copy takes a PER_TENSOR or GIVEN second scale");
+  if (rnd == MXQ_ROUND_RNE_4OVER6)
+    return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize_rht: the Four-Over-Six choice is for ROW and TILE copies");
   if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR) return fail(MXQ_EINVAL, "nvfp4_quantize_rht: bad rounding");
   if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
     return fail(MXQ_EINVAL, "nvfp4_quantize_rht: bad scale layout");

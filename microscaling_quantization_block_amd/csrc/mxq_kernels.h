@@ -20,14 +20,15 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
 hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                      float* gscale, hipStream_t st);
 // gmode: 0 = per row (computed), 1 = per tensor (tagged amax in gscales[0]),
-// 2 = given (S in gscales[0])
+// 2 = given (S in gscales[0]).  rm: 0 = RNE, 1 = stochastic rounding, 2 = RNE
+// with the Four-Over-Six block-scale choice.
 hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
-                            int gmode, bool mfma, bool sr, uint64_t seed, uint32_t sid,
+                            int gmode, bool mfma, int rm, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st);
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                               float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
+                               float* gscales, int gmode, int rm, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st);
 // rht: the random Hadamard transform of each 16-row block before quantizing
 // (sign_mask bit i negates row i of the block)

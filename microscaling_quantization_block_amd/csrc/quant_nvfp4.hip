@@ -43,11 +43,13 @@ namespace mxq {
 // a BF16 magnitude widened) and S.
 struct BlockScale { uint32_t code; float r; };
 
-__device__ __forceinline__ BlockScale nv_block_scale(float a_b, float S) {
+// m = 6 maps the block max onto the largest E2M1 value (plain NVFP4); m = 4
+// is Four-Over-Six's second candidate.
+__device__ __forceinline__ BlockScale nv_block_scale(float a_b, float S, float m = 6.0f) {
   BlockScale bs;
   if (!(S > 0.0f)) { bs.code = 0; bs.r = 0.0f; return bs; }
-  float six_s = 6.0f * S;
-  float t = a_b / six_s;
+  float m_s = m * S;
+  float t = a_b / m_s;
   // saturating encode: with a caller-given S, t may exceed the E4M3 range
   // (every value >= 448 rounds to 448; the hardware conversion would not
   // saturate on its own)
@@ -111,6 +113,57 @@ __device__ __forceinline__ uint32_t amax8_bits(uint4 v) {
   return m << 16;
 }
 
+// ------------------------------------------------------------ Four-Over-Six
+// "NVFP4 RL training" / "The 4-bitter Lesson", section on Four-Over-Six for
+// RL weights and activations: a block may scale its max onto 4 instead of 6,
+// which moves values near the max out of the grid's widest gap.  Each block
+// is encoded under both block scales (a_b / (6 S) and a_b / (4 S), E4M3,
+// saturating), and keeps 4 iff the binary32 sum of squared dequantization
+// errors is strictly smaller.  The sum is a pairwise tree in element order
+// (neighbours first); for a 16x16 tile, each row's 16 squares by that tree,
+// then the 16 row sums by it in row order.  A dequantized value is
+// fl(fl(value(code) s_b) S), as the dequantizer computes it.
+
+// Squares of the 8 errors of one chunk (BF16 values v, codes q), summed by
+// the first three levels of the tree.
+__device__ __forceinline__ float nv_sse8(uint4 v, uint32_t q, float sb, float S) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  mxq_f32x2 c[4];
+  c[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+  c[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+  c[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+  c[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ea = bf16_lo(w[i]) - (c[i].x * sb) * S;
+    const float eb = bf16_hi(w[i]) - (c[i].y * sb) * S;
+    p[i] = ea * ea + eb * eb;                 // three roundings, no fused multiply-add
+  }
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// One candidate's codes for a chunk of 8 values and the chunk's error sum.
+struct Cand8 { uint32_t q; float e; };
+__device__ __forceinline__ Cand8 nv_cand8(uint4 v, const BlockScale& bs, float S) {
+  const u32x4 none = {0, 0, 0, 0};
+  Cand8 c;
+  c.q = nv_encode8<false>(v, bs.r, none);
+  c.e = nv_sse8(v, c.q, e4m3_to_f32(bs.code), S);
+  return c;
+}
+
+// A whole 16-value block held by one lane: the chosen scale code and codes.
+struct Enc16 { uint32_t code, q0, q1; };
+__device__ __forceinline__ Enc16 nv_encode16_46(uint4 v0, uint4 v1, float a_b, float S) {
+  const BlockScale b6 = nv_block_scale(a_b, S, 6.0f), b4 = nv_block_scale(a_b, S, 4.0f);
+  const Cand8 x60 = nv_cand8(v0, b6, S), x61 = nv_cand8(v1, b6, S);
+  const Cand8 x40 = nv_cand8(v0, b4, S), x41 = nv_cand8(v1, b4, S);
+  const float e6 = x60.e + x61.e, e4 = x40.e + x41.e;
+  if (e4 < e6) return Enc16{b4.code, x40.q, x41.q};
+  return Enc16{b6.code, x60.q, x61.q};
+}
+
 // Second-level scale of a tensor-scaled call.  gmode 1: gscale[0] holds the
 // tagged amax (bit 31 set) or, once some block wrote it back, S itself.
 // gmode 2: S given by the caller.
@@ -129,12 +182,14 @@ __device__ __forceinline__ float tensor_scale(const float* g, int gmode) {
 // while the current one is encoded; a prefetch past the end is clamped to
 // the last row (a valid address, never used).  FULL: every lane's blocks
 // exist (cols == 1024 BPT).
-template <int BPT, bool SR, bool FULL>
+// RM: 0 = RNE, 1 = stochastic rounding, 2 = RNE with the Four-Over-Six choice.
+template <int BPT, int RM, bool FULL>
 __global__ __launch_bounds__(256) void nvfp4_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
     uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t W = (int64_t)gridDim.x * 4;
   int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -174,17 +229,26 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
     for (int k = 0; k < BPT; ++k) {
       const int64_t b = lane + 64 * k;
       if (FULL || b < bpr) {
-        const BlockScale bs = nv_block_scale(__uint_as_float(ab[k]), S);
-        u32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
-        if (SR) {
-          const uint64_t n = (uint64_t)(r * cols + b * 16) >> 3;
-          d0 = philox_draws8(n, seed, stream_id, tensor_tag);
-          d1 = philox_draws8(n + 1, seed, stream_id, tensor_tag);
+        uint32_t q0, q1, code;
+        if (RM == 2) {
+          const Enc16 e = nv_encode16_46(v[k][0], v[k][1], __uint_as_float(ab[k]), S);
+          q0 = e.q0;
+          q1 = e.q1;
+          code = e.code;
+        } else {
+          const BlockScale bs = nv_block_scale(__uint_as_float(ab[k]), S);
+          u32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+          if (SR) {
+            const uint64_t n = (uint64_t)(r * cols + b * 16) >> 3;
+            d0 = philox_draws8(n, seed, stream_id, tensor_tag);
+            d1 = philox_draws8(n + 1, seed, stream_id, tensor_tag);
+          }
+          q0 = nv_encode8<SR>(v[k][0], bs.r, d0);
+          q1 = nv_encode8<SR>(v[k][1], bs.r, d1);
+          code = bs.code;
         }
-        const uint32_t q0 = nv_encode8<SR>(v[k][0], bs.r, d0);
-        const uint32_t q1 = nv_encode8<SR>(v[k][1], bs.r, d1);
         *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = make_uint2(q0, q1);
-        bscales[scale_offset(r, b, bpr, mfma_layout)] = (uint8_t)bs.code;
+        bscales[scale_offset(r, b, bpr, mfma_layout)] = (uint8_t)code;
       }
     }
   };
@@ -204,12 +268,13 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
 
 // Rows too long to keep in registers: two passes over the row (the second
 // read is served from cache).  One wave per row.
-template <bool SR>
+template <int RM>
 __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
     uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -234,13 +299,27 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     uint4 v = c < cpr ? *reinterpret_cast<const uint4*>(xr + c * 8) : make_uint4(0, 0, 0, 0);
     uint32_t ab = amax8_bits(v);
     float a = __uint_as_float(umax(ab, lane_xor_u32(ab, 1)));
-    if (c < cpr) {
-      BlockScale bs = nv_block_scale(a, S);
+    uint32_t q, code;
+    if (RM == 2) {
+      // the block's two halves sit in lanes c and c ^ 1: the tree's last
+      // level adds their half sums (the same in both lanes)
+      const BlockScale b6 = nv_block_scale(a, S, 6.0f), b4 = nv_block_scale(a, S, 4.0f);
+      const Cand8 x6 = nv_cand8(v, b6, S), x4 = nv_cand8(v, b4, S);
+      const float e6 = x6.e + __uint_as_float(lane_xor_u32(__float_as_uint(x6.e), 1));
+      const float e4 = x4.e + __uint_as_float(lane_xor_u32(__float_as_uint(x4.e), 1));
+      const bool take4 = e4 < e6;
+      q = take4 ? x4.q : x6.q;
+      code = take4 ? b4.code : b6.code;
+    } else {
+      const BlockScale bs = nv_block_scale(a, S);
       u32x4 dr = {0, 0, 0, 0};
-      if (SR) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
-      uint32_t q = nv_encode8<SR>(v, bs.r, dr);
+      if (SR && c < cpr) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
+      q = nv_encode8<SR>(v, bs.r, dr);
+      code = bs.code;
+    }
+    if (c < cpr) {
       *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
-      if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)bs.code;
+      if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)code;
     }
   }
 }
@@ -250,12 +329,13 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
 // owns columns [8j, 8j+8) of rows 4rg..4rg+3 of the strip, and the 8 lanes
 // {16 rg + 2t, 16 rg + 2t + 1 : rg = 0..3} form tile t (amax by three lane
 // exchanges).  Consecutive lanes read consecutive 16-byte chunks of a row.
-template <bool SR>
+template <int RM>
 __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id,
     uint32_t tensor_tag) {
+  constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t cpr = cols >> 3;
   const int64_t j = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + (lane & 15);
@@ -274,6 +354,40 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
   mb = umax(mb, lane_xor_u32(mb, 32));
   const float S = tensor_scale(gscales, gmode);
   if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
+  if (RM == 2) {
+    // Four-Over-Six per tile.  Tree order: a lane's 8 columns of a row (three
+    // levels), the row's other half in lane ^ 1, the lane's 4 rows (two
+    // levels), then the row groups in lane ^ 16 and lane ^ 32.  Every lane of
+    // the tile ends with the same sums (each addition is commutative); lanes
+    // of a tile past the last column carry unused values through the
+    // exchanges and store nothing.
+    const BlockScale b6 = nv_block_scale(__uint_as_float(mb), S, 6.0f);
+    const BlockScale b4 = nv_block_scale(__uint_as_float(mb), S, 4.0f);
+    uint32_t q6[4], q4[4];
+    float r6[4], r4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Cand8 c6 = nv_cand8(v[i], b6, S), c4 = nv_cand8(v[i], b4, S);
+      q6[i] = c6.q;
+      q4[i] = c4.q;
+      r6[i] = c6.e + __uint_as_float(lane_xor_u32(__float_as_uint(c6.e), 1));
+      r4[i] = c4.e + __uint_as_float(lane_xor_u32(__float_as_uint(c4.e), 1));
+    }
+    float e6 = (r6[0] + r6[1]) + (r6[2] + r6[3]);
+    float e4 = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    e6 = e6 + __uint_as_float(lane_xor_u32(__float_as_uint(e6), 16));
+    e4 = e4 + __uint_as_float(lane_xor_u32(__float_as_uint(e4), 16));
+    e6 = e6 + __uint_as_float(lane_xor_u32(__float_as_uint(e6), 32));
+    e4 = e4 + __uint_as_float(lane_xor_u32(__float_as_uint(e4), 32));
+    const bool take4 = e4 < e6;
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint32_t*>(codes + (r0 + i) * ld_codes + j * 4) = take4 ? q4[i] : q6[i];
+    if ((j & 1) == 0 && rg == 0)
+      bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)(take4 ? b4.code : b6.code);
+    return;
+  }
   if (!valid) return;
   const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
 #pragma unroll
@@ -490,7 +604,7 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t co
 }
 
 
-template <bool SR>
+template <int RM>
 static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                                int gmode, bool mfma, uint64_t seed, uint32_t sid, uint32_t tag,
@@ -507,17 +621,17 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
     hipLaunchKernelGGL(kern, grid, block, 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
                        gscales, gmode, (int)mfma, seed, sid, tag);
   };
-  if (bpr == 64) go(nvfp4_row_kernel<1, SR, true>);
-  else if (bpr < 64) go(nvfp4_row_kernel<1, SR, false>);
-  else if (bpr == 128) go(nvfp4_row_kernel<2, SR, true>);
-  else if (bpr < 128) go(nvfp4_row_kernel<2, SR, false>);
-  else if (bpr == 256) go(nvfp4_row_kernel<4, SR, true>);
-  else if (bpr < 256) go(nvfp4_row_kernel<4, SR, false>);
-  else if (bpr == 512) go(nvfp4_row_kernel<8, SR, true>);
-  else if (bpr < 512) go(nvfp4_row_kernel<8, SR, false>);
+  if (bpr == 64) go(nvfp4_row_kernel<1, RM, true>);
+  else if (bpr < 64) go(nvfp4_row_kernel<1, RM, false>);
+  else if (bpr == 128) go(nvfp4_row_kernel<2, RM, true>);
+  else if (bpr < 128) go(nvfp4_row_kernel<2, RM, false>);
+  else if (bpr == 256) go(nvfp4_row_kernel<4, RM, true>);
+  else if (bpr < 256) go(nvfp4_row_kernel<4, RM, false>);
+  else if (bpr == 512) go(nvfp4_row_kernel<8, RM, true>);
+  else if (bpr < 512) go(nvfp4_row_kernel<8, RM, false>);
   else
     // one wave per row (no row loop in this kernel)
-    hipLaunchKernelGGL(nvfp4_row_long_kernel<SR>, dim3((unsigned)((rows + 3) / 4)), block, 0, st, x,
+    hipLaunchKernelGGL(nvfp4_row_long_kernel<RM>, dim3((unsigned)((rows + 3) / 4)), block, 0, st, x,
                        rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed,
                        sid, tag);
   return hipGetLastError();
@@ -525,27 +639,32 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
 
 hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
-                            int gmode, bool mfma, bool sr, uint64_t seed, uint32_t sid,
+                            int gmode, bool mfma, int rm, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st) {
-  return sr ? row_dispatch<true>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode,
-                                 mfma, seed, sid, tag, st)
-            : row_dispatch<false>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode,
-                                  mfma, seed, sid, tag, st);
+  if (rm == 1)
+    return row_dispatch<1>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma,
+                           seed, sid, tag, st);
+  if (rm == 2)
+    return row_dispatch<2>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma,
+                           seed, sid, tag, st);
+  return row_dispatch<0>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma, seed,
+                         sid, tag, st);
 }
 
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
-                               float* gscales, int gmode, bool sr, uint64_t seed, uint32_t sid,
+                               float* gscales, int gmode, int rm, uint64_t seed, uint32_t sid,
                                uint32_t tag, hipStream_t st) {
   // four waves per workgroup, each 128 columns of a 16-row strip
   dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
   if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
-  if (sr)
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
-  else
-    hipLaunchKernelGGL((nvfp4_tile16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, seed, sid, tag);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
+                       gscales, gmode, seed, sid, tag);
+  };
+  if (rm == 1) go(nvfp4_tile16_kernel<1>);
+  else if (rm == 2) go(nvfp4_tile16_kernel<2>);
+  else go(nvfp4_tile16_kernel<0>);
   return hipGetLastError();
 }
 

@@ -86,6 +86,10 @@ def test_nvfp4_quantize_rejects_bad_arguments():
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 20, FAKE, FAKE, None) == 3
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, R.RNE, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, None, None) == 1
     assert call(FAKE, 16, 32, 32, B.ROW, G.PER_ROW, 7, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE, FAKE, None) == 1
+    # Four-Over-Six: ROW and TILE only
+    assert call(FAKE, 16, 32, 32, B.COL, G.PER_TENSOR, R.RNE_4OVER6, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE,
+                FAKE, None) == 4
+    assert "Four-Over-Six" in _err(L)
 
 
 def test_nvfp4_quantize_rht_rejects_bad_arguments():
@@ -100,6 +104,7 @@ def test_nvfp4_quantize_rht_rejects_bad_arguments():
     assert call(24, 32, 0x1234, G.PER_TENSOR) == 2
     assert call(32, 24, 0x1234, G.PER_TENSOR) == 2
     assert call(32, 32, 0x1234, G.PER_TENSOR, rnd=5) == 1
+    assert call(32, 32, 0x1234, G.PER_TENSOR, rnd=R.RNE_4OVER6) == 4
     assert call(32, 32, 0x1234, G.PER_TENSOR, lay=Lay.MFMA) == 2          # rows % 64
     assert call(32, 32, 0x1234, G.PER_TENSOR, ldc=8) == 1                 # ld_codes < rows/2
     assert call(32, 32, 0x1234, G.PER_TENSOR, x=FAKE_ODD) == 3
