@@ -389,7 +389,28 @@ def rows_report():
     out("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(torch, lambda: m.mx_gemm(
         m.Operand(m.Format.MXFP8, dd[2], dd[3]), m.Operand(m.Format.MXFP8, d4[2], d4[3]), 2 * I4, H4, T4, out=dw4), 5),
         flops=f, peak=PEAK_FP8_TFLOPS)
-    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo
+    # the same layer with DeepSeek-style blockwise FP8 (1x128 / 128x128, power-of-two scales)
+    b4 = m.fp8bw_quantize(x4, block=m.Block.DUAL)
+    out("f4", "fp8 blockwise dual 1x128 + 128x1 (X)", [T4, H4], _time_us(torch, lambda: m.fp8bw_quantize(
+        x4, block=m.Block.DUAL, codes=b4[0], scales=b4[1], codes_col=b4[2], scales_col=b4[3]), 10),
+        nbytes=n * 2 + 2 * n + 2 * (n // 128))
+    bw4 = m.fp8bw_quantize(w4, block=m.Block.TILE, transposed_copy=True)
+    out("f4", "fp8 blockwise 128x128 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(
+        torch, lambda: m.fp8bw_quantize(w4, block=m.Block.TILE, codes=bw4[0], scales=bw4[1], codes_col=bw4[2],
+                                        scales_col=bw4[3], transposed_copy=True), 10),
+        nbytes=nw * 2 + 2 * nw + 2 * (nw // 16384))
+    bd = m.fp8bw_quantize(dyg4, block=m.Block.DUAL)
+    F8 = m.Format.FP8_B128
+    out("f4", "fp8 blockwise FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(F8, b4[0], b4[1]), m.Operand(F8, bw4[0], bw4[1], block=m.Block.TILE), T4, 2 * I4, H4, out=y4), 5),
+        flops=f, peak=PEAK_FP8_TFLOPS)
+    out("f4", "fp8 blockwise DGRAD gate_up (transposed 128x128 copy)", [T4, H4, 2 * I4], _time_us(
+        torch, lambda: m.mx_gemm(m.Operand(F8, bd[0], bd[1]), m.Operand(F8, bw4[2], bw4[3], block=m.Block.TILE),
+                                 T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
+    out("f4", "fp8 blockwise WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(
+        torch, lambda: m.mx_gemm(m.Operand(F8, bd[2], bd[3]), m.Operand(F8, b4[2], b4[3]), 2 * I4, H4, T4, out=dw4),
+        5), flops=f, peak=PEAK_FP8_TFLOPS)
+    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo, b4, bw4, bd
     torch.cuda.empty_cache()
 
     # ---- Qwen3-30B-A3B-shaped MoE layer, NVFP4 (tokens 8192, hidden 2048, 128 experts, I 768, top-8)

@@ -61,7 +61,10 @@ typedef enum {
 typedef enum {
   MXQ_FMT_MXFP8 = 0,     /* E4M3 codes (1 byte) + E8M0 scales                  */
   MXQ_FMT_NVFP4 = 1,     /* E2M1 codes (2 per byte) + E4M3 scales + FP32 scale */
-  MXQ_FMT_BF16 = 2       /* plain BF16 (GEMM operands only)                    */
+  MXQ_FMT_BF16 = 2,      /* plain BF16 (GEMM operands only)                    */
+  MXQ_FMT_FP8_B128 = 3   /* DeepSeek-style blockwise FP8: E4M3 codes (1 byte)
+                          * + E8M0 power-of-two scales per 1x128 row block or
+                          * 128x128 tile, linear layout (fp8bw_quantize)       */
 } mxq_format;
 
 typedef enum {
@@ -233,14 +236,43 @@ mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int
                               void* stream);
 
 /*
+ * fp8bw_quantize -- DeepSeek-style blockwise FP8 of a BF16 matrix x [rows,
+ * cols], with power-of-two scales.  The blockwise FP8 recipe quantizes
+ * weights in [128, 128] blocks and input activations and output gradients in
+ * [1, 128] blocks ("NVIDIA NeMo RL agora roda treino ... FP8 ponta a ponta",
+ * section "FP8 nas camadas lineares"); on Blackwell that recipe's learner is
+ * restricted to power-of-two scales ("End-to-End MXFP8 Reinforcement Learning
+ * on Blackwell", Table 1), which is also what the scaled MFMA takes here.
+ * Rule: the MXFP8 rule over a 128-value block (or a 128x128 tile): e is the
+ * smallest integer in [-127, 127] with amax <= 448 * 2^e (-127 for a zero
+ * block), stored as the E8M0 byte e + 127; codes are E4M3 RNE of x * 2^-e.
+ *
+ *   block   ROW  (1x128):  codes [rows, cols] (ld_codes), scales [rows, cols/128]
+ *           COL  (128x1):  transposed copy, codes [cols, rows], scales [cols, rows/128]
+ *           TILE (128x128): codes [rows, cols], scales [rows/128, cols/128];
+ *                           with codes_col/scales_col also the transposed copy
+ *                           ([cols, rows], scales [cols/128, rows/128]), the
+ *                           same codes transposed (DGRAD reads it untransposed)
+ *           DUAL: ROW into codes/scales and COL into codes_col/scales_col
+ * Shapes: cols % 128 == 0; rows % 128 == 0 except for ROW.  Alignment: x and
+ * codes 16-byte aligned, ld_x*2 and ld_codes multiples of 16.  The scales are
+ * always in the linear layout; the GEMM takes them as MXQ_FMT_FP8_B128.
+ */
+mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                          uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
+                          void* stream);
+
+/*
  * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16 (the operand of the
  * dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
  * COL copy that is [input cols, input rows]); block says how its scales are
  * laid out (ROW for a COL copy too, since the stored copy is row-blocked).
- *   MXFP8: bf16_RNE(value(c) * 2^e)  (exact unless beyond the BF16 range)
+ *   MXFP8, FP8_B128: bf16_RNE(value(c) * 2^e)  (exact unless beyond the BF16 range)
  *   NVFP4: bf16_RNE(fl(fl(value(c) * s_b) * S))
- *   ld_codes  elements for MXFP8, BYTES for NVFP4; ld_out elements.
- *   gscales   NVFP4 only ([rows] for PER_ROW, [1] otherwise); may be NULL for MXFP8.
+ *   ld_codes  elements for MXFP8 and FP8_B128, BYTES for NVFP4; ld_out elements.
+ *   gscales   NVFP4 only ([rows] for PER_ROW, [1] otherwise); may be NULL otherwise.
+ *   FP8_B128: LINEAR scales, gs NONE, cols % 128 (and rows % 128 for TILE).
  */
 mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
                          const uint8_t* scales, const float* gscales,
@@ -283,9 +315,9 @@ typedef struct {
  *   FPROP  Y  = X  * W^T : A = rowwise X,  B = W (rowwise or tile)
  *   DGRAD  dX = dY * W   : A = rowwise dY, B = W tile copy with transposed=1
  *   WGRAD  dW = dY^T * X : A = columnwise dY copy, B = columnwise X copy
- * A and B must have the same format (MXFP8 x MXFP8 on the scaled MFMA,
- * NVFP4 x NVFP4 dequantized exactly to FP16 for the FP16 MFMA, or
- * BF16 x BF16); mixed formats give MXQ_EUNSUPPORTED.
+ * A and B must have the same format (MXFP8 x MXFP8 or FP8_B128 x FP8_B128
+ * on the scaled MFMA, NVFP4 x NVFP4 dequantized exactly to FP16 for the FP16
+ * MFMA, or BF16 x BF16); mixed formats give MXQ_EUNSUPPORTED.
  *   c, ldc              BF16 output, row-major
  *   num_groups          0 for a dense GEMM; else grouped (MoE experts)
  *   group_row_offsets   device int32 [num_groups+1], non-decreasing, from 0 to
@@ -293,7 +325,7 @@ typedef struct {
  *   a_row_index         device int32 [M] or NULL: row r of C reads A row
  *                       a_row_index[r] (gather), every entry in [0, a_rows)
  *   a_rows              rows stored in A (== M when a_row_index is NULL)
- * Shapes: K % 32 (MXFP8), K % 16 (NVFP4), K % 8 (BF16); a transposed B needs
+ * Shapes: K % 32 (MXFP8), K % 128 (FP8_B128), K % 16 (NVFP4), K % 8 (BF16); a transposed B needs
  * N and K multiples of its tile size.  M, N any positive size.
  * Offsets and indices are read on the device and are NOT validated: values
  * outside the stated ranges give undefined results.

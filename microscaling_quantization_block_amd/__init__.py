@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
-           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
+           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
+           "mx_dequantize", "mx_gemm",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,7 @@ class Format(enum.IntEnum):
     MXFP8 = 0
     NVFP4 = 1
     BF16 = 2
+    FP8_B128 = 3
 
 
 class Block(enum.IntEnum):
@@ -83,6 +85,7 @@ def lib():
     L = ctypes.CDLL(library_path)
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     L.mx_quantize.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8bw_quantize.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp, i64, vp, vp]
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
     L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
                                      vp, vp]
@@ -91,8 +94,8 @@ def lib():
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
-    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
-              "mx_swiglu", "mx_gemm_set_tile"):
+    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
+              "mx_dequantize", "mx_gemm", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
     L.mxq_status_str.restype = ctypes.c_char_p
@@ -160,6 +163,42 @@ def mx_quantize(x, block=Block.ROW, layout=Layout.LINEAR, codes=None, scales=Non
     ldcc = codes_col.stride(0) if codes_col is not None else 0
     _check(lib().mx_quantize(_ptr(x), rows, cols, x.stride(0), int(block), int(layout), _ptr(codes),
                              ldc, _ptr(scales), _ptr(codes_col), ldcc, _ptr(scales_col), _stream(stream)))
+    if codes_col is not None:
+        return codes, scales, codes_col, scales_col
+    return codes, scales
+
+
+def fp8bw_quantize(x, block=Block.ROW, codes=None, scales=None, codes_col=None, scales_col=None,
+                   transposed_copy=False, stream=None):
+    """Blockwise FP8 (1x128 / 128x1 / 128x128 blocks, power-of-two scales).
+    Returns (codes, scales) or, for DUAL and for TILE with transposed_copy,
+    (codes, scales, codes_col, scales_col).  GEMM operands use
+    Format.FP8_B128."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    block = Block(block)
+    if block == Block.COL:
+        codes = _u8((cols, rows), dev) if codes is None else codes
+        scales = _u8((cols, rows // 128), dev) if scales is None else scales
+    elif block == Block.TILE:
+        codes = _u8((rows, cols), dev) if codes is None else codes
+        scales = _u8((rows // 128, cols // 128), dev) if scales is None else scales
+    else:
+        codes = _u8((rows, cols), dev) if codes is None else codes
+        scales = _u8((rows, cols // 128), dev) if scales is None else scales
+    if block == Block.DUAL:
+        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
+        scales_col = _u8((cols, rows // 128), dev) if scales_col is None else scales_col
+    elif block == Block.TILE and transposed_copy:
+        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
+        scales_col = _u8((cols // 128, rows // 128), dev) if scales_col is None else scales_col
+    else:
+        codes_col = scales_col = None
+    ldcc = codes_col.stride(0) if codes_col is not None else 0
+    _check(lib().fp8bw_quantize(_ptr(x), rows, cols, x.stride(0), int(block), _ptr(codes),
+                                codes.stride(0), _ptr(scales), _ptr(codes_col), ldcc,
+                                _ptr(scales_col), _stream(stream)))
     if codes_col is not None:
         return codes, scales, codes_col, scales_col
     return codes, scales

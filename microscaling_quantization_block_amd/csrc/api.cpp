@@ -95,13 +95,48 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     return fail(MXQ_EALIGN, "mx_quantize: pointers and leading dimensions must be 16-byte aligned");
   hipError_t e;
   if (block == MXQ_BLOCK_ROW)
-    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, mfma, S(stream));
+    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, mfma, false, S(stream));
   else
     e = mxq::launch_mxfp8_tile(block == MXQ_BLOCK_COL ? 0 : block == MXQ_BLOCK_TILE ? 1 : 2, x,
                                rows, cols, ld_x, codes, ld_codes, scales,
                                second ? codes_col : nullptr, ld_codes_col,
-                               second ? scales_col : nullptr, mfma, S(stream));
+                               second ? scales_col : nullptr, mfma, false, S(stream));
   return hip_status(e, "mx_quantize");
+}
+
+mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                          uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
+                          void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "fp8bw_quantize: negative size");
+  if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE &&
+      block != MXQ_BLOCK_DUAL)
+    return fail(MXQ_EINVAL, "fp8bw_quantize: block must be ROW, COL, TILE or DUAL");
+  if (rows == 0 || cols == 0) return ok();
+  if (!x || !codes || !scales) return fail(MXQ_EINVAL, "fp8bw_quantize: null pointer");
+  if (block == MXQ_BLOCK_DUAL && (!codes_col || !scales_col))
+    return fail(MXQ_EINVAL, "fp8bw_quantize: DUAL needs codes_col and scales_col");
+  const bool tile_t = block == MXQ_BLOCK_TILE && codes_col;
+  if (tile_t && !scales_col) return fail(MXQ_EINVAL, "fp8bw_quantize: a transposed TILE copy needs scales_col");
+  const bool second = block == MXQ_BLOCK_DUAL || tile_t;
+  if (cols % 128) return fail(MXQ_ESHAPE, "fp8bw_quantize: cols %% 128 != 0 (cols=%lld)", (long long)cols);
+  if (block != MXQ_BLOCK_ROW && rows % 128)
+    return fail(MXQ_ESHAPE, "fp8bw_quantize: rows %% 128 != 0 for a COL/TILE/DUAL copy (rows=%lld)", (long long)rows);
+  const int64_t need_row = block == MXQ_BLOCK_COL ? rows : cols;
+  if (ld_x < cols || ld_codes < need_row || (second && ld_codes_col < rows))
+    return fail(MXQ_EINVAL, "fp8bw_quantize: leading dimension smaller than the row");
+  if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes % 16 ||
+      (second && (!aligned16(codes_col) || ld_codes_col % 16)))
+    return fail(MXQ_EALIGN, "fp8bw_quantize: pointers and leading dimensions must be 16-byte aligned");
+  hipError_t e;
+  if (block == MXQ_BLOCK_ROW)
+    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, false, true, S(stream));
+  else
+    e = mxq::launch_mxfp8_tile(block == MXQ_BLOCK_COL ? 0 : block == MXQ_BLOCK_TILE ? 1 : 2, x,
+                               rows, cols, ld_x, codes, ld_codes, scales,
+                               second ? codes_col : nullptr, ld_codes_col,
+                               second ? scales_col : nullptr, false, true, S(stream));
+  return hip_status(e, "fp8bw_quantize");
 }
 
 mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -214,7 +249,8 @@ mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
                          mxq_block block, mxq_gscale gs, mxq_scale_layout layout, uint16_t* out,
                          int64_t ld_out, void* stream) {
   if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "mx_dequantize: negative size");
-  if (fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4) return fail(MXQ_EINVAL, "mx_dequantize: format must be MXFP8 or NVFP4");
+  if (fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4 && fmt != MXQ_FMT_FP8_B128)
+    return fail(MXQ_EINVAL, "mx_dequantize: format must be MXFP8, NVFP4 or FP8_B128");
   if (block == MXQ_BLOCK_COL || block == MXQ_BLOCK_DUAL)
     return fail(MXQ_EUNSUPPORTED, "mx_dequantize: pass ROW for a stored columnwise copy (it is row-blocked)");
   if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_TILE) return fail(MXQ_EINVAL, "mx_dequantize: bad block");
@@ -228,14 +264,22 @@ mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
     return fail(MXQ_EALIGN, "mx_dequantize: codes/out 16-byte aligned, ld_out*2 %% 16 == 0, ld_codes %% 8 == 0");
   if (ld_out < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_out < cols");
   hipError_t e;
-  if (fmt == MXQ_FMT_MXFP8) {
+  if (fmt == MXQ_FMT_FP8_B128) {
+    if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: FP8_B128 has no second-level scale");
+    if (mfma) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: FP8_B128 scales are linear");
+    if (cols % 128 || (block == MXQ_BLOCK_TILE && rows % 128))
+      return fail(MXQ_ESHAPE, "mx_dequantize: FP8_B128 needs cols %% 128 == 0 (and rows %% 128 for TILE)");
+    if (ld_codes < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_codes < cols");
+    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, false, true,
+                             out, ld_out, S(stream));
+  } else if (fmt == MXQ_FMT_MXFP8) {
     if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: MXFP8 has no second-level scale");
     if (cols % 32 || (block == MXQ_BLOCK_TILE && rows % 32))
       return fail(MXQ_ESHAPE, "mx_dequantize: MXFP8 needs cols %% 32 == 0 (and rows %% 32 for TILE)");
     if (mfma && (rows % 32 || cols % 128)) return fail(MXQ_ESHAPE, "mx_dequantize: MFMA layout needs rows %% 32, cols %% 128");
     if (ld_codes < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_codes < cols");
-    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, mfma, out,
-                             ld_out, S(stream));
+    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, mfma, false,
+                             out, ld_out, S(stream));
   } else {
     if (!gscales) return fail(MXQ_EINVAL, "mx_dequantize: NVFP4 needs gscales");
     if (gs != MXQ_GS_PER_ROW && gs != MXQ_GS_PER_TENSOR && gs != MXQ_GS_GIVEN)
@@ -256,11 +300,14 @@ mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
 static mxq_status check_operand(const char* name, const mxq_operand* o, bool is_b, int64_t rows,
                                 int64_t K, int64_t N_for_bt) {
   if (!o->data) return fail(MXQ_EINVAL, "mx_gemm: %s->data is NULL", name);
-  if (o->fmt != MXQ_FMT_MXFP8 && o->fmt != MXQ_FMT_NVFP4 && o->fmt != MXQ_FMT_BF16)
+  if (o->fmt != MXQ_FMT_MXFP8 && o->fmt != MXQ_FMT_NVFP4 && o->fmt != MXQ_FMT_BF16 &&
+      o->fmt != MXQ_FMT_FP8_B128)
     return fail(MXQ_EINVAL, "mx_gemm: %s has a bad format", name);
   if (!aligned16(o->data)) return fail(MXQ_EALIGN, "mx_gemm: %s->data not 16-byte aligned", name);
   if (o->transposed && !is_b) return fail(MXQ_EUNSUPPORTED, "mx_gemm: only B may be stored transposed");
-  const int blk = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : 1;
+  const int blk = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : o->fmt == MXQ_FMT_FP8_B128 ? 128 : 1;
+  if (o->fmt == MXQ_FMT_FP8_B128 && o->layout != MXQ_LAYOUT_LINEAR)
+    return fail(MXQ_EUNSUPPORTED, "mx_gemm: FP8_B128 scales of %s are linear", name);
   if (o->fmt == MXQ_FMT_BF16) {
     if (o->block != MXQ_BLOCK_NONE) return fail(MXQ_EINVAL, "mx_gemm: a BF16 %s takes block NONE", name);
     if ((o->ld * 2) % 16) return fail(MXQ_EALIGN, "mx_gemm: %s->ld*2 %% 16 != 0", name);
@@ -291,7 +338,7 @@ static mxq_status check_operand(const char* name, const mxq_operand* o, bool is_
   if (o->transposed) {
     if (o->fmt != MXQ_FMT_BF16 && o->block != MXQ_BLOCK_TILE)
       return fail(MXQ_EUNSUPPORTED, "mx_gemm: a transposed quantized B must be tile-blocked");
-    const int t = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : 8;
+    const int t = o->fmt == MXQ_FMT_MXFP8 ? 32 : o->fmt == MXQ_FMT_NVFP4 ? 16 : o->fmt == MXQ_FMT_FP8_B128 ? 128 : 8;
     if (N_for_bt % t || K % t) return fail(MXQ_ESHAPE, "mx_gemm: transposed B needs N and K multiples of %d", t);
     if (o->ld < N_for_bt) return fail(MXQ_EINVAL, "mx_gemm: B->ld < N");
   } else {
@@ -314,7 +361,7 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   if (num_groups > 0 && !group_row_offsets) return fail(MXQ_EINVAL, "mx_gemm: grouped call without offsets");
   if (!a_row_index && a_rows != M) return fail(MXQ_EINVAL, "mx_gemm: a_rows must equal M without a gather index");
   if (a_rows < 1) return fail(MXQ_EINVAL, "mx_gemm: a_rows < 1");
-  const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16 : 8;
+  const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16 : a->fmt == MXQ_FMT_FP8_B128 ? 128 : 8;
   if (K % blk) return fail(MXQ_ESHAPE, "mx_gemm: K %% %d != 0 (K=%lld)", blk, (long long)K);
   if (ldc < N) return fail(MXQ_EINVAL, "mx_gemm: ldc < N");
   mxq_status s = check_operand("A", a, false, a_rows, K, 0);
@@ -346,8 +393,10 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   g.b_mfma_layout = b->layout == MXQ_LAYOUT_MFMA;
   g.b_tile = b->block == MXQ_BLOCK_TILE;
   g.b_group_elems = (b->transposed ? K : N) * b->ld;
-  const int bb = b->fmt == MXQ_FMT_MXFP8 ? 32 : 16;
+  const int bb = b->fmt == MXQ_FMT_MXFP8 ? 32 : b->fmt == MXQ_FMT_FP8_B128 ? 128 : 16;
   g.b_group_scales = b->fmt == MXQ_FMT_BF16 ? 0 : (g.b_tile ? (N / bb) * (K / bb) : N * (K / bb));
+  g.a_b128 = a->fmt == MXQ_FMT_FP8_B128;
+  g.b_b128 = b->fmt == MXQ_FMT_FP8_B128;
   g.M = M;
   g.N = N;
   g.K = K;
@@ -357,7 +406,8 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   g.num_groups = num_groups;
   g.offsets = group_row_offsets;
   g.row_index = a_row_index;
-  const int path = a->fmt == MXQ_FMT_MXFP8 ? mxq::P_FP8 : a->fmt == MXQ_FMT_NVFP4 ? mxq::P_F16 : mxq::P_BF16;
+  const int path = (a->fmt == MXQ_FMT_MXFP8 || a->fmt == MXQ_FMT_FP8_B128) ? mxq::P_FP8
+                   : a->fmt == MXQ_FMT_NVFP4 ? mxq::P_F16 : mxq::P_BF16;
   return hip_status(mxq::launch_gemm(path, b->transposed != 0, g, S(stream)), "mx_gemm");
 }
 

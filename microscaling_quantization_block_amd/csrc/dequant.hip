@@ -13,12 +13,13 @@
 
 namespace mxq {
 
-// MXFP8: one lane per 8 codes.  tile = 1 for 32x32 scales.
+// MXFP8: one lane per 8 codes.  tile = 1 for 32x32 scales; b128 = 1 for
+// blockwise FP8 (128-wide blocks, 128x128 tiles, linear scales).
 // IDX32: the chunk index fits 32 bits, so the row comes from a 32-bit division.
 template <bool IDX32>
 __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
-    int64_t rows, int64_t cols, int tile, int mfma_layout, uint16_t* __restrict__ out,
+    int64_t rows, int64_t cols, int tile, int mfma_layout, int b128, uint16_t* __restrict__ out,
     int64_t ld_out) {
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
@@ -34,8 +35,9 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
       c = id - r * cpr;
     }
     uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + c * 8);
-    uint32_t s = tile ? scales[(r >> 5) * (cols >> 5) + (c >> 2)]
-                      : scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)];
+    uint32_t s = b128 ? scales[tile ? (r >> 7) * (cols >> 7) + (c >> 4) : r * (cols >> 7) + (c >> 4)]
+                 : tile ? scales[(r >> 5) * (cols >> 5) + (c >> 2)]
+                        : scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)];
     int e = (int)s - 127;
     uint32_t w[2] = {q.x, q.y};
     uint32_t o[4];
@@ -130,12 +132,12 @@ static unsigned grid_for(int64_t total) {
 }
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
-                           int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,
-                           int64_t ld_out, hipStream_t st) {
+                           int64_t rows, int64_t cols, bool tile, bool mfma, bool b128,
+                           uint16_t* out, int64_t ld_out, hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   auto kern = total < (int64_t(1) << 32) ? dq_mxfp8_kernel<true> : dq_mxfp8_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(grid_for(total)), dim3(256), 0, st, codes, ld_codes, scales, rows,
-                     cols, (int)tile, (int)mfma, out, ld_out);
+                     cols, (int)tile, (int)mfma, (int)b128, out, ld_out);
   return hipGetLastError();
 }
 

@@ -290,10 +290,14 @@ constexpr int stages_per_barrier() { return (DIST == 2 && PATH == P_F16 && !BT &
 // are read from LDS chunk 4h + ks.  This removes B's LDS writes and reads
 // (a third of the LDS traffic of a 128x128 tile) at the cost of converting
 // each B column once per wave row.
+// B128: blockwise FP8 (MXQ_FMT_FP8_B128): 128-wide power-of-two scale blocks,
+// one byte per row (or 128-row tile) and stage; a compile-time choice, since
+// even an untaken branch on it in the stage loop slowed MXFP8 by 70%.
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false,
-          bool BD = false>
+          bool BD = false, bool B128 = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert(!SDW || PATH != P_BF16, "scale words: MXFP8 and NVFP4 only");
+  static_assert(!B128 || (PATH == P_FP8 && SDW), "128-wide blocks: FP8 path with scale words");
   static_assert(!BD || (PATH != P_FP8 && !BT && !PP && DIST == 2), "B direct: 16-bit MFMA, row-major B, two sets");
   static_assert(!BD || PATH != P_F16 || SDW, "B direct NVFP4 reads scale words");
   constexpr bool SDWB = SDW && !BT && PATH == P_FP8;
@@ -374,16 +378,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   const int64_t a_row_bytes = PATH == P_F16 ? (p.lda >> 1) : p.lda * ESZ_A;
   const int64_t b_row_bytes = PATH == P_F16 ? (p.ldb >> 1) : p.ldb * (PATH == P_BF16 ? 2 : 1);
   const rsrc_t rA = make_rsrc(p.a, p.a_rows * a_row_bytes);
-  const rsrc_t rAs = make_rsrc(p.a_scales, p.a_scales ? p.a_rows * (p.K >> (PATH == P_FP8 ? 5 : 4)) : 0);
+  // (128-wide blocks: the size rounds up to whole words, since a scale byte is
+  // fetched with the aligned word holding it; those bytes never cross a page
+  // and are never used)
+  const rsrc_t rAs = make_rsrc(p.a_scales, p.a_scales ? (PATH == P_FP8 && B128
+                                                             ? (p.a_rows * (p.K >> 7) + 3) & ~int64_t(3)
+                                                             : p.a_rows * (p.K >> (PATH == P_FP8 ? 5 : 4)))
+                                                      : 0);
   const rsrc_t rB = make_rsrc(bbase, (BT ? p.K : p.N) * b_row_bytes);
-  const rsrc_t rBs = make_rsrc(bscl, bscl ? p.b_group_scales : 0);
+  const rsrc_t rBs = make_rsrc(bscl, bscl ? (PATH == P_FP8 && B128 ? (p.b_group_scales + 3) & ~int64_t(3)
+                                                                     : p.b_group_scales)
+                                         : 0);
   const uint32_t arb = (uint32_t)a_row_bytes, brb = (uint32_t)b_row_bytes;
 
   // Scale-byte offsets advance by a fixed step per stage: 4 blocks per stage
   // (NVFP4: 64 / 16; MXFP8: 128 / 32), i.e. 4 bytes in a linear layout and
   // one 128-byte chunk in the MFMA layout (blocks 4j..4j+3 of 32 rows).
-  const int nb16 = K >> 4, nb32 = K >> 5;
-  const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;
+  // Blockwise FP8 (128-wide blocks): one scale byte per row and stage, the
+  // same for both 64-wide K slices and both lane halves.
+  const int nb16 = K >> 4, nb32 = K >> 5, nb128 = K >> 7;
+  const uint32_t a_sstep = B128 ? 1u : p.a_mfma_layout ? 128u : 4u;
 
   // per-lane A chunks: row, chunk, byte offset at stage 0, scale offset at stage 0
   int a_c[A_CH], a_r[A_CH];
@@ -528,7 +542,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       sa_off[tm][ks] = (PATH == P_FP8 && sa_ok[tm])
-                           ? (uint32_t)scale_offset(sa_row[tm], ks * 2 + hl, nb32, p.a_mfma_layout) : 0u;
+                           ? (B128 ? (uint32_t)(sa_row[tm] * nb128)
+                                       : (uint32_t)scale_offset(sa_row[tm], ks * 2 + hl, nb32, p.a_mfma_layout))
+                           : 0u;
   }
   uint32_t sb_step = 4u;
 #pragma unroll
@@ -540,21 +556,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       const int kb = ks * 2 + hl;
       uint32_t so = 0;
       if (PATH == P_FP8) {
-        if (BT) so = (uint32_t)(kb * (N >> 5) + (n >> 5));            // stored [K/32, N/32]
+        if (B128) {
+          if (BT) so = (uint32_t)(n >> 7);                              // stored [K/128, N/128]
+          else if (p.b_tile) so = (uint32_t)((n >> 7) * nb128);
+          else so = (uint32_t)(n * nb128);
+        } else if (BT) so = (uint32_t)(kb * (N >> 5) + (n >> 5));       // stored [K/32, N/32]
         else if (p.b_tile) so = (uint32_t)((n >> 5) * nb32 + kb);
         else so = (uint32_t)scale_offset(n, kb, nb32, p.b_mfma_layout);
       }
       sb_off[tn][ks] = so;
     }
   }
-  if (PATH == P_FP8) sb_step = BT ? 4u * (uint32_t)(N >> 5) : (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
+  if (PATH == P_FP8)
+    sb_step = B128 ? (BT ? (uint32_t)(N >> 7) : 1u)
+                       : BT ? 4u * (uint32_t)(N >> 5) : (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 
   auto load_scales = [&](int kt, int set) {
     if (PATH == P_FP8) {
       // (the word of blocks 4kt..4kt+3 starts hl bytes before block 4kt + hl)
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        if constexpr (SDW) {
+        if constexpr (B128) {
+          // 128-wide blocks: the stage's one byte, replicated into the bytes
+          // the two K slices select
+          const uint32_t o = sa_off[tm][0] + (uint32_t)kt;
+          const bool ok = sa_ok[tm] && kt < nb128;
+          sa_[set][tm][0] = ((bload4(rAs, in_range(ok, o & ~3u)) >> (8 * (o & 3u))) & 0xFFu) * 0x01010101u;
+        } else if constexpr (SDW) {
           const bool ok = sa_ok[tm] && kt * 4 < nb32;
           sa_[set][tm][0] = bload4(rAs, in_range(ok, sa_off[tm][0] - hl + (uint32_t)kt * a_sstep)) >> (8 * hl);
         } else {
@@ -567,9 +595,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        if constexpr (SDWB) {
+        if constexpr (B128 && SDWB) {
+          const uint32_t o = sb_off[tn][0] + (uint32_t)kt * sb_step;
+          const bool ok = sb_ok[tn] && kt < nb128;
+          sb_[set][tn][0] = ((bload4(rBs, in_range(ok, o & ~3u)) >> (8 * (o & 3u))) & 0xFFu) * 0x01010101u;
+        } else if constexpr (SDWB) {
           const bool ok = sb_ok[tn] && kt * 4 < nb32;
           sb_[set][tn][0] = bload4(rBs, in_range(ok, sb_off[tn][0] - hl + (uint32_t)kt * sb_step)) >> (8 * hl);
+        } else if constexpr (B128) {
+          // transposed B: the same byte for both K slices, from its aligned word
+          const uint32_t o = sb_off[tn][0] + (uint32_t)kt * sb_step;
+          const bool ok = sb_ok[tn] && kt < nb128;
+          sb_[set][tn][0] = sb_[set][tn][1] = bload4(rBs, in_range(ok, o & ~3u)) >> (8 * (o & 3u));
         } else {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
@@ -1058,14 +1095,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
 
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW, bool BD = false>
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW, bool BD = false,
+          bool B128 = false>
 static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_n = (a.N + BN - 1) / BN;
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + (BD ? 0 : BN)) * LDS_ROW;
-  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD>;
+  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD, B128>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1084,6 +1122,9 @@ static constexpr bool gemm_b_direct() { return true; }
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   if constexpr (PATH == P_FP8) {
+    // one scale word per row and stage (128-wide blocks, K % 128 == 0: their
+    // one byte, replicated)
+    if (a.a_b128) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, false, true>(a, st);
     if ((a.K >> 5) % 4 == 0) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true>(a, st);
   } else if constexpr (PATH == P_F16) {
     if constexpr (!BT && !PP && DIST == 2)

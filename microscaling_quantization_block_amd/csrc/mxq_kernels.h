@@ -6,14 +6,16 @@
 
 namespace mxq {
 
+// b128: DeepSeek-style blockwise FP8 (128-value blocks, power-of-two scales,
+// linear scale layouts); mfma ignored.
 hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, bool b128,
                             hipStream_t st);
-// mode: 0 = COL (32x1, transposed copy), 1 = TILE (32x32), 2 = DUAL (ROW + COL)
+// mode: 0 COL, 1 TILE (codes_col optional transposed copy), 2 DUAL
 hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
-                             bool mfma, hipStream_t st);
+                             bool mfma, bool b128, hipStream_t st);
 
 // per-tensor amax: zeroes gscale[0], then leaves the tensor amax there tagged
 // with bit 31 (the quantize kernel decodes it and writes S back)
@@ -43,8 +45,8 @@ hipError_t launch_nvfp4_tensor_scale_rht(const uint16_t* x, int64_t rows, int64_
                                          hipStream_t st);
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
-                           int64_t rows, int64_t cols, bool tile, bool mfma, uint16_t* out,
-                           int64_t ld_out, hipStream_t st);
+                           int64_t rows, int64_t cols, bool tile, bool mfma, bool b128,
+                           uint16_t* out, int64_t ld_out, hipStream_t st);
 hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            const float* gscales, int64_t rows, int64_t cols, bool tile,
                            int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st);
@@ -65,7 +67,8 @@ struct GemmArgs {
   const float* b_gs;
   int64_t ldb;                 // elements
   int b_mfma_layout;
-  int b_tile;                  // 2D blocks (32x32 / 16x16)
+  int b_tile;                  // 2D blocks (32x32 / 16x16 / 128x128)
+  int a_b128, b_b128;          // FP8 path: 128-wide power-of-two scale blocks (linear)
   int64_t b_group_elems;       // elements between groups' matrices (N * ldb)
   int64_t b_group_scales;      // scale bytes between groups
   int64_t M, N, K;

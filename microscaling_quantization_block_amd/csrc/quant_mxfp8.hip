@@ -51,9 +51,12 @@ __device__ __forceinline__ uint32_t absmax8(uint4 v) {
 }
 
 // ---------------------------------------------------------------- ROW 1x32
-// One lane per 8 elements, 4 lanes per block; each lane handles UNROLL chunks
-// spaced a grid apart so several 16-byte loads are in flight.
-template <int UNROLL>
+// One lane per 8 elements, LPB lanes per block (4: MXFP8's 32 values; 16: a
+// 128-value blockwise-FP8 block); each lane handles UNROLL chunks spaced a
+// grid apart so several 16-byte loads are in flight.  A block's lanes are
+// aligned and consecutive (cols is a multiple of the block), so they run the
+// loop's iterations together and can exchange their maxima.
+template <int UNROLL, int LPB>
 __global__ __launch_bounds__(256) void mxfp8_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales, int mfma_layout) {
@@ -74,14 +77,14 @@ __global__ __launch_bounds__(256) void mxfp8_row_kernel(
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       uint32_t m = absmax8(v[u]);
-      m = umax(m, lane_xor_u32(m, 1));
-      m = umax(m, lane_xor_u32(m, 2));
+#pragma unroll
+      for (int o = 1; o < LPB; o <<= 1) m = umax(m, lane_xor_u32(m, o));
       uint32_t s = e8m0_from_amax_bits(m);
       if (id[u] < total) {
         int64_t r = id[u] / cpr, c = id[u] - r * cpr;
         uint2 out = mx_encode8(v[u], s);
         *reinterpret_cast<uint2*>(codes + r * ld_codes + c * 8) = out;
-        if ((c & 3) == 0) scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)] = (uint8_t)s;
+        if (c % LPB == 0) scales[scale_offset(r, c / LPB, cols / (8 * LPB), mfma_layout)] = (uint8_t)s;
       }
     }
   }
@@ -110,7 +113,14 @@ __device__ __forceinline__ int mx_slot(int r, int ch) {
   return r * 16 + (ch ^ (r & 3) ^ (((r >> 5) & 3) << 2));
 }
 
-template <int MODE>   // 0 = COL, 1 = TILE, 2 = DUAL
+// B128 (blockwise FP8, power-of-two scales): the blocks are 128 wide, so a
+// row's block is the tile's whole row (its four 32-column maxima combined by
+// two lane exchanges), a column's block the tile's whole column (its four
+// 32-row groups likewise), and TILE's block the whole 128x128 tile (a wave
+// reduction, then the four waves through LDS).  Scales are linear:
+// [rows, cols/128], [cols, rows/128], [rows/128, cols/128].  The shapes are
+// whole tiles (checked on the host).
+template <int MODE, bool B128>   // MODE 0 = COL, 1 = TILE, 2 = DUAL
 __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
@@ -118,6 +128,7 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
     int mfma_layout) {
   __shared__ uint4 tile[TR * TC / 8];
   __shared__ uint32_t tscale[4][4];            // TILE: scale of 32x32 tile (group, block)
+  __shared__ uint32_t wmax[4];                 // TILE with B128: each wave's maximum
   const int64_t r0 = (int64_t)blockIdx.y * TR;
   const int64_t c0 = (int64_t)blockIdx.x * TC;
   const int t = threadIdx.x;
@@ -149,10 +160,23 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
       uint32_t mt = umax(m[0], m[1]);
 #pragma unroll
       for (int o = 4; o < 64; o <<= 1) mt = umax(mt, lane_xor_u32(mt, o));
+      if (B128) {
+        mt = umax(mt, lane_xor_u32(mt, 1));
+        mt = umax(mt, lane_xor_u32(mt, 2));
+        if (l == 0) wmax[w] = mt;
+        __syncthreads();
+        mt = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
+      }
       s[0] = s[1] = e8m0_from_amax_bits(mt);
     } else {
-      s[0] = e8m0_from_amax_bits(m[0]);
-      s[1] = e8m0_from_amax_bits(m[1]);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (B128) {
+          m[k] = umax(m[k], lane_xor_u32(m[k], 1));
+          m[k] = umax(m[k], lane_xor_u32(m[k], 2));
+        }
+        s[k] = e8m0_from_amax_bits(m[k]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -164,10 +188,17 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
         *reinterpret_cast<uint4*>(dst) = make_uint4(o0.x, o0.y, o1.x, o1.y);
         *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o2.x, o2.y, o3.x, o3.y);
         if (MODE == 1) {
-          if ((r & 31) == 0) {
+          if (B128) {
+            if (t == 0) {
+              scales[(r0 >> 7) * (cols >> 7) + (c0 >> 7)] = (uint8_t)s[k];
+              tscale[0][0] = s[k];
+            }
+          } else if ((r & 31) == 0) {
             scales[((r0 + r) >> 5) * (cols >> 5) + ((c0 >> 5) + j)] = (uint8_t)s[k];
             tscale[w][j] = s[k];
           }
+        } else if (B128) {
+          if (j == 0) scales[(r0 + r) * (cols >> 7) + (c0 >> 7)] = (uint8_t)s[k];
         } else {
           scales[scale_offset(r0 + r, (c0 >> 5) + j, cols >> 5, mfma_layout)] = (uint8_t)s[k];
         }
@@ -183,7 +214,6 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = t + 256 * k, g = i & 3, c = i >> 2;
-      if (r0 + 32 * g >= rows || c0 + c >= cols) continue;
       uint32_t col[16];                          // 32 values, two per word (row pairs)
       uint32_t m = 0;
 #pragma unroll
@@ -193,7 +223,12 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
         col[q] = a | (b << 16);
         m = umax(m, bf16x2_absmax_bits(col[q]));
       }
-      const uint32_t s = MODE == 1 ? tscale[g][c >> 5] : e8m0_from_amax_bits(m);
+      if (B128) {                                // the column's four 32-row groups
+        m = umax(m, lane_xor_u32(m, 1));
+        m = umax(m, lane_xor_u32(m, 2));
+      }
+      if (r0 + 32 * g >= rows || c0 + c >= cols) continue;
+      const uint32_t s = MODE == 1 ? (B128 ? tscale[0][0] : tscale[g][c >> 5]) : e8m0_from_amax_bits(m);
       uint32_t o[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -205,7 +240,13 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
       *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
       if (MODE == 1) {
-        if ((c & 31) == 0) scales_col[((c0 + c) >> 5) * (rows >> 5) + ((r0 >> 5) + g)] = (uint8_t)s;
+        if (B128) {
+          if (t == 0 && k == 0) scales_col[(c0 >> 7) * (rows >> 7) + (r0 >> 7)] = (uint8_t)s;
+        } else if ((c & 31) == 0) {
+          scales_col[((c0 + c) >> 5) * (rows >> 5) + ((r0 >> 5) + g)] = (uint8_t)s;
+        }
+      } else if (B128) {
+        if (g == 0) dscales[(c0 + c) * (rows >> 7) + (r0 >> 7)] = (uint8_t)s;
       } else {
         dscales[scale_offset(c0 + c, (r0 >> 5) + g, rows >> 5, mfma_layout)] = (uint8_t)s;
       }
@@ -255,23 +296,27 @@ __global__ __launch_bounds__(256) void mxfp8_tile32_kernel(
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, bool b128,
                             hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   constexpr int UNROLL = 4;
   int64_t blocks = (total + 256 * UNROLL - 1) / (256 * UNROLL);
   if (blocks < 1) blocks = 1;
   if (blocks > (1 << 20)) blocks = 1 << 20;
-  hipLaunchKernelGGL((mxfp8_row_kernel<UNROLL>), dim3((unsigned)blocks), dim3(256), 0, st, x,
-                     rows, cols, ld_x, codes, ld_codes, scales, (int)mfma);
+  if (b128)
+    hipLaunchKernelGGL((mxfp8_row_kernel<UNROLL, 16>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       rows, cols, ld_x, codes, ld_codes, scales, 0);
+  else
+    hipLaunchKernelGGL((mxfp8_row_kernel<UNROLL, 4>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       rows, cols, ld_x, codes, ld_codes, scales, (int)mfma);
   return hipGetLastError();
 }
 
 hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
-                             bool mfma, hipStream_t st) {
-  if (mode == 1 && !codes_col) {
+                             bool mfma, bool b128, hipStream_t st) {
+  if (mode == 1 && !codes_col && !b128) {
     dim3 g32((unsigned)((cols + T32C - 1) / T32C), (unsigned)(rows / T32R));
     if (g32.y > 65535u) return hipErrorInvalidValue;     // more row strips than a grid holds
     hipLaunchKernelGGL(mxfp8_tile32_kernel, g32, dim3(256), 0, st, x, rows, cols, ld_x, codes,
@@ -280,15 +325,19 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
   }
   dim3 grid((unsigned)((cols + TC - 1) / TC), (unsigned)((rows + TR - 1) / TR));
   if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
-  if (mode == 0)
-    hipLaunchKernelGGL((mxfp8_tile_kernel<0>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, scales, codes_col, ld_codes_col, scales_col, (int)mfma);
-  else if (mode == 1)
-    hipLaunchKernelGGL((mxfp8_tile_kernel<1>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, scales, codes_col, ld_codes_col, scales_col, (int)mfma);
-  else
-    hipLaunchKernelGGL((mxfp8_tile_kernel<2>), grid, dim3(256), 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, scales, codes_col, ld_codes_col, scales_col, (int)mfma);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, x, rows, cols, ld_x, codes, ld_codes, scales,
+                       codes_col, ld_codes_col, scales_col, (int)mfma);
+  };
+  if (b128) {
+    if (mode == 0) go(mxfp8_tile_kernel<0, true>);
+    else if (mode == 1) go(mxfp8_tile_kernel<1, true>);
+    else go(mxfp8_tile_kernel<2, true>);
+  } else {
+    if (mode == 0) go(mxfp8_tile_kernel<0, false>);
+    else if (mode == 1) go(mxfp8_tile_kernel<1, false>);
+    else go(mxfp8_tile_kernel<2, false>);
+  }
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "mx_dequantize", "mx_gemm",
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize", "mx_gemm",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
 
@@ -110,6 +110,21 @@ def test_nvfp4_quantize_rht_rejects_bad_arguments():
     assert call(32, 32, 0x1234, G.PER_TENSOR, x=FAKE_ODD) == 3
     assert call(32, 32, 0x1234, G.PER_TENSOR, g=None) == 1
     assert call(0, 32, 0x1234, G.PER_TENSOR) == 0                         # empty: nothing launched
+
+
+def test_fp8bw_quantize_rejects_bad_arguments():
+    m, L = _lib()
+    B = m.Block
+    call = lambda x, rows, cols, ld, blk, cc=None: L.fp8bw_quantize(x, rows, cols, ld, blk, FAKE, cols, FAKE,
+                                                                   cc, rows, FAKE if cc else None, None)
+    assert call(FAKE, 128, 96, 96, B.ROW) == 2                    # cols % 128
+    assert "cols % 128" in _err(L)
+    assert call(FAKE, 96, 128, 128, B.COL) == 2                   # rows % 128 for COL
+    assert call(FAKE, 128, 128, 128, B.DUAL) == 1                 # DUAL needs the second copy
+    assert call(FAKE_ODD, 128, 128, 128, B.ROW) == 3
+    assert call(None, 128, 128, 128, B.ROW) == 1
+    assert call(FAKE, 128, 128, 128, 9) == 1
+    assert call(FAKE, 0, 128, 128, B.ROW) == 0
 
 
 def test_mx_gemm_rejects_bad_arguments():

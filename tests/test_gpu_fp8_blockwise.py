@@ -1,0 +1,165 @@
+"""GPU parity of blockwise FP8 (1x128 / 128x1 / 128x128 blocks, power-of-two
+scales) against oracle/fp8_blockwise.py: the quantizer byte for byte (codes
+and E8M0 scales, every block kind, the TILE's transposed copy, DUAL), the
+dequantizer bit for bit, and the GEMMs (FPROP, DGRAD with the weight read
+transposed or through its transposed copy, WGRAD on the columnwise copies)
+within the GEMM bounds of the oracle's dequantize-then-matmul; exact equality
+with unit scales and small codes; every tile configuration the same bits."""
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import fp8_blockwise as OB
+from oracle import gemm as G
+from tests.util import requires_gpu, to_dev_bf16, from_dev_bf16, to_np, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def mxq():
+    import microscaling_quantization_block_amd as m
+    return m
+
+
+def _edge(rows, cols, seed):
+    """Per-row log-normal magnitudes, a zero row, negative zeros, BF16
+    subnormals, the largest BF16 and random finite bit patterns."""
+    rs = np.random.default_rng(seed)
+    x = F.bf16_rne(rs.standard_normal((rows, cols)) * np.exp(rs.standard_normal((rows, 1)) * 3))
+    x[0] = 0
+    if rows > 1:
+        x[1] = 0x8000
+    if rows > 2:
+        x[2] = rs.integers(1, 0x80, cols).astype(np.uint16)
+    if rows > 3:
+        x[3, 5] = 0x7F7F
+        x[3, 6] = 0xFF7F
+    if rows > 4:
+        x[4] = (rs.integers(0, 0x7F80, cols) | (rs.integers(0, 2, cols) << 15)).astype(np.uint16)
+    return x
+
+
+def _v(bits):
+    return F.bf16_bits_to_f64(bits)
+
+
+@pytest.mark.parametrize("shape", [(64, 512), (37, 384), (5, 128), (1000, 1024)])
+def test_rows_1x128(shape):
+    m = mxq()
+    x = _edge(*shape, 71)
+    say(f"fp8bw ROW {shape}")
+    c, s = m.fp8bw_quantize(to_dev_bf16(x))
+    rc, rs = OB.quantize_rows(_v(x))
+    assert np.array_equal(to_np(s), rs) and np.array_equal(to_np(c), rc)
+    dq = m.mx_dequantize(m.Format.FP8_B128, c, s, *shape)
+    assert np.array_equal(from_dev_bf16(dq), OB.dequantize_bf16(rc, rs))
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256), (1024, 640)])
+def test_col_tile_dual(shape):
+    m = mxq()
+    x = _edge(*shape, 72)
+    v = _v(x)
+    xd = to_dev_bf16(x)
+    say(f"fp8bw COL/TILE/DUAL {shape}")
+    c, s = m.fp8bw_quantize(xd, block=m.Block.COL)
+    rc, rs = OB.quantize_cols(v)
+    assert np.array_equal(to_np(s), rs) and np.array_equal(to_np(c), rc)
+    c, s = m.fp8bw_quantize(xd, block=m.Block.TILE)
+    tc, ts = OB.quantize_tile(v)
+    assert np.array_equal(to_np(s), ts) and np.array_equal(to_np(c), tc)
+    dq = m.mx_dequantize(m.Format.FP8_B128, c, s, *shape, block=m.Block.TILE)
+    assert np.array_equal(from_dev_bf16(dq), OB.dequantize_bf16(tc, ts, "128x128"))
+    c, s, ct, st = m.fp8bw_quantize(xd, block=m.Block.TILE, transposed_copy=True)
+    tct, tst = OB.quantize_tile(np.ascontiguousarray(v.T))
+    assert np.array_equal(to_np(c), tc) and np.array_equal(to_np(s), ts)
+    assert np.array_equal(to_np(ct), tct) and np.array_equal(to_np(st), tst)
+    c, s, cc, sc = m.fp8bw_quantize(xd, block=m.Block.DUAL)
+    r1, s1 = OB.quantize_rows(v)
+    assert np.array_equal(to_np(c), r1) and np.array_equal(to_np(s), s1)
+    assert np.array_equal(to_np(cc), rc) and np.array_equal(to_np(sc), rs)
+
+
+def _op(m, c, s, tile=False, transposed=False):
+    return m.Operand(m.Format.FP8_B128, c, s, block=m.Block.TILE if tile else m.Block.ROW,
+                     transposed=transposed)
+
+
+def _check(out, a64, b64):
+    frob, worst, ok = G.check(from_dev_bf16(out), a64, b64, a64, b64, rtol_frob=1e-2)
+    assert ok, f"frobenius {frob:.3e}, worst element ratio {worst:.3f}"
+
+
+def test_fprop_dgrad_wgrad():
+    m = mxq()
+    T, H, I = 512, 384, 256
+    rs = np.random.default_rng(73)
+    x = F.bf16_rne(rs.standard_normal((T, H)) * np.exp(rs.standard_normal((T, 1))))
+    w = F.bf16_rne(rs.standard_normal((I, H)) * 0.02)
+    dy = F.bf16_rne(rs.standard_normal((T, I)) * 1e-3)
+    say(f"fp8bw FPROP / DGRAD / WGRAD T={T} H={H} I={I}")
+    cx, sx, cxc, sxc = m.fp8bw_quantize(to_dev_bf16(x), block=m.Block.DUAL)
+    cw, sw, cwt, swt = m.fp8bw_quantize(to_dev_bf16(w), block=m.Block.TILE, transposed_copy=True)
+    cd, sd, cdc, sdc = m.fp8bw_quantize(to_dev_bf16(dy), block=m.Block.DUAL)
+    X64 = OB.dequantize_f64(*OB.quantize_rows(_v(x)))
+    W64 = OB.dequantize_f64(*OB.quantize_tile(_v(w)), "128x128")
+    D64 = OB.dequantize_f64(*OB.quantize_rows(_v(dy)))
+    # FPROP Y = X W^T
+    _check(m.mx_gemm(_op(m, cx, sx), _op(m, cw, sw, tile=True), T, I, H), X64, W64)
+    # DGRAD dX = dY W: W read transposed, and its transposed copy read as is
+    Wt = np.ascontiguousarray(W64.T)
+    d1 = m.mx_gemm(_op(m, cd, sd), _op(m, cw, sw, tile=True, transposed=True), T, H, I)
+    _check(d1, D64, Wt)
+    d2 = m.mx_gemm(_op(m, cd, sd), _op(m, cwt, swt, tile=True), T, H, I)
+    assert np.array_equal(from_dev_bf16(d1), from_dev_bf16(d2))
+    # WGRAD dW = dY^T X on the columnwise copies
+    DC = OB.dequantize_f64(*OB.quantize_cols(_v(dy)))
+    XC = OB.dequantize_f64(*OB.quantize_cols(_v(x)))
+    _check(m.mx_gemm(_op(m, cdc, sdc), _op(m, cxc, sxc), I, H, T), DC, XC)
+
+
+def test_unit_scale_exact_and_tiles_same_bits():
+    m = mxq()
+    import torch
+    rs = np.random.default_rng(74)
+    M, N, K = 384, 256, 1024
+    # codes of small integers (|v| <= 16) with unit scales: every product and
+    # sum is exact, so C equals bf16(exact)
+    ints = np.arange(-16, 17)
+    av, bv = rs.choice(ints, (M, K)).astype(np.float64), rs.choice(ints, (N, K)).astype(np.float64)
+    ca, cb = F.encode_e4m3_rne(av), F.encode_e4m3_rne(bv)
+    one_a = torch.full((M, K // 128), 127, dtype=torch.uint8, device="cuda")
+    one_b = torch.full((N // 128, K // 128), 127, dtype=torch.uint8, device="cuda")
+    say("fp8bw unit-scale exact 384x256x1024, every tile")
+    A = _op(m, torch.from_numpy(ca).cuda(), one_a)
+    B = _op(m, torch.from_numpy(cb).cuda(), one_b, tile=True)
+    exact = F.bf16_rne(av @ bv.T)
+    outs = []
+    try:
+        for t in range(-1, 7):
+            m.mx_gemm_set_tile(t)
+            outs.append(from_dev_bf16(m.mx_gemm(A, B, M, N, K)))
+    finally:
+        m.mx_gemm_set_tile(-1)
+    for o in outs:
+        assert np.array_equal(o, exact)
+    # random operands: every tile configuration gives the same bits
+    x = F.bf16_rne(rs.standard_normal((M, K)))
+    w = F.bf16_rne(rs.standard_normal((N, K)) * 0.05)
+    cx, sx = m.fp8bw_quantize(to_dev_bf16(x))
+    cw, sw = m.fp8bw_quantize(to_dev_bf16(w), block=m.Block.TILE)
+    ref = None
+    try:
+        for t in range(-1, 7):
+            m.mx_gemm_set_tile(t)
+            o = from_dev_bf16(m.mx_gemm(_op(m, cx, sx), _op(m, cw, sw, tile=True), M, N, K))
+            ref = o if ref is None else ref
+            assert np.array_equal(o, ref), f"tile {t}"
+    finally:
+        m.mx_gemm_set_tile(-1)
+    _check_arr = G.check(ref, OB.dequantize_f64(*OB.quantize_rows(_v(x))),
+                         OB.dequantize_f64(*OB.quantize_tile(_v(w)), "128x128"),
+                         OB.dequantize_f64(*OB.quantize_rows(_v(x))),
+                         OB.dequantize_f64(*OB.quantize_tile(_v(w)), "128x128"))
+    assert _check_arr[2]
