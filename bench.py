@@ -455,6 +455,11 @@ def rows_report():
     h = torch.empty((Mr, I3), dtype=torch.bfloat16, device=dev)
     out("a8", "MoE SwiGLU", [Mr, I3], _time_us(torch, lambda: m.mx_swiglu(gu, I3, out=h), 10),
         nbytes=Mr * N2 * 2 + Mr * I3 * 2)
+    hf = torch.empty_like(h)
+    out("f3", "MoE grouped gate_up with SwiGLU in the epilogue (writes H)", [Mr, N2, H3], _time_us(
+        torch, lambda: m.mx_gemm_swiglu(A, Bgu, Mr, I3, H3, out=hf, group_row_offsets=off_d, a_row_index=idx_d,
+                                        a_rows=T3), 10), flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS)
+    del hf
     ch, sh, Sh = m.nvfp4_quantize(h)
     out("a8", "MoE per-token Q(H)", [Mr, I3], _time_us(torch, lambda: m.nvfp4_quantize(
         h, codes=ch, block_scales=sh, gscales=Sh), 10), nbytes=Mr * I3 * 2 + Mr * I3 // 2 + Mr * I3 // 16 + Mr * 4)

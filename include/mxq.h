@@ -365,6 +365,29 @@ mxq_status mx_gemm_set_tile(int32_t tile);
 mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
                      uint16_t* h, int64_t ld_h, void* stream);
 
+/*
+ * mx_gemm_swiglu -- the MoE gate_up GEMM with the SwiGLU fused into its
+ * epilogue: H[M, inter] = silu(G) * U with [G | U] = A * B^T, computed exactly
+ * as mx_swiglu(mx_gemm(...)) computes it (the GEMM's BF16 products, then the
+ * same binary32 SwiGLU), without the [M, 2*inter] BF16 round trip through HBM.
+ * The pages attribute part of NVFP4's training cost to the unfused steps
+ * around the expert GEMMs ("Miles Blackwell RL ...", section "Um Quantizador
+ * Compartilhado É o Verdadeiro Mecanismo").
+ *   a, b      NVFP4 operands as for mx_gemm; b holds, per group, the gate rows
+ *             [0, inter) then the up rows [inter, 2*inter) (row-major, not
+ *             transposed; ROW or TILE blocks)
+ *   h, ldh    BF16 output [M, inter], row-major
+ *   other arguments as for mx_gemm (grouped launch, gather index)
+ * Shapes: inter % 64 == 0, K % 64 == 0.  Other formats or a transposed B give
+ * MXQ_EUNSUPPORTED.  The per-token requantization of H is a separate call
+ * (nvfp4_quantize): its second scale needs the whole row of H, which no
+ * workgroup tile holds.
+ */
+mxq_status mx_gemm_swiglu(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t inter,
+                          int64_t K, int64_t a_rows, uint16_t* h, int64_t ldh, int32_t num_groups,
+                          const int32_t* group_row_offsets, const int32_t* a_row_index,
+                          void* stream);
+
 const char* mxq_status_str(mxq_status s);
 const char* mxq_last_error(void);
 int mxq_version(void);

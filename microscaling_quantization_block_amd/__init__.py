@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
            "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
-           "mx_dequantize", "mx_gemm",
+           "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,10 +92,12 @@ def lib():
     L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
     L.mx_gemm.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
                           vp, i64, ctypes.c_int32, vp, vp, vp]
+    L.mx_gemm_swiglu.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
+                          vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
     for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
-              "mx_dequantize", "mx_gemm", "mx_swiglu", "mx_gemm_set_tile"):
+              "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
     L.mxq_status_str.restype = ctypes.c_char_p
@@ -300,6 +302,22 @@ def mx_gemm(a, b, M, N, K, out=None, group_row_offsets=None, a_row_index=None, a
     _check(lib().mx_gemm(ctypes.byref(ca), ctypes.byref(cb), M, N, K, int(a_rows), _ptr(out),
                          out.stride(0), ng, _ptr(group_row_offsets), _ptr(a_row_index),
                          _stream(stream)))
+    return out
+
+
+def mx_gemm_swiglu(a, b, M, inter, K, out=None, group_row_offsets=None, a_row_index=None, a_rows=None,
+                   stream=None):
+    """H[M, inter] = SwiGLU of the gate_up GEMM A B^T (B: gate rows then up
+    rows), fused into the GEMM's epilogue; NVFP4 operands."""
+    dev = a.data.device
+    out = torch.empty((M, inter), dtype=torch.bfloat16, device=dev) if out is None else out
+    ng = 0 if group_row_offsets is None else group_row_offsets.numel() - 1
+    if a_rows is None:
+        a_rows = M
+    ca, cb = a._c(), b._c()
+    _check(lib().mx_gemm_swiglu(ctypes.byref(ca), ctypes.byref(cb), M, inter, K, int(a_rows), _ptr(out),
+                                out.stride(0), ng, _ptr(group_row_offsets), _ptr(a_row_index),
+                                _stream(stream)))
     return out
 
 

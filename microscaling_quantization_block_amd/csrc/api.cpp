@@ -349,9 +349,11 @@ static mxq_status check_operand(const char* name, const mxq_operand* o, bool is_
   return MXQ_OK;
 }
 
-mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
-                   int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
-                   const int32_t* group_row_offsets, const int32_t* a_row_index, void* stream) {
+// inter > 0: the gate_up GEMM with SwiGLU fused (N = 2 inter, c = H [M, inter]).
+static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
+                            int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
+                            const int32_t* group_row_offsets, const int32_t* a_row_index,
+                            int64_t inter, void* stream) {
   if (!a || !b) return fail(MXQ_EINVAL, "mx_gemm: null operand");
   if (M < 0 || N < 0 || K < 0 || num_groups < 0 || a_rows < 0) return fail(MXQ_EINVAL, "mx_gemm: negative size");
   if (a->fmt != b->fmt) return fail(MXQ_EUNSUPPORTED, "mx_gemm: A and B formats differ");
@@ -363,7 +365,14 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   if (a_rows < 1) return fail(MXQ_EINVAL, "mx_gemm: a_rows < 1");
   const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16 : a->fmt == MXQ_FMT_FP8_B128 ? 128 : 8;
   if (K % blk) return fail(MXQ_ESHAPE, "mx_gemm: K %% %d != 0 (K=%lld)", blk, (long long)K);
-  if (ldc < N) return fail(MXQ_EINVAL, "mx_gemm: ldc < N");
+  if (ldc < (inter ? inter : N)) return fail(MXQ_EINVAL, "mx_gemm: ldc smaller than the output row");
+  if (inter) {
+    if (a->fmt != MXQ_FMT_NVFP4)
+      return fail(MXQ_EUNSUPPORTED, "mx_gemm_swiglu: the fused SwiGLU epilogue is built for NVFP4 operands");
+    if (b->transposed) return fail(MXQ_EUNSUPPORTED, "mx_gemm_swiglu: B must be row-major (the gate_up weight)");
+    if (inter % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: inter %% 64 != 0 (inter=%lld)", (long long)inter);
+    if (K % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: K %% 64 != 0 (K=%lld)", (long long)K);
+  }
   mxq_status s = check_operand("A", a, false, a_rows, K, 0);
   if (s != MXQ_OK) return s;
   s = check_operand("B", b, true, N, K, N);
@@ -406,9 +415,25 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_
   g.num_groups = num_groups;
   g.offsets = group_row_offsets;
   g.row_index = a_row_index;
+  g.swiglu_inter = inter;
   const int path = (a->fmt == MXQ_FMT_MXFP8 || a->fmt == MXQ_FMT_FP8_B128) ? mxq::P_FP8
                    : a->fmt == MXQ_FMT_NVFP4 ? mxq::P_F16 : mxq::P_BF16;
-  return hip_status(mxq::launch_gemm(path, b->transposed != 0, g, S(stream)), "mx_gemm");
+  return hip_status(mxq::launch_gemm(path, b->transposed != 0, g, S(stream)), inter ? "mx_gemm_swiglu" : "mx_gemm");
+}
+
+mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
+                   int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
+                   const int32_t* group_row_offsets, const int32_t* a_row_index, void* stream) {
+  return gemm_impl(a, b, M, N, K, a_rows, c, ldc, num_groups, group_row_offsets, a_row_index, 0, stream);
+}
+
+mxq_status mx_gemm_swiglu(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t inter,
+                          int64_t K, int64_t a_rows, uint16_t* h, int64_t ldh, int32_t num_groups,
+                          const int32_t* group_row_offsets, const int32_t* a_row_index, void* stream) {
+  if (inter < 0) return fail(MXQ_EINVAL, "mx_gemm_swiglu: negative size");
+  if (inter == 0 || M == 0) return ok();
+  return gemm_impl(a, b, M, 2 * inter, K, a_rows, h, ldh, num_groups, group_row_offsets, a_row_index,
+                   inter, stream);
 }
 
 // ---------------------------------------------------------------- SwiGLU

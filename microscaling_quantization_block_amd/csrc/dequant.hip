@@ -113,13 +113,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
     uint4 u = *reinterpret_cast<const uint4*>(gu + r * ld_gu + inter + c * 8);
     uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w}, o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
-      float u0 = bf16_lo(uw[i]), u1 = bf16_hi(uw[i]);
-      float h0 = g0 / (1.0f + expf(-g0)) * u0;
-      float h1 = g1 / (1.0f + expf(-g1)) * u1;
-      o[i] = f32x2_to_bf16x2(h0, h1);
-    }
+    for (int i = 0; i < 4; ++i) o[i] = swiglu_bf16x2(gw[i], uw[i]);
     *reinterpret_cast<uint4*>(h + r * ld_h + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }

@@ -293,11 +293,19 @@ constexpr int stages_per_barrier() { return (DIST == 2 && PATH == P_F16 && !BT &
 // B128: blockwise FP8 (MXQ_FMT_FP8_B128): 128-wide power-of-two scale blocks,
 // one byte per row (or 128-row tile) and stage; a compile-time choice, since
 // even an untaken branch on it in the stage loop slowed MXFP8 by 70%.
+// SWI: the MoE gate_up GEMM with SwiGLU in its epilogue (NVFP4, row-major B).
+// B holds gate rows [0, I) and up rows [I, 2I) (I = p.swiglu_inter, N = 2I);
+// each wave's WN output columns take WN/2 gate rows and the matching WN/2 up
+// rows (logical column q WN + j reads gate row q WN/2 + j, or up row
+// I + q WN/2 + j - WN/2), so the epilogue pairs them in the wave's own LDS
+// slab and writes H [M, I] = SwiGLU(gate, up) from the BF16 products, the
+// values the unfused GEMM would store.  Needs I % 64 == 0.
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW = false,
-          bool BD = false, bool B128 = false>
+          bool BD = false, bool B128 = false, bool SWI = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert(!SDW || PATH != P_BF16, "scale words: MXFP8 and NVFP4 only");
   static_assert(!B128 || (PATH == P_FP8 && SDW), "128-wide blocks: FP8 path with scale words");
+  static_assert(!SWI || (PATH == P_F16 && !BT), "fused SwiGLU: NVFP4, row-major B");
   static_assert(!BD || (PATH != P_FP8 && !BT && !PP && DIST == 2), "B direct: 16-bit MFMA, row-major B, two sets");
   static_assert(!BD || PATH != P_F16 || SDW, "B direct NVFP4 reads scale words");
   constexpr bool SDWB = SDW && !BT && PATH == P_FP8;
@@ -342,6 +350,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
+  // B row that feeds logical output column n (the identity unless SWI)
+  auto brow = [&](int n) -> int {
+    if constexpr (SWI) {
+      constexpr int P = (BN / WGN) / 2;
+      const int q = n / (2 * P), j = n - q * (2 * P);
+      return j < P ? q * P + j : (int)p.swiglu_inter + q * P + (j - P);
+    }
+    return n;
+  };
   // loader: thread within its share, and the share's first A and B row
   const int grp = PP ? (tid >> 8) : 0;
   const int ltid = PP ? (tid & 255) : tid;
@@ -429,8 +446,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     const int r = lb0 + id / CPR, c = id % CPR;
     b_r[i] = r;
     b_c[i] = c;
-    const int n = n0 + r;
-    b_ok[i] = !BT && n < N;
+    const int n = brow(n0 + r);
+    b_ok[i] = !BT && n0 + r < N;
     b_off[i] = (uint32_t)n * brb + (uint32_t)c * CB;
     b_soff[i] = 0;
     if (PATH == P_F16 && !BT)
@@ -454,7 +471,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int n = b_ok[i] ? n0 + b_r[i] : 0;
+      const int n = b_ok[i] ? brow(n0 + b_r[i]) : 0;
       b_voff[i] = in_range(b_ok[i], (uint32_t)n * brb + (uint32_t)b_c[i] * CB);
       const uint32_t so = p.b_tile ? (uint32_t)((n >> 4) * nb16 + b_c[i])
                                    : (uint32_t)scale_offset(n, b_c[i], nb16, p.b_mfma_layout);
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     for (int tn = 0; tn < TN; ++tn) {
       const int n = n0 + wn * WN + tn * 32 + (lane & 31);
       bd_ok[tn] = n < N;
-      const int nn = bd_ok[tn] ? n : 0;
+      const int nn = bd_ok[tn] ? brow(n) : 0;
       bd_off[tn] = (uint32_t)nn * brb + (uint32_t)(lane >> 5) * (PATH == P_F16 ? 16u : 64u);
       bd_soff[tn] = PATH == P_F16 ? (p.b_tile ? (uint32_t)((nn >> 4) * nb16)
                                               : (uint32_t)scale_offset(nn, 0, nb16, p.b_mfma_layout))
@@ -1070,6 +1087,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
             make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
       }
+    if constexpr (SWI) {
+      // gate chunk cc and up chunk cc + ECH/2 of a staged row -> 8 values of H
+      // (the wave's block of 2P logical columns is whole: 2I % WN == 0)
+      constexpr int ECH2 = ECH / 2, ERI2 = 64 / ECH2;
+      const bool wave_in = n0 + wn * WN < N;
+#pragma unroll
+      for (int it = 0; it < 32 / ERI2; ++it) {
+        const int rr = it * ERI2 + lane / ECH2, cc = lane % ECH2;
+        const uint4 gv = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+        const uint4 uv = *reinterpret_cast<const uint4*>(E + rr * EROW + (cc + ECH2) * 16);
+        const int64_t m = to.m0 + wm * WM + tm * 32 + rr;
+        const int hc = ((n0 + wn * WN) >> 1) + cc * 8;
+        if (wave_in && m < to.m_end) {
+          const uint4 hv = make_uint4(swiglu_bf16x2(gv.x, uv.x), swiglu_bf16x2(gv.y, uv.y),
+                                      swiglu_bf16x2(gv.z, uv.z), swiglu_bf16x2(gv.w, uv.w));
+          uint16_t* const dst = p.c + m * p.ldc + hc;
+          if (vec16) {
+            *reinterpret_cast<uint4*>(dst) = hv;
+          } else {
+            const uint32_t w[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int it = 0; it < 32 / ERI; ++it) {
       const int rr = it * ERI + lane / ECH, cc = lane % ECH;
@@ -1092,18 +1136,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------ launcher
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false>
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false, bool SWI = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
 
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SDW, bool BD = false,
-          bool B128 = false>
+          bool B128 = false, bool SWI = false>
 static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   int64_t tiles_n = (a.N + BN - 1) / BN;
   int64_t tiles_m = a.num_groups == 0 ? (a.M + BM - 1) / BM : a.M / BM + a.num_groups;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + (BD ? 0 : BN)) * LDS_ROW;
-  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD, B128>;
+  auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD, B128, SWI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1119,9 +1163,14 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
 // loads per lane and stage and BF16 is bound by LDS, not by the conversion).
 static constexpr bool gemm_b_direct() { return true; }
 
-template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP>
+template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP, bool SWI>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  if constexpr (PATH == P_FP8) {
+  if constexpr (SWI) {
+    // NVFP4, row-major B (the gate_up weight), K % 64 == 0 (checked on the host)
+    if constexpr (!PP && DIST == 2)
+      if (gemm_b_direct()) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, true, false, true>(a, st);
+    return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, false, false, true>(a, st);
+  } else if constexpr (PATH == P_FP8) {
     // one scale word per row and stage (128-wide blocks, K % 128 == 0: their
     // one byte, replicated)
     if (a.a_b128) return launch_k<PATH, BM, BN, BT, DIST, WGM, WGN, PP, true, false, true>(a, st);
@@ -1148,7 +1197,7 @@ void gemm_set_tile(int tile) { g_tile_override.store(tile, std::memory_order_rel
 // Tile choice: the largest tile that still gives every CU work.  Larger wave
 // tiles need fewer LDS fragment bytes per MFMA; 8-wave workgroups put two
 // waves on each SIMD.
-template <int PATH, bool BT>
+template <int PATH, bool BT, bool SWI = false>
 static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
   const int64_t cus = 256;
   int t = g_tile_override.load(std::memory_order_relaxed);
@@ -1171,17 +1220,18 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
     else t = mid ? 5 : 1;
   }
   switch (t) {
-    case 6: return launch_t<PATH, 256, 256, BT, 1, 4, 2, true>(a, st);
-    case 5: return launch_t<PATH, 256, 128, BT, 1, 4, 2, true>(a, st);
-    case 4: return launch_t<PATH, 128, 128, BT, 1, 4, 2, true>(a, st);
-    case 3: return launch_t<PATH, 256, 256, BT, 1, 2, 4>(a, st);
-    case 2: return launch_t<PATH, 256, 128, BT, 1, 4, 2>(a, st);
-    case 1: return launch_t<PATH, 128, 128, BT, 2, 2, 4>(a, st);
-    default: return launch_t<PATH, 128, 128, BT, 2, 2, 2>(a, st);
+    case 6: return launch_t<PATH, 256, 256, BT, 1, 4, 2, true, SWI>(a, st);
+    case 5: return launch_t<PATH, 256, 128, BT, 1, 4, 2, true, SWI>(a, st);
+    case 4: return launch_t<PATH, 128, 128, BT, 1, 4, 2, true, SWI>(a, st);
+    case 3: return launch_t<PATH, 256, 256, BT, 1, 2, 4, false, SWI>(a, st);
+    case 2: return launch_t<PATH, 256, 128, BT, 1, 4, 2, false, SWI>(a, st);
+    case 1: return launch_t<PATH, 128, 128, BT, 2, 2, 4, false, SWI>(a, st);
+    default: return launch_t<PATH, 128, 128, BT, 2, 2, 2, false, SWI>(a, st);
   }
 }
 
 hipError_t launch_gemm(int path, bool bt, const GemmArgs& a, hipStream_t st) {
+  if (a.swiglu_inter) return launch_p<P_F16, false, true>(a, st);
   if (path == P_FP8) return bt ? launch_p<P_FP8, true>(a, st) : launch_p<P_FP8, false>(a, st);
   if (path == P_F16) return bt ? launch_p<P_F16, true>(a, st) : launch_p<P_F16, false>(a, st);
   return bt ? launch_p<P_BF16, true>(a, st) : launch_p<P_BF16, false>(a, st);

@@ -137,6 +137,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return umax(umax(a, b), umax(c, d));
 }
 
+// SwiGLU of two BF16 pairs (gate g, up u; element 0 in the low half):
+// bf16_RNE(g / (1 + exp(-g)) * u) in binary32, with the hardware exp2 and
+// reciprocal (a few binary32 ulps; the result is rounded to BF16).  The
+// standalone kernel and the GEMM epilogue that fuses it share this code, so
+// their bits agree.  exp(-g) = inf for very negative g gives -0.
+__device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t g, uint32_t u) {
+  const float g0 = bf16_lo(g), g1 = bf16_hi(g);
+  const float u0 = bf16_lo(u), u1 = bf16_hi(u);
+  const float h0 = __fdividef(g0, 1.0f + __expf(-g0)) * u0;
+  const float h1 = __fdividef(g1, 1.0f + __expf(-g1)) * u1;
+  return f32x2_to_bf16x2(h0, h1);
+}
+
 // MFMA scale layout (1D blocks): chunks of 32 rows x 4 blocks, 128 bytes.
 __device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t blocks_per_row,
                                                 bool mfma) {

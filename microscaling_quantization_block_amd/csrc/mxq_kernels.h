@@ -69,6 +69,7 @@ struct GemmArgs {
   int b_mfma_layout;
   int b_tile;                  // 2D blocks (32x32 / 16x16 / 128x128)
   int a_b128, b_b128;          // FP8 path: 128-wide power-of-two scale blocks (linear)
+  int64_t swiglu_inter;        // > 0: NVFP4 gate_up with SwiGLU fused, c = H [M, inter], N = 2 inter
   int64_t b_group_elems;       // elements between groups' matrices (N * ldb)
   int64_t b_group_scales;      // scale bytes between groups
   int64_t M, N, K;

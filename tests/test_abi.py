@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize", "mx_gemm",
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize",
+                 "mx_gemm", "mx_gemm_swiglu",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
 
@@ -152,6 +153,21 @@ def test_mx_gemm_rejects_bad_arguments():
     assert gemm(op(F.MXFP8), op(F.MXFP8, block=B.TILE, transposed=1), N=48) == 2
     # empty GEMM: no launch
     assert gemm(op(F.MXFP8), op(F.MXFP8), M=0) == 0
+    # blockwise FP8: K % 128, linear scales
+    assert gemm(op(F.FP8_B128), op(F.FP8_B128, block=B.TILE), K=64) == 2
+
+    def fused(a, b, M=32, inter=64, K=64, ldh=64):
+        return L.mx_gemm_swiglu(ctypes.byref(a), ctypes.byref(b), M, inter, K, M, FAKE, ldh, 0, None, None,
+                                None)
+
+    nv = lambda gs, **k: op(F.NVFP4, gs=gs, **k)
+    assert fused(op(F.MXFP8), op(F.MXFP8)) == 4                            # NVFP4 only
+    assert "NVFP4" in _err(L)
+    assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), inter=96, ldh=96) == 2   # inter % 64
+    assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR, block=B.TILE, transposed=1)) == 4
+    assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), ldh=32) == 1             # ldh < inter
+    assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), inter=0) == 0            # nothing to do
+    assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), inter=-64) == 1
 
 
 def test_dequantize_and_swiglu_reject_bad_arguments():

@@ -75,6 +75,10 @@ def run_moe_layer(m, d, check=True):
     Bgu = m.Operand(m.Format.NVFP4, cgu.view(E * N2, H // 2), sgu, Sgu, gs=m.GScale.PER_TENSOR)
     gu = m.mx_gemm(A, Bgu, M, N2, H, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T)
     h = m.mx_swiglu(gu, I)
+    if I % 64 == 0 and H % 64 == 0:
+        # the gate_up GEMM with the SwiGLU in its epilogue gives the same bits
+        hf = m.mx_gemm_swiglu(A, Bgu, M, I, H, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T)
+        assert np.array_equal(from_dev_bf16(hf), from_dev_bf16(h))
     ch, sh, Sh = m.nvfp4_quantize(h, gs=m.GScale.PER_ROW)
     Bdn = m.Operand(m.Format.NVFP4, cdn.view(E * H, I // 2), sdn, Sdn, gs=m.GScale.PER_TENSOR)
     y = m.mx_gemm(m.Operand(m.Format.NVFP4, ch, sh, Sh, gs=m.GScale.PER_ROW), Bdn, M, H, I,
@@ -146,3 +150,42 @@ def test_moe_gather_equals_pre_gathered():
     y2 = m.mx_gemm(m.Operand(m.Format.NVFP4, cg, sg, Sg, gs=m.GScale.PER_ROW), B, 96, 64, 128,
                    group_row_offsets=torch.from_numpy(off).cuda())
     assert np.array_equal(from_dev_bf16(y1), from_dev_bf16(y2))
+
+
+@pytest.mark.parametrize("I,dense", [(128, False), (192, False), (64, True), (320, True)])
+def test_fused_swiglu_every_tile(I, dense):
+    """mx_gemm_swiglu equals mx_swiglu(mx_gemm(...)) bit for bit under every
+    workgroup tile: grouped with a gather (an empty group included) or dense;
+    2I = 384 and 640 leave waves of the last tile past N."""
+    import torch
+    m = mxq()
+    rs = np.random.default_rng(33)
+    H, T = 256, 192
+    E = 1 if dense else 5
+    w = F.bf16_rne(rs.standard_normal((E, 2 * I, H)) * 0.05)
+    x = F.bf16_rne(rs.standard_normal((T, H)))
+    cw, sw, Sw = quantize_experts(m, w)
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw.view(E * 2 * I, H // 2), sw, Sw, gs=m.GScale.PER_TENSOR)
+    if dense:
+        kw, M = {}, T
+    else:
+        M = 300
+        off = np.array([0, 70, 70, 171, 260, 300], dtype=np.int32)     # group 1 empty
+        idx = rs.integers(0, T, M).astype(np.int32)
+        kw = dict(group_row_offsets=torch.from_numpy(off).cuda(), a_row_index=torch.from_numpy(idx).cuda(),
+                  a_rows=T)
+    say(f"fused SwiGLU I={I} dense={dense}")
+    try:
+        for t in range(-1, 7):
+            m.mx_gemm_set_tile(t)
+            gu = m.mx_gemm(A, B, M, 2 * I, H, **kw)
+            ref = from_dev_bf16(m.mx_swiglu(gu, I))
+            got = from_dev_bf16(m.mx_gemm_swiglu(A, B, M, I, H, **kw))
+            assert np.array_equal(got, ref), f"tile {t}"
+    finally:
+        m.mx_gemm_set_tile(-1)
+    # and close to the float64 SwiGLU of the GPU's own gate_up (as for mx_swiglu)
+    ref64 = F.bf16_bits_to_f64(moe.swiglu_f64(from_dev_bf16(gu), I))
+    assert np.all(np.abs(F.bf16_bits_to_f64(got) - ref64) <= 2.0 ** -7 * np.abs(ref64) + 1e-30)
