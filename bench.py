@@ -478,6 +478,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time bound for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the device-copy and host-call probes (keeps traced runs to the step)")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches instead of HIP-graph replays")
     ap.add_argument("--overlap", action="store_true",
@@ -607,7 +609,7 @@ def main():
         "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[4]) * 1e-3) / 1e12, 1),
         "kernels": kernels,
         "roofline": roofline,
-        "measured_reference": measured_reference(m, torch),
+        "measured_reference": None if args.no_reference else measured_reference(m, torch),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
