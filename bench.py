@@ -47,8 +47,9 @@ SETS = 10
 
 # algorithmic bytes / flops per launch
 BYTES_QX = M * K * 2 + M * K // 2 + M * (K // 16) + M * 4
-BYTES_QW = 2 * N * K * 2 + N * K // 2 + (N // 16) * (K // 16) + 4
-BYTES_DQW = N * K // 2 + (N // 16) * (K // 16) + 4 + N * K * 2
+# Q(W) and DQ(W) in one pass: two reads of W (amax, quantize), codes, scales,
+# S and the BF16 dequantized copy
+BYTES_QDQW = 2 * N * K * 2 + N * K // 2 + (N // 16) * (K // 16) + 4 + N * K * 2
 FLOPS_FPROP = 2 * M * N * K
 FLOPS_DGRAD = 2 * M * K * N
 
@@ -147,18 +148,14 @@ def make_sets(m, torch, data):
 
 
 def step_concurrent(m, s, side, torch):
-    """The same five stages with the weight path (Q(W), then DQ(W)) on a
-    second stream: Q(W) runs beside Q(X), DQ(W) beside FPROP.  FPROP waits
-    for Q(W) and DGRAD for DQ(W); the side stream joins back before the end."""
+    """The same stages with the weight path (Q(W) with DQ(W)) on a second
+    stream beside Q(X); FPROP waits for it."""
     main = torch.cuda.current_stream()
     side.wait_stream(main)
     with torch.cuda.stream(side):
-        m.nvfp4_quantize(s["w"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=s["cw"],
-                         block_scales=s["sw"], gscales=s["Sw"])
+        m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
         qw_done = torch.cuda.Event()
         qw_done.record(side)
-        m.mx_dequantize(m.Format.NVFP4, s["cw"], s["sw"], N, K, block=m.Block.TILE, gscales=s["Sw"],
-                        gs=m.GScale.PER_TENSOR, out=s["wdq"])
     m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
     main.wait_event(qw_done)
     m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
@@ -171,27 +168,25 @@ def step_concurrent(m, s, side, torch):
 
 
 def step(m, s, ev=None):
-    """The five stages; ev (list of 6 events) brackets each stage if given."""
+    """The four stages: per-token Q(X); 16x16 Q(W) with its dequantized copy
+    DQ(W) written in the same pass; FPROP; dequantized-backward DGRAD.  ev
+    (list of 5 events) brackets each stage if given."""
     def mark(i):
         if ev is not None:
             ev[i].record()
     mark(0)
     m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
     mark(1)
-    m.nvfp4_quantize(s["w"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=s["cw"],
-                     block_scales=s["sw"], gscales=s["Sw"])
+    m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
     mark(2)
     m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
               m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
                         gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
     mark(3)
-    m.mx_dequantize(m.Format.NVFP4, s["cw"], s["sw"], N, K, block=m.Block.TILE, gscales=s["Sw"],
-                    gs=m.GScale.PER_TENSOR, out=s["wdq"])
-    mark(4)
     m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
               m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
               out=s["dx"])
-    mark(5)
+    mark(4)
 
 
 def cpu_baseline(data, min_seconds):
@@ -524,7 +519,7 @@ def main():
     # per-stage timing: plain launches with HIP events around each stage, on
     # the stream the library launches on (torch's current stream)
     log(f"per-stage timing, {args.steps} eager steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -556,15 +551,15 @@ def main():
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) / args.steps * 1e3
 
-    names = ["quantize_x_nvfp4_1x16_per_token", "quantize_w_nvfp4_16x16_per_tensor",
-             "gemm_fprop_nvfp4", "dequantize_w_nvfp4", "gemm_dgrad_bf16_dequantized"]
-    stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(5)]
+    names = ["quantize_x_nvfp4_1x16_per_token", "quantize_dequantize_w_nvfp4_16x16_per_tensor",
+             "gemm_fprop_nvfp4", "gemm_dgrad_bf16_dequantized"]
+    stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(4)]
     kernels = {}
     for j, nm in enumerate(names):
         us = stage_ms[j] * 1e3
         d = {"us": round(us, 2)}
-        if j in (0, 1, 3):
-            b = [BYTES_QX, BYTES_QW, None, BYTES_DQW][j]
+        if j in (0, 1):
+            b = [BYTES_QX, BYTES_QDQW][j]
             gbps = b / (us * 1e-6) / 1e9
             d.update(bytes=b, GBps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
         else:
@@ -574,7 +569,7 @@ def main():
             if j == 2:
                 d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
         kernels[nm] = d
-    dom = max(range(5), key=lambda j: stage_ms[j])
+    dom = max(range(4), key=lambda j: stage_ms[j])
     dk = kernels[names[dom]]
     if "TFLOPs" in dk:
         roofline = dict(kernel=names[dom], bound="mfma", achieved=dk["TFLOPs"], peak=PEAK_F16_TFLOPS,
@@ -583,8 +578,8 @@ def main():
         roofline = dict(kernel=names[dom], bound="hbm", achieved=dk["GBps"], peak=PEAK_HBM_GBPS,
                         unit="GB/s", frac=dk["frac_hbm"], traffic=measured_traffic(names[dom]))
     value = (FLOPS_FPROP + FLOPS_DGRAD) / (ms_step * 1e-3) / 1e12
-    qbytes = BYTES_QX + BYTES_QW + BYTES_DQW
-    qus = (stage_ms[0] + stage_ms[1] + stage_ms[3]) * 1e3
+    qbytes = BYTES_QX + BYTES_QDQW
+    qus = (stage_ms[0] + stage_ms[1]) * 1e3
     out = {
         "metric": "MX/NVFP4 quantize GB/s + block-scaled GEMM TFLOP/s (% of gfx950 peak)",
         "value": round(value, 2),
@@ -595,18 +590,18 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_eager": round(ms_eager, 4),
         "launch": ("eager" if args.eager else
-                   "hip_graph" + (", weight path (Q(W), DQ(W)) on a second stream" if args.overlap else "")),
+                   "hip_graph" + (", weight path (Q(W) with DQ(W)) on a second stream" if args.overlap else "")),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1/e4m3/fp32) -> f16 MFMA, f32 accumulate; bf16 MFMA for DGRAD",
         "data": "synthetic",
         "config": {"workload": "nvfp4_linear_tokens4096_hidden2048_out768",
-                   "stages": "per-token Q(X) 4096x2048, 16x16 Q(W) 768x2048, FPROP 4096x768x2048, "
-                             "DQ(W), dequantized-backward DGRAD 4096x2048x768",
+                   "stages": "per-token Q(X) 4096x2048, 16x16 Q(W) 768x2048 with DQ(W) in the same pass, "
+                             "FPROP 4096x768x2048, dequantized-backward DGRAD 4096x2048x768",
                    "tokens": M, "hidden": K, "out_features": N, "buffer_sets": SETS},
         "quantize_GBps": round(qbytes / (qus * 1e-6) / 1e9, 1),
-        "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[4]) * 1e-3) / 1e12, 1),
+        "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12, 1),
         "kernels": kernels,
         "roofline": roofline,
         "measured_reference": None if args.no_reference else measured_reference(m, torch),

@@ -198,6 +198,24 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           void* stream);
 
 /*
+ * nvfp4_quantize_dq -- nvfp4_quantize with block TILE (16x16, the weight
+ * copy) that also writes, in the same pass, the dequantized BF16 copy
+ * dq[r, c] = bf16_RNE(fl(fl(value(code) * s_b) * S)) -- exactly what
+ * mx_dequantize returns for that copy -- for the dequantized backward, whose
+ * BF16 GEMMs read DQ(Q(w)) ("NVFP4 RL training" / "The 4-bitter Lesson",
+ * section on the dequantized backward).  Saves the dequantizer's launch and
+ * its re-read of the codes.
+ *   gs      PER_TENSOR or GIVEN;  rnd  RNE or RNE_4OVER6 (SR: MXQ_EUNSUPPORTED)
+ *   dq      BF16 [rows, cols], ld_dq elements (16-byte aligned, ld_dq*2 % 16 == 0)
+ *   other arguments, shapes and errors as nvfp4_quantize with block TILE,
+ *   LINEAR scale layout.
+ */
+mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             mxq_gscale gs, mxq_round rnd, uint8_t* codes, int64_t ld_codes_bytes,
+                             uint8_t* block_scales, float* gscales, uint16_t* dq, int64_t ld_dq,
+                             void* stream);
+
+/*
  * nvfp4_quantize_rht -- columnwise NVFP4 copy (COL, 16x1 blocks, stored
  * transposed) of the random Hadamard transform of x [rows, cols].  The NVFP4
  * pretraining recipe applies this transform to the two inputs of the WGRAD

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
-           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
+           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
            "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
@@ -87,6 +87,7 @@ def lib():
     L.mx_quantize.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, i64, vp, vp]
     L.fp8bw_quantize.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp, i64, vp, vp]
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
+    L.nvfp4_quantize_dq.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, vp, i64, vp]
     L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
                                      vp, vp]
     L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
@@ -96,7 +97,7 @@ def lib():
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
-    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize",
+    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
               "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
@@ -232,6 +233,27 @@ def nvfp4_quantize(x, block=Block.ROW, gs=GScale.PER_ROW, rnd=Round.RNE, seed=0,
                                 int(seed), int(stream_id), int(tensor_tag), int(layout), _ptr(codes),
                                 codes.stride(0), _ptr(block_scales), _ptr(gscales), _stream(stream)))
     return codes, block_scales, gscales
+
+
+def nvfp4_quantize_dq(x, gs=GScale.PER_TENSOR, rnd=Round.RNE, codes=None, block_scales=None,
+                      gscales=None, dq=None, stream=None):
+    """16x16 NVFP4 weight copy plus its dequantized BF16 copy in one pass.
+    Returns (codes, block scales, S, dq)."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    gs = GScale(gs)
+    codes = _u8((rows, cols // 2), dev) if codes is None else codes
+    block_scales = _u8((rows // 16, cols // 16), dev) if block_scales is None else block_scales
+    if gscales is None:
+        if gs == GScale.GIVEN:
+            raise ValueError("gs=GIVEN needs gscales")
+        gscales = torch.empty(1, dtype=torch.float32, device=dev)
+    dq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dq is None else dq
+    _check(lib().nvfp4_quantize_dq(_ptr(x), rows, cols, x.stride(0), int(gs), int(rnd), _ptr(codes),
+                                   codes.stride(0), _ptr(block_scales), _ptr(gscales), _ptr(dq),
+                                   dq.stride(0), _stream(stream)))
+    return codes, block_scales, gscales, dq
 
 
 def nvfp4_quantize_rht(x, sign_mask, gs=GScale.PER_TENSOR, rnd=Round.RNE, seed=0, stream_id=1,

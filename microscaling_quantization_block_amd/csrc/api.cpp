@@ -139,11 +139,12 @@ mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   return hip_status(e, "fp8bw_quantize");
 }
 
-mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                          mxq_block block, mxq_gscale gs, mxq_round rnd, uint64_t seed,
-                          uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
-                          uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
-                          float* gscales, void* stream) {
+// dq != nullptr: also the dequantized BF16 copy (TILE only)
+static mxq_status nvfp4_quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                      mxq_block block, mxq_gscale gs, mxq_round rnd, uint64_t seed,
+                                      uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
+                                      uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                                      float* gscales, uint16_t* dq, int64_t ld_dq, void* stream) {
   if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "nvfp4_quantize: negative size");
   if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE)
     return fail(block == MXQ_BLOCK_DUAL ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
@@ -180,6 +181,12 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
       ((uintptr_t)gscales & 3u))
     return fail(MXQ_EALIGN, "nvfp4_quantize: x/codes must be 16-byte aligned, ld_x*2 %% 16 == 0, "
                             "ld_codes_bytes %% 8 == 0, gscales 4-byte aligned");
+  if (dq) {
+    if (block != MXQ_BLOCK_TILE)
+      return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize_dq: the fused dequantized copy is for TILE copies");
+    if (ld_dq < cols) return fail(MXQ_EINVAL, "nvfp4_quantize_dq: ld_dq < cols");
+    if (!aligned16(dq) || (ld_dq * 2) % 16) return fail(MXQ_EALIGN, "nvfp4_quantize_dq: dq 16-byte aligned, ld_dq*2 %% 16 == 0");
+  }
   hipStream_t st = S(stream);
   const int rm = rnd == MXQ_ROUND_SR ? 1 : rnd == MXQ_ROUND_RNE_4OVER6 ? 2 : 0;
   hipError_t e = hipSuccess;
@@ -195,11 +202,31 @@ mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                               gmode, mfma, rm, seed, stream_id, tensor_tag, st);
   else if (block == MXQ_BLOCK_TILE)
     e = mxq::launch_nvfp4_tile16(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                                 gmode, rm, seed, stream_id, tensor_tag, st);
+                                 gmode, rm, seed, stream_id, tensor_tag, dq, ld_dq, st);
   else
     e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
                               gmode, mfma, rm == 1, false, 0u, seed, stream_id, tensor_tag, st);
-  return hip_status(e, "nvfp4_quantize");
+  return hip_status(e, dq ? "nvfp4_quantize_dq" : "nvfp4_quantize");
+}
+
+mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, mxq_gscale gs, mxq_round rnd, uint64_t seed,
+                          uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
+                          uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                          float* gscales, void* stream) {
+  return nvfp4_quantize_impl(x, rows, cols, ld_x, block, gs, rnd, seed, stream_id, tensor_tag, layout,
+                             codes, ld_codes_bytes, block_scales, gscales, nullptr, 0, stream);
+}
+
+mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                             mxq_gscale gs, mxq_round rnd, uint8_t* codes, int64_t ld_codes_bytes,
+                             uint8_t* block_scales, float* gscales, uint16_t* dq, int64_t ld_dq,
+                             void* stream) {
+  if (!dq && rows > 0 && cols > 0) return fail(MXQ_EINVAL, "nvfp4_quantize_dq: dq is NULL");
+  if (rnd == MXQ_ROUND_SR)
+    return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize_dq: weights take RNE or RNE_4OVER6");
+  return nvfp4_quantize_impl(x, rows, cols, ld_x, MXQ_BLOCK_TILE, gs, rnd, 0, 0, 0, MXQ_LAYOUT_LINEAR,
+                             codes, ld_codes_bytes, block_scales, gscales, dq, ld_dq, stream);
 }
 
 mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,

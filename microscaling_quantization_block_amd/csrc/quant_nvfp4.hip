@@ -329,12 +329,27 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
 // owns columns [8j, 8j+8) of rows 4rg..4rg+3 of the strip, and the 8 lanes
 // {16 rg + 2t, 16 rg + 2t + 1 : rg = 0..3} form tile t (amax by three lane
 // exchanges).  Consecutive lanes read consecutive 16-byte chunks of a row.
+// dq (optional): also the dequantized copy bf16_RNE(fl(fl(value(code) s_b) S))
+// [rows, cols] (ld_dq elements), the operand of the dequantized backward,
+// from the codes just encoded (the dequantizer's arithmetic and order).
+__device__ __forceinline__ uint4 nv_dq8(uint32_t q, float sb, float S) {
+  mxq_f32x2 c[4];
+  c[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+  c[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+  c[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+  c[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x2_to_bf16x2((c[i].x * sb) * S, (c[i].y * sb) * S);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <int RM>
 __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id,
-    uint32_t tensor_tag) {
+    uint32_t tensor_tag, uint16_t* __restrict__ dq, int64_t ld_dq) {
   constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t cpr = cols >> 3;
@@ -381,15 +396,20 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     e4 = e4 + __uint_as_float(lane_xor_u32(__float_as_uint(e4), 32));
     const bool take4 = e4 < e6;
     if (!valid) return;
+    const float sbc = e4m3_to_f32(take4 ? b4.code : b6.code);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint32_t*>(codes + (r0 + i) * ld_codes + j * 4) = take4 ? q4[i] : q6[i];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t q = take4 ? q4[i] : q6[i];
+      *reinterpret_cast<uint32_t*>(codes + (r0 + i) * ld_codes + j * 4) = q;
+      if (dq) *reinterpret_cast<uint4*>(dq + (r0 + i) * ld_dq + j * 8) = nv_dq8(q, sbc, S);
+    }
     if ((j & 1) == 0 && rg == 0)
       bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)(take4 ? b4.code : b6.code);
     return;
   }
   if (!valid) return;
   const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
+  const float sbc = e4m3_to_f32(bs.code);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t r = r0 + i;
@@ -397,6 +417,7 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
     const uint32_t q = nv_encode8<SR>(v[i], bs.r, dr);
     *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
+    if (dq) *reinterpret_cast<uint4*>(dq + r * ld_dq + j * 8) = nv_dq8(q, sbc, S);
   }
   if ((j & 1) == 0 && rg == 0) bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
 }
@@ -654,13 +675,13 @@ hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
                                float* gscales, int gmode, int rm, uint64_t seed, uint32_t sid,
-                               uint32_t tag, hipStream_t st) {
+                               uint32_t tag, uint16_t* dq, int64_t ld_dq, hipStream_t st) {
   // four waves per workgroup, each 128 columns of a 16-row strip
   dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
   if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
-                       gscales, gmode, seed, sid, tag);
+                       gscales, gmode, seed, sid, tag, dq, ld_dq);
   };
   if (rm == 1) go(nvfp4_tile16_kernel<1>);
   else if (rm == 2) go(nvfp4_tile16_kernel<2>);

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize",
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize",
                  "mx_gemm", "mx_gemm_swiglu",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
@@ -91,6 +91,20 @@ def test_nvfp4_quantize_rejects_bad_arguments():
     assert call(FAKE, 16, 32, 32, B.COL, G.PER_TENSOR, R.RNE_4OVER6, 0, 0, 0, Lay.LINEAR, FAKE, 16, FAKE,
                 FAKE, None) == 4
     assert "Four-Over-Six" in _err(L)
+
+
+def test_nvfp4_quantize_dq_rejects_bad_arguments():
+    m, L = _lib()
+    G, R = m.GScale, m.Round
+    call = lambda gs, rnd=R.RNE, dq=FAKE, ld_dq=32, rows=32, x=FAKE: \
+        L.nvfp4_quantize_dq(x, rows, 32, 32, gs, rnd, FAKE, 16, FAKE, FAKE, dq, ld_dq, None)
+    assert call(G.PER_TENSOR, rnd=R.SR) == 4
+    assert call(G.PER_ROW) == 4                       # a tiled copy takes a per-tensor scale
+    assert call(G.PER_TENSOR, dq=None) == 1
+    assert call(G.PER_TENSOR, ld_dq=16) == 1
+    assert call(G.PER_TENSOR, dq=FAKE_ODD) == 3
+    assert call(G.PER_TENSOR, rows=24) == 2
+    assert call(G.PER_TENSOR, x=FAKE_ODD) == 3
 
 
 def test_nvfp4_quantize_rht_rejects_bad_arguments():

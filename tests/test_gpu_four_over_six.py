@@ -100,6 +100,9 @@ def test_tile16_four_over_six(shape):
     dq = m.mx_dequantize(m.Format.NVFP4, c, s, shape[0], shape[1], block=m.Block.TILE, gscales=S,
                          gs=m.GScale.PER_TENSOR)
     assert np.array_equal(from_dev_bf16(dq), ON.dequantize_bf16(rc, rs, rS, "16x16", "per_tensor"))
+    c2, s2, S2, dq2 = m.nvfp4_quantize_dq(to_dev_bf16(x), rnd=m.Round.RNE_4OVER6)
+    assert np.array_equal(to_np(c2), rc) and np.array_equal(to_np(s2), rs)
+    assert np.array_equal(from_dev_bf16(dq2), from_dev_bf16(dq))
     if shape == (768, 2048):
         assert take4.any() and not take4.all()           # both candidates occur (3% at 4 here)
 

@@ -260,6 +260,11 @@ def test_nvfp4_tile16(shape, rnd):
     dq = m.mx_dequantize(m.Format.NVFP4, c, s, shape[0], shape[1], block=m.Block.TILE, gscales=S,
                          gs=m.GScale.PER_TENSOR)
     assert np.array_equal(from_dev_bf16(dq), ON.dequantize_bf16(rc, rs, rS, "16x16", "per_tensor"))
+    if rnd == "rne":
+        # the same copy and its dequantized BF16 copy in one pass
+        c2, s2, S2, dq2 = m.nvfp4_quantize_dq(to_dev_bf16(x))
+        assert np.array_equal(to_np(c2), rc) and np.array_equal(to_np(s2), rs) and np.array_equal(to_np(S2), rS)
+        assert np.array_equal(from_dev_bf16(dq2), from_dev_bf16(dq))
 
 
 @pytest.mark.parametrize("shape,rnd", [((64, 96), "rne"), ((48, 32), "sr"), ((256, 512), "sr")])
