@@ -1,0 +1,319 @@
+"""Parity at the full sizes of the benchmark's configurations 3, 4 and 5, in
+the launch configuration the benchmark times, on sampled outputs the oracle
+computes one by one (configurations 1 and 2 are checked whole elsewhere):
+
+* quantizers: sampled rows (and, for columnwise copies, sampled columns) are
+  byte-identical to the oracle's, with the per-tensor second scales checked
+  against fl(max|x| / 2688) from an exact device max; stochastic-rounding
+  draws are the oracle's Philox draws of the sampled elements' own indices;
+* GEMMs: sampled output elements against the oracle's dequantize-then-matmul
+  of the sampled operand rows (Frobenius error over the sample <= 1e-2 and
+  the element-wise BF16-accumulation bound);
+* the MoE layer's fused SwiGLU epilogue equals the unfused path in full, and
+  MXFP8 DGRAD through the transposed weight copy equals DGRAD reading the
+  weight transposed, in full.
+Inputs follow the benchmark's recipe (seeded device normals for the dense
+MLPs, the numpy recipe for the MoE layer)."""
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import moe
+from oracle import mxfp8 as OM
+from oracle import nvfp4 as ON
+from oracle.philox import element_r16
+import synth
+from tests.util import requires_gpu, to_dev_bf16, from_dev_bf16, to_np, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def mxq():
+    import microscaling_quantization_block_amd as m
+    return m
+
+
+def _idx(t, rows):
+    import torch
+    return torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+
+
+def _rows(t, rows):
+    return t[_idx(t, rows)]
+
+
+def _cols_bits(t, cols):
+    """BF16 bits of columns `cols` of a device matrix, as rows [len(cols), R]."""
+    return from_dev_bf16(t[:, _idx(t, cols)].t().contiguous())
+
+
+def _tensor_S(t):
+    a = float(t.abs().max().float().item())          # the BF16 maximum, exact
+    return np.float32(np.float32(a) / np.float32(2688.0))
+
+
+def _sample(n, k, rs, edges=True):
+    s = set(rs.choice(n, size=min(k, n), replace=False).tolist())
+    if edges:
+        s |= {0, n - 1}
+    return np.array(sorted(s), dtype=np.int64)
+
+
+def _nv_rows(bits, row_ids, cols_total, S_rows, rnd="rne", seed=0, stream=0):
+    """Oracle 1x16 quantization of some rows of a larger tensor; stochastic
+    draws come from the elements' indices row * cols_total + col there."""
+    v = F.bf16_bits_to_f64(bits)
+    r16 = None
+    if rnd == "sr":
+        r, c = np.meshgrid(np.asarray(row_ids, dtype=np.int64), np.arange(v.shape[1], dtype=np.int64),
+                           indexing="ij")
+        r16 = element_r16(r * cols_total + c, seed, stream, 0)
+    return ON._rows_1x16(v, np.asarray(S_rows, dtype=np.float32), rnd, r16)
+
+
+def _nv_cols(bits_cols, col_ids, cols_total, S, rnd="rne", seed=0, stream=1):
+    """Oracle columnwise (16x1) copy rows for some columns c of a [R, cols_total]
+    tensor: bits_cols [len(col_ids), R]; element (r, c) draws with index
+    r * cols_total + c."""
+    v = F.bf16_bits_to_f64(bits_cols)
+    r16 = None
+    if rnd == "sr":
+        c, r = np.meshgrid(np.asarray(col_ids, dtype=np.int64), np.arange(v.shape[1], dtype=np.int64),
+                           indexing="ij")
+        r16 = element_r16(r * cols_total + c, seed, stream, 0)
+    S_rows = np.full(v.shape[0], S, dtype=np.float32)
+    return ON._rows_1x16(v, S_rows, rnd, r16)
+
+
+def _nv_dq(codes, scales, S):
+    S = np.asarray(S, dtype=np.float32).reshape(-1)
+    gs = "per_row" if S.size > 1 else "per_tensor"
+    return (ON.dequantize_f64(codes, scales, S, "1x16", gs), ON.dequantize_f32(codes, scales, S, "1x16", gs))
+
+
+def _check(c_sub_bits, a, b):
+    frob, worst, ok = G.check(c_sub_bits, a[0], b[0], a[1], b[1], rtol_frob=1e-2)
+    assert ok, f"frobenius {frob:.3e}, worst element ratio {worst:.3f}"
+
+
+def _sub(c, rows, cols):
+    return from_dev_bf16(_rows(c, rows)[:, _idx(c, cols)])
+
+
+# ------------------------------------------------------------------ config 5
+
+def test_config5_llama3_8b_nvfp4_mlp_sampled():
+    """Llama-3-8B-shaped MLP, NVFP4: 32768 tokens, hidden 4096, gate_up 28672;
+    per-token X, 16x16 W, stochastic rounding (seed 0) for dY rowwise (stream
+    0) and columnwise (stream 1); FPROP, DGRAD (W read transposed), WGRAD."""
+    m = mxq()
+    rs = np.random.default_rng(55)
+    T, H, N2 = 32768, 4096, 2 * 14336
+    dev = "cuda"
+    say("config 5 full size: generating X, W_gate_up, dY")
+    x = synth.torch_normal_bf16((T, H), 1.0, 51, dev)
+    w = synth.torch_normal_bf16((N2, H), 0.02, 53, dev)
+    dy = synth.torch_normal_bf16((T, N2), 1e-3, 54, dev)
+    say("config 5: quantizers")
+    cx, sx, Sx = m.nvfp4_quantize(x)
+    cw, sw, Sw = m.nvfp4_quantize(w, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    cd, sd, Sd = m.nvfp4_quantize(dy, rnd=m.Round.SR, seed=0, stream_id=0)
+    cdc, sdc, Sdc = m.nvfp4_quantize(dy, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR,
+                                     seed=0, stream_id=1)
+    cxc, sxc, Sxc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    rt = _sample(T, 14, rs)
+    hc = _sample(H, 14, rs)
+    strips = _sample(N2 // 16, 3, rs)
+    rw = np.concatenate([np.arange(16 * s, 16 * s + 16) for s in strips])
+    ic = _sample(N2, 14, rs)
+    # X per-token rows
+    xb = from_dev_bf16(_rows(x, rt))
+    Sx_r = ON.second_scale(np.abs(F.bf16_bits_to_f64(xb)).max(axis=1))
+    ocx, osx = _nv_rows(xb, rt, H, Sx_r)
+    assert np.array_equal(to_np(Sx)[rt], Sx_r)
+    assert np.array_equal(to_np(_rows(cx, rt)), ocx) and np.array_equal(to_np(_rows(sx, rt)), osx)
+    # W: per-tensor S and whole 16-row strips
+    assert to_np(Sw)[0] == _tensor_S(w)
+    for s in strips:
+        wb = F.bf16_bits_to_f64(from_dev_bf16(w[16 * s:16 * s + 16]))
+        oc, os_, _ = ON.quantize_tile16(wb, "given", S_given=to_np(Sw)[0])
+        assert np.array_equal(to_np(cw[16 * s:16 * s + 16]), oc) and np.array_equal(to_np(sw[s:s + 1]), os_)
+    # dY per-token rows with stochastic rounding
+    db = from_dev_bf16(_rows(dy, rt))
+    Sd_r = ON.second_scale(np.abs(F.bf16_bits_to_f64(db)).max(axis=1))
+    ocd, osd = _nv_rows(db, rt, N2, Sd_r, "sr", 0, 0)
+    assert np.array_equal(to_np(Sd)[rt], Sd_r)
+    assert np.array_equal(to_np(_rows(cd, rt)), ocd) and np.array_equal(to_np(_rows(sd, rt)), osd)
+    # columnwise copies: sampled columns of dY (SR, stream 1) and of X (RNE)
+    assert to_np(Sdc)[0] == _tensor_S(dy) and to_np(Sxc)[0] == _tensor_S(x)
+    occ, osc = _nv_cols(_cols_bits(dy, ic), ic, N2, to_np(Sdc)[0], "sr", 0, 1)
+    assert np.array_equal(to_np(_rows(cdc, ic)), occ) and np.array_equal(to_np(_rows(sdc, ic)), osc)
+    oxc, oxs = _nv_cols(_cols_bits(x, hc), hc, H, to_np(Sxc)[0])
+    assert np.array_equal(to_np(_rows(cxc, hc)), oxc) and np.array_equal(to_np(_rows(sxc, hc)), oxs)
+
+    A_x = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B_w = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    say("config 5: FPROP 32768x28672x4096")
+    y = m.mx_gemm(A_x, B_w, T, N2, H)
+    ax = _nv_dq(ocx, osx, Sx_r)
+    wrows = rw[rs.choice(len(rw), 12, replace=False)]
+    w_codes = to_np(_rows(cw, wrows))
+    w_sc = to_np(sw)[wrows // 16]                       # a tile's scale serves its 16 rows
+    bw = _nv_dq(w_codes, w_sc, to_np(Sw))
+    _check(_sub(y, rt, wrows), ax, bw)
+    del y
+    say("config 5: DGRAD 32768x4096x28672 (16x16 W read transposed)")
+    dx = m.mx_gemm(m.Operand(m.Format.NVFP4, cd, sd, Sd, gs=m.GScale.PER_ROW),
+                   m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
+                             transposed=True), T, H, N2)
+    ad = _nv_dq(ocd, osd, Sd_r)
+    # rows of W^T = columns of W: nibble h of every row of the (strip-checked) copy
+    cw_all, sw_all = to_np(cw), to_np(sw)
+    e2 = F.e2m1_value((cw_all[:, hc // 2] >> (4 * (hc % 2))[None, :]) & 0xF).T        # [len(hc), N2]
+    sbt = F.e4m3_value(sw_all[:, hc // 16]).T.repeat(16, axis=1)                         # [len(hc), N2]
+    Sw0 = to_np(Sw)[0]
+    bt32 = ((e2.astype(np.float32) * sbt.astype(np.float32)).astype(np.float32) * Sw0).astype(np.float32)
+    bt64 = e2 * sbt * np.float64(Sw0)
+    _check(_sub(dx, rt, hc), ad, (bt64, bt32))
+    del dx
+    say("config 5: WGRAD 28672x4096x32768 (columnwise copies)")
+    dw = m.mx_gemm(m.Operand(m.Format.NVFP4, cdc, sdc, Sdc, gs=m.GScale.PER_TENSOR),
+                   m.Operand(m.Format.NVFP4, cxc, sxc, Sxc, gs=m.GScale.PER_TENSOR), N2, H, T)
+    _check(_sub(dw, ic, hc), _nv_dq(occ, osc, to_np(Sdc)), _nv_dq(oxc, oxs, to_np(Sxc)))
+
+
+# ------------------------------------------------------------------ config 4
+
+def test_config4_qwen3_8b_mxfp8_mlp_sampled():
+    """Qwen3-8B-shaped MLP, MXFP8: 8192 tokens, hidden 4096, gate_up 24576;
+    DUAL copies of X and dY, the 32x32 weight with its transposed copy;
+    FPROP, DGRAD both ways (equal bits), WGRAD."""
+    m = mxq()
+    rs = np.random.default_rng(44)
+    T, H, N2 = 8192, 4096, 2 * 12288
+    dev = "cuda"
+    say("config 4 full size: generating X, W_gate_up, dY")
+    x = synth.torch_normal_bf16((T, H), 1.0, 41, dev)
+    w = synth.torch_normal_bf16((N2, H), 0.02, 43, dev)
+    dy = synth.torch_normal_bf16((T, N2), 1e-3, 44, dev)
+    say("config 4: quantizers")
+    cx, sx, cxc, sxc = m.mx_quantize(x, block=m.Block.DUAL)
+    cw, sw, cwt, swt = m.mx_quantize(w, block=m.Block.TILE, transposed_copy=True)
+    cd, sd, cdc, sdc = m.mx_quantize(dy, block=m.Block.DUAL)
+    rt, hc, ic = _sample(T, 14, rs), _sample(H, 14, rs), _sample(N2, 14, rs)
+    wstrips = _sample(N2 // 32, 2, rs)
+    tstrips = _sample(H // 32, 2, rs)
+
+    def rows_q(t, rows):
+        return OM.quantize_rowwise(F.bf16_bits_to_f64(from_dev_bf16(_rows(t, rows))))
+
+    def cols_q(t, cols):
+        return OM.quantize_rowwise(F.bf16_bits_to_f64(_cols_bits(t, cols)))
+
+    ox = rows_q(x, rt)
+    assert np.array_equal(to_np(_rows(cx, rt)), ox[0]) and np.array_equal(to_np(_rows(sx, rt)), ox[1])
+    oxc = cols_q(x, hc)
+    assert np.array_equal(to_np(_rows(cxc, hc)), oxc[0]) and np.array_equal(to_np(_rows(sxc, hc)), oxc[1])
+    od = rows_q(dy, rt)
+    assert np.array_equal(to_np(_rows(cd, rt)), od[0]) and np.array_equal(to_np(_rows(sd, rt)), od[1])
+    odc = cols_q(dy, ic)
+    assert np.array_equal(to_np(_rows(cdc, ic)), odc[0]) and np.array_equal(to_np(_rows(sdc, ic)), odc[1])
+    for s in wstrips:                                   # 32-row strips of W, 32x32 tiles
+        oc, osc = OM.quantize_tile32(F.bf16_bits_to_f64(from_dev_bf16(w[32 * s:32 * s + 32])))
+        assert np.array_equal(to_np(cw[32 * s:32 * s + 32]), oc) and np.array_equal(to_np(sw[s:s + 1]), osc)
+    for s in tstrips:                                   # the transposed copy: 32-column strips of W
+        oc, osc = OM.quantize_tile32(F.bf16_bits_to_f64(_cols_bits(w, np.arange(32 * s, 32 * s + 32))))
+        assert np.array_equal(to_np(cwt[32 * s:32 * s + 32]), oc) and np.array_equal(to_np(swt[s:s + 1]), osc)
+
+    def dq(codes, scales):
+        v = OM.dequantize_f64(codes, scales)
+        return v, v.astype(np.float32)
+
+    Op = lambda c, s, **k: m.Operand(m.Format.MXFP8, c, s, **k)
+    say("config 4: FPROP 8192x24576x4096")
+    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N2, H)
+    wrows = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in wstrips])[::5]
+    bw = dq(to_np(_rows(cw, wrows)), to_np(sw)[wrows // 32])
+    _check(_sub(y, rt, wrows), dq(*ox), bw)
+    del y
+    say("config 4: DGRAD 8192x4096x24576, both ways")
+    dx1 = m.mx_gemm(Op(cd, sd), Op(cw, sw, block=m.Block.TILE, transposed=True), T, H, N2)
+    dx2 = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, H, N2)
+    assert np.array_equal(from_dev_bf16(dx1), from_dev_bf16(dx2))
+    trows = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in tstrips])[::5]
+    bt = dq(to_np(_rows(cwt, trows)), to_np(swt)[trows // 32])
+    _check(_sub(dx2, rt, trows), dq(*od), bt)
+    del dx1, dx2
+    say("config 4: WGRAD 24576x4096x8192")
+    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N2, H, T)
+    _check(_sub(dw, ic, hc), dq(*odc), dq(*oxc))
+
+
+# ------------------------------------------------------------------ config 3
+
+def test_config3_qwen3_30b_a3b_moe_sampled():
+    """Qwen3-30B-A3B-shaped MoE layer: 8192 tokens, hidden 2048, 128 experts,
+    I 768, top-8 (65536 routed rows); grouped gate_up with a gather, SwiGLU
+    (fused and unfused), per-token Q(H), grouped down."""
+    import torch
+    from tests.test_gpu_moe import quantize_experts
+    m = mxq()
+    rs = np.random.default_rng(33)
+    say("config 3 full size: generating the layer")
+    d = synth.config3()
+    x, logits = d["x"], d["logits"]
+    T, H = x.shape
+    E, N2, _ = d["w_gu"].shape
+    I = N2 // 2
+    top = moe.route_topk(logits, d["topk"])
+    row_token, off = moe.group_rows(top, E)
+    M = len(row_token)
+    say("config 3: quantizers and grouped GEMMs")
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+    cgu, sgu, Sgu = quantize_experts(m, d["w_gu"])
+    cdn, sdn, Sdn = quantize_experts(m, d["w_dn"])
+    off_d, idx_d = torch.from_numpy(off).cuda(), torch.from_numpy(row_token).cuda()
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    Bgu = m.Operand(m.Format.NVFP4, cgu.view(E * N2, H // 2), sgu, Sgu, gs=m.GScale.PER_TENSOR)
+    gu = m.mx_gemm(A, Bgu, M, N2, H, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T)
+    h = m.mx_swiglu(gu, I)
+    hf = m.mx_gemm_swiglu(A, Bgu, M, I, H, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T)
+    assert np.array_equal(from_dev_bf16(hf), from_dev_bf16(h))
+    del hf
+    ch, sh, Sh = m.nvfp4_quantize(h, gs=m.GScale.PER_ROW)
+    Bdn = m.Operand(m.Format.NVFP4, cdn.view(E * H, I // 2), sdn, Sdn, gs=m.GScale.PER_TENSOR)
+    y = m.mx_gemm(m.Operand(m.Format.NVFP4, ch, sh, Sh, gs=m.GScale.PER_ROW), Bdn, M, H, I,
+                  group_row_offsets=off_d)
+    # every expert's joint gate/up scale and down scale
+    wgu_max = np.abs(F.bf16_bits_to_f64(d["w_gu"].reshape(E, -1))).max(axis=1)
+    wdn_max = np.abs(F.bf16_bits_to_f64(d["w_dn"].reshape(E, -1))).max(axis=1)
+    assert np.array_equal(to_np(Sgu), ON.second_scale(wgu_max))
+    assert np.array_equal(to_np(Sdn), ON.second_scale(wdn_max))
+    say("config 3: sampled checks")
+    rows = _sample(M, 12, rs)
+    jg, jd = _sample(N2, 12, rs), _sample(H, 12, rs)
+    gu_bits = from_dev_bf16(_rows(gu, rows))
+    h_bits = from_dev_bf16(_rows(h, rows))
+    for r in rows:
+        g = int(np.searchsorted(off, r, side="right") - 1)
+        tok = int(row_token[r])
+        xb = x[tok:tok + 1]
+        Sxr = ON.second_scale(np.abs(F.bf16_bits_to_f64(xb)).max(axis=1))
+        ocx, osx = _nv_rows(xb, [tok], H, Sxr)
+        assert np.array_equal(to_np(cx[tok:tok + 1]), ocx) and np.array_equal(to_np(sx[tok:tok + 1]), osx)
+        ocw, osw = _nv_rows(d["w_gu"][g][jg], jg, H, np.full(len(jg), to_np(Sgu)[g], np.float32))
+        assert np.array_equal(to_np(cgu[g][_idx(cgu, jg)]), ocw)
+        _check(_sub(gu, [r], jg), _nv_dq(ocx, osx, Sxr), _nv_dq(ocw, osw, to_np(Sgu)[g:g + 1]))
+        # Q(H) of the GPU's own H row, then the down GEMM on it
+        hv = h_bits[list(rows).index(r)][None]
+        Shr = ON.second_scale(np.abs(F.bf16_bits_to_f64(hv)).max(axis=1))
+        och, osh = _nv_rows(hv, [r], I, Shr)
+        assert np.array_equal(to_np(ch[r:r + 1]), och) and np.array_equal(to_np(sh[r:r + 1]), osh)
+        ocd, osd = _nv_rows(d["w_dn"][g][jd], jd, I, np.full(len(jd), to_np(Sdn)[g], np.float32))
+        assert np.array_equal(to_np(cdn[g][_idx(cdn, jd)]), ocd)
+        _check(_sub(y, [r], jd), _nv_dq(och, osh, Shr), _nv_dq(ocd, osd, to_np(Sdn)[g:g + 1]))
+    # SwiGLU within a few BF16 ulps of the float64 reference on the GPU's gate_up
+    ref = F.bf16_bits_to_f64(moe.swiglu_f64(gu_bits, I))
+    assert np.all(np.abs(F.bf16_bits_to_f64(h_bits) - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
