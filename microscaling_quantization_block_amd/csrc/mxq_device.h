@@ -73,21 +73,25 @@ __device__ __forceinline__ uint32_t f32_to_e2m1_rne(float y) {
 
 // Stochastic rounding onto the E2M1 grid: with lo <= |y| < hi the grid
 // neighbours, round up iff r16 < (|y| - lo) / (hi - lo) * 2^16; |y| >= 6
-// gives 6.  Branch-free: t = |y| * {2, 1, 1/2} on [0, 2), [2, 4), [4, 6)
-// puts the neighbours of every range one apart, so the lower code is
-// floor(t) + {0, 2, 4} and the fraction is t - floor(t); every step is exact
-// (power-of-two scalings of a binary32 value and its floor).
+// gives 6.  On [2^e, 2^(e+1)) (e = 0, 1, 2; [0, 1) with e = 0) the grid step
+// is 2^(e-1), so t = |y| * 2^(1-e) puts the neighbours one apart at
+// floor(t) and floor(t) + 1, whose codes are those values plus 2e.  Rounding
+// up iff r16 * 2^-16 < t - floor(t) is ceil(t - r16 * 2^-16) = floor(t) + 1
+// (else floor(t)): t - r16 * 2^-16 is exact for t >= 1 (both operands
+// within 24 bits of the result) and keeps its sign for t < 1, and one fused
+// multiply-add rounds the exact product once.  Codes past 7 (|y| >= 6)
+// saturate.  Every step is a power-of-two scaling, an exact subtraction or an
+// integer operation.
 __device__ __forceinline__ uint32_t f32_to_e2m1_sr(float y, uint32_t r16) {
   const uint32_t b = __float_as_uint(y);
-  const uint32_t s = (b >> 28) & 8u;
   const float a = __uint_as_float(b & 0x7FFFFFFFu);
-  const bool lt2 = a < 2.0f, lt4 = a < 4.0f;
-  const float t = a * (lt2 ? 2.0f : lt4 ? 1.0f : 0.5f);
-  const float fl = __builtin_floorf(t);
-  const uint32_t lo = (uint32_t)fl + (lt2 ? 0u : lt4 ? 2u : 4u);
-  const bool up = (float)r16 < (t - fl) * 65536.0f;
-  const uint32_t mag = a >= 6.0f ? 7u : lo + (up ? 1u : 0u);
-  return s | mag;
+  const int E = (int)((b >> 23) & 0xFFu) - 127;                 // floor(log2 |y|) for normals
+  const int e = E < 0 ? 0 : E > 2 ? 2 : E;
+  const float t = __builtin_ldexpf(a, 1 - e);
+  // (clamped first: far beyond 6, t would not fit the integer conversion)
+  const float z = __builtin_fminf(__builtin_fmaf(-(float)r16, 0x1p-16f, t), 8.0f);
+  const uint32_t c = (uint32_t)__builtin_ceilf(z) + 2u * (uint32_t)e;
+  return ((b >> 28) & 8u) | (c < 7u ? c : 7u);
 }
 
 // ------------------------------------------------------------------ Philox

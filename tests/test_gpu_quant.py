@@ -233,6 +233,25 @@ def test_nvfp4_row_stochastic_rounding(seed, tag):
     _nv_check_row(m, x, m.GScale.PER_ROW, rnd="sr", seed=seed, tag=tag)
 
 
+@pytest.mark.parametrize("seed", [0, 7, 2 ** 33 + 5])
+def test_nvfp4_sr_encoder_every_bf16_value(seed):
+    """Every BF16 magnitude in [0, 6], both signs, through the stochastic
+    encoder: each 16-value block leads with 6 and S = 1 is given, so s_b = 1,
+    r = 1 and y = x exactly; the draws differ per element and per seed."""
+    m = mxq()
+    import torch
+    mags = np.arange(0, 0x40C1, dtype=np.uint16)                    # BF16 0 .. 6.0
+    vals = np.concatenate([mags, mags | 0x8000])
+    rows = -(-len(vals) // 15)
+    x = np.full(rows * 15, 0x3F80, dtype=np.uint16)                 # pad with 1.0
+    x[:len(vals)] = vals
+    x = x.reshape(rows, 15)
+    six = np.full((rows, 1), 0x40C0, dtype=np.uint16)
+    x = np.concatenate([six, x], axis=1)                             # [rows, 16]
+    say(f"nvfp4 SR encoder, every BF16 value in [0, 6], seed {seed}")
+    _nv_check_row(m, x, m.GScale.GIVEN, rnd="sr", seed=seed, S_given=np.float32(1.0))
+
+
 def test_nvfp4_row_mfma_layout():
     m = mxq()
     x = _edge_bf16(64, 256, 24, nvfp4=True)
