@@ -52,51 +52,47 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
   }
 }
 
-// NVFP4: one lane per 16-element block (8 code bytes, one scale).
+// NVFP4: one lane per half block (8 values, 4 code bytes), so each 16-byte
+// store instruction of a wave covers one contiguous kilobyte of output.
 // gmode: 0 = S per row, 1 = S per tensor.  tile = 1 for 16x16 scales.
 // Codes become binary32 through the hardware FP4 conversion with unit scale
-// (exact code values); IDX32: the block index fits 32 bits, so the row comes
-// from a 32-bit division.
+// (exact code values); IDX32: the half-block index fits 32 bits, so the row
+// comes from a 32-bit division.
 template <bool IDX32>
 __global__ __launch_bounds__(256) void dq_nvfp4_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ gscales, int64_t rows, int64_t cols, int tile, int gmode,
     int mfma_layout, uint16_t* __restrict__ out, int64_t ld_out) {
-  const int64_t bpr = cols >> 4;
-  const int64_t total = rows * bpr;
+  const int64_t hpr = cols >> 3, bpr = cols >> 4;
+  const int64_t total = rows * hpr;
   for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total;
        id += (int64_t)gridDim.x * 256) {
-    int64_t r, b;
+    int64_t r, h;
     if (IDX32) {
-      const uint32_t u = (uint32_t)id, d = (uint32_t)bpr, q32 = u / d;
+      const uint32_t u = (uint32_t)id, d = (uint32_t)hpr, q32 = u / d;
       r = q32;
-      b = u - q32 * d;
+      h = u - q32 * d;
     } else {
-      r = id / bpr;
-      b = id - r * bpr;
+      r = id / hpr;
+      h = id - r * hpr;
     }
-    const uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + b * 8);
+    const int64_t b = h >> 1;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * ld_codes + h * 4);
     const uint32_t sc = tile ? scales[(r >> 4) * bpr + b] : scales[scale_offset(r, b, bpr, mfma_layout)];
     const float sb = e4m3_to_f32(sc);
     const float S = gmode == 0 ? gscales[r] : gscales[0];
-    const uint32_t w[2] = {q.x, q.y};
-    mxq_f32x2 v[8];            // byte i: elements 2i (low nibble) and 2i + 1
+    mxq_f32x2 v[4];            // byte i of w: elements 2i (low nibble) and 2i + 1
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      v[4 * j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0);
-      v[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1);
-      v[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2);
-      v[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3);
-    }
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float da = (v[i].x * sb) * S, db = (v[i].y * sb) * S;   // exact product, then one rounding
       o[i] = f32x2_to_bf16x2(da, db);
     }
-    uint16_t* dst = out + r * ld_out + b * 16;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<uint4*>(out + r * ld_out + h * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -138,7 +134,7 @@ hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t
 hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            const float* gscales, int64_t rows, int64_t cols, bool tile,
                            int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st) {
-  const int64_t total = rows * (cols / 16);
+  const int64_t total = rows * (cols / 8);
   auto kern = total < (int64_t(1) << 32) ? dq_nvfp4_kernel<true> : dq_nvfp4_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(grid_for(total)), dim3(256), 0, st, codes, ld_codes, scales,
                      gscales, rows, cols, (int)tile, gmode, (int)mfma, out, ld_out);
