@@ -5,10 +5,10 @@ One step = one pass over one batch of the NVFP4 workload with 4096 tokens,
 hidden 2048 and 768 outputs (the second configuration of the benchmark set):
   1. per-token NVFP4 quantization of the activations X [4096, 2048]
   2. 16x16 NVFP4 quantization of the weight W [768, 2048] (per-tensor scale:
-     an amax pass, then the quantize pass)
+     an amax pass, then the quantize pass, which also writes the dequantized
+     BF16 copy DQ(Q(W)) [768, 2048], the dequantized-backward operand)
   3. FPROP  Y [4096, 768]  = Q(X) Q(W)^T       (NVFP4 x NVFP4, BF16 out)
-  4. DQ(Q(W)) -> BF16 [768, 2048]              (dequantized backward operand)
-  5. DGRAD dX [4096, 2048] = dY DQ(Q(W))       (BF16, weight read transposed)
+  4. DGRAD dX [4096, 2048] = dY DQ(Q(W))       (BF16, weight read transposed)
 Inputs are seeded synthetic tensors (the pages' models and datasets stand in
 as shapes and distributions only), resident in HBM before timing; ten
 buffer sets (> 512 MB in total) rotate so reads come from HBM rather than
@@ -16,15 +16,16 @@ the 256 MB last-level cache.
 
 Prints ONE JSON line on stdout.  `value` is the step's GEMM throughput: the
 two GEMMs' algorithmic flops (2*M*N*K each) over the whole step's time,
-quantization and dequantization included.  The timed steps replay the step
+quantization and dequantization included.  The step is timed two ways, both
+reported: plain launches back to back on one stream, and replays of the step
 captured once per buffer set as a HIP graph (the library records no memsets,
-so every node is a kernel), on one stream in stage order.  `--overlap`
-instead forks the weight path (Q(W), then DQ(W)), which depends on no
-activation, to a second stream (Q(W) beside Q(X), DQ(W) beside FPROP); on
-MI355X that measured slower.  `--eager` times plain launches; the eager
-time is always reported beside the graph time.  Per-kernel times, GB/s, TFLOP/s
-and fractions of peak are in "kernels"; "roofline" describes the kernel with
-the largest share of the step.  The CPU oracle, timed on a bounded sample of
+so every node is a kernel); `value` takes the faster and `launch` names it.
+`--overlap` forks the weight path (Q(W) with DQ(W)), which depends on no
+activation, to a second stream inside the graph; on MI355X that measured
+slower.  `--eager` skips the graph.  Per-stage times (HIP events around each
+stage of spin-fronted eager steps), GB/s, TFLOP/s and fractions of peak are
+in "kernels"; "roofline" times the stage with the largest share again over
+runs of back-to-back launches.  The CPU oracle, timed on a bounded sample of
 the same step, is reported as "cpu_baseline".
 """
 
@@ -167,26 +168,73 @@ def step_concurrent(m, s, side, torch):
               out=s["dx"])
 
 
+def stages(m):
+    """The four stages of the step, each a function of one buffer set: per-token
+    Q(X); 16x16 Q(W) with its dequantized copy DQ(W) written in the same pass;
+    FPROP; dequantized-backward DGRAD."""
+    def qx(s):
+        m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
+
+    def qdqw(s):
+        m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
+
+    def fprop(s):
+        m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
+                  m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
+                            gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
+
+    def dgrad(s):
+        m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
+                  m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
+                  out=s["dx"])
+    return [qx, qdqw, fprop, dgrad]
+
+
 def step(m, s, ev=None):
-    """The four stages: per-token Q(X); 16x16 Q(W) with its dequantized copy
-    DQ(W) written in the same pass; FPROP; dequantized-backward DGRAD.  ev
-    (list of 5 events) brackets each stage if given."""
-    def mark(i):
+    """One step: the four stages in order.  ev (list of 5 events) brackets
+    each stage if given."""
+    for i, fn in enumerate(stages(m)):
         if ev is not None:
             ev[i].record()
-    mark(0)
-    m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
-    mark(1)
-    m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
-    mark(2)
-    m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
-              m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
-                        gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
-    mark(3)
-    m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
-              m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
-              out=s["dx"])
-    mark(4)
+        fn(s)
+    if ev is not None:
+        ev[4].record()
+
+
+def batch_us(torch, fn, sets, spin, repeats):
+    """Mean time of one launch of `fn` over back-to-back launches on every
+    buffer set in turn: HIP events around each run of len(sets) launches,
+    each run behind a spin kernel so that the launches are all queued before
+    the first event fires."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(repeats)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        torch.cuda._sleep(spin)
+        a.record()
+        for s_ in sets:
+            fn(s_)
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / (repeats * len(sets)) * 1e3
+
+
+SPIN_US = 100.0        # longer than the host takes to enqueue one step
+BATCH_SPIN_US = 300.0  # longer than it takes to enqueue one launch per buffer set
+
+
+def spin_cycles(torch, us):
+    """Argument of torch.cuda._sleep (a one-thread spin on the GPU clock
+    counter) that spins for about `us` microseconds, from one timed probe."""
+    probe = 1 << 20
+    torch.cuda._sleep(probe)                      # first launch outside the probe
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(probe)
+    b.record()
+    torch.cuda.synchronize()
+    per_us = probe / max(a.elapsed_time(b) * 1e3, 1.0)
+    return max(int(per_us * us), 1)
 
 
 def cpu_baseline(data, min_seconds):
@@ -516,20 +564,30 @@ def main():
         step(m, sets[i % SETS])
     torch.cuda.synchronize()
 
-    # per-stage timing: plain launches with HIP events around each stage, on
-    # the stream the library launches on (torch's current stream)
-    log(f"per-stage timing, {args.steps} eager steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} eager steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(m, sets[i % SETS], events[i])
+        step(m, sets[i % SETS])
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) / args.steps * 1e3
 
-    if args.eager:
-        ms_step = ms_eager
-    else:
+    # per-stage timing: HIP events around each stage, on the stream the
+    # library launches on (torch's current stream).  A spin kernel ahead of
+    # each step keeps the GPU busy while the host enqueues the four stages, so
+    # the stages run back to back and each event pair brackets its kernels,
+    # not the host's launch overhead.
+    spin = spin_cycles(torch, SPIN_US)
+    log(f"per-stage timing, {args.steps} eager steps, each behind a {SPIN_US:.0f} us spin")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        torch.cuda._sleep(spin)
+        step(m, sets[i % SETS], events[i])
+    torch.cuda.synchronize()
+
+    ms_graph = None
+    if not args.eager:
         log("capturing one HIP graph per buffer set")
         side = torch.cuda.Stream()              # default priority
         graphs = []
@@ -549,7 +607,10 @@ def main():
         for i in range(args.steps):
             graphs[i % SETS].replay()
         torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+        ms_graph = (time.perf_counter() - t0) / args.steps * 1e3
+    # the headline is the faster of the two ways of launching the same step
+    graph_wins = ms_graph is not None and ms_graph < ms_eager
+    ms_step = ms_graph if graph_wins else ms_eager
 
     names = ["quantize_x_nvfp4_1x16_per_token", "quantize_dequantize_w_nvfp4_16x16_per_tensor",
              "gemm_fprop_nvfp4", "gemm_dgrad_bf16_dequantized"]
@@ -569,14 +630,26 @@ def main():
             if j == 2:
                 d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
         kernels[nm] = d
+    # the dominant kernel, timed again over runs of back-to-back launches (an
+    # event pair around every launch adds its own packets to each figure)
     dom = max(range(4), key=lambda j: stage_ms[j])
-    dk = kernels[names[dom]]
-    if "TFLOPs" in dk:
-        roofline = dict(kernel=names[dom], bound="mfma", achieved=dk["TFLOPs"], peak=PEAK_F16_TFLOPS,
-                        unit="TFLOP/s", frac=dk["frac_mfma"], traffic=measured_traffic(names[dom]))
+    reps = max(args.steps // 10, 2)
+    log(f"roofline kernel {names[dom]}: {reps} runs of {SETS} back-to-back launches")
+    dom_us = batch_us(torch, stages(m)[dom], sets, spin_cycles(torch, BATCH_SPIN_US), reps)
+    how = (f"HIP events around {reps} runs of {SETS} back-to-back launches (one per buffer set), "
+           "each run behind a spin kernel")
+    if dom >= 2:
+        f = FLOPS_FPROP if dom == 2 else FLOPS_DGRAD
+        tf = f / (dom_us * 1e-6) / 1e12
+        roofline = dict(kernel=names[dom], bound="mfma", achieved=round(tf, 1), peak=PEAK_F16_TFLOPS,
+                        unit="TFLOP/s", frac=round(tf / PEAK_F16_TFLOPS, 4),
+                        traffic=measured_traffic(names[dom]), us_per_launch=round(dom_us, 2), timing=how)
     else:
-        roofline = dict(kernel=names[dom], bound="hbm", achieved=dk["GBps"], peak=PEAK_HBM_GBPS,
-                        unit="GB/s", frac=dk["frac_hbm"], traffic=measured_traffic(names[dom]))
+        b = [BYTES_QX, BYTES_QDQW][dom]
+        gbps = b / (dom_us * 1e-6) / 1e9
+        roofline = dict(kernel=names[dom], bound="hbm", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS,
+                        unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
+                        traffic=measured_traffic(names[dom]), us_per_launch=round(dom_us, 2), timing=how)
     value = (FLOPS_FPROP + FLOPS_DGRAD) / (ms_step * 1e-3) / 1e12
     qbytes = BYTES_QX + BYTES_QDQW
     qus = (stage_ms[0] + stage_ms[1]) * 1e3
@@ -589,8 +662,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_eager": round(ms_eager, 4),
-        "launch": ("eager" if args.eager else
-                   "hip_graph" + (", weight path (Q(W) with DQ(W)) on a second stream" if args.overlap else "")),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
+        "launch": ("hip_graph" + (", weight path (Q(W) with DQ(W)) on a second stream" if args.overlap else "")
+                   if graph_wins else "eager (back-to-back launches on one stream)"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
