@@ -534,6 +534,8 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
 // ------------------------------------------------------------ tensor amax
 __global__ void nv_zero_u32(uint32_t* p) { *p = 0u; }
 
+// IDX32: the chunk index fits 32 bits, so rows come from 32-bit divisions.
+template <bool IDX32>
 __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                       int64_t cols, int64_t ld_x,
                                                       uint32_t* __restrict__ out_bits) {
@@ -547,7 +549,15 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t id = base + u * stride;
-      const int64_t r = id / cpr, c = id - r * cpr;
+      int64_t r, c;
+      if (IDX32) {
+        const uint32_t i32 = (uint32_t)id, d = (uint32_t)cpr, q32 = i32 / d;
+        r = q32;
+        c = i32 - q32 * d;
+      } else {
+        r = id / cpr;
+        c = id - r * cpr;
+      }
       v[u] = id < total ? *reinterpret_cast<const uint4*>(x + r * ld_x + c * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -619,8 +629,8 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t co
   int64_t blocks = (total + 1023) / 1024;          // 4 chunks per lane
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld_x,
-                     bits);
+  auto kern = total < (int64_t(1) << 32) ? nv_amax_kernel<true> : nv_amax_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld_x, bits);
   return hipGetLastError();
 }
 
