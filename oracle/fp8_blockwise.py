@@ -22,8 +22,15 @@ Readings:
    128x128 tiles: codes [rows, cols], scales [rows/128, cols/128].  A tile's
    scale serves its rows and its columns, so the tile copy of x^T is the same
    codes transposed.
-3. FP32 block scales (the other arm of that table) are not built: they need
-   the partial sums of each 128-wide K block scaled outside the MFMA.
+3. FP32 block scales (the other arm of that table, and the DeepSeek-V3
+   recipe itself): s = amax / 448 rounded to binary32, codes RNE E4M3 of
+   x / s (binary32 division, correctly rounded, clamped to +-448 since the
+   rounded quotient of the block maximum may exceed 448 by an ulp).  A zero
+   block stores s = 0 and zero codes.  Dequantization is value(c) * s
+   (exact in float64; BF16 copies round the binary32 product, as the
+   kernels compute it).  A GEMM on such operands is the dequantize-then-
+   matmul definition; its kernel scales each 128-wide K block's partial sums
+   by s_a * s_b outside the MFMA.
 
 Test infrastructure only (see the package docstring).
 """
@@ -87,3 +94,61 @@ def dequantize_f64(codes, scales, block="1x128"):
 
 def dequantize_bf16(codes, scales, block="1x128"):
     return bf16_rne(dequantize_f64(codes, scales, block))
+
+
+# ------------------------------------------------------------ FP32 scales
+
+def _quantize_blocks_f32(xb):
+    """xb [..., n] float64 (BF16 values) -> (codes, binary32 scales [...])."""
+    amax = np.max(np.abs(xb), axis=-1).astype(np.float32)        # exact: BF16 values
+    s = amax / np.float32(E4M3_MAX)                                 # binary32, rounded once
+    safe = np.where(s == 0, np.float32(1), s)
+    q = xb.astype(np.float32) / safe[..., None]                     # binary32 quotient
+    q = np.clip(q, -np.float32(E4M3_MAX), np.float32(E4M3_MAX))
+    q = np.where((s == 0)[..., None], np.float32(0), q)
+    return encode_e4m3_rne(q.astype(np.float64)), s.astype(np.float32)
+
+
+def quantize_rows_f32(x):
+    """1x128 blocks along cols, binary32 scales [rows, cols/128]."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    assert cols % BLOCK == 0
+    codes, sc = _quantize_blocks_f32(x.reshape(rows, cols // BLOCK, BLOCK))
+    return codes.reshape(rows, cols), sc
+
+
+def quantize_cols_f32(x):
+    """128x1 blocks along rows, the copy stored transposed ([cols, rows])."""
+    return quantize_rows_f32(np.ascontiguousarray(np.asarray(x, dtype=np.float64).T))
+
+
+def quantize_tile_f32(x):
+    """One binary32 scale per 128x128 tile, [rows/128, cols/128]."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    assert rows % BLOCK == 0 and cols % BLOCK == 0
+    t = x.reshape(rows // BLOCK, BLOCK, cols // BLOCK, BLOCK).transpose(0, 2, 1, 3)
+    codes, sc = _quantize_blocks_f32(t.reshape(rows // BLOCK, cols // BLOCK, BLOCK * BLOCK))
+    codes = codes.reshape(rows // BLOCK, cols // BLOCK, BLOCK, BLOCK).transpose(0, 2, 1, 3)
+    return codes.reshape(rows, cols), sc
+
+
+def scale_f32_per_element(scales, block):
+    s = np.asarray(scales, dtype=np.float64)
+    if block == "1x128":
+        return np.repeat(s, BLOCK, axis=1)
+    if block == "128x128":
+        return np.repeat(np.repeat(s, BLOCK, axis=0), BLOCK, axis=1)
+    raise ValueError(block)
+
+
+def dequantize_f32s_f64(codes, scales, block="1x128"):
+    """Exact value(c) * s of every element."""
+    return e4m3_value(codes) * scale_f32_per_element(scales, block)
+
+
+def dequantize_f32s_bf16(codes, scales, block="1x128"):
+    """BF16 copy: the binary32 product value(c) * s, rounded to BF16."""
+    p = (e4m3_value(codes).astype(np.float32) * scale_f32_per_element(scales, block).astype(np.float32))
+    return bf16_rne(p.astype(np.float64))
