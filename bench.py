@@ -453,7 +453,30 @@ def rows_report():
     out("f4", "fp8 blockwise WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(
         torch, lambda: m.mx_gemm(m.Operand(F8, bd[2], bd[3]), m.Operand(F8, b4[2], b4[3]), 2 * I4, H4, T4, out=dw4),
         5), flops=f, peak=PEAK_FP8_TFLOPS)
-    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo, b4, bw4, bd
+    # and with binary32 block scales (the partial sums of each 128-K block
+    # scaled outside the MFMA, in a kernel of its own)
+    del bd
+    f4 = m.fp8bw_quantize_f32(x4, block=m.Block.DUAL)
+    out("f4", "fp8 blockwise f32-scale dual 1x128 + 128x1 (X)", [T4, H4], _time_us(torch, lambda: m.fp8bw_quantize_f32(
+        x4, block=m.Block.DUAL, codes=f4[0], scales=f4[1], codes_col=f4[2], scales_col=f4[3]), 10),
+        nbytes=n * 2 + 2 * n + 8 * (n // 128))
+    fw4 = m.fp8bw_quantize_f32(w4, block=m.Block.TILE, transposed_copy=True)
+    out("f4", "fp8 blockwise f32-scale 128x128 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(
+        torch, lambda: m.fp8bw_quantize_f32(w4, block=m.Block.TILE, codes=fw4[0], scales=fw4[1], codes_col=fw4[2],
+                                            scales_col=fw4[3], transposed_copy=True), 10),
+        nbytes=nw * 2 + 2 * nw + 8 * (nw // 16384))
+    fd = m.fp8bw_quantize_f32(dyg4, block=m.Block.DUAL)
+    F32S = m.Format.FP8_B128_F32
+    out("f4", "fp8 blockwise f32-scale FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(
+        m.Operand(F32S, f4[0], f4[1]), m.Operand(F32S, fw4[0], fw4[1], block=m.Block.TILE), T4, 2 * I4, H4, out=y4),
+        5), flops=f, peak=PEAK_FP8_TFLOPS)
+    out("f4", "fp8 blockwise f32-scale DGRAD gate_up (transposed 128x128 copy)", [T4, H4, 2 * I4], _time_us(
+        torch, lambda: m.mx_gemm(m.Operand(F32S, fd[0], fd[1]), m.Operand(F32S, fw4[2], fw4[3], block=m.Block.TILE),
+                                 T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
+    out("f4", "fp8 blockwise f32-scale WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(
+        torch, lambda: m.mx_gemm(m.Operand(F32S, fd[2], fd[3]), m.Operand(F32S, f4[2], f4[3]), 2 * I4, H4, T4,
+                                 out=dw4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
+    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo, b4, bw4, f4, fw4, fd
     torch.cuda.empty_cache()
 
     # ---- Qwen3-30B-A3B-shaped MoE layer, NVFP4 (tokens 8192, hidden 2048, 128 experts, I 768, top-8)

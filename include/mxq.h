@@ -62,9 +62,12 @@ typedef enum {
   MXQ_FMT_MXFP8 = 0,     /* E4M3 codes (1 byte) + E8M0 scales                  */
   MXQ_FMT_NVFP4 = 1,     /* E2M1 codes (2 per byte) + E4M3 scales + FP32 scale */
   MXQ_FMT_BF16 = 2,      /* plain BF16 (GEMM operands only)                    */
-  MXQ_FMT_FP8_B128 = 3   /* DeepSeek-style blockwise FP8: E4M3 codes (1 byte)
+  MXQ_FMT_FP8_B128 = 3,  /* DeepSeek-style blockwise FP8: E4M3 codes (1 byte)
                           * + E8M0 power-of-two scales per 1x128 row block or
                           * 128x128 tile, linear layout (fp8bw_quantize)       */
+  MXQ_FMT_FP8_B128_F32 = 4 /* the same blocks with binary32 scales (an operand's
+                          * scales pointer then points to 4-byte aligned
+                          * floats; fp8bw_quantize_f32)                        */
 } mxq_format;
 
 typedef enum {
@@ -282,15 +285,34 @@ mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           void* stream);
 
 /*
+ * fp8bw_quantize_f32 -- blockwise FP8 with binary32 block scales, the
+ * DeepSeek-V3 recipe itself and the FP32-scale arm of the blockwise
+ * comparison ("End-to-End MXFP8 Reinforcement Learning on Blackwell",
+ * Table 1).  Same blocks, layouts, shapes and alignment as fp8bw_quantize;
+ * the scales are floats (4-byte aligned).
+ * Rule: s = amax / 448 in binary32 (one correctly rounded division; amax over
+ * the 128 values or the 128x128 tile); codes are E4M3 RNE of the binary32
+ * quotient x / s clamped to [-448, 448] (the quotient of the block maximum
+ * can exceed 448 by an ulp and then encodes as 448).  A zero block stores
+ * s = 0 and zero codes.  The GEMM takes the copies as MXQ_FMT_FP8_B128_F32.
+ */
+mxq_status fp8bw_quantize_f32(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              mxq_block block, uint8_t* codes, int64_t ld_codes, float* scales,
+                              uint8_t* codes_col, int64_t ld_codes_col, float* scales_col,
+                              void* stream);
+
+/*
  * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16 (the operand of the
  * dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
  * COL copy that is [input cols, input rows]); block says how its scales are
  * laid out (ROW for a COL copy too, since the stored copy is row-blocked).
  *   MXFP8, FP8_B128: bf16_RNE(value(c) * 2^e)  (exact unless beyond the BF16 range)
+ *   FP8_B128_F32: bf16_RNE(fl32(value(c) * s))
  *   NVFP4: bf16_RNE(fl(fl(value(c) * s_b) * S))
  *   ld_codes  elements for MXFP8 and FP8_B128, BYTES for NVFP4; ld_out elements.
  *   gscales   NVFP4 only ([rows] for PER_ROW, [1] otherwise); may be NULL otherwise.
- *   FP8_B128: LINEAR scales, gs NONE, cols % 128 (and rows % 128 for TILE).
+ *   FP8_B128, FP8_B128_F32: LINEAR scales, gs NONE, cols % 128 (and rows %
+ *   128 for TILE); FP8_B128_F32 scales are 4-byte aligned floats.
  */
 mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
                          const uint8_t* scales, const float* gscales,
@@ -336,6 +358,11 @@ typedef struct {
  * A and B must have the same format (MXFP8 x MXFP8 or FP8_B128 x FP8_B128
  * on the scaled MFMA, NVFP4 x NVFP4 dequantized exactly to FP16 for the FP16
  * MFMA, or BF16 x BF16); mixed formats give MXQ_EUNSUPPORTED.
+ * FP8_B128_F32 x FP8_B128_F32 (binary32 block scales): each 128-wide K
+ * block's partial sums come from the scaled MFMA with unit scales and are
+ * accumulated as fma(s_a(m, kb) * s_b(n, kb), P_kb, acc) in binary32.  Dense
+ * only (num_groups 0, no gather), operands as stored (transposed = 0: DGRAD
+ * reads the weight's transposed TILE copy), ROW or TILE scales for either.
  *   c, ldc              BF16 output, row-major
  *   num_groups          0 for a dense GEMM; else grouped (MoE experts)
  *   group_row_offsets   device int32 [num_groups+1], non-decreasing, from 0 to
@@ -343,7 +370,7 @@ typedef struct {
  *   a_row_index         device int32 [M] or NULL: row r of C reads A row
  *                       a_row_index[r] (gather), every entry in [0, a_rows)
  *   a_rows              rows stored in A (== M when a_row_index is NULL)
- * Shapes: K % 32 (MXFP8), K % 128 (FP8_B128), K % 16 (NVFP4), K % 8 (BF16); a transposed B needs
+ * Shapes: K % 32 (MXFP8), K % 128 (FP8_B128, FP8_B128_F32), K % 16 (NVFP4), K % 8 (BF16); a transposed B needs
  * N and K multiples of its tile size.  M, N any positive size.
  * Offsets and indices are read on the device and are NOT validated: values
  * outside the stated ranges give undefined results.

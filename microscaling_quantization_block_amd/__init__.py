@@ -19,6 +19,7 @@ import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
            "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+           "fp8bw_quantize_f32",
            "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
@@ -31,6 +32,7 @@ class Format(enum.IntEnum):
     NVFP4 = 1
     BF16 = 2
     FP8_B128 = 3
+    FP8_B128_F32 = 4
 
 
 class Block(enum.IntEnum):
@@ -86,6 +88,7 @@ def lib():
     i64, u64, u32, vp, ci = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     L.mx_quantize.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, i64, vp, vp]
     L.fp8bw_quantize.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8bw_quantize_f32.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp, i64, vp, vp]
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
     L.nvfp4_quantize_dq.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, vp, i64, vp]
     L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
@@ -98,6 +101,7 @@ def lib():
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
     for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+              "fp8bw_quantize_f32",
               "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
@@ -171,40 +175,55 @@ def mx_quantize(x, block=Block.ROW, layout=Layout.LINEAR, codes=None, scales=Non
     return codes, scales
 
 
+def _fp8bw(fn, sdt, x, block, codes, scales, codes_col, scales_col, transposed_copy, stream):
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    block = Block(block)
+    u8 = lambda shape: _u8(shape, dev)
+    sc = lambda shape: torch.empty(shape, dtype=sdt, device=dev)
+    if block == Block.COL:
+        codes = u8((cols, rows)) if codes is None else codes
+        scales = sc((cols, rows // 128)) if scales is None else scales
+    elif block == Block.TILE:
+        codes = u8((rows, cols)) if codes is None else codes
+        scales = sc((rows // 128, cols // 128)) if scales is None else scales
+    else:
+        codes = u8((rows, cols)) if codes is None else codes
+        scales = sc((rows, cols // 128)) if scales is None else scales
+    if block == Block.DUAL:
+        codes_col = u8((cols, rows)) if codes_col is None else codes_col
+        scales_col = sc((cols, rows // 128)) if scales_col is None else scales_col
+    elif block == Block.TILE and transposed_copy:
+        codes_col = u8((cols, rows)) if codes_col is None else codes_col
+        scales_col = sc((cols // 128, rows // 128)) if scales_col is None else scales_col
+    else:
+        codes_col = scales_col = None
+    ldcc = codes_col.stride(0) if codes_col is not None else 0
+    _check(fn(_ptr(x), rows, cols, x.stride(0), int(block), _ptr(codes), codes.stride(0),
+              _ptr(scales), _ptr(codes_col), ldcc, _ptr(scales_col), _stream(stream)))
+    if codes_col is not None:
+        return codes, scales, codes_col, scales_col
+    return codes, scales
+
+
 def fp8bw_quantize(x, block=Block.ROW, codes=None, scales=None, codes_col=None, scales_col=None,
                    transposed_copy=False, stream=None):
     """Blockwise FP8 (1x128 / 128x1 / 128x128 blocks, power-of-two scales).
     Returns (codes, scales) or, for DUAL and for TILE with transposed_copy,
     (codes, scales, codes_col, scales_col).  GEMM operands use
     Format.FP8_B128."""
-    _check_2d(x, torch.bfloat16, "x")
-    rows, cols = x.shape
-    dev = x.device
-    block = Block(block)
-    if block == Block.COL:
-        codes = _u8((cols, rows), dev) if codes is None else codes
-        scales = _u8((cols, rows // 128), dev) if scales is None else scales
-    elif block == Block.TILE:
-        codes = _u8((rows, cols), dev) if codes is None else codes
-        scales = _u8((rows // 128, cols // 128), dev) if scales is None else scales
-    else:
-        codes = _u8((rows, cols), dev) if codes is None else codes
-        scales = _u8((rows, cols // 128), dev) if scales is None else scales
-    if block == Block.DUAL:
-        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
-        scales_col = _u8((cols, rows // 128), dev) if scales_col is None else scales_col
-    elif block == Block.TILE and transposed_copy:
-        codes_col = _u8((cols, rows), dev) if codes_col is None else codes_col
-        scales_col = _u8((cols // 128, rows // 128), dev) if scales_col is None else scales_col
-    else:
-        codes_col = scales_col = None
-    ldcc = codes_col.stride(0) if codes_col is not None else 0
-    _check(lib().fp8bw_quantize(_ptr(x), rows, cols, x.stride(0), int(block), _ptr(codes),
-                                codes.stride(0), _ptr(scales), _ptr(codes_col), ldcc,
-                                _ptr(scales_col), _stream(stream)))
-    if codes_col is not None:
-        return codes, scales, codes_col, scales_col
-    return codes, scales
+    return _fp8bw(lib().fp8bw_quantize, torch.uint8, x, block, codes, scales, codes_col,
+                  scales_col, transposed_copy, stream)
+
+
+def fp8bw_quantize_f32(x, block=Block.ROW, codes=None, scales=None, codes_col=None,
+                       scales_col=None, transposed_copy=False, stream=None):
+    """Blockwise FP8 with binary32 block scales (float32 tensors of the
+    shapes fp8bw_quantize gives its byte scales).  GEMM operands use
+    Format.FP8_B128_F32."""
+    return _fp8bw(lib().fp8bw_quantize_f32, torch.float32, x, block, codes, scales, codes_col,
+                  scales_col, transposed_copy, stream)
 
 
 def nvfp4_quantize(x, block=Block.ROW, gs=GScale.PER_ROW, rnd=Round.RNE, seed=0, stream_id=0,

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmxq.so")
-SOURCES = ["api.cpp", "quant_mxfp8.hip", "quant_nvfp4.hip", "dequant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant_mxfp8.hip", "quant_nvfp4.hip", "dequant.hip", "gemm.hip", "gemm_fp8s.hip"]
 
 
 def hipcc():

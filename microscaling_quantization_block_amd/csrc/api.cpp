@@ -104,39 +104,60 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
   return hip_status(e, "mx_quantize");
 }
 
-mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                          mxq_block block, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
-                          uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
-                          void* stream) {
-  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "fp8bw_quantize: negative size");
+// kind 1: power-of-two (E8M0) scales; 2: binary32 scales (scales point to floats)
+static mxq_status fp8bw_impl(const char* fn, int kind, const uint16_t* x, int64_t rows, int64_t cols,
+                             int64_t ld_x, mxq_block block, uint8_t* codes, int64_t ld_codes,
+                             uint8_t* scales, uint8_t* codes_col, int64_t ld_codes_col,
+                             uint8_t* scales_col, void* stream) {
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "%s: negative size", fn);
   if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE &&
       block != MXQ_BLOCK_DUAL)
-    return fail(MXQ_EINVAL, "fp8bw_quantize: block must be ROW, COL, TILE or DUAL");
+    return fail(MXQ_EINVAL, "%s: block must be ROW, COL, TILE or DUAL", fn);
   if (rows == 0 || cols == 0) return ok();
-  if (!x || !codes || !scales) return fail(MXQ_EINVAL, "fp8bw_quantize: null pointer");
+  if (!x || !codes || !scales) return fail(MXQ_EINVAL, "%s: null pointer", fn);
   if (block == MXQ_BLOCK_DUAL && (!codes_col || !scales_col))
-    return fail(MXQ_EINVAL, "fp8bw_quantize: DUAL needs codes_col and scales_col");
+    return fail(MXQ_EINVAL, "%s: DUAL needs codes_col and scales_col", fn);
   const bool tile_t = block == MXQ_BLOCK_TILE && codes_col;
-  if (tile_t && !scales_col) return fail(MXQ_EINVAL, "fp8bw_quantize: a transposed TILE copy needs scales_col");
+  if (tile_t && !scales_col) return fail(MXQ_EINVAL, "%s: a transposed TILE copy needs scales_col", fn);
   const bool second = block == MXQ_BLOCK_DUAL || tile_t;
-  if (cols % 128) return fail(MXQ_ESHAPE, "fp8bw_quantize: cols %% 128 != 0 (cols=%lld)", (long long)cols);
+  if (cols % 128) return fail(MXQ_ESHAPE, "%s: cols %% 128 != 0 (cols=%lld)", fn, (long long)cols);
   if (block != MXQ_BLOCK_ROW && rows % 128)
-    return fail(MXQ_ESHAPE, "fp8bw_quantize: rows %% 128 != 0 for a COL/TILE/DUAL copy (rows=%lld)", (long long)rows);
+    return fail(MXQ_ESHAPE, "%s: rows %% 128 != 0 for a COL/TILE/DUAL copy (rows=%lld)", fn, (long long)rows);
   const int64_t need_row = block == MXQ_BLOCK_COL ? rows : cols;
   if (ld_x < cols || ld_codes < need_row || (second && ld_codes_col < rows))
-    return fail(MXQ_EINVAL, "fp8bw_quantize: leading dimension smaller than the row");
+    return fail(MXQ_EINVAL, "%s: leading dimension smaller than the row", fn);
   if (!aligned16(x) || !aligned16(codes) || (ld_x * 2) % 16 || ld_codes % 16 ||
       (second && (!aligned16(codes_col) || ld_codes_col % 16)))
-    return fail(MXQ_EALIGN, "fp8bw_quantize: pointers and leading dimensions must be 16-byte aligned");
+    return fail(MXQ_EALIGN, "%s: pointers and leading dimensions must be 16-byte aligned", fn);
+  if (kind == 2 && ((reinterpret_cast<uintptr_t>(scales) & 3) ||
+                    (second && (reinterpret_cast<uintptr_t>(scales_col) & 3))))
+    return fail(MXQ_EALIGN, "%s: binary32 scales must be 4-byte aligned", fn);
   hipError_t e;
   if (block == MXQ_BLOCK_ROW)
-    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, false, true, S(stream));
+    e = mxq::launch_mxfp8_row(x, rows, cols, ld_x, codes, ld_codes, scales, false, kind, S(stream));
   else
     e = mxq::launch_mxfp8_tile(block == MXQ_BLOCK_COL ? 0 : block == MXQ_BLOCK_TILE ? 1 : 2, x,
                                rows, cols, ld_x, codes, ld_codes, scales,
                                second ? codes_col : nullptr, ld_codes_col,
-                               second ? scales_col : nullptr, false, true, S(stream));
-  return hip_status(e, "fp8bw_quantize");
+                               second ? scales_col : nullptr, false, kind, S(stream));
+  return hip_status(e, fn);
+}
+
+mxq_status fp8bw_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          mxq_block block, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                          uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
+                          void* stream) {
+  return fp8bw_impl("fp8bw_quantize", 1, x, rows, cols, ld_x, block, codes, ld_codes, scales,
+                    codes_col, ld_codes_col, scales_col, stream);
+}
+
+mxq_status fp8bw_quantize_f32(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              mxq_block block, uint8_t* codes, int64_t ld_codes, float* scales,
+                              uint8_t* codes_col, int64_t ld_codes_col, float* scales_col,
+                              void* stream) {
+  return fp8bw_impl("fp8bw_quantize_f32", 2, x, rows, cols, ld_x, block, codes, ld_codes,
+                    reinterpret_cast<uint8_t*>(scales), codes_col, ld_codes_col,
+                    reinterpret_cast<uint8_t*>(scales_col), stream);
 }
 
 // dq != nullptr: also the dequantized BF16 copy (TILE only)
@@ -276,8 +297,9 @@ mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
                          mxq_block block, mxq_gscale gs, mxq_scale_layout layout, uint16_t* out,
                          int64_t ld_out, void* stream) {
   if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "mx_dequantize: negative size");
-  if (fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4 && fmt != MXQ_FMT_FP8_B128)
-    return fail(MXQ_EINVAL, "mx_dequantize: format must be MXFP8, NVFP4 or FP8_B128");
+  if (fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4 && fmt != MXQ_FMT_FP8_B128 &&
+      fmt != MXQ_FMT_FP8_B128_F32)
+    return fail(MXQ_EINVAL, "mx_dequantize: format must be MXFP8, NVFP4, FP8_B128 or FP8_B128_F32");
   if (block == MXQ_BLOCK_COL || block == MXQ_BLOCK_DUAL)
     return fail(MXQ_EUNSUPPORTED, "mx_dequantize: pass ROW for a stored columnwise copy (it is row-blocked)");
   if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_TILE) return fail(MXQ_EINVAL, "mx_dequantize: bad block");
@@ -291,14 +313,16 @@ mxq_status mx_dequantize(mxq_format fmt, const uint8_t* codes, int64_t ld_codes,
     return fail(MXQ_EALIGN, "mx_dequantize: codes/out 16-byte aligned, ld_out*2 %% 16 == 0, ld_codes %% 8 == 0");
   if (ld_out < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_out < cols");
   hipError_t e;
-  if (fmt == MXQ_FMT_FP8_B128) {
-    if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: FP8_B128 has no second-level scale");
-    if (mfma) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: FP8_B128 scales are linear");
+  if (fmt == MXQ_FMT_FP8_B128 || fmt == MXQ_FMT_FP8_B128_F32) {
+    if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: blockwise FP8 has no second-level scale");
+    if (mfma) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: blockwise FP8 scales are linear");
     if (cols % 128 || (block == MXQ_BLOCK_TILE && rows % 128))
-      return fail(MXQ_ESHAPE, "mx_dequantize: FP8_B128 needs cols %% 128 == 0 (and rows %% 128 for TILE)");
+      return fail(MXQ_ESHAPE, "mx_dequantize: blockwise FP8 needs cols %% 128 == 0 (and rows %% 128 for TILE)");
     if (ld_codes < cols) return fail(MXQ_EINVAL, "mx_dequantize: ld_codes < cols");
-    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, false, true,
-                             out, ld_out, S(stream));
+    if (fmt == MXQ_FMT_FP8_B128_F32 && (reinterpret_cast<uintptr_t>(scales) & 3))
+      return fail(MXQ_EALIGN, "mx_dequantize: binary32 scales must be 4-byte aligned");
+    e = mxq::launch_dq_mxfp8(codes, ld_codes, scales, rows, cols, block == MXQ_BLOCK_TILE, false,
+                             fmt == MXQ_FMT_FP8_B128_F32 ? 2 : 1, out, ld_out, S(stream));
   } else if (fmt == MXQ_FMT_MXFP8) {
     if (gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_dequantize: MXFP8 has no second-level scale");
     if (cols % 32 || (block == MXQ_BLOCK_TILE && rows % 32))
@@ -376,6 +400,50 @@ static mxq_status check_operand(const char* name, const mxq_operand* o, bool is_
   return MXQ_OK;
 }
 
+// Blockwise FP8 with binary32 block scales: dense, row-major operands, ROW
+// ([rows, K/128]) or TILE ([rows/128, K/128]) scales, its own kernel.
+static mxq_status check_fp8s(const char* name, const mxq_operand* o, int64_t rows, int64_t K) {
+  if (!o->data || !o->scales) return fail(MXQ_EINVAL, "mx_gemm: %s->data or ->scales is NULL", name);
+  if (o->transposed)
+    return fail(MXQ_EUNSUPPORTED, "mx_gemm: FP8_B128_F32 operands are read as stored (use the transposed TILE copy)");
+  if (o->block != MXQ_BLOCK_ROW && o->block != MXQ_BLOCK_TILE)
+    return fail(MXQ_EINVAL, "mx_gemm: %s block must be ROW or TILE", name);
+  if (o->layout != MXQ_LAYOUT_LINEAR) return fail(MXQ_EUNSUPPORTED, "mx_gemm: FP8_B128_F32 scales of %s are linear", name);
+  if (o->gs != MXQ_GS_NONE) return fail(MXQ_EUNSUPPORTED, "mx_gemm: FP8_B128_F32 has no second-level scale");
+  if (!aligned16(o->data) || o->ld % 16) return fail(MXQ_EALIGN, "mx_gemm: %s data 16-byte aligned, ld %% 16 == 0", name);
+  if (reinterpret_cast<uintptr_t>(o->scales) & 3) return fail(MXQ_EALIGN, "mx_gemm: %s binary32 scales 4-byte aligned", name);
+  if (o->ld < K) return fail(MXQ_EINVAL, "mx_gemm: %s->ld < K", name);
+  if (o->block == MXQ_BLOCK_TILE && rows % 128)
+    return fail(MXQ_ESHAPE, "mx_gemm: tile-blocked %s needs rows %% 128 == 0", name);
+  return MXQ_OK;
+}
+
+static mxq_status gemm_fp8s_impl(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N,
+                                 int64_t K, uint16_t* c, int64_t ldc, int32_t num_groups,
+                                 const int32_t* a_row_index, void* stream) {
+  if (num_groups > 0 || a_row_index)
+    return fail(MXQ_EUNSUPPORTED, "mx_gemm: FP8_B128_F32 is dense (no groups, no gather)");
+  mxq_status s = check_fp8s("A", a, M, K);
+  if (s != MXQ_OK) return s;
+  s = check_fp8s("B", b, N, K);
+  if (s != MXQ_OK) return s;
+  mxq::Fp8sArgs g = {};
+  g.a = static_cast<const uint8_t*>(a->data);
+  g.a_scales = reinterpret_cast<const float*>(a->scales);
+  g.lda = a->ld;
+  g.a_tile = a->block == MXQ_BLOCK_TILE;
+  g.b = static_cast<const uint8_t*>(b->data);
+  g.b_scales = reinterpret_cast<const float*>(b->scales);
+  g.ldb = b->ld;
+  g.b_tile = b->block == MXQ_BLOCK_TILE;
+  g.c = c;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return hip_status(mxq::launch_gemm_fp8s(g, S(stream)), "mx_gemm");
+}
+
 // inter > 0: the gate_up GEMM with SwiGLU fused (N = 2 inter, c = H [M, inter]).
 static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
                             int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
@@ -390,7 +458,8 @@ static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t 
   if (num_groups > 0 && !group_row_offsets) return fail(MXQ_EINVAL, "mx_gemm: grouped call without offsets");
   if (!a_row_index && a_rows != M) return fail(MXQ_EINVAL, "mx_gemm: a_rows must equal M without a gather index");
   if (a_rows < 1) return fail(MXQ_EINVAL, "mx_gemm: a_rows < 1");
-  const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16 : a->fmt == MXQ_FMT_FP8_B128 ? 128 : 8;
+  const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16
+                  : (a->fmt == MXQ_FMT_FP8_B128 || a->fmt == MXQ_FMT_FP8_B128_F32) ? 128 : 8;
   if (K % blk) return fail(MXQ_ESHAPE, "mx_gemm: K %% %d != 0 (K=%lld)", blk, (long long)K);
   if (ldc < (inter ? inter : N)) return fail(MXQ_EINVAL, "mx_gemm: ldc smaller than the output row");
   if (inter) {
@@ -400,6 +469,8 @@ static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t 
     if (inter % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: inter %% 64 != 0 (inter=%lld)", (long long)inter);
     if (K % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: K %% 64 != 0 (K=%lld)", (long long)K);
   }
+  if (a->fmt == MXQ_FMT_FP8_B128_F32)
+    return gemm_fp8s_impl(a, b, M, N, K, c, ldc, num_groups, a_row_index, stream);
   mxq_status s = check_operand("A", a, false, a_rows, K, 0);
   if (s != MXQ_OK) return s;
   s = check_operand("B", b, true, N, K, N);

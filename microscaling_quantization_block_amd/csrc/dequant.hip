@@ -14,7 +14,8 @@
 namespace mxq {
 
 // MXFP8: one lane per 8 codes.  tile = 1 for 32x32 scales; b128 = 1 for
-// blockwise FP8 (128-wide blocks, 128x128 tiles, linear scales).
+// blockwise FP8 (128-wide blocks, 128x128 tiles, linear scales), 2 for
+// blockwise FP8 with binary32 scales.
 // IDX32: the chunk index fits 32 bits, so the row comes from a 32-bit division.
 template <bool IDX32>
 __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
@@ -35,18 +36,28 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(
       c = id - r * cpr;
     }
     uint2 q = *reinterpret_cast<const uint2*>(codes + r * ld_codes + c * 8);
-    uint32_t s = b128 ? scales[tile ? (r >> 7) * (cols >> 7) + (c >> 4) : r * (cols >> 7) + (c >> 4)]
-                 : tile ? scales[(r >> 5) * (cols >> 5) + (c >> 2)]
-                        : scales[scale_offset(r, c >> 2, cols >> 5, mfma_layout)];
-    int e = (int)s - 127;
+    const int64_t si = b128 ? (tile ? (r >> 7) * (cols >> 7) + (c >> 4) : r * (cols >> 7) + (c >> 4))
+                            : tile ? (r >> 5) * (cols >> 5) + (c >> 2)
+                                   : scale_offset(r, c >> 2, cols >> 5, mfma_layout);
     uint32_t w[2] = {q.x, q.y};
     uint32_t o[4];
+    if (b128 == 2) {
+      // binary32 block scale: the product value(c) * s rounded once to binary32
+      const float sc = reinterpret_cast<const float*>(scales)[si];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t word = w[i >> 1] >> (16 * (i & 1));
-      float a = __builtin_ldexpf(e4m3_to_f32(word & 0xFF), e);
-      float b = __builtin_ldexpf(e4m3_to_f32((word >> 8) & 0xFF), e);
-      o[i] = f32x2_to_bf16x2(a, b);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t word = w[i >> 1] >> (16 * (i & 1));
+        o[i] = f32x2_to_bf16x2(e4m3_to_f32(word & 0xFF) * sc, e4m3_to_f32((word >> 8) & 0xFF) * sc);
+      }
+    } else {
+      int e = (int)scales[si] - 127;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t word = w[i >> 1] >> (16 * (i & 1));
+        float a = __builtin_ldexpf(e4m3_to_f32(word & 0xFF), e);
+        float b = __builtin_ldexpf(e4m3_to_f32((word >> 8) & 0xFF), e);
+        o[i] = f32x2_to_bf16x2(a, b);
+      }
     }
     *reinterpret_cast<uint4*>(out + r * ld_out + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -122,7 +133,7 @@ static unsigned grid_for(int64_t total) {
 }
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
-                           int64_t rows, int64_t cols, bool tile, bool mfma, bool b128,
+                           int64_t rows, int64_t cols, bool tile, bool mfma, int b128,
                            uint16_t* out, int64_t ld_out, hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   auto kern = total < (int64_t(1) << 32) ? dq_mxfp8_kernel<true> : dq_mxfp8_kernel<false>;

@@ -6,16 +6,17 @@
 
 namespace mxq {
 
-// b128: DeepSeek-style blockwise FP8 (128-value blocks, power-of-two scales,
-// linear scale layouts); mfma ignored.
+// b128: 1 = DeepSeek-style blockwise FP8 (128-value blocks, power-of-two
+// scales, linear scale layouts), 2 = the same with binary32 scales (scales
+// then points to floats); mfma ignored for both.
 hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, bool b128,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, int b128,
                             hipStream_t st);
 // mode: 0 COL, 1 TILE (codes_col optional transposed copy), 2 DUAL
 hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
-                             bool mfma, bool b128, hipStream_t st);
+                             bool mfma, int b128, hipStream_t st);
 
 // per-tensor amax: zeroes gscale[0], then leaves the tensor amax there tagged
 // with bit 31 (the quantize kernel decodes it and writes S back)
@@ -46,13 +47,31 @@ hipError_t launch_nvfp4_tensor_scale_rht(const uint16_t* x, int64_t rows, int64_
                                          hipStream_t st);
 
 hipError_t launch_dq_mxfp8(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
-                           int64_t rows, int64_t cols, bool tile, bool mfma, bool b128,
+                           int64_t rows, int64_t cols, bool tile, bool mfma, int b128,
                            uint16_t* out, int64_t ld_out, hipStream_t st);
 hipError_t launch_dq_nvfp4(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                            const float* gscales, int64_t rows, int64_t cols, bool tile,
                            int gmode, bool mfma, uint16_t* out, int64_t ld_out, hipStream_t st);
 hipError_t launch_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
                          uint16_t* h, int64_t ld_h, hipStream_t st);
+
+// Blockwise FP8 GEMM with binary32 block scales: C = A B^T, A [M, K] and
+// B [N, K] E4M3 codes (row-major, lda / ldb bytes), scales [rows, K/128]
+// (ROW) or [rows/128, K/128] (TILE), C BF16 [M, N] (ldc elements).
+struct Fp8sArgs {
+  const uint8_t* a;
+  const float* a_scales;
+  int64_t lda;
+  int a_tile;
+  const uint8_t* b;
+  const float* b_scales;
+  int64_t ldb;
+  int b_tile;
+  uint16_t* c;
+  int64_t ldc;
+  int64_t M, N, K;
+};
+hipError_t launch_gemm_fp8s(const Fp8sArgs& a, hipStream_t st);
 
 enum Path { P_FP8 = 0, P_F16 = 1, P_BF16 = 2 };
 

@@ -50,13 +50,57 @@ __device__ __forceinline__ uint32_t absmax8(uint4 v) {
               umax(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
 }
 
+// Blockwise FP8 with binary32 scales (F32S): s = amax / 448 (one correctly
+// rounded division), codes E4M3 RNE of the binary32 quotient x / s clamped to
+// +-448 (the quotient of the block maximum may exceed 448 by an ulp); a zero
+// block stores s = 0 and zero codes.  A scale travels as its binary32 bits in
+// the same uint32_t that carries an E8M0 code otherwise.
+__device__ __forceinline__ uint32_t f32s_from_amax_bits(uint32_t amax16) {
+  return __float_as_uint(__uint_as_float(amax16 << 16) / 448.0f);
+}
+
+__device__ __forceinline__ uint2 f32s_encode8(uint4 v, uint32_t sbits) {
+  const float sc = __uint_as_float(sbits);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.0f, b = 0.0f;
+    if (sbits != 0u) {
+      a = fminf(fmaxf(bf16_lo(w[i]) / sc, -448.0f), 448.0f);
+      b = fminf(fmaxf(bf16_hi(w[i]) / sc, -448.0f), 448.0f);
+    }
+    o[i] = f32x2_to_e4m3(a, b);
+  }
+  return make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+}
+
+template <bool F32S>
+__device__ __forceinline__ uint32_t blk_scale(uint32_t amax16) {
+  if constexpr (F32S) return f32s_from_amax_bits(amax16);
+  return e8m0_from_amax_bits(amax16);
+}
+
+template <bool F32S>
+__device__ __forceinline__ uint2 blk_encode8(uint4 v, uint32_t s) {
+  if constexpr (F32S) return f32s_encode8(v, s);
+  return mx_encode8(v, s);
+}
+
+// store scale s at element index i of a byte (E8M0) or binary32 scale array
+template <bool F32S>
+__device__ __forceinline__ void blk_store(uint8_t* scales, int64_t i, uint32_t s) {
+  if constexpr (F32S) reinterpret_cast<float*>(scales)[i] = __uint_as_float(s);
+  else scales[i] = (uint8_t)s;
+}
+
 // ---------------------------------------------------------------- ROW 1x32
 // One lane per 8 elements, LPB lanes per block (4: MXFP8's 32 values; 16: a
 // 128-value blockwise-FP8 block); each lane handles UNROLL chunks spaced a
 // grid apart so several 16-byte loads are in flight.  A block's lanes are
 // aligned and consecutive (cols is a multiple of the block), so they run the
 // loop's iterations together and can exchange their maxima.
-template <int UNROLL, int LPB>
+template <int UNROLL, int LPB, bool F32S = false>
 __global__ __launch_bounds__(256) void mxfp8_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales, int mfma_layout) {
@@ -79,12 +123,12 @@ __global__ __launch_bounds__(256) void mxfp8_row_kernel(
       uint32_t m = absmax8(v[u]);
 #pragma unroll
       for (int o = 1; o < LPB; o <<= 1) m = umax(m, lane_xor_u32(m, o));
-      uint32_t s = e8m0_from_amax_bits(m);
+      uint32_t s = blk_scale<F32S>(m);
       if (id[u] < total) {
         int64_t r = id[u] / cpr, c = id[u] - r * cpr;
-        uint2 out = mx_encode8(v[u], s);
+        uint2 out = blk_encode8<F32S>(v[u], s);
         *reinterpret_cast<uint2*>(codes + r * ld_codes + c * 8) = out;
-        if (c % LPB == 0) scales[scale_offset(r, c / LPB, cols / (8 * LPB), mfma_layout)] = (uint8_t)s;
+        if (c % LPB == 0) blk_store<F32S>(scales, scale_offset(r, c / LPB, cols / (8 * LPB), mfma_layout), s);
       }
     }
   }
@@ -120,7 +164,7 @@ __device__ __forceinline__ int mx_slot(int r, int ch) {
 // reduction, then the four waves through LDS).  Scales are linear:
 // [rows, cols/128], [cols, rows/128], [rows/128, cols/128].  The shapes are
 // whole tiles (checked on the host).
-template <int MODE, bool B128>   // MODE 0 = COL, 1 = TILE, 2 = DUAL
+template <int MODE, bool B128, bool F32S = false>   // MODE 0 = COL, 1 = TILE, 2 = DUAL
 __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
@@ -167,7 +211,7 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
         __syncthreads();
         mt = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
       }
-      s[0] = s[1] = e8m0_from_amax_bits(mt);
+      s[0] = s[1] = blk_scale<F32S>(mt);
     } else {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -175,22 +219,22 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
           m[k] = umax(m[k], lane_xor_u32(m[k], 1));
           m[k] = umax(m[k], lane_xor_u32(m[k], 2));
         }
-        s[k] = e8m0_from_amax_bits(m[k]);
+        s[k] = blk_scale<F32S>(m[k]);
       }
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int r = 32 * w + 16 * k + (l >> 2);
       if (r0 + r < rows && c0 + 32 * j < cols) {
-        const uint2 o0 = mx_encode8(v[k][0], s[k]), o1 = mx_encode8(v[k][1], s[k]);
-        const uint2 o2 = mx_encode8(v[k][2], s[k]), o3 = mx_encode8(v[k][3], s[k]);
+        const uint2 o0 = blk_encode8<F32S>(v[k][0], s[k]), o1 = blk_encode8<F32S>(v[k][1], s[k]);
+        const uint2 o2 = blk_encode8<F32S>(v[k][2], s[k]), o3 = blk_encode8<F32S>(v[k][3], s[k]);
         uint8_t* dst = codes + (r0 + r) * ld_codes + c0 + 32 * j;
         *reinterpret_cast<uint4*>(dst) = make_uint4(o0.x, o0.y, o1.x, o1.y);
         *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o2.x, o2.y, o3.x, o3.y);
         if (MODE == 1) {
           if (B128) {
             if (t == 0) {
-              scales[(r0 >> 7) * (cols >> 7) + (c0 >> 7)] = (uint8_t)s[k];
+              blk_store<F32S>(scales, (r0 >> 7) * (cols >> 7) + (c0 >> 7), s[k]);
               tscale[0][0] = s[k];
             }
           } else if ((r & 31) == 0) {
@@ -198,7 +242,7 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
             tscale[w][j] = s[k];
           }
         } else if (B128) {
-          if (j == 0) scales[(r0 + r) * (cols >> 7) + (c0 >> 7)] = (uint8_t)s[k];
+          if (j == 0) blk_store<F32S>(scales, (r0 + r) * (cols >> 7) + (c0 >> 7), s[k]);
         } else {
           scales[scale_offset(r0 + r, (c0 >> 5) + j, cols >> 5, mfma_layout)] = (uint8_t)s[k];
         }
@@ -228,11 +272,11 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
         m = umax(m, lane_xor_u32(m, 2));
       }
       if (r0 + 32 * g >= rows || c0 + c >= cols) continue;
-      const uint32_t s = MODE == 1 ? (B128 ? tscale[0][0] : tscale[g][c >> 5]) : e8m0_from_amax_bits(m);
+      const uint32_t s = MODE == 1 ? (B128 ? tscale[0][0] : tscale[g][c >> 5]) : blk_scale<F32S>(m);
       uint32_t o[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint2 e = mx_encode8(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
+        const uint2 e = blk_encode8<F32S>(make_uint4(col[4 * q], col[4 * q + 1], col[4 * q + 2], col[4 * q + 3]), s);
         o[2 * q] = e.x;
         o[2 * q + 1] = e.y;
       }
@@ -241,12 +285,12 @@ __global__ __launch_bounds__(256) void mxfp8_tile_kernel(
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
       if (MODE == 1) {
         if (B128) {
-          if (t == 0 && k == 0) scales_col[(c0 >> 7) * (rows >> 7) + (r0 >> 7)] = (uint8_t)s;
+          if (t == 0 && k == 0) blk_store<F32S>(scales_col, (c0 >> 7) * (rows >> 7) + (r0 >> 7), s);
         } else if ((c & 31) == 0) {
           scales_col[((c0 + c) >> 5) * (rows >> 5) + ((r0 >> 5) + g)] = (uint8_t)s;
         }
       } else if (B128) {
-        if (g == 0) dscales[(c0 + c) * (rows >> 7) + (r0 >> 7)] = (uint8_t)s;
+        if (g == 0) blk_store<F32S>(dscales, (c0 + c) * (rows >> 7) + (r0 >> 7), s);
       } else {
         dscales[scale_offset(c0 + c, (r0 >> 5) + g, rows >> 5, mfma_layout)] = (uint8_t)s;
       }
@@ -296,14 +340,17 @@ __global__ __launch_bounds__(256) void mxfp8_tile32_kernel(
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, bool b128,
+                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, bool mfma, int b128,
                             hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   constexpr int UNROLL = 4;
   int64_t blocks = (total + 256 * UNROLL - 1) / (256 * UNROLL);
   if (blocks < 1) blocks = 1;
   if (blocks > (1 << 20)) blocks = 1 << 20;
-  if (b128)
+  if (b128 == 2)
+    hipLaunchKernelGGL((mxfp8_row_kernel<UNROLL, 16, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       x, rows, cols, ld_x, codes, ld_codes, scales, 0);
+  else if (b128)
     hipLaunchKernelGGL((mxfp8_row_kernel<UNROLL, 16>), dim3((unsigned)blocks), dim3(256), 0, st, x,
                        rows, cols, ld_x, codes, ld_codes, scales, 0);
   else
@@ -315,7 +362,7 @@ hipError_t launch_mxfp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t cols,
                              int64_t ld_x, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              uint8_t* codes_col, int64_t ld_codes_col, uint8_t* scales_col,
-                             bool mfma, bool b128, hipStream_t st) {
+                             bool mfma, int b128, hipStream_t st) {
   if (mode == 1 && !codes_col && !b128) {
     dim3 g32((unsigned)((cols + T32C - 1) / T32C), (unsigned)(rows / T32R));
     if (g32.y > 65535u) return hipErrorInvalidValue;     // more row strips than a grid holds
@@ -329,7 +376,11 @@ hipError_t launch_mxfp8_tile(int mode, const uint16_t* x, int64_t rows, int64_t 
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, x, rows, cols, ld_x, codes, ld_codes, scales,
                        codes_col, ld_codes_col, scales_col, (int)mfma);
   };
-  if (b128) {
+  if (b128 == 2) {
+    if (mode == 0) go(mxfp8_tile_kernel<0, true, true>);
+    else if (mode == 1) go(mxfp8_tile_kernel<1, true, true>);
+    else go(mxfp8_tile_kernel<2, true, true>);
+  } else if (b128) {
     if (mode == 0) go(mxfp8_tile_kernel<0, true>);
     else if (mode == 1) go(mxfp8_tile_kernel<1, true>);
     else go(mxfp8_tile_kernel<2, true>);

@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize", "mx_dequantize",
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+                 "fp8bw_quantize_f32", "mx_dequantize",
                  "mx_gemm", "mx_gemm_swiglu",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
@@ -142,6 +143,21 @@ def test_fp8bw_quantize_rejects_bad_arguments():
     assert call(FAKE, 0, 128, 128, B.ROW) == 0
 
 
+def test_fp8bw_quantize_f32_rejects_bad_arguments():
+    m, L = _lib()
+    B = m.Block
+    odd4 = ctypes.c_void_p(0x10002)                 # not 4-byte aligned
+    call = lambda rows, cols, blk, sc=FAKE, cc=None, scc=None: L.fp8bw_quantize_f32(
+        FAKE, rows, cols, cols, blk, FAKE, cols if blk != B.COL else rows, sc, cc, rows, scc, None)
+    assert call(128, 96, B.ROW) == 2 and "fp8bw_quantize_f32" in _err(L)
+    assert call(96, 128, B.TILE) == 2
+    assert call(128, 128, B.ROW, sc=odd4) == 3 and "4-byte" in _err(L)
+    assert call(128, 128, B.DUAL, cc=FAKE, scc=odd4) == 3
+    assert call(128, 128, B.DUAL) == 1                # DUAL needs the second copy
+    assert call(128, 128, B.ROW, sc=None) == 1
+    assert call(0, 128, B.ROW) == 0
+
+
 def test_mx_gemm_rejects_bad_arguments():
     m, L = _lib()
     F, B, G = m.Format, m.Block, m.GScale
@@ -169,6 +185,18 @@ def test_mx_gemm_rejects_bad_arguments():
     assert gemm(op(F.MXFP8), op(F.MXFP8), M=0) == 0
     # blockwise FP8: K % 128, linear scales
     assert gemm(op(F.FP8_B128), op(F.FP8_B128, block=B.TILE), K=64) == 2
+    # blockwise FP8 with binary32 scales: dense, as stored, aligned scales
+    f32 = lambda **k: op(F.FP8_B128_F32, ld=128, **k)
+    assert gemm(f32(), f32(), K=64) == 2                                 # K % 128
+    assert gemm(f32(), op(F.FP8_B128, ld=128), K=128) == 4              # mixed formats
+    assert gemm(f32(), f32(transposed=1), K=128) == 4                   # read as stored
+    assert gemm(f32(), f32(block=B.TILE), K=128) == 2                   # TILE needs N % 128
+    assert gemm(f32(), f32(scales=0x10002), K=128) == 3                 # scale alignment
+    assert gemm(f32(), f32(scales=None), K=128) == 1
+    assert gemm(f32(gs=G.PER_TENSOR), f32(), K=128) == 4
+    assert L.mx_gemm(ctypes.byref(f32()), ctypes.byref(f32()), 32, 32, 128, 32, FAKE, 32, 1, FAKE,
+                     None, None) == 4                                    # grouped
+    assert "dense" in _err(L)
 
     def fused(a, b, M=32, inter=64, K=64, ldh=64):
         return L.mx_gemm_swiglu(ctypes.byref(a), ctypes.byref(b), M, inter, K, M, FAKE, ldh, 0, None, None,
@@ -191,6 +219,10 @@ def test_dequantize_and_swiglu_reject_bad_arguments():
     assert L.mx_dequantize(F.NVFP4, FAKE, 32, FAKE, None, 32, 64, B.ROW, G.PER_ROW, Lay.LINEAR, FAKE, 64, None) == 1
     assert L.mx_dequantize(F.MXFP8, FAKE, 64, FAKE, None, 32, 64, B.ROW, G.PER_ROW, Lay.LINEAR, FAKE, 64, None) == 4
     assert L.mx_dequantize(F.BF16, FAKE, 64, FAKE, None, 32, 64, B.ROW, G.NONE, Lay.LINEAR, FAKE, 64, None) == 1
+    assert L.mx_dequantize(F.FP8_B128_F32, FAKE, 128, ctypes.c_void_p(0x10002), None, 32, 128, B.ROW,
+                           G.NONE, Lay.LINEAR, FAKE, 128, None) == 3     # binary32 scale alignment
+    assert L.mx_dequantize(F.FP8_B128_F32, FAKE, 128, FAKE, None, 32, 96, B.ROW, G.NONE, Lay.LINEAR,
+                           FAKE, 128, None) == 2
     assert L.mx_swiglu(FAKE, 4, 12, 24, FAKE, 12, None) == 2
     assert L.mx_swiglu(FAKE_ODD, 4, 16, 32, FAKE, 16, None) == 3
 

@@ -163,3 +163,98 @@ def test_unit_scale_exact_and_tiles_same_bits():
                          OB.dequantize_f64(*OB.quantize_rows(_v(x))),
                          OB.dequantize_f64(*OB.quantize_tile(_v(w)), "128x128"))
     assert _check_arr[2]
+
+
+# ------------------------------------------------------------ binary32 scales
+
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (1024, 640)])
+def test_f32_scales_every_block_kind(shape):
+    m = mxq()
+    x = _edge(*shape, 75)
+    v = _v(x)
+    xd = to_dev_bf16(x)
+    say(f"fp8bw f32 ROW/COL/TILE/DUAL {shape}")
+    c, s = m.fp8bw_quantize_f32(xd)
+    rc, rs = OB.quantize_rows_f32(v)
+    assert to_np(s).dtype == np.float32
+    assert np.array_equal(to_np(s).view(np.uint32), rs.view(np.uint32)) and np.array_equal(to_np(c), rc)
+    dq = m.mx_dequantize(m.Format.FP8_B128_F32, c, s, *shape)
+    assert np.array_equal(from_dev_bf16(dq), OB.dequantize_f32s_bf16(rc, rs))
+    c, s = m.fp8bw_quantize_f32(xd, block=m.Block.COL)
+    cc, cs = OB.quantize_cols_f32(v)
+    assert np.array_equal(to_np(s).view(np.uint32), cs.view(np.uint32)) and np.array_equal(to_np(c), cc)
+    c, s, ct, st = m.fp8bw_quantize_f32(xd, block=m.Block.TILE, transposed_copy=True)
+    tc, ts = OB.quantize_tile_f32(v)
+    assert np.array_equal(to_np(s).view(np.uint32), ts.view(np.uint32)) and np.array_equal(to_np(c), tc)
+    assert np.array_equal(to_np(ct), tc.T) and np.array_equal(to_np(st), ts.T)
+    dq = m.mx_dequantize(m.Format.FP8_B128_F32, c, s, *shape, block=m.Block.TILE)
+    assert np.array_equal(from_dev_bf16(dq), OB.dequantize_f32s_bf16(tc, ts, "128x128"))
+    c, s, c2, s2 = m.fp8bw_quantize_f32(xd, block=m.Block.DUAL)
+    assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(to_np(c2), cc) and np.array_equal(to_np(s2).view(np.uint32), cs.view(np.uint32))
+
+
+def test_f32_scales_tiny_and_huge_blocks():
+    """Blocks whose binary32 scale is subnormal (BF16 subnormal maxima) or
+    near the top of the range, rows of any count (ROW)."""
+    m = mxq()
+    rs_ = np.random.default_rng(76)
+    x = F.bf16_rne(rs_.standard_normal((37, 512)))
+    x[:, :128] = rs_.integers(1, 0x80, (37, 128)).astype(np.uint16) | (rs_.integers(0, 2, (37, 128)) << 15).astype(np.uint16)
+    x[:, 128:256] = F.bf16_rne(rs_.standard_normal((37, 128)) * 2.0 ** 120)
+    x[:, 256:384] = F.bf16_rne(rs_.standard_normal((37, 128)) * 2.0 ** -125)
+    say("fp8bw f32 ROW 37x512 subnormal and huge blocks")
+    c, s = m.fp8bw_quantize_f32(to_dev_bf16(x))
+    rc, rsc = OB.quantize_rows_f32(_v(x))
+    assert np.array_equal(to_np(s).view(np.uint32), rsc.view(np.uint32))
+    assert np.array_equal(to_np(c), rc)
+
+
+def _opf(m, c, s, tile=False):
+    return m.Operand(m.Format.FP8_B128_F32, c, s, block=m.Block.TILE if tile else m.Block.ROW)
+
+
+def test_f32_scales_fprop_dgrad_wgrad():
+    m = mxq()
+    T, H, I = 512, 384, 256
+    rs = np.random.default_rng(77)
+    x = F.bf16_rne(rs.standard_normal((T, H)) * np.exp(rs.standard_normal((T, 1))))
+    w = F.bf16_rne(rs.standard_normal((I, H)) * 0.02)
+    dy = F.bf16_rne(rs.standard_normal((T, I)) * 1e-3)
+    say(f"fp8bw f32 FPROP / DGRAD / WGRAD T={T} H={H} I={I}")
+    cx, sx, cxc, sxc = m.fp8bw_quantize_f32(to_dev_bf16(x), block=m.Block.DUAL)
+    cw, sw, cwt, swt = m.fp8bw_quantize_f32(to_dev_bf16(w), block=m.Block.TILE, transposed_copy=True)
+    cd, sd, cdc, sdc = m.fp8bw_quantize_f32(to_dev_bf16(dy), block=m.Block.DUAL)
+    X64 = OB.dequantize_f32s_f64(*OB.quantize_rows_f32(_v(x)))
+    W64 = OB.dequantize_f32s_f64(*OB.quantize_tile_f32(_v(w)), "128x128")
+    D64 = OB.dequantize_f32s_f64(*OB.quantize_rows_f32(_v(dy)))
+    _check(m.mx_gemm(_opf(m, cx, sx), _opf(m, cw, sw, tile=True), T, I, H), X64, W64)
+    _check(m.mx_gemm(_opf(m, cd, sd), _opf(m, cwt, swt, tile=True), T, H, I), D64, np.ascontiguousarray(W64.T))
+    DC = OB.dequantize_f32s_f64(*OB.quantize_cols_f32(_v(dy)))
+    XC = OB.dequantize_f32s_f64(*OB.quantize_cols_f32(_v(x)))
+    _check(m.mx_gemm(_opf(m, cdc, sdc), _opf(m, cxc, sxc), I, H, T), DC, XC)
+
+
+@pytest.mark.parametrize("M,N,K,tile_b", [(384, 256, 1024, True), (600, 416, 384, False),
+                                          (130, 1, 128, False), (1, 128, 256, True)])
+def test_f32_scales_exact_block_scaling(M, N, K, tile_b):
+    """Small-integer codes with scales from {0.5, 0.75, 1, 1.25, 1.5, 2}
+    per (row, K block) and per (tile, K block): every partial sum, scale
+    product and accumulation is exact in binary32, so C equals the BF16
+    rounding of the exact result: a wrong block index anywhere shows.
+    Ragged M and N run through the tails of the tiles."""
+    import torch
+    m = mxq()
+    rs = np.random.default_rng(78 + M)
+    ints = np.arange(-16, 17)
+    av, bv = rs.choice(ints, (M, K)).astype(np.float64), rs.choice(ints, (N, K)).astype(np.float64)
+    grid = np.array([0.5, 0.75, 1.0, 1.25, 1.5, 2.0])
+    sa = rs.choice(grid, (M, K // 128)).astype(np.float32)
+    sb = rs.choice(grid, ((N // 128) if tile_b else N, K // 128)).astype(np.float32)
+    say(f"fp8bw f32 exact {M}x{N}x{K} tile_b={tile_b}")
+    A = _opf(m, torch.from_numpy(F.encode_e4m3_rne(av)).cuda(), torch.from_numpy(sa).cuda())
+    B = _opf(m, torch.from_numpy(F.encode_e4m3_rne(bv)).cuda(), torch.from_numpy(sb).cuda(), tile=tile_b)
+    a64 = OB.dequantize_f32s_f64(F.encode_e4m3_rne(av), sa)
+    b64 = OB.dequantize_f32s_f64(F.encode_e4m3_rne(bv), sb, "128x128" if tile_b else "1x128")
+    out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
+    assert np.array_equal(out, F.bf16_rne(a64 @ b64.T))
