@@ -20,6 +20,7 @@ import pytest
 
 from oracle import formats as F
 from oracle import gemm as G
+from oracle import fp8_blockwise as OB
 from oracle import moe
 from oracle import mxfp8 as OM
 from oracle import nvfp4 as ON
@@ -247,6 +248,73 @@ def test_config4_qwen3_8b_mxfp8_mlp_sampled():
     _check(_sub(dx2, rt, trows), dq(*od), bt)
     del dx1, dx2
     say("config 4: WGRAD 24576x4096x8192")
+    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N2, H, T)
+    _check(_sub(dw, ic, hc), dq(*odc), dq(*oxc))
+
+
+@pytest.mark.parametrize("kind", ["pow2", "f32"])
+def test_config4_blockwise_fp8_sampled(kind):
+    """The Qwen3-8B-shaped MLP with DeepSeek-style blockwise FP8, both scale
+    kinds: DUAL 1x128 copies of X and dY, the 128x128 weight with its
+    transposed copy (sampled rows, columns and 128-row / 128-column strips
+    against the oracle, codes and scales bit for bit); FPROP, DGRAD (the
+    transposed copy) and WGRAD on sampled outputs."""
+    m = mxq()
+    rs = np.random.default_rng(45)
+    T, H, N2 = 8192, 4096, 2 * 12288
+    dev = "cuda"
+    f32 = kind == "f32"
+    quant = m.fp8bw_quantize_f32 if f32 else m.fp8bw_quantize
+    q_rows = OB.quantize_rows_f32 if f32 else OB.quantize_rows
+    q_tile = OB.quantize_tile_f32 if f32 else OB.quantize_tile
+    deq = OB.dequantize_f32s_f64 if f32 else OB.dequantize_f64
+    fmt = m.Format.FP8_B128_F32 if f32 else m.Format.FP8_B128
+    same = (lambda a, b: np.array_equal(a.view(np.uint32), b.view(np.uint32))) if f32 else np.array_equal
+    say(f"config 4 full size, blockwise FP8 ({kind}): generating X, W_gate_up, dY")
+    x = synth.torch_normal_bf16((T, H), 1.0, 41, dev)
+    w = synth.torch_normal_bf16((N2, H), 0.02, 43, dev)
+    dy = synth.torch_normal_bf16((T, N2), 1e-3, 44, dev)
+    say(f"config 4 ({kind}): quantizers")
+    cx, sx, cxc, sxc = quant(x, block=m.Block.DUAL)
+    cw, sw, cwt, swt = quant(w, block=m.Block.TILE, transposed_copy=True)
+    cd, sd, cdc, sdc = quant(dy, block=m.Block.DUAL)
+    rt, hc, ic = _sample(T, 14, rs), _sample(H, 14, rs), _sample(N2, 14, rs)
+    wstrips, tstrips = _sample(N2 // 128, 2, rs), _sample(H // 128, 2, rs)
+
+    def check_rows(c, sc, o):
+        assert np.array_equal(to_np(c), o[0]) and same(to_np(sc), o[1])
+
+    ox = q_rows(F.bf16_bits_to_f64(from_dev_bf16(_rows(x, rt))))
+    check_rows(_rows(cx, rt), _rows(sx, rt), ox)
+    oxc = q_rows(F.bf16_bits_to_f64(_cols_bits(x, hc)))
+    check_rows(_rows(cxc, hc), _rows(sxc, hc), oxc)
+    od = q_rows(F.bf16_bits_to_f64(from_dev_bf16(_rows(dy, rt))))
+    check_rows(_rows(cd, rt), _rows(sd, rt), od)
+    odc = q_rows(F.bf16_bits_to_f64(_cols_bits(dy, ic)))
+    check_rows(_rows(cdc, ic), _rows(sdc, ic), odc)
+    for st in wstrips:                                  # 128-row strips of W, 128x128 tiles
+        oc, osc = q_tile(F.bf16_bits_to_f64(from_dev_bf16(w[128 * st:128 * st + 128])))
+        check_rows(cw[128 * st:128 * st + 128], sw[st:st + 1], (oc, osc))
+    for st in tstrips:                                  # the transposed copy: 128-column strips
+        oc, osc = q_tile(F.bf16_bits_to_f64(_cols_bits(w, np.arange(128 * st, 128 * st + 128))))
+        check_rows(cwt[128 * st:128 * st + 128], swt[st:st + 1], (oc, osc))
+
+    def dq(codes, scales):
+        v = deq(codes, scales)
+        return v, v.astype(np.float32)
+
+    Op = lambda c, sc, **k: m.Operand(fmt, c, sc, **k)
+    say(f"config 4 ({kind}): FPROP 8192x24576x4096")
+    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N2, H)
+    wrows = np.concatenate([np.arange(128 * st, 128 * st + 128) for st in wstrips])[::9]
+    _check(_sub(y, rt, wrows), dq(*ox), dq(to_np(_rows(cw, wrows)), to_np(sw)[wrows // 128]))
+    del y
+    say(f"config 4 ({kind}): DGRAD 8192x4096x24576 (transposed tile copy)")
+    dx = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, H, N2)
+    trows = np.concatenate([np.arange(128 * st, 128 * st + 128) for st in tstrips])[::9]
+    _check(_sub(dx, rt, trows), dq(*od), dq(to_np(_rows(cwt, trows)), to_np(swt)[trows // 128]))
+    del dx
+    say(f"config 4 ({kind}): WGRAD 24576x4096x8192")
     dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N2, H, T)
     _check(_sub(dw, ic, hc), dq(*odc), dq(*oxc))
 
