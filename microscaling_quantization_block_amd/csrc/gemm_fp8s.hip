@@ -44,6 +44,9 @@ __device__ __forceinline__ int fs_slot(int r, int ch) { return r * 8 + (ch ^ ((r
 
 }  // namespace
 
+// BU: B has 128x128 tile scales, so its scale is one value per stage for the
+// whole workgroup (tiles start at multiples of 128)
+template <bool BU>
 __global__ __launch_bounds__(256, 2) void gemm_fp8s_kernel(Fp8sArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -144,13 +147,19 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8s_kernel(Fp8sArgs p) {
         for (int j = 0; j < 16; ++j) part[j] = 0.0f;
         part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0][tn], af[0][tm], part, 0, 0, 0, 127, 0, 127);
         part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1][tn], af[1][tm], part, 0, 0, 0, 127, 0, 127);
+        if constexpr (BU) {
+          const float f = sa * LS[FS_BM];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 sb = *reinterpret_cast<const float4*>(LS + FS_BM + wn * 64 + tn * 32 + 8 * g + 4 * h);
-          const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+          for (int j = 0; j < 16; ++j) acc[tm][tn][j] = __builtin_fmaf(f, part[j], acc[tm][tn][j]);
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[tm][tn][4 * g + i] = __builtin_fmaf(sa * sbv[i], part[4 * g + i], acc[tm][tn][4 * g + i]);
+          for (int g = 0; g < 4; ++g) {
+            const float4 sb = *reinterpret_cast<const float4*>(LS + FS_BM + wn * 64 + tn * 32 + 8 * g + 4 * h);
+            const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[tm][tn][4 * g + i] = __builtin_fmaf(sa * sbv[i], part[4 * g + i], acc[tm][tn][4 * g + i]);
+          }
         }
       }
     }
@@ -196,15 +205,17 @@ hipError_t launch_gemm_fp8s(const Fp8sArgs& a, hipStream_t st) {
   const int64_t tiles = ((a.M + FS_BM - 1) / FS_BM) * ((a.N + FS_BN - 1) / FS_BN);
   if (tiles < 1 || tiles >= (1ll << 31)) return hipErrorInvalidValue;
   const size_t lds = 2 * (size_t)FS_BUF;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8s_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_fp8s_kernel, dim3((unsigned)tiles), dim3(256), lds, st, a);
-  return hipGetLastError();
+  auto go = [&](auto kern, bool& attr_set) -> hipError_t {
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, st, a);
+    return hipGetLastError();
+  };
+  static bool set_u = false, set_r = false;
+  return a.b_tile ? go(gemm_fp8s_kernel<true>, set_u) : go(gemm_fp8s_kernel<false>, set_r);
 }
 
 }  // namespace mxq
