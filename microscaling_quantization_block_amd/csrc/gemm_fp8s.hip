@@ -54,15 +54,21 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8s_kernel(Fp8sArgs p) {
   const int r32 = lane & 31, h = lane >> 5;
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
-  // contiguous range of tiles (n fastest, so an XCD's tiles share A panels)
+  // contiguous range of the tile order below
   const int tiles_n = (int)((p.N + FS_BN - 1) / FS_BN);
   const int G = (int)gridDim.x;
   const int b = blockIdx.x;
   const int q8 = G >> 3, r8 = G & 7, x = b & 7;
   if ((b >> 3) >= q8 + (x < r8 ? 1 : 0)) return;             // (the grid holds exactly the tiles)
   const int logical = x * q8 + (x < r8 ? x : r8) + (b >> 3);
-  const int64_t m0 = (int64_t)(logical / tiles_n) * FS_BM;
-  const int64_t n0 = (int64_t)(logical % tiles_n) * FS_BN;
+  // grouped order: runs of 8 tile rows walked column by column, so the
+  // tiles in flight on an XCD form a block that shares A and B panels in its
+  // L2 (row by row, they would share one A panel and stream all of B)
+  const int tiles_m = G / tiles_n;
+  const int grp = logical / (8 * tiles_n), in = logical - grp * 8 * tiles_n;
+  const int gm = min(8, tiles_m - grp * 8);
+  const int64_t m0 = (int64_t)(grp * 8 + in % gm) * FS_BM;
+  const int64_t n0 = (int64_t)(in / gm) * FS_BN;
   const int nk = (int)(p.K / FS_BK);
   const int64_t kb_stride = p.K / FS_BK;                      // scales per row
 
