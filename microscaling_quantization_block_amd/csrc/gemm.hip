@@ -1164,12 +1164,8 @@ static hipError_t launch_k(const GemmArgs& a, hipStream_t st) {
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   size_t lds = 2 * (size_t)stages_per_barrier<PATH, BT, DIST, PP>() * (BM + (BD ? 0 : BN)) * LDS_ROW;
   auto kern = gemm_kernel<PATH, BM, BN, BT, DIST, WGM, WGN, PP, SDW, BD, B128, SWI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint32_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void*)kern, (int)lds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * WGM * WGN), lds, st, a);
   return hipGetLastError();
 }

@@ -211,16 +211,12 @@ hipError_t launch_gemm_fp8s(const Fp8sArgs& a, hipStream_t st) {
   const int64_t tiles = ((a.M + FS_BM - 1) / FS_BM) * ((a.N + FS_BN - 1) / FS_BN);
   if (tiles < 1 || tiles >= (1ll << 31)) return hipErrorInvalidValue;
   const size_t lds = 2 * (size_t)FS_BUF;
-  auto go = [&](auto kern, bool& attr_set) -> hipError_t {
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+  auto go = [&](auto kern, std::atomic<uint32_t>& lds_set) -> hipError_t {
+    if (hipError_t e = ensure_lds_limit((const void*)kern, (int)lds, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, st, a);
     return hipGetLastError();
   };
-  static bool set_u = false, set_r = false;
+  static std::atomic<uint32_t> set_u{0}, set_r{0};
   return a.b_tile ? go(gemm_fp8s_kernel<true>, set_u) : go(gemm_fp8s_kernel<false>, set_r);
 }
 

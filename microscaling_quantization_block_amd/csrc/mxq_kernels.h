@@ -4,7 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mxq {
+
+// Raises kernel fn's dynamic-LDS limit to `bytes` on the current device, once
+// per device (bit d of `done` records device d; devices from 32 on set it on
+// every call).  Safe to call from several host threads.
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint32_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = dev < 32 ? (1u << dev) : 0u;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // b128: 1 = DeepSeek-style blockwise FP8 (128-value blocks, power-of-two
 // scales, linear scale layouts), 2 = the same with binary32 scales (scales
