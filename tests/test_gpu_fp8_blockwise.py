@@ -258,3 +258,31 @@ def test_f32_scales_exact_block_scaling(M, N, K, tile_b):
     b64 = OB.dequantize_f32s_f64(F.encode_e4m3_rne(bv), sb, "128x128" if tile_b else "1x128")
     out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
     assert np.array_equal(out, F.bf16_rne(a64 @ b64.T))
+
+
+def test_f32_scales_strided_buffers():
+    """Binary32-scale quantizer on a column slice of a wider BF16 tensor,
+    writing into a wider code buffer; the GEMM reading row-padded operands and
+    writing a column slice of a wider output (ld > cols everywhere)."""
+    import torch
+    m = mxq()
+    rs = np.random.default_rng(79)
+    R, C, W = 256, 384, 640
+    full = F.bf16_rne(rs.standard_normal((R, W)) * 3)
+    xd = to_dev_bf16(full)[:, 128:128 + C]
+    say("fp8bw f32 strided 256x384 (ld 640) into ld 512, GEMM into a slice of ld 700")
+    codes = torch.zeros((R, 512), dtype=torch.uint8, device="cuda")[:, :C]
+    c, s = m.fp8bw_quantize_f32(xd, codes=codes)
+    rc, rsc = OB.quantize_rows_f32(F.bf16_bits_to_f64(full[:, 128:128 + C]))
+    assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(s).view(np.uint32), rsc.view(np.uint32))
+    wv = F.bf16_rne(rs.standard_normal((256, C)) * 0.05)
+    cw, sw = m.fp8bw_quantize_f32(to_dev_bf16(wv), block=m.Block.TILE)
+    out = torch.zeros((R, 700), dtype=torch.bfloat16, device="cuda")
+    view = out[:, 40:40 + 256]
+    m.mx_gemm(_opf(m, c, s), _opf(m, cw, sw, tile=True), R, 256, C, out=view)
+    got = from_dev_bf16(view.contiguous())
+    _check(view.contiguous(), OB.dequantize_f32s_f64(rc, rsc),
+           OB.dequantize_f32s_f64(*OB.quantize_tile_f32(F.bf16_bits_to_f64(wv)), "128x128"))
+    rest = from_dev_bf16(out)
+    assert np.all(rest[:, :40] == 0) and np.all(rest[:, 296:] == 0)      # nothing outside the slice
+    assert got.shape == (R, 256)
