@@ -236,13 +236,15 @@ def test_f32_scales_fprop_dgrad_wgrad():
 
 
 @pytest.mark.parametrize("M,N,K,tile_b", [(384, 256, 1024, True), (600, 416, 384, False),
-                                          (130, 1, 128, False), (1, 128, 256, True)])
+                                          (130, 1, 128, False), (1, 128, 256, True),
+                                          (4100, 2048, 256, True), (4096, 2050, 128, False)])
 def test_f32_scales_exact_block_scaling(M, N, K, tile_b):
     """Small-integer codes with scales from {0.5, 0.75, 1, 1.25, 1.5, 2}
     per (row, K block) and per (tile, K block): every partial sum, scale
     product and accumulation is exact in binary32, so C equals the BF16
     rounding of the exact result: a wrong block index anywhere shows.
-    Ragged M and N run through the tails of the tiles."""
+    Ragged M and N run through the tails of the tiles; the last two shapes
+    take several rounds of tiles over the CUs."""
     import torch
     m = mxq()
     rs = np.random.default_rng(78 + M)
