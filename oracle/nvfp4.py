@@ -19,7 +19,9 @@ Readings taken where the pages are silent (listed in the design notes):
    s_b = RNE-saturating E4M3 of t (s_b = 0 when S = 0).
 3. If s_b = 0 the block's codes are signed zeros.  Otherwise
    r = fl(1 / fl(s_b * S)), y = fl(x * r), code = RNE (or SR) E2M1 of y,
-   saturating at 6.
+   saturating at 6.  For S < 2^-64 the same steps run in a frame scaled by
+   2^64 (x and S times 2^64, both exact), which keeps s_b * S a binary32
+   normal for every finite BF16 input; see encode_block_elements.
 4. Packing: element 2j in the low nibble, 2j+1 in the high nibble.
 5. SR draws come from Philox4x32-10 (see philox.py), 16 bits per element,
    counter from the element's index in the logical input.
@@ -63,14 +65,32 @@ def block_scale(a_b, S):
     return encode_e4m3_rne(t.astype(np.float64))
 
 
+TINY_S = np.float32(2.0 ** -64)        # below it, the reciprocal is taken in a scaled frame
+FRAME = np.float32(2.0 ** 64)
+
+
 def encode_block_elements(x, sb_code, S, rnd="rne", r16=None):
-    """Element codes of blocks: x [..., 16] float64, sb_code/S broadcast [..., 1]."""
+    """Element codes of blocks: x [..., 16] float64, sb_code/S broadcast [..., 1].
+
+    y = fl(x * fl(1 / fl(s_b * S))), then RNE (or SR) onto E2M1.  When S is
+    below 2^-64 the product s_b * S can fall below binary32's normal range (its
+    reciprocal then loses bits or overflows to infinity, and 0 * inf would be
+    NaN), so the chain is taken in a frame scaled by the exact power of two
+    2^64: y = fl(fl(x * 2^64) * fl(1 / fl(s_b * fl(S * 2^64)))).  Wherever
+    s_b * S is a binary32 normal both forms give the same y (every scaling by
+    2^64 is exact there), so this only changes blocks whose s_b * S is
+    subnormal.  (x * 2^64 exceeds the binary32 range only for |x| >= 2^64
+    under a caller-given S < 2^-64; the infinite y then saturates at 6, as
+    the exact quotient would.)"""
     sb = e4m3_value(sb_code).astype(F32)
     S = np.asarray(S, dtype=F32)
+    frame = np.where(S < TINY_S, FRAME, F32(1.0)).astype(F32)
     with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
-        denom = (sb * S).astype(F32)
+        xf = (x.astype(F32) * frame).astype(F32)
+        Sf = (S * frame).astype(F32)
+        denom = (sb * Sf).astype(F32)
         r = (F32(1.0) / denom).astype(F32)
-        y = (x.astype(F32) * r).astype(F32)
+        y = (xf * r).astype(F32)
     zero_block = (sb == 0) | (S == 0)
     y = np.where(zero_block, np.copysign(F32(0.0), x.astype(F32)), y)
     if rnd == "rne":

@@ -125,12 +125,23 @@ def test_grouped_gemm_matches_per_row():
 
 
 def test_swiglu_reference():
-    gu = F.bf16_rne(np.array([[0.0, 1.0, -2.0, 3.0, 2.0, -1.0, 0.5, 4.0]]))
-    h = F.bf16_bits_to_f64(moe.swiglu_f64(gu, 4))
-    g = np.array([0.0, 1.0, -2.0, 3.0])
-    u = np.array([2.0, -1.0, 0.5, 4.0])
-    want = g * u / (1 + np.exp(-g))
-    assert np.allclose(h, want, rtol=2 ** -8)
+    """SwiGLU h = silu(g) * u with the gate in the first half of the row.
+    Pinned to textbook values of the logistic function sigma(x) = 1 / (1 +
+    e^-x) (sigma(1) = 0.7310585786300049, sigma(2) = 0.8807970779778823,
+    sigma(3) = 0.9525741268224334), so silu(g) * u = g * sigma(g) * u is known
+    without evaluating exp: a swapped gate/up, a flipped exponent sign or a
+    missing factor changes the BF16 result."""
+    s1, s2, s3 = 0.7310585786300049, 0.8807970779778823, 0.9525741268224334
+    #       g:   1,    -2,   3,   0,   2     u:  -1,  0.5,  4,   2,  1
+    gu = F.bf16_rne(np.array([[1.0, -2.0, 3.0, 0.0, 2.0, -1.0, 0.5, 4.0, 2.0, 1.0]]))
+    want = np.array([[1.0 * s1 * -1.0,              # -0.7310585786...
+                      -2.0 * (1.0 - s2) * 0.5,      # -0.1192029220...
+                      3.0 * s3 * 4.0,               # 11.430889521...
+                      0.0,
+                      2.0 * s2 * 1.0]])             # 1.7615941559...
+    assert np.array_equal(moe.swiglu_f64(gu, 5), F.bf16_rne(want))
+    # the BF16 codes themselves, for the first three
+    assert [int(v) for v in moe.swiglu_f64(gu, 5)[0, :3]] == [0xBF3B, 0xBDF4, 0x4137]
 
 
 def test_mfma_layout_is_a_permutation_and_round_trips():

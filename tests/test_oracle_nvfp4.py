@@ -209,3 +209,102 @@ def test_dequantize_f32_product_is_exact():
     assert np.array_equal(v.astype(np.float32).astype(np.float64), v)   # c * s_b exact in binary32
     d32 = N.dequantize_f32(c, s, S, "1x16", "per_row")
     assert np.array_equal(d32, (v.astype(np.float32) * S.reshape(-1, 1)).astype(np.float32))
+
+
+# ---------------------------------------------------------------- tiny scales
+# For S < 2^-64 the element chain runs in a frame scaled by 2^64 (s_b * S can
+# be subnormal there, and its reciprocal would lose bits or overflow).  Pinned
+# by what holds without looking at the frame: a power-of-two scaling of the
+# whole input moves S and nothing else (the two-level scale absorbs it), the
+# dequantized values stay within half an E2M1 step (in units of s_b * S) of x,
+# and zeros stay signed zeros.
+
+def _tiny_rows(seed, rows, cols, log2_amax):
+    """Rows whose amax is 2^log2_amax[r] and whose nonzero entries lie within
+    2^6 of it (so that a further scaling by 2^-60 stays BF16-normal)."""
+    rs = np.random.default_rng(seed)
+    mant = rs.uniform(1.0, 2.0, (rows, cols)) * rs.choice([-1.0, 1.0], (rows, cols))
+    expo = rs.integers(-6, 0, (rows, cols))
+    x = mant * np.exp2(expo) * np.exp2(np.asarray(log2_amax, dtype=np.float64))[:, None]
+    x[rs.random((rows, cols)) < 0.05] = 0.0
+    return F.bf16_bits_to_f64(F.bf16_rne(x))
+
+
+def test_power_of_two_scaling_moves_only_the_second_scale():
+    """Q(x * 2^-60) == Q(x) in codes and block scales, S scaled by 2^-60, for
+    rows whose S crosses from above 2^-64 to below it; per-row and per-tensor,
+    1x16, 16x1 and 16x16, RNE and SR."""
+    x = _tiny_rows(20, 16, 64, np.linspace(-50, -40, 16))
+    xs = x * 2.0 ** -60
+    assert np.array_equal(F.bf16_bits_to_f64(F.bf16_rne(xs)), xs)       # the scaling is exact
+    for rnd in ("rne", "sr"):
+        c0, s0, S0 = N.quantize_rowwise(x, "per_row", rnd=rnd, seed=3)
+        c1, s1, S1 = N.quantize_rowwise(xs, "per_row", rnd=rnd, seed=3)
+        assert np.all(S0 >= N.TINY_S) and np.all(S1 < N.TINY_S)
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+        assert np.array_equal(S1, (S0 * np.float32(2.0 ** -60)).astype(np.float32))
+        for q in (N.quantize_colwise, N.quantize_tile16):
+            c0, s0, S0 = q(x, "per_tensor", rnd=rnd, seed=3)
+            c1, s1, S1 = q(xs, "per_tensor", rnd=rnd, seed=3)
+            assert S1[0] < N.TINY_S <= S0[0]
+            assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
+# largest half gap between an E2M1 magnitude and its grid neighbours
+_HALF_GAP = {0.0: 0.25, 0.5: 0.25, 1.0: 0.25, 1.5: 0.25, 2.0: 0.5, 3.0: 0.5, 4.0: 1.0, 6.0: 1.0}
+
+
+def test_tiny_rows_dequantize_within_half_a_step():
+    """Rows with amax from about 2^-113 (S still a binary32 normal) to 2^-64 and
+    blocks down to 2^-24 below their row's amax (so that s_b * S is
+    subnormal): |DQ(Q(x)) - x| <= s_b S (half gap + 2^-18) element by element
+    wherever |x| <= 7 s_b S (RNE onto the grid), code 6 beyond (saturation),
+    zeros encode as signed zeros, and some blocks do take the scaled frame
+    with a subnormal s_b * S."""
+    rs = np.random.default_rng(21)
+    rows, cols = 32, 128
+    amax = np.linspace(-112, -65, rows)
+    x = _tiny_rows(22, rows, cols, amax)
+    # spread the blocks of each row over 24 binades below the row's amax
+    shrink = np.exp2(-rs.integers(0, 24, (rows, cols // 16))).repeat(16, axis=1)
+    shrink[:, 0] = 1.0
+    x = F.bf16_bits_to_f64(F.bf16_rne(x * shrink))
+    x[:, 5] = -0.0
+    codes, sb, S = N.quantize_rowwise(x, "per_row")
+    assert np.all((S > 0) & (S < N.TINY_S)) and np.all(S >= np.float32(2.0 ** -126))
+    den = F.e4m3_value(sb).astype(np.float32) * np.repeat(S[:, None], cols // 16, axis=1)
+    assert np.any((den > 0) & (den < np.float32(2.0 ** -126)))               # subnormal s_b * S occurs
+    c = N.unpack_nibbles(codes)
+    v = F.e2m1_value(c)
+    unit = np.repeat(F.e4m3_value(sb), 16, axis=1) * S[:, None].astype(np.float64)
+    dq = N.dequantize_f64(codes, sb, S, "1x16", "per_row")
+    gap = np.vectorize(lambda a: _HALF_GAP[abs(a)])(v)
+    live = np.repeat(sb != 0, 16, axis=1)
+    assert live.mean() > 0.5
+    # past 7 steps the code saturates at 6; that happens only under an E4M3
+    # subnormal block scale, whose rounding can leave a_b / (s_b S) well above 6
+    over = live & (np.abs(x) > 7.0 * unit)
+    assert np.all(np.abs(v[over]) == 6.0) and np.all(np.signbit(v[over]) == np.signbit(x[over]))
+    assert np.all(np.repeat(F.e4m3_value(sb), 16, axis=1)[over] < 2.0 ** -6)
+    ok = live & ~over
+    assert np.all(np.abs(dq - x)[ok] <= (unit * (gap + 2.0 ** -18))[ok])
+    # a block whose scale rounds to zero has t = a_b / (6 S) <= 2^-10
+    Sx = np.repeat(S[:, None].astype(np.float64), cols, axis=1)
+    assert np.all(np.abs(x[~live]) <= 6.0 * Sx[~live] * 2.0 ** -10 * (1 + 2.0 ** -20))
+    zero = x == 0
+    assert np.array_equal(c[zero] & 7, np.zeros(zero.sum(), dtype=c.dtype))
+    assert np.array_equal((c[zero] >> 3) & 1, np.signbit(x[zero]).astype(c.dtype))
+
+
+def test_smallest_row_of_the_advisor_case():
+    """The row [2^-126, 2^-128, 0 x 14]: S = fl(2^-126 / 2688) is subnormal
+    and s_b * S = 448 S is below 2^-128, so an unscaled reciprocal is
+    infinite.  The block max encodes as 6 under s_b = 448, 2^-128 as 1.5, and
+    the zeros as zeros."""
+    x = np.zeros((1, 16))
+    x[0, 0], x[0, 1] = 2.0 ** -126, 2.0 ** -128
+    codes, sb, S = N.quantize_rowwise(x, "per_row")
+    assert S[0] < np.float32(2.0 ** -126)                                   # subnormal
+    assert int(sb[0, 0]) == 0x7E
+    c = N.unpack_nibbles(codes)[0]
+    assert c[0] == 7 and c[1] == 3 and np.all(c[2:] == 0)
