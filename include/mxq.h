@@ -126,6 +126,14 @@ typedef enum {
 /*
  * mx_quantize -- MXFP8 quantization of a BF16 matrix x [rows, cols].
  *
+ * Format: 32 E4M3 values share one E8M0 scale ("Miles Blackwell RL Troca a
+ * Uniformidade BF16 por MXFP8 e NVFP4 Nativos", section "O Suporte Miles
+ * Blackwell Agora Abrange Todo o Loop de RL"; "End-to-End MXFP8 Reinforcement
+ * Learning on Blackwell", Table 10 F6: the scale keeps only an exponent).
+ * Rowwise and columnwise copies are both made from the original values
+ * (Miles page, section "Um Quantizador Compartilhado É o Verdadeiro
+ * Mecanismo"), which is what DUAL does from one read.
+ *
  * Block rule (the pages give none; this is the plainest reading of "no block
  * overflows after scaling"): the block's E8M0 exponent e is the smallest
  * integer in [-127, 127] with max|x| <= 448 * 2^e (all-zero block: e = -127,
@@ -160,6 +168,16 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
 /*
  * nvfp4_quantize -- NVFP4 quantization of a BF16 matrix x [rows, cols].
  *
+ * Format and recipe: 16 E2M1 values share an E4M3 block scale under a second
+ * FP32 scale computed online per token, and one fused op yields packed FP4,
+ * block scales and token scales ("Miles Blackwell RL ...", sections "O
+ * Suporte Miles Blackwell Agora Abrange Todo o Loop de RL" and "Um
+ * Quantizador Compartilhado É o Verdadeiro Mecanismo"); per-tensor second
+ * scales, 16x16 weight blocks, 1x16 activation and gradient blocks, RNE for
+ * weights and activations and stochastic rounding for gradients ("Train
+ * models faster with JAX and MaxText using NVFP4 on NVIDIA Blackwell",
+ * section "NVFP4 pretraining recipe").
+ *
  * Steps, each fl() one binary32 IEEE operation (round-to-nearest-even,
  * subnormals kept, no fused multiply-add):
  *   S   = fl(A / 2688), A = max|x| over the row (PER_ROW) or tensor
@@ -190,7 +208,10 @@ mxq_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
  * Shapes: cols % 16 == 0 (ROW); rows % 16 == 0 and cols % 16 == 0 (COL,
  * TILE).  Alignment: x, codes 16-byte aligned, ld_x*2 and ld_codes_bytes
  * multiples of 16; gscales 4-byte aligned.
- * Precondition for exactness: a nonzero row/tensor has A >= 2^-64.
+ * When S < 2^-64 the element step is taken with x and S scaled by 2^64
+ * (exact): code = E2M1 of fl(fl(x*2^64) * fl(1 / fl(s_b*fl(S*2^64)))), which
+ * equals the unscaled step wherever s_b*S is a binary32 normal and keeps it
+ * finite for every finite BF16 input.
  */
 mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                           mxq_block block, mxq_gscale gs, mxq_round rnd,
@@ -302,8 +323,9 @@ mxq_status fp8bw_quantize_f32(const uint16_t* x, int64_t rows, int64_t cols, int
                               void* stream);
 
 /*
- * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16 (the operand of the
- * dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
+ * mx_dequantize -- DQ(Q(x)) of one stored copy to BF16, the operand of the
+ * dequantized backward, whose BF16 GEMMs read DQ(Q(w)) ("NVFP4 RL training" /
+ * "The 4-bitter Lesson", section on the dequantized backward).  (rows, cols) is the shape of the STORED copy (for a
  * COL copy that is [input cols, input rows]); block says how its scales are
  * laid out (ROW for a COL copy too, since the stored copy is row-blocked).
  *   MXFP8, FP8_B128: bf16_RNE(value(c) * 2^e)  (exact unless beyond the BF16 range)
@@ -351,7 +373,16 @@ typedef struct {
 } mxq_operand;
 
 /*
- * mx_gemm -- C[M, N] = sum_k A[m, k] * B[n, k], FP32 accumulation, BF16 out.
+ * mx_gemm -- C[M, N] = sum_k A[m, k] * B[n, k], FP32 accumulation, BF16 out:
+ * the FPROP, DGRAD and WGRAD GEMMs of a linear layer on its quantized
+ * operands, with BF16 outputs ("Train models faster with JAX and MaxText
+ * using NVFP4 on NVIDIA Blackwell", section "NVFP4 pretraining recipe"; MXFP8
+ * on every GEMM: "Miles Blackwell RL ...", section "O Suporte Miles Blackwell
+ * Agora Abrange Todo o Loop de RL"), dense or grouped per MoE expert with the
+ * routed rows gathered ("Miles Blackwell RL ...", same section: the routed
+ * experts run in NVFP4).  a_rows extends the call beyond the four-argument
+ * shape (M, N, K): with a gather index the rows of A are not the rows of C,
+ * so the library needs A's own row count to bound its loads.
  *   FPROP  Y  = X  * W^T : A = rowwise X,  B = W (rowwise or tile)
  *   DGRAD  dX = dY * W   : A = rowwise dY, B = W tile copy with transposed=1
  *   WGRAD  dW = dY^T * X : A = columnwise dY copy, B = columnwise X copy
@@ -382,8 +413,11 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b,
                    const int32_t* a_row_index, void* stream);
 
 /*
- * mx_gemm_set_tile -- force the workgroup tile of every later mx_gemm call in
- * the process (a tuning and test aid; the default is the measured choice).
+ * mx_gemm_set_tile -- force the workgroup tile of the later mx_gemm and
+ * mx_gemm_swiglu calls made FROM THE CALLING HOST THREAD (a tuning and test
+ * aid; the default is the measured choice).  The setting is thread-local, the
+ * one piece of state the library keeps besides the thread-local error text;
+ * other threads are unaffected.
  *   tile  -1  the measured choice per path and shape (default)
  *          0  128x128, 4 waves (2x2), two staging sets
  *          1  128x128, 8 waves (2x4), two staging sets
@@ -394,8 +428,8 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b,
  *          6  256x256, 8 waves in two ping-pong groups
  * Every configuration computes the same result bit for bit (the K order of
  * the accumulation does not depend on the tile).  Returns MXQ_EINVAL outside
- * [-1, 6].  Not synchronised with launches already queued: it applies to
- * calls made after it returns.
+ * [-1, 6].  It applies to calls made after it returns; launches already
+ * queued keep their tile.
  */
 mxq_status mx_gemm_set_tile(int32_t tile);
 

@@ -331,11 +331,49 @@ class Operand:
                         1 if self.transposed else 0)
 
 
+def _check_gemm_args(a, b, M, ncols, out, group_row_offsets, a_row_index, num_groups_expected=None):
+    """Host-side checks of what the library reads on the device without
+    validating: the group offsets, the gather index, the output and the
+    second-scale tensors (the C ABI checks formats, shapes and alignment)."""
+    for name, op in (("a", a), ("b", b)):
+        if not isinstance(op, Operand):
+            raise TypeError(f"{name} must be an Operand")
+        if not (isinstance(op.data, torch.Tensor) and op.data.is_cuda):
+            raise TypeError(f"{name}.data must be a CUDA tensor")
+        if op.gscales is not None and (op.gscales.dtype != torch.float32 or not op.gscales.is_cuda
+                                       or not op.gscales.is_contiguous()):
+            raise TypeError(f"{name}.gscales must be a contiguous float32 CUDA tensor")
+    if not (isinstance(out, torch.Tensor) and out.is_cuda and out.dtype == torch.bfloat16 and out.dim() == 2):
+        raise TypeError("out must be a 2-D bfloat16 CUDA tensor")
+    if out.shape[0] < M or out.shape[1] < ncols or out.stride(1) != 1:
+        raise ValueError(f"out must hold [{M}, {ncols}] with unit column stride, got {tuple(out.shape)} "
+                         f"strides {out.stride()}")
+    if group_row_offsets is not None:
+        g = group_row_offsets
+        if not (isinstance(g, torch.Tensor) and g.is_cuda and g.dtype == torch.int32 and g.dim() == 1
+                and g.is_contiguous()):
+            raise TypeError("group_row_offsets must be a contiguous 1-D int32 CUDA tensor")
+        if g.numel() < 2:
+            raise ValueError("group_row_offsets needs num_groups + 1 >= 2 entries")
+        if b.gscales is not None and b.gscales.numel() < g.numel() - 1:
+            raise ValueError("b.gscales needs one scale per group")
+    if a_row_index is not None:
+        i = a_row_index
+        if not (isinstance(i, torch.Tensor) and i.is_cuda and i.dtype == torch.int32 and i.dim() == 1
+                and i.is_contiguous()):
+            raise TypeError("a_row_index must be a contiguous 1-D int32 CUDA tensor")
+        if i.numel() != M:
+            raise ValueError(f"a_row_index must have M = {M} entries, got {i.numel()}")
+
+
 def mx_gemm(a, b, M, N, K, out=None, group_row_offsets=None, a_row_index=None, a_rows=None,
             stream=None):
-    """C[M, N] = sum_k A[m, k] B[n, k] in BF16 (FP32 accumulation)."""
+    """C[M, N] = sum_k A[m, k] B[n, k] in BF16 (FP32 accumulation).  Grouped
+    (MoE) launches take int32 group_row_offsets [num_groups + 1] and an
+    optional int32 gather index a_row_index [M] into the a_rows rows of A."""
     dev = a.data.device
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check_gemm_args(a, b, M, N, out, group_row_offsets, a_row_index)
     ng = 0 if group_row_offsets is None else group_row_offsets.numel() - 1
     if a_rows is None:
         a_rows = M
@@ -352,6 +390,7 @@ def mx_gemm_swiglu(a, b, M, inter, K, out=None, group_row_offsets=None, a_row_in
     rows), fused into the GEMM's epilogue; NVFP4 operands."""
     dev = a.data.device
     out = torch.empty((M, inter), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check_gemm_args(a, b, M, inter, out, group_row_offsets, a_row_index)
     ng = 0 if group_row_offsets is None else group_row_offsets.numel() - 1
     if a_rows is None:
         a_rows = M

@@ -1201,10 +1201,11 @@ static int64_t tile_count(const GemmArgs& a, int bm, int bn) {
 }
 
 // Forced tile configuration (the case numbers of launch_p), or -1 for the
-// measured choice.  Process-wide; set through mx_gemm_set_tile.
-static std::atomic<int> g_tile_override{-1};
+// measured choice.  Per host thread (set through mx_gemm_set_tile), so a
+// tuning thread never changes the tiles of another thread's calls.
+static thread_local int g_tile_override = -1;
 
-void gemm_set_tile(int tile) { g_tile_override.store(tile, std::memory_order_relaxed); }
+void gemm_set_tile(int tile) { g_tile_override = tile; }
 
 // Tile choice: the largest tile that still gives every CU work.  Larger wave
 // tiles need fewer LDS fragment bytes per MFMA; 8-wave workgroups put two
@@ -1212,7 +1213,7 @@ void gemm_set_tile(int tile) { g_tile_override.store(tile, std::memory_order_rel
 template <int PATH, bool BT, bool SWI = false>
 static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
   const int64_t cus = 256;
-  int t = g_tile_override.load(std::memory_order_relaxed);
+  int t = g_tile_override;
   if (t < 0) {
     // measured on MI355X (8192^3, 8192x24576x4096, 8192x28672x4096,
     // 8192x1536x2048, 4096x768x2048, 4096x2048x768, grouped 128 x 512 rows):

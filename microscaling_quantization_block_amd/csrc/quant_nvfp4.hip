@@ -16,6 +16,13 @@
 //   s_b = E4M3_RNE(a_b / (6 * S))  (0 when S == 0)
 //   r   = 1 / (s_b * S)            (once per block)
 //   q   = E2M1(x * r)              (RNE, or SR with a Philox4x32-10 draw)
+// When S < 2^-64, s_b * S can fall below the binary32 normal range (its
+// reciprocal would lose bits or overflow, and a zero times infinity is NaN),
+// so r and q are taken in a frame scaled by 2^64: r = 1 / (s_b * (S * 2^64)),
+// q = E2M1((x * 2^64) * r).  Every scaling by 2^64 is exact, so wherever
+// s_b * S is normal this gives the unscaled result.  S is uniform across a
+// wave (one wave per token, or one S per tensor), so the kernels branch on it
+// once and the common path pays nothing.
 // Divisions are the correctly rounded IEEE ones (the build keeps HIP's
 // correctly rounded fp32 division and sqrt).
 //
@@ -37,11 +44,17 @@
 #include "mxq_device.h"
 #include "mxq_kernels.h"
 
+#include <type_traits>
+
 namespace mxq {
 
 // Block scale and per-block reciprocal from the block amax (binary32 bits of
-// a BF16 magnitude widened) and S.
+// a BF16 magnitude widened) and S.  r is the reciprocal in the frame of S:
+// scaled by 2^-64 when S < 2^-64 (TINY_S), where the encoders scale x by 2^64.
 struct BlockScale { uint32_t code; float r; };
+
+constexpr float TINY_S = 0x1p-64f;
+constexpr float FRAME = 0x1p64f;
 
 // m = 6 maps the block max onto the largest E2M1 value (plain NVFP4); m = 4
 // is Four-Over-Six's second candidate.
@@ -56,10 +69,15 @@ __device__ __forceinline__ BlockScale nv_block_scale(float a_b, float S, float m
   t = t < 448.0f ? t : 448.0f;
   bs.code = f32x2_to_e4m3(t, 0.0f) & 0xFFu;
   float sb = e4m3_to_f32(bs.code);
-  float den = sb * S;
+  const float Sf = S < TINY_S ? S * FRAME : S;   // exact
+  float den = sb * Sf;
   bs.r = bs.code ? 1.0f / den : 0.0f;
   return bs;
 }
+
+// x in the frame of S (TINY: S < 2^-64, x times 2^64, exact).
+template <bool TINY>
+__device__ __forceinline__ float nv_frame(float x) { return TINY ? x * FRAME : x; }
 
 // Encode the 8 BF16 values of one chunk with reciprocal r; returns 8 nibbles
 // (element 2j in the low nibble of byte j).  zero_block forces signed zeros.
@@ -77,15 +95,15 @@ __device__ __forceinline__ uint32_t e2m1_rne_pair(uint32_t old, float a, float b
 
 // A block whose scale code is 0 has r = 0, and x * 0 is the signed zero of
 // the (finite) input, so zero blocks need no separate path.
-template <bool SR>
+template <bool SR, bool TINY = false>
 __device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, u32x4 draws) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t d[4] = {draws.x, draws.y, draws.z, draws.w};
   float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    y[2 * i] = bf16_lo(w[i]) * r;
-    y[2 * i + 1] = bf16_hi(w[i]) * r;
+    y[2 * i] = nv_frame<TINY>(bf16_lo(w[i])) * r;
+    y[2 * i + 1] = nv_frame<TINY>(bf16_hi(w[i])) * r;
   }
   if (SR) {
     uint32_t out = 0;
@@ -103,6 +121,14 @@ __device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, u32x4 draws) {
   out = e2m1_rne_pair<2>(out, y[4], y[5]);
   out = e2m1_rne_pair<3>(out, y[6], y[7]);
   return out;
+}
+
+// Calls f(std::true_type) when S is below 2^-64 (the scaled frame), else
+// f(std::false_type).  S is wave-uniform at every call site.
+template <class F>
+__device__ __forceinline__ void with_frame(float S, F&& f) {
+  if (S < TINY_S) f(std::true_type{});
+  else f(std::false_type{});
 }
 
 // Max |x| of 8 BF16 values as the binary32 bit pattern of the magnitude
@@ -145,20 +171,22 @@ __device__ __forceinline__ float nv_sse8(uint4 v, uint32_t q, float sb, float S)
 
 // One candidate's codes for a chunk of 8 values and the chunk's error sum.
 struct Cand8 { uint32_t q; float e; };
+template <bool TINY>
 __device__ __forceinline__ Cand8 nv_cand8(uint4 v, const BlockScale& bs, float S) {
   const u32x4 none = {0, 0, 0, 0};
   Cand8 c;
-  c.q = nv_encode8<false>(v, bs.r, none);
+  c.q = nv_encode8<false, TINY>(v, bs.r, none);
   c.e = nv_sse8(v, c.q, e4m3_to_f32(bs.code), S);
   return c;
 }
 
 // A whole 16-value block held by one lane: the chosen scale code and codes.
 struct Enc16 { uint32_t code, q0, q1; };
+template <bool TINY>
 __device__ __forceinline__ Enc16 nv_encode16_46(uint4 v0, uint4 v1, float a_b, float S) {
   const BlockScale b6 = nv_block_scale(a_b, S, 6.0f), b4 = nv_block_scale(a_b, S, 4.0f);
-  const Cand8 x60 = nv_cand8(v0, b6, S), x61 = nv_cand8(v1, b6, S);
-  const Cand8 x40 = nv_cand8(v0, b4, S), x41 = nv_cand8(v1, b4, S);
+  const Cand8 x60 = nv_cand8<TINY>(v0, b6, S), x61 = nv_cand8<TINY>(v1, b6, S);
+  const Cand8 x40 = nv_cand8<TINY>(v0, b4, S), x41 = nv_cand8<TINY>(v1, b4, S);
   const float e6 = x60.e + x61.e, e4 = x40.e + x41.e;
   if (e4 < e6) return Enc16{b4.code, x40.q, x41.q};
   return Enc16{b6.code, x60.q, x61.q};
@@ -225,32 +253,35 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
       S = __uint_as_float(wave_max_u32(mb)) / 2688.0f;
       if (lane == 0) gscales[r] = S;
     }
+    with_frame(S, [&](auto tiny) {
+      constexpr bool TINY = decltype(tiny)::value;
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int64_t b = lane + 64 * k;
-      if (FULL || b < bpr) {
-        uint32_t q0, q1, code;
-        if (RM == 2) {
-          const Enc16 e = nv_encode16_46(v[k][0], v[k][1], __uint_as_float(ab[k]), S);
-          q0 = e.q0;
-          q1 = e.q1;
-          code = e.code;
-        } else {
-          const BlockScale bs = nv_block_scale(__uint_as_float(ab[k]), S);
-          u32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
-          if (SR) {
-            const uint64_t n = (uint64_t)(r * cols + b * 16) >> 3;
-            d0 = philox_draws8(n, seed, stream_id, tensor_tag);
-            d1 = philox_draws8(n + 1, seed, stream_id, tensor_tag);
+      for (int k = 0; k < BPT; ++k) {
+        const int64_t b = lane + 64 * k;
+        if (FULL || b < bpr) {
+          uint32_t q0, q1, code;
+          if (RM == 2) {
+            const Enc16 e = nv_encode16_46<TINY>(v[k][0], v[k][1], __uint_as_float(ab[k]), S);
+            q0 = e.q0;
+            q1 = e.q1;
+            code = e.code;
+          } else {
+            const BlockScale bs = nv_block_scale(__uint_as_float(ab[k]), S);
+            u32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+            if (SR) {
+              const uint64_t n = (uint64_t)(r * cols + b * 16) >> 3;
+              d0 = philox_draws8(n, seed, stream_id, tensor_tag);
+              d1 = philox_draws8(n + 1, seed, stream_id, tensor_tag);
+            }
+            q0 = nv_encode8<SR, TINY>(v[k][0], bs.r, d0);
+            q1 = nv_encode8<SR, TINY>(v[k][1], bs.r, d1);
+            code = bs.code;
           }
-          q0 = nv_encode8<SR>(v[k][0], bs.r, d0);
-          q1 = nv_encode8<SR>(v[k][1], bs.r, d1);
-          code = bs.code;
+          *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = make_uint2(q0, q1);
+          bscales[scale_offset(r, b, bpr, mfma_layout)] = (uint8_t)code;
         }
-        *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = make_uint2(q0, q1);
-        bscales[scale_offset(r, b, bpr, mfma_layout)] = (uint8_t)code;
       }
-    }
+    });
   };
   uint4 va[BPT][2], vb[BPT][2];
   load(row, va);
@@ -300,23 +331,26 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     uint32_t ab = amax8_bits(v);
     float a = __uint_as_float(umax(ab, lane_xor_u32(ab, 1)));
     uint32_t q, code;
-    if (RM == 2) {
-      // the block's two halves sit in lanes c and c ^ 1: the tree's last
-      // level adds their half sums (the same in both lanes)
-      const BlockScale b6 = nv_block_scale(a, S, 6.0f), b4 = nv_block_scale(a, S, 4.0f);
-      const Cand8 x6 = nv_cand8(v, b6, S), x4 = nv_cand8(v, b4, S);
-      const float e6 = x6.e + __uint_as_float(lane_xor_u32(__float_as_uint(x6.e), 1));
-      const float e4 = x4.e + __uint_as_float(lane_xor_u32(__float_as_uint(x4.e), 1));
-      const bool take4 = e4 < e6;
-      q = take4 ? x4.q : x6.q;
-      code = take4 ? b4.code : b6.code;
-    } else {
-      const BlockScale bs = nv_block_scale(a, S);
-      u32x4 dr = {0, 0, 0, 0};
-      if (SR && c < cpr) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
-      q = nv_encode8<SR>(v, bs.r, dr);
-      code = bs.code;
-    }
+    with_frame(S, [&](auto tiny) {
+      constexpr bool TINY = decltype(tiny)::value;
+      if (RM == 2) {
+        // the block's two halves sit in lanes c and c ^ 1: the tree's last
+        // level adds their half sums (the same in both lanes)
+        const BlockScale b6 = nv_block_scale(a, S, 6.0f), b4 = nv_block_scale(a, S, 4.0f);
+        const Cand8 x6 = nv_cand8<TINY>(v, b6, S), x4 = nv_cand8<TINY>(v, b4, S);
+        const float e6 = x6.e + __uint_as_float(lane_xor_u32(__float_as_uint(x6.e), 1));
+        const float e4 = x4.e + __uint_as_float(lane_xor_u32(__float_as_uint(x4.e), 1));
+        const bool take4 = e4 < e6;
+        q = take4 ? x4.q : x6.q;
+        code = take4 ? b4.code : b6.code;
+      } else {
+        const BlockScale bs = nv_block_scale(a, S);
+        u32x4 dr = {0, 0, 0, 0};
+        if (SR && c < cpr) dr = philox_draws8((uint64_t)(row * cols + c * 8) >> 3, seed, stream_id, tensor_tag);
+        q = nv_encode8<SR, TINY>(v, bs.r, dr);
+        code = bs.code;
+      }
+    });
     if (c < cpr) {
       *reinterpret_cast<uint32_t*>(codes + row * ld_codes + c * 4) = q;
       if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)code;
@@ -380,13 +414,21 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     const BlockScale b4 = nv_block_scale(__uint_as_float(mb), S, 4.0f);
     uint32_t q6[4], q4[4];
     float r6[4], r4[4];
+    with_frame(S, [&](auto tiny) {
+      constexpr bool TINY = decltype(tiny)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const Cand8 c6 = nv_cand8<TINY>(v[i], b6, S), c4 = nv_cand8<TINY>(v[i], b4, S);
+        q6[i] = c6.q;
+        q4[i] = c4.q;
+        r6[i] = c6.e;
+        r4[i] = c4.e;
+      }
+    });
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const Cand8 c6 = nv_cand8(v[i], b6, S), c4 = nv_cand8(v[i], b4, S);
-      q6[i] = c6.q;
-      q4[i] = c4.q;
-      r6[i] = c6.e + __uint_as_float(lane_xor_u32(__float_as_uint(c6.e), 1));
-      r4[i] = c4.e + __uint_as_float(lane_xor_u32(__float_as_uint(c4.e), 1));
+      r6[i] = r6[i] + __uint_as_float(lane_xor_u32(__float_as_uint(r6[i]), 1));
+      r4[i] = r4[i] + __uint_as_float(lane_xor_u32(__float_as_uint(r4[i]), 1));
     }
     float e6 = (r6[0] + r6[1]) + (r6[2] + r6[3]);
     float e4 = (r4[0] + r4[1]) + (r4[2] + r4[3]);
@@ -410,15 +452,18 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
   if (!valid) return;
   const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
   const float sbc = e4m3_to_f32(bs.code);
+  with_frame(S, [&](auto tiny) {
+    constexpr bool TINY = decltype(tiny)::value;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = r0 + i;
-    u32x4 dr = {0, 0, 0, 0};
-    if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
-    const uint32_t q = nv_encode8<SR>(v[i], bs.r, dr);
-    *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
-    if (dq) *reinterpret_cast<uint4*>(dq + r * ld_dq + j * 8) = nv_dq8(q, sbc, S);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + i;
+      u32x4 dr = {0, 0, 0, 0};
+      if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
+      const uint32_t q = nv_encode8<SR, TINY>(v[i], bs.r, dr);
+      *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
+      if (dq) *reinterpret_cast<uint4*>(dq + r * ld_dq + j * 8) = nv_dq8(q, sbc, S);
+    }
+  });
   if ((j & 1) == 0 && rg == 0) bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
 }
 
@@ -505,8 +550,13 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
     // a zero block has r = 0, and a finite u times 0 is u's signed zero
     float yv[16];
+    if (S < TINY_S) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) yv[i] = u[i] * bs.r;
+      for (int i = 0; i < 16; ++i) yv[i] = nv_frame<true>(u[i]) * bs.r;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) yv[i] = u[i] * bs.r;
+    }
     uint32_t out[2] = {0, 0};
     if (SR) {
 #pragma unroll

@@ -505,3 +505,29 @@ def test_nvfp4_gemm_mfma_scale_layout_same_bits(M, N, K):
         assert np.array_equal(from_dev_bf16(m.mx_gemm(Am, Bm, M, N, K)), ref)
     finally:
         m.mx_gemm_set_tile(-1)
+
+
+@pytest.mark.parametrize("path,K", [("mxfp8", 8192), ("nvfp4", 16384), ("bf16", 4096)])
+@pytest.mark.parametrize("bt", [False, True])
+def test_grouped_tile_order_with_a_ragged_last_run(path, K, bt):
+    """A dense GEMM whose B (8 MB) exceeds an XCD's L2 and whose rows hold at
+    most 64 tiles takes the grouped tile order: runs of 8 tile rows (128-row
+    tiles) or 4 (256-row tiles) walked column by column.  M = 1100 gives 9 or
+    5 tile rows, so the last run is ragged.  The default tile is compared whole
+    with the oracle, and every forced tile must give the same bits."""
+    m = mxq()
+    M, N = 1100, 1024
+    x = _bf16((M, K), 1.0, 70)
+    w = _bf16((N, K), 0.02, 71)
+    A, B, (a64, a32, b64, b32) = _path_operands(m, path, bt, x, w)
+    say(f"grouped tile order {path} bt={bt} {M}x{N}x{K}")
+    ref = m.mx_gemm(A, B, M, N, K)
+    _assert_gemm(ref, a64, b64, a32, b32)
+    ref = from_dev_bf16(ref)
+    try:
+        for t in range(7):
+            m.mx_gemm_set_tile(t)
+            out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
+            assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
+    finally:
+        m.mx_gemm_set_tile(-1)
