@@ -115,3 +115,24 @@ def torch_normal_bf16(shape, std, seed, device):
     g.manual_seed(int(seed))
     t = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
     return t.to(torch.bfloat16)
+
+
+# Dense-MLP tensors of configurations 4 and 5, generated on the device (shared
+# by the benchmark and the full-size parity tests): name -> (shape, std, seed).
+def mlp_tensors(cfg):
+    c = CONFIGS[cfg]
+    T, H, I = c["T"], c["H"], c["I"]
+    base = 40 if cfg == 4 else 50
+    return {
+        "x": ((T, H), 1.0, base + 1),            # gate_up input
+        "w_gu": ((2 * I, H), 0.02, base + 3),     # gate_up weight [N, K]
+        "dy_gu": ((T, 2 * I), 1e-3, base + 4),    # gate_up output gradient
+        "h": ((T, I), 1.0, base + 5),             # down input
+        "w_dn": ((H, I), 0.02, base + 6),         # down weight [N, K]
+        "dy_dn": ((T, H), 1e-3, base + 7),        # down output gradient
+    }
+
+
+def mlp_tensor(cfg, name, device):
+    shape, std, seed = mlp_tensors(cfg)[name]
+    return torch_normal_bf16(shape, std, seed, device)

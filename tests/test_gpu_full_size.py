@@ -1,19 +1,26 @@
-"""Parity at the full sizes of the benchmark's configurations 3, 4 and 5, in
-the launch configuration the benchmark times, on sampled outputs the oracle
-computes one by one (configurations 1 and 2 are checked whole elsewhere):
+"""Parity at the full sizes of configurations 3, 4 and 5, in the launch
+configuration the benchmark times (configurations 1 and 2 are checked whole
+elsewhere):
 
-* quantizers: sampled rows (and, for columnwise copies, sampled columns) are
-  byte-identical to the oracle's, with the per-tensor second scales checked
-  against fl(max|x| / 2688) from an exact device max; stochastic-rounding
-  draws are the oracle's Philox draws of the sampled elements' own indices;
-* GEMMs: sampled output elements against the oracle's dequantize-then-matmul
-  of the sampled operand rows (Frobenius error over the sample <= 1e-2 and
-  the element-wise BF16-accumulation bound);
+* quantizers, FULL TENSOR: every stored copy of every input is compared byte
+  for byte with the oracle, which runs chunk by chunk (rows, or columns for
+  columnwise copies) on the host's cores (tests/parity_pool.py); per-tensor
+  second scales are checked against fl(max|x| / 2688) from an exact device
+  maximum and then handed to the chunks; stochastic-rounding draws are the
+  oracle's Philox draws at each element's own index ("Um Quantizador
+  Compartilhado É o Verdadeiro Mecanismo" in "Miles Blackwell RL ..." asks for
+  a byte-by-byte contract);
+* GEMMs, EVERY OUTPUT TILE: one row in each 128-row band and one column in
+  each 128-column band (so every 128- or 256-wide workgroup tile holds checked
+  outputs, and the last row and column are always in), against the oracle's
+  dequantize-then-matmul of the GPU's own operand copies (which the quantizer
+  tests verify): Frobenius error over the sample <= 1e-2 and the element-wise
+  BF16-accumulation bound;
 * the MoE layer's fused SwiGLU epilogue equals the unfused path in full, and
   MXFP8 DGRAD through the transposed weight copy equals DGRAD reading the
   weight transposed, in full.
-Inputs follow the benchmark's recipe (seeded device normals for the dense
-MLPs, the numpy recipe for the MoE layer)."""
+Inputs follow the benchmark's recipe (synth.mlp_tensor for the dense MLPs,
+synth.config3 for the MoE layer)."""
 
 import numpy as np
 import pytest
@@ -24,11 +31,13 @@ from oracle import fp8_blockwise as OB
 from oracle import moe
 from oracle import mxfp8 as OM
 from oracle import nvfp4 as ON
-from oracle.philox import element_r16
 import synth
+from tests import parity_pool as P
 from tests.util import requires_gpu, to_dev_bf16, from_dev_bf16, to_np, say
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
+
+CHUNK = 4 << 20          # elements per oracle chunk
 
 
 def mxq():
@@ -41,13 +50,16 @@ def _idx(t, rows):
     return torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
 
 
-def _rows(t, rows):
-    return t[_idx(t, rows)]
+def _sub(c, rows, cols):
+    """BF16 bits of C[rows][:, cols]."""
+    return from_dev_bf16(c[_idx(c, rows)][:, _idx(c, cols)])
 
 
-def _cols_bits(t, cols):
-    """BF16 bits of columns `cols` of a device matrix, as rows [len(cols), R]."""
-    return from_dev_bf16(t[:, _idx(t, cols)].t().contiguous())
+def _bands(n, rs, band=128):
+    """One index in each band of `band` consecutive indices, plus the last."""
+    starts = np.arange(0, n, band)
+    pick = starts + rs.integers(0, np.minimum(band, n - starts))
+    return np.unique(np.concatenate([pick, [n - 1]])).astype(np.int64)
 
 
 def _tensor_S(t):
@@ -55,214 +67,243 @@ def _tensor_S(t):
     return np.float32(np.float32(a) / np.float32(2688.0))
 
 
-def _sample(n, k, rs, edges=True):
-    s = set(rs.choice(n, size=min(k, n), replace=False).tolist())
-    if edges:
-        s |= {0, n - 1}
-    return np.array(sorted(s), dtype=np.int64)
+def _check(c_dev, rows, cols, a, b, what):
+    frob, worst, ok = G.check(_sub(c_dev, rows, cols), a[0], b[0], a[1], b[1], rtol_frob=1e-2)
+    say(f"{what}: {len(rows)}x{len(cols)} outputs, frobenius {frob:.2e}, worst ratio {worst:.3f}")
+    assert ok, f"{what}: frobenius {frob:.3e}, worst element ratio {worst:.3f}"
 
 
-def _nv_rows(bits, row_ids, cols_total, S_rows, rnd="rne", seed=0, stream=0):
-    """Oracle 1x16 quantization of some rows of a larger tensor; stochastic
-    draws come from the elements' indices row * cols_total + col there."""
-    v = F.bf16_bits_to_f64(bits)
-    r16 = None
-    if rnd == "sr":
-        r, c = np.meshgrid(np.asarray(row_ids, dtype=np.int64), np.arange(v.shape[1], dtype=np.int64),
-                           indexing="ij")
-        r16 = element_r16(r * cols_total + c, seed, stream, 0)
-    return ON._rows_1x16(v, np.asarray(S_rows, dtype=np.float32), rnd, r16)
+def _pool(tasks):
+    bad = P.run(tasks, say)
+    assert not bad, f"{len(bad)} chunks differ, e.g. {bad[:3]}"
 
 
-def _nv_cols(bits_cols, col_ids, cols_total, S, rnd="rne", seed=0, stream=1):
-    """Oracle columnwise (16x1) copy rows for some columns c of a [R, cols_total]
-    tensor: bits_cols [len(col_ids), R]; element (r, c) draws with index
-    r * cols_total + c."""
-    v = F.bf16_bits_to_f64(bits_cols)
-    r16 = None
-    if rnd == "sr":
-        c, r = np.meshgrid(np.asarray(col_ids, dtype=np.int64), np.arange(v.shape[1], dtype=np.int64),
-                           indexing="ij")
-        r16 = element_r16(r * cols_total + c, seed, stream, 0)
-    S_rows = np.full(v.shape[0], S, dtype=np.float32)
-    return ON._rows_1x16(v, S_rows, rnd, r16)
+# ------------------------------------------------------------ NVFP4 helpers
 
-
-def _nv_dq(codes, scales, S):
+def _nv_dq(codes, scales, S, per_row):
+    """(float64, binary32) dequantized rows of a stored 1x16-blocked copy."""
     S = np.asarray(S, dtype=np.float32).reshape(-1)
-    gs = "per_row" if S.size > 1 else "per_tensor"
+    gs = "per_row" if per_row else "per_tensor"
     return (ON.dequantize_f64(codes, scales, S, "1x16", gs), ON.dequantize_f32(codes, scales, S, "1x16", gs))
 
 
-def _check(c_sub_bits, a, b):
-    frob, worst, ok = G.check(c_sub_bits, a[0], b[0], a[1], b[1], rtol_frob=1e-2)
-    assert ok, f"frobenius {frob:.3e}, worst element ratio {worst:.3f}"
+def _nv_rows_dq(c, s, S, rows, per_row):
+    Sv = to_np(S)
+    return _nv_dq(to_np(c[_idx(c, rows)]), to_np(s[_idx(s, rows)]), Sv[rows] if per_row else Sv, per_row)
 
 
-def _sub(c, rows, cols):
-    return from_dev_bf16(_rows(c, rows)[:, _idx(c, cols)])
+def _nv_tile_rows_dq(c, s, S, rows):
+    """Rows of a 16x16-tiled copy: the tile scales of a row's strip serve its
+    16-value blocks."""
+    return _nv_dq(to_np(c[_idx(c, rows)]), to_np(s)[np.asarray(rows) // 16], to_np(S), False)
+
+
+def _nv_tile_cols_dq(c, s, S, cols):
+    """Rows of the transpose of a 16x16-tiled copy [N, K]: column j of the
+    copy, c(W[n, j]) s(n/16, j/16) S for every n."""
+    cw, sw, S0 = to_np(c), to_np(s), np.float32(to_np(S)[0])
+    cols = np.asarray(cols)
+    e2 = F.e2m1_value((cw[:, cols // 2] >> (4 * (cols % 2))[None, :]) & 0xF).T       # [len(cols), N]
+    sb = F.e4m3_value(sw[:, cols // 16]).T.repeat(16, axis=1)                         # [len(cols), N]
+    b32 = ((e2.astype(np.float32) * sb.astype(np.float32)).astype(np.float32) * S0).astype(np.float32)
+    return e2 * sb * np.float64(S0), b32
+
+
+def _nv_full_tasks(store, name, x_dev, copies):
+    """Chunk tasks for the stored NVFP4 copies of x: copies is a list of
+    (kind, codes, scales, S, per_row, rnd, seed, stream) with kind nv_row,
+    nv_col or nv_tile; a per-tensor S is checked here against the exact
+    device maximum, a per-row S by the chunks."""
+    T, C = x_dev.shape
+    px = store.put(name, from_dev_bf16(x_dev))
+    tasks = []
+    S_t = None
+    for i, (kind, c, s, S, per_row, rnd, seed, stream) in enumerate(copies):
+        p = dict(x=px, codes=store.put(f"{name}_c{i}", to_np(c)), scales=store.put(f"{name}_s{i}", to_np(s)),
+                 rnd=rnd, seed=seed, stream=stream)
+        if per_row:
+            p["gS"] = store.put(f"{name}_S{i}", to_np(S))
+        else:
+            if S_t is None:
+                S_t = _tensor_S(x_dev)
+            assert to_np(S)[0] == S_t, f"{name}: per-tensor S {to_np(S)[0]} != fl(amax / 2688) {S_t}"
+            p["S"] = float(S_t)
+        n, step, align = {"nv_row": (T, CHUNK // C, 1), "nv_col": (C, CHUNK // T, 1),
+                          "nv_tile": (T, CHUNK // C, 16)}[kind]
+        tasks += [(kind, f"{name}:{kind}:{rnd}:{a}", a, b, p) for a, b in P.chunks(n, max(step, 1), align)]
+    return tasks
+
+
+def _nv_copies(m, name, x):
+    """The stored NVFP4 copies of one config-5 tensor, as the benchmark step
+    makes them ("dy_gu:row" / "dy_gu:col": one of the two gradient copies)."""
+    if name.startswith("w"):
+        c, s, S = m.nvfp4_quantize(x, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+        return [("nv_tile", c, s, S, False, "rne", 0, 0)]
+    if name.startswith("dy"):
+        out = []
+        if not name.endswith(":col"):
+            c, s, S = m.nvfp4_quantize(x, gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=0, stream_id=0)
+            out.append(("nv_row", c, s, S, True, "sr", 0, 0))
+        if not name.endswith(":row"):
+            c, s, S = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
+                                       stream_id=1)
+            out.append(("nv_col", c, s, S, False, "sr", 0, 1))
+        return out
+    c, s, S = m.nvfp4_quantize(x, gs=m.GScale.PER_ROW)
+    cc, sc, Sc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    return [("nv_row", c, s, S, True, "rne", 0, 0), ("nv_col", cc, sc, Sc, False, "rne", 0, 1)]
 
 
 # ------------------------------------------------------------------ config 5
 
-def test_config5_llama3_8b_nvfp4_mlp_sampled():
-    """Llama-3-8B-shaped MLP, NVFP4: 32768 tokens, hidden 4096, gate_up 28672;
-    per-token X, 16x16 W, stochastic rounding (seed 0) for dY rowwise (stream
-    0) and columnwise (stream 1); FPROP, DGRAD (W read transposed), WGRAD."""
+@pytest.mark.parametrize("name", ["x", "w_gu", "h", "w_dn", "dy_dn", "dy_gu:row", "dy_gu:col"])
+def test_config5_quantizers_full_tensor(name):
+    """Llama-3-8B-shaped MLP, NVFP4, every input of both linears: X and H
+    per-token rowwise RNE plus columnwise per-tensor RNE; the 16x16 weights;
+    dY per-token rowwise SR (seed 0, stream 0) and columnwise per-tensor SR
+    (stream 1)."""
     m = mxq()
-    rs = np.random.default_rng(55)
-    T, H, N2 = 32768, 4096, 2 * 14336
-    dev = "cuda"
-    say("config 5 full size: generating X, W_gate_up, dY")
-    x = synth.torch_normal_bf16((T, H), 1.0, 51, dev)
-    w = synth.torch_normal_bf16((N2, H), 0.02, 53, dev)
-    dy = synth.torch_normal_bf16((T, N2), 1e-3, 54, dev)
-    say("config 5: quantizers")
+    base = name.split(":")[0]
+    say(f"config 5 {name}: generating {synth.mlp_tensors(5)[base][0]}")
+    x = synth.mlp_tensor(5, base, "cuda")
+    copies = _nv_copies(m, name, x)
+    store = P.Store()
+    try:
+        tasks = _nv_full_tasks(store, base, x, copies)
+        del copies, x
+        say(f"config 5 {name}: {len(tasks)} oracle chunks on {P.workers()} cores")
+        _pool(tasks)
+    finally:
+        store.close()
+
+
+@pytest.mark.parametrize("lin", ["gate_up", "down"])
+def test_config5_gemms_every_tile(lin):
+    """FPROP Y = X W^T, DGRAD dX = dY W (the 16x16 weight read transposed) and
+    WGRAD dW = dY^T X (columnwise copies) of each linear."""
+    m = mxq()
+    rs = np.random.default_rng(5 if lin == "gate_up" else 6)
+    xn, wn, dn = ("x", "w_gu", "dy_gu") if lin == "gate_up" else ("h", "w_dn", "dy_dn")
+    x, w, dy = (synth.mlp_tensor(5, n, "cuda") for n in (xn, wn, dn))
+    T, K = x.shape
+    N = w.shape[0]
+    say(f"config 5 {lin}: quantizers")
     cx, sx, Sx = m.nvfp4_quantize(x)
+    cxc, sxc, Sxc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
     cw, sw, Sw = m.nvfp4_quantize(w, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
     cd, sd, Sd = m.nvfp4_quantize(dy, rnd=m.Round.SR, seed=0, stream_id=0)
-    cdc, sdc, Sdc = m.nvfp4_quantize(dy, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR,
-                                     seed=0, stream_id=1)
-    cxc, sxc, Sxc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
-    rt = _sample(T, 14, rs)
-    hc = _sample(H, 14, rs)
-    strips = _sample(N2 // 16, 3, rs)
-    rw = np.concatenate([np.arange(16 * s, 16 * s + 16) for s in strips])
-    ic = _sample(N2, 14, rs)
-    # X per-token rows
-    xb = from_dev_bf16(_rows(x, rt))
-    Sx_r = ON.second_scale(np.abs(F.bf16_bits_to_f64(xb)).max(axis=1))
-    ocx, osx = _nv_rows(xb, rt, H, Sx_r)
-    assert np.array_equal(to_np(Sx)[rt], Sx_r)
-    assert np.array_equal(to_np(_rows(cx, rt)), ocx) and np.array_equal(to_np(_rows(sx, rt)), osx)
-    # W: per-tensor S and whole 16-row strips
-    assert to_np(Sw)[0] == _tensor_S(w)
-    for s in strips:
-        wb = F.bf16_bits_to_f64(from_dev_bf16(w[16 * s:16 * s + 16]))
-        oc, os_, _ = ON.quantize_tile16(wb, "given", S_given=to_np(Sw)[0])
-        assert np.array_equal(to_np(cw[16 * s:16 * s + 16]), oc) and np.array_equal(to_np(sw[s:s + 1]), os_)
-    # dY per-token rows with stochastic rounding
-    db = from_dev_bf16(_rows(dy, rt))
-    Sd_r = ON.second_scale(np.abs(F.bf16_bits_to_f64(db)).max(axis=1))
-    ocd, osd = _nv_rows(db, rt, N2, Sd_r, "sr", 0, 0)
-    assert np.array_equal(to_np(Sd)[rt], Sd_r)
-    assert np.array_equal(to_np(_rows(cd, rt)), ocd) and np.array_equal(to_np(_rows(sd, rt)), osd)
-    # columnwise copies: sampled columns of dY (SR, stream 1) and of X (RNE)
-    assert to_np(Sdc)[0] == _tensor_S(dy) and to_np(Sxc)[0] == _tensor_S(x)
-    occ, osc = _nv_cols(_cols_bits(dy, ic), ic, N2, to_np(Sdc)[0], "sr", 0, 1)
-    assert np.array_equal(to_np(_rows(cdc, ic)), occ) and np.array_equal(to_np(_rows(sdc, ic)), osc)
-    oxc, oxs = _nv_cols(_cols_bits(x, hc), hc, H, to_np(Sxc)[0])
-    assert np.array_equal(to_np(_rows(cxc, hc)), oxc) and np.array_equal(to_np(_rows(sxc, hc)), oxs)
+    cdc, sdc, Sdc = m.nvfp4_quantize(dy, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
+                                     stream_id=1)
+    del x, w, dy
+    NV = m.Format.NVFP4
+    rT, rN, rK = _bands(T, rs), _bands(N, rs), _bands(K, rs)
 
-    A_x = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
-    B_w = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
-    say("config 5: FPROP 32768x28672x4096")
-    y = m.mx_gemm(A_x, B_w, T, N2, H)
-    ax = _nv_dq(ocx, osx, Sx_r)
-    wrows = rw[rs.choice(len(rw), 12, replace=False)]
-    w_codes = to_np(_rows(cw, wrows))
-    w_sc = to_np(sw)[wrows // 16]                       # a tile's scale serves its 16 rows
-    bw = _nv_dq(w_codes, w_sc, to_np(Sw))
-    _check(_sub(y, rt, wrows), ax, bw)
+    say(f"config 5 {lin}: FPROP {T}x{N}x{K}")
+    y = m.mx_gemm(m.Operand(NV, cx, sx, Sx, gs=m.GScale.PER_ROW),
+                  m.Operand(NV, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR), T, N, K)
+    _check(y, rT, rN, _nv_rows_dq(cx, sx, Sx, rT, True), _nv_tile_rows_dq(cw, sw, Sw, rN), f"{lin} FPROP")
     del y
-    say("config 5: DGRAD 32768x4096x28672 (16x16 W read transposed)")
-    dx = m.mx_gemm(m.Operand(m.Format.NVFP4, cd, sd, Sd, gs=m.GScale.PER_ROW),
-                   m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
-                             transposed=True), T, H, N2)
-    ad = _nv_dq(ocd, osd, Sd_r)
-    # rows of W^T = columns of W: nibble h of every row of the (strip-checked) copy
-    cw_all, sw_all = to_np(cw), to_np(sw)
-    e2 = F.e2m1_value((cw_all[:, hc // 2] >> (4 * (hc % 2))[None, :]) & 0xF).T        # [len(hc), N2]
-    sbt = F.e4m3_value(sw_all[:, hc // 16]).T.repeat(16, axis=1)                         # [len(hc), N2]
-    Sw0 = to_np(Sw)[0]
-    bt32 = ((e2.astype(np.float32) * sbt.astype(np.float32)).astype(np.float32) * Sw0).astype(np.float32)
-    bt64 = e2 * sbt * np.float64(Sw0)
-    _check(_sub(dx, rt, hc), ad, (bt64, bt32))
+    say(f"config 5 {lin}: DGRAD {T}x{K}x{N}")
+    dx = m.mx_gemm(m.Operand(NV, cd, sd, Sd, gs=m.GScale.PER_ROW),
+                   m.Operand(NV, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=True), T, K, N)
+    _check(dx, rT, rK, _nv_rows_dq(cd, sd, Sd, rT, True), _nv_tile_cols_dq(cw, sw, Sw, rK), f"{lin} DGRAD")
     del dx
-    say("config 5: WGRAD 28672x4096x32768 (columnwise copies)")
-    dw = m.mx_gemm(m.Operand(m.Format.NVFP4, cdc, sdc, Sdc, gs=m.GScale.PER_TENSOR),
-                   m.Operand(m.Format.NVFP4, cxc, sxc, Sxc, gs=m.GScale.PER_TENSOR), N2, H, T)
-    _check(_sub(dw, ic, hc), _nv_dq(occ, osc, to_np(Sdc)), _nv_dq(oxc, oxs, to_np(Sxc)))
+    say(f"config 5 {lin}: WGRAD {N}x{K}x{T}")
+    dw = m.mx_gemm(m.Operand(NV, cdc, sdc, Sdc, gs=m.GScale.PER_TENSOR),
+                   m.Operand(NV, cxc, sxc, Sxc, gs=m.GScale.PER_TENSOR), N, K, T)
+    _check(dw, rN, rK, _nv_rows_dq(cdc, sdc, Sdc, rN, False), _nv_rows_dq(cxc, sxc, Sxc, rK, False),
+           f"{lin} WGRAD")
 
 
 # ------------------------------------------------------------------ config 4
 
-def test_config4_qwen3_8b_mxfp8_mlp_sampled():
-    """Qwen3-8B-shaped MLP, MXFP8: 8192 tokens, hidden 4096, gate_up 24576;
-    DUAL copies of X and dY, the 32x32 weight with its transposed copy;
-    FPROP, DGRAD both ways (equal bits), WGRAD."""
+def _mx_full_tasks(store, name, x_dev, copies):
+    T, C = x_dev.shape
+    px = store.put(name, from_dev_bf16(x_dev))
+    tasks = []
+    for i, (kind, c, s) in enumerate(copies):
+        p = dict(x=px, codes=store.put(f"{name}_c{i}", to_np(c)), scales=store.put(f"{name}_s{i}", to_np(s)))
+        n, step, align = {"mx_row": (T, CHUNK // C, 1), "mx_col": (C, CHUNK // T, 1),
+                          "mx_tile": (T, CHUNK // C, 32), "mx_tile_t": (C, CHUNK // T, 32)}[kind]
+        tasks += [(kind, f"{name}:{kind}:{a}", a, b, p) for a, b in P.chunks(n, max(step, 1), align)]
+    return tasks
+
+
+@pytest.mark.parametrize("name", ["x", "w_gu", "dy_gu", "h", "w_dn", "dy_dn"])
+def test_config4_quantizers_full_tensor(name):
+    """Qwen3-8B-shaped MLP, MXFP8, every input of both linears: DUAL (rowwise
+    and columnwise) copies of X, H and dY; the 32x32 weights with their
+    transposed copies."""
     m = mxq()
-    rs = np.random.default_rng(44)
-    T, H, N2 = 8192, 4096, 2 * 12288
-    dev = "cuda"
-    say("config 4 full size: generating X, W_gate_up, dY")
-    x = synth.torch_normal_bf16((T, H), 1.0, 41, dev)
-    w = synth.torch_normal_bf16((N2, H), 0.02, 43, dev)
-    dy = synth.torch_normal_bf16((T, N2), 1e-3, 44, dev)
-    say("config 4: quantizers")
+    say(f"config 4 {name}: generating {synth.mlp_tensors(4)[name][0]}")
+    x = synth.mlp_tensor(4, name, "cuda")
+    if name.startswith("w"):
+        c, s, ct, st_ = m.mx_quantize(x, block=m.Block.TILE, transposed_copy=True)
+        copies = [("mx_tile", c, s), ("mx_tile_t", ct, st_)]
+    else:
+        c, s, cc, sc = m.mx_quantize(x, block=m.Block.DUAL)
+        copies = [("mx_row", c, s), ("mx_col", cc, sc)]
+    store = P.Store()
+    try:
+        tasks = _mx_full_tasks(store, name, x, copies)
+        del copies, x
+        say(f"config 4 {name}: {len(tasks)} oracle chunks on {P.workers()} cores")
+        _pool(tasks)
+    finally:
+        store.close()
+
+
+def _mx_dq(codes, scales):
+    v = OM.dequantize_f64(codes, scales)
+    return v, v.astype(np.float32)
+
+
+@pytest.mark.parametrize("lin", ["gate_up", "down"])
+def test_config4_gemms_every_tile(lin):
+    """FPROP, DGRAD (the transposed 32x32 copy, and the weight read
+    transposed: equal bits in full), WGRAD (columnwise copies)."""
+    m = mxq()
+    rs = np.random.default_rng(7 if lin == "gate_up" else 8)
+    xn, wn, dn = ("x", "w_gu", "dy_gu") if lin == "gate_up" else ("h", "w_dn", "dy_dn")
+    x, w, dy = (synth.mlp_tensor(4, n, "cuda") for n in (xn, wn, dn))
+    T, K = x.shape
+    N = w.shape[0]
+    say(f"config 4 {lin}: quantizers")
     cx, sx, cxc, sxc = m.mx_quantize(x, block=m.Block.DUAL)
     cw, sw, cwt, swt = m.mx_quantize(w, block=m.Block.TILE, transposed_copy=True)
     cd, sd, cdc, sdc = m.mx_quantize(dy, block=m.Block.DUAL)
-    rt, hc, ic = _sample(T, 14, rs), _sample(H, 14, rs), _sample(N2, 14, rs)
-    wstrips = _sample(N2 // 32, 2, rs)
-    tstrips = _sample(H // 32, 2, rs)
-
-    def rows_q(t, rows):
-        return OM.quantize_rowwise(F.bf16_bits_to_f64(from_dev_bf16(_rows(t, rows))))
-
-    def cols_q(t, cols):
-        return OM.quantize_rowwise(F.bf16_bits_to_f64(_cols_bits(t, cols)))
-
-    ox = rows_q(x, rt)
-    assert np.array_equal(to_np(_rows(cx, rt)), ox[0]) and np.array_equal(to_np(_rows(sx, rt)), ox[1])
-    oxc = cols_q(x, hc)
-    assert np.array_equal(to_np(_rows(cxc, hc)), oxc[0]) and np.array_equal(to_np(_rows(sxc, hc)), oxc[1])
-    od = rows_q(dy, rt)
-    assert np.array_equal(to_np(_rows(cd, rt)), od[0]) and np.array_equal(to_np(_rows(sd, rt)), od[1])
-    odc = cols_q(dy, ic)
-    assert np.array_equal(to_np(_rows(cdc, ic)), odc[0]) and np.array_equal(to_np(_rows(sdc, ic)), odc[1])
-    for s in wstrips:                                   # 32-row strips of W, 32x32 tiles
-        oc, osc = OM.quantize_tile32(F.bf16_bits_to_f64(from_dev_bf16(w[32 * s:32 * s + 32])))
-        assert np.array_equal(to_np(cw[32 * s:32 * s + 32]), oc) and np.array_equal(to_np(sw[s:s + 1]), osc)
-    for s in tstrips:                                   # the transposed copy: 32-column strips of W
-        oc, osc = OM.quantize_tile32(F.bf16_bits_to_f64(_cols_bits(w, np.arange(32 * s, 32 * s + 32))))
-        assert np.array_equal(to_np(cwt[32 * s:32 * s + 32]), oc) and np.array_equal(to_np(swt[s:s + 1]), osc)
-
-    def dq(codes, scales):
-        v = OM.dequantize_f64(codes, scales)
-        return v, v.astype(np.float32)
-
+    del x, w, dy
     Op = lambda c, s, **k: m.Operand(m.Format.MXFP8, c, s, **k)
-    say("config 4: FPROP 8192x24576x4096")
-    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N2, H)
-    wrows = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in wstrips])[::5]
-    bw = dq(to_np(_rows(cw, wrows)), to_np(sw)[wrows // 32])
-    _check(_sub(y, rt, wrows), dq(*ox), bw)
+    rT, rN, rK = _bands(T, rs), _bands(N, rs), _bands(K, rs)
+    rows = lambda c, s, r: _mx_dq(to_np(c[_idx(c, r)]), to_np(s[_idx(s, r)]))
+    tile_rows = lambda c, s, r: _mx_dq(to_np(c[_idx(c, r)]), to_np(s)[np.asarray(r) // 32])
+
+    say(f"config 4 {lin}: FPROP {T}x{N}x{K}")
+    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N, K)
+    _check(y, rT, rN, rows(cx, sx, rT), tile_rows(cw, sw, rN), f"{lin} FPROP")
     del y
-    say("config 4: DGRAD 8192x4096x24576, both ways")
-    dx1 = m.mx_gemm(Op(cd, sd), Op(cw, sw, block=m.Block.TILE, transposed=True), T, H, N2)
-    dx2 = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, H, N2)
+    say(f"config 4 {lin}: DGRAD {T}x{K}x{N}, both ways")
+    dx1 = m.mx_gemm(Op(cd, sd), Op(cw, sw, block=m.Block.TILE, transposed=True), T, K, N)
+    dx2 = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, K, N)
     assert np.array_equal(from_dev_bf16(dx1), from_dev_bf16(dx2))
-    trows = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in tstrips])[::5]
-    bt = dq(to_np(_rows(cwt, trows)), to_np(swt)[trows // 32])
-    _check(_sub(dx2, rt, trows), dq(*od), bt)
-    del dx1, dx2
-    say("config 4: WGRAD 24576x4096x8192")
-    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N2, H, T)
-    _check(_sub(dw, ic, hc), dq(*odc), dq(*oxc))
+    del dx1
+    _check(dx2, rT, rK, rows(cd, sd, rT), tile_rows(cwt, swt, rK), f"{lin} DGRAD")
+    del dx2
+    say(f"config 4 {lin}: WGRAD {N}x{K}x{T}")
+    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N, K, T)
+    _check(dw, rN, rK, rows(cdc, sdc, rN), rows(cxc, sxc, rK), f"{lin} WGRAD")
 
 
 @pytest.mark.parametrize("kind", ["pow2", "f32"])
-def test_config4_blockwise_fp8_sampled(kind):
-    """The Qwen3-8B-shaped MLP with DeepSeek-style blockwise FP8, both scale
-    kinds: DUAL 1x128 copies of X and dY, the 128x128 weight with its
-    transposed copy (sampled rows, columns and 128-row / 128-column strips
-    against the oracle, codes and scales bit for bit); FPROP, DGRAD (the
-    transposed copy) and WGRAD on sampled outputs."""
+def test_config4_blockwise_fp8(kind):
+    """The Qwen3-8B-shaped gate_up linear with DeepSeek-style blockwise FP8,
+    both scale kinds: DUAL 1x128 copies of X and dY and the 128x128 weight
+    with its transposed copy (sampled rows, columns and 128-row / 128-column
+    strips against the oracle, codes and scales bit for bit); FPROP, DGRAD
+    (the transposed copy) and WGRAD on every output tile."""
     m = mxq()
     rs = np.random.default_rng(45)
-    T, H, N2 = 8192, 4096, 2 * 12288
-    dev = "cuda"
     f32 = kind == "f32"
     quant = m.fp8bw_quantize_f32 if f32 else m.fp8bw_quantize
     q_rows = OB.quantize_rows_f32 if f32 else OB.quantize_rows
@@ -270,61 +311,70 @@ def test_config4_blockwise_fp8_sampled(kind):
     deq = OB.dequantize_f32s_f64 if f32 else OB.dequantize_f64
     fmt = m.Format.FP8_B128_F32 if f32 else m.Format.FP8_B128
     same = (lambda a, b: np.array_equal(a.view(np.uint32), b.view(np.uint32))) if f32 else np.array_equal
-    say(f"config 4 full size, blockwise FP8 ({kind}): generating X, W_gate_up, dY")
-    x = synth.torch_normal_bf16((T, H), 1.0, 41, dev)
-    w = synth.torch_normal_bf16((N2, H), 0.02, 43, dev)
-    dy = synth.torch_normal_bf16((T, N2), 1e-3, 44, dev)
+    say(f"config 4, blockwise FP8 ({kind}): generating X, W_gate_up, dY")
+    x, w, dy = (synth.mlp_tensor(4, n, "cuda") for n in ("x", "w_gu", "dy_gu"))
+    T, K = x.shape
+    N = w.shape[0]
     say(f"config 4 ({kind}): quantizers")
     cx, sx, cxc, sxc = quant(x, block=m.Block.DUAL)
     cw, sw, cwt, swt = quant(w, block=m.Block.TILE, transposed_copy=True)
     cd, sd, cdc, sdc = quant(dy, block=m.Block.DUAL)
-    rt, hc, ic = _sample(T, 14, rs), _sample(H, 14, rs), _sample(N2, 14, rs)
-    wstrips, tstrips = _sample(N2 // 128, 2, rs), _sample(H // 128, 2, rs)
+    rt, hc, ic = P_sample(T, rs), P_sample(K, rs), P_sample(N, rs)
+    wstrips, tstrips = P_sample(N // 128, rs, 2), P_sample(K // 128, rs, 2)
+
+    def cols_bits(t, cols):
+        return from_dev_bf16(t[:, _idx(t, cols)].t().contiguous())
 
     def check_rows(c, sc, o):
         assert np.array_equal(to_np(c), o[0]) and same(to_np(sc), o[1])
 
-    ox = q_rows(F.bf16_bits_to_f64(from_dev_bf16(_rows(x, rt))))
-    check_rows(_rows(cx, rt), _rows(sx, rt), ox)
-    oxc = q_rows(F.bf16_bits_to_f64(_cols_bits(x, hc)))
-    check_rows(_rows(cxc, hc), _rows(sxc, hc), oxc)
-    od = q_rows(F.bf16_bits_to_f64(from_dev_bf16(_rows(dy, rt))))
-    check_rows(_rows(cd, rt), _rows(sd, rt), od)
-    odc = q_rows(F.bf16_bits_to_f64(_cols_bits(dy, ic)))
-    check_rows(_rows(cdc, ic), _rows(sdc, ic), odc)
+    check_rows(cx[_idx(cx, rt)], sx[_idx(sx, rt)], q_rows(F.bf16_bits_to_f64(from_dev_bf16(x[_idx(x, rt)]))))
+    check_rows(cxc[_idx(cxc, hc)], sxc[_idx(sxc, hc)], q_rows(F.bf16_bits_to_f64(cols_bits(x, hc))))
+    check_rows(cd[_idx(cd, rt)], sd[_idx(sd, rt)], q_rows(F.bf16_bits_to_f64(from_dev_bf16(dy[_idx(dy, rt)]))))
+    check_rows(cdc[_idx(cdc, ic)], sdc[_idx(sdc, ic)], q_rows(F.bf16_bits_to_f64(cols_bits(dy, ic))))
     for st in wstrips:                                  # 128-row strips of W, 128x128 tiles
         oc, osc = q_tile(F.bf16_bits_to_f64(from_dev_bf16(w[128 * st:128 * st + 128])))
         check_rows(cw[128 * st:128 * st + 128], sw[st:st + 1], (oc, osc))
     for st in tstrips:                                  # the transposed copy: 128-column strips
-        oc, osc = q_tile(F.bf16_bits_to_f64(_cols_bits(w, np.arange(128 * st, 128 * st + 128))))
+        oc, osc = q_tile(F.bf16_bits_to_f64(cols_bits(w, np.arange(128 * st, 128 * st + 128))))
         check_rows(cwt[128 * st:128 * st + 128], swt[st:st + 1], (oc, osc))
+    del x, w, dy
 
     def dq(codes, scales):
         v = deq(codes, scales)
         return v, v.astype(np.float32)
 
+    rows = lambda c, s, r: dq(to_np(c[_idx(c, r)]), to_np(s[_idx(s, r)]))
+    tile_rows = lambda c, s, r: dq(to_np(c[_idx(c, r)]), to_np(s)[np.asarray(r) // 128])
+    rT, rN, rK = _bands(T, rs), _bands(N, rs), _bands(K, rs)
     Op = lambda c, sc, **k: m.Operand(fmt, c, sc, **k)
-    say(f"config 4 ({kind}): FPROP 8192x24576x4096")
-    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N2, H)
-    wrows = np.concatenate([np.arange(128 * st, 128 * st + 128) for st in wstrips])[::9]
-    _check(_sub(y, rt, wrows), dq(*ox), dq(to_np(_rows(cw, wrows)), to_np(sw)[wrows // 128]))
+    say(f"config 4 ({kind}): FPROP {T}x{N}x{K}")
+    y = m.mx_gemm(Op(cx, sx), Op(cw, sw, block=m.Block.TILE), T, N, K)
+    _check(y, rT, rN, rows(cx, sx, rT), tile_rows(cw, sw, rN), f"blockwise {kind} FPROP")
     del y
-    say(f"config 4 ({kind}): DGRAD 8192x4096x24576 (transposed tile copy)")
-    dx = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, H, N2)
-    trows = np.concatenate([np.arange(128 * st, 128 * st + 128) for st in tstrips])[::9]
-    _check(_sub(dx, rt, trows), dq(*od), dq(to_np(_rows(cwt, trows)), to_np(swt)[trows // 128]))
+    say(f"config 4 ({kind}): DGRAD {T}x{K}x{N} (transposed tile copy)")
+    dx = m.mx_gemm(Op(cd, sd), Op(cwt, swt, block=m.Block.TILE), T, K, N)
+    _check(dx, rT, rK, rows(cd, sd, rT), tile_rows(cwt, swt, rK), f"blockwise {kind} DGRAD")
     del dx
-    say(f"config 4 ({kind}): WGRAD 24576x4096x8192")
-    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N2, H, T)
-    _check(_sub(dw, ic, hc), dq(*odc), dq(*oxc))
+    say(f"config 4 ({kind}): WGRAD {N}x{K}x{T}")
+    dw = m.mx_gemm(Op(cdc, sdc), Op(cxc, sxc), N, K, T)
+    _check(dw, rN, rK, rows(cdc, sdc, rN), rows(cxc, sxc, rK), f"blockwise {kind} WGRAD")
+
+
+def P_sample(n, rs, k=14):
+    s = set(rs.choice(n, size=min(k, n), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(s), dtype=np.int64)
 
 
 # ------------------------------------------------------------------ config 3
 
-def test_config3_qwen3_30b_a3b_moe_sampled():
+def test_config3_qwen3_30b_a3b_moe():
     """Qwen3-30B-A3B-shaped MoE layer: 8192 tokens, hidden 2048, 128 experts,
-    I 768, top-8 (65536 routed rows); grouped gate_up with a gather, SwiGLU
-    (fused and unfused), per-token Q(H), grouped down."""
+    I 768, top-8 (65536 routed rows).  Full-tensor parity of per-token Q(X),
+    every expert's joint gate/up and down weights (one S per expert matrix)
+    and per-token Q(H) of the GPU's own H; the grouped gate_up (row gather)
+    and down GEMMs on every output tile of every expert; SwiGLU fused and
+    unfused equal in full."""
     import torch
     from tests.test_gpu_moe import quantize_experts
     m = mxq()
@@ -359,29 +409,57 @@ def test_config3_qwen3_30b_a3b_moe_sampled():
     wdn_max = np.abs(F.bf16_bits_to_f64(d["w_dn"].reshape(E, -1))).max(axis=1)
     assert np.array_equal(to_np(Sgu), ON.second_scale(wgu_max))
     assert np.array_equal(to_np(Sdn), ON.second_scale(wdn_max))
-    say("config 3: sampled checks")
-    rows = _sample(M, 12, rs)
-    jg, jd = _sample(N2, 12, rs), _sample(H, 12, rs)
-    gu_bits = from_dev_bf16(_rows(gu, rows))
-    h_bits = from_dev_bf16(_rows(h, rows))
-    for r in rows:
-        g = int(np.searchsorted(off, r, side="right") - 1)
-        tok = int(row_token[r])
-        xb = x[tok:tok + 1]
-        Sxr = ON.second_scale(np.abs(F.bf16_bits_to_f64(xb)).max(axis=1))
-        ocx, osx = _nv_rows(xb, [tok], H, Sxr)
-        assert np.array_equal(to_np(cx[tok:tok + 1]), ocx) and np.array_equal(to_np(sx[tok:tok + 1]), osx)
-        ocw, osw = _nv_rows(d["w_gu"][g][jg], jg, H, np.full(len(jg), to_np(Sgu)[g], np.float32))
-        assert np.array_equal(to_np(cgu[g][_idx(cgu, jg)]), ocw)
-        _check(_sub(gu, [r], jg), _nv_dq(ocx, osx, Sxr), _nv_dq(ocw, osw, to_np(Sgu)[g:g + 1]))
-        # Q(H) of the GPU's own H row, then the down GEMM on it
-        hv = h_bits[list(rows).index(r)][None]
-        Shr = ON.second_scale(np.abs(F.bf16_bits_to_f64(hv)).max(axis=1))
-        och, osh = _nv_rows(hv, [r], I, Shr)
-        assert np.array_equal(to_np(ch[r:r + 1]), och) and np.array_equal(to_np(sh[r:r + 1]), osh)
-        ocd, osd = _nv_rows(d["w_dn"][g][jd], jd, I, np.full(len(jd), to_np(Sdn)[g], np.float32))
-        assert np.array_equal(to_np(cdn[g][_idx(cdn, jd)]), ocd)
-        _check(_sub(y, [r], jd), _nv_dq(och, osh, Shr), _nv_dq(ocd, osd, to_np(Sdn)[g:g + 1]))
+
+    say("config 3: full-tensor quantizer parity")
+    store = P.Store()
+    try:
+        tasks = []
+        p = dict(x=store.put("x", x), codes=store.put("cx", to_np(cx)), scales=store.put("sx", to_np(sx)),
+                 gS=store.put("Sx", to_np(Sx)), rnd="rne", seed=0, stream=0)
+        tasks += [("nv_row", f"x:{a}", a, b, p) for a, b in P.chunks(T, CHUNK // H)]
+        hb = from_dev_bf16(h)
+        p = dict(x=store.put("h", hb), codes=store.put("ch", to_np(ch)), scales=store.put("sh", to_np(sh)),
+                 gS=store.put("Sh", to_np(Sh)), rnd="rne", seed=0, stream=0)
+        tasks += [("nv_row", f"h:{a}", a, b, p) for a, b in P.chunks(M, CHUNK // I)]
+        for nm, w, c, s, S in (("w_gu", d["w_gu"], cgu, sgu, Sgu), ("w_dn", d["w_dn"], cdn, sdn, Sdn)):
+            rows_e = w.shape[1]
+            px = store.put(nm, w.reshape(E * rows_e, -1))
+            pc = store.put(nm + "_c", to_np(c).reshape(E * rows_e, -1))
+            ps = store.put(nm + "_s", to_np(s).reshape(E * rows_e, -1))
+            Sv = to_np(S)
+            for e in range(E):                           # one chunk per expert, its own S
+                tasks.append(("nv_row", f"{nm}:{e}", e * rows_e, (e + 1) * rows_e,
+                              dict(x=px, codes=pc, scales=ps, S=float(Sv[e]), rnd="rne", seed=0, stream=0)))
+        say(f"config 3: {len(tasks)} oracle chunks on {P.workers()} cores")
+        _pool(tasks)
+    finally:
+        store.close()
+
+    say("config 3: every output tile of every expert")
+    jg, jd = _bands(N2, rs), _bands(H, rs)
+    cxn, sxn, Sxn = to_np(cx), to_np(sx), to_np(Sx)
+    chn, shn, Shn = to_np(ch), to_np(sh), to_np(Sh)
+    cgun, sgun, Sgun = to_np(cgu), to_np(sgu), to_np(Sgu)
+    cdnn, sdnn, Sdnn = to_np(cdn), to_np(sdn), to_np(Sdn)
+    checked = 0
+    for g in range(E):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        rows = lo + _bands(hi - lo, rs)                 # every m-tile of this expert
+        toks = row_token[rows]
+        a = _nv_dq(cxn[toks], sxn[toks], Sxn[toks], True)
+        b = _nv_dq(cgun[g][jg], sgun[g][jg], Sgun[g:g + 1], False)
+        frob, worst, ok = G.check(_sub(gu, rows, jg), a[0], b[0], a[1], b[1])
+        assert ok, f"expert {g} gate_up: frobenius {frob:.3e}, worst {worst:.3f}"
+        a = _nv_dq(chn[rows], shn[rows], Shn[rows], True)
+        b = _nv_dq(cdnn[g][jd], sdnn[g][jd], Sdnn[g:g + 1], False)
+        frob, worst, ok = G.check(_sub(y, rows, jd), a[0], b[0], a[1], b[1])
+        assert ok, f"expert {g} down: frobenius {frob:.3e}, worst {worst:.3f}"
+        checked += len(rows)
+    say(f"config 3: {checked} rows x ({len(jg)} gate_up + {len(jd)} down) columns checked")
     # SwiGLU within a few BF16 ulps of the float64 reference on the GPU's gate_up
-    ref = F.bf16_bits_to_f64(moe.swiglu_f64(gu_bits, I))
-    assert np.all(np.abs(F.bf16_bits_to_f64(h_bits) - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+    rows = _bands(M, rs, 256)
+    ref = F.bf16_bits_to_f64(moe.swiglu_f64(from_dev_bf16(gu[_idx(gu, rows)]), I))
+    hv = F.bf16_bits_to_f64(hb[rows])
+    assert np.all(np.abs(hv - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
