@@ -1,32 +1,33 @@
 #!/usr/bin/env python3
-"""Benchmark of the NVFP4 linear-layer hot path on one MI355X.
+"""Benchmark of the microscaling hot path on one MI355X.
 
-One step = one pass over one batch of the NVFP4 workload with 4096 tokens,
-hidden 2048 and 768 outputs (the second configuration of the benchmark set):
-  1. per-token NVFP4 quantization of the activations X [4096, 2048]
-  2. 16x16 NVFP4 quantization of the weight W [768, 2048] (per-tensor scale:
-     an amax pass, then the quantize pass, which also writes the dequantized
-     BF16 copy DQ(Q(W)) [768, 2048], the dequantized-backward operand)
-  3. FPROP  Y [4096, 768]  = Q(X) Q(W)^T       (NVFP4 x NVFP4, BF16 out)
-  4. DGRAD dX [4096, 2048] = dY DQ(Q(W))       (BF16, weight read transposed)
-Inputs are seeded synthetic tensors (the pages' models and datasets stand in
-as shapes and distributions only), resident in HBM before timing; ten
-buffer sets (> 512 MB in total) rotate so reads come from HBM rather than
-the 256 MB last-level cache.
+Headline workload: the Llama-3-8B-shaped dense MLP in NVFP4 of the NVFP4
+pretraining pages (sequence 8192 x micro-batch 4 = 32768 tokens, hidden 4096,
+intermediate 14336).  One step = one training pass over one batch of both
+linears, gate_up (4096 -> 28672) and down (14336 -> 4096), each:
+   1. Q(X)  rowwise 1x16, per-token S, RNE            (FPROP operand)
+   2. Q(X)  columnwise 16x1, per-tensor S, RNE        (WGRAD operand)
+   3. Q(W)  16x16 tiles, per-tensor S, RNE            (FPROP, and DGRAD read transposed)
+   4. FPROP  Y  = Q(X) Q(W)^T                         (BF16 out)
+   5. Q(dY) rowwise 1x16, per-token S, stochastic rounding (seed 0, stream 0)
+   6. Q(dY) columnwise 16x1, per-tensor S, stochastic rounding (stream 1)
+   7. DGRAD dX = Q(dY) Q(W)                           (the 16x16 copy read transposed)
+   8. WGRAD dW = Q(dY)^T Q(X)                         (the two columnwise copies)
+Each linear is measured on its own seeded inputs (the SwiGLU between them is
+not part of this path).  Inputs are seeded synthetic tensors (synth.mlp_tensor;
+the pages' model and dataset stand in as shapes and distributions only),
+resident in HBM before timing; a step moves about 9 GB, far more than the
+256 MB last-level cache.
 
-Prints ONE JSON line on stdout.  `value` is the step's GEMM throughput: the
-two GEMMs' algorithmic flops (2*M*N*K each) over the whole step's time,
-quantization and dequantization included.  The step is timed two ways, both
-reported: plain launches back to back on one stream, and replays of the step
-captured once per buffer set as a HIP graph (the library records no memsets,
-so every node is a kernel); `value` takes the faster and `launch` names it.
-`--overlap` forks the weight path (Q(W) with DQ(W)), which depends on no
-activation, to a second stream inside the graph; on MI355X that measured
-slower.  `--eager` skips the graph.  Per-stage times (HIP events around each
-stage of spin-fronted eager steps), GB/s, TFLOP/s and fractions of peak are
-in "kernels"; "roofline" times the stage with the largest share again over
-runs of back-to-back launches.  The CPU oracle, timed on a bounded sample of
-the same step, is reported as "cpu_baseline".
+Prints ONE JSON line on stdout.  `value` = the step's GEMM throughput: the six
+GEMMs' algorithmic flops (2 M N K each, 34.6 TFLOP per step) over the whole
+step's wall time, quantization included.  Every stage carries a HIP event
+pair on the launch stream inside the timed steps; "kernels" gives each
+stage's time, GB/s or TFLOP/s and fraction of peak, and "roofline" the stage
+with the largest share (its average launch duration from those events).  The
+CPU oracle, timed on a bounded sample of the same step, is "cpu_baseline".
+"config2" repeats the smaller NVFP4 linear of the second configuration
+(4096 tokens, 2048 -> 768, with the dequantized-backward DGRAD).
 """
 
 import argparse
@@ -40,19 +41,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-M, K, N = 4096, 2048, 768
+T, HID, INTER = 32768, 4096, 14336
 PEAK_HBM_GBPS = 8000.0
-PEAK_F16_TFLOPS = 2500.0     # dense FP16/BF16 MFMA
+PEAK_F16_TFLOPS = 2500.0     # dense FP16/BF16 MFMA (the dtype the NVFP4 GEMM issues)
 PEAK_FP4_TFLOPS = 10100.0    # dense FP4 MFMA (context for the NVFP4 GEMM)
-SETS = 10
+PEAK_FP8_TFLOPS = 5000.0
 
-# algorithmic bytes / flops per launch
-BYTES_QX = M * K * 2 + M * K // 2 + M * (K // 16) + M * 4
-# Q(W) and DQ(W) in one pass: two reads of W (amax, quantize), codes, scales,
-# S and the BF16 dequantized copy
-BYTES_QDQW = 2 * N * K * 2 + N * K // 2 + (N // 16) * (K // 16) + 4 + N * K * 2
-FLOPS_FPROP = 2 * M * N * K
-FLOPS_DGRAD = 2 * M * K * N
+# (linear, input, weight, output gradient, K, N)
+LINEARS = [("gate_up", "x", "w_gu", "dy_gu", HID, 2 * INTER), ("down", "h", "w_dn", "dy_dn", INTER, HID)]
+STEP_FLOPS = sum(3 * 2 * T * N * K for _, _, _, _, K, N in LINEARS)
 
 
 def log(msg):
@@ -124,193 +121,253 @@ def measured_traffic(kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_sets(m, torch, data):
-    import numpy as np
+# ---------------------------------------------------------------- the step
+
+def make_buffers(m, torch):
+    """Inputs (seeded, on the device) and every output of the step."""
+    import synth
     dev = "cuda"
-
-    def bf(b):
-        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x0, w0, dy0 = bf(data["x"]), bf(data["w"]), bf(data["dy"])
-    sets = []
-    for _ in range(SETS):
-        s = dict(x=x0.clone(), w=w0.clone(), dy=dy0.clone())
-        s["cx"] = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-        s["sx"] = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
-        s["Sx"] = torch.empty(M, dtype=torch.float32, device=dev)
-        s["cw"] = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-        s["sw"] = torch.empty((N // 16, K // 16), dtype=torch.uint8, device=dev)
-        s["Sw"] = torch.empty(1, dtype=torch.float32, device=dev)
-        s["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        s["wdq"] = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-        s["dx"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        sets.append(s)
-    return sets
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
+    b = {}
+    for lin, xn, wn, dn, K, N in LINEARS:
+        d = dict(x=synth.mlp_tensor(5, xn, dev), w=synth.mlp_tensor(5, wn, dev), dy=synth.mlp_tensor(5, dn, dev),
+                 K=K, N=N)
+        d.update(cx=u8(T, K // 2), sx=u8(T, K // 16), Sx=f32(T),
+                 cxc=u8(K, T // 2), sxc=u8(K, T // 16), Sxc=f32(1),
+                 cw=u8(N, K // 2), sw=u8(N // 16, K // 16), Sw=f32(1),
+                 cd=u8(T, N // 2), sd=u8(T, N // 16), Sd=f32(T),
+                 cdc=u8(N, T // 2), sdc=u8(N, T // 16), Sdc=f32(1),
+                 y=bf(T, N), dx=bf(T, K), dw=bf(N, K))
+        b[lin] = d
+    return b
 
 
-def step_concurrent(m, s, side, torch):
-    """The same stages with the weight path (Q(W) with DQ(W)) on a second
-    stream beside Q(X); FPROP waits for it."""
-    main = torch.cuda.current_stream()
-    side.wait_stream(main)
-    with torch.cuda.stream(side):
-        m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
-        qw_done = torch.cuda.Event()
-        qw_done.record(side)
-    m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
-    main.wait_event(qw_done)
-    m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
-              m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
-                        gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
-    main.wait_stream(side)
-    m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
-              m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
-              out=s["dx"])
+def stages(m, b):
+    """The step's 16 stages: (name, fn, algorithmic bytes or None, flops or None)."""
+    out = []
+    NV = m.Format.NVFP4
+    for lin, _, _, _, K, N in LINEARS:
+        d = b[lin]
+
+        def qx(d=d):
+            m.nvfp4_quantize(d["x"], gs=m.GScale.PER_ROW, codes=d["cx"], block_scales=d["sx"], gscales=d["Sx"])
+
+        def qxc(d=d):
+            m.nvfp4_quantize(d["x"], block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=d["cxc"],
+                             block_scales=d["sxc"], gscales=d["Sxc"])
+
+        def qw(d=d):
+            m.nvfp4_quantize(d["w"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=d["cw"],
+                             block_scales=d["sw"], gscales=d["Sw"])
+
+        def fprop(d=d, K=K, N=N):
+            m.mx_gemm(m.Operand(NV, d["cx"], d["sx"], d["Sx"], gs=m.GScale.PER_ROW),
+                      m.Operand(NV, d["cw"], d["sw"], d["Sw"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR),
+                      T, N, K, out=d["y"])
+
+        def qd(d=d):
+            m.nvfp4_quantize(d["dy"], gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=0, stream_id=0, codes=d["cd"],
+                             block_scales=d["sd"], gscales=d["Sd"])
+
+        def qdc(d=d):
+            m.nvfp4_quantize(d["dy"], block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
+                             stream_id=1, codes=d["cdc"], block_scales=d["sdc"], gscales=d["Sdc"])
+
+        def dgrad(d=d, K=K, N=N):
+            m.mx_gemm(m.Operand(NV, d["cd"], d["sd"], d["Sd"], gs=m.GScale.PER_ROW),
+                      m.Operand(NV, d["cw"], d["sw"], d["Sw"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
+                                transposed=True), T, K, N, out=d["dx"])
+
+        def wgrad(d=d, K=K, N=N):
+            m.mx_gemm(m.Operand(NV, d["cdc"], d["sdc"], d["Sdc"], gs=m.GScale.PER_TENSOR),
+                      m.Operand(NV, d["cxc"], d["sxc"], d["Sxc"], gs=m.GScale.PER_TENSOR), N, K, T, out=d["dw"])
+
+        nx, nw, nd = T * K, N * K, T * N
+        f = 2 * T * N * K
+        out += [(f"{lin}_quantize_x_rowwise_per_token_rne", qx, nx * 2 + nx // 2 + nx // 16 + T * 4, None),
+                # per-tensor copies read x twice (the amax pass, then the quantize pass)
+                (f"{lin}_quantize_x_colwise_per_tensor_rne", qxc, 2 * nx * 2 + nx // 2 + nx // 16 + 4, None),
+                (f"{lin}_quantize_w_16x16_per_tensor_rne", qw, 2 * nw * 2 + nw // 2 + nw // 256 + 4, None),
+                (f"{lin}_gemm_fprop_nvfp4", fprop, None, f),
+                (f"{lin}_quantize_dy_rowwise_per_token_sr", qd, nd * 2 + nd // 2 + nd // 16 + T * 4, None),
+                (f"{lin}_quantize_dy_colwise_per_tensor_sr", qdc, 2 * nd * 2 + nd // 2 + nd // 16 + 4, None),
+                (f"{lin}_gemm_dgrad_nvfp4", dgrad, None, f),
+                (f"{lin}_gemm_wgrad_nvfp4", wgrad, None, f)]
+    return out
 
 
-def stages(m):
-    """The four stages of the step, each a function of one buffer set: per-token
-    Q(X); 16x16 Q(W) with its dequantized copy DQ(W) written in the same pass;
-    FPROP; dequantized-backward DGRAD."""
-    def qx(s):
-        m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
-
-    def qdqw(s):
-        m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
-
-    def fprop(s):
-        m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
-                  m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
-                            gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
-
-    def dgrad(s):
-        m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
-                  m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
-                  out=s["dx"])
-    return [qx, qdqw, fprop, dgrad]
+def stage_entry(us, nbytes, flops):
+    d = {"us": round(us, 1)}
+    if nbytes is not None:
+        gbps = nbytes / (us * 1e-6) / 1e9
+        d.update(bytes=int(nbytes), GBps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
+    else:
+        tf = flops / (us * 1e-6) / 1e12
+        d.update(flops=int(flops), TFLOPs=round(tf, 1), frac_mfma=round(tf / PEAK_F16_TFLOPS, 4),
+                 frac_fp4_peak=round(tf / PEAK_FP4_TFLOPS, 4))
+    return d
 
 
-def step(m, s, ev=None):
-    """One step: the four stages in order.  ev (list of 5 events) brackets
-    each stage if given."""
-    for i, fn in enumerate(stages(m)):
-        if ev is not None:
-            ev[i].record()
-        fn(s)
-    if ev is not None:
-        ev[4].record()
+# ---------------------------------------------------------------- CPU baseline
 
-
-def batch_us(torch, fn, sets, spin, repeats):
-    """Mean time of one launch of `fn` over back-to-back launches on every
-    buffer set in turn: HIP events around each run of len(sets) launches,
-    each run behind a spin kernel so that the launches are all queued before
-    the first event fires."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(repeats)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        torch.cuda._sleep(spin)
-        a.record()
-        for s_ in sets:
-            fn(s_)
-        b.record()
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / (repeats * len(sets)) * 1e3
-
-
-SPIN_US = 100.0        # longer than the host takes to enqueue one step
-BATCH_SPIN_US = 300.0  # longer than it takes to enqueue one launch per buffer set
-
-
-def spin_cycles(torch, us):
-    """Argument of torch.cuda._sleep (a one-thread spin on the GPU clock
-    counter) that spins for about `us` microseconds, from one timed probe."""
-    probe = 1 << 20
-    torch.cuda._sleep(probe)                      # first launch outside the probe
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    torch.cuda._sleep(probe)
-    b.record()
-    torch.cuda.synchronize()
-    per_us = probe / max(a.elapsed_time(b) * 1e3, 1.0)
-    return max(int(per_us * us), 1)
-
-
-def cpu_baseline(data, min_seconds):
-    """The oracle, as it stands, on the same step: the full step (all tokens)
-    repeated until at least `min_seconds` of CPU time have passed; the sample
-    is bounded by that time."""
+def cpu_baseline(min_seconds, tokens=256, feats=512):
+    """The oracle, as it stands, on a bounded sample of the same step: both
+    linears restricted to their first `tokens` tokens and first `feats`
+    output features (all K), every stage as the GPU runs it (per-token RNE
+    and columnwise copies of X, 16x16 W, SR rowwise and columnwise dY, FPROP,
+    DGRAD and WGRAD as float64 dequantize-then-matmul), repeated until
+    `min_seconds` have passed.  Inputs are synth.mlp_tensor's tensors (the
+    GPU's inputs) copied to the host before the sample is cut."""
     import numpy as np
+    import torch
+    import synth
     from oracle import formats as F, nvfp4 as ON, gemm as G
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = len(os.sched_getaffinity(0))
-    xv = F.bf16_bits_to_f64(data["x"])
-    wv = F.bf16_bits_to_f64(data["w"])
-    dyv = F.bf16_bits_to_f64(data["dy"])
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    sample = []
+    for lin, xn, wn, dn, K, N in LINEARS:
+        x = synth.mlp_tensor(5, xn, "cuda")[:tokens]
+        w = synth.mlp_tensor(5, wn, "cuda")[:feats]
+        dy = synth.mlp_tensor(5, dn, "cuda")[:tokens, :feats]
+        sample.append((F.bf16_bits_to_f64(host(x)), F.bf16_bits_to_f64(host(w)), F.bf16_bits_to_f64(host(dy))))
+        del x, w, dy
+    torch.cuda.empty_cache()
+    flops = sum(3 * 2 * tokens * feats * K for _, _, _, _, K, _ in LINEARS)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        wc, wsb, wS = ON.quantize_tile16(wv)
-        w64 = ON.dequantize_f64(wc, wsb, wS, "16x16", "per_tensor")
-        wdq = ON.dequantize_bf16(wc, wsb, wS, "16x16", "per_tensor")
-        xc, xsb, xS = ON.quantize_rowwise(xv, "per_row")
-        x64 = ON.dequantize_f64(xc, xsb, xS, "1x16", "per_row")
-        y = F.bf16_rne(G.gemm_f64(x64, w64))
-        dx = F.bf16_rne(G.gemm_f64(dyv, F.bf16_bits_to_f64(wdq).T.copy()))
+        for xv, wv, dyv in sample:
+            xc, xs, xS = ON.quantize_rowwise(xv, "per_row")
+            xcc, xcs, xcS = ON.quantize_colwise(xv)
+            wc, ws, wS = ON.quantize_tile16(wv)
+            dc, ds, dS = ON.quantize_rowwise(dyv, "per_row", rnd="sr", seed=0, stream_id=0)
+            dcc, dcs, dcS = ON.quantize_colwise(dyv, rnd="sr", seed=0, stream_id=1)
+            x64 = ON.dequantize_f64(xc, xs, xS, "1x16", "per_row")
+            w64 = ON.dequantize_f64(wc, ws, wS, "16x16", "per_tensor")
+            d64 = ON.dequantize_f64(dc, ds, dS, "1x16", "per_row")
+            y = F.bf16_rne(G.gemm_f64(x64, w64))
+            dx = F.bf16_rne(G.gemm_f64(d64, w64.T.copy()))
+            dw = F.bf16_rne(G.gemm_f64(ON.dequantize_f64(dcc, dcs, dcS, "1x16", "per_tensor"),
+                                       ON.dequantize_f64(xcc, xcs, xcS, "1x16", "per_tensor")))
+            assert y.shape == (tokens, feats) and dx.shape == xv.shape and dw.shape == wv.shape
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
     t_step = el / reps
-    assert y.shape == (M, N) and dx.shape == (M, K)
-    return dict(value=(FLOPS_FPROP + FLOPS_DGRAD) / t_step / 1e12, unit="TFLOP/s",
-                cores=int(blas_threads), kind="oracle",
-                sample=(f"the full step ({M} tokens: Q(X), 16x16 Q(W), DQ(W), FPROP and DGRAD "
-                        f"as float64 dequantize-then-matmul) repeated {reps} times in {el:.1f} s; "
-                        f"quantizers single-threaded NumPy, matmuls on {blas_threads} BLAS threads"),
-                seconds_per_step=round(t_step, 3))
+    return dict(value=flops / t_step / 1e12, unit="TFLOP/s", cores=int(blas_threads), kind="oracle",
+                sample=(f"the step restricted to the first {tokens} tokens and {feats} output features of "
+                        f"each linear (all 16 stages, GEMMs as float64 dequantize-then-matmul), repeated "
+                        f"{reps} times in {el:.1f} s; quantizers single-threaded NumPy, matmuls on "
+                        f"{blas_threads} BLAS threads"),
+                seconds_per_sample_step=round(t_step, 3), sample_gemm_flops=int(flops))
+
+
+# ---------------------------------------------------------------- config 2
+
+def config2_step(m, torch, steps):
+    """The second configuration's NVFP4 linear (4096 tokens, 2048 -> 768):
+    per-token Q(X), 16x16 Q(W) with DQ(W) in the same pass, FPROP and the
+    dequantized-backward BF16 DGRAD, over ten rotating buffer sets (> 512 MB)."""
+    import numpy as np
+    import synth
+    M, K, N = 4096, 2048, 768
+    data = synth.config2()
+    dev = "cuda"
+
+    def bfd(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, w0, dy0 = bfd(data["x"]), bfd(data["w"]), bfd(data["dy"])
+    sets = []
+    for _ in range(10):
+        s = dict(x=x0.clone(), w=w0.clone(), dy=dy0.clone())
+        s.update(cx=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                 sx=torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                 Sx=torch.empty(M, dtype=torch.float32, device=dev),
+                 cw=torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                 sw=torch.empty((N // 16, K // 16), dtype=torch.uint8, device=dev),
+                 Sw=torch.empty(1, dtype=torch.float32, device=dev),
+                 y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 wdq=torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+                 dx=torch.empty((M, K), dtype=torch.bfloat16, device=dev))
+        sets.append(s)
+
+    def step(s):
+        m.nvfp4_quantize(s["x"], gs=m.GScale.PER_ROW, codes=s["cx"], block_scales=s["sx"], gscales=s["Sx"])
+        m.nvfp4_quantize_dq(s["w"], codes=s["cw"], block_scales=s["sw"], gscales=s["Sw"], dq=s["wdq"])
+        m.mx_gemm(m.Operand(m.Format.NVFP4, s["cx"], s["sx"], s["Sx"], gs=m.GScale.PER_ROW),
+                  m.Operand(m.Format.NVFP4, s["cw"], s["sw"], s["Sw"], block=m.Block.TILE,
+                            gs=m.GScale.PER_TENSOR), M, N, K, out=s["y"])
+        m.mx_gemm(m.Operand(m.Format.BF16, s["dy"], block=m.Block.NONE),
+                  m.Operand(m.Format.BF16, s["wdq"], block=m.Block.NONE, transposed=True), M, K, N,
+                  out=s["dx"])
+
+    for i in range(20):
+        step(sets[i % 10])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % 10])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    flops = 2 * (2 * M * N * K)
+    return {"workload": "nvfp4_linear_tokens4096_hidden2048_out768 (Q(X), Q(W)+DQ(W), FPROP, "
+                        "dequantized-backward DGRAD)",
+            "ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1), "steps": steps,
+            "launch": "eager, ten rotating buffer sets"}
 
 
 # ---------------------------------------------------------------- --rows
-PEAK_FP8_TFLOPS = 5000.0
 
-
-def _time_us(torch, fn, iters, warm_ms=30.0):
-    # warm up until about warm_ms of work has run (at least three calls): the
-    # clock drops while the host sets up a row, and a cold start reads slow
+def _time_rot(torch, fns, iters, warm_ms=30.0):
+    """Mean time of one launch, cycling over `fns` (one closure per buffer set,
+    so that reads come from HBM rather than the last-level cache): warm up for
+    about warm_ms (at least one pass over the sets), then HIP events around
+    `iters` launches."""
     t0, n = time.perf_counter(), 0
-    while n < 3 or (time.perf_counter() - t0) * 1e3 < warm_ms:
-        fn()
+    while n < max(3, len(fns)) or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        fns[n % len(fns)]()
         n += 1
         if n % 4 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(iters):
-        fn()
+    for i in range(iters):
+        fns[i % len(fns)]()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters * 1e3
+
+
+ROT_BYTES = 640 << 20     # buffer sets per row: enough copies of the inputs to exceed this
+
+
+def _copies(nbytes):
+    return max(2, -(-ROT_BYTES // max(int(nbytes), 1)))
 
 
 def rows_report():
     """Each hot-path row at the other configurations' shapes: quantizers and
     dequantizers against HBM bandwidth, GEMMs against their dtype's MFMA
     peak, the MoE stages of the Qwen3-30B-A3B-shaped layer.  One JSON line
-    per measurement (HIP events around repeated launches, inputs resident)."""
+    per measurement.  Every row cycles over copies of its inputs totalling
+    more than 640 MB, so that they come from HBM, not the 256 MB cache."""
     import numpy as np
     import torch
     import microscaling_quantization_block_amd as m
     import synth
     dev = "cuda"
 
-    def out(row, what, shape, us, nbytes=None, flops=None, peak=None, fp4=False):
-        d = dict(row=row, what=what, shape=shape, us=round(us, 2))
+    def out(row, what, shape, us, nbytes=None, flops=None, peak=None, fp4=False, sets=None):
+        d = dict(row=row, what=what, shape=shape, us=round(us, 2), buffer_sets=sets)
         if nbytes is not None:
             gbps = nbytes / (us * 1e-6) / 1e9
             d.update(bytes=int(nbytes), GBps=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
@@ -323,160 +380,168 @@ def rows_report():
                 d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
         print(json.dumps(d), flush=True)
 
+    def quant_row(row, what, x, call, nbytes, iters=10):
+        """call(x_copy) -> closure; x copies rotated."""
+        n = _copies(x.numel() * 2)
+        xs = [x] + [x.clone() for _ in range(n - 1)]
+        fns = [call(xi) for xi in xs]
+        out(row, what, list(x.shape), _time_rot(torch, fns, iters), nbytes=nbytes, sets=n)
+        del xs, fns
+
     # ---- Llama-3-8B-shaped dense MLP, NVFP4 (tokens 32768, hidden 4096, I 14336)
     T5, H5, I5 = 32768, 4096, 14336
-    x5 = synth.torch_normal_bf16((T5, H5), 1.0, 51, dev)
+    x5 = synth.mlp_tensor(5, "x", dev)
     n = T5 * H5
     cx, sx, Sx = m.nvfp4_quantize(x5)
-    out("a1-a3", "nvfp4 1x16 per-token RNE (X)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
-        x5, codes=cx, block_scales=sx, gscales=Sx), 10), nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
-    out("f2", "nvfp4 1x16 per-token RNE + Four-Over-Six (X)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
-        x5, rnd=m.Round.RNE_4OVER6, codes=cx, block_scales=sx, gscales=Sx), 10),
-        nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
-    dy5 = synth.torch_normal_bf16((T5, H5), 1e-3, 52, dev)          # down-projection output gradient
+    quant_row("a1-a3", "nvfp4 1x16 per-token RNE (X)", x5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, codes=cx, block_scales=sx, gscales=Sx), n * 2 + n // 2 + n // 16 + T5 * 4)
+    quant_row("f2", "nvfp4 1x16 per-token RNE + Four-Over-Six (X)", x5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, rnd=m.Round.RNE_4OVER6, codes=cx, block_scales=sx, gscales=Sx), n * 2 + n // 2 + n // 16 + T5 * 4)
+    dy5 = synth.mlp_tensor(5, "dy_dn", dev)                  # down-projection output gradient [T, 4096]
     cg, sg, Sg = m.nvfp4_quantize(dy5, rnd=m.Round.SR)
-    out("a1-a3", "nvfp4 1x16 per-token SR (dY)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
-        dy5, rnd=m.Round.SR, codes=cg, block_scales=sg, gscales=Sg), 10), nbytes=n * 2 + n // 2 + n // 16 + T5 * 4)
+    quant_row("a1-a3", "nvfp4 1x16 per-token SR (dY)", dy5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, rnd=m.Round.SR, codes=cg, block_scales=sg, gscales=Sg), n * 2 + n // 2 + n // 16 + T5 * 4)
     cgc, sgc, Sgc = m.nvfp4_quantize(dy5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1)
-    out("a1-a3", "nvfp4 16x1 columnwise per-tensor SR (dY^T, WGRAD)", [T5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
-        dy5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1, codes=cgc,
-        block_scales=sgc, gscales=Sgc), 10), nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
-    # the WGRAD inputs under the random Hadamard transform (two passes, both transforming)
-    out("f1", "nvfp4 16x1 columnwise + RHT per-tensor SR (dY^T, WGRAD)", [T5, H5], _time_us(
-        torch, lambda: m.nvfp4_quantize_rht(dy5, 0x6B2D, rnd=m.Round.SR, codes=cgc, block_scales=sgc,
-                                            gscales=Sgc), 10), nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
-    out("f1", "nvfp4 16x1 columnwise + RHT per-tensor RNE (X^T, WGRAD)", [T5, H5], _time_us(
-        torch, lambda: m.nvfp4_quantize_rht(x5, 0x6B2D, codes=cgc, block_scales=sgc, gscales=Sgc), 10),
-        nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
-    out("a1-a3", "nvfp4 16x1 columnwise per-tensor RNE (X^T, WGRAD)", [T5, H5], _time_us(
-        torch, lambda: m.nvfp4_quantize(x5, block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=cgc,
-                                        block_scales=sgc, gscales=Sgc), 10),
-        nbytes=2 * n * 2 + n // 2 + n // 16 + 4)
-    w5 = synth.torch_normal_bf16((2 * I5, H5), 0.02, 53, dev)       # gate_up weight [N, K]
+    quant_row("a1-a3", "nvfp4 16x1 columnwise per-tensor SR (dY^T, WGRAD)", dy5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1, codes=cgc,
+        block_scales=sgc, gscales=Sgc), 2 * n * 2 + n // 2 + n // 16 + 4)
+    quant_row("f1", "nvfp4 16x1 columnwise + RHT per-tensor SR (dY^T, WGRAD)", dy5, lambda xi: lambda:
+              m.nvfp4_quantize_rht(xi, 0x6B2D, rnd=m.Round.SR, codes=cgc, block_scales=sgc, gscales=Sgc),
+              2 * n * 2 + n // 2 + n // 16 + 4)
+    quant_row("f1", "nvfp4 16x1 columnwise + RHT per-tensor RNE (X^T, WGRAD)", x5, lambda xi: lambda:
+              m.nvfp4_quantize_rht(xi, 0x6B2D, codes=cgc, block_scales=sgc, gscales=Sgc),
+              2 * n * 2 + n // 2 + n // 16 + 4)
+    quant_row("a1-a3", "nvfp4 16x1 columnwise per-tensor RNE (X^T, WGRAD)", x5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=cgc, block_scales=sgc, gscales=Sgc),
+        2 * n * 2 + n // 2 + n // 16 + 4)
+    w5 = synth.mlp_tensor(5, "w_gu", dev)                    # gate_up weight [N, K]
     nw = w5.numel()
     cw, sw, Sw = m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
-    out("a1-a3", "nvfp4 16x16 per-tensor (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.nvfp4_quantize(
-        w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=cw, block_scales=sw, gscales=Sw), 10),
-        nbytes=2 * nw * 2 + nw // 2 + nw // 256 + 4)
-    out("f2", "nvfp4 16x16 per-tensor + Four-Over-Six (W_gate_up)", [2 * I5, H5], _time_us(
-        torch, lambda: m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
-                                        rnd=m.Round.RNE_4OVER6, codes=cw, block_scales=sw, gscales=Sw), 10),
-        nbytes=2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    quant_row("a1-a3", "nvfp4 16x16 per-tensor (W_gate_up)", w5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=cw, block_scales=sw, gscales=Sw),
+        2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    quant_row("f2", "nvfp4 16x16 per-tensor + Four-Over-Six (W_gate_up)", w5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, rnd=m.Round.RNE_4OVER6, codes=cw, block_scales=sw,
+        gscales=Sw), 2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    nsets = _copies(nw // 2)
+    cws = [cw] + [cw.clone() for _ in range(nsets - 1)]
     wdq = torch.empty_like(w5)
-    out("a4", "nvfp4 dequantize 16x16 -> bf16 (W_gate_up)", [2 * I5, H5], _time_us(torch, lambda: m.mx_dequantize(
-        m.Format.NVFP4, cw, sw, 2 * I5, H5, block=m.Block.TILE, gscales=Sw, gs=m.GScale.PER_TENSOR, out=wdq), 10),
-        nbytes=nw // 2 + nw // 256 + 4 + nw * 2)
-    y5 = torch.empty((T5, 2 * I5), dtype=torch.bfloat16, device=dev)
+    out("a4", "nvfp4 dequantize 16x16 -> bf16 (W_gate_up)", [2 * I5, H5], _time_rot(torch, [
+        (lambda c=c: m.mx_dequantize(m.Format.NVFP4, c, sw, 2 * I5, H5, block=m.Block.TILE, gscales=Sw,
+                                     gs=m.GScale.PER_TENSOR, out=wdq)) for c in cws], 10),
+        nbytes=nw // 2 + nw // 256 + 4 + nw * 2, sets=nsets)
+    del cws, wdq, w5
+    # GEMMs of the gate_up linear: operands rotated over copies of the codes
     f = 2.0 * T5 * 2 * I5 * H5
-    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
-    B = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
-    out("a6", "nvfp4 FPROP gate_up", [T5, 2 * I5, H5], _time_us(torch, lambda: m.mx_gemm(A, B, T5, 2 * I5, H5, out=y5), 3),
-        flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
-    del y5, wdq
-    dyg = synth.torch_normal_bf16((T5, 2 * I5), 1e-3, 54, dev)       # gate_up output gradient
+    y5 = torch.empty((T5, 2 * I5), dtype=torch.bfloat16, device=dev)
+    nsets = _copies(cx.numel() + cw.numel())
+    ops = [(cx.clone(), cw.clone()) for _ in range(nsets)]
+    out("a6", "nvfp4 FPROP gate_up", [T5, 2 * I5, H5], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.NVFP4, a, sx, Sx, gs=m.GScale.PER_ROW),
+                                    m.Operand(m.Format.NVFP4, b, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR),
+                                    T5, 2 * I5, H5, out=y5)) for a, b in ops], 4),
+        flops=f, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
+    del y5, ops
+    dyg = synth.mlp_tensor(5, "dy_gu", dev)                  # gate_up output gradient
     cdg, sdg, Sdg = m.nvfp4_quantize(dyg, rnd=m.Round.SR)
     dx5 = torch.empty((T5, H5), dtype=torch.bfloat16, device=dev)
-    Bt = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=True)
-    Ad = m.Operand(m.Format.NVFP4, cdg, sdg, Sdg, gs=m.GScale.PER_ROW)
-    out("a6", "nvfp4 DGRAD gate_up (16x16 weight read transposed)", [T5, H5, 2 * I5],
-        _time_us(torch, lambda: m.mx_gemm(Ad, Bt, T5, H5, 2 * I5, out=dx5), 3), flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
+    nsets = _copies(cdg.numel() + cw.numel())
+    ops = [(cdg.clone(), cw.clone()) for _ in range(nsets)]
+    out("a6", "nvfp4 DGRAD gate_up (16x16 weight read transposed)", [T5, H5, 2 * I5], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.NVFP4, a, sdg, Sdg, gs=m.GScale.PER_ROW),
+                                    m.Operand(m.Format.NVFP4, b, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
+                                              transposed=True), T5, H5, 2 * I5, out=dx5)) for a, b in ops], 4),
+        flops=f, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
+    del ops, dx5, cdg
     ccg, scg, Scg = m.nvfp4_quantize(dyg, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1)
     ccx, scx, Scx = m.nvfp4_quantize(x5, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    del dyg
     dw = torch.empty((2 * I5, H5), dtype=torch.bfloat16, device=dev)
-    Ag = m.Operand(m.Format.NVFP4, ccg, scg, Scg, gs=m.GScale.PER_TENSOR)
-    Bx = m.Operand(m.Format.NVFP4, ccx, scx, Scx, gs=m.GScale.PER_TENSOR)
-    out("a6", "nvfp4 WGRAD gate_up (columnwise copies)", [2 * I5, H5, T5],
-        _time_us(torch, lambda: m.mx_gemm(Ag, Bx, 2 * I5, H5, T5, out=dw), 3), flops=f, peak=PEAK_F16_TFLOPS, fp4=True)
-    del x5, dy5, w5, dyg, cdg, ccg, dx5, dw, cx, cg, cgc, cw, ccx
+    nsets = _copies(ccg.numel() + ccx.numel())
+    ops = [(ccg.clone(), ccx.clone()) for _ in range(nsets)]
+    out("a6", "nvfp4 WGRAD gate_up (columnwise copies)", [2 * I5, H5, T5], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.NVFP4, a, scg, Scg, gs=m.GScale.PER_TENSOR),
+                                    m.Operand(m.Format.NVFP4, b, scx, Scx, gs=m.GScale.PER_TENSOR),
+                                    2 * I5, H5, T5, out=dw)) for a, b in ops], 4),
+        flops=f, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
+    del x5, dy5, dw, ops, cx, cg, cgc, cw, ccx, ccg
     torch.cuda.empty_cache()
 
     # ---- Qwen3-8B-shaped dense MLP, MXFP8 (tokens 8192, hidden 4096, I 12288)
     T4, H4, I4 = 8192, 4096, 12288
-    x4 = synth.torch_normal_bf16((T4, H4), 1.0, 41, dev)
+    x4 = synth.mlp_tensor(4, "x", dev)
     n = T4 * H4
     mc, ms = m.mx_quantize(x4)
-    out("a1-a3", "mxfp8 1x32 (X)", [T4, H4], _time_us(torch, lambda: m.mx_quantize(x4, codes=mc, scales=ms), 10),
-        nbytes=n * 2 + n + n // 32)
+    quant_row("a1-a3", "mxfp8 1x32 (X)", x4, lambda xi: lambda: m.mx_quantize(xi, codes=mc, scales=ms),
+              n * 2 + n + n // 32)
     d4 = m.mx_quantize(x4, block=m.Block.DUAL)
-    out("a1-a3", "mxfp8 dual rowwise + columnwise (X)", [T4, H4], _time_us(torch, lambda: m.mx_quantize(
-        x4, block=m.Block.DUAL, codes=d4[0], scales=d4[1], codes_col=d4[2], scales_col=d4[3]), 10),
-        nbytes=n * 2 + 2 * n + 2 * (n // 32))
-    w4 = synth.torch_normal_bf16((2 * I4, H4), 0.02, 43, dev)
+    quant_row("a1-a3", "mxfp8 dual rowwise + columnwise (X)", x4, lambda xi: lambda: m.mx_quantize(
+        xi, block=m.Block.DUAL, codes=d4[0], scales=d4[1], codes_col=d4[2], scales_col=d4[3]),
+        n * 2 + 2 * n + 2 * (n // 32))
+    w4 = synth.mlp_tensor(4, "w_gu", dev)
     nw = w4.numel()
     wc, wsc = m.mx_quantize(w4, block=m.Block.TILE)
-    out("a1-a3", "mxfp8 32x32 (W_gate_up)", [2 * I4, H4], _time_us(torch, lambda: m.mx_quantize(
-        w4, block=m.Block.TILE, codes=wc, scales=wsc), 10), nbytes=nw * 2 + nw + nw // 1024)
+    quant_row("a1-a3", "mxfp8 32x32 (W_gate_up)", w4, lambda xi: lambda: m.mx_quantize(
+        xi, block=m.Block.TILE, codes=wc, scales=wsc), nw * 2 + nw + nw // 1024)
     wt4 = m.mx_quantize(w4, block=m.Block.TILE, transposed_copy=True)
-    out("a1-a3", "mxfp8 32x32 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(torch, lambda: m.mx_quantize(
-        w4, block=m.Block.TILE, codes=wt4[0], scales=wt4[1], codes_col=wt4[2], scales_col=wt4[3],
-        transposed_copy=True), 10), nbytes=nw * 2 + 2 * nw + 2 * (nw // 1024))
+    quant_row("a1-a3", "mxfp8 32x32 + transposed copy (W_gate_up)", w4, lambda xi: lambda: m.mx_quantize(
+        xi, block=m.Block.TILE, codes=wt4[0], scales=wt4[1], codes_col=wt4[2], scales_col=wt4[3],
+        transposed_copy=True), nw * 2 + 2 * nw + 2 * (nw // 1024))
+    nsets = _copies(mc.numel())
+    mcs = [mc] + [mc.clone() for _ in range(nsets - 1)]
     xo = torch.empty_like(x4)
-    out("a4", "mxfp8 dequantize 1x32 -> bf16 (X)", [T4, H4], _time_us(torch, lambda: m.mx_dequantize(
-        m.Format.MXFP8, mc, ms, T4, H4, out=xo), 10), nbytes=n + n // 32 + n * 2)
+    out("a4", "mxfp8 dequantize 1x32 -> bf16 (X)", [T4, H4], _time_rot(torch, [
+        (lambda c=c: m.mx_dequantize(m.Format.MXFP8, c, ms, T4, H4, out=xo)) for c in mcs], 10),
+        nbytes=n + n // 32 + n * 2, sets=nsets)
+    del mcs, xo
     y4 = torch.empty((T4, 2 * I4), dtype=torch.bfloat16, device=dev)
-    f = 2.0 * T4 * 2 * I4 * H4
-    A = m.Operand(m.Format.MXFP8, mc, ms)
-    B = m.Operand(m.Format.MXFP8, wc, wsc, block=m.Block.TILE)
-    out("a5", "mxfp8 FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(A, B, T4, 2 * I4, H4, out=y4), 5),
-        flops=f, peak=PEAK_FP8_TFLOPS)
-    dyg4 = synth.torch_normal_bf16((T4, 2 * I4), 1e-3, 44, dev)
-    dd = m.mx_quantize(dyg4, block=m.Block.DUAL)
     dx4 = torch.empty((T4, H4), dtype=torch.bfloat16, device=dev)
-    out("a5", "mxfp8 DGRAD gate_up (32x32 weight read transposed)", [T4, H4, 2 * I4], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(m.Format.MXFP8, dd[0], dd[1]), m.Operand(m.Format.MXFP8, wc, wsc, block=m.Block.TILE, transposed=True),
-        T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
-    out("a5", "mxfp8 DGRAD gate_up (transposed 32x32 copy)", [T4, H4, 2 * I4], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(m.Format.MXFP8, dd[0], dd[1]), m.Operand(m.Format.MXFP8, wt4[2], wt4[3], block=m.Block.TILE),
-        T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
     dw4 = torch.empty((2 * I4, H4), dtype=torch.bfloat16, device=dev)
-    out("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(m.Format.MXFP8, dd[2], dd[3]), m.Operand(m.Format.MXFP8, d4[2], d4[3]), 2 * I4, H4, T4, out=dw4), 5),
-        flops=f, peak=PEAK_FP8_TFLOPS)
-    # the same layer with DeepSeek-style blockwise FP8 (1x128 / 128x128, power-of-two scales)
-    b4 = m.fp8bw_quantize(x4, block=m.Block.DUAL)
-    out("f4", "fp8 blockwise dual 1x128 + 128x1 (X)", [T4, H4], _time_us(torch, lambda: m.fp8bw_quantize(
-        x4, block=m.Block.DUAL, codes=b4[0], scales=b4[1], codes_col=b4[2], scales_col=b4[3]), 10),
-        nbytes=n * 2 + 2 * n + 2 * (n // 128))
-    bw4 = m.fp8bw_quantize(w4, block=m.Block.TILE, transposed_copy=True)
-    out("f4", "fp8 blockwise 128x128 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(
-        torch, lambda: m.fp8bw_quantize(w4, block=m.Block.TILE, codes=bw4[0], scales=bw4[1], codes_col=bw4[2],
-                                        scales_col=bw4[3], transposed_copy=True), 10),
-        nbytes=nw * 2 + 2 * nw + 2 * (nw // 16384))
-    bd = m.fp8bw_quantize(dyg4, block=m.Block.DUAL)
-    F8 = m.Format.FP8_B128
-    out("f4", "fp8 blockwise FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(F8, b4[0], b4[1]), m.Operand(F8, bw4[0], bw4[1], block=m.Block.TILE), T4, 2 * I4, H4, out=y4), 5),
-        flops=f, peak=PEAK_FP8_TFLOPS)
-    out("f4", "fp8 blockwise DGRAD gate_up (transposed 128x128 copy)", [T4, H4, 2 * I4], _time_us(
-        torch, lambda: m.mx_gemm(m.Operand(F8, bd[0], bd[1]), m.Operand(F8, bw4[2], bw4[3], block=m.Block.TILE),
-                                 T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
-    out("f4", "fp8 blockwise WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(
-        torch, lambda: m.mx_gemm(m.Operand(F8, bd[2], bd[3]), m.Operand(F8, b4[2], b4[3]), 2 * I4, H4, T4, out=dw4),
-        5), flops=f, peak=PEAK_FP8_TFLOPS)
-    # and with binary32 block scales (the partial sums of each 128-K block
-    # scaled outside the MFMA, in a kernel of its own)
-    del bd
-    f4 = m.fp8bw_quantize_f32(x4, block=m.Block.DUAL)
-    out("f4", "fp8 blockwise f32-scale dual 1x128 + 128x1 (X)", [T4, H4], _time_us(torch, lambda: m.fp8bw_quantize_f32(
-        x4, block=m.Block.DUAL, codes=f4[0], scales=f4[1], codes_col=f4[2], scales_col=f4[3]), 10),
-        nbytes=n * 2 + 2 * n + 8 * (n // 128))
-    fw4 = m.fp8bw_quantize_f32(w4, block=m.Block.TILE, transposed_copy=True)
-    out("f4", "fp8 blockwise f32-scale 128x128 + transposed copy (W_gate_up)", [2 * I4, H4], _time_us(
-        torch, lambda: m.fp8bw_quantize_f32(w4, block=m.Block.TILE, codes=fw4[0], scales=fw4[1], codes_col=fw4[2],
-                                            scales_col=fw4[3], transposed_copy=True), 10),
-        nbytes=nw * 2 + 2 * nw + 8 * (nw // 16384))
-    fd = m.fp8bw_quantize_f32(dyg4, block=m.Block.DUAL)
-    F32S = m.Format.FP8_B128_F32
-    out("f4", "fp8 blockwise f32-scale FPROP gate_up", [T4, 2 * I4, H4], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(F32S, f4[0], f4[1]), m.Operand(F32S, fw4[0], fw4[1], block=m.Block.TILE), T4, 2 * I4, H4, out=y4),
-        5), flops=f, peak=PEAK_FP8_TFLOPS)
-    out("f4", "fp8 blockwise f32-scale DGRAD gate_up (transposed 128x128 copy)", [T4, H4, 2 * I4], _time_us(
-        torch, lambda: m.mx_gemm(m.Operand(F32S, fd[0], fd[1]), m.Operand(F32S, fw4[2], fw4[3], block=m.Block.TILE),
-                                 T4, H4, 2 * I4, out=dx4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
-    out("f4", "fp8 blockwise f32-scale WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], _time_us(
-        torch, lambda: m.mx_gemm(m.Operand(F32S, fd[2], fd[3]), m.Operand(F32S, f4[2], f4[3]), 2 * I4, H4, T4,
-                                 out=dw4), 5), flops=f, peak=PEAK_FP8_TFLOPS)
-    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4, xo, b4, bw4, f4, fw4, fd
+    f = 2.0 * T4 * 2 * I4 * H4
+    dyg4 = synth.mlp_tensor(4, "dy_gu", dev)
+    dd = m.mx_quantize(dyg4, block=m.Block.DUAL)
+
+    def gemm_row(row, what, shape, a_ops, b_ops, mnk, outt, fmt, peak, a_kw=None, b_kw=None, iters=5):
+        nsets = _copies(a_ops[0].numel() + b_ops[0].numel())
+        sets = [(a_ops[0].clone(), b_ops[0].clone()) for _ in range(nsets)]
+        fns = [(lambda a=a, b=b: m.mx_gemm(m.Operand(fmt, a, a_ops[1], **(a_kw or {})),
+                                           m.Operand(fmt, b, b_ops[1], **(b_kw or {})), *mnk, out=outt))
+               for a, b in sets]
+        out(row, what, shape, _time_rot(torch, fns, iters), flops=f, peak=peak, sets=nsets)
+
+    MX = m.Format.MXFP8
+    gemm_row("a5", "mxfp8 FPROP gate_up", [T4, 2 * I4, H4], (mc, ms), (wc, wsc), (T4, 2 * I4, H4), y4, MX,
+             PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
+    gemm_row("a5", "mxfp8 DGRAD gate_up (32x32 weight read transposed)", [T4, H4, 2 * I4], (dd[0], dd[1]),
+             (wc, wsc), (T4, H4, 2 * I4), dx4, MX, PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE, transposed=True))
+    gemm_row("a5", "mxfp8 DGRAD gate_up (transposed 32x32 copy)", [T4, H4, 2 * I4], (dd[0], dd[1]),
+             (wt4[2], wt4[3]), (T4, H4, 2 * I4), dx4, MX, PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
+    gemm_row("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], (dd[2], dd[3]), (d4[2], d4[3]),
+             (2 * I4, H4, T4), dw4, MX, PEAK_FP8_TFLOPS)
+    # the same layer with DeepSeek-style blockwise FP8 (1x128 / 128x128)
+    for f32s in (False, True):
+        q = m.fp8bw_quantize_f32 if f32s else m.fp8bw_quantize
+        F8 = m.Format.FP8_B128_F32 if f32s else m.Format.FP8_B128
+        tag = "f32-scale " if f32s else ""
+        sb = 4 if f32s else 1
+        b4 = q(x4, block=m.Block.DUAL)
+        quant_row("f4", f"fp8 blockwise {tag}dual 1x128 + 128x1 (X)", x4, lambda xi: lambda: q(
+            xi, block=m.Block.DUAL, codes=b4[0], scales=b4[1], codes_col=b4[2], scales_col=b4[3]),
+            n * 2 + 2 * n + 2 * sb * (n // 128))
+        bw4 = q(w4, block=m.Block.TILE, transposed_copy=True)
+        quant_row("f4", f"fp8 blockwise {tag}128x128 + transposed copy (W_gate_up)", w4, lambda xi: lambda: q(
+            xi, block=m.Block.TILE, codes=bw4[0], scales=bw4[1], codes_col=bw4[2], scales_col=bw4[3],
+            transposed_copy=True), nw * 2 + 2 * nw + 2 * sb * (nw // 16384))
+        bd = q(dyg4, block=m.Block.DUAL)
+        gemm_row("f4", f"fp8 blockwise {tag}FPROP gate_up", [T4, 2 * I4, H4], (b4[0], b4[1]), (bw4[0], bw4[1]),
+                 (T4, 2 * I4, H4), y4, F8, PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
+        gemm_row("f4", f"fp8 blockwise {tag}DGRAD gate_up (transposed 128x128 copy)", [T4, H4, 2 * I4],
+                 (bd[0], bd[1]), (bw4[2], bw4[3]), (T4, H4, 2 * I4), dx4, F8, PEAK_FP8_TFLOPS,
+                 b_kw=dict(block=m.Block.TILE))
+        gemm_row("f4", f"fp8 blockwise {tag}WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], (bd[2], bd[3]),
+                 (b4[2], b4[3]), (2 * I4, H4, T4), dw4, F8, PEAK_FP8_TFLOPS)
+        del b4, bw4, bd
+    del x4, w4, wt4, dyg4, dd, d4, y4, dx4, dw4
     torch.cuda.empty_cache()
 
     # ---- Qwen3-30B-A3B-shaped MoE layer, NVFP4 (tokens 8192, hidden 2048, 128 experts, I 768, top-8)
@@ -494,13 +559,13 @@ def rows_report():
     off = np.cumsum(off).astype(np.int32)
     Mr = len(row_token)
 
-    def bf(b):
+    def bfd(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x3 = bf(d["x"])
+    x3 = bfd(d["x"])
     cx3, sx3, Sx3 = m.nvfp4_quantize(x3)
-    wgu = bf(d["w_gu"].reshape(E * N2, H3)).view(E, N2, H3)
-    wdn = bf(d["w_dn"].reshape(E * H3, I3)).view(E, H3, I3)
+    wgu = bfd(d["w_gu"].reshape(E * N2, H3)).view(E, N2, H3)
+    wdn = bfd(d["w_dn"].reshape(E * H3, I3)).view(E, H3, I3)
     cgu = torch.empty((E, N2, H3 // 2), dtype=torch.uint8, device=dev)
     sgu = torch.empty((E, N2, H3 // 16), dtype=torch.uint8, device=dev)
     Sgu = torch.empty(E, dtype=torch.float32, device=dev)
@@ -512,47 +577,54 @@ def rows_report():
         m.nvfp4_quantize(wdn[e], gs=m.GScale.PER_TENSOR, codes=cdn[e], block_scales=sdn[e], gscales=Sdn[e:e + 1])
     off_d = torch.from_numpy(off).to(dev)
     idx_d = torch.from_numpy(row_token).to(dev)
+    nsets = _copies(cgu.numel())                                   # the 201 MB of NVFP4 gate_up weights
+    wsets = [cgu] + [cgu.clone() for _ in range(nsets - 1)]
     A = m.Operand(m.Format.NVFP4, cx3, sx3, Sx3, gs=m.GScale.PER_ROW)
-    Bgu = m.Operand(m.Format.NVFP4, cgu.view(E * N2, H3 // 2), sgu, Sgu, gs=m.GScale.PER_TENSOR)
     gu = torch.empty((Mr, N2), dtype=torch.bfloat16, device=dev)
-    out("a8", "MoE grouped gate_up (row gather, 128 experts)", [Mr, N2, H3], _time_us(torch, lambda: m.mx_gemm(
-        A, Bgu, Mr, N2, H3, out=gu, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T3), 10),
-        flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS)
+    Bs = [m.Operand(m.Format.NVFP4, w.view(E * N2, H3 // 2), sgu, Sgu, gs=m.GScale.PER_TENSOR) for w in wsets]
+    out("a8", "MoE grouped gate_up (row gather, 128 experts)", [Mr, N2, H3], _time_rot(torch, [
+        (lambda B=B: m.mx_gemm(A, B, Mr, N2, H3, out=gu, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T3))
+        for B in Bs], 10), flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS, sets=nsets)
     h = torch.empty((Mr, I3), dtype=torch.bfloat16, device=dev)
-    out("a8", "MoE SwiGLU", [Mr, I3], _time_us(torch, lambda: m.mx_swiglu(gu, I3, out=h), 10),
-        nbytes=Mr * N2 * 2 + Mr * I3 * 2)
+    nsets_g = _copies(gu.numel() * 2)
+    gus = [gu] + [gu.clone() for _ in range(nsets_g - 1)]
+    out("a8", "MoE SwiGLU", [Mr, I3], _time_rot(torch, [(lambda g=g: m.mx_swiglu(g, I3, out=h)) for g in gus], 10),
+        nbytes=Mr * N2 * 2 + Mr * I3 * 2, sets=nsets_g)
+    del gus
     hf = torch.empty_like(h)
-    out("f3", "MoE grouped gate_up with SwiGLU in the epilogue (writes H)", [Mr, N2, H3], _time_us(
-        torch, lambda: m.mx_gemm_swiglu(A, Bgu, Mr, I3, H3, out=hf, group_row_offsets=off_d, a_row_index=idx_d,
-                                        a_rows=T3), 10), flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS)
-    del hf
+    out("f3", "MoE grouped gate_up with SwiGLU in the epilogue (writes H)", [Mr, N2, H3], _time_rot(torch, [
+        (lambda B=B: m.mx_gemm_swiglu(A, B, Mr, I3, H3, out=hf, group_row_offsets=off_d, a_row_index=idx_d,
+                                      a_rows=T3)) for B in Bs], 10),
+        flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS, sets=nsets)
+    del hf, Bs, wsets
     ch, sh, Sh = m.nvfp4_quantize(h)
-    out("a8", "MoE per-token Q(H)", [Mr, I3], _time_us(torch, lambda: m.nvfp4_quantize(
-        h, codes=ch, block_scales=sh, gscales=Sh), 10), nbytes=Mr * I3 * 2 + Mr * I3 // 2 + Mr * I3 // 16 + Mr * 4)
-    Bdn = m.Operand(m.Format.NVFP4, cdn.view(E * H3, I3 // 2), sdn, Sdn, gs=m.GScale.PER_TENSOR)
+    quant_row("a8", "MoE per-token Q(H)", h, lambda xi: lambda: m.nvfp4_quantize(
+        xi, codes=ch, block_scales=sh, gscales=Sh), Mr * I3 * 2 + Mr * I3 // 2 + Mr * I3 // 16 + Mr * 4)
     y3 = torch.empty((Mr, H3), dtype=torch.bfloat16, device=dev)
-    out("a8", "MoE grouped down", [Mr, H3, I3], _time_us(torch, lambda: m.mx_gemm(
-        m.Operand(m.Format.NVFP4, ch, sh, Sh, gs=m.GScale.PER_ROW), Bdn, Mr, H3, I3, out=y3,
-        group_row_offsets=off_d), 10), flops=2.0 * Mr * H3 * I3, peak=PEAK_F16_TFLOPS)
+    nsets = _copies(cdn.numel())
+    Bs = [m.Operand(m.Format.NVFP4, w.view(E * H3, I3 // 2), sdn, Sdn, gs=m.GScale.PER_TENSOR)
+          for w in [cdn] + [cdn.clone() for _ in range(nsets - 1)]]
+    Ah = m.Operand(m.Format.NVFP4, ch, sh, Sh, gs=m.GScale.PER_ROW)
+    out("a8", "MoE grouped down", [Mr, H3, I3], _time_rot(torch, [
+        (lambda B=B: m.mx_gemm(Ah, B, Mr, H3, I3, out=y3, group_row_offsets=off_d)) for B in Bs], 10),
+        flops=2.0 * Mr * H3 * I3, peak=PEAK_F16_TFLOPS, sets=nsets)
 
+
+# ---------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time bound for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference", action="store_true",
-                    help="skip the device-copy and host-call probes (keeps traced runs to the step)")
-    ap.add_argument("--eager", action="store_true",
-                    help="time plain launches instead of HIP-graph replays")
-    ap.add_argument("--overlap", action="store_true",
-                    help="capture the weight path (Q(W), DQ(W)) on a second stream (measured "
-                         "slower on MI355X: 83.0 vs 73.7 us per step)")
+                    help="skip the device-copy and host-call probes and the second configuration "
+                         "(keeps traced and counted runs to the step)")
     ap.add_argument("--rows", action="store_true",
-                    help="only time each hot-path row at the other configurations' shapes "
+                    help="only time each hot-path row at the configurations' shapes "
                          "(one JSON line per measurement)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
@@ -566,7 +638,6 @@ def main():
 
     import torch
     import microscaling_quantization_block_amd as m
-    import synth
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
@@ -577,105 +648,55 @@ def main():
         rows_report()
         return
     m.lib()
-    log("generating synthetic inputs (seeded)")
-    data = synth.config2()
-    sets = make_sets(m, torch, data)
+    log("generating synthetic inputs (seeded, on the device)")
+    b = make_buffers(m, torch)
+    st = stages(m, b)
     torch.cuda.synchronize()
 
     log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(m, sets[i % SETS])
+    for _ in range(args.warmup):
+        for _, fn, _, _ in st:
+            fn()
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} eager steps")
+    # the timed steps: back-to-back launches on one stream (torch's current
+    # stream, which the library launches on), an event pair around every stage
+    log(f"timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(st) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(m, sets[i % SETS])
+        for j, (_, fn, _, _) in enumerate(st):
+            ev[i][j].record()
+            fn()
+        ev[i][-1].record()
     torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) / args.steps * 1e3
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    stage_us = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps * 1e3 for j in range(len(st))]
+    ms_events = sum(e[0].elapsed_time(e[-1]) for e in ev) / args.steps
 
-    # per-stage timing: HIP events around each stage, on the stream the
-    # library launches on (torch's current stream).  A spin kernel ahead of
-    # each step keeps the GPU busy while the host enqueues the four stages, so
-    # the stages run back to back and each event pair brackets its kernels,
-    # not the host's launch overhead.
-    spin = spin_cycles(torch, SPIN_US)
-    log(f"per-stage timing, {args.steps} eager steps, each behind a {SPIN_US:.0f} us spin")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        torch.cuda._sleep(spin)
-        step(m, sets[i % SETS], events[i])
-    torch.cuda.synchronize()
-
-    ms_graph = None
-    if not args.eager:
-        log("capturing one HIP graph per buffer set")
-        side = torch.cuda.Stream()              # default priority
-        graphs = []
-        for s_ in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                if args.overlap:
-                    step_concurrent(m, s_, side, torch)
-                else:
-                    step(m, s_)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % SETS].replay()
-        torch.cuda.synchronize()
-        log(f"timing {args.steps} graph-replayed steps")
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % SETS].replay()
-        torch.cuda.synchronize()
-        ms_graph = (time.perf_counter() - t0) / args.steps * 1e3
-    # the headline is the faster of the two ways of launching the same step
-    graph_wins = ms_graph is not None and ms_graph < ms_eager
-    ms_step = ms_graph if graph_wins else ms_eager
-
-    names = ["quantize_x_nvfp4_1x16_per_token", "quantize_dequantize_w_nvfp4_16x16_per_tensor",
-             "gemm_fprop_nvfp4", "gemm_dgrad_bf16_dequantized"]
-    stage_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j in range(4)]
-    kernels = {}
-    for j, nm in enumerate(names):
-        us = stage_ms[j] * 1e3
-        d = {"us": round(us, 2)}
-        if j in (0, 1):
-            b = [BYTES_QX, BYTES_QDQW][j]
-            gbps = b / (us * 1e-6) / 1e9
-            d.update(bytes=b, GBps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4))
-        else:
-            f = FLOPS_FPROP if j == 2 else FLOPS_DGRAD
-            tf = f / (us * 1e-6) / 1e12
-            d.update(flops=f, TFLOPs=round(tf, 1), frac_mfma=round(tf / PEAK_F16_TFLOPS, 4))
-            if j == 2:
-                d["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
-        kernels[nm] = d
-    # the dominant kernel, timed again over runs of back-to-back launches (an
-    # event pair around every launch adds its own packets to each figure)
-    dom = max(range(4), key=lambda j: stage_ms[j])
-    reps = max(args.steps // 10, 2)
-    log(f"roofline kernel {names[dom]}: {reps} runs of {SETS} back-to-back launches")
-    dom_us = batch_us(torch, stages(m)[dom], sets, spin_cycles(torch, BATCH_SPIN_US), reps)
-    how = (f"HIP events around {reps} runs of {SETS} back-to-back launches (one per buffer set), "
-           "each run behind a spin kernel")
-    if dom >= 2:
-        f = FLOPS_FPROP if dom == 2 else FLOPS_DGRAD
-        tf = f / (dom_us * 1e-6) / 1e12
-        roofline = dict(kernel=names[dom], bound="mfma", achieved=round(tf, 1), peak=PEAK_F16_TFLOPS,
-                        unit="TFLOP/s", frac=round(tf / PEAK_F16_TFLOPS, 4),
-                        traffic=measured_traffic(names[dom]), us_per_launch=round(dom_us, 2), timing=how)
+    kernels = {name: stage_entry(us, nb, fl) for (name, _, nb, fl), us in zip(st, stage_us)}
+    dom = max(range(len(st)), key=lambda j: stage_us[j])
+    name, _, nb, fl = st[dom]
+    us = stage_us[dom]
+    how = (f"HIP events on the launch stream around this stage in each of the {args.steps} timed steps "
+           "(one launch per step)")
+    if fl is not None:
+        tf = fl / (us * 1e-6) / 1e12
+        roofline = dict(kernel=name, bound="mfma", achieved=round(tf, 1), peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
+                        frac=round(tf / PEAK_F16_TFLOPS, 4), traffic=measured_traffic(name),
+                        peak_dtype="fp16 (the MFMA the exact NVFP4 dequant-on-load issues)",
+                        frac_fp4_peak=round(tf / PEAK_FP4_TFLOPS, 4), fp4_peak=PEAK_FP4_TFLOPS,
+                        us_per_launch=round(us, 1), timing=how)
     else:
-        b = [BYTES_QX, BYTES_QDQW][dom]
-        gbps = b / (dom_us * 1e-6) / 1e9
-        roofline = dict(kernel=names[dom], bound="hbm", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS,
-                        unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
-                        traffic=measured_traffic(names[dom]), us_per_launch=round(dom_us, 2), timing=how)
-    value = (FLOPS_FPROP + FLOPS_DGRAD) / (ms_step * 1e-3) / 1e12
-    qbytes = BYTES_QX + BYTES_QDQW
-    qus = (stage_ms[0] + stage_ms[1]) * 1e3
+        gbps = nb / (us * 1e-6) / 1e9
+        roofline = dict(kernel=name, bound="hbm", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                        frac=round(gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(name),
+                        us_per_launch=round(us, 1), timing=how)
+    value = STEP_FLOPS / (ms_step * 1e-3) / 1e12
+    q_us = sum(u for (_, _, nbx, _), u in zip(st, stage_us) if nbx is not None)
+    q_bytes = sum(nbx for (_, _, nbx, _) in st if nbx is not None)
+    g_us = sum(u for (_, _, _, flx), u in zip(st, stage_us) if flx is not None)
     out = {
         "metric": "MX/NVFP4 quantize GB/s + block-scaled GEMM TFLOP/s (% of gfx950 peak)",
         "value": round(value, 2),
@@ -683,30 +704,39 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "ms_per_step_eager": round(ms_eager, 4),
-        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
-        "launch": ("hip_graph" + (", weight path (Q(W) with DQ(W)) on a second stream" if args.overlap else "")
-                   if graph_wins else "eager (back-to-back launches on one stream)"),
+        "ms_per_step": round(ms_step, 3),
+        "ms_per_step_events": round(ms_events, 3),
+        "launch": "eager (back-to-back launches on one stream)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1/e4m3/fp32) -> f16 MFMA, f32 accumulate; bf16 MFMA for DGRAD",
+        "dtype": "nvfp4 (e2m1/e4m3/fp32) -> f16 MFMA, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": "nvfp4_linear_tokens4096_hidden2048_out768",
-                   "stages": "per-token Q(X) 4096x2048, 16x16 Q(W) 768x2048 with DQ(W) in the same pass, "
-                             "FPROP 4096x768x2048, dequantized-backward DGRAD 4096x2048x768",
-                   "tokens": M, "hidden": K, "out_features": N, "buffer_sets": SETS},
-        "quantize_GBps": round(qbytes / (qus * 1e-6) / 1e9, 1),
-        "gemm_TFLOPs": round((FLOPS_FPROP + FLOPS_DGRAD) / ((stage_ms[2] + stage_ms[3]) * 1e-3) / 1e12, 1),
+        "config": {"workload": "llama3_8b_mlp_nvfp4_tokens32768_hidden4096_inter14336",
+                   "stages": "per linear (gate_up 4096->28672, down 14336->4096): Q(X) rowwise per-token RNE, "
+                             "Q(X) columnwise per-tensor RNE, Q(W) 16x16 per-tensor RNE, FPROP, Q(dY) rowwise "
+                             "per-token SR, Q(dY) columnwise per-tensor SR, DGRAD (W read transposed), WGRAD",
+                   "tokens": T, "hidden": HID, "intermediate": INTER, "seq_len": 8192, "micro_batch": 4,
+                   "gemm_tflop_per_step": round(STEP_FLOPS / 1e12, 3)},
+        "quantize_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+        "quantize_frac_hbm": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "gemm_TFLOPs": round(STEP_FLOPS / (g_us * 1e-6) / 1e12, 1),
+        "gemm_frac_fp16_peak": round(STEP_FLOPS / (g_us * 1e-6) / 1e12 / PEAK_F16_TFLOPS, 4),
         "kernels": kernels,
         "roofline": roofline,
-        "measured_reference": None if args.no_reference else measured_reference(m, torch),
+        "config2": None,
+        "measured_reference": None,
         "cpu_baseline": None,
     }
+    del b, st, ev
+    torch.cuda.empty_cache()
+    if not args.no_reference:
+        log("second configuration (4096 tokens, 2048 -> 768), 200 steps")
+        out["config2"] = config2_step(m, torch, 200)
+        out["measured_reference"] = measured_reference(m, torch)
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
