@@ -7,11 +7,12 @@ intermediate 14336).  One step = one training pass over one batch of both
 linears, gate_up (4096 -> 28672) and down (14336 -> 4096), each:
    1. Q(X)  rowwise 1x16, per-token S, RNE            (FPROP operand)
    2. Q(X)  columnwise 16x1, per-tensor S, RNE        (WGRAD operand)
-   3. Q(W)  16x16 tiles, per-tensor S, RNE            (FPROP, and DGRAD read transposed)
+   3. Q(W)  16x16 tiles, per-tensor S, RNE, with the transposed copy (the 16x16
+            copy of W^T, written in the same pass)        (FPROP; DGRAD)
    4. FPROP  Y  = Q(X) Q(W)^T                         (BF16 out)
    5. Q(dY) rowwise 1x16, per-token S, stochastic rounding (seed 0, stream 0)
    6. Q(dY) columnwise 16x1, per-tensor S, stochastic rounding (stream 1)
-   7. DGRAD dX = Q(dY) Q(W)                           (the 16x16 copy read transposed)
+   7. DGRAD dX = Q(dY) Q(W)                           (the transposed 16x16 copy)
    8. WGRAD dW = Q(dY)^T Q(X)                         (the two columnwise copies)
 Each linear is measured on its own seeded inputs (the SwiGLU between them is
 not part of this path).  Inputs are seeded synthetic tensors (synth.mlp_tensor;
@@ -137,6 +138,7 @@ def make_buffers(m, torch):
         d.update(cx=u8(T, K // 2), sx=u8(T, K // 16), Sx=f32(T),
                  cxc=u8(K, T // 2), sxc=u8(K, T // 16), Sxc=f32(1),
                  cw=u8(N, K // 2), sw=u8(N // 16, K // 16), Sw=f32(1),
+                 cwt=u8(K, N // 2), swt=u8(K // 16, N // 16),
                  cd=u8(T, N // 2), sd=u8(T, N // 16), Sd=f32(T),
                  cdc=u8(N, T // 2), sdc=u8(N, T // 16), Sdc=f32(1),
                  y=bf(T, N), dx=bf(T, K), dw=bf(N, K))
@@ -159,8 +161,9 @@ def stages(m, b):
                              block_scales=d["sxc"], gscales=d["Sxc"])
 
         def qw(d=d):
-            m.nvfp4_quantize(d["w"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=d["cw"],
-                             block_scales=d["sw"], gscales=d["Sw"])
+            # the 16x16 copy and its transposed copy (DGRAD's B) from one pass
+            m.nvfp4_quantize_tile_t(d["w"], gs=m.GScale.PER_TENSOR, codes=d["cw"], block_scales=d["sw"],
+                                    codes_t=d["cwt"], block_scales_t=d["swt"], gscales=d["Sw"])
 
         def fprop(d=d, K=K, N=N):
             m.mx_gemm(m.Operand(NV, d["cx"], d["sx"], d["Sx"], gs=m.GScale.PER_ROW),
@@ -177,8 +180,8 @@ def stages(m, b):
 
         def dgrad(d=d, K=K, N=N):
             m.mx_gemm(m.Operand(NV, d["cd"], d["sd"], d["Sd"], gs=m.GScale.PER_ROW),
-                      m.Operand(NV, d["cw"], d["sw"], d["Sw"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
-                                transposed=True), T, K, N, out=d["dx"])
+                      m.Operand(NV, d["cwt"], d["swt"], d["Sw"], block=m.Block.TILE, gs=m.GScale.PER_TENSOR),
+                      T, K, N, out=d["dx"])
 
         def wgrad(d=d, K=K, N=N):
             m.mx_gemm(m.Operand(NV, d["cdc"], d["sdc"], d["Sdc"], gs=m.GScale.PER_TENSOR),
@@ -189,7 +192,8 @@ def stages(m, b):
         out += [(f"{lin}_quantize_x_rowwise_per_token_rne", qx, nx * 2 + nx // 2 + nx // 16 + T * 4, None),
                 # per-tensor copies read x twice (the amax pass, then the quantize pass)
                 (f"{lin}_quantize_x_colwise_per_tensor_rne", qxc, 2 * nx * 2 + nx // 2 + nx // 16 + 4, None),
-                (f"{lin}_quantize_w_16x16_per_tensor_rne", qw, 2 * nw * 2 + nw // 2 + nw // 256 + 4, None),
+                # ... and the weight (two reads) with its transposed copy
+                (f"{lin}_quantize_w_16x16_per_tensor_rne", qw, 2 * nw * 2 + 2 * (nw // 2 + nw // 256) + 4, None),
                 (f"{lin}_gemm_fprop_nvfp4", fprop, None, f),
                 (f"{lin}_quantize_dy_rowwise_per_token_sr", qd, nd * 2 + nd // 2 + nd // 16 + T * 4, None),
                 (f"{lin}_quantize_dy_colwise_per_tensor_sr", qdc, 2 * nd * 2 + nd // 2 + nd // 16 + 4, None),
@@ -714,8 +718,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3_8b_mlp_nvfp4_tokens32768_hidden4096_inter14336",
                    "stages": "per linear (gate_up 4096->28672, down 14336->4096): Q(X) rowwise per-token RNE, "
-                             "Q(X) columnwise per-tensor RNE, Q(W) 16x16 per-tensor RNE, FPROP, Q(dY) rowwise "
-                             "per-token SR, Q(dY) columnwise per-tensor SR, DGRAD (W read transposed), WGRAD",
+                             "Q(X) columnwise per-tensor RNE, Q(W) 16x16 per-tensor RNE with its transposed "
+                             "copy, FPROP, Q(dY) rowwise per-token SR, Q(dY) columnwise per-tensor SR, DGRAD "
+                             "(the transposed weight copy), WGRAD",
                    "tokens": T, "hidden": HID, "intermediate": INTER, "seq_len": 8192, "micro_batch": 4,
                    "gemm_tflop_per_step": round(STEP_FLOPS / 1e12, 3)},
         "quantize_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1),

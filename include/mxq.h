@@ -240,6 +240,28 @@ mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int6
                              void* stream);
 
 /*
+ * nvfp4_quantize_tile_t -- nvfp4_quantize with block TILE (16x16, the weight
+ * copy) that also writes, in the same pass, the transposed copy: the 16x16
+ * quantization of x^T.  A 16x16 tile's scale serves its rows and its columns,
+ * so FPROP and DGRAD share the tile scales ("Train models faster with JAX and
+ * MaxText using NVFP4 on NVIDIA Blackwell", section "NVFP4 pretraining
+ * recipe"), and the transposed copy is exactly the codes transposed and the
+ * scale grid transposed.  DGRAD (dX = dY W) then reads it row-major as B
+ * (transposed = 0) instead of transposing the weight on its way into the GEMM.
+ *   codes_t         [cols, rows/2] bytes (ld_codes_t_bytes), two codes per
+ *                   byte, even row index in the low nibble; 8-byte aligned,
+ *                   ld_codes_t_bytes % 8 == 0
+ *   block_scales_t  [cols/16, rows/16] E4M3, LINEAR
+ *   other arguments, shapes and errors as nvfp4_quantize with block TILE,
+ *   LINEAR scale layout (any rounding: the codes are transposed as encoded).
+ */
+mxq_status nvfp4_quantize_tile_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                 mxq_gscale gs, mxq_round rnd, uint64_t seed, uint32_t stream_id,
+                                 uint32_t tensor_tag, uint8_t* codes, int64_t ld_codes_bytes,
+                                 uint8_t* block_scales, uint8_t* codes_t, int64_t ld_codes_t_bytes,
+                                 uint8_t* block_scales_t, float* gscales, void* stream);
+
+/*
  * nvfp4_quantize_rht -- columnwise NVFP4 copy (COL, 16x1 blocks, stored
  * transposed) of the random Hadamard transform of x [rows, cols].  The NVFP4
  * pretraining recipe applies this transform to the two inputs of the WGRAD

@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
-           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+           "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
+           "fp8bw_quantize",
            "fp8bw_quantize_f32",
            "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
@@ -91,6 +92,8 @@ def lib():
     L.fp8bw_quantize_f32.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp, i64, vp, vp]
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i64, ci, ci, ci, u64, u32, u32, ci, vp, i64, vp, vp, vp]
     L.nvfp4_quantize_dq.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, vp, i64, vp]
+    L.nvfp4_quantize_tile_t.argtypes = [vp, i64, i64, i64, ci, ci, u64, u32, u32, vp, i64, vp, vp, i64, vp,
+                                        vp, vp]
     L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
                                      vp, vp]
     L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
@@ -100,7 +103,8 @@ def lib():
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
-    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+    for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
+           "fp8bw_quantize",
               "fp8bw_quantize_f32",
               "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
@@ -273,6 +277,31 @@ def nvfp4_quantize_dq(x, gs=GScale.PER_TENSOR, rnd=Round.RNE, codes=None, block_
                                    codes.stride(0), _ptr(block_scales), _ptr(gscales), _ptr(dq),
                                    dq.stride(0), _stream(stream)))
     return codes, block_scales, gscales, dq
+
+
+def nvfp4_quantize_tile_t(x, gs=GScale.PER_TENSOR, rnd=Round.RNE, seed=0, stream_id=0, tensor_tag=0,
+                          codes=None, block_scales=None, codes_t=None, block_scales_t=None, gscales=None,
+                          stream=None):
+    """16x16 NVFP4 copy of x and its transposed copy (the 16x16 copy of x^T)
+    in one pass.  Returns (codes, block scales, codes_t [cols, rows/2],
+    block_scales_t [cols/16, rows/16], S)."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    gs = GScale(gs)
+    codes = _u8((rows, cols // 2), dev) if codes is None else codes
+    block_scales = _u8((rows // 16, cols // 16), dev) if block_scales is None else block_scales
+    codes_t = _u8((cols, rows // 2), dev) if codes_t is None else codes_t
+    block_scales_t = _u8((cols // 16, rows // 16), dev) if block_scales_t is None else block_scales_t
+    if gscales is None:
+        if gs == GScale.GIVEN:
+            raise ValueError("gs=GIVEN needs gscales")
+        gscales = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib().nvfp4_quantize_tile_t(_ptr(x), rows, cols, x.stride(0), int(gs), int(rnd), int(seed),
+                                       int(stream_id), int(tensor_tag), _ptr(codes), codes.stride(0),
+                                       _ptr(block_scales), _ptr(codes_t), codes_t.stride(0),
+                                       _ptr(block_scales_t), _ptr(gscales), _stream(stream)))
+    return codes, block_scales, codes_t, block_scales_t, gscales
 
 
 def nvfp4_quantize_rht(x, sign_mask, gs=GScale.PER_TENSOR, rnd=Round.RNE, seed=0, stream_id=1,

@@ -160,12 +160,15 @@ mxq_status fp8bw_quantize_f32(const uint16_t* x, int64_t rows, int64_t cols, int
                     reinterpret_cast<uint8_t*>(scales_col), stream);
 }
 
-// dq != nullptr: also the dequantized BF16 copy (TILE only)
+// dq != nullptr: also the dequantized BF16 copy (TILE only); codes_t !=
+// nullptr: also the transposed copy (TILE only)
 static mxq_status nvfp4_quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                       mxq_block block, mxq_gscale gs, mxq_round rnd, uint64_t seed,
                                       uint32_t stream_id, uint32_t tensor_tag, mxq_scale_layout layout,
                                       uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
-                                      float* gscales, uint16_t* dq, int64_t ld_dq, void* stream) {
+                                      float* gscales, uint16_t* dq, int64_t ld_dq, void* stream,
+                                      uint8_t* codes_t = nullptr, int64_t ld_codes_t = 0,
+                                      uint8_t* block_scales_t = nullptr) {
   if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "nvfp4_quantize: negative size");
   if (block != MXQ_BLOCK_ROW && block != MXQ_BLOCK_COL && block != MXQ_BLOCK_TILE)
     return fail(block == MXQ_BLOCK_DUAL ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
@@ -208,6 +211,14 @@ static mxq_status nvfp4_quantize_impl(const uint16_t* x, int64_t rows, int64_t c
     if (ld_dq < cols) return fail(MXQ_EINVAL, "nvfp4_quantize_dq: ld_dq < cols");
     if (!aligned16(dq) || (ld_dq * 2) % 16) return fail(MXQ_EALIGN, "nvfp4_quantize_dq: dq 16-byte aligned, ld_dq*2 %% 16 == 0");
   }
+  if (codes_t) {
+    if (block != MXQ_BLOCK_TILE)
+      return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize_tile_t: the transposed copy is for TILE copies");
+    if (!block_scales_t) return fail(MXQ_EINVAL, "nvfp4_quantize_tile_t: block_scales_t is NULL");
+    if (ld_codes_t < rows / 2) return fail(MXQ_EINVAL, "nvfp4_quantize_tile_t: ld_codes_t_bytes < rows / 2");
+    if (((uintptr_t)codes_t & 7u) || ld_codes_t % 8)
+      return fail(MXQ_EALIGN, "nvfp4_quantize_tile_t: codes_t 8-byte aligned, ld_codes_t_bytes %% 8 == 0");
+  }
   hipStream_t st = S(stream);
   const int rm = rnd == MXQ_ROUND_SR ? 1 : rnd == MXQ_ROUND_RNE_4OVER6 ? 2 : 0;
   hipError_t e = hipSuccess;
@@ -223,11 +234,12 @@ static mxq_status nvfp4_quantize_impl(const uint16_t* x, int64_t rows, int64_t c
                               gmode, mfma, rm, seed, stream_id, tensor_tag, st);
   else if (block == MXQ_BLOCK_TILE)
     e = mxq::launch_nvfp4_tile16(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
-                                 gmode, rm, seed, stream_id, tensor_tag, dq, ld_dq, st);
+                                 gmode, rm, seed, stream_id, tensor_tag, dq, ld_dq, codes_t, ld_codes_t,
+                                 block_scales_t, st);
   else
     e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales,
                               gmode, mfma, rm == 1, false, 0u, seed, stream_id, tensor_tag, st);
-  return hip_status(e, dq ? "nvfp4_quantize_dq" : "nvfp4_quantize");
+  return hip_status(e, dq ? "nvfp4_quantize_dq" : codes_t ? "nvfp4_quantize_tile_t" : "nvfp4_quantize");
 }
 
 mxq_status nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -248,6 +260,17 @@ mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int6
     return fail(MXQ_EUNSUPPORTED, "nvfp4_quantize_dq: weights take RNE or RNE_4OVER6");
   return nvfp4_quantize_impl(x, rows, cols, ld_x, MXQ_BLOCK_TILE, gs, rnd, 0, 0, 0, MXQ_LAYOUT_LINEAR,
                              codes, ld_codes_bytes, block_scales, gscales, dq, ld_dq, stream);
+}
+
+mxq_status nvfp4_quantize_tile_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                 mxq_gscale gs, mxq_round rnd, uint64_t seed, uint32_t stream_id,
+                                 uint32_t tensor_tag, uint8_t* codes, int64_t ld_codes_bytes,
+                                 uint8_t* block_scales, uint8_t* codes_t, int64_t ld_codes_t_bytes,
+                                 uint8_t* block_scales_t, float* gscales, void* stream) {
+  if (!codes_t && rows > 0 && cols > 0) return fail(MXQ_EINVAL, "nvfp4_quantize_tile_t: codes_t is NULL");
+  return nvfp4_quantize_impl(x, rows, cols, ld_x, MXQ_BLOCK_TILE, gs, rnd, seed, stream_id, tensor_tag,
+                             MXQ_LAYOUT_LINEAR, codes, ld_codes_bytes, block_scales, gscales, nullptr, 0,
+                             stream, codes_t, ld_codes_t_bytes, block_scales_t);
 }
 
 mxq_status nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,

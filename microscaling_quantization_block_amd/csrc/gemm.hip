@@ -119,11 +119,12 @@ __device__ __forceinline__ void fp4x8_to_f16(uint32_t w, h2 s, uint32_t out[4]) 
   out[3] = __builtin_bit_cast(uint32_t, c3 * s);
 }
 
-// E4M3 byte SEL of v as FP16 (exact: every E4M3 value is an FP16 normal),
-// in both halves; the splat folds into the multiply's operand select.
-template <int SEL>
+// E4M3 byte 0 of v as FP16 (exact: every E4M3 value is an FP16 normal), in
+// both halves; the splat folds into the multiply's operand select.  The
+// packed conversion (bytes 0 and 1) needs no old value to merge into, unlike
+// the single-byte form, which costs a register clear per scale.
 __device__ __forceinline__ h2 e4m3_to_h2(uint32_t v) {
-  const h2 r = __builtin_amdgcn_cvt_scalef32_f16_fp8(h2{0, 0}, v, 1.0f, SEL, false);
+  const h2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
   return h2{r.x, r.x};
 }
 
@@ -494,9 +495,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       b_svoff[i] = in_range(b_ok[i], so & ~3u);
     }
   }
-  // transposed B: lane -> (k group, n group of 8), n fastest for coalesced row
-  // reads; K and N are multiples of the tile size, so a group is in or out whole.
-  const int bt_ng = lb0 / 8 + ltid % (LBN / 8), bt_kg = ltid / (LBN / 8);
+  // transposed B: lane -> (k group, n group of 8); K and N are multiples of
+  // the tile size, so a group is in or out whole.  Each lane's LDS stores are
+  // 8-byte runs (its K range of one column) in rows 8 apart, and a store
+  // instruction serves 16 lanes per cycle over 32 banks.  With the n groups
+  // fastest, those 16 lanes wrote 8 distinct 16-byte slots at the same half
+  // (two-way conflicts); instead each 16 lanes take 8 consecutive n groups
+  // (8 distinct slots under slot_of) times two k groups of opposite parity
+  // (the two halves of a slot): lane bits 0-2 pick the n group, bit 3 the k
+  // parity, the higher bits the rest.  The global loads of a wave still cover
+  // the same whole row segments.
+  constexpr int NG = LBN / 8;
+  const int bt_ng = lb0 / 8 + (NG % 16 == 0 ? (ltid & 7) + 8 * ((ltid >> 4) % (NG / 8)) : ltid % NG);
+  const int bt_kg = NG % 16 == 0 ? ((ltid >> 3) & 1) + 2 * ((ltid >> 4) / (NG / 8)) : ltid / NG;
   const bool bt_nok = n0 + bt_ng * 8 < N;
   constexpr int ESZ_BT = PATH == P_FP8 ? 1 : 2;                // bytes per value in LDS
   const uint32_t bt_off = (uint32_t)(bt_kg * R_BT) * brb +
@@ -743,7 +754,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // FP16 chunks (slots 2c, 2c + 1); otherwise the 16 bytes as they are.
   auto store_chunk = [&](uint8_t* row, int r, int c, const uint32_t* w, uint32_t sraw) {
     if (PATH == P_F16) {
-      const h2 sp = e4m3_to_h2<0>(sraw);
+      const h2 sp = e4m3_to_h2(sraw);
       uint32_t o0[4], o1[4];
       fp4x8_to_f16(w[0], sp, o0);
       fp4x8_to_f16(w[1], sp, o1);
@@ -771,7 +782,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     } else {
       const int kbyte = bt_kg * R_BT * ESZ_BT;         // this lane's K range: 4, 8 or 16 bytes
       if constexpr (PATH == P_F16) {
-        const h2 sp = e4m3_to_h2<0>(rbt_s >> bt_ssh);
+        const h2 sp = e4m3_to_h2(rbt_s >> bt_ssh);
         uint32_t hv[R_BT][4];
 #pragma unroll
         for (int q = 0; q < R_BT; ++q) fp4x8_to_f16(rbt[q][0], sp, hv[q]);
@@ -947,6 +958,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   uint8_t* const L0 = lds;
   uint8_t* const L1 = lds + SS * STAGE_BYTES;
   if constexpr (PP) {
+    // NVFP4: the group issuing MFMAs runs at a raised wave priority, so that
+    // on each SIMD its instructions win the issue arbitration against the
+    // other group's FP4 -> FP16 conversions and stores (a per-wave priority
+    // inside the kernel; measured on the config-5 GEMMs: FPROP and WGRAD
+    // 4-5% faster; the MXFP8 kernels, which convert nothing, 2% slower).
+    auto compute_pp = [&](const uint8_t* L, int set) {
+      if constexpr (PATH == P_F16) __builtin_amdgcn_s_setprio(1);
+      compute(L, set);
+      if constexpr (PATH == P_F16) __builtin_amdgcn_s_setprio(0);
+    };
     // prologue: both halves of stage 0 in buffer 0, stage 1 staged in
     // registers, MXFP8 scale sets 0 and 1 for stages 0 and 1
     load_stage(0, 0);
@@ -961,14 +982,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     // them into the idle buffer.
     if (grp == 0) {
       for (int kt = 0; kt < nk; kt += 2) {
-        compute(L0, 0);                      // C(kt)
+        compute_pp(L0, 0);                      // C(kt)
         __syncthreads();
         store_stage(L1, 0);                  // M: stage kt+1 -> buffer 1
         load_stage(kt + 2, 0);
         load_scales(kt + 2, 0);
         __syncthreads();
         if (kt + 1 < nk) {
-          compute(L1, 1);                    // C(kt+1)
+          compute_pp(L1, 1);                    // C(kt+1)
           __syncthreads();
           store_stage(L0, 0);                // M: stage kt+2 -> buffer 0
           load_stage(kt + 3, 0);
@@ -982,14 +1003,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         load_stage(kt + 2, 0);
         load_scales(kt + 1, 1);
         __syncthreads();
-        compute(L0, 0);                      // C(kt)
+        compute_pp(L0, 0);                      // C(kt)
         __syncthreads();
         if (kt + 1 < nk) {
           store_stage(L0, 0);                // M: stage kt+2 -> buffer 0
           load_stage(kt + 3, 0);
           load_scales(kt + 2, 0);
           __syncthreads();
-          compute(L1, 1);                    // C(kt+1)
+          compute_pp(L1, 1);                    // C(kt+1)
           __syncthreads();
         }
       }

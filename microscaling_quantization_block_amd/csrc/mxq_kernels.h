@@ -45,11 +45,14 @@ hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                             int gmode, bool mfma, int rm, uint64_t seed, uint32_t sid,
                             uint32_t tag, hipStream_t st);
-// dq (optional, else nullptr): the dequantized BF16 copy written in the same pass
+// dq (optional, else nullptr): the dequantized BF16 copy written in the same pass;
+// codes_t (optional, with bscales_t): the transposed copy [cols, rows/2] bytes,
+// scales [cols/16, rows/16]
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
                                float* gscales, int gmode, int rm, uint64_t seed, uint32_t sid,
-                               uint32_t tag, uint16_t* dq, int64_t ld_dq, hipStream_t st);
+                               uint32_t tag, uint16_t* dq, int64_t ld_dq, uint8_t* codes_t,
+                               int64_t ld_codes_t, uint8_t* bscales_t, hipStream_t st);
 // rht: the random Hadamard transform of each 16-row block before quantizing
 // (sign_mask bit i negates row i of the block)
 hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,

@@ -297,8 +297,83 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
   }
 }
 
-// Rows too long to keep in registers: two passes over the row (the second
-// read is served from cache).  One wave per row.
+// Long rows (more than 8192 values, up to 32768): one workgroup of 256
+// threads per row, the whole row held in registers, so the row is read from
+// HBM once.  Thread t owns chunks c = t + 256 i (8 values each, i < CPT); a
+// 16-value block is the chunk pair (c, c ^ 1), held by threads t and t ^ 1 of
+// one wave.  The token amax is a wave reduction, then one across the four
+// waves through LDS.  Same arithmetic as the one-wave kernels.
+template <int CPT, int RM>
+__global__ __launch_bounds__(256) void nvfp4_row_wg_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    float* __restrict__ gscales, int gmode, int mfma_layout,
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+  constexpr bool SR = RM == 1;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int cpr = (int)(cols >> 3);
+  const uint16_t* xr = x + row * ld_x;
+  uint4 v[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    v[i] = c < cpr ? *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t ab[CPT];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    ab[i] = amax8_bits(v[i]);
+    mb = umax(mb, ab[i]);
+  }
+  float S;
+  if (gmode == 0) {
+    __shared__ uint32_t wmax[4];
+    mb = wave_max_u32(mb);
+    if ((tid & 63) == 0) wmax[tid >> 6] = mb;
+    __syncthreads();
+    mb = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
+    S = __uint_as_float(mb) / 2688.0f;
+    if (tid == 0) gscales[row] = S;
+  } else {
+    S = tensor_scale(gscales, gmode);
+    if (gmode == 1 && tid == 0) gscales[0] = S;
+  }
+  const int64_t bpr = cols >> 4;
+  with_frame(S, [&](auto tiny) {
+    constexpr bool TINY = decltype(tiny)::value;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      // a block's two chunks are both in range or both out (cols % 16 == 0)
+      const float a = __uint_as_float(umax(ab[i], lane_xor_u32(ab[i], 1)));
+      uint32_t q, code;
+      if (RM == 2) {
+        const BlockScale b6 = nv_block_scale(a, S, 6.0f), b4 = nv_block_scale(a, S, 4.0f);
+        const Cand8 x6 = nv_cand8<TINY>(v[i], b6, S), x4 = nv_cand8<TINY>(v[i], b4, S);
+        const float e6 = x6.e + __uint_as_float(lane_xor_u32(__float_as_uint(x6.e), 1));
+        const float e4 = x4.e + __uint_as_float(lane_xor_u32(__float_as_uint(x4.e), 1));
+        const bool take4 = e4 < e6;
+        q = take4 ? x4.q : x6.q;
+        code = take4 ? b4.code : b6.code;
+      } else {
+        const BlockScale bs = nv_block_scale(a, S);
+        u32x4 dr = {0, 0, 0, 0};
+        if (SR && c < cpr) dr = philox_draws8((uint64_t)(row * cols + (int64_t)c * 8) >> 3, seed, stream_id, tensor_tag);
+        q = nv_encode8<SR, TINY>(v[i], bs.r, dr);
+        code = bs.code;
+      }
+      if (c < cpr) {
+        *reinterpret_cast<uint32_t*>(codes + row * ld_codes + (int64_t)c * 4) = q;
+        if ((c & 1) == 0) bscales[scale_offset(row, c >> 1, bpr, mfma_layout)] = (uint8_t)code;
+      }
+    }
+  });
+}
+
+// Rows longer than 32768 values: two passes over the row (the second read
+// mostly misses the cache).  One wave per row.
 template <int RM>
 __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -378,12 +453,19 @@ __device__ __forceinline__ uint4 nv_dq8(uint32_t q, float sb, float S) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int RM>
+// TT: also the transposed copy, the 16x16 quantization of x^T ([cols, rows]
+// codes, [cols/16, rows/16] scales): a 16x16 tile's scale serves its rows and
+// its columns, so that copy is these codes transposed.  Each wave stages its
+// 16 rows x 128 columns of codes in LDS and writes 128 transposed rows of 8
+// bytes (16 codes); the tile scales go to the transposed scale grid.  A DGRAD
+// reads it row-major instead of transposing the weight on the way into LDS.
+template <int RM, bool TT>
 __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, uint64_t seed, uint32_t stream_id,
-    uint32_t tensor_tag, uint16_t* __restrict__ dq, int64_t ld_dq) {
+    uint32_t tensor_tag, uint16_t* __restrict__ dq, int64_t ld_dq,
+    uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ bscales_t) {
   constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t cpr = cols >> 3;
@@ -403,6 +485,7 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
   mb = umax(mb, lane_xor_u32(mb, 32));
   const float S = tensor_scale(gscales, gmode);
   if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
+  uint32_t q[4], code;
   if (RM == 2) {
     // Four-Over-Six per tile.  Tree order: a lane's 8 columns of a row (three
     // levels), the row's other half in lane ^ 1, the lane's 4 rows (two
@@ -437,34 +520,59 @@ __global__ __launch_bounds__(256) void nvfp4_tile16_kernel(
     e6 = e6 + __uint_as_float(lane_xor_u32(__float_as_uint(e6), 32));
     e4 = e4 + __uint_as_float(lane_xor_u32(__float_as_uint(e4), 32));
     const bool take4 = e4 < e6;
-    if (!valid) return;
-    const float sbc = e4m3_to_f32(take4 ? b4.code : b6.code);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t q = take4 ? q4[i] : q6[i];
-      *reinterpret_cast<uint32_t*>(codes + (r0 + i) * ld_codes + j * 4) = q;
-      if (dq) *reinterpret_cast<uint4*>(dq + (r0 + i) * ld_dq + j * 8) = nv_dq8(q, sbc, S);
-    }
-    if ((j & 1) == 0 && rg == 0)
-      bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)(take4 ? b4.code : b6.code);
-    return;
+    for (int i = 0; i < 4; ++i) q[i] = take4 ? q4[i] : q6[i];
+    code = take4 ? b4.code : b6.code;
+  } else {
+    const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
+    with_frame(S, [&](auto tiny) {
+      constexpr bool TINY = decltype(tiny)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 dr = {0, 0, 0, 0};
+        if (SR) dr = philox_draws8((uint64_t)((r0 + i) * cols + jc * 8) >> 3, seed, stream_id, tensor_tag);
+        q[i] = nv_encode8<SR, TINY>(v[i], bs.r, dr);
+      }
+    });
+    code = bs.code;
   }
-  if (!valid) return;
-  const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
-  const float sbc = e4m3_to_f32(bs.code);
-  with_frame(S, [&](auto tiny) {
-    constexpr bool TINY = decltype(tiny)::value;
+  if (valid) {
+    const float sbc = e4m3_to_f32(code);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + i;
-      u32x4 dr = {0, 0, 0, 0};
-      if (SR) dr = philox_draws8((uint64_t)(r * cols + j * 8) >> 3, seed, stream_id, tensor_tag);
-      const uint32_t q = nv_encode8<SR, TINY>(v[i], bs.r, dr);
-      *reinterpret_cast<uint32_t*>(codes + r * ld_codes + j * 4) = q;
-      if (dq) *reinterpret_cast<uint4*>(dq + r * ld_dq + j * 8) = nv_dq8(q, sbc, S);
+      *reinterpret_cast<uint32_t*>(codes + (r0 + i) * ld_codes + j * 4) = q[i];
+      if (dq) *reinterpret_cast<uint4*>(dq + (r0 + i) * ld_dq + j * 8) = nv_dq8(q[i], sbc, S);
     }
-  });
-  if ((j & 1) == 0 && rg == 0) bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)bs.code;
+    if ((j & 1) == 0 && rg == 0) {
+      bscales[(int64_t)blockIdx.y * (cols >> 4) + (j >> 1)] = (uint8_t)code;
+      if (TT) bscales_t[(j >> 1) * (rows >> 4) + blockIdx.y] = (uint8_t)code;
+    }
+  }
+  if constexpr (TT) {
+    // stage: tw[wave][row r of the strip][chunk jj of the wave] = the 8 codes
+    // of row r, columns 8jj .. 8jj + 7 (no lane has returned: every lane of the
+    // workgroup reaches the barrier)
+    __shared__ uint32_t tw[4][16][16];
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tw[w][rg * 4 + i][lane & 15] = q[i];
+    __syncthreads();
+    // lane -> columns 2l, 2l + 1 of the wave's 128: chunk l / 4, codes k, k + 1
+    const int jl = lane >> 2, k = 2 * (lane & 3);
+    const int64_t jg = ((int64_t)blockIdx.x * 4 + w) * 16 + jl;
+    if (jg < cpr) {
+      uint32_t o[4] = {0, 0, 0, 0};              // column k: o[0..1], column k + 1: o[2..3]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t word = tw[w][r][jl];
+        o[r >> 3] |= ((word >> (4 * k)) & 0xFu) << (4 * (r & 7));
+        o[2 + (r >> 3)] |= ((word >> (4 * k + 4)) & 0xFu) << (4 * (r & 7));
+      }
+      const int64_t c0 = jg * 8 + k;
+      *reinterpret_cast<uint2*>(codes_t + c0 * ld_codes_t + (int64_t)blockIdx.y * 8) = make_uint2(o[0], o[1]);
+      *reinterpret_cast<uint2*>(codes_t + (c0 + 1) * ld_codes_t + (int64_t)blockIdx.y * 8) = make_uint2(o[2], o[3]);
+    }
+  }
 }
 
 // ------------------------------------------------------------ COL (16x1)
@@ -710,6 +818,13 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
   else if (bpr < 256) go(nvfp4_row_kernel<4, RM, false>);
   else if (bpr == 512) go(nvfp4_row_kernel<8, RM, true>);
   else if (bpr < 512) go(nvfp4_row_kernel<8, RM, false>);
+  else if (cols <= 16384 && rows <= 0x7FFFFFFF)
+    // a workgroup per row, the row in registers (8 chunks per thread)
+    hipLaunchKernelGGL((nvfp4_row_wg_kernel<8, RM>), dim3((unsigned)rows), block, 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
+  else if (cols <= 32768 && rows <= 0x7FFFFFFF)
+    hipLaunchKernelGGL((nvfp4_row_wg_kernel<16, RM>), dim3((unsigned)rows), block, 0, st, x, rows, cols, ld_x,
+                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
   else
     // one wave per row (no row loop in this kernel)
     hipLaunchKernelGGL(nvfp4_row_long_kernel<RM>, dim3((unsigned)((rows + 3) / 4)), block, 0, st, x,
@@ -735,17 +850,24 @@ hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales,
                                float* gscales, int gmode, int rm, uint64_t seed, uint32_t sid,
-                               uint32_t tag, uint16_t* dq, int64_t ld_dq, hipStream_t st) {
+                               uint32_t tag, uint16_t* dq, int64_t ld_dq, uint8_t* codes_t,
+                               int64_t ld_codes_t, uint8_t* bscales_t, hipStream_t st) {
   // four waves per workgroup, each 128 columns of a 16-row strip
   dim3 grid((unsigned)((cols / 8 + 63) / 64), (unsigned)(rows / 16));
   if (grid.y > 65535u) return hipErrorInvalidValue;      // more row strips than a grid holds
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
-                       gscales, gmode, seed, sid, tag, dq, ld_dq);
+                       gscales, gmode, seed, sid, tag, dq, ld_dq, codes_t, ld_codes_t, bscales_t);
   };
-  if (rm == 1) go(nvfp4_tile16_kernel<1>);
-  else if (rm == 2) go(nvfp4_tile16_kernel<2>);
-  else go(nvfp4_tile16_kernel<0>);
+  if (codes_t) {
+    if (rm == 1) go(nvfp4_tile16_kernel<1, true>);
+    else if (rm == 2) go(nvfp4_tile16_kernel<2, true>);
+    else go(nvfp4_tile16_kernel<0, true>);
+  } else {
+    if (rm == 1) go(nvfp4_tile16_kernel<1, false>);
+    else if (rm == 2) go(nvfp4_tile16_kernel<2, false>);
+    else go(nvfp4_tile16_kernel<0, false>);
+  }
   return hipGetLastError();
 }
 

@@ -79,8 +79,11 @@ def _task(t):
             else:                                      # element (r, c) of x: index r * cols + c
                 r16 = np.ascontiguousarray(_nv_r16(idx_r, idx_c, x.shape[1], p["seed"], p["stream"]).T)
         rc, rs = ON._rows_1x16(v, S_rows, p.get("rnd", "rne"), r16)
-    elif kind == "nv_tile":
-        v = F.bf16_bits_to_f64(np.asarray(x[a0:a1]))
+    elif kind in ("nv_tile", "nv_tile_t"):
+        if kind == "nv_tile":
+            v = F.bf16_bits_to_f64(np.asarray(x[a0:a1]))
+        else:                                          # the transposed copy: columns a0..a1 of x, as rows
+            v = F.bf16_bits_to_f64(np.ascontiguousarray(np.asarray(x[:, a0:a1]).T))
         rc, rs, _ = ON.quantize_tile16(v, "given", S_given=np.float32(p["S"]))
         gs = _load(p["scales"])[a0 // 16:a1 // 16]
         gc = _load(p["codes"])[a0:a1]

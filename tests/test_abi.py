@@ -15,6 +15,11 @@ HEADER = os.path.join(ROOT, "include", "mxq.h")
 
 def _lib():
     import microscaling_quantization_block_amd as m
+    # tests/test_host_sanitizers.py reruns this file against a host-only
+    # build of the C ABI under AddressSanitizer and UndefinedBehaviorSanitizer
+    sanitized = os.environ.get("MXQ_TEST_SANITIZED_LIBRARY")
+    if sanitized:
+        m.library_path = sanitized
     if not os.path.exists(m.library_path):
         pytest.skip("libmxq.so not built (run __graft_entry__.build())")
     return m, m.lib()
@@ -29,7 +34,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_rht", "fp8bw_quantize",
+    for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t",
+                 "nvfp4_quantize_rht", "fp8bw_quantize",
                  "fp8bw_quantize_f32", "mx_dequantize",
                  "mx_gemm", "mx_gemm_swiglu",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
@@ -106,6 +112,21 @@ def test_nvfp4_quantize_dq_rejects_bad_arguments():
     assert call(G.PER_TENSOR, dq=FAKE_ODD) == 3
     assert call(G.PER_TENSOR, rows=24) == 2
     assert call(G.PER_TENSOR, x=FAKE_ODD) == 3
+
+
+def test_nvfp4_quantize_tile_t_rejects_bad_arguments():
+    m, L = _lib()
+    G, R = m.GScale, m.Round
+    call = lambda gs=G.PER_TENSOR, ct=FAKE, ldt=16, st=FAKE, rows=32, cols=32, x=FAKE: \
+        L.nvfp4_quantize_tile_t(x, rows, cols, cols, gs, R.RNE, 0, 0, 0, FAKE, 16, FAKE, ct, ldt, st, FAKE, None)
+    assert call(ct=None) == 1
+    assert call(st=None) == 1
+    assert call(ldt=8) == 1                            # shorter than rows / 2
+    assert call(ldt=20) == 3                           # not a multiple of 8
+    assert call(ct=ctypes.c_void_p(0x10004)) == 3      # not 8-byte aligned
+    assert call(gs=G.PER_ROW) == 4                    # a tiled copy takes a per-tensor scale
+    assert call(rows=24) == 2
+    assert call(rows=0) == 0 and call(rows=0, ct=None) == 0
 
 
 def test_nvfp4_quantize_rht_rejects_bad_arguments():

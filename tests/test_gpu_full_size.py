@@ -129,7 +129,7 @@ def _nv_full_tasks(store, name, x_dev, copies):
             assert to_np(S)[0] == S_t, f"{name}: per-tensor S {to_np(S)[0]} != fl(amax / 2688) {S_t}"
             p["S"] = float(S_t)
         n, step, align = {"nv_row": (T, CHUNK // C, 1), "nv_col": (C, CHUNK // T, 1),
-                          "nv_tile": (T, CHUNK // C, 16)}[kind]
+                          "nv_tile": (T, CHUNK // C, 16), "nv_tile_t": (C, CHUNK // T, 16)}[kind]
         tasks += [(kind, f"{name}:{kind}:{rnd}:{a}", a, b, p) for a, b in P.chunks(n, max(step, 1), align)]
     return tasks
 
@@ -138,8 +138,9 @@ def _nv_copies(m, name, x):
     """The stored NVFP4 copies of one config-5 tensor, as the benchmark step
     makes them ("dy_gu:row" / "dy_gu:col": one of the two gradient copies)."""
     if name.startswith("w"):
-        c, s, S = m.nvfp4_quantize(x, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
-        return [("nv_tile", c, s, S, False, "rne", 0, 0)]
+        # the 16x16 copy and its transposed copy (the 16x16 copy of W^T)
+        c, s, ct, st, S = m.nvfp4_quantize_tile_t(x, gs=m.GScale.PER_TENSOR)
+        return [("nv_tile", c, s, S, False, "rne", 0, 0), ("nv_tile_t", ct, st, S, False, "rne", 0, 0)]
     if name.startswith("dy"):
         out = []
         if not name.endswith(":col"):
@@ -191,7 +192,7 @@ def test_config5_gemms_every_tile(lin):
     say(f"config 5 {lin}: quantizers")
     cx, sx, Sx = m.nvfp4_quantize(x)
     cxc, sxc, Sxc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
-    cw, sw, Sw = m.nvfp4_quantize(w, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    cw, sw, cwt, swt, Sw = m.nvfp4_quantize_tile_t(w, gs=m.GScale.PER_TENSOR)
     cd, sd, Sd = m.nvfp4_quantize(dy, rnd=m.Round.SR, seed=0, stream_id=0)
     cdc, sdc, Sdc = m.nvfp4_quantize(dy, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
                                      stream_id=1)
@@ -204,9 +205,13 @@ def test_config5_gemms_every_tile(lin):
                   m.Operand(NV, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR), T, N, K)
     _check(y, rT, rN, _nv_rows_dq(cx, sx, Sx, rT, True), _nv_tile_rows_dq(cw, sw, Sw, rN), f"{lin} FPROP")
     del y
-    say(f"config 5 {lin}: DGRAD {T}x{K}x{N}")
+    say(f"config 5 {lin}: DGRAD {T}x{K}x{N}, the transposed copy and the weight read transposed")
     dx = m.mx_gemm(m.Operand(NV, cd, sd, Sd, gs=m.GScale.PER_ROW),
-                   m.Operand(NV, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=True), T, K, N)
+                   m.Operand(NV, cwt, swt, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR), T, K, N)
+    dx2 = m.mx_gemm(m.Operand(NV, cd, sd, Sd, gs=m.GScale.PER_ROW),
+                    m.Operand(NV, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, transposed=True), T, K, N)
+    assert np.array_equal(from_dev_bf16(dx), from_dev_bf16(dx2))
+    del dx2
     _check(dx, rT, rK, _nv_rows_dq(cd, sd, Sd, rT, True), _nv_tile_cols_dq(cw, sw, Sw, rK), f"{lin} DGRAD")
     del dx
     say(f"config 5 {lin}: WGRAD {N}x{K}x{T}")

@@ -322,3 +322,55 @@ def test_swiglu_close_to_reference():
     ref = moe.swiglu_f64(gu, 96)
     a, b = F.bf16_bits_to_f64(h), F.bf16_bits_to_f64(ref)
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30)
+
+
+@pytest.mark.parametrize("cols", [8208, 16384, 20000, 32768, 32784])
+@pytest.mark.parametrize("rnd", ["rne", "sr", "4over6"])
+def test_nvfp4_long_rows(cols, rnd):
+    """Rows past 8192 values: one workgroup per row with the row in registers
+    (up to 16384 values with 8 chunks per thread, up to 32768 with 16, chunk
+    counts that do not fill the last pass), and the two-pass kernel beyond."""
+    m = mxq()
+    from oracle import four_over_six as O46
+    x = _edge_bf16(6, cols, 33, nvfp4=True)
+    v = _vals(x)
+    R = {"rne": m.Round.RNE, "sr": m.Round.SR, "4over6": m.Round.RNE_4OVER6}[rnd]
+    say(f"nvfp4 ROW long rows 6x{cols} {rnd}")
+    c, s, S = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW, rnd=R, seed=4)
+    if rnd == "4over6":
+        rc, rs, rS = O46.quantize_rowwise(v, "per_row")
+    else:
+        rc, rs, rS = ON.quantize_rowwise(v, "per_row", rnd=rnd, seed=4)
+    assert np.array_equal(to_np(S), rS)
+    assert np.array_equal(to_np(s), rs)
+    assert np.array_equal(to_np(c), rc)
+
+
+@pytest.mark.parametrize("shape,rnd", [((768, 2048), "rne"), ((48, 80), "rne"), ((64, 96), "sr"),
+                                       ((96, 1040), "4over6"), ((4096, 14336), "rne")])
+def test_nvfp4_tile16_with_transposed_copy(shape, rnd):
+    """The 16x16 copy and, from the same pass, the transposed copy: equal to
+    the oracle's 16x16 quantization of x^T (the codes and the tile scales
+    transposed), with the plain copy unchanged."""
+    m = mxq()
+    from oracle import four_over_six as O46
+    x = F.bf16_rne(np.random.default_rng(34).standard_normal(shape) * 0.02)
+    if shape[0] < 100:
+        x = _edge_bf16(*shape, 34, nvfp4=True)
+    v = _vals(x)
+    R = {"rne": m.Round.RNE, "sr": m.Round.SR, "4over6": m.Round.RNE_4OVER6}[rnd]
+    say(f"nvfp4 TILE with transposed copy {shape} {rnd}")
+    c, s, ct, st, S = m.nvfp4_quantize_tile_t(to_dev_bf16(x), rnd=R, seed=6)
+    if rnd == "4over6":
+        rc, rs, rS = O46.quantize_tile16(v)
+        tc, ts, tS = O46.quantize_tile16(np.ascontiguousarray(v.T))
+    else:
+        rc, rs, rS = ON.quantize_tile16(v, rnd=rnd, seed=6)
+        tc, ts, tS = ON.unpack_nibbles(rc).T, rs.T, rS          # the copy of x^T: transposed codes
+        tc = ON.pack_nibbles(np.ascontiguousarray(tc))
+        if rnd == "rne":
+            oc, os_, oS = ON.quantize_tile16(np.ascontiguousarray(v.T))
+            assert np.array_equal(oc, tc) and np.array_equal(os_, ts) and np.array_equal(oS, tS)
+    assert np.array_equal(to_np(S), rS)
+    assert np.array_equal(to_np(s), rs) and np.array_equal(to_np(c), rc)
+    assert np.array_equal(to_np(st), ts) and np.array_equal(to_np(ct), tc)
