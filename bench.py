@@ -5,13 +5,16 @@ Headline workload: the Llama-3-8B-shaped dense MLP in NVFP4 of the NVFP4
 pretraining pages (sequence 8192 x micro-batch 4 = 32768 tokens, hidden 4096,
 intermediate 14336).  One step = one training pass over one batch of both
 linears, gate_up (4096 -> 28672) and down (14336 -> 4096), each:
-   1. Q(X)  rowwise 1x16, per-token S, RNE            (FPROP operand)
-   2. Q(X)  columnwise 16x1, per-tensor S, RNE        (WGRAD operand)
+   1. Q(X)  rowwise 1x16, per-token S, RNE            (FPROP operand), then
+            columnwise 16x1, per-tensor S, RNE        (WGRAD operand); the
+            rowwise pass also accumulates the tensor amax
+   2. (the columnwise copy of step 1)
    3. Q(W)  16x16 tiles, per-tensor S, RNE, with the transposed copy (the 16x16
             copy of W^T, written in the same pass)        (FPROP; DGRAD)
    4. FPROP  Y  = Q(X) Q(W)^T                         (BF16 out)
-   5. Q(dY) rowwise 1x16, per-token S, stochastic rounding (seed 0, stream 0)
-   6. Q(dY) columnwise 16x1, per-tensor S, stochastic rounding (stream 1)
+   5. Q(dY) rowwise 1x16, per-token S, stochastic rounding (seed 0, stream 0), then
+            columnwise 16x1, per-tensor S, stochastic rounding (stream 1)
+   6. (the columnwise copy of step 5)
    7. DGRAD dX = Q(dY) Q(W)                           (the transposed 16x16 copy)
    8. WGRAD dW = Q(dY)^T Q(X)                         (the two columnwise copies)
 Each linear is measured on its own seeded inputs (the SwiGLU between them is
@@ -147,18 +150,17 @@ def make_buffers(m, torch):
 
 
 def stages(m, b):
-    """The step's 16 stages: (name, fn, algorithmic bytes or None, flops or None)."""
+    """The step's 12 stages: (name, fn, algorithmic bytes or None, flops or None)."""
     out = []
     NV = m.Format.NVFP4
     for lin, _, _, _, K, N in LINEARS:
         d = b[lin]
 
         def qx(d=d):
-            m.nvfp4_quantize(d["x"], gs=m.GScale.PER_ROW, codes=d["cx"], block_scales=d["sx"], gscales=d["Sx"])
-
-        def qxc(d=d):
-            m.nvfp4_quantize(d["x"], block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=d["cxc"],
-                             block_scales=d["sxc"], gscales=d["Sxc"])
+            # rowwise per-token copy, then the columnwise per-tensor copy (its
+            # tensor amax accumulated by the rowwise pass)
+            m.nvfp4_quantize_rowcol(d["x"], codes=d["cx"], block_scales=d["sx"], gscales=d["Sx"],
+                                    codes_col=d["cxc"], block_scales_col=d["sxc"], gscale_col=d["Sxc"])
 
         def qw(d=d):
             # the 16x16 copy and its transposed copy (DGRAD's B) from one pass
@@ -171,12 +173,9 @@ def stages(m, b):
                       T, N, K, out=d["y"])
 
         def qd(d=d):
-            m.nvfp4_quantize(d["dy"], gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=0, stream_id=0, codes=d["cd"],
-                             block_scales=d["sd"], gscales=d["Sd"])
-
-        def qdc(d=d):
-            m.nvfp4_quantize(d["dy"], block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
-                             stream_id=1, codes=d["cdc"], block_scales=d["sdc"], gscales=d["Sdc"])
+            m.nvfp4_quantize_rowcol(d["dy"], rnd=m.Round.SR, seed=0, codes=d["cd"], block_scales=d["sd"],
+                                    gscales=d["Sd"], codes_col=d["cdc"], block_scales_col=d["sdc"],
+                                    gscale_col=d["Sdc"])
 
         def dgrad(d=d, K=K, N=N):
             m.mx_gemm(m.Operand(NV, d["cd"], d["sd"], d["Sd"], gs=m.GScale.PER_ROW),
@@ -189,14 +188,14 @@ def stages(m, b):
 
         nx, nw, nd = T * K, N * K, T * N
         f = 2 * T * N * K
-        out += [(f"{lin}_quantize_x_rowwise_per_token_rne", qx, nx * 2 + nx // 2 + nx // 16 + T * 4, None),
-                # per-tensor copies read x twice (the amax pass, then the quantize pass)
-                (f"{lin}_quantize_x_colwise_per_tensor_rne", qxc, 2 * nx * 2 + nx // 2 + nx // 16 + 4, None),
+        # the two copies of x (and of dY) read it twice: the rowwise pass, which
+        # also accumulates the tensor amax, and the columnwise pass
+        rc = lambda n, rows: 2 * n * 2 + 2 * (n // 2 + n // 16) + rows * 4 + 4
+        out += [(f"{lin}_quantize_x_rowwise_and_colwise_rne", qx, rc(nx, T), None),
                 # ... and the weight (two reads) with its transposed copy
                 (f"{lin}_quantize_w_16x16_per_tensor_rne", qw, 2 * nw * 2 + 2 * (nw // 2 + nw // 256) + 4, None),
                 (f"{lin}_gemm_fprop_nvfp4", fprop, None, f),
-                (f"{lin}_quantize_dy_rowwise_per_token_sr", qd, nd * 2 + nd // 2 + nd // 16 + T * 4, None),
-                (f"{lin}_quantize_dy_colwise_per_tensor_sr", qdc, 2 * nd * 2 + nd // 2 + nd // 16 + 4, None),
+                (f"{lin}_quantize_dy_rowwise_and_colwise_sr", qd, rc(nd, T), None),
                 (f"{lin}_gemm_dgrad_nvfp4", dgrad, None, f),
                 (f"{lin}_gemm_wgrad_nvfp4", wgrad, None, f)]
     return out
@@ -418,12 +417,30 @@ def rows_report():
     quant_row("a1-a3", "nvfp4 16x1 columnwise per-tensor RNE (X^T, WGRAD)", x5, lambda xi: lambda: m.nvfp4_quantize(
         xi, block=m.Block.COL, gs=m.GScale.PER_TENSOR, codes=cgc, block_scales=sgc, gscales=Sgc),
         2 * n * 2 + n // 2 + n // 16 + 4)
+    rcb = 2 * n * 2 + 2 * (n // 2 + n // 16) + T5 * 4 + 4
+    quant_row("a1-a3", "nvfp4 rowwise per-token + columnwise per-tensor, two passes, RNE (X)", x5, lambda xi: lambda:
+              m.nvfp4_quantize_rowcol(xi, codes=cx, block_scales=sx, gscales=Sx, codes_col=cgc,
+                                      block_scales_col=sgc, gscale_col=Sgc), rcb)
+    quant_row("a1-a3", "nvfp4 rowwise per-token + columnwise per-tensor, two passes, SR (dY)", dy5, lambda xi: lambda:
+              m.nvfp4_quantize_rowcol(xi, rnd=m.Round.SR, codes=cg, block_scales=sg, gscales=Sg, codes_col=cgc,
+                                      block_scales_col=sgc, gscale_col=Sgc), rcb)
+    h5 = synth.mlp_tensor(5, "h", dev)
+    nh = h5.numel()
+    ch5, sh5, Sh5 = m.nvfp4_quantize(h5)
+    quant_row("a1-a3", "nvfp4 1x16 per-token RNE, rows of 14336 (H)", h5, lambda xi: lambda: m.nvfp4_quantize(
+        xi, codes=ch5, block_scales=sh5, gscales=Sh5), nh * 2 + nh // 2 + nh // 16 + T5 * 4)
+    del h5, ch5, sh5
     w5 = synth.mlp_tensor(5, "w_gu", dev)                    # gate_up weight [N, K]
     nw = w5.numel()
     cw, sw, Sw = m.nvfp4_quantize(w5, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
     quant_row("a1-a3", "nvfp4 16x16 per-tensor (W_gate_up)", w5, lambda xi: lambda: m.nvfp4_quantize(
         xi, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, codes=cw, block_scales=sw, gscales=Sw),
         2 * nw * 2 + nw // 2 + nw // 256 + 4)
+    cwt, swt = torch.empty((H5, I5), dtype=torch.uint8, device=dev), torch.empty((H5 // 16, 2 * I5 // 16), dtype=torch.uint8, device=dev)
+    quant_row("a1-a3", "nvfp4 16x16 per-tensor + transposed copy (W_gate_up)", w5, lambda xi: lambda:
+              m.nvfp4_quantize_tile_t(xi, codes=cw, block_scales=sw, codes_t=cwt, block_scales_t=swt, gscales=Sw),
+              2 * nw * 2 + 2 * (nw // 2 + nw // 256) + 4)
+    del cwt, swt
     quant_row("f2", "nvfp4 16x16 per-tensor + Four-Over-Six (W_gate_up)", w5, lambda xi: lambda: m.nvfp4_quantize(
         xi, block=m.Block.TILE, gs=m.GScale.PER_TENSOR, rnd=m.Round.RNE_4OVER6, codes=cw, block_scales=sw,
         gscales=Sw), 2 * nw * 2 + nw // 2 + nw // 256 + 4)
@@ -717,10 +734,10 @@ def main():
         "dtype": "nvfp4 (e2m1/e4m3/fp32) -> f16 MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "llama3_8b_mlp_nvfp4_tokens32768_hidden4096_inter14336",
-                   "stages": "per linear (gate_up 4096->28672, down 14336->4096): Q(X) rowwise per-token RNE, "
-                             "Q(X) columnwise per-tensor RNE, Q(W) 16x16 per-tensor RNE with its transposed "
-                             "copy, FPROP, Q(dY) rowwise per-token SR, Q(dY) columnwise per-tensor SR, DGRAD "
-                             "(the transposed weight copy), WGRAD",
+                   "stages": "per linear (gate_up 4096->28672, down 14336->4096): Q(X) rowwise per-token RNE "
+                             "and columnwise per-tensor RNE (two passes), Q(W) 16x16 per-tensor RNE with its "
+                             "transposed copy, FPROP, Q(dY) rowwise per-token SR and columnwise per-tensor SR "
+                             "(two passes), DGRAD (the transposed weight copy), WGRAD",
                    "tokens": T, "hidden": HID, "intermediate": INTER, "seq_len": 8192, "micro_batch": 4,
                    "gemm_tflop_per_step": round(STEP_FLOPS / 1e12, 3)},
         "quantize_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1),

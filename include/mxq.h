@@ -240,6 +240,37 @@ mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int6
                              void* stream);
 
 /*
+ * nvfp4_quantize_rowcol -- the two NVFP4 copies a linear layer needs of an
+ * activation or output gradient x [rows, cols]: the rowwise copy with a
+ * per-token second scale (FPROP / DGRAD operand) and the columnwise copy with
+ * a per-tensor second scale (WGRAD operand), both made from x ("Miles
+ * Blackwell RL ...", section "Um Quantizador Compartilhado É o Verdadeiro
+ * Mecanismo": rowwise and columnwise copies from the high-precision
+ * original; "Train models faster with JAX and MaxText using NVFP4 on NVIDIA
+ * Blackwell", section "NVFP4 pretraining recipe": 1x16 blocks, SR for
+ * gradients).  Exactly what nvfp4_quantize returns for block ROW with
+ * PER_ROW and for block COL with PER_TENSOR, but in two passes instead of
+ * three: the rowwise pass also accumulates the tensor amax that the
+ * columnwise copy's S needs.  Stochastic rounding (rnd SR) draws with
+ * stream_id 0 for the rowwise copy and 1 for the columnwise copy.
+ *   rnd        RNE or SR (RNE_4OVER6: MXQ_EUNSUPPORTED)
+ *   codes, block_scales, gscales        the ROW copy (codes [rows, cols/2]
+ *              bytes, scales per layout, gscales [rows])
+ *   codes_col, block_scales_col, gscale_col   the COL copy (codes [cols,
+ *              rows/2] bytes, scales [cols, rows/16] per layout, gscale_col
+ *              [1]; between the two passes gscale_col[0] holds the tagged
+ *              amax; it must not alias gscales)
+ *   layout     LINEAR or MFMA for both copies (MFMA: rows, cols % 64 == 0)
+ * Shapes: rows % 16 == 0, cols % 16 == 0.  Alignment as nvfp4_quantize for
+ * each copy.
+ */
+mxq_status nvfp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                 mxq_round rnd, uint64_t seed, uint32_t tensor_tag, mxq_scale_layout layout,
+                                 uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                                 float* gscales, uint8_t* codes_col, int64_t ld_codes_col_bytes,
+                                 uint8_t* block_scales_col, float* gscale_col, void* stream);
+
+/*
  * nvfp4_quantize_tile_t -- nvfp4_quantize with block TILE (16x16, the weight
  * copy) that also writes, in the same pass, the transposed copy: the 16x16
  * quantization of x^T.  A 16x16 tile's scale serves its rows and its columns,

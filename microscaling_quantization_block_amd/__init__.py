@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError",
            "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
-           "fp8bw_quantize",
+           "nvfp4_quantize_rowcol", "fp8bw_quantize",
            "fp8bw_quantize_f32",
            "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
@@ -94,6 +94,8 @@ def lib():
     L.nvfp4_quantize_dq.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp, vp, i64, vp]
     L.nvfp4_quantize_tile_t.argtypes = [vp, i64, i64, i64, ci, ci, u64, u32, u32, vp, i64, vp, vp, i64, vp,
                                         vp, vp]
+    L.nvfp4_quantize_rowcol.argtypes = [vp, i64, i64, i64, ci, u64, u32, ci, vp, i64, vp, vp, vp, i64, vp, vp,
+                                        vp]
     L.nvfp4_quantize_rht.argtypes = [vp, i64, i64, i64, u32, ci, ci, u64, u32, u32, ci, vp, i64, vp,
                                      vp, vp]
     L.mx_dequantize.argtypes = [ci, vp, i64, vp, vp, i64, i64, ci, ci, ci, vp, i64, vp]
@@ -104,7 +106,7 @@ def lib():
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
     for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
-           "fp8bw_quantize",
+           "nvfp4_quantize_rowcol", "fp8bw_quantize",
               "fp8bw_quantize_f32",
               "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
@@ -277,6 +279,28 @@ def nvfp4_quantize_dq(x, gs=GScale.PER_TENSOR, rnd=Round.RNE, codes=None, block_
                                    codes.stride(0), _ptr(block_scales), _ptr(gscales), _ptr(dq),
                                    dq.stride(0), _stream(stream)))
     return codes, block_scales, gscales, dq
+
+
+def nvfp4_quantize_rowcol(x, rnd=Round.RNE, seed=0, tensor_tag=0, layout=Layout.LINEAR, codes=None,
+                          block_scales=None, gscales=None, codes_col=None, block_scales_col=None,
+                          gscale_col=None, stream=None):
+    """The rowwise per-token copy and the columnwise per-tensor copy of x in
+    two passes (SR draws: stream 0 rowwise, 1 columnwise).  Returns (codes,
+    block scales, S [rows], codes_col [cols, rows/2], block scales_col, S_col [1])."""
+    _check_2d(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    codes = _u8((rows, cols // 2), dev) if codes is None else codes
+    block_scales = _u8((rows, cols // 16), dev) if block_scales is None else block_scales
+    gscales = torch.empty(rows, dtype=torch.float32, device=dev) if gscales is None else gscales
+    codes_col = _u8((cols, rows // 2), dev) if codes_col is None else codes_col
+    block_scales_col = _u8((cols, rows // 16), dev) if block_scales_col is None else block_scales_col
+    gscale_col = torch.empty(1, dtype=torch.float32, device=dev) if gscale_col is None else gscale_col
+    _check(lib().nvfp4_quantize_rowcol(_ptr(x), rows, cols, x.stride(0), int(rnd), int(seed), int(tensor_tag),
+                                       int(layout), _ptr(codes), codes.stride(0), _ptr(block_scales),
+                                       _ptr(gscales), _ptr(codes_col), codes_col.stride(0),
+                                       _ptr(block_scales_col), _ptr(gscale_col), _stream(stream)))
+    return codes, block_scales, gscales, codes_col, block_scales_col, gscale_col
 
 
 def nvfp4_quantize_tile_t(x, gs=GScale.PER_TENSOR, rnd=Round.RNE, seed=0, stream_id=0, tensor_tag=0,

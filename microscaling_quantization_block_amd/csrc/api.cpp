@@ -262,6 +262,49 @@ mxq_status nvfp4_quantize_dq(const uint16_t* x, int64_t rows, int64_t cols, int6
                              codes, ld_codes_bytes, block_scales, gscales, dq, ld_dq, stream);
 }
 
+mxq_status nvfp4_quantize_rowcol(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                 mxq_round rnd, uint64_t seed, uint32_t tensor_tag, mxq_scale_layout layout,
+                                 uint8_t* codes, int64_t ld_codes_bytes, uint8_t* block_scales,
+                                 float* gscales, uint8_t* codes_col, int64_t ld_codes_col_bytes,
+                                 uint8_t* block_scales_col, float* gscale_col, void* stream) {
+  const char* fn = "nvfp4_quantize_rowcol";
+  if (rows < 0 || cols < 0) return fail(MXQ_EINVAL, "%s: negative size", fn);
+  if (rnd != MXQ_ROUND_RNE && rnd != MXQ_ROUND_SR)
+    return fail(rnd == MXQ_ROUND_RNE_4OVER6 ? MXQ_EUNSUPPORTED : MXQ_EINVAL,
+                "%s: rounding must be RNE or SR (the columnwise copy takes no Four-Over-Six choice)", fn);
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA) return fail(MXQ_EINVAL, "%s: bad scale layout", fn);
+  if (rows == 0 || cols == 0) return ok();
+  if (!x || !codes || !block_scales || !gscales || !codes_col || !block_scales_col || !gscale_col)
+    return fail(MXQ_EINVAL, "%s: null pointer", fn);
+  if (cols % 16 || rows % 16)
+    return fail(MXQ_ESHAPE, "%s: rows and cols must be multiples of 16 (rows=%lld, cols=%lld)", fn,
+                (long long)rows, (long long)cols);
+  const bool mfma = layout == MXQ_LAYOUT_MFMA;
+  if (mfma && (rows % 64 || cols % 64))
+    return fail(MXQ_ESHAPE, "%s: the MFMA scale layout of both copies needs rows and cols multiples of 64", fn);
+  if (ld_x < cols || ld_codes_bytes < cols / 2 || ld_codes_col_bytes < rows / 2)
+    return fail(MXQ_EINVAL, "%s: leading dimension smaller than the row", fn);
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(codes_col) || (ld_x * 2) % 16 || ld_codes_bytes % 8 ||
+      ld_codes_col_bytes % 8 || ((uintptr_t)gscales & 3u) || ((uintptr_t)gscale_col & 3u))
+    return fail(MXQ_EALIGN, "%s: x/codes/codes_col 16-byte aligned, ld_x*2 %% 16 == 0, ld_codes_bytes and "
+                            "ld_codes_col_bytes %% 8 == 0, gscales and gscale_col 4-byte aligned", fn);
+  if (gscale_col == gscales || (gscale_col >= gscales && gscale_col < gscales + rows))
+    return fail(MXQ_EINVAL, "%s: gscale_col must not alias gscales", fn);
+  hipStream_t st = S(stream);
+  const int rm = rnd == MXQ_ROUND_SR ? 1 : 0;
+  uint32_t* acc = reinterpret_cast<uint32_t*>(gscale_col);
+  // the rowwise pass leaves the tagged tensor amax in gscale_col[0], which
+  // the columnwise pass turns into S (and stores back), as in PER_TENSOR mode
+  hipError_t e = mxq::launch_zero_u32(acc, st);
+  if (e == hipSuccess)
+    e = mxq::launch_nvfp4_row(x, rows, cols, ld_x, codes, ld_codes_bytes, block_scales, gscales, 0, mfma, rm,
+                              seed, 0, tensor_tag, st, acc);
+  if (e == hipSuccess)
+    e = mxq::launch_nvfp4_col(x, rows, cols, ld_x, codes_col, ld_codes_col_bytes, block_scales_col, gscale_col,
+                              1, mfma, rm == 1, false, 0u, seed, 1, tensor_tag, st);
+  return hip_status(e, fn);
+}
+
 mxq_status nvfp4_quantize_tile_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                  mxq_gscale gs, mxq_round rnd, uint64_t seed, uint32_t stream_id,
                                  uint32_t tensor_tag, uint8_t* codes, int64_t ld_codes_bytes,

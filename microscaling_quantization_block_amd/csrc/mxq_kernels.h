@@ -41,10 +41,13 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t co
 // gmode: 0 = per row (computed), 1 = per tensor (tagged amax in gscales[0]),
 // 2 = given (S in gscales[0]).  rm: 0 = RNE, 1 = stochastic rounding, 2 = RNE
 // with the Four-Over-Six block-scale choice.
+// amax_out (per-row mode only): also accumulate the tensor amax there as
+// tagged binary32 bits (the protocol of launch_nvfp4_tensor_scale; zero it first)
 hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                             int gmode, bool mfma, int rm, uint64_t seed, uint32_t sid,
-                            uint32_t tag, hipStream_t st);
+                            uint32_t tag, hipStream_t st, uint32_t* amax_out = nullptr);
+hipError_t launch_zero_u32(uint32_t* p, hipStream_t st);
 // dq (optional, else nullptr): the dequantized BF16 copy written in the same pass;
 // codes_t (optional, with bscales_t): the transposed copy [cols, rows/2] bytes,
 // scales [cols/16, rows/16]

@@ -201,6 +201,17 @@ __device__ __forceinline__ float tensor_scale(const float* g, int gmode) {
   return __uint_as_float(v);
 }
 
+// Tensor amax accumulated by a rowwise per-token pass (for the columnwise
+// per-tensor copy made next from the same tensor): the tagged binary32
+// magnitude bits of a row (or a wave's rows) go into *amax_out by an unsigned
+// atomic max, skipped when the value there is already at least as large (a
+// stale read only costs an extra atomic; the maximum is order-independent).
+__device__ __forceinline__ void amax_accumulate(uint32_t* amax_out, uint32_t bits) {
+  const uint32_t tagged = bits | 0x80000000u;
+  if (__hip_atomic_load(amax_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tagged)
+    atomicMax(amax_out, tagged);
+}
+
 // ------------------------------------------------------------ ROW (1x16)
 // gmode: 0 = per row (S computed here and stored), 1 = per tensor (tagged
 // amax, see tensor_scale), 2 = given.  One wave per row; lane owns the
@@ -211,12 +222,14 @@ __device__ __forceinline__ float tensor_scale(const float* g, int gmode) {
 // the last row (a valid address, never used).  FULL: every lane's blocks
 // exist (cols == 1024 BPT).
 // RM: 0 = RNE, 1 = stochastic rounding, 2 = RNE with the Four-Over-Six choice.
+// amax_out (per-token mode only, else nullptr): also accumulate the tensor
+// amax there (see amax_accumulate), one atomic per wave.
 template <int BPT, int RM, bool FULL>
 __global__ __launch_bounds__(256) void nvfp4_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
-    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag, uint32_t* __restrict__ amax_out) {
   constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t W = (int64_t)gridDim.x * 4;
@@ -238,6 +251,7 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
       v[k][1] = *reinterpret_cast<const uint4*>(xr + bb * 16 + 8);
     }
   };
+  uint32_t wave_amax = 0;
   auto process = [&](int64_t r, uint4 (*v)[2]) {
     uint32_t ab[BPT];
 #pragma unroll
@@ -250,7 +264,9 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
       uint32_t mb = ab[0];
 #pragma unroll
       for (int k = 1; k < BPT; ++k) mb = umax(mb, ab[k]);
-      S = __uint_as_float(wave_max_u32(mb)) / 2688.0f;
+      mb = wave_max_u32(mb);
+      wave_amax = umax(wave_amax, mb);
+      S = __uint_as_float(mb) / 2688.0f;
       if (lane == 0) gscales[r] = S;
     }
     with_frame(S, [&](auto tiny) {
@@ -295,6 +311,7 @@ __global__ __launch_bounds__(256) void nvfp4_row_kernel(
     row += W;
     if (row >= rows) break;
   }
+  if (amax_out && lane == 0) amax_accumulate(amax_out, wave_amax);
 }
 
 // Long rows (more than 8192 values, up to 32768): one workgroup of 256
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(256) void nvfp4_row_wg_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
-    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag, uint32_t* __restrict__ amax_out) {
   constexpr bool SR = RM == 1;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -335,7 +352,10 @@ __global__ __launch_bounds__(256) void nvfp4_row_wg_kernel(
     __syncthreads();
     mb = umax(umax(wmax[0], wmax[1]), umax(wmax[2], wmax[3]));
     S = __uint_as_float(mb) / 2688.0f;
-    if (tid == 0) gscales[row] = S;
+    if (tid == 0) {
+      gscales[row] = S;
+      if (amax_out) amax_accumulate(amax_out, mb);
+    }
   } else {
     S = tensor_scale(gscales, gmode);
     if (gmode == 1 && tid == 0) gscales[0] = S;
@@ -379,7 +399,7 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout,
-    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag) {
+    uint64_t seed, uint32_t stream_id, uint32_t tensor_tag, uint32_t* __restrict__ amax_out) {
   constexpr bool SR = RM == 1;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -394,7 +414,10 @@ __global__ __launch_bounds__(256) void nvfp4_row_long_kernel(
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) mb = umax(mb, lane_xor_u32(mb, o));
     S = __uint_as_float(mb) / 2688.0f;
-    if (lane == 0) gscales[row] = S;
+    if (lane == 0) {
+      gscales[row] = S;
+      if (amax_out) amax_accumulate(amax_out, mb);
+    }
   } else {
     S = tensor_scale(gscales, gmode);
     if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
@@ -779,6 +802,11 @@ __global__ __launch_bounds__(256) void nv_amax_rht_kernel(const uint16_t* __rest
 }
 
 // ------------------------------------------------------------ launchers
+hipError_t launch_zero_u32(uint32_t* p, hipStream_t st) {
+  hipLaunchKernelGGL(nv_zero_u32, dim3(1), dim3(1), 0, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                      float* gscale, hipStream_t st) {
   uint32_t* bits = reinterpret_cast<uint32_t*>(gscale);
@@ -797,7 +825,7 @@ template <int RM>
 static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                                int gmode, bool mfma, uint64_t seed, uint32_t sid, uint32_t tag,
-                               hipStream_t st) {
+                               uint32_t* amax_out, hipStream_t st) {
   // at most 2048 workgroups of 4 waves (32 waves per CU, 8 per SIMD: the
   // stochastic-rounding encode is VALU work that needs them to hide its
   // dependent chains, and short rows need them to keep loads in flight); a
@@ -808,7 +836,7 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
   const int64_t bpr = cols / 16;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, st, x, rows, cols, ld_x, codes, ld_codes, bscales,
-                       gscales, gmode, (int)mfma, seed, sid, tag);
+                       gscales, gmode, (int)mfma, seed, sid, tag, amax_out);
   };
   if (bpr == 64) go(nvfp4_row_kernel<1, RM, true>);
   else if (bpr < 64) go(nvfp4_row_kernel<1, RM, false>);
@@ -821,30 +849,30 @@ static hipError_t row_dispatch(const uint16_t* x, int64_t rows, int64_t cols, in
   else if (cols <= 16384 && rows <= 0x7FFFFFFF)
     // a workgroup per row, the row in registers (8 chunks per thread)
     hipLaunchKernelGGL((nvfp4_row_wg_kernel<8, RM>), dim3((unsigned)rows), block, 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
+                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag, amax_out);
   else if (cols <= 32768 && rows <= 0x7FFFFFFF)
     hipLaunchKernelGGL((nvfp4_row_wg_kernel<16, RM>), dim3((unsigned)rows), block, 0, st, x, rows, cols, ld_x,
-                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag);
+                       codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag, amax_out);
   else
     // one wave per row (no row loop in this kernel)
     hipLaunchKernelGGL(nvfp4_row_long_kernel<RM>, dim3((unsigned)((rows + 3) / 4)), block, 0, st, x,
                        rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed,
-                       sid, tag);
+                       sid, tag, amax_out);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* codes, int64_t ld_codes, uint8_t* bscales, float* gscales,
                             int gmode, bool mfma, int rm, uint64_t seed, uint32_t sid,
-                            uint32_t tag, hipStream_t st) {
+                            uint32_t tag, hipStream_t st, uint32_t* amax_out) {
   if (rm == 1)
     return row_dispatch<1>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma,
-                           seed, sid, tag, st);
+                           seed, sid, tag, amax_out, st);
   if (rm == 2)
     return row_dispatch<2>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma,
-                           seed, sid, tag, st);
+                           seed, sid, tag, amax_out, st);
   return row_dispatch<0>(x, rows, cols, ld_x, codes, ld_codes, bscales, gscales, gmode, mfma, seed,
-                         sid, tag, st);
+                         sid, tag, amax_out, st);
 }
 
 hipError_t launch_nvfp4_tile16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,

@@ -16,9 +16,10 @@ hipError_t launch_nvfp4_tensor_scale(const uint16_t*, int64_t, int64_t, int64_t,
   return hipErrorNoDevice;
 }
 hipError_t launch_nvfp4_row(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, int64_t, uint8_t*,
-                            float*, int, bool, int, uint64_t, uint32_t, uint32_t, hipStream_t) {
+                            float*, int, bool, int, uint64_t, uint32_t, uint32_t, hipStream_t, uint32_t*) {
   return hipErrorNoDevice;
 }
+hipError_t launch_zero_u32(uint32_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_nvfp4_tile16(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, int64_t, uint8_t*,
                                float*, int, int, uint64_t, uint32_t, uint32_t, uint16_t*, int64_t,
                                uint8_t*, int64_t, uint8_t*, hipStream_t) {

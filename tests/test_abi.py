@@ -35,7 +35,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t",
-                 "nvfp4_quantize_rht", "fp8bw_quantize",
+                 "nvfp4_quantize_rht", "nvfp4_quantize_rowcol", "fp8bw_quantize",
                  "fp8bw_quantize_f32", "mx_dequantize",
                  "mx_gemm", "mx_gemm_swiglu",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
@@ -127,6 +127,24 @@ def test_nvfp4_quantize_tile_t_rejects_bad_arguments():
     assert call(gs=G.PER_ROW) == 4                    # a tiled copy takes a per-tensor scale
     assert call(rows=24) == 2
     assert call(rows=0) == 0 and call(rows=0, ct=None) == 0
+
+
+def test_nvfp4_quantize_rowcol_rejects_bad_arguments():
+    m, L = _lib()
+    R, Lay = m.Round, m.Layout
+    G1, G2 = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+    call = lambda rows=32, cols=32, rnd=R.RNE, lay=Lay.LINEAR, ldc=16, ldcc=16, g=G1, gc=G2, x=FAKE, cc=FAKE: \
+        L.nvfp4_quantize_rowcol(x, rows, cols, cols, rnd, 0, 0, lay, FAKE, ldc, FAKE, g, cc, ldcc, FAKE, gc, None)
+    assert call(rnd=R.RNE_4OVER6) == 4
+    assert call(rnd=7) == 1
+    assert call(lay=5) == 1
+    assert call(cc=None) == 1 and call(gc=None) == 1
+    assert call(rows=24) == 2 and call(cols=40) == 2
+    assert call(lay=Lay.MFMA) == 2                    # MFMA layout of both copies: multiples of 64
+    assert call(ldcc=8) == 1                           # shorter than rows / 2
+    assert call(x=FAKE_ODD) == 3 and call(ldcc=20) == 3
+    assert call(gc=G1) == 1                            # the tensor scale must not alias the row scales
+    assert call(rows=0) == 0
 
 
 def test_nvfp4_quantize_rht_rejects_bad_arguments():

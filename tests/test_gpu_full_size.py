@@ -141,19 +141,17 @@ def _nv_copies(m, name, x):
         # the 16x16 copy and its transposed copy (the 16x16 copy of W^T)
         c, s, ct, st, S = m.nvfp4_quantize_tile_t(x, gs=m.GScale.PER_TENSOR)
         return [("nv_tile", c, s, S, False, "rne", 0, 0), ("nv_tile_t", ct, st, S, False, "rne", 0, 0)]
-    if name.startswith("dy"):
-        out = []
-        if not name.endswith(":col"):
-            c, s, S = m.nvfp4_quantize(x, gs=m.GScale.PER_ROW, rnd=m.Round.SR, seed=0, stream_id=0)
-            out.append(("nv_row", c, s, S, True, "sr", 0, 0))
-        if not name.endswith(":row"):
-            c, s, S = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
-                                       stream_id=1)
-            out.append(("nv_col", c, s, S, False, "sr", 0, 1))
-        return out
-    c, s, S = m.nvfp4_quantize(x, gs=m.GScale.PER_ROW)
-    cc, sc, Sc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
-    return [("nv_row", c, s, S, True, "rne", 0, 0), ("nv_col", cc, sc, Sc, False, "rne", 0, 1)]
+    # both copies of an activation or gradient from the two-pass entry point
+    # (SR for gradients: stream 0 rowwise, 1 columnwise)
+    sr = name.startswith("dy")
+    c, s, S, cc, sc, Sc = m.nvfp4_quantize_rowcol(x, rnd=m.Round.SR if sr else m.Round.RNE, seed=0)
+    rnd = "sr" if sr else "rne"
+    out = []
+    if not name.endswith(":col"):
+        out.append(("nv_row", c, s, S, True, rnd, 0, 0))
+    if not name.endswith(":row"):
+        out.append(("nv_col", cc, sc, Sc, False, rnd, 0, 1))
+    return out
 
 
 # ------------------------------------------------------------------ config 5
@@ -190,12 +188,9 @@ def test_config5_gemms_every_tile(lin):
     T, K = x.shape
     N = w.shape[0]
     say(f"config 5 {lin}: quantizers")
-    cx, sx, Sx = m.nvfp4_quantize(x)
-    cxc, sxc, Sxc = m.nvfp4_quantize(x, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
+    cx, sx, Sx, cxc, sxc, Sxc = m.nvfp4_quantize_rowcol(x)
     cw, sw, cwt, swt, Sw = m.nvfp4_quantize_tile_t(w, gs=m.GScale.PER_TENSOR)
-    cd, sd, Sd = m.nvfp4_quantize(dy, rnd=m.Round.SR, seed=0, stream_id=0)
-    cdc, sdc, Sdc = m.nvfp4_quantize(dy, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, seed=0,
-                                     stream_id=1)
+    cd, sd, Sd, cdc, sdc, Sdc = m.nvfp4_quantize_rowcol(dy, rnd=m.Round.SR, seed=0)
     del x, w, dy
     NV = m.Format.NVFP4
     rT, rN, rK = _bands(T, rs), _bands(N, rs), _bands(K, rs)

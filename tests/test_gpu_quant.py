@@ -374,3 +374,31 @@ def test_nvfp4_tile16_with_transposed_copy(shape, rnd):
     assert np.array_equal(to_np(S), rS)
     assert np.array_equal(to_np(s), rs) and np.array_equal(to_np(c), rc)
     assert np.array_equal(to_np(st), ts) and np.array_equal(to_np(ct), tc)
+
+
+@pytest.mark.parametrize("shape", [(48, 256), (64, 2048), (32, 8208), (16, 32784), (96, 1024)])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_nvfp4_rowcol_equals_the_two_copies(shape, rnd):
+    """nvfp4_quantize_rowcol gives exactly the ROW per-token copy (stream 0)
+    and the COL per-tensor copy (stream 1) of separate calls, whichever row
+    kernel runs (one wave per row, one workgroup per row, two passes), and
+    both copies equal the oracle's; the MFMA scale layout as well."""
+    m = mxq()
+    x = _edge_bf16(*shape, 35, nvfp4=True)
+    v = _vals(x)
+    xd = to_dev_bf16(x)
+    R = m.Round.SR if rnd == "sr" else m.Round.RNE
+    lays = [m.Layout.LINEAR] + ([m.Layout.MFMA] if shape[0] % 64 == 0 and shape[1] % 64 == 0 else [])
+    for lay in lays:
+        say(f"nvfp4 rowcol {shape} {rnd} layout {int(lay)}")
+        c, s, S, cc, sc, Sc = m.nvfp4_quantize_rowcol(xd, rnd=R, seed=8, layout=lay)
+        c1, s1, S1 = m.nvfp4_quantize(xd, gs=m.GScale.PER_ROW, rnd=R, seed=8, stream_id=0, layout=lay)
+        c2, s2, S2 = m.nvfp4_quantize(xd, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=R, seed=8, stream_id=1,
+                                      layout=lay)
+        for a, b in ((c, c1), (s, s1), (S, S1), (cc, c2), (sc, s2), (Sc, S2)):
+            assert np.array_equal(to_np(a), to_np(b))
+    rc, rs, rS = ON.quantize_rowwise(v, "per_row", rnd=rnd, seed=8, stream_id=0)
+    cc_, cs_, cS_ = ON.quantize_colwise(v, rnd=rnd, seed=8, stream_id=1)
+    c, s, S, cc, sc, Sc = m.nvfp4_quantize_rowcol(xd, rnd=R, seed=8)
+    assert np.array_equal(to_np(c), rc) and np.array_equal(to_np(s), rs) and np.array_equal(to_np(S), rS)
+    assert np.array_equal(to_np(cc), cc_) and np.array_equal(to_np(sc), cs_) and np.array_equal(to_np(Sc), cS_)
