@@ -391,6 +391,58 @@ def rows_report():
         out(row, what, list(x.shape), _time_rot(torch, fns, iters), nbytes=nbytes, sets=n)
         del xs, fns
 
+    def bfd(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- the small MXFP8 case: 256x512 activations, 256x512x256 GEMM
+    d1 = synth.config1()
+    x1, w1 = bfd(d1["x"]), bfd(d1["w"])
+    n1 = x1.numel()
+    c1, s1 = m.mx_quantize(x1)
+    quant_row("a1-a3", "mxfp8 1x32 (X, 256x512)", x1, lambda xi: lambda: m.mx_quantize(xi, codes=c1, scales=s1),
+              n1 * 2 + n1 + n1 // 32)
+    o1 = torch.empty_like(x1)
+    out("a4", "mxfp8 dequantize 1x32 -> bf16 (X, 256x512)", [256, 512], _time_rot(torch, [
+        (lambda: m.mx_dequantize(m.Format.MXFP8, c1, s1, 256, 512, out=o1))], 50),
+        nbytes=n1 + n1 // 32 + n1 * 2, sets=1)
+    cw1, sw1 = m.mx_quantize(w1)
+    y1 = torch.empty((256, 256), dtype=torch.bfloat16, device=dev)
+    out("a5", "mxfp8 GEMM 256x256x512", [256, 256, 512], _time_rot(torch, [
+        (lambda: m.mx_gemm(m.Operand(m.Format.MXFP8, c1, s1), m.Operand(m.Format.MXFP8, cw1, sw1),
+                           256, 256, 512, out=y1))], 50),
+        flops=2.0 * 256 * 256 * 512, peak=PEAK_FP8_TFLOPS, sets=1)
+
+    # ---- the NVFP4 linear: 4096 tokens, 2048 -> 768
+    d2 = synth.config2()
+    x2, w2, dy2 = bfd(d2["x"]), bfd(d2["w"]), bfd(d2["dy"])
+    M2, K2, N2 = 4096, 2048, 768
+    n2, nw2 = x2.numel(), w2.numel()
+    c2, s2, S2 = m.nvfp4_quantize(x2)
+    quant_row("a1-a3", "nvfp4 1x16 per-token RNE (X, 4096x2048)", x2, lambda xi: lambda: m.nvfp4_quantize(
+        xi, codes=c2, block_scales=s2, gscales=S2), n2 * 2 + n2 // 2 + n2 // 16 + M2 * 4)
+    cw2, sw2, Sw2 = m.nvfp4_quantize(w2, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+    wdq2 = torch.empty_like(w2)
+    quant_row("a1-a4", "nvfp4 16x16 per-tensor + DQ(W) in the same pass (W, 768x2048)", w2, lambda xi: lambda:
+              m.nvfp4_quantize_dq(xi, codes=cw2, block_scales=sw2, gscales=Sw2, dq=wdq2),
+              2 * nw2 * 2 + nw2 // 2 + nw2 // 256 + 4 + nw2 * 2)
+    y2 = torch.empty((M2, N2), dtype=torch.bfloat16, device=dev)
+    nsets = _copies(c2.numel() + cw2.numel())
+    ops = [(c2.clone(), cw2.clone()) for _ in range(nsets)]
+    out("a6", "nvfp4 FPROP 4096x768x2048", [M2, N2, K2], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.NVFP4, a, s2, S2, gs=m.GScale.PER_ROW),
+                                    m.Operand(m.Format.NVFP4, b, sw2, Sw2, block=m.Block.TILE,
+                                              gs=m.GScale.PER_TENSOR), M2, N2, K2, out=y2)) for a, b in ops], 50),
+        flops=2.0 * M2 * N2 * K2, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
+    dx2 = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
+    nsets = _copies(dy2.numel() * 2 + wdq2.numel() * 2)
+    ops = [(dy2.clone(), wdq2.clone()) for _ in range(nsets)]
+    out("a7", "dequantized-backward DGRAD (BF16) 4096x2048x768", [M2, K2, N2], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.BF16, a, block=m.Block.NONE),
+                                    m.Operand(m.Format.BF16, b, block=m.Block.NONE, transposed=True),
+                                    M2, K2, N2, out=dx2)) for a, b in ops], 50),
+        flops=2.0 * M2 * N2 * K2, peak=PEAK_F16_TFLOPS, sets=nsets)
+    del x2, w2, dy2, ops
+
     # ---- Llama-3-8B-shaped dense MLP, NVFP4 (tokens 32768, hidden 4096, I 14336)
     T5, H5, I5 = 32768, 4096, 14336
     x5 = synth.mlp_tensor(5, "x", dev)
@@ -473,7 +525,19 @@ def rows_report():
                                     m.Operand(m.Format.NVFP4, b, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR,
                                               transposed=True), T5, H5, 2 * I5, out=dx5)) for a, b in ops], 4),
         flops=f, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
-    del ops, dx5, cdg
+    del ops
+    cwt, swt = torch.empty((H5, I5), dtype=torch.uint8, device=dev), torch.empty((H5 // 16, 2 * I5 // 16), dtype=torch.uint8, device=dev)
+    w5 = synth.mlp_tensor(5, "w_gu", dev)
+    m.nvfp4_quantize_tile_t(w5, codes=cw, block_scales=sw, codes_t=cwt, block_scales_t=swt, gscales=Sw)
+    del w5
+    nsets = _copies(cdg.numel() + cwt.numel())
+    ops = [(cdg.clone(), cwt.clone()) for _ in range(nsets)]
+    out("a6", "nvfp4 DGRAD gate_up (transposed 16x16 copy)", [T5, H5, 2 * I5], _time_rot(torch, [
+        (lambda a=a, b=b: m.mx_gemm(m.Operand(m.Format.NVFP4, a, sdg, Sdg, gs=m.GScale.PER_ROW),
+                                    m.Operand(m.Format.NVFP4, b, swt, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR),
+                                    T5, H5, 2 * I5, out=dx5)) for a, b in ops], 4),
+        flops=f, peak=PEAK_F16_TFLOPS, fp4=True, sets=nsets)
+    del ops, dx5, cdg, cwt, swt
     ccg, scg, Scg = m.nvfp4_quantize(dyg, block=m.Block.COL, gs=m.GScale.PER_TENSOR, rnd=m.Round.SR, stream_id=1)
     ccx, scx, Scx = m.nvfp4_quantize(x5, block=m.Block.COL, gs=m.GScale.PER_TENSOR)
     del dyg
@@ -539,6 +603,26 @@ def rows_report():
              (wt4[2], wt4[3]), (T4, H4, 2 * I4), dx4, MX, PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
     gemm_row("a5", "mxfp8 WGRAD gate_up (columnwise copies)", [2 * I4, H4, T4], (dd[2], dd[3]), (d4[2], d4[3]),
              (2 * I4, H4, T4), dw4, MX, PEAK_FP8_TFLOPS)
+    # the down linear: H [8192, 12288] -> [8192, 4096]
+    h4 = synth.mlp_tensor(4, "h", dev)
+    wd4 = synth.mlp_tensor(4, "w_dn", dev)
+    dyd4 = synth.mlp_tensor(4, "dy_dn", dev)
+    hq = m.mx_quantize(h4, block=m.Block.DUAL)
+    wdq4 = m.mx_quantize(wd4, block=m.Block.TILE, transposed_copy=True)
+    ddq = m.mx_quantize(dyd4, block=m.Block.DUAL)
+    del h4, wd4, dyd4
+    yd4 = torch.empty((T4, H4), dtype=torch.bfloat16, device=dev)
+    dhd4 = torch.empty((T4, I4), dtype=torch.bfloat16, device=dev)
+    dwd4 = torch.empty((H4, I4), dtype=torch.bfloat16, device=dev)
+    f = 2.0 * T4 * H4 * I4
+    gemm_row("a5", "mxfp8 FPROP down", [T4, H4, I4], (hq[0], hq[1]), (wdq4[0], wdq4[1]), (T4, H4, I4), yd4, MX,
+             PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
+    gemm_row("a5", "mxfp8 DGRAD down (transposed 32x32 copy)", [T4, I4, H4], (ddq[0], ddq[1]), (wdq4[2], wdq4[3]),
+             (T4, I4, H4), dhd4, MX, PEAK_FP8_TFLOPS, b_kw=dict(block=m.Block.TILE))
+    gemm_row("a5", "mxfp8 WGRAD down (columnwise copies)", [H4, I4, T4], (ddq[2], ddq[3]), (hq[2], hq[3]),
+             (H4, I4, T4), dwd4, MX, PEAK_FP8_TFLOPS)
+    del hq, wdq4, ddq, yd4, dhd4, dwd4
+    f = 2.0 * T4 * 2 * I4 * H4
     # the same layer with DeepSeek-style blockwise FP8 (1x128 / 128x128)
     for f32s in (False, True):
         q = m.fp8bw_quantize_f32 if f32s else m.fp8bw_quantize
@@ -579,9 +663,6 @@ def rows_report():
     np.add.at(off, pairs[:, 1] + 1, 1)
     off = np.cumsum(off).astype(np.int32)
     Mr = len(row_token)
-
-    def bfd(b):
-        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
 
     x3 = bfd(d["x"])
     cx3, sx3, Sx3 = m.nvfp4_quantize(x3)

@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t f32s_from_amax_bits(uint32_t amax16) {
 // x - q0 s by one FMA and the corrected q0 + residual * r by another.  The
 // result can differ from RN(x / s) in its last bits, but for every BF16 x in
 // a block and every scale s >= 2^-80 of a BF16 block maximum it gives the
-// same E4M3 code (an exhaustive check over all 5.1e8 such pairs is among the
+// same E4M3 code (an exhaustive check over all 1.0e9 such pairs is among the
 // host tests); smaller scales divide directly.
 // (The sign is x's: for x = -0 the corrected sum would come out +0.)
 __device__ __forceinline__ float f32s_quotient(float x, float sc, float r) {
