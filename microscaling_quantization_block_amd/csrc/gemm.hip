@@ -41,6 +41,7 @@
 #include "mxq_kernels.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace mxq {
 
@@ -221,6 +222,41 @@ __device__ __forceinline__ TileOrigin tile_origin(const GemmArgs& p, int mt, int
   return o;
 }
 
+// ------------------------------------------------------------ tile order
+// XCD-aware tile id: workgroup b runs on XCD b % 8; each XCD gets a
+// contiguous range of the G = tiles_m x tiles_n real tiles (a grouped grid is
+// sized for the most m-tiles any split of M could need, and each XCD's
+// surplus workgroups, the last in its dispatch order, exit: false).  Within
+// the range, runs of gm_rows tile rows are walked column by column.
+__device__ __forceinline__ bool xcd_tile(int tiles_m, int tiles_n, int gm_rows, int& mt, int& nt) {
+  const int G = tiles_m * tiles_n;
+  const int b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int q8 = G >> 3, r8 = G & 7, x = b & 7;
+  if ((b >> 3) >= q8 + (x < r8 ? 1 : 0)) return false;
+  const int logical = x * q8 + (x < r8 ? x : r8) + (b >> 3);
+  const int tgrp = logical / (gm_rows * tiles_n), gin = logical - tgrp * gm_rows * tiles_n;
+  const int gm = min(gm_rows, tiles_m - tgrp * gm_rows);
+  mt = tgrp * gm_rows + gin % gm;
+  nt = gin / gm;
+  return true;
+}
+
+// Runs of tile rows for the walk above (1: row by row).  Runs of GM tile rows
+// walked column by column let the tiles in flight on an XCD form a block that
+// shares A and B panels in its L2 (row by row, each row of tiles streams all
+// of B again).  GM keeps the block's A and B bytes about equal for the 32-64
+// tiles an XCD runs at once: 8 rows of 128-row tiles, 4 of 256-row tiles.
+// Measured on MI355X: DGRAD and WGRAD shapes (at most 64 tiles per row) gain
+// 3-16%; rows longer than that (an FPROP with N = 24576) run faster in row
+// order, where the eight XCDs walk the same B panels together; grouped
+// launches keep row order too (neighbouring m-tiles belong to different
+// experts), and so do launches whose whole B fits an XCD's 4 MB L2 (there,
+// row order lets each XCD read only its own A rows: the 4096x768x2048 NVFP4
+// FPROP read 12.8 MB grouped against 11.3 MB, in the same time).
+__device__ __forceinline__ int tile_run_rows(const GemmArgs& p, int tiles_n, int bm, int64_t b_bytes) {
+  return (p.num_groups || tiles_n > 64 || b_bytes <= ((int64_t)4 << 20)) ? 1 : (bm >= 256 ? 4 : 8);
+}
+
 // Transposes of R x 8 register blocks (R K-rows, 8 N-columns) into the R
 // K-values of one column j, packed in K order.
 // 16-bit values: row q holds 8 values in 4 words (column j = half j&1 of word j>>1).
@@ -325,37 +361,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert(WM % 32 == 0 && WN % 32 == 0 && TM >= 1 && TN >= 1, "wave tile");
   constexpr int KSTEP = PATH == P_FP8 ? 128 : 64;          // K elements per stage
 
-  // ---- XCD-aware tile id: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of the real tiles.  A grouped grid is sized for the most
-  // m-tiles any split of M could need; its real count comes from the offsets,
-  // and each XCD's surplus workgroups (the last in its dispatch order) exit,
-  // so the real tiles are spread over all eight XCDs.
+  // ---- tile id (XCD-aware, xcd_tile; a grouped grid's real m-tile count
+  // comes from the offsets)
   const int lane0 = threadIdx.x & 63;
   const int tiles_n = gridDim.x;
   const int tiles_m = p.num_groups ? group_mtiles<BM>(p, lane0) : (int)gridDim.y;
-  const int G = tiles_m * tiles_n;
-  const int b = blockIdx.y * gridDim.x + blockIdx.x;
-  const int q8 = G >> 3, r8 = G & 7, x = b & 7;
-  if ((b >> 3) >= q8 + (x < r8 ? 1 : 0)) return;
-  const int logical = x * q8 + (x < r8 ? x : r8) + (b >> 3);
-  // grouped order: runs of GM tile rows walked column by column, so the
-  // tiles in flight on an XCD form a block that shares A and B panels in its
-  // L2 (row by row, each row of tiles streams all of B again).  GM keeps the
-  // block's A and B bytes about equal for the 32-64 tiles an XCD runs at
-  // once: 8 rows of 128-row tiles, 4 of 256-row tiles.  Measured on MI355X:
-  // DGRAD and WGRAD shapes (at most 64 tiles per row) gain 3-16%; rows longer
-  // than that (an FPROP with N = 24576) run faster in row order, where the
-  // eight XCDs walk the same B panels together; grouped launches keep row
-  // order too (neighbouring m-tiles belong to different experts), and so do
-  // launches whose whole B fits an XCD's 4 MB L2 (there, row order lets each
-  // XCD read only its own A rows: the 4096x768x2048 NVFP4 FPROP read 12.8 MB
-  // grouped against 11.3 MB, in the same time).
   const int64_t b_bytes = (int64_t)p.N * p.K * (PATH == P_BF16 ? 2 : 1) / (PATH == P_F16 ? 2 : 1);
-  const int GM = (p.num_groups || tiles_n > 64 || b_bytes <= ((int64_t)4 << 20)) ? 1 : (BM >= 256 ? 4 : 8);
-  const int tgrp = logical / (GM * tiles_n), gin = logical - tgrp * GM * tiles_n;
-  const int gm = min(GM, tiles_m - tgrp * GM);
-  const int mt = tgrp * GM + gin % gm;
-  const int nt = gin / gm;
+  int mt, nt;
+  if (!xcd_tile(tiles_m, tiles_n, tile_run_rows(p, tiles_n, BM, b_bytes), mt, nt)) return;
 
   const TileOrigin to = tile_origin<BM>(p, mt, lane0);
   if (!to.active) return;
@@ -1172,6 +1185,298 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   }
 }
 
+// ------------------------------------------------------------ MXFP8, direct to LDS
+// A second MXFP8 kernel for dense launches with row-major B and K % 128 == 0
+// (FPROP with the 32x32 weight copy, DGRAD with its transposed copy, WGRAD with
+// the columnwise copies).  The register-staged kernel above spends most of its
+// time moving data: its 256x128 tile writes 48 KB into LDS per 128 of K from
+// registers, and in a stage without loads and stores (a timing-only ablation)
+// it already runs 36% faster, while without its MFMAs only 18% faster.  Here:
+//  * the global loads write LDS themselves (buffer_load_dwordx4 ... lds: lane
+//    l of a wave's load lands at the instruction's LDS base + 16 l; checked on
+//    the chip), so there are no staging registers and no LDS store
+//    instructions; out-of-range rows read zeros through the buffer range
+//    check, as in the kernel above;
+//  * that frees the registers for a 256x256 tile on 4 waves (one per SIMD),
+//    each wave 128x128: 16 MFMAs per 64 of K against 8 fragment reads, so LDS
+//    reads per MFMA halve and global bytes per MFMA halve against 256x128;
+//  * stages of 64 K (32 KB: 256 A rows and 256 B rows of 64 bytes) in four
+//    LDS buffers; the loads of stage s + 3 are issued while stage s is
+//    computed, and one barrier per stage orders them: at the barrier of stage
+//    s every wave has waited for its share of stage s + 1 and has finished
+//    reading stage s - 1, whose buffer the next loads overwrite;
+//  * fragments are read a stage ahead (two register sets): the reads of
+//    stage s + 1 run under the MFMAs of stage s;
+//  * the E8M0 scale words travel the same way: a stage pair's words (2 KB)
+//    are loaded into LDS with its even stage and read once per pair.
+// Measured (8192x24576x4096 MXFP8 FPROP, and DGRAD / WGRAD of the same
+// layer): 1311 / 1140 / 1272 us for the kernel above, 963-989 / 815-845 /
+// 854-885 us here.  Timing-only ablations of this kernel: without its loads
+// 698 / 546 / 538 us, without its waits for them no faster (the prefetch
+// hides the latency), every tile loading the same data 10% faster (little is
+// bound by HBM), without its barriers 8% faster.
+// A row's 64 bytes are four 16-byte chunks, chunk c in slot c ^ ((r >> 2) & 3):
+// the fragment reads (16 consecutive rows, one chunk) then cover all 64 banks.
+// A DMA instruction fills 16 consecutive rows; lane l takes row l / 4, slot
+// l % 4 and so loads chunk (l % 4) ^ ((row >> 2) & 3) of that row.
+// Each lane feeds its MFMAs the same K bytes and scale bytes as the kernel
+// above (chunks h and 2 + h of a 64-wide slice), so both give the same bits.
+constexpr int DMA_BM = 256, DMA_BN = 256;
+constexpr int DMA_ROW = 64;                                 // LDS bytes per row and stage
+constexpr int DMA_DATA = (DMA_BM + DMA_BN) * DMA_ROW;       // 32 KB of A and B rows
+constexpr int DMA_SC = 2048;                                // a stage pair's scale words (A, then B)
+constexpr int DMA_STAGE = DMA_DATA + DMA_SC;
+constexpr int DMA_NBUF = 4;
+
+typedef unsigned srd_t __attribute__((ext_vector_type(4)));   // a buffer descriptor in SGPRs
+
+// A raw buffer descriptor as four scalar words (base, stride 0, size in
+// bytes, the same flags as make_rsrc).
+__device__ __forceinline__ srd_t make_srd(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return srd_t{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
+}
+
+// Loads into LDS: lane l's 16 (or 4) bytes at voff land at LDS address
+// m0 + 16 l (4 l).  Written as assembly so that the compiler, which cannot
+// tell these LDS writes from the fragment reads of other buffers, does not
+// wait for every load in flight before each LDS read; the kernel waits for
+// them itself (wait_vmcnt), counting every vector-memory instruction it
+// issues, and issues no other vector-memory loads in its main loop.
+__device__ __forceinline__ void dma16(const srd_t& srd, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4(const srd_t& srd, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(lds_addr) : "memory");
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+  int mt, nt;
+  // runs of 4 tile rows whatever the row length (FPROP 8192x24576x4096: 963
+  // against 1038 us in row order; DGRAD and WGRAD shapes the same or better)
+  if (!xcd_tile(tiles_m, tiles_n, p.N * p.K <= ((int64_t)4 << 20) ? 1 : 4, mt, nt)) return;
+  const int K = (int)p.K, N = (int)p.N, M = (int)p.M;
+  const int m0 = mt * DMA_BM, n0 = nt * DMA_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (the loads' LDS base)
+  const int wm = w >> 1, wn = w & 1;                        // wave tile: rows wm*128, columns wn*128
+  const int h = lane >> 5, r32 = lane & 31;
+  const int nk = K / 64;
+  const int nb32 = K >> 5;
+  const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+
+  const srd_t sA = make_srd(p.a, p.a_rows * p.lda);
+  const srd_t sB = make_srd(p.b, p.N * p.ldb);
+  const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb32);
+  const srd_t sBs = make_srd(p.b_scales, p.b_group_scales);
+  const uint32_t arb = (uint32_t)p.lda, brb = (uint32_t)p.ldb;
+
+  // Data: wave w fills rows (4w + i) * 16 .. + 16 of A and of B.
+  uint32_t a_dv[4], b_dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (4 * w + i) * 16 + (lane >> 2);
+    const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    const bool aok = m0 + r < M, bok = n0 + r < N;
+    a_dv[i] = in_range(aok, (uint32_t)(aok ? m0 + r : 0) * arb + c * 16u);
+    b_dv[i] = in_range(bok, (uint32_t)(bok ? n0 + r : 0) * brb + c * 16u);
+  }
+  // E8M0 scale words: the word of blocks 4q .. 4q + 3 of a row covers stage
+  // pair q (stages 2q, 2q + 1).  A pair's words ride with its even stage:
+  // entry E = 32 half + r (16 bytes) holds the words of rows 128 half + r +
+  // 32 t, t = 0..3, so a lane reads its four tiles' words at once.  Wave w
+  // loads A entries 16w .. 16w + 15 and B entries likewise (lane l: entry
+  // 16w + l / 4, tile l % 4).
+  uint32_t a_sv, b_sv;
+  {
+    const int E = 16 * w + (lane >> 2), t = lane & 3;
+    const int r = (E >> 5) * 128 + (E & 31) + 32 * t;
+    const bool aok = m0 + r < M, bok = n0 + r < N;
+    a_sv = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 0, nb32, p.a_mfma_layout) : 0u);
+    const int n = n0 + r;
+    b_sv = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 5) * nb32) : (uint32_t)scale_offset(n, 0, nb32, p.b_mfma_layout))
+                             : 0u);
+  }
+  const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;
+  const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
+
+  // stage s (in range or not) into buffer s % 4, with pair s / 2's scale
+  // words when s is even; stages past the end read zeros, never computed
+  // part i of stage s: A rows (i < 4) or B rows (i >= 4) of this wave
+  auto dma_part = [&](int s, int i) {
+    const uint32_t L = lbase + (uint32_t)((s & (DMA_NBUF - 1)) * DMA_STAGE);
+    const uint32_t ko = s < nk ? (uint32_t)s * 64u : 0x80000000u;
+    if (i < 4) dma16(sA, L + (uint32_t)((4 * w + i) * 1024), a_dv[i] + ko);
+    else dma16(sB, L + (uint32_t)(DMA_BM * DMA_ROW + (4 * w + i - 4) * 1024), b_dv[i - 4] + ko);
+  };
+  auto dma_sc = [&](int s) {          // the scale words of pair s / 2 (s even)
+    const uint32_t L = lbase + (uint32_t)((s & (DMA_NBUF - 1)) * DMA_STAGE);
+    const int q = s >> 1;
+    const bool qin = s < nk;
+    dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? a_sv + (uint32_t)q * a_sstep : 0x80000000u);
+    dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? b_sv + (uint32_t)q * b_sstep : 0x80000000u);
+  };
+  auto dma = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_part(s, i);
+    if ((s & 1) == 0) dma_sc(s);
+  };
+
+  // fragment reads: tile t of A (rows wm*128 + 32t + r) and of B
+  const int ra = wm * 128 + r32, rb = wn * 128 + r32;           // (r >> 2) & 3 is the same for r + 32t
+  const uint32_t fa0 = (uint32_t)(ra * DMA_ROW + ((h ^ ((ra >> 2) & 3)) << 4));
+  const uint32_t fa1 = (uint32_t)(ra * DMA_ROW + (((2 + h) ^ ((ra >> 2) & 3)) << 4));
+  const uint32_t fb0 = (uint32_t)(DMA_BM * DMA_ROW + rb * DMA_ROW + ((h ^ ((rb >> 2) & 3)) << 4));
+  const uint32_t fb1 = (uint32_t)(DMA_BM * DMA_ROW + rb * DMA_ROW + (((2 + h) ^ ((rb >> 2) & 3)) << 4));
+  const uint32_t fsa = (uint32_t)(DMA_DATA + (wm * 32 + r32) * 16);
+  const uint32_t fsb = (uint32_t)(DMA_DATA + 1024 + (wn * 32 + r32) * 16);
+  v8i fa[2][4], fb[2][4];
+  // part k of stage s's fragments: A tile k (k < 4) or B tile k - 4
+  auto read_part = [&](int s, int set, int k) {
+    const uint8_t* L = lds + (s & (DMA_NBUF - 1)) * DMA_STAGE;
+    const int t = k & 3;
+    const uint32_t o0 = k < 4 ? fa0 : fb0, o1 = k < 4 ? fa1 : fb1;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(L + o0 + t * 32 * DMA_ROW);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(L + o1 + t * 32 * DMA_ROW);
+    const v8i v = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    if (k < 4) fa[set][t] = v;
+    else fb[set][t] = v;
+  };
+  auto read = [&](int s, int set) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) read_part(s, set, k);
+  };
+  // a stage pair's scale words (lane half h: its block's byte to byte 0/2)
+  struct Sc { uint32_t a[4], b[4]; };
+  auto read_sc = [&](int s) {
+    const uint8_t* L = lds + (s & (DMA_NBUF - 1)) * DMA_STAGE;
+    const uint4 va = *reinterpret_cast<const uint4*>(L + fsa);
+    const uint4 vb = *reinterpret_cast<const uint4*>(L + fsb);
+    Sc v;
+    v.a[0] = va.x >> (8 * h); v.a[1] = va.y >> (8 * h); v.a[2] = va.z >> (8 * h); v.a[3] = va.w >> (8 * h);
+    v.b[0] = vb.x >> (8 * h); v.b[1] = vb.y >> (8 * h); v.b[2] = vb.z >> (8 * h); v.b[3] = vb.w >> (8 * h);
+    return v;
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Vector-memory instructions a lane issues: 8 per stage loaded, plus 2
+  // scale loads with every even stage.  At the top of stage s the loads of
+  // stage s + 1 (with its scales) must be done; issued after them: those of
+  // stage s + 2, with scales when s + 2 is even: 10 after an even s, 8 after
+  // an odd one.
+  dma(0);
+  dma(1);
+  dma(2);
+  wait_vmcnt<18>();                  // stage 0 and its scales landed (this lane's share)
+  asm volatile("s_barrier" ::: "memory");
+  read(0, 0);
+  Sc cur = read_sc(0), nxt;
+
+  // Two stages per iteration (K % 128 == 0: nk is even): stage 2j uses
+  // fragment set 0 and scale byte 0 of pair j, stage 2j + 1 set 1 and byte 2.
+  for (int s = 0; s < nk; s += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 0) wait_vmcnt<10>();  // stage s + u + 1 landed (this lane's share)
+      else wait_vmcnt<8>();
+      asm volatile("s_barrier" ::: "memory");
+      // Each MFMA is followed by a slice of the other work, so that the
+      // matrix pipe is fed while the LDS reads and the loads drain: after
+      // MFMAs 0-7 two of the next stage's 16 fragment reads each, after MFMAs
+      // 8-15 one of this wave's 8 loads of stage s + 3 (a wave that issued
+      // them all at once stalled behind the full load queue before its first
+      // MFMA).  Scheduling barriers keep this order.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tm = i >> 2, tn = i & 3;
+        if (u == 0)
+          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[0][tn], fa[0][tm], acc[tm][tn], 0, 0, 0, (int)cur.b[tn], 0, (int)cur.a[tm]);
+        else
+          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[1][tn], fa[1][tm], acc[tm][tn], 0, 0, 2, (int)cur.b[tn], 2, (int)cur.a[tm]);
+        if (i < 8) {
+          read_part(s + u + 1, u ^ 1, i);
+          if (u == 1 && i == 7) nxt = read_sc(s + 2);
+        } else {
+          dma_part(s + u + 3, i - 8);
+          if (u == 1 && i == 15) dma_sc(s + u + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    cur = nxt;
+  }
+
+  // ------------------------------------------------ epilogue (as in gemm_kernel)
+  wait_vmcnt<0>();                     // no load still writing LDS
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int WN = 128;
+  constexpr int EROW = WN * 2 + 8;
+  constexpr int ECH = WN / 8;
+  constexpr int ERI = 64 / ECH;
+  uint8_t* const E = lds + w * (32 * EROW);
+  const bool vec16 = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+    uint8_t* const er = E + r32 * EROW + h * 8;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
+            make_uint2(f32x2_to_bf16x2(acc[tm][tn][4 * g], acc[tm][tn][4 * g + 1]),
+                       f32x2_to_bf16x2(acc[tm][tn][4 * g + 2], acc[tm][tn][4 * g + 3]));
+#pragma unroll
+    for (int it = 0; it < 32 / ERI; ++it) {
+      const int rr = it * ERI + lane / ECH, cc = lane % ECH;
+      const uint4 val = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+      const int64_t m = m0 + wm * 128 + tm * 32 + rr;
+      const int n = n0 + wn * WN + cc * 8;
+      if (m < M) {
+        uint16_t* const dst = p.c + m * p.ldc + n;
+        if (vec16 && n + 7 < N) {
+          *reinterpret_cast<uint4*>(dst) = val;
+        } else {
+          const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) dst[i] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+        }
+      }
+    }
+  }
+}
+
+static hipError_t launch_fp8_dma(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
+  if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
+  const size_t lds = (size_t)DMA_NBUF * DMA_STAGE;
+  static std::atomic<uint32_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_dma_kernel, (int)lds, lds_set); e != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(gemm_fp8_dma_kernel, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ launcher
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false, bool SWI = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
@@ -1235,6 +1540,13 @@ template <int PATH, bool BT, bool SWI = false>
 static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
   const int64_t cus = 256;
   int t = g_tile_override;
+  if constexpr (PATH == P_FP8 && !BT && !SWI) {
+    // MXFP8 takes the direct-to-LDS 256x256 kernel (configuration 7) once its
+    // tiles fill the CUs, where it applies: dense, row-major B, 32-wide blocks
+    const bool dma_ok = a.num_groups == 0 && !a.row_index && !a.a_b128 && !a.b_b128 && a.K % 128 == 0;
+    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus))) return launch_fp8_dma(a, st);
+  }
+  if (t == 7) t = -1;                    // configuration 7 where it does not apply: the measured choice
   if (t < 0) {
     // measured on MI355X (8192^3, 8192x24576x4096, 8192x28672x4096,
     // 8192x1536x2048, 4096x768x2048, 4096x2048x768, grouped 128 x 512 rows):

@@ -144,6 +144,50 @@ def test_mxfp8_mfma_layout_operands():
     _assert_gemm(out, a64, b64, a64, b64)
 
 
+@pytest.mark.parametrize("M,N,K,a_mfma,b_kind", [
+    (600, 416, 384, False, "row"),        # 3 x 2 tiles, ragged M; 6 stages: one unrolled body + 2
+    (256, 256, 128, True, "row_mfma"),    # one tile, 2 stages (the tail alone)
+    (544, 320, 1024, True, "tile"),       # 32x32 weight scales; 16 stages, no tail
+    (1000, 300, 640, False, "row"),       # ragged N (not a multiple of 32); 10 stages
+    (768, 352, 768, False, "row_mfma"),   # 12 stages: three unrolled bodies
+])
+def test_mxfp8_direct_to_lds_kernel(M, N, K, a_mfma, b_kind):
+    """Configuration 7 (MXFP8, 256x256 tiles on 4 waves, operands loaded
+    straight into LDS) on ragged shapes, with linear and MFMA-layout scales
+    and 32x32 weight tiles: matches the oracle and gives the bits of the
+    register-staged 256x128 kernel (configuration 5)."""
+    m = mxq()
+    x = _bf16((M, K), 1.0, 80)
+    w = _bf16((N, K), 0.02, 81)
+    say(f"mxfp8 direct-to-LDS {M}x{N}x{K} a_mfma={a_mfma} b={b_kind}")
+    la = m.Layout.MFMA if a_mfma else m.Layout.LINEAR
+    cx, sx = m.mx_quantize(to_dev_bf16(x), layout=la)
+    A = m.Operand(m.Format.MXFP8, cx, sx, layout=la)
+    rcx, rsx = OM.quantize_rowwise(F.bf16_bits_to_f64(x))
+    a64 = OM.dequantize_f64(rcx, rsx)
+    if b_kind == "tile":
+        cw, sw = m.mx_quantize(to_dev_bf16(w), block=m.Block.TILE)
+        B = m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE)
+        rcw, rsw = OM.quantize_tile32(F.bf16_bits_to_f64(w))
+        b64 = OM.dequantize_f64(rcw, rsw, "32x32")
+    else:
+        lb = m.Layout.MFMA if b_kind == "row_mfma" else m.Layout.LINEAR
+        cw, sw = m.mx_quantize(to_dev_bf16(w), layout=lb)
+        B = m.Operand(m.Format.MXFP8, cw, sw, layout=lb)
+        rcw, rsw = OM.quantize_rowwise(F.bf16_bits_to_f64(w))
+        b64 = OM.dequantize_f64(rcw, rsw)
+    try:
+        m.mx_gemm_set_tile(7)
+        out7 = m.mx_gemm(A, B, M, N, K)
+        _assert_gemm(out7, a64, b64, a64, b64)
+        m.mx_gemm_set_tile(5)
+        out5 = m.mx_gemm(A, B, M, N, K)
+    finally:
+        m.mx_gemm_set_tile(-1)
+    o7, o5 = from_dev_bf16(out7), from_dev_bf16(out5)
+    assert np.array_equal(o7, o5), f"{int(np.sum(o7 != o5))} elements differ from the 256x128 kernel"
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def _nv_ops(m, x, w, w_tile=True):
@@ -346,7 +390,7 @@ def test_gemm_large_tile_variants(path, bt, K):
 @pytest.mark.parametrize("bt", [False, True])
 @pytest.mark.parametrize("K", [320, 384])
 def test_every_tile_configuration_gives_the_same_bits(path, bt, K):
-    """All seven workgroup tiles (forced with mx_gemm_set_tile) on one ragged
+    """All eight workgroup tiles (forced with mx_gemm_set_tile) on one ragged
     problem: the measured default is checked against the oracle, and every
     forced tile must return the same BF16 bits (each output element sums its
     K products in the same order whatever the tile)."""
@@ -360,7 +404,7 @@ def test_every_tile_configuration_gives_the_same_bits(path, bt, K):
     _assert_gemm(ref, a64, b64, a32, b32)
     ref = from_dev_bf16(ref)
     try:
-        for t in range(7):
+        for t in range(8):
             m.mx_gemm_set_tile(t)
             out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
@@ -426,7 +470,7 @@ def test_every_tile_configuration_grouped(path):
                                       a32[rows], b32[g * N:(g + 1) * N])
             assert ok, f"expert {g}: frobenius {frob:.3e}, worst {worst:.3f}"
     try:
-        for t in range(7):
+        for t in range(8):
             m.mx_gemm_set_tile(t)
             out = run()
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
@@ -525,7 +569,7 @@ def test_grouped_tile_order_with_a_ragged_last_run(path, K, bt):
     _assert_gemm(ref, a64, b64, a32, b32)
     ref = from_dev_bf16(ref)
     try:
-        for t in range(7):
+        for t in range(8):
             m.mx_gemm_set_tile(t)
             out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
