@@ -479,12 +479,13 @@ mxq_status mx_gemm(const mxq_operand* a, const mxq_operand* b,
  *          4  128x128, 8 waves in two ping-pong groups
  *          5  256x128, 8 waves in two ping-pong groups
  *          6  256x256, 8 waves in two ping-pong groups
- *          7  MXFP8 only: 256x256, 4 waves, operands loaded straight into
- *             LDS (dense launches with row-major B and K % 128 == 0; any
- *             other call under 7 takes the measured choice)
+ *          7  MXFP8 and NVFP4: 256x256, 4 waves, operands loaded straight
+ *             into LDS (dense launches with row-major B; K % 128 == 0; any
+ *             other call under 7 or 8 takes the measured choice)
+ *          8  NVFP4: the same on 8 waves
  * Every configuration computes the same result bit for bit (the K order of
  * the accumulation does not depend on the tile).  Returns MXQ_EINVAL outside
- * [-1, 7].  It applies to calls made after it returns; launches already
+ * [-1, 8].  It applies to calls made after it returns; launches already
  * queued keep their tile.
  */
 mxq_status mx_gemm_set_tile(int32_t tile);

@@ -466,6 +466,6 @@ def mx_swiglu(gu, inter, out=None, stream=None):
 
 def mx_gemm_set_tile(tile):
     """Force the GEMM workgroup tile of every later mx_gemm call in the process
-    (0..7, as listed at mx_gemm_set_tile in include/mxq.h), or restore the
+    (0..8, as listed at mx_gemm_set_tile in include/mxq.h), or restore the
     measured choice with -1."""
     _check(lib().mx_gemm_set_tile(int(tile)))

@@ -614,7 +614,7 @@ mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld
 }
 
 mxq_status mx_gemm_set_tile(int32_t tile) {
-  if (tile < -1 || tile > 7) return fail(MXQ_EINVAL, "mx_gemm_set_tile: tile %d outside [-1, 7]", (int)tile);
+  if (tile < -1 || tile > 8) return fail(MXQ_EINVAL, "mx_gemm_set_tile: tile %d outside [-1, 8]", (int)tile);
   mxq::gemm_set_tile((int)tile);
   return ok();
 }

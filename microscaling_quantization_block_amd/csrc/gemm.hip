@@ -1477,6 +1477,299 @@ static hipError_t launch_fp8_dma(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ NVFP4, direct to LDS
+// The NVFP4 counterpart of the kernel above, for dense launches with row-major
+// B and K % 128 == 0 (FPROP with the 16x16 weight copy, DGRAD with its
+// transposed copy, WGRAD with the columnwise copies).  LDS holds the operands
+// as they are stored, FP4 codes and E4M3 scale bytes, loaded straight into it;
+// each wave converts the fragments it feeds its MFMAs (hardware FP4 -> FP16
+// with unit scale, times the block scale: exact, as in the kernel above).
+// Against staging FP16 tiles through LDS this moves a quarter of the LDS
+// bytes and drops the LDS store instructions, at the cost of converting each
+// A and B value twice (the two waves that share a row or column of tiles).
+//  * 256x256 tile on 4 waves (one per SIMD), each 128x128: per 16 of K,
+//    16 MFMAs (v_mfma_f32_32x32x16_f16) and 8 fragment conversions.
+//  * Stages of 128 K: 256 A rows and 256 B rows of 64 code bytes (chunk c of
+//    a row in slot c ^ ((r >> 2) & 3), as above), then the rows' scale words
+//    (two per row and stage: blocks 8s .. 8s + 3 and 8s + 4 .. 8s + 7), in
+//    four LDS buffers of 36 KB; the loads of stage s + 3 are issued while
+//    stage s computes; one barrier per stage.
+//  * A lane (row r, K half h) reads, per 64 K, the 16 code bytes of K
+//    [32h, 32h + 32) of its row for each of its 8 tiles, a 64-K step ahead;
+//    K step ks (16 K) takes codes [32h + 8ks, +8) (one word), the order every
+//    16-bit path uses, so the bits equal the other tiles'.  Conversions run a
+//    K step ahead of the MFMAs.
+// Scale words in LDS: entry E = 32 half + r (32 bytes) holds, for tiles
+// t = 0..3 (rows 128 half + r + 32t), the stage's two words of each.
+constexpr int NVD_ROW = 64;                                // code bytes per row and stage (128 K)
+constexpr int NVD_DATA = (DMA_BM + DMA_BN) * NVD_ROW;      // 32 KB
+constexpr int NVD_SC = (DMA_BM + DMA_BN) * 8;              // 4 KB of scale words
+constexpr int NVD_STAGE = NVD_DATA + NVD_SC;
+constexpr int NVD_NBUF = 4;
+
+// NW = 4: waves 2x2, each 128x128 (one wave per SIMD); NW = 8: waves 2x4,
+// each 128x64 (two per SIMD, so one wave's conversions and loads can issue
+// while the other's MFMAs run, at 6 conversions per 8 MFMAs instead of 8 per
+// 16).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
+  constexpr int WGN = NW / 2;                               // waves across N
+  constexpr int WN = DMA_BN / WGN;                          // 128 or 64 columns per wave
+  constexpr int TM = 4, TN = WN / 32;                       // 32x32 tiles per wave
+  constexpr int NF = TM + TN;                               // fragments per K step
+  constexpr int CI = 16 / NW;                               // 1 KB code loads per operand and wave
+  constexpr int SI = 8 / NW;                                // scale-word loads per operand and wave
+  constexpr int NV = 2 * CI + 2 * SI;                       // vector-memory instructions per stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+  int mt, nt;
+  if (!xcd_tile(tiles_m, tiles_n, (p.N * p.K / 2) <= ((int64_t)4 << 20) ? 1 : 4, mt, nt)) return;
+  const int K = (int)p.K, N = (int)p.N, M = (int)p.M;
+  const int m0 = mt * DMA_BM, n0 = nt * DMA_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WGN, wn = w % WGN;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int nk = K / 128;
+  const int nb16 = K >> 4;
+  const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+
+  const uint32_t arb = (uint32_t)(p.lda >> 1), brb = (uint32_t)(p.ldb >> 1);   // code bytes per row
+  const srd_t sA = make_srd(p.a, p.a_rows * (int64_t)arb);
+  const srd_t sB = make_srd(p.b, p.N * (int64_t)brb);
+  const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb16);
+  const srd_t sBs = make_srd(p.b_scales, p.b_group_scales);
+
+  // codes: wave w fills rows (CI w + i) * 16 .. + 16 of A and of B
+  uint32_t a_dv[CI], b_dv[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int r = (CI * w + i) * 16 + (lane >> 2);
+    const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    const bool aok = m0 + r < M, bok = n0 + r < N;
+    a_dv[i] = in_range(aok, (uint32_t)(aok ? m0 + r : 0) * arb + c * 16u);
+    b_dv[i] = in_range(bok, (uint32_t)(bok ? n0 + r : 0) * brb + c * 16u);
+  }
+  // scale words: entry E (32 bytes) = 32 half + r holds, for tiles t = 0..3
+  // (rows 128 half + r + 32t), the stage's two words; wave w loads entries
+  // 8 (SI w + i) .. + 8 of A and of B; lane l: entry + l / 8, tile (l % 8) / 2,
+  // word l % 2
+  uint32_t a_sv[SI], b_sv[SI];
+#pragma unroll
+  for (int i = 0; i < SI; ++i) {
+    const int E = 8 * (SI * w + i) + (lane >> 3), t = (lane & 7) >> 1, sub = lane & 1;
+    const int r = (E >> 5) * 128 + (E & 31) + 32 * t;
+    const bool aok = m0 + r < M, bok = n0 + r < N;
+    a_sv[i] = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 4 * sub, nb16, p.a_mfma_layout) : 0u);
+    const int n = n0 + r;
+    b_sv[i] = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 4) * nb16 + 4 * sub)
+                                            : (uint32_t)scale_offset(n, 4 * sub, nb16, p.b_mfma_layout))
+                                : 0u);
+  }
+  const uint32_t a_sst = p.a_mfma_layout ? 256u : 8u;
+  const uint32_t b_sst = (p.b_tile || !p.b_mfma_layout) ? 8u : 256u;
+
+  // part i of stage s: A code rows (i < CI), B code rows, A scale words, B
+  // scale words
+  auto dma_part = [&](int s, int i) {
+    const uint32_t L = lbase + (uint32_t)((s & (NVD_NBUF - 1)) * NVD_STAGE);
+    const bool sin = s < nk;
+    const uint32_t ko = sin ? (uint32_t)s * 64u : 0x80000000u;
+    if (i < CI) {
+      dma16(sA, L + (uint32_t)((CI * w + i) * 1024), a_dv[i] + ko);
+    } else if (i < 2 * CI) {
+      const int j = i - CI;
+      dma16(sB, L + (uint32_t)(DMA_BM * NVD_ROW + (CI * w + j) * 1024), b_dv[j] + ko);
+    } else if (i < 2 * CI + SI) {
+      const int j = i - 2 * CI;
+      dma4(sAs, L + NVD_DATA + (uint32_t)((8 * (SI * w + j)) * 32), sin ? a_sv[j] + (uint32_t)s * a_sst : 0x80000000u);
+    } else {
+      const int j = i - 2 * CI - SI;
+      dma4(sBs, L + NVD_DATA + 2048u + (uint32_t)((8 * (SI * w + j)) * 32),
+           sin ? b_sv[j] + (uint32_t)s * b_sst : 0x80000000u);
+    }
+  };
+  auto dma = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dma_part(s, i);
+  };
+
+  // Raw code chunks: 16 bytes of K [32h, 32h + 32) of one 64-K half of a
+  // stage, for the wave's A tiles (f < TM) and B tiles (f >= TM).  One set:
+  // each half is read right after the conversions of the previous one are
+  // issued.
+  const int ra = wm * 128 + r32, rb = wn * WN + r32;
+  const uint32_t cra = (uint32_t)(ra * NVD_ROW), crb = (uint32_t)(DMA_BM * NVD_ROW + rb * NVD_ROW);
+  const uint32_t swa = (uint32_t)((ra >> 2) & 3), swb = (uint32_t)((rb >> 2) & 3);
+  uint4 raw[NF];
+  auto read_raw = [&](int s, int half, int f) {
+    const uint8_t* L = lds + (s & (NVD_NBUF - 1)) * NVD_STAGE;
+    const uint32_t c = (uint32_t)(2 * half + h);
+    const uint32_t o = f < TM ? cra + (uint32_t)(f * 32 * NVD_ROW) + ((c ^ swa) << 4)
+                              : crb + (uint32_t)((f - TM) * 32 * NVD_ROW) + ((c ^ swb) << 4);
+    raw[f] = *reinterpret_cast<const uint4*>(L + o);
+  };
+  // block scales of a stage as FP16 pairs: per fragment and 64-K half, the
+  // lane's two blocks (K [32h, 32h + 16) and [32h + 16, 32h + 32)), converted
+  // once per stage (exact: E4M3 values are FP16 normals)
+  h2 sc[NF][2];
+  auto read_sc = [&](int s) {
+    const uint8_t* L = lds + (s & (NVD_NBUF - 1)) * NVD_STAGE + NVD_DATA;
+    const uint4* ea = reinterpret_cast<const uint4*>(L + (wm * 32 + r32) * 32);
+    const uint32_t sh = 16u * (uint32_t)h;
+    const uint4 a0 = ea[0], a1 = ea[1];
+    const uint32_t av[4][2] = {{a0.x, a0.y}, {a0.z, a0.w}, {a1.x, a1.y}, {a1.z, a1.w}};
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) sc[t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[t][hf] >> sh, 1.0f, false);
+    // B: rows wn WN + r + 32t lie in half (wn WN) / 128, tiles from (wn WN % 128) / 32
+    const int eb = ((wn * WN) >> 7) * 32 + r32, tb = ((wn * WN) & 127) >> 5;
+    const uint4* pb = reinterpret_cast<const uint4*>(L + 2048 + eb * 32 + tb * 8);
+    if constexpr (TN == 4) {
+      const uint4 b0 = pb[0], b1 = pb[1];
+      const uint32_t bv[4][2] = {{b0.x, b0.y}, {b0.z, b0.w}, {b1.x, b1.y}, {b1.z, b1.w}};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          sc[TM + t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bv[t][hf] >> sh, 1.0f, false);
+    } else {
+      const uint4 b0 = pb[0];
+      const uint32_t bv[2][2] = {{b0.x, b0.y}, {b0.z, b0.w}};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          sc[TM + t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bv[t][hf] >> sh, 1.0f, false);
+    }
+  };
+  // FP16 operands of one K step, two sets
+  v8h cv[2][NF];
+  auto convert = [&](const uint4& r, h2 s01, int ks, v8h& dst) {
+    const h2 sp = (ks >> 1) ? h2{s01.y, s01.y} : h2{s01.x, s01.x};
+    const uint32_t word = ks == 0 ? r.x : ks == 1 ? r.y : ks == 2 ? r.z : r.w;
+    uint32_t o[4];
+    fp4x8_to_f16(word, sp, o);
+    dst = __builtin_bit_cast(v8h, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Vector-memory instructions per lane and stage: NV.  At the top of stage
+  // s the loads of stage s + 1 must be done; issued after them: stage s + 2's.
+  dma(0);
+  dma(1);
+  dma(2);
+  wait_vmcnt<2 * NV>();
+  asm volatile("s_barrier" ::: "memory");
+  read_sc(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) read_raw(0, 0, f);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) convert(raw[f], sc[f][0], 0, cv[0][f]);
+
+  // One stage: 8 K steps of TM TN MFMAs.  After MFMA i of a K step: the
+  // conversion of fragment i of the next K step (i < NF); in K step 2, the
+  // raw read of fragment i - 2 of this stage's second half (its conversion
+  // from the first half is issued by then); in K step 4 the loads of stage
+  // s + 3; in K step 6 the raw read of fragment i - 2 of the next stage's
+  // first half and, last, its scale words.  Scheduling barriers keep the order.
+  constexpr int NM = TM * TN;
+  static_assert(NF + 2 <= NM + 2 && NV <= NM, "slots");
+  for (int s = 0; s < nk; ++s) {
+    wait_vmcnt<NV>();                                      // stage s + 1 landed (this lane's share)
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int set = kk & 1;
+      const int nkk = (kk + 1) & 7;                        // next K step (of this stage or the next)
+      const int nhalf = nkk >> 2, nks = nkk & 3;
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int tm = i / TN, tn = i % TN;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cv[set][TM + tn], cv[set][tm], acc[tm][tn], 0, 0, 0);
+        if (i < NF) convert(raw[i], sc[i][nhalf], nks, cv[set ^ 1][i]);
+        if (kk == 2 && i >= 2 && i - 2 < NF) read_raw(s, 1, i - 2);
+        if (kk == 2 && i == NM - 1)
+#pragma unroll
+          for (int f = NM - 2; f < NF; ++f) read_raw(s, 1, f);
+        if (kk == 4 && i < NV) dma_part(s + 3, i);
+        if (kk == 6 && i >= 2 && i - 2 < NF) read_raw(s + 1, 0, i - 2);
+        if (kk == 6 && i == NM - 1) {
+#pragma unroll
+          for (int f = NM - 2; f < NF; ++f) read_raw(s + 1, 0, f);
+          read_sc(s + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ------------------------------------------------ epilogue (as in gemm_kernel)
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int EROW = WN * 2 + 8;
+  constexpr int ECH = WN / 8;
+  constexpr int ERI = 64 / ECH;
+  uint8_t* const E = lds + w * (32 * EROW);
+  const bool vec16 = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+  const float sbg = p.b_gs[0];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int srow = m0 + wm * 128 + tm * 32 + r32;
+    const float sa = srow < M ? (p.a_gs_per_row ? p.a_gs[srow] : p.a_gs[0]) : 0.0f;
+    uint8_t* const er = E + r32 * EROW + h * 8;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (acc[tm][tn][4 * g + i] * sa) * sbg;
+        *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
+            make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
+      }
+#pragma unroll
+    for (int it = 0; it < 32 / ERI; ++it) {
+      const int rr = it * ERI + lane / ECH, cc = lane % ECH;
+      const uint4 val = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+      const int64_t m = m0 + wm * 128 + tm * 32 + rr;
+      const int n = n0 + wn * WN + cc * 8;
+      if (m < M) {
+        uint16_t* const dst = p.c + m * p.ldc + n;
+        if (vec16 && n + 7 < N) {
+          *reinterpret_cast<uint4*>(dst) = val;
+        } else {
+          const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) dst[i] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+        }
+      }
+    }
+  }
+}
+
+template <int NW>
+static hipError_t launch_nvfp4_dma(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
+  if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
+  const size_t lds = (size_t)NVD_NBUF * NVD_STAGE;
+  static std::atomic<uint32_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_nvfp4_dma_kernel<NW>, (int)lds, lds_set); e != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(gemm_nvfp4_dma_kernel<NW>, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * NW), lds, st, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ launcher
 template <int PATH, int BM, int BN, bool BT, int DIST, int WGM, int WGN, bool PP = false, bool SWI = false>
 static hipError_t launch_t(const GemmArgs& a, hipStream_t st);
@@ -1546,7 +1839,15 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
     const bool dma_ok = a.num_groups == 0 && !a.row_index && !a.a_b128 && !a.b_b128 && a.K % 128 == 0;
     if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus))) return launch_fp8_dma(a, st);
   }
-  if (t == 7) t = -1;                    // configuration 7 where it does not apply: the measured choice
+  if constexpr (PATH == P_F16 && !BT && !SWI) {
+    // NVFP4 likewise takes its direct-to-LDS kernel on 4 waves (7) for dense
+    // launches with row-major B and K % 128 == 0 that fill the CUs; 8 is the
+    // same kernel on 8 waves (measured no faster)
+    const bool dma_ok = a.num_groups == 0 && !a.row_index && a.K % 128 == 0;
+    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus))) return launch_nvfp4_dma<4>(a, st);
+    if (dma_ok && t == 8) return launch_nvfp4_dma<8>(a, st);
+  }
+  if (t >= 7) t = -1;                    // configurations 7, 8 where they do not apply: the measured choice
   if (t < 0) {
     // measured on MI355X (8192^3, 8192x24576x4096, 8192x28672x4096,
     // 8192x1536x2048, 4096x768x2048, 4096x2048x768, grouped 128 x 512 rows):

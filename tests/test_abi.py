@@ -268,6 +268,6 @@ def test_dequantize_and_swiglu_reject_bad_arguments():
 
 def test_gemm_set_tile_range():
     m, L = _lib()
-    assert L.mx_gemm_set_tile(8) == 1 and "outside" in _err(L)
+    assert L.mx_gemm_set_tile(9) == 1 and "outside" in _err(L)
     assert L.mx_gemm_set_tile(-2) == 1
     assert L.mx_gemm_set_tile(-1) == 0                # the default; no device work

@@ -188,6 +188,55 @@ def test_mxfp8_direct_to_lds_kernel(M, N, K, a_mfma, b_kind):
     assert np.array_equal(o7, o5), f"{int(np.sum(o7 != o5))} elements differ from the 256x128 kernel"
 
 
+@pytest.mark.parametrize("M,N,K,a_mfma,b_kind", [
+    (600, 416, 384, False, "tile"),       # 3 x 2 tiles, ragged M; 3 stages of 128 K
+    (256, 256, 128, True, "row_mfma"),    # one tile, one stage
+    (544, 320, 1024, True, "tile"),       # 16x16 weight scales; 8 stages
+    (1000, 300, 640, False, "row"),       # ragged N; 5 stages
+    (768, 352, 1280, False, "row_mfma"),  # 10 stages
+])
+@pytest.mark.parametrize("tile", [7, 8])
+def test_nvfp4_direct_to_lds_kernel(M, N, K, a_mfma, b_kind, tile):
+    """Configuration 7 for NVFP4 (256x256 tiles on 4 waves, codes and scale
+    words loaded straight into LDS, each wave converting its fragments) on
+    ragged shapes, with linear and MFMA-layout scales and 16x16 weight
+    tiles: matches the oracle and gives the bits of the ping-pong 256x256
+    kernel (configuration 6)."""
+    m = mxq()
+    x = _bf16((M, K), 1.0, 82)
+    w = _bf16((N, K), 0.02, 83)
+    say(f"nvfp4 direct-to-LDS tile {tile} {M}x{N}x{K} a_mfma={a_mfma} b={b_kind}")
+    la = m.Layout.MFMA if a_mfma else m.Layout.LINEAR
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW, layout=la)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW, layout=la)
+    rc, rs, rS = ON.quantize_rowwise(F.bf16_bits_to_f64(x), "per_row")
+    a64 = ON.dequantize_f64(rc, rs, rS, "1x16", "per_row")
+    a32 = ON.dequantize_f32(rc, rs, rS, "1x16", "per_row")
+    if b_kind == "tile":
+        cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(w), block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+        B = m.Operand(m.Format.NVFP4, cw, sw, Sw, block=m.Block.TILE, gs=m.GScale.PER_TENSOR)
+        wc, ws, wS = ON.quantize_tile16(F.bf16_bits_to_f64(w))
+        bl = "16x16"
+    else:
+        lb = m.Layout.MFMA if b_kind == "row_mfma" else m.Layout.LINEAR
+        cw, sw, Sw = m.nvfp4_quantize(to_dev_bf16(w), gs=m.GScale.PER_TENSOR, layout=lb)
+        B = m.Operand(m.Format.NVFP4, cw, sw, Sw, gs=m.GScale.PER_TENSOR, layout=lb)
+        wc, ws, wS = ON.quantize_rowwise(F.bf16_bits_to_f64(w), "per_tensor")
+        bl = "1x16"
+    b64 = ON.dequantize_f64(wc, ws, wS, bl, "per_tensor")
+    b32 = ON.dequantize_f32(wc, ws, wS, bl, "per_tensor")
+    try:
+        m.mx_gemm_set_tile(tile)
+        out7 = m.mx_gemm(A, B, M, N, K)
+        _assert_gemm(out7, a64, b64, a32, b32)
+        m.mx_gemm_set_tile(6)
+        out6 = m.mx_gemm(A, B, M, N, K)
+    finally:
+        m.mx_gemm_set_tile(-1)
+    o7, o6 = from_dev_bf16(out7), from_dev_bf16(out6)
+    assert np.array_equal(o7, o6), f"{int(np.sum(o7 != o6))} elements differ from the ping-pong kernel"
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def _nv_ops(m, x, w, w_tile=True):
@@ -390,7 +439,7 @@ def test_gemm_large_tile_variants(path, bt, K):
 @pytest.mark.parametrize("bt", [False, True])
 @pytest.mark.parametrize("K", [320, 384])
 def test_every_tile_configuration_gives_the_same_bits(path, bt, K):
-    """All eight workgroup tiles (forced with mx_gemm_set_tile) on one ragged
+    """All nine workgroup tiles (forced with mx_gemm_set_tile) on one ragged
     problem: the measured default is checked against the oracle, and every
     forced tile must return the same BF16 bits (each output element sums its
     K products in the same order whatever the tile)."""
@@ -404,7 +453,7 @@ def test_every_tile_configuration_gives_the_same_bits(path, bt, K):
     _assert_gemm(ref, a64, b64, a32, b32)
     ref = from_dev_bf16(ref)
     try:
-        for t in range(8):
+        for t in range(9):
             m.mx_gemm_set_tile(t)
             out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
@@ -470,7 +519,7 @@ def test_every_tile_configuration_grouped(path):
                                       a32[rows], b32[g * N:(g + 1) * N])
             assert ok, f"expert {g}: frobenius {frob:.3e}, worst {worst:.3f}"
     try:
-        for t in range(8):
+        for t in range(9):
             m.mx_gemm_set_tile(t)
             out = run()
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
@@ -569,7 +618,7 @@ def test_grouped_tile_order_with_a_ragged_last_run(path, K, bt):
     _assert_gemm(ref, a64, b64, a32, b32)
     ref = from_dev_bf16(ref)
     try:
-        for t in range(8):
+        for t in range(9):
             m.mx_gemm_set_tile(t)
             out = from_dev_bf16(m.mx_gemm(A, B, M, N, K))
             assert np.array_equal(out, ref), f"tile {t}: {int(np.sum(out != ref))} elements differ"
