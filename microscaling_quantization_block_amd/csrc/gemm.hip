@@ -1258,6 +1258,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// B128: blockwise FP8 (128-wide power-of-two blocks, linear scales): a row's
+// one scale byte per stage pair, fetched with the aligned word holding it and
+// replicated into all four bytes (both K slices and lane halves take it).
+template <bool B128>
 __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tiles_n = gridDim.x, tiles_m = gridDim.y;
@@ -1272,13 +1276,13 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   const int wm = w >> 1, wn = w & 1;                        // wave tile: rows wm*128, columns wn*128
   const int h = lane >> 5, r32 = lane & 31;
   const int nk = K / 64;
-  const int nb32 = K >> 5;
+  const int nb32 = K >> 5, nb128 = K >> 7;
   const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
 
   const srd_t sA = make_srd(p.a, p.a_rows * p.lda);
   const srd_t sB = make_srd(p.b, p.N * p.ldb);
-  const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb32);
-  const srd_t sBs = make_srd(p.b_scales, p.b_group_scales);
+  const srd_t sAs = make_srd(p.a_scales, B128 ? (p.a_rows * nb128 + 3) & ~int64_t(3) : p.a_rows * nb32);
+  const srd_t sBs = make_srd(p.b_scales, B128 ? (p.b_group_scales + 3) & ~int64_t(3) : p.b_group_scales);
   const uint32_t arb = (uint32_t)p.lda, brb = (uint32_t)p.ldb;
 
   // Data: wave w fills rows (4w + i) * 16 .. + 16 of A and of B.
@@ -1302,10 +1306,16 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
     const int E = 16 * w + (lane >> 2), t = lane & 3;
     const int r = (E >> 5) * 128 + (E & 31) + 32 * t;
     const bool aok = m0 + r < M, bok = n0 + r < N;
-    a_sv = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 0, nb32, p.a_mfma_layout) : 0u);
     const int n = n0 + r;
-    b_sv = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 5) * nb32) : (uint32_t)scale_offset(n, 0, nb32, p.b_mfma_layout))
-                             : 0u);
+    if constexpr (B128) {
+      // the byte of pair 0 (the load takes the aligned word of pair q's byte)
+      a_sv = in_range(aok, aok ? (uint32_t)((m0 + r) * nb128) : 0u);
+      b_sv = in_range(bok, bok ? (uint32_t)((p.b_tile ? (n >> 7) : n) * nb128) : 0u);
+    } else {
+      a_sv = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 0, nb32, p.a_mfma_layout) : 0u);
+      b_sv = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 5) * nb32) : (uint32_t)scale_offset(n, 0, nb32, p.b_mfma_layout))
+                               : 0u);
+    }
   }
   const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;
   const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
@@ -1323,8 +1333,13 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
     const uint32_t L = lbase + (uint32_t)((s & (DMA_NBUF - 1)) * DMA_STAGE);
     const int q = s >> 1;
     const bool qin = s < nk;
-    dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? a_sv + (uint32_t)q * a_sstep : 0x80000000u);
-    dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? b_sv + (uint32_t)q * b_sstep : 0x80000000u);
+    if constexpr (B128) {
+      dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? (a_sv + (uint32_t)q) & ~3u : 0x80000000u);
+      dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? (b_sv + (uint32_t)q) & ~3u : 0x80000000u);
+    } else {
+      dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? a_sv + (uint32_t)q * a_sstep : 0x80000000u);
+      dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? b_sv + (uint32_t)q * b_sstep : 0x80000000u);
+    }
   };
   auto dma = [&](int s) {
 #pragma unroll
@@ -1356,15 +1371,35 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) read_part(s, set, k);
   };
-  // a stage pair's scale words (lane half h: its block's byte to byte 0/2)
+  // a stage pair's scale words (lane half h: its block's byte to byte 0/2;
+  // B128: the row's byte of the pair, in all four bytes)
   struct Sc { uint32_t a[4], b[4]; };
+  // B128: byte position of pair 0's byte in its word, per tile row of the lane
+  uint32_t a_b3[4] = {0, 0, 0, 0}, b_b3[4] = {0, 0, 0, 0};
+  if constexpr (B128) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a_b3[t] = (uint32_t)((m0 + ra + 32 * t) * nb128) & 3u;
+      b_b3[t] = (uint32_t)((p.b_tile ? ((n0 + rb + 32 * t) >> 7) : (n0 + rb + 32 * t)) * nb128) & 3u;
+    }
+  }
   auto read_sc = [&](int s) {
     const uint8_t* L = lds + (s & (DMA_NBUF - 1)) * DMA_STAGE;
     const uint4 va = *reinterpret_cast<const uint4*>(L + fsa);
     const uint4 vb = *reinterpret_cast<const uint4*>(L + fsb);
     Sc v;
-    v.a[0] = va.x >> (8 * h); v.a[1] = va.y >> (8 * h); v.a[2] = va.z >> (8 * h); v.a[3] = va.w >> (8 * h);
-    v.b[0] = vb.x >> (8 * h); v.b[1] = vb.y >> (8 * h); v.b[2] = vb.z >> (8 * h); v.b[3] = vb.w >> (8 * h);
+    if constexpr (B128) {
+      const uint32_t q = (uint32_t)(s >> 1);
+      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v.a[t] = ((wa[t] >> (8 * ((a_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
+        v.b[t] = ((wb[t] >> (8 * ((b_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
+      }
+    } else {
+      v.a[0] = va.x >> (8 * h); v.a[1] = va.y >> (8 * h); v.a[2] = va.z >> (8 * h); v.a[3] = va.w >> (8 * h);
+      v.b[0] = vb.x >> (8 * h); v.b[1] = vb.y >> (8 * h); v.b[2] = vb.z >> (8 * h); v.b[3] = vb.w >> (8 * h);
+    }
     return v;
   };
 
@@ -1466,14 +1501,15 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   }
 }
 
+template <bool B128>
 static hipError_t launch_fp8_dma(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   const size_t lds = (size_t)DMA_NBUF * DMA_STAGE;
   static std::atomic<uint32_t> lds_set{0};
-  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_dma_kernel, (int)lds, lds_set); e != hipSuccess)
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_dma_kernel<B128>, (int)lds, lds_set); e != hipSuccess)
     return e;
-  hipLaunchKernelGGL(gemm_fp8_dma_kernel, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(gemm_fp8_dma_kernel<B128>, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1510,8 +1546,11 @@ constexpr int NVD_NBUF = 4;
 // NW = 4: waves 2x2, each 128x128 (one wave per SIMD); NW = 8: waves 2x4,
 // each 128x64 (two per SIMD, so one wave's conversions and loads can issue
 // while the other's MFMAs run, at 6 conversions per 8 MFMAs instead of 8 per
-// 16).
-template <int NW>
+// 16).  GRP: grouped (MoE) launches, tiles placed as in gemm_kernel, A rows
+// gathered through the row index, B and its scales and S per group.  SWI:
+// the gate_up GEMM with SwiGLU in the epilogue (as in gemm_kernel: each
+// wave's WN logical columns read WN/2 gate rows and the matching up rows).
+template <int NW, bool GRP = false, bool SWI = false>
 __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   constexpr int WGN = NW / 2;                               // waves across N
   constexpr int WN = DMA_BN / WGN;                          // 128 or 64 columns per wave
@@ -1521,24 +1560,40 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   constexpr int SI = 8 / NW;                                // scale-word loads per operand and wave
   constexpr int NV = 2 * CI + 2 * SI;                       // vector-memory instructions per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
-  int mt, nt;
-  if (!xcd_tile(tiles_m, tiles_n, (p.N * p.K / 2) <= ((int64_t)4 << 20) ? 1 : 4, mt, nt)) return;
-  const int K = (int)p.K, N = (int)p.N, M = (int)p.M;
-  const int m0 = mt * DMA_BM, n0 = nt * DMA_BN;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int tiles_n = gridDim.x;
+  const int tiles_m = GRP ? group_mtiles<DMA_BM>(p, lane) : (int)gridDim.y;
+  int mt, nt;
+  if (!xcd_tile(tiles_m, tiles_n, (GRP || (p.N * p.K / 2) <= ((int64_t)4 << 20)) ? 1 : 4, mt, nt)) return;
+  const TileOrigin to = tile_origin<DMA_BM>(p, mt, lane);
+  if (!to.active) return;
+  const int K = (int)p.K, N = (int)p.N;
+  const int m0 = (int)to.m0, m_end = (int)to.m_end, grp = to.group;
+  const int n0 = nt * DMA_BN;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WGN, wn = w % WGN;
+  // A row behind output row m, B row behind logical column n
+  auto arow = [&](int m) -> int { return p.row_index ? p.row_index[m] : m; };
+  auto brow = [&](int n) -> int {
+    if constexpr (SWI) {
+      constexpr int P = WN / 2;
+      const int q = n / (2 * P), j = n - q * (2 * P);
+      return j < P ? q * P + j : (int)p.swiglu_inter + q * P + (j - P);
+    }
+    return n;
+  };
   const int h = lane >> 5, r32 = lane & 31;
   const int nk = K / 128;
   const int nb16 = K >> 4;
   const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
 
   const uint32_t arb = (uint32_t)(p.lda >> 1), brb = (uint32_t)(p.ldb >> 1);   // code bytes per row
+  const uint8_t* bbase = p.b + (int64_t)grp * (p.b_group_elems >> 1);
+  const uint8_t* bsbase = p.b_scales + (int64_t)grp * p.b_group_scales;
   const srd_t sA = make_srd(p.a, p.a_rows * (int64_t)arb);
-  const srd_t sB = make_srd(p.b, p.N * (int64_t)brb);
+  const srd_t sB = make_srd(bbase, p.N * (int64_t)brb);
   const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb16);
-  const srd_t sBs = make_srd(p.b_scales, p.b_group_scales);
+  const srd_t sBs = make_srd(bsbase, p.b_group_scales);
 
   // codes: wave w fills rows (CI w + i) * 16 .. + 16 of A and of B
   uint32_t a_dv[CI], b_dv[CI];
@@ -1546,9 +1601,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   for (int i = 0; i < CI; ++i) {
     const int r = (CI * w + i) * 16 + (lane >> 2);
     const uint32_t c = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
-    const bool aok = m0 + r < M, bok = n0 + r < N;
-    a_dv[i] = in_range(aok, (uint32_t)(aok ? m0 + r : 0) * arb + c * 16u);
-    b_dv[i] = in_range(bok, (uint32_t)(bok ? n0 + r : 0) * brb + c * 16u);
+    const bool aok = m0 + r < m_end, bok = n0 + r < N;
+    a_dv[i] = in_range(aok, (uint32_t)(aok ? arow(m0 + r) : 0) * arb + c * 16u);
+    b_dv[i] = in_range(bok, (uint32_t)(bok ? brow(n0 + r) : 0) * brb + c * 16u);
   }
   // scale words: entry E (32 bytes) = 32 half + r holds, for tiles t = 0..3
   // (rows 128 half + r + 32t), the stage's two words; wave w loads entries
@@ -1559,9 +1614,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   for (int i = 0; i < SI; ++i) {
     const int E = 8 * (SI * w + i) + (lane >> 3), t = (lane & 7) >> 1, sub = lane & 1;
     const int r = (E >> 5) * 128 + (E & 31) + 32 * t;
-    const bool aok = m0 + r < M, bok = n0 + r < N;
-    a_sv[i] = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 4 * sub, nb16, p.a_mfma_layout) : 0u);
-    const int n = n0 + r;
+    const bool aok = m0 + r < m_end, bok = n0 + r < N;
+    a_sv[i] = in_range(aok, aok ? (uint32_t)scale_offset(arow(m0 + r), 4 * sub, nb16, p.a_mfma_layout) : 0u);
+    const int n = bok ? brow(n0 + r) : 0;
     b_sv[i] = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 4) * nb16 + 4 * sub)
                                             : (uint32_t)scale_offset(n, 4 * sub, nb16, p.b_mfma_layout))
                                 : 0u);
@@ -1721,11 +1776,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   constexpr int ERI = 64 / ECH;
   uint8_t* const E = lds + w * (32 * EROW);
   const bool vec16 = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
-  const float sbg = p.b_gs[0];
+  const float sbg = p.b_gs[grp];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const int srow = m0 + wm * 128 + tm * 32 + r32;
-    const float sa = srow < M ? (p.a_gs_per_row ? p.a_gs[srow] : p.a_gs[0]) : 0.0f;
+    const int mrow = m0 + wm * 128 + tm * 32 + r32;
+    const float sa = mrow < m_end ? (p.a_gs_per_row ? p.a_gs[arow(mrow)] : p.a_gs[0]) : 0.0f;
     uint8_t* const er = E + r32 * EROW + h * 8;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
@@ -1737,13 +1792,39 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
         *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
             make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
       }
+    if constexpr (SWI) {
+      // gate chunk cc and up chunk cc + ECH / 2 of a staged row -> 8 values of H
+      constexpr int ECH2 = ECH / 2, ERI2 = 64 / ECH2;
+      const bool wave_in = n0 + wn * WN < N;
+#pragma unroll
+      for (int it = 0; it < 32 / ERI2; ++it) {
+        const int rr = it * ERI2 + lane / ECH2, cc = lane % ECH2;
+        const uint4 gv = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+        const uint4 uv = *reinterpret_cast<const uint4*>(E + rr * EROW + (cc + ECH2) * 16);
+        const int64_t m = m0 + wm * 128 + tm * 32 + rr;
+        const int hc = ((n0 + wn * WN) >> 1) + cc * 8;
+        if (wave_in && m < m_end) {
+          const uint4 hv = make_uint4(swiglu_bf16x2(gv.x, uv.x), swiglu_bf16x2(gv.y, uv.y),
+                                      swiglu_bf16x2(gv.z, uv.z), swiglu_bf16x2(gv.w, uv.w));
+          uint16_t* const dst = p.c + m * p.ldc + hc;
+          if (vec16) {
+            *reinterpret_cast<uint4*>(dst) = hv;
+          } else {
+            const uint32_t wv[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int it = 0; it < 32 / ERI; ++it) {
       const int rr = it * ERI + lane / ECH, cc = lane % ECH;
       const uint4 val = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
       const int64_t m = m0 + wm * 128 + tm * 32 + rr;
       const int n = n0 + wn * WN + cc * 8;
-      if (m < M) {
+      if (m < m_end) {
         uint16_t* const dst = p.c + m * p.ldc + n;
         if (vec16 && n + 7 < N) {
           *reinterpret_cast<uint4*>(dst) = val;
@@ -1758,15 +1839,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   }
 }
 
-template <int NW>
+template <int NW, bool GRP = false, bool SWI = false>
 static hipError_t launch_nvfp4_dma(const GemmArgs& a, hipStream_t st) {
-  const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
+  const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN;
+  int64_t tiles_m = GRP ? a.M / DMA_BM + a.num_groups : (a.M + DMA_BM - 1) / DMA_BM;
+  if (tiles_m < 1) tiles_m = 1;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   const size_t lds = (size_t)NVD_NBUF * NVD_STAGE;
+  auto kern = gemm_nvfp4_dma_kernel<NW, GRP, SWI>;
   static std::atomic<uint32_t> lds_set{0};
-  if (hipError_t e = ensure_lds_limit((const void*)gemm_nvfp4_dma_kernel<NW>, (int)lds, lds_set); e != hipSuccess)
-    return e;
-  hipLaunchKernelGGL(gemm_nvfp4_dma_kernel<NW>, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * NW), lds, st, a);
+  if (hipError_t e = ensure_lds_limit((const void*)kern, (int)lds, lds_set); e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1834,18 +1917,28 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
   const int64_t cus = 256;
   int t = g_tile_override;
   if constexpr (PATH == P_FP8 && !BT && !SWI) {
-    // MXFP8 takes the direct-to-LDS 256x256 kernel (configuration 7) once its
-    // tiles fill the CUs, where it applies: dense, row-major B, 32-wide blocks
-    const bool dma_ok = a.num_groups == 0 && !a.row_index && !a.a_b128 && !a.b_b128 && a.K % 128 == 0;
-    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus))) return launch_fp8_dma(a, st);
-  }
-  if constexpr (PATH == P_F16 && !BT && !SWI) {
-    // NVFP4 likewise takes its direct-to-LDS kernel on 4 waves (7) for dense
-    // launches with row-major B and K % 128 == 0 that fill the CUs; 8 is the
-    // same kernel on 8 waves (measured no faster)
+    // MXFP8 and blockwise FP8 take the direct-to-LDS 256x256 kernel
+    // (configuration 7) once its tiles fill the CUs, where it applies: dense,
+    // row-major B, K % 128 == 0
     const bool dma_ok = a.num_groups == 0 && !a.row_index && a.K % 128 == 0;
-    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus))) return launch_nvfp4_dma<4>(a, st);
-    if (dma_ok && t == 8) return launch_nvfp4_dma<8>(a, st);
+    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus)))
+      return a.a_b128 ? launch_fp8_dma<true>(a, st) : launch_fp8_dma<false>(a, st);
+  }
+  if constexpr (PATH == P_F16 && !BT) {
+    // NVFP4 likewise takes its direct-to-LDS kernel on 4 waves (7) for
+    // launches with row-major B and K % 128 == 0 that fill the CUs, dense or
+    // grouped, with or without the fused SwiGLU; 8 is the same kernel on 8
+    // waves (measured no faster; dense only)
+    const bool dma_ok = a.K % 128 == 0;
+    // grouped launches only with K >= 2048: the MoE down GEMM (K = 768, six
+    // stages per tile) measured 300 against 278 us on the ping-pong kernel,
+    // the gate_up (K = 2048) 461 against 473 us
+    if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus && (a.num_groups == 0 || a.K >= 2048)))) {
+      if (a.num_groups) return launch_nvfp4_dma<4, true, SWI>(a, st);
+      return launch_nvfp4_dma<4, false, SWI>(a, st);
+    }
+    if constexpr (!SWI)
+      if (dma_ok && t == 8 && a.num_groups == 0) return launch_nvfp4_dma<8>(a, st);
   }
   if (t >= 7) t = -1;                    // configurations 7, 8 where they do not apply: the measured choice
   if (t < 0) {

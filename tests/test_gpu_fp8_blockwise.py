@@ -137,7 +137,7 @@ def test_unit_scale_exact_and_tiles_same_bits():
     exact = F.bf16_rne(av @ bv.T)
     outs = []
     try:
-        for t in range(-1, 7):
+        for t in range(-1, 9):
             m.mx_gemm_set_tile(t)
             outs.append(from_dev_bf16(m.mx_gemm(A, B, M, N, K)))
     finally:
@@ -151,7 +151,7 @@ def test_unit_scale_exact_and_tiles_same_bits():
     cw, sw = m.fp8bw_quantize(to_dev_bf16(w), block=m.Block.TILE)
     ref = None
     try:
-        for t in range(-1, 7):
+        for t in range(-1, 9):
             m.mx_gemm_set_tile(t)
             o = from_dev_bf16(m.mx_gemm(_op(m, cx, sx), _op(m, cw, sw, tile=True), M, N, K))
             ref = o if ref is None else ref
@@ -288,3 +288,33 @@ def test_f32_scales_strided_buffers():
     rest = from_dev_bf16(out)
     assert np.all(rest[:, :40] == 0) and np.all(rest[:, 296:] == 0)      # nothing outside the slice
     assert got.shape == (R, 256)
+
+
+@pytest.mark.parametrize("M,N,K,b_tile", [(600, 256, 384, True), (300, 384, 640, False), (512, 512, 1152, True)])
+def test_fp8bw_direct_to_lds_kernel(M, N, K, b_tile):
+    """Blockwise FP8 on configuration 7 (the direct-to-LDS 256x256 kernel):
+    K = 128 x odd puts a row's scale byte at every position of its word;
+    ragged M and N; 128x128 weight tiles or 1x128 rows.  Same bits as the
+    256x128 kernel (configuration 5), within the GEMM bound of the oracle."""
+    m = mxq()
+    rs = np.random.default_rng(75)
+    x = F.bf16_rne(rs.standard_normal((M, K)))
+    w = F.bf16_rne(rs.standard_normal((N, K)) * 0.05)
+    say(f"fp8bw direct-to-LDS {M}x{N}x{K} b_tile={b_tile}")
+    cx, sx = m.fp8bw_quantize(to_dev_bf16(x))
+    if b_tile:
+        cw, sw = m.fp8bw_quantize(to_dev_bf16(w), block=m.Block.TILE)
+        b64 = OB.dequantize_f64(*OB.quantize_tile(_v(w)), "128x128")
+    else:
+        cw, sw = m.fp8bw_quantize(to_dev_bf16(w))
+        b64 = OB.dequantize_f64(*OB.quantize_rows(_v(w)))
+    a64 = OB.dequantize_f64(*OB.quantize_rows(_v(x)))
+    outs = {}
+    try:
+        for t in (7, 5):
+            m.mx_gemm_set_tile(t)
+            outs[t] = from_dev_bf16(m.mx_gemm(_op(m, cx, sx), _op(m, cw, sw, tile=b_tile), M, N, K))
+    finally:
+        m.mx_gemm_set_tile(-1)
+    assert np.array_equal(outs[7], outs[5]), f"{int(np.sum(outs[7] != outs[5]))} elements differ"
+    assert G.check(outs[7], a64, b64, a64, b64)[2]

@@ -178,7 +178,7 @@ def test_fused_swiglu_every_tile(I, dense):
                   a_rows=T)
     say(f"fused SwiGLU I={I} dense={dense}")
     try:
-        for t in range(-1, 7):
+        for t in range(-1, 9):
             m.mx_gemm_set_tile(t)
             gu = m.mx_gemm(A, B, M, 2 * I, H, **kw)
             ref = from_dev_bf16(m.mx_swiglu(gu, I))
