@@ -272,6 +272,109 @@ def cpu_baseline(min_seconds, tokens=256, feats=512):
                 seconds_per_sample_step=round(t_step, 3), sample_gemm_flops=int(flops))
 
 
+def oracle_rates(min_seconds=1.0):
+    """The oracle's own throughput per configuration on this host (part of the
+    CPU-baseline leg; no GPU): each operation on the named sample, repeated for
+    at least `min_seconds`; one JSON line each.  Quantizers are single-threaded
+    NumPy, matmuls run on the BLAS threads.  The config-4/5 samples are rows of
+    tensors drawn with NumPy at the same shapes and distributions as the GPU's
+    device-generated ones."""
+    import numpy as np
+    import synth
+    from oracle import formats as F, nvfp4 as ON, mxfp8 as OM, gemm as G
+    cores = len(os.sched_getaffinity(0))
+
+    def timed(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                return el / n
+
+    def rec(cfg, what, sample, fn, elems=None, nbytes=None, flops=None):
+        sec = timed(fn)
+        d = dict(cfg=cfg, what=what, sample=sample, seconds=round(sec, 4), cores=cores)
+        if elems:
+            d["Melem_s"] = round(elems / sec / 1e6, 2)
+        if nbytes:
+            d["GBps"] = round(nbytes / sec / 1e9, 3)
+        if flops:
+            d["GFLOPs"] = round(flops / sec / 1e9, 2)
+        print(json.dumps(d), flush=True)
+
+    f64 = F.bf16_bits_to_f64
+    d = synth.config1()
+    x, w = f64(d["x"]), f64(d["w"])
+    n = x.size
+    rec(1, "mxfp8 1x32 quantize", "whole 256x512", lambda: OM.quantize_rowwise(x), n, 3 * n + n // 32)
+    c, sc = OM.quantize_rowwise(x)
+    cw, sw = OM.quantize_rowwise(w)
+    rec(1, "mxfp8 dequantize", "whole", lambda: OM.dequantize_bf16(c, sc), n, n + n // 32 + 2 * n)
+    rec(1, "mxfp8 GEMM f64 (dequantize, then matmul)", "whole 256x512x256",
+        lambda: G.gemm_f64(OM.dequantize_f64(c, sc), OM.dequantize_f64(cw, sw)), flops=2 * 256 * 256 * 512)
+    d = synth.config2()
+    x, w, dy = f64(d["x"]), f64(d["w"]), f64(d["dy"])
+    n, nw = x.size, w.size
+    rec(2, "nvfp4 per-token quantize", "whole 4096x2048", lambda: ON.quantize_rowwise(x, "per_row"), n,
+        2 * n + n // 2 + n // 16 + 4096 * 4)
+    rec(2, "nvfp4 16x16 weight quantize", "whole 768x2048", lambda: ON.quantize_tile16(w), nw,
+        4 * nw + nw // 2 + nw // 256 + 4)
+    xc, xs, xS = ON.quantize_rowwise(x, "per_row")
+    wc, wsb, wS = ON.quantize_tile16(w)
+    rec(2, "nvfp4 FPROP f64", "whole 4096x768x2048",
+        lambda: G.gemm_f64(ON.dequantize_f64(xc, xs, xS, "1x16", "per_row"),
+                           ON.dequantize_f64(wc, wsb, wS, "16x16", "per_tensor")), flops=2 * 4096 * 768 * 2048)
+    rec(2, "nvfp4 dequantize (W)", "whole", lambda: ON.dequantize_bf16(wc, wsb, wS, "16x16", "per_tensor"), nw,
+        nw // 2 + nw // 256 + 2 * nw)
+    wdq = f64(ON.dequantize_bf16(wc, wsb, wS, "16x16", "per_tensor"))
+    rec(2, "dequantized-backward DGRAD f64", "whole 4096x2048x768", lambda: G.gemm_f64(dy, wdq.T.copy()),
+        flops=2 * 4096 * 2048 * 768)
+    d = synth.config3()
+    x3 = f64(d["x"][:2048])
+    n = x3.size
+    rec(3, "nvfp4 per-token quantize (X)", "2048 of 8192 tokens", lambda: ON.quantize_rowwise(x3, "per_row"), n,
+        2 * n + n // 2 + n // 16 + 2048 * 4)
+    we = f64(d["w_gu"][0])
+    rec(3, "nvfp4 expert weight quantize (one S over gate and up)", "1 of 128 experts",
+        lambda: ON.quantize_rowwise(we, "per_tensor"), we.size, 4 * we.size + we.size // 2 + we.size // 16 + 4)
+    wc, ws, wS = ON.quantize_rowwise(we, "per_tensor")
+    xc, xs, xS = ON.quantize_rowwise(x3[:512], "per_row")
+    rec(3, "grouped gate_up GEMM f64, one expert", "512 rows x 1536 x 2048",
+        lambda: G.gemm_f64(ON.dequantize_f64(xc, xs, xS, "1x16", "per_row"),
+                           ON.dequantize_f64(wc, ws, wS, "1x16", "per_tensor")), flops=2 * 512 * 1536 * 2048)
+    for cfg in (4, 5):
+        K = 4096
+        xs_ = f64(synth.normal_bf16((256, K), 1.0, cfg, 0))
+        ws_ = f64(synth.normal_bf16((1024, K), 0.02, cfg, 1))
+        n = xs_.size
+        if cfg == 4:
+            rec(4, "mxfp8 dual (rowwise + columnwise) quantize", "256 x 4096",
+                lambda: (OM.quantize_rowwise(xs_), OM.quantize_colwise(xs_)), n, 4 * n + 2 * (n // 32))
+            rec(4, "mxfp8 32x32 weight quantize", "1024 x 4096", lambda: OM.quantize_tile32(ws_), ws_.size,
+                3 * ws_.size)
+            a, sa = OM.quantize_rowwise(xs_)
+            b, sb = OM.quantize_tile32(ws_)
+            rec(4, "mxfp8 FPROP f64", "256 x 1024 x 4096 of 8192 x 24576 x 4096",
+                lambda: G.gemm_f64(OM.dequantize_f64(a, sa), OM.dequantize_f64(b, sb, "32x32")),
+                flops=2 * 256 * 1024 * K)
+        else:
+            rec(5, "nvfp4 per-token RNE quantize", "256 x 4096", lambda: ON.quantize_rowwise(xs_, "per_row"), n,
+                2 * n + n // 2 + n // 16 + 256 * 4)
+            rec(5, "nvfp4 per-token SR quantize", "256 x 4096",
+                lambda: ON.quantize_rowwise(xs_, "per_row", rnd="sr"), n, 2 * n + n // 2 + n // 16 + 256 * 4)
+            rec(5, "nvfp4 columnwise SR quantize", "256 x 4096", lambda: ON.quantize_colwise(xs_, rnd="sr"), n,
+                4 * n + n // 2 + n // 16 + 4)
+            rec(5, "nvfp4 16x16 weight quantize", "1024 x 4096", lambda: ON.quantize_tile16(ws_), ws_.size,
+                4 * ws_.size + ws_.size // 2 + ws_.size // 256 + 4)
+            a, sa, Sa = ON.quantize_rowwise(xs_, "per_row")
+            b, sb, Sb = ON.quantize_tile16(ws_)
+            rec(5, "nvfp4 FPROP f64", "256 x 1024 x 4096 of 32768 x 28672 x 4096",
+                lambda: G.gemm_f64(ON.dequantize_f64(a, sa, Sa, "1x16", "per_row"),
+                                   ON.dequantize_f64(b, sb, Sb, "16x16", "per_tensor")), flops=2 * 256 * 1024 * K)
+
+
 # ---------------------------------------------------------------- config 2
 
 def config2_step(m, torch, steps):
@@ -730,7 +833,12 @@ def main():
                          "(one JSON line per measurement)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
+    ap.add_argument("--oracle-rates", action="store_true",
+                    help="only time the CPU oracle per configuration on this host (no GPU)")
     args = ap.parse_args()
+    if args.oracle_rates:
+        oracle_rates()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
