@@ -67,7 +67,8 @@ GEMM_SOURCE = os.path.join(ROOT, "microscaling_quantization_block_amd", "csrc", 
 
 def measured_reference(m, torch):
     """Context for the spec peaks: the bandwidth of a plain device copy of
-    COPY_BYTES (read + write bytes over time, HIP events, 20 copies), and the
+    COPY_BYTES (read + write bytes over time, HIP events, 20 copies) and of a
+    reduction that only reads them, and the
     host cost of one library call from Python (binding + C ABI + launch,
     2000 back-to-back calls of a 64x64 MXFP8 dequantize, no synchronization)."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -82,7 +83,20 @@ def measured_reference(m, torch):
     b.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * COPY_BYTES * 20 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # read-only: torch's sum over the same bytes as float32 (a reduction reads
+    # everything once and writes a scalar)
+    f = src.view(torch.float32)
+    for _ in range(3):
+        f.sum()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(20):
+        f.sum()
+    b.record()
+    torch.cuda.synchronize()
+    read_gbps = COPY_BYTES * 20 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, f
     x = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     c, s = m.mx_quantize(x)
     out = torch.empty_like(x)
@@ -95,8 +109,10 @@ def measured_reference(m, torch):
     host_us = (time.perf_counter() - t0) / 2000 * 1e6
     torch.cuda.synchronize()
     return {"copy_GBps": round(copy_gbps, 1), "copy_frac_of_hbm_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "read_GBps": round(read_gbps, 1), "read_frac_of_hbm_peak": round(read_gbps / PEAK_HBM_GBPS, 4),
             "host_us_per_call": round(host_us, 2),
-            "note": "device copy of 256 MiB (read + write bytes); host time of one Python -> C ABI call"}
+            "note": "device copy of 256 MiB (read + write bytes); a float32 sum over the same 256 MiB (read "
+                    "bytes); host time of one Python -> C ABI call"}
 
 
 def copy_calibration():
