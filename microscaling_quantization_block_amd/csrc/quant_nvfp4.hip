@@ -106,14 +106,7 @@ __device__ __forceinline__ uint32_t nv_encode8(uint4 v, float r, u32x4 draws) {
     y[2 * i + 1] = nv_frame<TINY>(bf16_hi(w[i])) * r;
   }
   if (SR) {
-    uint32_t out = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t qa = f32_to_e2m1_sr(y[2 * i], d[i] & 0xFFFFu);
-      uint32_t qb = f32_to_e2m1_sr(y[2 * i + 1], d[i] >> 16);
-      out |= (qa | (qb << 4)) << (8 * i);
-    }
-    return out;
+    return f32x8_to_e2m1_sr(y, d);
   }
   uint32_t out = 0;
   out = e2m1_rne_pair<0>(out, y[0], y[1]);
@@ -668,6 +661,10 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
         rr16[i] = (k & 1) ? (d >> 16) : (d & 0xFFFFu);
       }
     }
+    // the draws of rows 2i and 2i + 1 as one word (low and high half)
+    uint32_t dw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dw[i] = rr16[2 * i] | (rr16[2 * i + 1] << 16);
     float u[16];
     if (RHT) {
       rht_column(col, sign_mask, u);
@@ -690,12 +687,8 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     }
     uint32_t out[2] = {0, 0};
     if (SR) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t qa = f32_to_e2m1_sr(yv[2 * i], rr16[2 * i]);
-        uint32_t qb = f32_to_e2m1_sr(yv[2 * i + 1], rr16[2 * i + 1]);
-        out[i >> 2] |= (qa | (qb << 4)) << (8 * (i & 3));
-      }
+      out[0] = f32x8_to_e2m1_sr(yv, dw);
+      out[1] = f32x8_to_e2m1_sr(yv + 8, dw + 4);
     } else {
       out[0] = e2m1_rne_pair<0>(out[0], yv[0], yv[1]);
       out[0] = e2m1_rne_pair<1>(out[0], yv[2], yv[3]);

@@ -5,7 +5,8 @@ on inputs whose second scale S is tiny.
   and the smallest subnormal), both signs, under each of the 126 positive
   finite E4M3 block scales and several caller-given S (powers of two, whose
   anchors then give each scale exactly, and one that is not), through the
-  rowwise quantizer: codes and scales byte-identical to the oracle.  The same
+  rowwise quantizer: codes and scales byte-identical to the oracle, for
+  round-to-nearest-even and for stochastic rounding (two seeds).  The same
   with a block maximum past 448 * 6 * S (a saturated block scale, elements
   far beyond 6, including products that overflow binary32).
 * Rows, tiles and columns whose S is below 2^-64 (where the element chain
@@ -55,11 +56,12 @@ def _rows(blocks, per_row=64):
     return np.concatenate([blocks, z]).reshape(-1, per_row * 16)
 
 
-def _check_given(m, x, S, what):
-    say(f"nvfp4 element encode {what}: {x.shape[0]}x{x.shape[1]} given S={float(S):.4g}")
+def _check_given(m, x, S, what, rnd="rne", seed=0):
+    say(f"nvfp4 element encode {what}: {x.shape[0]}x{x.shape[1]} given S={float(S):.4g} {rnd} seed {seed}")
     Sd = __import__("torch").tensor([float(S)], dtype=__import__("torch").float32, device="cuda")
-    c, s, _ = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.GIVEN, gscales=Sd)
-    rc, rs, _ = ON.quantize_rowwise(F.bf16_bits_to_f64(x), "given", S_given=S)
+    c, s, _ = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.GIVEN, gscales=Sd,
+                               rnd=m.Round.SR if rnd == "sr" else m.Round.RNE, seed=seed)
+    rc, rs, _ = ON.quantize_rowwise(F.bf16_bits_to_f64(x), "given", rnd=rnd, seed=seed, S_given=S)
     assert np.array_equal(to_np(s), rs)
     assert np.array_equal(to_np(c), rc)
     return rs
@@ -81,8 +83,27 @@ def test_every_bf16_magnitude_under_every_e4m3_block_scale(S):
         assert set(np.unique(rs).tolist()) >= set(range(1, 127))
 
 
+@pytest.mark.parametrize("seed", [3, 2 ** 40 + 17])
+@pytest.mark.parametrize("S", [1.0, 0.0123, 2.0 ** -70])
+def test_every_bf16_magnitude_under_every_e4m3_block_scale_sr(S, seed):
+    """Stochastic rounding onto E2M1 (the hardware conversion with the
+    magnitude first rounded up to a multiple of 2^-17) of the same inputs:
+    every BF16 magnitude that can share a block with a given block maximum,
+    under all 126 positive finite block scales.  With S = 0.0123 the
+    reciprocals are not powers of two, so y = x * r carries full binary32
+    mantissas (the fraction bits below 2^-16 decide the boundary cases);
+    2^-70 runs the chain in the scaled frame."""
+    m = mxq()
+    S = np.float32(S)
+    e4 = F.e4m3_value(np.arange(1, 127))
+    anchors = F.bf16_rne(e4 * 6.0 * np.float64(S))
+    x = _rows(np.concatenate([_blocks_for(a) for a in anchors]))
+    _check_given(m, x, S, "all scales", rnd="sr", seed=seed)
+
+
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
 @pytest.mark.parametrize("S", [1.0, 2.0 ** -70])
-def test_saturated_block_scale_and_overflowing_products(S):
+def test_saturated_block_scale_and_overflowing_products(S, rnd):
     """Block maxima far past 448 * 6 * S: the scale saturates at 448 and the
     elements at 6, including products x * r beyond the binary32 range."""
     m = mxq()
@@ -90,7 +111,7 @@ def test_saturated_block_scale_and_overflowing_products(S):
     anchors = F.bf16_rne(np.array([448.0 * 6.0 * 1.5, 448.0 * 6.0 * 2.0 ** 20, 3.0e38]) * np.float64(S))
     anchors = np.concatenate([anchors, np.array([0x7F7F], dtype=np.uint16)])
     x = _rows(np.concatenate([_blocks_for(a) for a in anchors]))
-    rs = _check_given(m, x, S, "saturation")
+    rs = _check_given(m, x, S, "saturation", rnd=rnd, seed=11)
     assert 0x7E in rs
 
 
