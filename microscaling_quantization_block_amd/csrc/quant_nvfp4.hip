@@ -34,6 +34,9 @@
 //   * nvfp4_col_kernel: each lane owns 8 columns x 16 rows, each column one
 //     16x1 block, written into the transposed copy (optionally after the
 //     random Hadamard transform of the 16 rows).
+//   * nvfp4_col_sr_pair_kernel: the same copy with stochastic rounding and
+//     no transform, each 16-row block split over two lanes (registers for
+//     four waves per SIMD instead of two).
 //   * per-tensor scale: a one-thread kernel zeroes gscale[0], then an
 //     unsigned atomic max on the magnitude bits (exact and order-independent)
 //     leaves A there tagged with bit 31.  The quantize kernel that follows
@@ -705,6 +708,72 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
   }
 }
 
+// Columnwise with stochastic rounding, no transform: the 16-row block of a
+// column is split over two lanes (rows 0-7 and 8-15), which take the block
+// maximum from each other.  A lane's 8 rows of data and their 8 Philox calls
+// then fit in about half the registers of the kernel above, which holds all
+// 16 (two waves per SIMD there, four here).  The two lanes of a pair compute
+// the same block scale; each writes its 4 code bytes, the first the scale.
+// A workgroup covers 8 strips (128 rows) x 128 columns.
+__global__ __launch_bounds__(256) void nvfp4_col_sr_pair_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
+    float* __restrict__ gscales, int gmode, int mfma_layout, uint64_t seed,
+    uint32_t stream_id, uint32_t tensor_tag, int64_t n_ct) {
+  const float S = tensor_scale(gscales, gmode);
+  if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
+  const int lane = threadIdx.x & 63;
+  const int hf = lane & 1;
+  const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
+  const int64_t strips = rows >> 4;
+  const int64_t strip = rt * 8 + ((lane >> 1) & 7);
+  const int64_t c0 = ct * 128 + (threadIdx.x >> 6) * 32 + (lane >> 4) * 8;
+  // the two lanes of a pair leave together (same strip, same columns)
+  if (strip >= strips || c0 >= cols) return;
+  const int64_t r0 = strip * 16 + hf * 8;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + c0);
+  u32x4 dr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + c0) >> 3, seed, stream_id, tensor_tag);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    // column k of row i: half (k & 1) of word (k >> 1); so is its draw
+    float u[8];
+    uint32_t rr16[8];
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = (k >> 1) == 0 ? v[i].x : (k >> 1) == 1 ? v[i].y : (k >> 1) == 2 ? v[i].z : v[i].w;
+      const uint32_t b = (k & 1) ? (w & 0xFFFF0000u) : (w << 16);     // binary32 bits
+      u[i] = __uint_as_float(b);
+      mb = umax(mb, b & 0x7FFFFFFFu);
+      const uint32_t d = (k >> 1) == 0 ? dr[i].x : (k >> 1) == 1 ? dr[i].y : (k >> 1) == 2 ? dr[i].z : dr[i].w;
+      rr16[i] = (k & 1) ? (d >> 16) : (d & 0xFFFFu);
+    }
+    mb = umax(mb, lane_xor_u32(mb, 1));
+    const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
+    // a zero block has r = 0, and a finite u times 0 is u's signed zero
+    float yv[8];
+    if (S < TINY_S) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[i] = nv_frame<true>(u[i]) * bs.r;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[i] = u[i] * bs.r;
+    }
+    uint32_t dw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dw[i] = rr16[2 * i] | (rr16[2 * i + 1] << 16);
+    const uint32_t q = f32x8_to_e2m1_sr(yv, dw);
+    const int64_t c = c0 + k;
+    *reinterpret_cast<uint32_t*>(codes + c * ld_codes + (r0 >> 1)) = q;
+    if (hf == 0) bscales[scale_offset(c, strip, strips, mfma_layout)] = (uint8_t)bs.code;
+  }
+}
+
 // ------------------------------------------------------------ tensor amax
 __global__ void nv_zero_u32(uint32_t* p) { *p = 0u; }
 
@@ -908,9 +977,14 @@ hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64
   if (rht) {
     if (sr) go(nvfp4_col_kernel<true, true>);
     else go(nvfp4_col_kernel<false, true>);
+  } else if (sr) {
+    // workgroup tile 128 rows x 128 columns
+    const int64_t n_rt2 = (rows / 16 + 7) / 8;
+    if (n_rt2 * n_ct > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(nvfp4_col_sr_pair_kernel, dim3((unsigned)(n_rt2 * n_ct)), dim3(256), 0, st, x, rows, cols,
+                       ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag, n_ct);
   } else {
-    if (sr) go(nvfp4_col_kernel<true, false>);
-    else go(nvfp4_col_kernel<false, false>);
+    go(nvfp4_col_kernel<false, false>);
   }
   return hipGetLastError();
 }
