@@ -34,9 +34,9 @@
 //   * nvfp4_col_kernel: each lane owns 8 columns x 16 rows, each column one
 //     16x1 block, written into the transposed copy (optionally after the
 //     random Hadamard transform of the 16 rows).
-//   * nvfp4_col_sr_pair_kernel: the same copy with stochastic rounding and
-//     no transform, each 16-row block split over two lanes (registers for
-//     four waves per SIMD instead of two).
+//   * nvfp4_col_pair_kernel: the same copy without the transform, each
+//     16-row block split over two lanes (with stochastic rounding, registers
+//     for four waves per SIMD instead of two).
 //   * per-tensor scale: a one-thread kernel zeroes gscale[0], then an
 //     unsigned atomic max on the magnitude bits (exact and order-independent)
 //     leaves A there tagged with bit 31.  The quantize kernel that follows
@@ -708,14 +708,15 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
   }
 }
 
-// Columnwise with stochastic rounding, no transform: the 16-row block of a
-// column is split over two lanes (rows 0-7 and 8-15), which take the block
-// maximum from each other.  A lane's 8 rows of data and their 8 Philox calls
-// then fit in about half the registers of the kernel above, which holds all
-// 16 (two waves per SIMD there, four here).  The two lanes of a pair compute
+// Columnwise without the transform: the 16-row block of a column is split
+// over two lanes (rows 0-7 and 8-15), which take the block maximum from each
+// other.  With stochastic rounding a lane's 8 rows of data and their 8
+// Philox calls then fit in about half the registers of the kernel above,
+// which holds all 16 (two waves per SIMD there, four here).  The two lanes of a pair compute
 // the same block scale; each writes its 4 code bytes, the first the scale.
 // A workgroup covers 8 strips (128 rows) x 128 columns.
-__global__ __launch_bounds__(256) void nvfp4_col_sr_pair_kernel(
+template <bool SR>
+__global__ __launch_bounds__(256) void nvfp4_col_pair_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ bscales,
     float* __restrict__ gscales, int gmode, int mfma_layout, uint64_t seed,
@@ -735,9 +736,11 @@ __global__ __launch_bounds__(256) void nvfp4_col_sr_pair_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + c0);
   u32x4 dr[8];
+  if (SR) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + c0) >> 3, seed, stream_id, tensor_tag);
+    for (int i = 0; i < 8; ++i)
+      dr[i] = philox_draws8((uint64_t)((r0 + i) * cols + c0) >> 3, seed, stream_id, tensor_tag);
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     // column k of row i: half (k & 1) of word (k >> 1); so is its draw
@@ -750,8 +753,10 @@ __global__ __launch_bounds__(256) void nvfp4_col_sr_pair_kernel(
       const uint32_t b = (k & 1) ? (w & 0xFFFF0000u) : (w << 16);     // binary32 bits
       u[i] = __uint_as_float(b);
       mb = umax(mb, b & 0x7FFFFFFFu);
-      const uint32_t d = (k >> 1) == 0 ? dr[i].x : (k >> 1) == 1 ? dr[i].y : (k >> 1) == 2 ? dr[i].z : dr[i].w;
-      rr16[i] = (k & 1) ? (d >> 16) : (d & 0xFFFFu);
+      if (SR) {
+        const uint32_t d = (k >> 1) == 0 ? dr[i].x : (k >> 1) == 1 ? dr[i].y : (k >> 1) == 2 ? dr[i].z : dr[i].w;
+        rr16[i] = (k & 1) ? (d >> 16) : (d & 0xFFFFu);
+      }
     }
     mb = umax(mb, lane_xor_u32(mb, 1));
     const BlockScale bs = nv_block_scale(__uint_as_float(mb), S);
@@ -764,10 +769,18 @@ __global__ __launch_bounds__(256) void nvfp4_col_sr_pair_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) yv[i] = u[i] * bs.r;
     }
-    uint32_t dw[4];
+    uint32_t q = 0;
+    if (SR) {
+      uint32_t dw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dw[i] = rr16[2 * i] | (rr16[2 * i + 1] << 16);
-    const uint32_t q = f32x8_to_e2m1_sr(yv, dw);
+      for (int i = 0; i < 4; ++i) dw[i] = rr16[2 * i] | (rr16[2 * i + 1] << 16);
+      q = f32x8_to_e2m1_sr(yv, dw);
+    } else {
+      q = e2m1_rne_pair<0>(q, yv[0], yv[1]);
+      q = e2m1_rne_pair<1>(q, yv[2], yv[3]);
+      q = e2m1_rne_pair<2>(q, yv[4], yv[5]);
+      q = e2m1_rne_pair<3>(q, yv[6], yv[7]);
+    }
     const int64_t c = c0 + k;
     *reinterpret_cast<uint32_t*>(codes + c * ld_codes + (r0 >> 1)) = q;
     if (hf == 0) bscales[scale_offset(c, strip, strips, mfma_layout)] = (uint8_t)bs.code;
@@ -978,11 +991,12 @@ hipError_t launch_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, int64
     if (sr) go(nvfp4_col_kernel<true, true>);
     else go(nvfp4_col_kernel<false, true>);
   } else if (sr) {
-    // workgroup tile 128 rows x 128 columns
+    // workgroup tile 128 rows x 128 columns (the pair split measured slower
+    // for round-to-nearest-even: 135.8 against 127.8 us at 32768x4096)
     const int64_t n_rt2 = (rows / 16 + 7) / 8;
     if (n_rt2 * n_ct > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(nvfp4_col_sr_pair_kernel, dim3((unsigned)(n_rt2 * n_ct)), dim3(256), 0, st, x, rows, cols,
-                       ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag, n_ct);
+    hipLaunchKernelGGL(nvfp4_col_pair_kernel<true>, dim3((unsigned)(n_rt2 * n_ct)), dim3(256), 0, st, x, rows,
+                       cols, ld_x, codes, ld_codes, bscales, gscales, gmode, (int)mfma, seed, sid, tag, n_ct);
   } else {
     go(nvfp4_col_kernel<false, false>);
   }
