@@ -817,7 +817,15 @@ def rows_report():
         (lambda B=B: m.mx_gemm_swiglu(A, B, Mr, I3, H3, out=hf, group_row_offsets=off_d, a_row_index=idx_d,
                                       a_rows=T3)) for B in Bs], 10),
         flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS, sets=nsets)
-    del hf, Bs, wsets
+    cq = torch.empty((Mr, I3 // 2), dtype=torch.uint8, device=dev)
+    sq = torch.empty((Mr * (I3 // 16),), dtype=torch.uint8, device=dev)
+    Sq = torch.empty((Mr,), dtype=torch.float32, device=dev)
+    out("f3", "MoE grouped gate_up with SwiGLU and per-token Q(H) in the epilogue (writes Q(H))", [Mr, N2, H3],
+        _time_rot(torch, [(lambda B=B: m.mx_gemm_swiglu_nvfp4(
+            A, B, Mr, I3, H3, group_row_offsets=off_d, a_row_index=idx_d, a_rows=T3, codes=cq, block_scales=sq,
+            gscales=Sq)) for B in Bs], 10),
+        flops=2.0 * Mr * N2 * H3, peak=PEAK_F16_TFLOPS, sets=nsets)
+    del hf, Bs, wsets, cq, sq, Sq
     ch, sh, Sh = m.nvfp4_quantize(h)
     quant_row("a8", "MoE per-token Q(H)", h, lambda xi: lambda: m.nvfp4_quantize(
         xi, codes=ch, block_scales=sh, gscales=Sh), Mr * I3 * 2 + Mr * I3 // 2 + Mr * I3 // 16 + Mr * 4)

@@ -515,14 +515,43 @@ mxq_status mx_swiglu(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld
  *   h, ldh    BF16 output [M, inter], row-major
  *   other arguments as for mx_gemm (grouped launch, gather index)
  * Shapes: inter % 64 == 0, K % 64 == 0.  Other formats or a transposed B give
- * MXQ_EUNSUPPORTED.  The per-token requantization of H is a separate call
- * (nvfp4_quantize): its second scale needs the whole row of H, which no
- * workgroup tile holds.
+ * MXQ_EUNSUPPORTED.  The per-token requantization of H is either a separate
+ * call (nvfp4_quantize) or fused, in mx_gemm_swiglu_nvfp4.
  */
 mxq_status mx_gemm_swiglu(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t inter,
                           int64_t K, int64_t a_rows, uint16_t* h, int64_t ldh, int32_t num_groups,
                           const int32_t* group_row_offsets, const int32_t* a_row_index,
                           void* stream);
+
+/*
+ * mx_gemm_swiglu_nvfp4 -- the MoE gate_up GEMM with the SwiGLU and the
+ * per-token NVFP4 requantization of H fused into its epilogue: the FP4
+ * codes, E4M3 block scales and FP32 token scales that
+ * nvfp4_quantize(H, ROW, PER_ROW, RNE) writes for H = mx_gemm_swiglu(...),
+ * byte for byte, without H's trip through HBM; H itself too when h is given.
+ * The pages describe the shared quantizer as one fused operation emitting
+ * packed FP4, block scales and token scales ("Miles Blackwell RL Troca a
+ * Uniformidade BF16 por MXFP8 e NVFP4 Nativos", section "Um Quantizador
+ * Compartilhado É o Verdadeiro Mecanismo").
+ *   a, b, M, inter, K, a_rows, num_groups, group_row_offsets, a_row_index
+ *                 as for mx_gemm_swiglu
+ *   codes         device, [M, inter / 2] bytes, row stride ld_codes (a
+ *                 multiple of 16, rows 16-byte aligned), two codes a byte
+ *                 (even column in the low nibble)
+ *   block_scales  device, M * inter / 16 E4M3 bytes, in `layout` (LINEAR:
+ *                 row-major [M, inter / 16]; MFMA: as nvfp4_quantize's MFMA
+ *                 layout, M % 32 == 0)
+ *   gscales       device, M floats: S of each token row (amax(H row) / 2688)
+ *   h, ldh        optional BF16 H [M, inter] (NULL: not written)
+ * Shapes: inter in {256, 512, 768} (a workgroup holds 32 whole rows of H),
+ * K % 64 == 0.  Errors as for mx_gemm_swiglu; MXQ_EALIGN for misaligned
+ * outputs.  Nothing is written on an error.
+ */
+mxq_status mx_gemm_swiglu_nvfp4(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t inter,
+                                int64_t K, int64_t a_rows, uint8_t* codes, int64_t ld_codes,
+                                uint8_t* block_scales, int32_t layout, float* gscales, uint16_t* h,
+                                int64_t ldh, int32_t num_groups, const int32_t* group_row_offsets,
+                                const int32_t* a_row_index, void* stream);
 
 const char* mxq_status_str(mxq_status s);
 const char* mxq_last_error(void);

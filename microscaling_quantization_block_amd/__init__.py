@@ -21,7 +21,7 @@ __all__ = ["Format", "Block", "GScale", "Round", "Layout", "Operand", "MXQError"
            "mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
            "nvfp4_quantize_rowcol", "fp8bw_quantize",
            "fp8bw_quantize_f32",
-           "mx_dequantize", "mx_gemm", "mx_gemm_swiglu",
+           "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_gemm_swiglu_nvfp4",
            "mx_swiglu", "mx_gemm_set_tile", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,12 +103,15 @@ def lib():
                           vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_gemm_swiglu.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
                           vp, i64, ctypes.c_int32, vp, vp, vp]
+    L.mx_gemm_swiglu_nvfp4.argtypes = [ctypes.POINTER(_Operand), ctypes.POINTER(_Operand), i64, i64, i64, i64,
+                                       vp, i64, vp, ctypes.c_int32, vp, vp, i64, ctypes.c_int32, vp, vp, vp]
     L.mx_swiglu.argtypes = [vp, i64, i64, i64, vp, i64, vp]
     L.mx_gemm_set_tile.argtypes = [ctypes.c_int32]
     for f in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t", "nvfp4_quantize_rht",
            "nvfp4_quantize_rowcol", "fp8bw_quantize",
               "fp8bw_quantize_f32",
-              "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_swiglu", "mx_gemm_set_tile"):
+              "mx_dequantize", "mx_gemm", "mx_gemm_swiglu", "mx_gemm_swiglu_nvfp4", "mx_swiglu",
+              "mx_gemm_set_tile"):
         getattr(L, f).restype = ci
     L.mxq_last_error.restype = ctypes.c_char_p
     L.mxq_status_str.restype = ctypes.c_char_p
@@ -396,11 +399,12 @@ def _check_gemm_args(a, b, M, ncols, out, group_row_offsets, a_row_index, num_gr
         if op.gscales is not None and (op.gscales.dtype != torch.float32 or not op.gscales.is_cuda
                                        or not op.gscales.is_contiguous()):
             raise TypeError(f"{name}.gscales must be a contiguous float32 CUDA tensor")
-    if not (isinstance(out, torch.Tensor) and out.is_cuda and out.dtype == torch.bfloat16 and out.dim() == 2):
-        raise TypeError("out must be a 2-D bfloat16 CUDA tensor")
-    if out.shape[0] < M or out.shape[1] < ncols or out.stride(1) != 1:
-        raise ValueError(f"out must hold [{M}, {ncols}] with unit column stride, got {tuple(out.shape)} "
-                         f"strides {out.stride()}")
+    if out is not None:
+        if not (isinstance(out, torch.Tensor) and out.is_cuda and out.dtype == torch.bfloat16 and out.dim() == 2):
+            raise TypeError("out must be a 2-D bfloat16 CUDA tensor")
+        if out.shape[0] < M or out.shape[1] < ncols or out.stride(1) != 1:
+            raise ValueError(f"out must hold [{M}, {ncols}] with unit column stride, got {tuple(out.shape)} "
+                             f"strides {out.stride()}")
     if group_row_offsets is not None:
         g = group_row_offsets
         if not (isinstance(g, torch.Tensor) and g.is_cuda and g.dtype == torch.int32 and g.dim() == 1
@@ -452,6 +456,43 @@ def mx_gemm_swiglu(a, b, M, inter, K, out=None, group_row_offsets=None, a_row_in
                                 out.stride(0), ng, _ptr(group_row_offsets), _ptr(a_row_index),
                                 _stream(stream)))
     return out
+
+
+def mx_gemm_swiglu_nvfp4(a, b, M, inter, K, group_row_offsets=None, a_row_index=None, a_rows=None,
+                         layout=Layout.LINEAR, with_h=False, codes=None, block_scales=None, gscales=None,
+                         h=None, stream=None):
+    """The gate_up GEMM with SwiGLU and the per-token NVFP4 quantization of H
+    in its epilogue.  Returns (codes [M, inter/2] uint8, block scales uint8,
+    per-token S float32 [M]), the bytes nvfp4_quantize(H) writes, plus H
+    [M, inter] BF16 when with_h (or h) is given."""
+    dev = a.data.device
+    if codes is None:
+        codes = torch.empty((M, inter // 2), dtype=torch.uint8, device=dev)
+    if block_scales is None:
+        block_scales = torch.empty((M * (inter // 16),), dtype=torch.uint8, device=dev)
+    if gscales is None:
+        gscales = torch.empty((M,), dtype=torch.float32, device=dev)
+    if h is None and with_h:
+        h = torch.empty((M, inter), dtype=torch.bfloat16, device=dev)
+    _check_gemm_args(a, b, M, inter, h, group_row_offsets, a_row_index)
+    _check_2d(codes, torch.uint8, "codes")
+    if codes.shape[0] < M or codes.shape[1] < inter // 2:
+        raise ValueError(f"codes must hold [{M}, {inter // 2}]")
+    for name, t, dt, n in (("block_scales", block_scales, torch.uint8, M * (inter // 16)),
+                           ("gscales", gscales, torch.float32, M)):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dt and t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous {dt} CUDA tensor")
+        if t.numel() < n:
+            raise ValueError(f"{name} needs {n} elements")
+    ng = 0 if group_row_offsets is None else group_row_offsets.numel() - 1
+    if a_rows is None:
+        a_rows = M
+    ca, cb = a._c(), b._c()
+    _check(lib().mx_gemm_swiglu_nvfp4(ctypes.byref(ca), ctypes.byref(cb), M, inter, K, int(a_rows), _ptr(codes),
+                                      codes.stride(0), _ptr(block_scales), int(layout), _ptr(gscales), _ptr(h),
+                                      0 if h is None else h.stride(0), ng, _ptr(group_row_offsets),
+                                      _ptr(a_row_index), _stream(stream)))
+    return (codes, block_scales, gscales, h) if h is not None else (codes, block_scales, gscales)
 
 
 def mx_swiglu(gu, inter, out=None, stream=None):

@@ -511,29 +511,41 @@ static mxq_status gemm_fp8s_impl(const mxq_operand* a, const mxq_operand* b, int
 }
 
 // inter > 0: the gate_up GEMM with SwiGLU fused (N = 2 inter, c = H [M, inter]).
+// The per-token NVFP4 copy of H that mx_gemm_swiglu_nvfp4 writes.
+struct QhArgs {
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  bool mfma;
+  float* gscales;
+};
+
 static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t N, int64_t K,
                             int64_t a_rows, uint16_t* c, int64_t ldc, int32_t num_groups,
                             const int32_t* group_row_offsets, const int32_t* a_row_index,
-                            int64_t inter, void* stream) {
+                            int64_t inter, void* stream, const QhArgs* q = nullptr) {
   if (!a || !b) return fail(MXQ_EINVAL, "mx_gemm: null operand");
   if (M < 0 || N < 0 || K < 0 || num_groups < 0 || a_rows < 0) return fail(MXQ_EINVAL, "mx_gemm: negative size");
   if (a->fmt != b->fmt) return fail(MXQ_EUNSUPPORTED, "mx_gemm: A and B formats differ");
   if (M == 0 || N == 0) return ok();
   if (K == 0) return fail(MXQ_EUNSUPPORTED, "mx_gemm: K == 0 (nothing would be written)");
-  if (!c) return fail(MXQ_EINVAL, "mx_gemm: c is NULL");
+  if (!c && !q) return fail(MXQ_EINVAL, "mx_gemm: c is NULL");
   if (num_groups > 0 && !group_row_offsets) return fail(MXQ_EINVAL, "mx_gemm: grouped call without offsets");
   if (!a_row_index && a_rows != M) return fail(MXQ_EINVAL, "mx_gemm: a_rows must equal M without a gather index");
   if (a_rows < 1) return fail(MXQ_EINVAL, "mx_gemm: a_rows < 1");
   const int blk = a->fmt == MXQ_FMT_MXFP8 ? 32 : a->fmt == MXQ_FMT_NVFP4 ? 16
                   : (a->fmt == MXQ_FMT_FP8_B128 || a->fmt == MXQ_FMT_FP8_B128_F32) ? 128 : 8;
   if (K % blk) return fail(MXQ_ESHAPE, "mx_gemm: K %% %d != 0 (K=%lld)", blk, (long long)K);
-  if (ldc < (inter ? inter : N)) return fail(MXQ_EINVAL, "mx_gemm: ldc smaller than the output row");
+  if (c && ldc < (inter ? inter : N)) return fail(MXQ_EINVAL, "mx_gemm: ldc smaller than the output row");
   if (inter) {
     if (a->fmt != MXQ_FMT_NVFP4)
       return fail(MXQ_EUNSUPPORTED, "mx_gemm_swiglu: the fused SwiGLU epilogue is built for NVFP4 operands");
     if (b->transposed) return fail(MXQ_EUNSUPPORTED, "mx_gemm_swiglu: B must be row-major (the gate_up weight)");
     if (inter % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: inter %% 64 != 0 (inter=%lld)", (long long)inter);
     if (K % 64) return fail(MXQ_ESHAPE, "mx_gemm_swiglu: K %% 64 != 0 (K=%lld)", (long long)K);
+    if (q && inter != 256 && inter != 512 && inter != 768)
+      return fail(MXQ_EUNSUPPORTED, "mx_gemm_swiglu_nvfp4: inter must be 256, 512 or 768 (inter=%lld)",
+                  (long long)inter);
   }
   if (a->fmt == MXQ_FMT_FP8_B128_F32)
     return gemm_fp8s_impl(a, b, M, N, K, c, ldc, num_groups, a_row_index, stream);
@@ -582,6 +594,9 @@ static mxq_status gemm_impl(const mxq_operand* a, const mxq_operand* b, int64_t 
   g.swiglu_inter = inter;
   const int path = (a->fmt == MXQ_FMT_MXFP8 || a->fmt == MXQ_FMT_FP8_B128) ? mxq::P_FP8
                    : a->fmt == MXQ_FMT_NVFP4 ? mxq::P_F16 : mxq::P_BF16;
+  if (q)
+    return hip_status(mxq::launch_gemm_swiglu_q(g, q->codes, q->ld_codes, q->scales, q->gscales, q->mfma, S(stream)),
+                      "mx_gemm_swiglu_nvfp4");
   return hip_status(mxq::launch_gemm(path, b->transposed != 0, g, S(stream)), inter ? "mx_gemm_swiglu" : "mx_gemm");
 }
 
@@ -598,6 +613,27 @@ mxq_status mx_gemm_swiglu(const mxq_operand* a, const mxq_operand* b, int64_t M,
   if (inter == 0 || M == 0) return ok();
   return gemm_impl(a, b, M, 2 * inter, K, a_rows, h, ldh, num_groups, group_row_offsets, a_row_index,
                    inter, stream);
+}
+
+mxq_status mx_gemm_swiglu_nvfp4(const mxq_operand* a, const mxq_operand* b, int64_t M, int64_t inter,
+                                int64_t K, int64_t a_rows, uint8_t* codes, int64_t ld_codes,
+                                uint8_t* block_scales, int32_t layout, float* gscales, uint16_t* h,
+                                int64_t ldh, int32_t num_groups, const int32_t* group_row_offsets,
+                                const int32_t* a_row_index, void* stream) {
+  if (inter < 0 || M < 0 || ld_codes < 0) return fail(MXQ_EINVAL, "mx_gemm_swiglu_nvfp4: negative size");
+  if (inter == 0 || M == 0) return ok();
+  if (!codes || !block_scales || !gscales) return fail(MXQ_EINVAL, "mx_gemm_swiglu_nvfp4: null output");
+  if (ld_codes < inter / 2) return fail(MXQ_EINVAL, "mx_gemm_swiglu_nvfp4: ld_codes smaller than a row's codes");
+  if (!aligned16(codes) || ld_codes % 16) return fail(MXQ_EALIGN, "mx_gemm_swiglu_nvfp4: codes rows must be 16-byte aligned");
+  if (layout != MXQ_LAYOUT_LINEAR && layout != MXQ_LAYOUT_MFMA)
+    return fail(MXQ_EINVAL, "mx_gemm_swiglu_nvfp4: bad scale layout");
+  if (layout == MXQ_LAYOUT_MFMA && M % 32)
+    return fail(MXQ_ESHAPE, "mx_gemm_swiglu_nvfp4: MFMA scale layout needs M %% 32 == 0");
+  if (h && (!aligned16(h) || (ldh * 2) % 16))
+    return fail(MXQ_EALIGN, "mx_gemm_swiglu_nvfp4: h rows must be 16-byte aligned");
+  const QhArgs q = {codes, ld_codes, block_scales, layout == MXQ_LAYOUT_MFMA, gscales};
+  return gemm_impl(a, b, M, 2 * inter, K, a_rows, h, ldh, num_groups, group_row_offsets, a_row_index, inter,
+                   stream, &q);
 }
 
 // ---------------------------------------------------------------- SwiGLU

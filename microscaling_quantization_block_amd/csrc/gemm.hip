@@ -39,6 +39,7 @@
 
 #include "mxq_device.h"
 #include "mxq_kernels.h"
+#include "nvfp4_device.h"
 
 #include <atomic>
 #include <type_traits>
@@ -1967,6 +1968,287 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
     case 2: return launch_t<PATH, 256, 128, BT, 1, 4, 2, false, SWI>(a, st);
     case 1: return launch_t<PATH, 128, 128, BT, 2, 2, 4, false, SWI>(a, st);
     default: return launch_t<PATH, 128, 128, BT, 2, 2, 2, false, SWI>(a, st);
+  }
+}
+
+// ------------------------------------------------------------ MoE gate_up with Q(H) in the epilogue
+// The experts' gate_up GEMM with the SwiGLU and the per-token NVFP4
+// requantization of H in its epilogue: the codes, E4M3 block scales and
+// per-token S that nvfp4_quantize (1x16 blocks, per-token S, RNE) gives for
+// H, byte for byte, and optionally H itself, without H's round trip through
+// HBM ("Miles Blackwell RL ...", section "Um Quantizador Compartilhado É o
+// Verdadeiro Mecanismo": one shared quantizer emitting packed FP4, block
+// scales and token scales).  S needs the amax of a token's whole H row, so a
+// workgroup owns whole rows: 32 tokens x all 2 inter gate_up columns, on 8
+// waves (two per SIMD), wave q holding the 32 rows x (P gate + P up) columns
+// of H columns [q P, q P + P), P = inter / 8.
+//  * Stages of 64 K in two LDS buffers: B's 2 inter code rows (32 bytes) in
+//    the order the waves read them (wave q: its P gate rows, then its P up
+//    rows), A's 32 code rows, then the rows' scale words (a row's 4 block
+//    scales of the stage), B's, then A's.  They are loaded straight into LDS,
+//    stage s + 1 as stage s begins, the loads spread over the waves; before
+//    the stage's last K step every wave waits for its own loads and a barrier
+//    makes all of stage s + 1 visible, whose fragments are then read and
+//    converted under that K step's MFMAs.
+//  * The K steps are those of the direct-to-LDS NVFP4 kernel (lane half h:
+//    K [32h + 8 ks, + 8) of a 64-K block), so H has the bits mx_gemm_swiglu
+//    gives.
+//  * Epilogue: H (the products' BF16 values through the shared SwiGLU) staged
+//    in LDS as whole rows; 16 threads per row take the row's amax and S =
+//    amax / 2688, then each its blocks through the quantizer's own block
+//    scale and encoder (nvfp4_device.h).
+constexpr int QH_BM = 32;                                   // tokens per workgroup
+constexpr int QH_ROW = 32;                                  // code bytes per row and stage (64 K)
+
+template <int P>
+struct QhLayout {
+  static constexpr int INTER = 8 * P;
+  static constexpr int NB = 2 * INTER;                      // B rows (gate_up columns)
+  static constexpr int B_CODES = 0;
+  static constexpr int A_CODES = NB * QH_ROW;
+  static constexpr int B_SC = A_CODES + QH_BM * QH_ROW;
+  static constexpr int A_SC = B_SC + NB * 4;
+  static constexpr int STAGE = A_SC + 256;                  // A's words: one 64-lane load, lanes 32+ write zeros
+  static constexpr int N_BC = NB * QH_ROW / 1024;           // 1 KB loads of B codes
+  static constexpr int N_BS = NB * 4 / 256;                 // 256-byte loads of B scale words
+  static constexpr int N_ITEMS = N_BC + 1 + N_BS + 1;       // then A codes, B words, A words
+  static constexpr int NI = (N_ITEMS + 7) / 8;              // loads per wave (at most)
+  static constexpr int HROW = INTER * 2 + 16;               // a staged H row (bytes)
+  static_assert(P % 32 == 0 && QH_BM * HROW <= 2 * STAGE, "layout");
+};
+
+struct QhOut {
+  uint8_t* codes;
+  int64_t ld_codes;                                        // bytes
+  uint8_t* scales;
+  float* gs;                                               // per-token S
+  int mfma;                                                // scale layout of the Q(H) copy
+};
+
+template <int P>
+__global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, QhOut o) {
+  using Lay = QhLayout<P>;
+  constexpr int INTER = Lay::INTER;
+  constexpr int TN = 2 * P / 32;                            // 32x32 tiles per wave (gate, then up)
+  constexpr int NF = 1 + TN;                                // fragments per K step (A, then B)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = p.num_groups ? group_mtiles<QH_BM>(p, lane) : (int)gridDim.x;
+  int mt, nt;
+  if (!xcd_tile(tiles_m, 1, 1, mt, nt)) return;
+  const TileOrigin to = tile_origin<QH_BM>(p, mt, lane);
+  if (!to.active) return;
+  const int K = (int)p.K;
+  const int m0 = (int)to.m0, m_end = (int)to.m_end, grp = to.group;
+  auto arow = [&](int m) -> int { return p.row_index ? p.row_index[m] : m; };
+  // B row (gate_up column) behind LDS row n: wave q = n / 2P reads gate rows
+  // q P .. q P + P, then the matching up rows
+  auto brow = [&](int n) -> int {
+    const int q = n / (2 * P), j = n - q * (2 * P);
+    return j < P ? q * P + j : INTER + q * P + (j - P);
+  };
+  const int h = lane >> 5, r32 = lane & 31;
+  const int nk = K / 64;
+  const int nb16 = K >> 4;
+  const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  const uint32_t arb = (uint32_t)(p.lda >> 1), brb = (uint32_t)(p.ldb >> 1);   // code bytes per row
+  const uint8_t* bbase = p.b + (int64_t)grp * (p.b_group_elems >> 1);
+  const uint8_t* bsbase = p.b_scales + (int64_t)grp * p.b_group_scales;
+  const srd_t sA = make_srd(p.a, p.a_rows * (int64_t)arb);
+  const srd_t sB = make_srd(bbase, 2 * (int64_t)INTER * brb);
+  const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb16);
+  const srd_t sBs = make_srd(bsbase, p.b_group_scales);
+  const uint32_t a_sst = p.a_mfma_layout ? 128u : 4u;                          // a word's step per stage
+  const uint32_t b_sst = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
+
+  // This wave's loads: item j = w + 8k.  B codes part j (rows 32j .. + 32:
+  // lane l takes row 32j + l / 2, half l % 2), A codes, B words part j'
+  // (rows 64j' + l), A words (lanes below 32).
+  uint32_t off[Lay::NI];
+#pragma unroll
+  for (int k = 0; k < Lay::NI; ++k) {
+    const int j = w + 8 * k;
+    uint32_t v = 0x80000000u;
+    if (j < Lay::N_BC) {
+      v = (uint32_t)brow(32 * j + (lane >> 1)) * brb + (uint32_t)(lane & 1) * 16u;
+    } else if (j == Lay::N_BC) {
+      const int r = lane >> 1;
+      const bool ok = m0 + r < m_end;
+      v = in_range(ok, (uint32_t)(ok ? arow(m0 + r) : 0) * arb + (uint32_t)(lane & 1) * 16u);
+    } else if (j < Lay::N_BC + 1 + Lay::N_BS) {
+      const int n = brow(64 * (j - Lay::N_BC - 1) + lane);
+      v = p.b_tile ? (uint32_t)((n >> 4) * nb16) : (uint32_t)scale_offset(n, 0, nb16, p.b_mfma_layout);
+    } else if (j == Lay::N_ITEMS - 1) {
+      const bool ok = lane < 32 && m0 + lane < m_end;
+      v = in_range(ok, ok ? (uint32_t)scale_offset(arow(m0 + lane), 0, nb16, p.a_mfma_layout) : 0u);
+    }
+    off[k] = v;
+  }
+  auto issue = [&](int s) {                                 // stage s into buffer s % 2
+    const uint32_t L = lbase + (uint32_t)((s & 1) * Lay::STAGE);
+#pragma unroll
+    for (int k = 0; k < Lay::NI; ++k) {
+      const int j = w + 8 * k;
+      if (j < Lay::N_BC) dma16(sB, L + (uint32_t)(Lay::B_CODES + j * 1024), off[k] + (uint32_t)s * 32u);
+      else if (j == Lay::N_BC) dma16(sA, L + (uint32_t)Lay::A_CODES, off[k] + (uint32_t)s * 32u);
+      else if (j < Lay::N_BC + 1 + Lay::N_BS)
+        dma4(sBs, L + (uint32_t)(Lay::B_SC + (j - Lay::N_BC - 1) * 256), off[k] + (uint32_t)s * b_sst);
+      else if (j == Lay::N_ITEMS - 1) dma4(sAs, L + (uint32_t)Lay::A_SC, off[k] + (uint32_t)s * a_sst);
+    }
+  };
+
+  // fragments of a stage: A (f = 0) and B tile f - 1 (LDS rows w 2P + 32(f - 1) + r)
+  uint4 raw[NF];
+  h2 sc[NF];
+  auto read = [&](int s) {
+    const uint8_t* L = lds + (s & 1) * Lay::STAGE;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = f == 0 ? r32 : w * 2 * P + 32 * (f - 1) + r32;
+      const uint32_t co = f == 0 ? (uint32_t)(Lay::A_CODES + row * QH_ROW) : (uint32_t)(Lay::B_CODES + row * QH_ROW);
+      const uint32_t so = f == 0 ? (uint32_t)(Lay::A_SC + row * 4) : (uint32_t)(Lay::B_SC + row * 4);
+      raw[f] = *reinterpret_cast<const uint4*>(L + co + h * 16);
+      // blocks 2h and 2h + 1 of the stage (K [32h, 32h + 32)) as FP16
+      sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*reinterpret_cast<const uint32_t*>(L + so) >> (16 * h),
+                                                       1.0f, false);
+    }
+  };
+  v8h cv[2][NF];
+  auto convert = [&](int f, int ks, v8h& dst) {
+    const h2 s01 = sc[f];
+    const h2 sp = (ks >> 1) ? h2{s01.y, s01.y} : h2{s01.x, s01.x};
+    const uint32_t word = ks == 0 ? raw[f].x : ks == 1 ? raw[f].y : ks == 2 ? raw[f].z : raw[f].w;
+    uint32_t q[4];
+    fp4x8_to_f16(word, sp, q);
+    dst = __builtin_bit_cast(v8h, make_uint4(q[0], q[1], q[2], q[3]));
+  };
+
+  v16f acc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+
+  issue(0);
+  wait_vmcnt<0>();
+  asm volatile("s_barrier" ::: "memory");
+  read(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) convert(f, 0, cv[0][f]);
+
+  for (int s = 0; s < nk; ++s) {
+    const bool more = s + 1 < nk;
+    // buffer (s + 1) % 2 last held stage s - 1, read during stage s - 2
+    if (more) issue(s + 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int set = ks & 1;
+      if (ks == 3 && more) {
+        wait_vmcnt<0>();                                    // this wave's share of stage s + 1
+        asm volatile("s_barrier" ::: "memory");
+        read(s + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cv[set][1 + i], cv[set][0], acc[i], 0, 0, 0);
+        // the conversions of the next K step (of this stage, or stage s + 1's first)
+        if (ks < 3 || more) {
+          convert(i, (ks + 1) & 3, cv[set ^ 1][i]);
+          if (i == TN - 1) convert(TN, (ks + 1) & 3, cv[set ^ 1][TN]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ------------------------------------------------ epilogue
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint8_t* const E = lds;                                   // 32 staged H rows
+  {
+    const float sbg = p.b_gs[grp];
+    const int mrow = m0 + r32;
+    const float sa = mrow < m_end ? (p.a_gs_per_row ? p.a_gs[arow(mrow)] : p.a_gs[0]) : 0.0f;
+    uint8_t* const er = E + r32 * Lay::HROW + (w * P) * 2 + h * 8;
+#pragma unroll
+    for (int t = 0; t < TN / 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float gv[4], uv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gv[i] = (acc[t][4 * g + i] * sa) * sbg;
+          uv[i] = (acc[t + TN / 2][4 * g + i] * sa) * sbg;
+        }
+        const uint32_t h01 = swiglu_bf16x2(f32x2_to_bf16x2(gv[0], gv[1]), f32x2_to_bf16x2(uv[0], uv[1]));
+        const uint32_t h23 = swiglu_bf16x2(f32x2_to_bf16x2(gv[2], gv[3]), f32x2_to_bf16x2(uv[2], uv[3]));
+        *reinterpret_cast<uint2*>(er + (t * 32 + g * 8) * 2) = make_uint2(h01, h23);
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 16 threads per token row, each INTER / 16 consecutive H values (whole
+  // 16-value blocks)
+  constexpr int PER = INTER / 16, NBLK = PER / 16;
+  const int rr = tid >> 4, part = tid & 15;
+  const int64_t m = m0 + rr;
+  uint4 v[2 * NBLK];
+#pragma unroll
+  for (int c = 0; c < 2 * NBLK; ++c)
+    v[c] = *reinterpret_cast<const uint4*>(E + rr * Lay::HROW + (part * PER + 8 * c) * 2);
+  uint32_t mb = 0;
+#pragma unroll
+  for (int c = 0; c < 2 * NBLK; ++c) mb = umax(mb, amax8_bits(v[c]));
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) mb = umax(mb, lane_xor_u32(mb, x));
+  const float S = __uint_as_float(mb) / 2688.0f;
+  if (m < m_end) {
+    if (part == 0) o.gs[m] = S;
+    with_frame(S, [&](auto tiny) {
+      constexpr bool TINY = decltype(tiny)::value;
+      const u32x4 none = {0, 0, 0, 0};
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const uint32_t ab = umax(amax8_bits(v[2 * b]), amax8_bits(v[2 * b + 1]));
+        const BlockScale bs = nv_block_scale(__uint_as_float(ab), S);
+        const uint32_t q0 = nv_encode8<false, TINY>(v[2 * b], bs.r, none);
+        const uint32_t q1 = nv_encode8<false, TINY>(v[2 * b + 1], bs.r, none);
+        const int blk = part * NBLK + b;
+        *reinterpret_cast<uint2*>(o.codes + m * o.ld_codes + blk * 8) = make_uint2(q0, q1);
+        o.scales[scale_offset(m, blk, INTER / 16, o.mfma)] = (uint8_t)bs.code;
+      }
+    });
+    if (p.c) {
+#pragma unroll
+      for (int c = 0; c < 2 * NBLK; ++c)
+        *reinterpret_cast<uint4*>(p.c + m * p.ldc + part * PER + 8 * c) = v[c];
+    }
+  }
+}
+
+template <int P>
+static hipError_t launch_swiglu_q_p(const GemmArgs& a, const QhOut& o, hipStream_t st) {
+  using Lay = QhLayout<P>;
+  int64_t tiles_m = a.num_groups ? a.M / QH_BM + a.num_groups : (a.M + QH_BM - 1) / QH_BM;
+  if (tiles_m < 1) tiles_m = 1;
+  if (tiles_m >= (1ll << 31)) return hipErrorInvalidValue;
+  const size_t lds = 2 * (size_t)Lay::STAGE;
+  static std::atomic<uint32_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_nvfp4_swiglu_q_kernel<P>, (int)lds, lds_set); e != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(gemm_nvfp4_swiglu_q_kernel<P>, dim3((unsigned)tiles_m), dim3(512), lds, st, a, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_swiglu_q(const GemmArgs& a, uint8_t* codes, int64_t ld_codes, uint8_t* scales, float* gs,
+                                bool mfma, hipStream_t st) {
+  const QhOut o = {codes, ld_codes, scales, gs, (int)mfma};
+  switch (a.swiglu_inter) {
+    case 256: return launch_swiglu_q_p<32>(a, o, st);
+    case 512: return launch_swiglu_q_p<64>(a, o, st);
+    case 768: return launch_swiglu_q_p<96>(a, o, st);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -124,6 +124,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int path, bool b_transposed, const GemmArgs& a, hipStream_t st);
+// NVFP4 gate_up GEMM with SwiGLU and the per-token NVFP4 quantization of H in
+// its epilogue (a.swiglu_inter in {256, 512, 768}; a.c = H or null).
+hipError_t launch_gemm_swiglu_q(const GemmArgs& a, uint8_t* codes, int64_t ld_codes, uint8_t* scales, float* gs,
+                                bool mfma, hipStream_t st);
 void gemm_set_tile(int tile);   // -1 = measured choice, 0..6 = forced configuration
 
 }  // namespace mxq

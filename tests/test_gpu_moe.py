@@ -189,3 +189,71 @@ def test_fused_swiglu_every_tile(I, dense):
     # and close to the float64 SwiGLU of the GPU's own gate_up (as for mx_swiglu)
     ref64 = F.bf16_bits_to_f64(moe.swiglu_f64(from_dev_bf16(gu), I))
     assert np.all(np.abs(F.bf16_bits_to_f64(got) - ref64) <= 2.0 ** -7 * np.abs(ref64) + 1e-30)
+
+
+@pytest.mark.parametrize("I,K,dense,layout,tiny", [
+    (768, 256, False, "linear", False),   # the config-3 width, grouped, a gather, an empty group
+    (512, 320, True, "linear", False),    # dense, ragged M, five 64-K stages
+    (256, 128, False, "mfma", False),     # MFMA scale layout of the Q(H) copy
+    (768, 2048, False, "linear", False),  # the config-3 K
+    (256, 192, True, "linear", True),     # token scales below 2^-64 (the scaled frame)
+])
+def test_fused_swiglu_requant(I, K, dense, layout, tiny):
+    """mx_gemm_swiglu_nvfp4 writes the bytes nvfp4_quantize(H, per-token S,
+    1x16, RNE) writes for H = mx_gemm_swiglu(...), and H itself; the
+    quantization of its H also equals the oracle's."""
+    import torch
+    m = mxq()
+    rs = np.random.default_rng(37 + I + K)
+    T = 160
+    E = 1 if dense else 6
+    w = F.bf16_rne(rs.standard_normal((E, 2 * I, K)) * 0.05)
+    x = F.bf16_rne(rs.standard_normal((T, K)) * (2.0 ** -30 if tiny else 1.0))
+    x[5] = 0                                                          # a token whose H row is zero
+    cw, sw, Sw = quantize_experts(m, w)
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw.view(E * 2 * I, K // 2), sw, Sw, gs=m.GScale.PER_TENSOR)
+    if dense:
+        kw, M = {}, (T if layout == "mfma" else T - 3)
+    else:
+        M = 320 if layout == "mfma" else 300
+        off = np.array([0, 64, 64, 150, 200, 263, M], dtype=np.int32)    # group 1 empty
+        idx = rs.integers(0, T, M).astype(np.int32)
+        idx[:3] = 5
+        kw = dict(group_row_offsets=torch.from_numpy(off).cuda(), a_row_index=torch.from_numpy(idx).cuda(),
+                  a_rows=T)
+    lay = m.Layout.MFMA if layout == "mfma" else m.Layout.LINEAR
+    say(f"fused SwiGLU + Q(H) I={I} K={K} dense={dense} layout={layout} tiny={tiny} M={M}")
+    h_ref = m.mx_gemm_swiglu(A, B, M, I, K, **kw)
+    cr, sr, Sr = m.nvfp4_quantize(h_ref, gs=m.GScale.PER_ROW, layout=lay)
+    c, s, S, h = m.mx_gemm_swiglu_nvfp4(A, B, M, I, K, layout=lay, with_h=True, **kw)
+    assert np.array_equal(from_dev_bf16(h), from_dev_bf16(h_ref))
+    assert np.array_equal(to_np(S), to_np(Sr))
+    assert np.array_equal(to_np(s).reshape(-1), to_np(sr).reshape(-1))
+    assert np.array_equal(to_np(c), to_np(cr))
+    # without H the same bytes
+    c2, s2, S2 = m.mx_gemm_swiglu_nvfp4(A, B, M, I, K, layout=lay, **kw)
+    assert np.array_equal(to_np(c2), to_np(c)) and np.array_equal(to_np(s2), to_np(s))
+    assert np.array_equal(to_np(S2), to_np(S))
+    if tiny:
+        assert np.all(to_np(S)[to_np(S) > 0] < 2.0 ** -64)
+    if layout == "linear":
+        hc, hs, hS = ON.quantize_rowwise(F.bf16_bits_to_f64(from_dev_bf16(h)), "per_row")
+        assert np.array_equal(to_np(c), hc)
+        assert np.array_equal(to_np(s).reshape(M, I // 16), hs)
+        assert np.array_equal(to_np(S), hS)
+
+
+def test_fused_swiglu_requant_rejects_other_widths():
+    import torch
+    m = mxq()
+    rs = np.random.default_rng(41)
+    x = F.bf16_rne(rs.standard_normal((64, 128)))
+    w = F.bf16_rne(rs.standard_normal((1, 2 * 320, 128)) * 0.05)
+    cw, sw, Sw = quantize_experts(m, w)
+    cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
+    A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
+    B = m.Operand(m.Format.NVFP4, cw.view(640, 64), sw, Sw, gs=m.GScale.PER_TENSOR)
+    with pytest.raises(m.MXQError):
+        m.mx_gemm_swiglu_nvfp4(A, B, 64, 320, 128)
