@@ -2009,10 +2009,8 @@ struct QhLayout {
   static constexpr int B_SC = A_CODES + QH_BM * QH_ROW;
   static constexpr int A_SC = B_SC + NB * 4;
   static constexpr int STAGE = A_SC + 256;                  // A's words: one 64-lane load, lanes 32+ write zeros
-  static constexpr int N_BC = NB * QH_ROW / 1024;           // 1 KB loads of B codes
-  static constexpr int N_BS = NB * 4 / 256;                 // 256-byte loads of B scale words
-  static constexpr int N_ITEMS = N_BC + 1 + N_BS + 1;       // then A codes, B words, A words
-  static constexpr int NI = (N_ITEMS + 7) / 8;              // loads per wave (at most)
+  static constexpr int BC_PW = 2 * P / 32;                  // 1 KB code loads per wave: its own 2P B rows
+  static constexpr int BS_PW = 2 * P / 64;                  // 256-byte scale-word loads per wave
   static constexpr int HROW = INTER * 2 + 16;               // a staged H row (bytes)
   static_assert(P % 32 == 0 && QH_BM * HROW <= 2 * STAGE, "layout");
 };
@@ -2024,6 +2022,10 @@ struct QhOut {
   float* gs;                                               // per-token S
   int mfma;                                                // scale layout of the Q(H) copy
 };
+
+// A code row's two 16-byte halves sit in slots h ^ ((r >> 3) & 1): the 16
+// rows of one LDS read pass then cover all 64 banks.
+__device__ __forceinline__ int qh_slot(int r, int h) { return h ^ ((r >> 3) & 1); }
 
 template <int P>
 __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, QhOut o) {
@@ -2062,55 +2064,58 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, Qh
   const uint32_t a_sst = p.a_mfma_layout ? 128u : 4u;                          // a word's step per stage
   const uint32_t b_sst = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 
-  // This wave's loads: item j = w + 8k.  B codes part j (rows 32j .. + 32:
-  // lane l takes row 32j + l / 2, half l % 2), A codes, B words part j'
-  // (rows 64j' + l), A words (lanes below 32).
-  uint32_t off[Lay::NI];
+  // This wave's loads: the code rows and scale words of its own 2P B rows
+  // (LDS rows 2P w ..), in 1 KB parts (lane l: row 32k + l / 2, slot l % 2,
+  // which holds half qh_slot of the row) and 256-byte parts (lane l: row
+  // 64k + l); wave 0 loads A's codes, wave 1 A's scale words (lanes below 32).
+  uint32_t bc_off[Lay::BC_PW], bs_off[Lay::BS_PW], a_off;
 #pragma unroll
-  for (int k = 0; k < Lay::NI; ++k) {
-    const int j = w + 8 * k;
-    uint32_t v = 0x80000000u;
-    if (j < Lay::N_BC) {
-      v = (uint32_t)brow(32 * j + (lane >> 1)) * brb + (uint32_t)(lane & 1) * 16u;
-    } else if (j == Lay::N_BC) {
-      const int r = lane >> 1;
-      const bool ok = m0 + r < m_end;
-      v = in_range(ok, (uint32_t)(ok ? arow(m0 + r) : 0) * arb + (uint32_t)(lane & 1) * 16u);
-    } else if (j < Lay::N_BC + 1 + Lay::N_BS) {
-      const int n = brow(64 * (j - Lay::N_BC - 1) + lane);
-      v = p.b_tile ? (uint32_t)((n >> 4) * nb16) : (uint32_t)scale_offset(n, 0, nb16, p.b_mfma_layout);
-    } else if (j == Lay::N_ITEMS - 1) {
-      const bool ok = lane < 32 && m0 + lane < m_end;
-      v = in_range(ok, ok ? (uint32_t)scale_offset(arow(m0 + lane), 0, nb16, p.a_mfma_layout) : 0u);
-    }
-    off[k] = v;
+  for (int k = 0; k < Lay::BC_PW; ++k) {
+    const int n = 2 * P * w + 32 * k + (lane >> 1);
+    bc_off[k] = (uint32_t)brow(n) * brb + (uint32_t)qh_slot(n, lane & 1) * 16u;
+  }
+#pragma unroll
+  for (int k = 0; k < Lay::BS_PW; ++k) {
+    const int n = brow(2 * P * w + 64 * k + lane);
+    bs_off[k] = p.b_tile ? (uint32_t)((n >> 4) * nb16) : (uint32_t)scale_offset(n, 0, nb16, p.b_mfma_layout);
+  }
+  if (w == 0) {
+    const int r = lane >> 1;
+    const bool ok = m0 + r < m_end;
+    a_off = in_range(ok, (uint32_t)(ok ? arow(m0 + r) : 0) * arb + (uint32_t)qh_slot(r, lane & 1) * 16u);
+  } else {
+    const bool ok = lane < 32 && m0 + lane < m_end;
+    a_off = in_range(ok, ok ? (uint32_t)scale_offset(arow(m0 + lane), 0, nb16, p.a_mfma_layout) : 0u);
   }
   auto issue = [&](int s) {                                 // stage s into buffer s % 2
     const uint32_t L = lbase + (uint32_t)((s & 1) * Lay::STAGE);
 #pragma unroll
-    for (int k = 0; k < Lay::NI; ++k) {
-      const int j = w + 8 * k;
-      if (j < Lay::N_BC) dma16(sB, L + (uint32_t)(Lay::B_CODES + j * 1024), off[k] + (uint32_t)s * 32u);
-      else if (j == Lay::N_BC) dma16(sA, L + (uint32_t)Lay::A_CODES, off[k] + (uint32_t)s * 32u);
-      else if (j < Lay::N_BC + 1 + Lay::N_BS)
-        dma4(sBs, L + (uint32_t)(Lay::B_SC + (j - Lay::N_BC - 1) * 256), off[k] + (uint32_t)s * b_sst);
-      else if (j == Lay::N_ITEMS - 1) dma4(sAs, L + (uint32_t)Lay::A_SC, off[k] + (uint32_t)s * a_sst);
-    }
+    for (int k = 0; k < Lay::BC_PW; ++k)
+      dma16(sB, L + (uint32_t)(Lay::B_CODES + (2 * P * w + 32 * k) * QH_ROW), bc_off[k] + (uint32_t)s * 32u);
+#pragma unroll
+    for (int k = 0; k < Lay::BS_PW; ++k)
+      dma4(sBs, L + (uint32_t)(Lay::B_SC + (2 * P * w + 64 * k) * 4), bs_off[k] + (uint32_t)s * b_sst);
+    if (w == 0) dma16(sA, L + (uint32_t)Lay::A_CODES, a_off + (uint32_t)s * 32u);
+    else if (w == 1) dma4(sAs, L + (uint32_t)Lay::A_SC, a_off + (uint32_t)s * a_sst);
   };
 
   // fragments of a stage: A (f = 0) and B tile f - 1 (LDS rows w 2P + 32(f - 1) + r)
   uint4 raw[NF];
   h2 sc[NF];
+  uint32_t co[NF], so[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int row = f == 0 ? r32 : w * 2 * P + 32 * (f - 1) + r32;
+    co[f] = (uint32_t)((f == 0 ? Lay::A_CODES : Lay::B_CODES) + row * QH_ROW + qh_slot(row, h) * 16);
+    so[f] = (uint32_t)((f == 0 ? Lay::A_SC : Lay::B_SC) + row * 4);
+  }
   auto read = [&](int s) {
     const uint8_t* L = lds + (s & 1) * Lay::STAGE;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int row = f == 0 ? r32 : w * 2 * P + 32 * (f - 1) + r32;
-      const uint32_t co = f == 0 ? (uint32_t)(Lay::A_CODES + row * QH_ROW) : (uint32_t)(Lay::B_CODES + row * QH_ROW);
-      const uint32_t so = f == 0 ? (uint32_t)(Lay::A_SC + row * 4) : (uint32_t)(Lay::B_SC + row * 4);
-      raw[f] = *reinterpret_cast<const uint4*>(L + co + h * 16);
+      raw[f] = *reinterpret_cast<const uint4*>(L + co[f]);
       // blocks 2h and 2h + 1 of the stage (K [32h, 32h + 32)) as FP16
-      sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*reinterpret_cast<const uint32_t*>(L + so) >> (16 * h),
+      sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*reinterpret_cast<const uint32_t*>(L + so[f]) >> (16 * h),
                                                        1.0f, false);
     }
   };

@@ -22,9 +22,9 @@ def mxq():
     return m
 
 
-def quantize_experts(m, w_bits):
+def quantize_experts(m, w_bits, layout=None):
     """Per-expert NVFP4 1x16 copies with one per-tensor S each (for W_gu that
-    S spans the gate/up pair)."""
+    S spans the gate/up pair), scales in `layout` (default LINEAR)."""
     import torch
     E, N, K = w_bits.shape
     codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
@@ -33,7 +33,7 @@ def quantize_experts(m, w_bits):
     wd = to_dev_bf16(w_bits.reshape(E * N, K)).view(E, N, K)
     for e in range(E):
         m.nvfp4_quantize(wd[e], gs=m.GScale.PER_TENSOR, codes=codes[e], block_scales=scales[e],
-                         gscales=gs[e:e + 1])
+                         gscales=gs[e:e + 1], layout=m.Layout.LINEAR if layout is None else layout)
     return codes, scales, gs
 
 
@@ -191,14 +191,14 @@ def test_fused_swiglu_every_tile(I, dense):
     assert np.all(np.abs(F.bf16_bits_to_f64(got) - ref64) <= 2.0 ** -7 * np.abs(ref64) + 1e-30)
 
 
-@pytest.mark.parametrize("I,K,dense,layout,tiny", [
-    (768, 256, False, "linear", False),   # the config-3 width, grouped, a gather, an empty group
-    (512, 320, True, "linear", False),    # dense, ragged M, five 64-K stages
-    (256, 128, False, "mfma", False),     # MFMA scale layout of the Q(H) copy
-    (768, 2048, False, "linear", False),  # the config-3 K
-    (256, 192, True, "linear", True),     # token scales below 2^-64 (the scaled frame)
+@pytest.mark.parametrize("I,K,dense,layout,tiny,b_mfma", [
+    (768, 256, False, "linear", False, False),   # the config-3 width, grouped, a gather, an empty group
+    (512, 320, True, "linear", False, False),    # dense, ragged M, five 64-K stages
+    (256, 128, False, "mfma", False, False),     # MFMA scale layout of the Q(H) copy
+    (768, 2048, False, "linear", False, True),   # the config-3 K; the weights' scales in the MFMA layout
+    (256, 192, True, "linear", True, False),     # token scales below 2^-64 (the scaled frame)
 ])
-def test_fused_swiglu_requant(I, K, dense, layout, tiny):
+def test_fused_swiglu_requant(I, K, dense, layout, tiny, b_mfma):
     """mx_gemm_swiglu_nvfp4 writes the bytes nvfp4_quantize(H, per-token S,
     1x16, RNE) writes for H = mx_gemm_swiglu(...), and H itself; the
     quantization of its H also equals the oracle's."""
@@ -210,10 +210,11 @@ def test_fused_swiglu_requant(I, K, dense, layout, tiny):
     w = F.bf16_rne(rs.standard_normal((E, 2 * I, K)) * 0.05)
     x = F.bf16_rne(rs.standard_normal((T, K)) * (2.0 ** -30 if tiny else 1.0))
     x[5] = 0                                                          # a token whose H row is zero
-    cw, sw, Sw = quantize_experts(m, w)
+    blay = m.Layout.MFMA if b_mfma else m.Layout.LINEAR
+    cw, sw, Sw = quantize_experts(m, w, blay)
     cx, sx, Sx = m.nvfp4_quantize(to_dev_bf16(x), gs=m.GScale.PER_ROW)
     A = m.Operand(m.Format.NVFP4, cx, sx, Sx, gs=m.GScale.PER_ROW)
-    B = m.Operand(m.Format.NVFP4, cw.view(E * 2 * I, K // 2), sw, Sw, gs=m.GScale.PER_TENSOR)
+    B = m.Operand(m.Format.NVFP4, cw.view(E * 2 * I, K // 2), sw, Sw, gs=m.GScale.PER_TENSOR, layout=blay)
     if dense:
         kw, M = {}, (T if layout == "mfma" else T - 3)
     else:
@@ -224,7 +225,7 @@ def test_fused_swiglu_requant(I, K, dense, layout, tiny):
         kw = dict(group_row_offsets=torch.from_numpy(off).cuda(), a_row_index=torch.from_numpy(idx).cuda(),
                   a_rows=T)
     lay = m.Layout.MFMA if layout == "mfma" else m.Layout.LINEAR
-    say(f"fused SwiGLU + Q(H) I={I} K={K} dense={dense} layout={layout} tiny={tiny} M={M}")
+    say(f"fused SwiGLU + Q(H) I={I} K={K} dense={dense} layout={layout} tiny={tiny} b_mfma={b_mfma} M={M}")
     h_ref = m.mx_gemm_swiglu(A, B, M, I, K, **kw)
     cr, sr, Sr = m.nvfp4_quantize(h_ref, gs=m.GScale.PER_ROW, layout=lay)
     c, s, S, h = m.mx_gemm_swiglu_nvfp4(A, B, M, I, K, layout=lay, with_h=True, **kw)
