@@ -1982,14 +1982,19 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
 // workgroup owns whole rows: 32 tokens x all 2 inter gate_up columns, on 8
 // waves (two per SIMD), wave q holding the 32 rows x (P gate + P up) columns
 // of H columns [q P, q P + P), P = inter / 8.
-//  * Stages of 64 K in two LDS buffers: B's 2 inter code rows (32 bytes) in
-//    the order the waves read them (wave q: its P gate rows, then its P up
-//    rows), A's 32 code rows, then the rows' scale words (a row's 4 block
-//    scales of the stage), B's, then A's.  They are loaded straight into LDS,
-//    stage s + 1 as stage s begins, the loads spread over the waves; before
-//    the stage's last K step every wave waits for its own loads and a barrier
-//    makes all of stage s + 1 visible, whose fragments are then read and
-//    converted under that K step's MFMAs.
+//  * Stages of 64 K.  B's 2 inter code rows sit in LDS in the order the
+//    waves read them (wave q: its P gate rows, then its P up rows), 64 bytes
+//    a row for a pair of stages; each wave loads and reads only its own rows,
+//    so it reloads them (the next pair) as soon as it has read the pair's
+//    second stage.  A's 32 code rows and the rows' scale words (a row's 4
+//    block scales of a stage), B's, then A's, sit in two stage buffers,
+//    stage s + 1 loaded as stage s begins.  Everything is loaded straight
+//    into LDS; before a stage's last K step every wave waits for its own
+//    loads and a barrier makes stage s + 1 visible, whose fragments are then
+//    read and converted under that K step's MFMAs.  (Measured at the
+//    Qwen3-30B-A3B MoE shape the kernel is bound by L2 requests: a B row's
+//    64 bytes per pair are one request, and the weights' scale words in the
+//    MFMA layout put 32 rows' words of a stage in one line.)
 //  * The K steps are those of the direct-to-LDS NVFP4 kernel (lane half h:
 //    K [32h + 8 ks, + 8) of a 64-K block), so H has the bits mx_gemm_swiglu
 //    gives.
@@ -2004,15 +2009,21 @@ template <int P>
 struct QhLayout {
   static constexpr int INTER = 8 * P;
   static constexpr int NB = 2 * INTER;                      // B rows (gate_up columns)
+  // B codes of a stage pair (128 K, 64 bytes a row), one region: each wave
+  // reads and reloads only its own rows
   static constexpr int B_CODES = 0;
-  static constexpr int A_CODES = NB * QH_ROW;
+  static constexpr int B_ROW = 2 * QH_ROW;
+  // then two buffers of a stage's A codes and the scale words
+  static constexpr int BUF = NB * B_ROW;
+  static constexpr int A_CODES = 0;                         // offsets within a buffer
   static constexpr int B_SC = A_CODES + QH_BM * QH_ROW;
   static constexpr int A_SC = B_SC + NB * 4;
   static constexpr int STAGE = A_SC + 256;                  // A's words: one 64-lane load, lanes 32+ write zeros
-  static constexpr int BC_PW = 2 * P / 32;                  // 1 KB code loads per wave: its own 2P B rows
+  static constexpr int LDS = BUF + 2 * STAGE;
+  static constexpr int BC_PW = 2 * P / 16;                  // 1 KB code loads per wave and stage pair (16 rows each)
   static constexpr int BS_PW = 2 * P / 64;                  // 256-byte scale-word loads per wave
   static constexpr int HROW = INTER * 2 + 16;               // a staged H row (bytes)
-  static_assert(P % 32 == 0 && QH_BM * HROW <= 2 * STAGE, "layout");
+  static_assert(P % 32 == 0 && QH_BM * HROW <= LDS, "layout");
 };
 
 struct QhOut {
@@ -2023,9 +2034,11 @@ struct QhOut {
   int mfma;                                                // scale layout of the Q(H) copy
 };
 
-// A code row's two 16-byte halves sit in slots h ^ ((r >> 3) & 1): the 16
-// rows of one LDS read pass then cover all 64 banks.
+// A's 32-byte code rows: the two 16-byte halves sit in slots h ^ ((r >> 3) &
+// 1); B's 64-byte rows (a stage pair): chunk c in slot c ^ ((r >> 2) & 3).
+// The 16 rows of one LDS read pass then cover all 64 banks.
 __device__ __forceinline__ int qh_slot(int r, int h) { return h ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int qh_bslot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 template <int P>
 __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, QhOut o) {
@@ -2065,14 +2078,16 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, Qh
   const uint32_t b_sst = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 
   // This wave's loads: the code rows and scale words of its own 2P B rows
-  // (LDS rows 2P w ..), in 1 KB parts (lane l: row 32k + l / 2, slot l % 2,
-  // which holds half qh_slot of the row) and 256-byte parts (lane l: row
-  // 64k + l); wave 0 loads A's codes, wave 1 A's scale words (lanes below 32).
+  // (LDS rows 2P w ..), the codes per stage pair in 1 KB parts (lane l: row
+  // 16k + l / 4, slot l % 4, which holds chunk qh_bslot of the row's 64
+  // bytes: one 64-byte request per row) and the words per stage in 256-byte
+  // parts (lane l: row 64k + l); wave 0 loads A's codes, wave 1 A's scale
+  // words (lanes below 32), per stage.
   uint32_t bc_off[Lay::BC_PW], bs_off[Lay::BS_PW], a_off;
 #pragma unroll
   for (int k = 0; k < Lay::BC_PW; ++k) {
-    const int n = 2 * P * w + 32 * k + (lane >> 1);
-    bc_off[k] = (uint32_t)brow(n) * brb + (uint32_t)qh_slot(n, lane & 1) * 16u;
+    const int n = 2 * P * w + 16 * k + (lane >> 2);
+    bc_off[k] = (uint32_t)brow(n) * brb + (uint32_t)qh_bslot(n, lane & 3) * 16u;
   }
 #pragma unroll
   for (int k = 0; k < Lay::BS_PW; ++k) {
@@ -2087,33 +2102,39 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, Qh
     const bool ok = lane < 32 && m0 + lane < m_end;
     a_off = in_range(ok, ok ? (uint32_t)scale_offset(arow(m0 + lane), 0, nb16, p.a_mfma_layout) : 0u);
   }
-  auto issue = [&](int s) {                                 // stage s into buffer s % 2
-    const uint32_t L = lbase + (uint32_t)((s & 1) * Lay::STAGE);
-#pragma unroll
-    for (int k = 0; k < Lay::BC_PW; ++k)
-      dma16(sB, L + (uint32_t)(Lay::B_CODES + (2 * P * w + 32 * k) * QH_ROW), bc_off[k] + (uint32_t)s * 32u);
+  auto issue = [&](int s) {                                 // stage s's A codes and words into buffer s % 2
+    const uint32_t L = lbase + (uint32_t)(Lay::BUF + (s & 1) * Lay::STAGE);
 #pragma unroll
     for (int k = 0; k < Lay::BS_PW; ++k)
       dma4(sBs, L + (uint32_t)(Lay::B_SC + (2 * P * w + 64 * k) * 4), bs_off[k] + (uint32_t)s * b_sst);
     if (w == 0) dma16(sA, L + (uint32_t)Lay::A_CODES, a_off + (uint32_t)s * 32u);
     else if (w == 1) dma4(sAs, L + (uint32_t)Lay::A_SC, a_off + (uint32_t)s * a_sst);
   };
+  auto issue_b = [&](int q) {                               // this wave's B codes of stages 2q, 2q + 1
+#pragma unroll
+    for (int k = 0; k < Lay::BC_PW; ++k)
+      dma16(sB, lbase + (uint32_t)(Lay::B_CODES + (2 * P * w + 16 * k) * Lay::B_ROW), bc_off[k] + (uint32_t)q * 64u);
+  };
 
   // fragments of a stage: A (f = 0) and B tile f - 1 (LDS rows w 2P + 32(f - 1) + r)
   uint4 raw[NF];
   h2 sc[NF];
-  uint32_t co[NF], so[NF];
+  uint32_t co[2][NF], so[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int row = f == 0 ? r32 : w * 2 * P + 32 * (f - 1) + r32;
-    co[f] = (uint32_t)((f == 0 ? Lay::A_CODES : Lay::B_CODES) + row * QH_ROW + qh_slot(row, h) * 16);
-    so[f] = (uint32_t)((f == 0 ? Lay::A_SC : Lay::B_SC) + row * 4);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      co[t][f] = f == 0 ? (uint32_t)(Lay::BUF + Lay::A_CODES + row * QH_ROW + qh_slot(row, h) * 16)
+                        : (uint32_t)(Lay::B_CODES + row * Lay::B_ROW + qh_bslot(row, 2 * t + h) * 16);
+    so[f] = (uint32_t)(Lay::BUF + (f == 0 ? Lay::A_SC : Lay::B_SC) + row * 4);
   }
   auto read = [&](int s) {
-    const uint8_t* L = lds + (s & 1) * Lay::STAGE;
+    const uint32_t t = (uint32_t)(s & 1);
+    const uint8_t* L = lds + t * Lay::STAGE;                // A and the words: buffer s % 2
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      raw[f] = *reinterpret_cast<const uint4*>(L + co[f]);
+      raw[f] = *reinterpret_cast<const uint4*>(f == 0 ? L + co[0][0] : lds + (t ? co[1][f] : co[0][f]));
       // blocks 2h and 2h + 1 of the stage (K [32h, 32h + 32)) as FP16
       sc[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(*reinterpret_cast<const uint32_t*>(L + so[f]) >> (16 * h),
                                                        1.0f, false);
@@ -2135,6 +2156,7 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, Qh
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
+  issue_b(0);
   issue(0);
   wait_vmcnt<0>();
   asm volatile("s_barrier" ::: "memory");
@@ -2150,9 +2172,16 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_swiglu_q_kernel(GemmArgs p, Qh
     for (int ks = 0; ks < 4; ++ks) {
       const int set = ks & 1;
       if (ks == 3 && more) {
-        wait_vmcnt<0>();                                    // this wave's share of stage s + 1
+        // this wave's share of stage s + 1 (and, s even, of the pair's B codes)
+        wait_vmcnt<0>();
         asm volatile("s_barrier" ::: "memory");
         read(s + 1);
+        if ((s & 1) == 0 && s + 2 < nk) {
+          // the pair's last reads of this wave's B rows are done: load the
+          // next pair (needed at the last K step of stage s + 1)
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          issue_b(s / 2 + 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -2238,7 +2267,7 @@ static hipError_t launch_swiglu_q_p(const GemmArgs& a, const QhOut& o, hipStream
   int64_t tiles_m = a.num_groups ? a.M / QH_BM + a.num_groups : (a.M + QH_BM - 1) / QH_BM;
   if (tiles_m < 1) tiles_m = 1;
   if (tiles_m >= (1ll << 31)) return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)Lay::STAGE;
+  const size_t lds = (size_t)Lay::LDS;
   static std::atomic<uint32_t> lds_set{0};
   if (hipError_t e = ensure_lds_limit((const void*)gemm_nvfp4_swiglu_q_kernel<P>, (int)lds, lds_set); e != hipSuccess)
     return e;
