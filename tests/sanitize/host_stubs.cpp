@@ -47,6 +47,9 @@ hipError_t launch_swiglu(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, 
 }
 hipError_t launch_gemm_fp8s(const Fp8sArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_gemm(int, bool, const GemmArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_gemm_swiglu_q(const GemmArgs&, uint8_t*, int64_t, uint8_t*, float*, bool, hipStream_t) {
+  return hipErrorNoDevice;
+}
 void gemm_set_tile(int) {}
 
 }  // namespace mxq

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     for want in ("mx_quantize", "nvfp4_quantize", "nvfp4_quantize_dq", "nvfp4_quantize_tile_t",
                  "nvfp4_quantize_rht", "nvfp4_quantize_rowcol", "fp8bw_quantize",
                  "fp8bw_quantize_f32", "mx_dequantize",
-                 "mx_gemm", "mx_gemm_swiglu",
+                 "mx_gemm", "mx_gemm_swiglu", "mx_gemm_swiglu_nvfp4",
                  "mx_swiglu", "mxq_status_str", "mxq_last_error", "mxq_version"):
         assert want in names
 
@@ -249,6 +249,26 @@ def test_mx_gemm_rejects_bad_arguments():
     assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), ldh=32) == 1             # ldh < inter
     assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), inter=0) == 0            # nothing to do
     assert fused(nv(G.PER_ROW), nv(G.PER_TENSOR), inter=-64) == 1
+
+    def fused_q(a, b, M=32, inter=256, K=64, codes=FAKE, ld_codes=128, scales=FAKE, layout=0, gsc=FAKE,
+                h=None, ldh=0):
+        return L.mx_gemm_swiglu_nvfp4(ctypes.byref(a), ctypes.byref(b), M, inter, K, M, codes, ld_codes, scales,
+                                      layout, gsc, h, ldh, 0, None, None, None)
+
+    A, Bw = nv(G.PER_ROW), nv(G.PER_TENSOR)
+    assert fused_q(op(F.MXFP8), op(F.MXFP8)) == 4                          # NVFP4 only
+    assert fused_q(A, Bw, inter=320, ld_codes=160) == 4                    # inter in {256, 512, 768}
+    assert "256, 512 or 768" in _err(L)
+    assert fused_q(A, Bw, codes=None) == 1                                 # outputs required
+    assert fused_q(A, Bw, scales=None) == 1
+    assert fused_q(A, Bw, gsc=None) == 1
+    assert fused_q(A, Bw, ld_codes=64) == 1                                # row of codes: inter / 2 bytes
+    assert fused_q(A, Bw, ld_codes=136) == 3                               # 16-byte rows
+    assert fused_q(A, Bw, layout=1, M=48) == 2                             # MFMA layout: M % 32
+    assert fused_q(A, Bw, layout=7) == 1
+    assert fused_q(A, Bw, h=FAKE, ldh=260) == 3                            # h rows 16-byte aligned
+    assert fused_q(A, Bw, K=96) == 2                                       # K % 64
+    assert fused_q(A, Bw, M=0) == 0                                        # nothing to do
 
 
 def test_dequantize_and_swiglu_reject_bad_arguments():
