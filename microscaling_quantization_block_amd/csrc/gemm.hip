@@ -1666,50 +1666,55 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
     raw[f] = *reinterpret_cast<const uint4*>(L + o);
   };
   // block scales of a stage as FP16 pairs: per fragment and 64-K half, the
-  // lane's two blocks (K [32h, 32h + 16) and [32h + 16, 32h + 32)), converted
-  // once per stage (exact: E4M3 values are FP16 normals)
+  // lane's two blocks (K [32h, 32h + 16) and [32h + 16, 32h + 32)) (exact:
+  // E4M3 values are FP16 normals).  The stage's scale words are read into scw
+  // and converted per fragment (cvt_sc).
   h2 sc[NF][2];
-  auto read_sc = [&](int s) {
+  uint32_t scw[NF][2];
+  auto read_scw = [&](int s) {
     const uint8_t* L = lds + (s & (NVD_NBUF - 1)) * NVD_STAGE + NVD_DATA;
     const uint4* ea = reinterpret_cast<const uint4*>(L + (wm * 32 + r32) * 32);
-    const uint32_t sh = 16u * (uint32_t)h;
     const uint4 a0 = ea[0], a1 = ea[1];
-    const uint32_t av[4][2] = {{a0.x, a0.y}, {a0.z, a0.w}, {a1.x, a1.y}, {a1.z, a1.w}};
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) sc[t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(av[t][hf] >> sh, 1.0f, false);
+    scw[0][0] = a0.x; scw[0][1] = a0.y; scw[1][0] = a0.z; scw[1][1] = a0.w;
+    scw[2][0] = a1.x; scw[2][1] = a1.y; scw[3][0] = a1.z; scw[3][1] = a1.w;
     // B: rows wn WN + r + 32t lie in half (wn WN) / 128, tiles from (wn WN % 128) / 32
     const int eb = ((wn * WN) >> 7) * 32 + r32, tb = ((wn * WN) & 127) >> 5;
     const uint4* pb = reinterpret_cast<const uint4*>(L + 2048 + eb * 32 + tb * 8);
+    const uint4 b0 = pb[0];
+    scw[TM][0] = b0.x; scw[TM][1] = b0.y; scw[TM + 1][0] = b0.z; scw[TM + 1][1] = b0.w;
     if constexpr (TN == 4) {
-      const uint4 b0 = pb[0], b1 = pb[1];
-      const uint32_t bv[4][2] = {{b0.x, b0.y}, {b0.z, b0.w}, {b1.x, b1.y}, {b1.z, b1.w}};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          sc[TM + t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bv[t][hf] >> sh, 1.0f, false);
-    } else {
-      const uint4 b0 = pb[0];
-      const uint32_t bv[2][2] = {{b0.x, b0.y}, {b0.z, b0.w}};
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          sc[TM + t][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bv[t][hf] >> sh, 1.0f, false);
+      const uint4 b1 = pb[1];
+      scw[TM + 2][0] = b1.x; scw[TM + 2][1] = b1.y; scw[TM + 3][0] = b1.z; scw[TM + 3][1] = b1.w;
     }
   };
-  // FP16 operands of one K step, two sets
-  v8h cv[2][NF];
-  auto convert = [&](const uint4& r, h2 s01, int ks, v8h& dst) {
+  auto cvt_sc = [&](int f) {
+    const uint32_t sh = 16u * (uint32_t)h;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) sc[f][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scw[f][hf] >> sh, 1.0f, false);
+  };
+  auto read_sc = [&](int s) {
+    read_scw(s);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) cvt_sc(f);
+  };
+  // FP16 operands of one K step, two sets (packed FP16 pairs)
+  uint4 cv[2][NF];
+  // part 0: values 0..3 of the lane's 8 (code bytes 0, 1), part 1: values 4..7
+  auto convert_part = [&](const uint4& r, h2 s01, int ks, int part, uint4& dst) {
     const h2 sp = (ks >> 1) ? h2{s01.y, s01.y} : h2{s01.x, s01.x};
     const uint32_t word = ks == 0 ? r.x : ks == 1 ? r.y : ks == 2 ? r.z : r.w;
-    uint32_t o[4];
-    fp4x8_to_f16(word, sp, o);
-    dst = __builtin_bit_cast(v8h, make_uint4(o[0], o[1], o[2], o[3]));
+    if (part == 0) {
+      dst.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sp);
+      dst.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sp);
+    } else {
+      dst.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sp);
+      dst.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sp);
+    }
   };
-
+  auto convert = [&](const uint4& r, h2 s01, int ks, uint4& dst) {
+    convert_part(r, s01, ks, 0, dst);
+    convert_part(r, s01, ks, 1, dst);
+  };
   v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -1717,6 +1722,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mfma = [&](int set, int tm, int tn) {
+    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, cv[set][TM + tn]),
+                                                         __builtin_bit_cast(v8h, cv[set][tm]), acc[tm][tn], 0, 0, 0);
+  };
 
   // Vector-memory instructions per lane and stage: NV.  At the top of stage
   // s the loads of stage s + 1 must be done; issued after them: stage s + 2's.
@@ -1731,14 +1740,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) convert(raw[f], sc[f][0], 0, cv[0][f]);
 
-  // One stage: 8 K steps of TM TN MFMAs.  After MFMA i of a K step: the
-  // conversion of fragment i of the next K step (i < NF); in K step 2, the
-  // raw read of fragment i - 2 of this stage's second half (its conversion
-  // from the first half is issued by then); in K step 4 the loads of stage
-  // s + 3; in K step 6 the raw read of fragment i - 2 of the next stage's
-  // first half and, last, its scale words.  Scheduling barriers keep the order.
   constexpr int NM = TM * TN;
-  static_assert(NF + 2 <= NM + 2 && NV <= NM, "slots");
+  static_assert(NV <= NM, "slots");
   for (int s = 0; s < nk; ++s) {
     wait_vmcnt<NV>();                                      // stage s + 1 landed (this lane's share)
     asm volatile("s_barrier" ::: "memory");
@@ -1748,23 +1751,53 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
       const int set = kk & 1;
       const int nkk = (kk + 1) & 7;                        // next K step (of this stage or the next)
       const int nhalf = nkk >> 2, nks = nkk & 3;
+      if constexpr (NF * 2 == NM) {
+        // 4 waves: after MFMA i of a K step, half i % 2 of the conversion of
+        // fragment f = i / 2 for the next K step (four VALU instructions,
+        // about what one 32-cycle MFMA hides); in K step 2, after MFMA
+        // 2f + 2 (f = 7: after MFMA 15), the raw read of fragment f of this
+        // stage's second half (its last conversion from the first half is
+        // issued by then); in K step 4 the loads of stage s + 3; in K step 6
+        // the scale words of the next stage (after MFMA 0) and the raw reads
+        // of its first half, placed as in K step 2; in K step 7 each
+        // fragment's block scales are converted just before its conversion.
 #pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        const int tm = i / TN, tn = i % TN;
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cv[set][TM + tn], cv[set][tm], acc[tm][tn], 0, 0, 0);
-        if (i < NF) convert(raw[i], sc[i][nhalf], nks, cv[set ^ 1][i]);
-        if (kk == 2 && i >= 2 && i - 2 < NF) read_raw(s, 1, i - 2);
-        if (kk == 2 && i == NM - 1)
-#pragma unroll
-          for (int f = NM - 2; f < NF; ++f) read_raw(s, 1, f);
-        if (kk == 4 && i < NV) dma_part(s + 3, i);
-        if (kk == 6 && i >= 2 && i - 2 < NF) read_raw(s + 1, 0, i - 2);
-        if (kk == 6 && i == NM - 1) {
-#pragma unroll
-          for (int f = NM - 2; f < NF; ++f) read_raw(s + 1, 0, f);
-          read_sc(s + 1);
+        for (int i = 0; i < NM; ++i) {
+          const int f = i >> 1, part = i & 1;
+          mfma(set, i / TN, i % TN);
+          if (kk == 7 && part == 0) cvt_sc(f);
+          convert_part(raw[f], sc[f][nhalf], nks, part, cv[set ^ 1][f]);
+          if (kk == 2 && part == 0 && f >= 1) read_raw(s, 1, f - 1);
+          if (kk == 2 && i == NM - 1) read_raw(s, 1, NF - 1);
+          if (kk == 4 && i < NV) dma_part(s + 3, i);
+          if (kk == 6 && i == 0) read_scw(s + 1);
+          if (kk == 6 && part == 0 && f >= 1) read_raw(s + 1, 0, f - 1);
+          if (kk == 6 && i == NM - 1) read_raw(s + 1, 0, NF - 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // 8 waves: after MFMA i of a K step, the conversion of fragment i of
+        // the next K step (i < NF); in K step 2, the raw read of fragment
+        // i - 2 of this stage's second half; in K step 4 the loads of stage
+        // s + 3; in K step 6 the raw read of fragment i - 2 of the next
+        // stage's first half and, last, its scale words.
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          mfma(set, i / TN, i % TN);
+          if (i < NF) convert(raw[i], sc[i][nhalf], nks, cv[set ^ 1][i]);
+          if (kk == 2 && i >= 2 && i - 2 < NF) read_raw(s, 1, i - 2);
+          if (kk == 2 && i == NM - 1)
+#pragma unroll
+            for (int f = NM - 2; f < NF; ++f) read_raw(s, 1, f);
+          if (kk == 4 && i < NV) dma_part(s + 3, i);
+          if (kk == 6 && i >= 2 && i - 2 < NF) read_raw(s + 1, 0, i - 2);
+          if (kk == 6 && i == NM - 1) {
+#pragma unroll
+            for (int f = NM - 2; f < NF; ++f) read_raw(s + 1, 0, f);
+            read_sc(s + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
