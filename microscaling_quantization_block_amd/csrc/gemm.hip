@@ -1687,15 +1687,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
       scw[TM + 2][0] = b1.x; scw[TM + 2][1] = b1.y; scw[TM + 3][0] = b1.z; scw[TM + 3][1] = b1.w;
     }
   };
-  auto cvt_sc = [&](int f) {
+  // the lane's two bytes of each word (lane half h) moved to the low half
+  auto shift_scw = [&](int f) {
     const uint32_t sh = 16u * (uint32_t)h;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) sc[f][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scw[f][hf] >> sh, 1.0f, false);
+    scw[f][0] >>= sh;
+    scw[f][1] >>= sh;
   };
+  auto cvt_sc = [&](int f, int hf) { sc[f][hf] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scw[f][hf], 1.0f, false); };
   auto read_sc = [&](int s) {
     read_scw(s);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) cvt_sc(f);
+    for (int f = 0; f < NF; ++f) {
+      shift_scw(f);
+      cvt_sc(f, 0);
+      cvt_sc(f, 1);
+    }
   };
   // FP16 operands of one K step, two sets (packed FP16 pairs)
   uint4 cv[2][NF];
@@ -1757,20 +1763,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
         // about what one 32-cycle MFMA hides); in K step 2, after MFMA
         // 2f + 2 (f = 7: after MFMA 15), the raw read of fragment f of this
         // stage's second half (its last conversion from the first half is
-        // issued by then); in K step 4 the loads of stage s + 3; in K step 6
-        // the scale words of the next stage (after MFMA 0) and the raw reads
-        // of its first half, placed as in K step 2; in K step 7 each
-        // fragment's block scales are converted just before its conversion.
+        // issued by then); in K steps 4 and 5 the loads of stage s + 3, half
+        // in each; in K step 6 the scale words of the next stage (after MFMA
+        // 0, shifted into place after MFMAs 4..11) and the raw reads of its
+        // first half, placed as in K step 2; in K step 7 each fragment's
+        // two block scales are converted, one before each half conversion.
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
           const int f = i >> 1, part = i & 1;
           mfma(set, i / TN, i % TN);
-          if (kk == 7 && part == 0) cvt_sc(f);
+          if (kk == 7) cvt_sc(f, part);
           convert_part(raw[f], sc[f][nhalf], nks, part, cv[set ^ 1][f]);
           if (kk == 2 && part == 0 && f >= 1) read_raw(s, 1, f - 1);
           if (kk == 2 && i == NM - 1) read_raw(s, 1, NF - 1);
-          if (kk == 4 && i < NV) dma_part(s + 3, i);
+          if (kk == 4 && i < NV / 2) dma_part(s + 3, i);
+          if (kk == 5 && i < NV - NV / 2) dma_part(s + 3, NV / 2 + i);
           if (kk == 6 && i == 0) read_scw(s + 1);
+          if (kk == 6 && i >= 4 && i - 4 < NF) shift_scw(i - 4);
           if (kk == 6 && part == 0 && f >= 1) read_raw(s + 1, 0, f - 1);
           if (kk == 6 && i == NM - 1) read_raw(s + 1, 0, NF - 1);
           __builtin_amdgcn_sched_barrier(0);
