@@ -1250,6 +1250,18 @@ __device__ __forceinline__ void dma16(const srd_t& srd, uint32_t lds_addr, uint3
 __device__ __forceinline__ void dma4(const srd_t& srd, uint32_t lds_addr, uint32_t voff) {
   asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(lds_addr) : "memory");
 }
+// The same with a wave-uniform byte offset soff added by the instruction
+// (its SGPR offset), so that a per-stage offset costs no VALU add.  soff must
+// keep every in-range lane inside its row; lanes whose voff is out of range
+// (bit 31 set) stay out of range.
+__device__ __forceinline__ void dma16s(const srd_t& srd, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(srd), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ void dma4s(const srd_t& srd, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(srd), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -1626,23 +1638,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
   const uint32_t b_sst = (p.b_tile || !p.b_mfma_layout) ? 8u : 256u;
 
   // part i of stage s: A code rows (i < CI), B code rows, A scale words, B
-  // scale words
+  // scale words.  The stage's K offset rides in the instruction's SGPR
+  // offset; a stage past the end loads through descriptors of zero size
+  // (zeros, no memory traffic).  Part 0 of a stage comes first.
+  srd_t cA = sA, cB = sB, cAs = sAs, cBs = sBs;
   auto dma_part = [&](int s, int i) {
     const uint32_t L = lbase + (uint32_t)((s & (NVD_NBUF - 1)) * NVD_STAGE);
     const bool sin = s < nk;
-    const uint32_t ko = sin ? (uint32_t)s * 64u : 0x80000000u;
+    if (i == 0) {
+      // the descriptors' sizes: zero from the first stage past the end
+      cA[2] = sin ? sA[2] : 0u;
+      cB[2] = sin ? sB[2] : 0u;
+      cAs[2] = sin ? sAs[2] : 0u;
+      cBs[2] = sin ? sBs[2] : 0u;
+    }
+    const uint32_t ko = sin ? (uint32_t)s * 64u : 0u;
     if (i < CI) {
-      dma16(sA, L + (uint32_t)((CI * w + i) * 1024), a_dv[i] + ko);
+      dma16s(cA, L + (uint32_t)((CI * w + i) * 1024), a_dv[i], ko);
     } else if (i < 2 * CI) {
       const int j = i - CI;
-      dma16(sB, L + (uint32_t)(DMA_BM * NVD_ROW + (CI * w + j) * 1024), b_dv[j] + ko);
+      dma16s(cB, L + (uint32_t)(DMA_BM * NVD_ROW + (CI * w + j) * 1024), b_dv[j], ko);
     } else if (i < 2 * CI + SI) {
       const int j = i - 2 * CI;
-      dma4(sAs, L + NVD_DATA + (uint32_t)((8 * (SI * w + j)) * 32), sin ? a_sv[j] + (uint32_t)s * a_sst : 0x80000000u);
+      dma4s(cAs, L + NVD_DATA + (uint32_t)((8 * (SI * w + j)) * 32), a_sv[j], sin ? (uint32_t)s * a_sst : 0u);
     } else {
       const int j = i - 2 * CI - SI;
-      dma4(sBs, L + NVD_DATA + 2048u + (uint32_t)((8 * (SI * w + j)) * 32),
-           sin ? b_sv[j] + (uint32_t)s * b_sst : 0x80000000u);
+      dma4s(cBs, L + NVD_DATA + 2048u + (uint32_t)((8 * (SI * w + j)) * 32), b_sv[j],
+            sin ? (uint32_t)s * b_sst : 0u);
     }
   };
   auto dma = [&](int s) {
