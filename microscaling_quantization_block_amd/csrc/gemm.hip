@@ -1779,56 +1779,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
       const int set = kk & 1;
       const int nkk = (kk + 1) & 7;                        // next K step (of this stage or the next)
       const int nhalf = nkk >> 2, nks = nkk & 3;
-      if constexpr (NF * 2 == NM) {
-        // 4 waves: after MFMA i of a K step, half i % 2 of the conversion of
-        // fragment f = i / 2 for the next K step (four VALU instructions,
-        // about what one 32-cycle MFMA hides); in K step 2, after MFMA
-        // 2f + 2 (f = 7: after MFMA 15), the raw read of fragment f of this
-        // stage's second half (its last conversion from the first half is
-        // issued by then); in K steps 4 and 5 the loads of stage s + 3, half
-        // in each; in K step 6 the scale words of the next stage (after MFMA
-        // 0, shifted into place after MFMAs 4..11) and the raw reads of its
-        // first half, placed as in K step 2; in K step 7 each fragment's
-        // two block scales are converted, one before each half conversion.
+      // After MFMA i of a K step: the half conversions j = i, i + NM, ... of
+      // the next K step (half j: part j % 2 of fragment j / 2; two
+      // conversions and two multiplies, four VALU instructions, about what
+      // one 32-cycle MFMA hides; 4 waves: one half per MFMA, 8 waves: one or
+      // two).  In K step 2 the raw read of fragment f of this stage's second
+      // half right after its last half conversion from the first half; in K
+      // steps 4 and 5 the loads of stage s + 3, half in each; in K step 6
+      // the scale words of the next stage (after MFMA 0, shifted into place
+      // after MFMAs 4, 5, ...) and the raw reads of its first half, placed
+      // as in K step 2; in K step 7 each fragment's two block scales are
+      // converted, one before each of its half conversions.
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          const int f = i >> 1, part = i & 1;
-          mfma(set, i / TN, i % TN);
+      for (int i = 0; i < NM; ++i) {
+        mfma(set, i / TN, i % TN);
+#pragma unroll
+        for (int j = i; j < 2 * NF; j += NM) {
+          const int f = j >> 1, part = j & 1;
           if (kk == 7) cvt_sc(f, part);
           convert_part(raw[f], sc[f][nhalf], nks, part, cv[set ^ 1][f]);
-          if (kk == 2 && part == 0 && f >= 1) read_raw(s, 1, f - 1);
-          if (kk == 2 && i == NM - 1) read_raw(s, 1, NF - 1);
-          if (kk == 4 && i < NV / 2) dma_part(s + 3, i);
-          if (kk == 5 && i < NV - NV / 2) dma_part(s + 3, NV / 2 + i);
-          if (kk == 6 && i == 0) read_scw(s + 1);
-          if (kk == 6 && i >= 4 && i - 4 < NF) shift_scw(i - 4);
-          if (kk == 6 && part == 0 && f >= 1) read_raw(s + 1, 0, f - 1);
-          if (kk == 6 && i == NM - 1) read_raw(s + 1, 0, NF - 1);
-          __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-        // 8 waves: after MFMA i of a K step, the conversion of fragment i of
-        // the next K step (i < NF); in K step 2, the raw read of fragment
-        // i - 2 of this stage's second half; in K step 4 the loads of stage
-        // s + 3; in K step 6 the raw read of fragment i - 2 of the next
-        // stage's first half and, last, its scale words.
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          mfma(set, i / TN, i % TN);
-          if (i < NF) convert(raw[i], sc[i][nhalf], nks, cv[set ^ 1][i]);
-          if (kk == 2 && i >= 2 && i - 2 < NF) read_raw(s, 1, i - 2);
-          if (kk == 2 && i == NM - 1)
-#pragma unroll
-            for (int f = NM - 2; f < NF; ++f) read_raw(s, 1, f);
-          if (kk == 4 && i < NV) dma_part(s + 3, i);
-          if (kk == 6 && i >= 2 && i - 2 < NF) read_raw(s + 1, 0, i - 2);
-          if (kk == 6 && i == NM - 1) {
-#pragma unroll
-            for (int f = NM - 2; f < NF; ++f) read_raw(s + 1, 0, f);
-            read_sc(s + 1);
+        for (int f = 0; f < NF; ++f) {
+          // slot of fragment f's second half; its raw chunk is reread after it
+          const int last = (2 * f + 1) % NM;
+          if (last + 1 == i || (last == NM - 1 && i == NM - 1)) {
+            if (kk == 2) read_raw(s, 1, f);
+            if (kk == 6) read_raw(s + 1, 0, f);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        if (kk == 4 && i < NV / 2) dma_part(s + 3, i);
+        if (kk == 5 && i < NV - NV / 2) dma_part(s + 3, NV / 2 + i);
+        if (kk == 6 && i == 0) read_scw(s + 1);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (kk == 6 && (4 + f < NM ? 4 + f : NM - 1) == i) shift_scw(f);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
