@@ -551,11 +551,14 @@ __global__ __launch_bounds__(256) void nvfp4_col_kernel(
     uint32_t stream_id, uint32_t tensor_tag, int64_t n_ct) {
   const float S = tensor_scale(gscales, gmode);
   if (gmode == 1 && threadIdx.x == 0) gscales[0] = S;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t rt = blockIdx.x / n_ct, ct = blockIdx.x - rt * n_ct;
   const int64_t strips = rows >> 4;
-  const int64_t strip = rt * 16 + (lane & 15);
-  const int64_t c0 = ct * 128 + (threadIdx.x >> 6) * 32 + (lane >> 4) * 8;
+  // a workgroup: 16 strips x 128 columns; wave w: strips 8 (w & 1) .. + 8,
+  // columns 64 (w >> 1) .. + 64; lane l: strip l % 8, 8 columns from 8 (l / 8),
+  // so each row's 128 bytes of a wave come from one 16-byte load of 8 lanes
+  const int64_t strip = rt * 16 + (wv & 1) * 8 + (lane & 7);
+  const int64_t c0 = ct * 128 + (wv >> 1) * 64 + (lane >> 3) * 8;
   if (strip >= strips || c0 >= cols) return;
   const int64_t r0 = strip * 16;
   uint4 v[16];
