@@ -105,6 +105,14 @@ __device__ __forceinline__ uint32_t in_range(bool ok, uint32_t off) {
   return off | ((uint32_t)!ok << 31);
 }
 
+// 16 bytes of output with the non-temporal hint: a GEMM's output is not read
+// again by the kernel, and streaming it past the caches leaves them to the
+// operand panels (config-5 NVFP4 GEMMs 0.5-2% faster)
+__device__ __forceinline__ void store_nt16(uint16_t* dst, uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
+}
+
 // ------------------------------------------------------------ FP4 -> FP16
 // Eight E2M1 codes (one word, element 2j in the low nibble of byte j) times
 // the block scale: four words of packed FP16 pairs.  Both steps are exact.
@@ -1502,7 +1510,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
       if (m < M) {
         uint16_t* const dst = p.c + m * p.ldc + n;
         if (vec16 && n + 7 < N) {
-          *reinterpret_cast<uint4*>(dst) = val;
+          store_nt16(dst, val);
         } else {
           const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
@@ -1859,7 +1867,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
                                       swiglu_bf16x2(gv.z, uv.z), swiglu_bf16x2(gv.w, uv.w));
           uint16_t* const dst = p.c + m * p.ldc + hc;
           if (vec16) {
-            *reinterpret_cast<uint4*>(dst) = hv;
+            store_nt16(dst, hv);
           } else {
             const uint32_t wv[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
@@ -1878,7 +1886,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_nvfp4_dma_kernel(GemmArgs p) {
       if (m < m_end) {
         uint16_t* const dst = p.c + m * p.ldc + n;
         if (vec16 && n + 7 < N) {
-          *reinterpret_cast<uint4*>(dst) = val;
+          store_nt16(dst, val);
         } else {
           const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
