@@ -1534,6 +1534,259 @@ static hipError_t launch_fp8_dma(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// MXFP8 (32-wide E8M0 blocks) on whole cache lines.  The kernel above loads
+// 64 bytes of each row per stage, half of a 128-byte line: its counters at
+// 8192x24576x4096 showed the load path (texture addresser and L1) busy 84% of
+// the time on one request per half line, a third of them for per-pair scale
+// words.  This kernel loads stage pairs (128 K: a row's whole line) and the
+// scale words in groups of four pairs:
+//  * two pair buffers of 64 KB (rows of 128 bytes, chunk c of row r in slot
+//    c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows cover
+//    all banks); a DMA instruction fills 8 rows, lane l taking row l / 8 and
+//    slot l % 8;
+//  * pair P + 2's loads are issued during stage 2P + 1 (one after each
+//    MFMA) into the buffer pair P has left; at the top of every odd stage the
+//    wave waits for all its loads and the workgroup meets at a barrier (pair
+//    P + 1 landed, pair P's buffer free): one barrier per pair;
+//  * scale words: a two-slot ring of 8 KB groups, group g (pairs 4g .. 4g + 3)
+//    as [row][pair] words, A's 256 rows then B's.  Lane l of a group load
+//    takes the word of pair l % 4 of row 16 k + l / 4 (k: the load's part),
+//    so a row's four words (16 contiguous bytes in the linear and tile
+//    layouts) are one request.  Part p of group g rides with odd stage
+//    8g - 9 + 2p: after the last read of group g - 2 in the same slot (pair
+//    4g - 5, read in stage 8g - 11) and before the first read of group g
+//    (pair 4g, read in stage 8g - 1).
+// Each lane feeds its MFMAs the same K bytes and scale bytes as the kernels
+// above, so all give the same bits.
+constexpr int FP8P_ROW = 128;                                // LDS bytes per row and stage pair
+constexpr int FP8P_DATA = (DMA_BM + DMA_BN) * FP8P_ROW;      // 64 KB of A and B rows
+constexpr int FP8P_SG = 2 * FP8P_DATA;                       // the scale-group ring
+constexpr int FP8P_SGS = 8192;                               // one group: 256 A rows, 256 B rows, 16 bytes each
+constexpr int FP8P_LDS = FP8P_SG + 2 * FP8P_SGS;             // 144 KB
+
+__global__ __launch_bounds__(256) void gemm_fp8_pair_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+  int mt, nt;
+  if (!xcd_tile(tiles_m, tiles_n, p.N * p.K <= ((int64_t)4 << 20) ? 1 : 4, mt, nt)) return;
+  const int K = (int)p.K, N = (int)p.N, M = (int)p.M;
+  const int m0 = mt * DMA_BM, n0 = nt * DMA_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (the loads' LDS base)
+  const int wm = w >> 1, wn = w & 1;                        // wave tile: rows wm*128, columns wn*128
+  const int h = lane >> 5, r32 = lane & 31;
+  const int np = K / 128;                                   // stage pairs
+  const int nb32 = K >> 5;
+  const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+
+  const srd_t sA = make_srd(p.a, p.a_rows * p.lda);
+  const srd_t sB = make_srd(p.b, p.N * p.ldb);
+  const srd_t sAs = make_srd(p.a_scales, p.a_rows * nb32);
+  const srd_t sBs = make_srd(p.b_scales, p.b_group_scales);
+  const uint32_t arb = (uint32_t)p.lda, brb = (uint32_t)p.ldb;
+
+  // Data: wave w fills rows 64 w + 8 i .. + 8 of A and of B (i = 0..7)
+  uint32_t a_dv[8], b_dv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 64 * w + 8 * i + (lane >> 3);
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+    const bool aok = m0 + r < M, bok = n0 + r < N;
+    a_dv[i] = in_range(aok, (uint32_t)(aok ? m0 + r : 0) * arb + c * 16u);
+    b_dv[i] = in_range(bok, (uint32_t)(bok ? n0 + r : 0) * brb + c * 16u);
+  }
+  // Scale groups.  Part k's rows lie 16 k below part 0's: a wave-uniform
+  // step in every layout, added through the instruction's SGPR offset; a
+  // lane's rows past the operand's end are marked in a 4-bit mask.
+  const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;      // a word's step per pair
+  const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
+  uint32_t a_gv, b_gv, a_gm = 0, b_gm = 0;
+  {
+    const int R = 64 * w + (lane >> 2), q = lane & 3;
+    const int n = n0 + R;
+    a_gv = (uint32_t)scale_offset(m0 + R, 0, nb32, p.a_mfma_layout) + (uint32_t)q * a_sstep;
+    b_gv = (p.b_tile ? (uint32_t)((n >> 5) * nb32) : (uint32_t)scale_offset(n, 0, nb32, p.b_mfma_layout)) +
+           (uint32_t)q * b_sstep;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a_gm |= (uint32_t)(m0 + R + 16 * k >= M) << k;
+      b_gm |= (uint32_t)(n + 16 * k >= N) << k;
+    }
+  }
+  // part k's step from part 0: (k / 2) 32-row chunks, plus 16 rows when k is odd
+  const uint32_t a_g2 = p.a_mfma_layout ? (uint32_t)(nb32 >> 2) * 128u : (uint32_t)(32 * nb32);
+  const uint32_t a_g1 = p.a_mfma_layout ? 64u : (uint32_t)(16 * nb32);
+  const uint32_t b_g2 = p.b_tile ? (uint32_t)nb32 : p.b_mfma_layout ? (uint32_t)(nb32 >> 2) * 128u : (uint32_t)(32 * nb32);
+  const uint32_t b_g1 = p.b_tile ? 0u : p.b_mfma_layout ? 64u : (uint32_t)(16 * nb32);
+
+  // load i (0..15) of pair P: A rows (i < 8) or B rows of this wave.  The
+  // pair's K offset rides in the SGPR offset (it keeps every lane inside its
+  // row); pairs past the end load through descriptors of zero size.
+  srd_t cA = sA, cB = sB;
+  auto dma_part = [&](int P, int i) {
+    const uint32_t L = lbase + (uint32_t)((P & 1) * FP8P_DATA);
+    const bool pin = P < np;
+    if (i == 0) {
+      cA[2] = pin ? sA[2] : 0u;
+      cB[2] = pin ? sB[2] : 0u;
+    }
+    const uint32_t ko = pin ? (uint32_t)P * 128u : 0u;
+    if (i < 8) dma16s(cA, L + (uint32_t)((64 * w + 8 * i) * FP8P_ROW), a_dv[i], ko);
+    else dma16s(cB, L + (uint32_t)(DMA_BM * FP8P_ROW + (64 * w + 8 * (i - 8)) * FP8P_ROW), b_dv[i - 8], ko);
+  };
+  // part k of scale group G: this wave's A and B words of rows 64 w + 16 k + (0..15)
+  auto dma_grp = [&](int G, int k) {
+    const uint32_t L = lbase + FP8P_SG + (uint32_t)((G & 1) * FP8P_SGS + (64 * w + 16 * k) * 16);
+    const bool gin = 4 * G < np;
+    srd_t gA = sAs, gB = sBs;
+    gA[2] = gin ? sAs[2] : 0u;
+    gB[2] = gin ? sBs[2] : 0u;
+    // lanes of pairs past the last (a partial last group) load nothing either:
+    // the SGPR offset escapes the range check, so every in-range lane's whole
+    // address must lie inside the operand's scales
+    const uint32_t pk = (uint32_t)(4 * G + (lane & 3) >= np) << 31;
+    const uint32_t av = a_gv | (((a_gm >> k) & 1u) << 31) | pk, bv = b_gv | (((b_gm >> k) & 1u) << 31) | pk;
+    const uint32_t ak = (uint32_t)(k >> 1) * a_g2 + (uint32_t)(k & 1) * a_g1;
+    const uint32_t bk = (uint32_t)(k >> 1) * b_g2 + (uint32_t)(k & 1) * b_g1;
+    dma4s(gA, L, av, gin ? (uint32_t)(4 * G) * a_sstep + ak : 0u);
+    dma4s(gB, L + 4096u, bv, gin ? (uint32_t)(4 * G) * b_sstep + bk : 0u);
+  };
+
+  // fragment reads: tile t of A (rows wm*128 + 32t + r) and of B, stage e of
+  // a pair: chunks 4e + h and 4e + 2 + h ((r >> 1) & 7 is the same for r + 32t)
+  const int ra = wm * 128 + r32, rb = wn * 128 + r32;
+  const uint32_t swa = (uint32_t)((ra >> 1) & 7), swb = (uint32_t)((rb >> 1) & 7);
+  const uint32_t cra = (uint32_t)(ra * FP8P_ROW), crb = (uint32_t)(DMA_BM * FP8P_ROW + rb * FP8P_ROW);
+  v8i fa[2][4], fb[2][4];
+  // part k of stage e of pair P's fragments: A tile k (k < 4) or B tile k - 4
+  auto read_part = [&](int P, int e, int set, int k) {
+    const uint8_t* L = lds + (P & 1) * FP8P_DATA;
+    const int t = k & 3;
+    const uint32_t base = (k < 4 ? cra : crb) + (uint32_t)(t * 32 * FP8P_ROW);
+    const uint32_t sw = k < 4 ? swa : swb;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(L + base + (((uint32_t)(4 * e + h) ^ sw) << 4));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(L + base + (((uint32_t)(4 * e + 2 + h) ^ sw) << 4));
+    const v8i v = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    if (k < 4) fa[set][t] = v;
+    else fb[set][t] = v;
+  };
+  // pair P's scale words (lane half h: its block's byte to byte 0/2)
+  struct Sc { uint32_t a[4], b[4]; };
+  auto read_sc = [&](int P) {
+    const uint8_t* G = lds + FP8P_SG + ((P >> 2) & 1) * FP8P_SGS + (P & 3) * 4;
+    Sc v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v.a[t] = *reinterpret_cast<const uint32_t*>(G + (ra + 32 * t) * 16) >> (8 * h);
+      v.b[t] = *reinterpret_cast<const uint32_t*>(G + 4096 + (rb + 32 * t) * 16) >> (8 * h);
+    }
+    return v;
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Prologue: pair 0, scale group 0, part 0 of group 1, pair 1.  Then wait
+  // for pair 0 and group 0 (18 loads of this lane issued after them).
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_part(0, i);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dma_grp(0, k);
+  dma_grp(1, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_part(1, i);
+  wait_vmcnt<18>();
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 8; ++k) read_part(0, 0, 0, k);
+  Sc cur = read_sc(0), nxt;
+
+  for (int P = 0; P < np; ++P) {
+    // stage 2P: fragment set 0, scale bytes 0; the reads of stage 2P + 1
+    // (same pair) after the first eight MFMAs, two each
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tm = i >> 2, tn = i & 3;
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fb[0][tn], fa[0][tm], acc[tm][tn], 0, 0, 0, (int)cur.b[tn], 0, (int)cur.a[tm]);
+      if (i < 8) read_part(P, 1, 1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage 2P + 1: every load of this wave landed (pair P + 1 and the scale
+    // parts issued with it), and every wave is done with pair P's buffer
+    wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tm = i >> 2, tn = i & 3;
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fb[1][tn], fa[1][tm], acc[tm][tn], 0, 0, 2, (int)cur.b[tn], 2, (int)cur.a[tm]);
+      if (i < 8) read_part(P + 1, 0, 0, i);
+      if (i == 7) nxt = read_sc(P + 1);
+      dma_part(P + 2, i);
+      if (i == 15) dma_grp((P + 5) >> 2, (P + 5) & 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
+  }
+
+  // ------------------------------------------------ epilogue (as above)
+  wait_vmcnt<0>();                     // no load still writing LDS
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int WN = 128;
+  constexpr int EROW = WN * 2 + 8;
+  constexpr int ECH = WN / 8;
+  constexpr int ERI = 64 / ECH;
+  uint8_t* const E = lds + w * (32 * EROW);
+  const bool vec16 = ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+    uint8_t* const er = E + r32 * EROW + h * 8;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(er + (tn * 32 + g * 8) * 2) =
+            make_uint2(f32x2_to_bf16x2(acc[tm][tn][4 * g], acc[tm][tn][4 * g + 1]),
+                       f32x2_to_bf16x2(acc[tm][tn][4 * g + 2], acc[tm][tn][4 * g + 3]));
+#pragma unroll
+    for (int it = 0; it < 32 / ERI; ++it) {
+      const int rr = it * ERI + lane / ECH, cc = lane % ECH;
+      const uint4 val = *reinterpret_cast<const uint4*>(E + rr * EROW + cc * 16);
+      const int64_t m = m0 + wm * 128 + tm * 32 + rr;
+      const int n = n0 + wn * WN + cc * 8;
+      if (m < M) {
+        uint16_t* const dst = p.c + m * p.ldc + n;
+        if (vec16 && n + 7 < N) {
+          store_nt16(dst, val);
+        } else {
+          const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) dst[i] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+        }
+      }
+    }
+  }
+}
+
+static hipError_t launch_fp8_pair(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
+  if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
+  static std::atomic<uint32_t> lds_set{0};
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_pair_kernel, FP8P_LDS, lds_set); e != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(gemm_fp8_pair_kernel, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), FP8P_LDS, st, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ NVFP4, direct to LDS
 // The NVFP4 counterpart of the kernel above, for dense launches with row-major
 // B and K % 128 == 0 (FPROP with the 16x16 weight copy, DGRAD with its
@@ -1981,7 +2234,7 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
     // row-major B, K % 128 == 0
     const bool dma_ok = a.num_groups == 0 && !a.row_index && a.K % 128 == 0;
     if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus)))
-      return a.a_b128 ? launch_fp8_dma<true>(a, st) : launch_fp8_dma<false>(a, st);
+      return a.a_b128 ? launch_fp8_dma<true>(a, st) : launch_fp8_pair(a, st);
   }
   if constexpr (PATH == P_F16 && !BT) {
     // NVFP4 likewise takes its direct-to-LDS kernel on 4 waves (7) for
