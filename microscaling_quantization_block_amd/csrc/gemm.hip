@@ -1194,10 +1194,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   }
 }
 
-// ------------------------------------------------------------ MXFP8, direct to LDS
-// A second MXFP8 kernel for dense launches with row-major B and K % 128 == 0
-// (FPROP with the 32x32 weight copy, DGRAD with its transposed copy, WGRAD with
-// the columnwise copies).  The register-staged kernel above spends most of its
+// ------------------------------------------------------------ FP8, direct to LDS
+// A second FP8 kernel for dense launches with row-major B and K % 128 == 0
+// (FPROP with the weight tile copy, DGRAD with its transposed copy, WGRAD with
+// the columnwise copies).  It serves blockwise FP8 with power-of-two scales;
+// MXFP8 takes its successor below, which loads whole cache lines.  The register-staged kernel above spends most of its
 // time moving data: its 256x128 tile writes 48 KB into LDS per 128 of K from
 // registers, and in a stage without loads and stores (a timing-only ablation)
 // it already runs 36% faster, while without its MFMAs only 18% faster.  Here:
@@ -1218,9 +1219,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 //    stage s + 1 run under the MFMAs of stage s;
 //  * the E8M0 scale words travel the same way: a stage pair's words (2 KB)
 //    are loaded into LDS with its even stage and read once per pair.
-// Measured (8192x24576x4096 MXFP8 FPROP, and DGRAD / WGRAD of the same
-// layer): 1311 / 1140 / 1272 us for the kernel above, 963-989 / 815-845 /
-// 854-885 us here.  Timing-only ablations of this kernel: without its loads
+// Measured when it still served MXFP8 (8192x24576x4096 FPROP, and DGRAD /
+// WGRAD of the same layer): 1311 / 1140 / 1272 us for the kernel above,
+// 963-989 / 815-845 / 854-885 us here.  Timing-only ablations of this kernel: without its loads
 // 698 / 546 / 538 us, without its waits for them no faster (the prefetch
 // hides the latency), every tile loading the same data 10% faster (little is
 // bound by HBM), without its barriers 8% faster.
@@ -1279,10 +1280,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// B128: blockwise FP8 (128-wide power-of-two blocks, linear scales): a row's
-// one scale byte per stage pair, fetched with the aligned word holding it and
+// Blockwise FP8 (128-wide power-of-two blocks, linear scales): a row's one
+// scale byte per stage pair, fetched with the aligned word holding it and
 // replicated into all four bytes (both K slices and lane halves take it).
-template <bool B128>
 __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tiles_n = gridDim.x, tiles_m = gridDim.y;
@@ -1297,13 +1297,13 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   const int wm = w >> 1, wn = w & 1;                        // wave tile: rows wm*128, columns wn*128
   const int h = lane >> 5, r32 = lane & 31;
   const int nk = K / 64;
-  const int nb32 = K >> 5, nb128 = K >> 7;
+  const int nb128 = K >> 7;
   const uint32_t lbase = (uint32_t)reinterpret_cast<uintptr_t>(lds);
 
   const srd_t sA = make_srd(p.a, p.a_rows * p.lda);
   const srd_t sB = make_srd(p.b, p.N * p.ldb);
-  const srd_t sAs = make_srd(p.a_scales, B128 ? (p.a_rows * nb128 + 3) & ~int64_t(3) : p.a_rows * nb32);
-  const srd_t sBs = make_srd(p.b_scales, B128 ? (p.b_group_scales + 3) & ~int64_t(3) : p.b_group_scales);
+  const srd_t sAs = make_srd(p.a_scales, (p.a_rows * nb128 + 3) & ~int64_t(3));
+  const srd_t sBs = make_srd(p.b_scales, (p.b_group_scales + 3) & ~int64_t(3));
   const uint32_t arb = (uint32_t)p.lda, brb = (uint32_t)p.ldb;
 
   // Data: wave w fills rows (4w + i) * 16 .. + 16 of A and of B.
@@ -1328,18 +1328,10 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
     const int r = (E >> 5) * 128 + (E & 31) + 32 * t;
     const bool aok = m0 + r < M, bok = n0 + r < N;
     const int n = n0 + r;
-    if constexpr (B128) {
-      // the byte of pair 0 (the load takes the aligned word of pair q's byte)
-      a_sv = in_range(aok, aok ? (uint32_t)((m0 + r) * nb128) : 0u);
-      b_sv = in_range(bok, bok ? (uint32_t)((p.b_tile ? (n >> 7) : n) * nb128) : 0u);
-    } else {
-      a_sv = in_range(aok, aok ? (uint32_t)scale_offset(m0 + r, 0, nb32, p.a_mfma_layout) : 0u);
-      b_sv = in_range(bok, bok ? (p.b_tile ? (uint32_t)((n >> 5) * nb32) : (uint32_t)scale_offset(n, 0, nb32, p.b_mfma_layout))
-                               : 0u);
-    }
+    // the byte of pair 0 (the load takes the aligned word of pair q's byte)
+    a_sv = in_range(aok, aok ? (uint32_t)((m0 + r) * nb128) : 0u);
+    b_sv = in_range(bok, bok ? (uint32_t)((p.b_tile ? (n >> 7) : n) * nb128) : 0u);
   }
-  const uint32_t a_sstep = p.a_mfma_layout ? 128u : 4u;
-  const uint32_t b_sstep = (p.b_tile || !p.b_mfma_layout) ? 4u : 128u;
 
   // stage s (in range or not) into buffer s % 4, with pair s / 2's scale
   // words when s is even; stages past the end read zeros, never computed
@@ -1354,13 +1346,8 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
     const uint32_t L = lbase + (uint32_t)((s & (DMA_NBUF - 1)) * DMA_STAGE);
     const int q = s >> 1;
     const bool qin = s < nk;
-    if constexpr (B128) {
-      dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? (a_sv + (uint32_t)q) & ~3u : 0x80000000u);
-      dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? (b_sv + (uint32_t)q) & ~3u : 0x80000000u);
-    } else {
-      dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? a_sv + (uint32_t)q * a_sstep : 0x80000000u);
-      dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? b_sv + (uint32_t)q * b_sstep : 0x80000000u);
-    }
+    dma4(sAs, L + DMA_DATA + (uint32_t)(w * 256), qin ? (a_sv + (uint32_t)q) & ~3u : 0x80000000u);
+    dma4(sBs, L + DMA_DATA + 1024u + (uint32_t)(w * 256), qin ? (b_sv + (uint32_t)q) & ~3u : 0x80000000u);
   };
   auto dma = [&](int s) {
 #pragma unroll
@@ -1392,34 +1379,26 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) read_part(s, set, k);
   };
-  // a stage pair's scale words (lane half h: its block's byte to byte 0/2;
-  // B128: the row's byte of the pair, in all four bytes)
+  // a stage pair's scale bytes: the row's byte of the pair, in all four bytes
   struct Sc { uint32_t a[4], b[4]; };
-  // B128: byte position of pair 0's byte in its word, per tile row of the lane
-  uint32_t a_b3[4] = {0, 0, 0, 0}, b_b3[4] = {0, 0, 0, 0};
-  if constexpr (B128) {
+  // byte position of pair 0's byte in its word, per tile row of the lane
+  uint32_t a_b3[4], b_b3[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a_b3[t] = (uint32_t)((m0 + ra + 32 * t) * nb128) & 3u;
-      b_b3[t] = (uint32_t)((p.b_tile ? ((n0 + rb + 32 * t) >> 7) : (n0 + rb + 32 * t)) * nb128) & 3u;
-    }
+  for (int t = 0; t < 4; ++t) {
+    a_b3[t] = (uint32_t)((m0 + ra + 32 * t) * nb128) & 3u;
+    b_b3[t] = (uint32_t)((p.b_tile ? ((n0 + rb + 32 * t) >> 7) : (n0 + rb + 32 * t)) * nb128) & 3u;
   }
   auto read_sc = [&](int s) {
     const uint8_t* L = lds + (s & (DMA_NBUF - 1)) * DMA_STAGE;
     const uint4 va = *reinterpret_cast<const uint4*>(L + fsa);
     const uint4 vb = *reinterpret_cast<const uint4*>(L + fsb);
     Sc v;
-    if constexpr (B128) {
-      const uint32_t q = (uint32_t)(s >> 1);
-      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+    const uint32_t q = (uint32_t)(s >> 1);
+    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v.a[t] = ((wa[t] >> (8 * ((a_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
-        v.b[t] = ((wb[t] >> (8 * ((b_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
-      }
-    } else {
-      v.a[0] = va.x >> (8 * h); v.a[1] = va.y >> (8 * h); v.a[2] = va.z >> (8 * h); v.a[3] = va.w >> (8 * h);
-      v.b[0] = vb.x >> (8 * h); v.b[1] = vb.y >> (8 * h); v.b[2] = vb.z >> (8 * h); v.b[3] = vb.w >> (8 * h);
+    for (int t = 0; t < 4; ++t) {
+      v.a[t] = ((wa[t] >> (8 * ((a_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
+      v.b[t] = ((wb[t] >> (8 * ((b_b3[t] + q) & 3u))) & 0xFFu) * 0x01010101u;
     }
     return v;
   };
@@ -1522,15 +1501,14 @@ __global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs p) {
   }
 }
 
-template <bool B128>
 static hipError_t launch_fp8_dma(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = (a.N + DMA_BN - 1) / DMA_BN, tiles_m = (a.M + DMA_BM - 1) / DMA_BM;
   if (tiles_n * tiles_m >= (1ll << 31) || tiles_m > 65535) return hipErrorInvalidValue;
   const size_t lds = (size_t)DMA_NBUF * DMA_STAGE;
   static std::atomic<uint32_t> lds_set{0};
-  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_dma_kernel<B128>, (int)lds, lds_set); e != hipSuccess)
+  if (hipError_t e = ensure_lds_limit((const void*)gemm_fp8_dma_kernel, (int)lds, lds_set); e != hipSuccess)
     return e;
-  hipLaunchKernelGGL(gemm_fp8_dma_kernel<B128>, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(gemm_fp8_dma_kernel, dim3((unsigned)tiles_n, (unsigned)tiles_m), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -2234,7 +2212,7 @@ static hipError_t launch_p(const GemmArgs& a, hipStream_t st) {
     // row-major B, K % 128 == 0
     const bool dma_ok = a.num_groups == 0 && !a.row_index && a.K % 128 == 0;
     if (dma_ok && (t == 7 || (t < 0 && tile_count(a, 256, 256) >= cus)))
-      return a.a_b128 ? launch_fp8_dma<true>(a, st) : launch_fp8_pair(a, st);
+      return a.a_b128 ? launch_fp8_dma(a, st) : launch_fp8_pair(a, st);
   }
   if constexpr (PATH == P_F16 && !BT) {
     // NVFP4 likewise takes its direct-to-LDS kernel on 4 waves (7) for
