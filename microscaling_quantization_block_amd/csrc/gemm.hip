@@ -1715,7 +1715,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_pair_kernel(GemmArgs p) {
     cur = nxt;
   }
 
-  // ------------------------------------------------ epilogue (as above)
+  // ------------------------------------------------ epilogue (as in gemm_kernel)
   wait_vmcnt<0>();                     // no load still writing LDS
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   constexpr int WN = 128;
@@ -1766,22 +1766,26 @@ static hipError_t launch_fp8_pair(const GemmArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ NVFP4, direct to LDS
-// The NVFP4 counterpart of the kernel above, for dense launches with row-major
-// B and K % 128 == 0 (FPROP with the 16x16 weight copy, DGRAD with its
-// transposed copy, WGRAD with the columnwise copies).  LDS holds the operands
-// as they are stored, FP4 codes and E4M3 scale bytes, loaded straight into it;
-// each wave converts the fragments it feeds its MFMAs (hardware FP4 -> FP16
-// with unit scale, times the block scale: exact, as in the kernel above).
+// The NVFP4 counterpart of the FP8 direct-to-LDS kernels above, for dense
+// launches with row-major B and K % 128 == 0 (FPROP with the 16x16 weight
+// copy, DGRAD with its transposed copy, WGRAD with the columnwise copies).
+// LDS holds the operands as they are stored, FP4 codes and E4M3 scale bytes,
+// loaded straight into it; each wave converts the fragments it feeds its
+// MFMAs (hardware FP4 -> FP16 with unit scale, times the block scale: exact,
+// as in the register-staged kernel).  Its stages load half lines (64 code
+// bytes of a row), like the first FP8 kernel: with four times the MFMA work
+// per loaded byte of FP8, its load path is 25-36% busy at the config-5
+// shapes, not its bound.
 // Against staging FP16 tiles through LDS this moves a quarter of the LDS
 // bytes and drops the LDS store instructions, at the cost of converting each
 // A and B value twice (the two waves that share a row or column of tiles).
 //  * 256x256 tile on 4 waves (one per SIMD), each 128x128: per 16 of K,
 //    16 MFMAs (v_mfma_f32_32x32x16_f16) and 8 fragment conversions.
 //  * Stages of 128 K: 256 A rows and 256 B rows of 64 code bytes (chunk c of
-//    a row in slot c ^ ((r >> 2) & 3), as above), then the rows' scale words
-//    (two per row and stage: blocks 8s .. 8s + 3 and 8s + 4 .. 8s + 7), in
-//    four LDS buffers of 36 KB; the loads of stage s + 3 are issued while
-//    stage s computes; one barrier per stage.
+//    a row in slot c ^ ((r >> 2) & 3), as in the first FP8 kernel), then the
+//    rows' scale words (two per row and stage: blocks 8s .. 8s + 3 and
+//    8s + 4 .. 8s + 7), in four LDS buffers of 36 KB; the loads of stage
+//    s + 3 are issued while stage s computes; one barrier per stage.
 //  * A lane (row r, K half h) reads, per 64 K, the 16 code bytes of K
 //    [32h, 32h + 32) of its row for each of its 8 tiles, a 64-K step ahead;
 //    K step ks (16 K) takes codes [32h + 8ks, +8) (one word), the order every
