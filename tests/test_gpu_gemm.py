@@ -189,6 +189,48 @@ def test_mxfp8_direct_to_lds_kernel(M, N, K, a_mfma, b_kind):
 
 
 @pytest.mark.parametrize("M,N,K,a_mfma,b_kind", [
+    (4100, 8224, 1024, False, "tile"),    # 17 x 33 tiles (more than one round), ragged M and N; 8 pairs
+    (8192, 4160, 1536, False, "row"),     # 32 x 17 tiles, ragged N; 12 pairs, linear scales on both
+    (4352, 8448, 2048, True, "row_mfma"), # 17 x 33 tiles; 16 pairs, MFMA-layout scales on both
+])
+def test_mxfp8_direct_to_lds_kernel_many_tiles(M, N, K, a_mfma, b_kind):
+    """Configuration 7 for MXFP8 (the whole-line kernel) over more tiles
+    than the CUs, in runs of four tile rows per XCD, with ragged edges and
+    every scale layout: matches the oracle and gives the bits of the
+    register-staged 256x128 kernel (configuration 5)."""
+    m = mxq()
+    x = _bf16((M, K), 1.0, 84)
+    w = _bf16((N, K), 0.02, 85)
+    say(f"mxfp8 direct-to-LDS, many tiles {M}x{N}x{K} a_mfma={a_mfma} b={b_kind}")
+    la = m.Layout.MFMA if a_mfma else m.Layout.LINEAR
+    cx, sx = m.mx_quantize(to_dev_bf16(x), layout=la)
+    A = m.Operand(m.Format.MXFP8, cx, sx, layout=la)
+    rcx, rsx = OM.quantize_rowwise(F.bf16_bits_to_f64(x))
+    a64 = OM.dequantize_f64(rcx, rsx)
+    if b_kind == "tile":
+        cw, sw = m.mx_quantize(to_dev_bf16(w), block=m.Block.TILE)
+        B = m.Operand(m.Format.MXFP8, cw, sw, block=m.Block.TILE)
+        rcw, rsw = OM.quantize_tile32(F.bf16_bits_to_f64(w))
+        b64 = OM.dequantize_f64(rcw, rsw, "32x32")
+    else:
+        lb = m.Layout.MFMA if b_kind == "row_mfma" else m.Layout.LINEAR
+        cw, sw = m.mx_quantize(to_dev_bf16(w), layout=lb)
+        B = m.Operand(m.Format.MXFP8, cw, sw, layout=lb)
+        rcw, rsw = OM.quantize_rowwise(F.bf16_bits_to_f64(w))
+        b64 = OM.dequantize_f64(rcw, rsw)
+    try:
+        m.mx_gemm_set_tile(7)
+        out7 = m.mx_gemm(A, B, M, N, K)
+        _assert_gemm(out7, a64, b64, a64, b64)
+        m.mx_gemm_set_tile(5)
+        out5 = m.mx_gemm(A, B, M, N, K)
+    finally:
+        m.mx_gemm_set_tile(-1)
+    o7, o5 = from_dev_bf16(out7), from_dev_bf16(out5)
+    assert np.array_equal(o7, o5), f"{int(np.sum(o7 != o5))} elements differ from the 256x128 kernel"
+
+
+@pytest.mark.parametrize("M,N,K,a_mfma,b_kind", [
     (600, 416, 384, False, "tile"),       # 3 x 2 tiles, ragged M; 3 stages of 128 K
     (256, 256, 128, True, "row_mfma"),    # one tile, one stage
     (544, 320, 1024, True, "tile"),       # 16x16 weight scales; 8 stages
